@@ -1,0 +1,119 @@
+"""Number formats of the decode path, decoded by their definitions (fp64).
+
+TEST INFRASTRUCTURE ONLY: part of the plain CPU oracle.  Nothing in the
+product path may import this package.
+
+The pages say the model ships "integer four builds" and that the output layer
+is quantized to 4 bits ("Flint 40B: Best Mid Sized LLM", transcript 05:39 and
+07:15; "Recursive Releases Flint...", section "Built by an Automated Research
+System").  They give no group size, scale type or nibble order, so the stored
+format is a stated choice:
+
+* symmetric int4 codes, one fp16 scale per group of 32 consecutive elements
+  along K; weight = (u - 8) * scale with stored code u in 0..15;
+* rows of K elements (K a multiple of 128) take K/2 bytes; element k of a row
+  sits in byte 64*t + 16*q + 4*j + e//2 with t = k//128, j = (k%128)//32,
+  q = (k%32)//8, e = k%8, low nibble for even e, high nibble for odd e;
+* scales are IEEE binary16 bit patterns, row-major [rows][K/32].
+
+Quantizer (offline, produces stored weights): per group a = max|w|,
+s = fp16_RNE(a/7) with a/7 in fp64; s == 0 gives all codes 8, otherwise
+q = clamp(round_half_even(w/s), -7, 7) and u = q + 8.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ floats
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> fp64.  A bf16 value is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """IEEE-754 binary16 bit patterns -> fp64 from the definition
+    (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b & 0x8000, -1.0, 1.0)
+    ex = (b >> 10) & 0x1F
+    fr = (b & 0x3FF).astype(np.float64)
+    normal = sign * (1.0 + fr / 1024.0) * np.exp2(ex.astype(np.float64) - 15.0)
+    subnormal = sign * (fr / 1024.0) * 2.0 ** -14
+    special = np.where(fr == 0, sign * np.inf, np.nan)
+    return np.where(ex == 0, subnormal, np.where(ex == 31, special, normal))
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    """fp64 -> binary16 bits, round to nearest even (numpy's conversion)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """fp64 -> bfloat16 bits, round to nearest even on the 8-bit significand.
+    Finite inputs within bf16's normal range (all the path produces)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    r = np.rint(m * 256.0)                  # 8 significant bits, ties to even
+    y = np.ldexp(r / 256.0, e)              # exact
+    return (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def f64_to_f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+# ------------------------------------------------------------------ int4
+
+
+def int4_positions(K: int):
+    """(byte index within a row, bit shift) of each element k = 0..K-1."""
+    assert K % 128 == 0
+    k = np.arange(K)
+    t, j, q, e = k // 128, (k % 128) // 32, (k % 32) // 8, k % 8
+    byte = 64 * t + 16 * q + 4 * j + e // 2
+    shift = 4 * (e % 2)
+    return byte, shift
+
+
+def unpack_codes(qbytes: np.ndarray, K: int) -> np.ndarray:
+    """Stored bytes [..., K/2] -> codes u [..., K] in 0..15."""
+    byte, shift = int4_positions(K)
+    b = np.asarray(qbytes, dtype=np.uint8)[..., byte]
+    return ((b >> shift.astype(np.uint8)) & 0xF).astype(np.int64)
+
+
+def pack_codes(u: np.ndarray) -> np.ndarray:
+    """Codes u [..., K] in 0..15 -> stored bytes [..., K/2]."""
+    u = np.asarray(u, dtype=np.int64)
+    K = u.shape[-1]
+    byte, shift = int4_positions(K)
+    out = np.zeros(u.shape[:-1] + (K // 2,), dtype=np.int64)
+    for k in range(K):
+        out[..., byte[k]] |= u[..., k] << shift[k]
+    return out.astype(np.uint8)
+
+
+def dequant(qbytes: np.ndarray, sbits: np.ndarray, K: int) -> np.ndarray:
+    """Stored int4 matrix -> fp64 weights [..., K]: w = (u - 8) * s[k // 32]."""
+    u = unpack_codes(qbytes, K)
+    s = f16_to_f64(sbits)
+    return (u - 8).astype(np.float64) * np.repeat(s, 32, axis=-1)
+
+
+def quantize(w: np.ndarray):
+    """fp32 weights [..., K] -> (codes u [..., K], scale bits [..., K/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    K = w.shape[-1]
+    g = w.reshape(w.shape[:-1] + (K // 32, 32)).astype(np.float64)
+    a = np.abs(g).max(axis=-1)
+    sbits = f64_to_f16_bits(a / 7.0)
+    s = f16_to_f64(sbits)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.clip(np.rint(g / s), -7, 7)
+    q = np.where(s == 0.0, 0.0, q)
+    u = (q + 8).astype(np.int64).reshape(w.shape)
+    return u, sbits

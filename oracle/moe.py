@@ -1,0 +1,224 @@
+"""Plain fp64 oracle of one sparse MoE layer decode step (and of a stack).
+
+TEST INFRASTRUCTURE ONLY: part of the plain CPU oracle.  Nothing in the
+product path may import this package.
+
+What the pages fix ("Flint 40B: Best Mid Sized LLM", transcript 02:35): each
+MoE layer holds 256 routed experts and a small router picks a few of them per
+token; only the picked experts run ("O que diferencia um MoE de 40 bilhões com
+2,5 bilhões ativos", noticiai.com.br page).  What they leave open is read as
+follows (each reading is also listed in the design notes):
+
+* router: logits l = W_r x + b in fp64 from fp32 weights and a bf16 x;
+* softmax over all E experts, then the k largest probabilities (ties: lower
+  expert index first), then the weights renormalized over the chosen set
+  (norm_topk=True) or kept as the softmax values (norm_topk=False);
+* expert: SwiGLU, h = silu(W_g x) * (W_u x) with silu(z) = z / (1 + e^-z),
+  then o = W_d h, all on dequantized int4 weights in fp64;
+* combine: y = sum over chosen experts of w_j o_j, added in ascending expert
+  index, rounded once to fp32 for comparison.
+
+Functions take host numpy arrays in the stored formats (see formats.py) and
+never share code with the GPU path.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from itertools import combinations
+
+import numpy as np
+
+from .formats import bf16_to_f64, dequant, f64_to_bf16_bits, f64_to_f32
+
+
+@dataclass
+class Layer:
+    """One MoE layer in the stored formats, with a count of weights read."""
+
+    router_w: np.ndarray            # fp32 [E][d]
+    router_b: np.ndarray | None     # fp32 [E] or None
+    gate_q: np.ndarray              # uint8 [E][f][d/2]
+    gate_s: np.ndarray              # uint16 [E][f][d/32]
+    up_q: np.ndarray
+    up_s: np.ndarray
+    down_q: np.ndarray              # uint8 [E][d][f/2]
+    down_s: np.ndarray              # uint16 [E][d][f/32]
+    weights_read: int = field(default=0)
+
+    @classmethod
+    def from_dict(cls, t: dict) -> "Layer":
+        return cls(t["router_w"], t.get("router_b"), t["gate_q"], t["gate_s"], t["up_q"], t["up_s"],
+                   t["down_q"], t["down_s"])
+
+    @property
+    def E(self) -> int:
+        return self.router_w.shape[0]
+
+    @property
+    def d(self) -> int:
+        return self.router_w.shape[1]
+
+    @property
+    def f(self) -> int:
+        return self.gate_q.shape[1]
+
+    def expert(self, e: int):
+        """Dequantized (W_g [f][d], W_u [f][d], W_d [d][f]) of expert e, counted as read."""
+        d, f = self.d, self.f
+        Wg = dequant(self.gate_q[e], self.gate_s[e], d)
+        Wu = dequant(self.up_q[e], self.up_s[e], d)
+        Wd = dequant(self.down_q[e], self.down_s[e], f)
+        self.weights_read += Wg.size + Wu.size + Wd.size
+        return Wg, Wu, Wd
+
+
+# ------------------------------------------------------------------ steps
+
+
+def router_logits(layer: Layer, x: np.ndarray) -> np.ndarray:
+    """l_e = sum_k W_r[e,k] x_k + b_e (fp64)."""
+    layer.weights_read += layer.router_w.size
+    l = layer.router_w.astype(np.float64) @ x
+    if layer.router_b is not None:
+        l = l + layer.router_b.astype(np.float64)
+    return l
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    z = np.exp(l - l.max())
+    return z / z.sum()
+
+
+def select_topk(p: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest p, largest first, lower index first on ties."""
+    order = sorted(range(len(p)), key=lambda e: (-p[e], e))
+    return np.array(order[:k], dtype=np.int64)
+
+
+def route(l: np.ndarray, k: int, norm_topk: bool = True):
+    """(chosen experts S, their weights w) from router logits."""
+    p = softmax(l)
+    S = select_topk(p, k)
+    w = p[S] / p[S].sum() if norm_topk else p[S]
+    return S, w
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_forward(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """SwiGLU expert: o = W_d (silu(W_g x) * (W_u x))."""
+    g = Wg @ x
+    u = Wu @ x
+    return Wd @ (silu(g) * u)
+
+
+def combine(S: np.ndarray, w: np.ndarray, outs: dict) -> np.ndarray:
+    """y = sum_j w_j o_j over the chosen experts in ascending expert index."""
+    y = np.zeros_like(next(iter(outs.values())))
+    for j in np.argsort(S, kind="stable"):
+        y = y + w[j] * outs[int(S[j])]
+    return y
+
+
+def topk_margin(l: np.ndarray, k: int) -> float:
+    """Gap between the k-th and (k+1)-th largest logit (inf when k == E)."""
+    s = np.sort(l)[::-1]
+    return float(s[k - 1] - s[k]) if k < len(s) else float("inf")
+
+
+# ------------------------------------------------------------------ layer
+
+
+def moe_forward(layer: Layer, x_bits: np.ndarray, k: int, norm_topk: bool = True) -> dict:
+    """One token through one MoE layer: only the chosen experts are evaluated."""
+    x = bf16_to_f64(x_bits)
+    l = router_logits(layer, x)
+    S, w = route(l, k, norm_topk)
+    outs = {int(e): expert_forward(*layer.expert(int(e)), x) for e in S}
+    y = combine(S, w, outs)
+    return dict(y=y, y32=f64_to_f32(y), idx=S, w=w, logits=l)
+
+
+def moe_forward_tokens(layer: Layer, X_bits: np.ndarray, k: int, norm_topk: bool = True) -> dict:
+    """T tokens, each routed on its own (row t of X is token t)."""
+    rs = [moe_forward(layer, X_bits[t], k, norm_topk) for t in range(X_bits.shape[0])]
+    return dict(y=np.stack([r["y"] for r in rs]), y32=np.stack([r["y32"] for r in rs]),
+                idx=np.stack([r["idx"] for r in rs]), w=np.stack([r["w"] for r in rs]),
+                logits=np.stack([r["logits"] for r in rs]))
+
+
+def moe_forward_masked(layer: Layer, x_bits: np.ndarray, k: int, norm_topk: bool = True) -> np.ndarray:
+    """Brute force: evaluate every expert, then keep the chosen ones by a
+    0/1 mask, y = sum_{e=0}^{E-1} (m_e w_e) o_e in ascending e."""
+    x = bf16_to_f64(x_bits)
+    l = router_logits(layer, x)
+    S, w = route(l, k, norm_topk)
+    mw = np.zeros(layer.E)
+    mw[S] = w
+    y = np.zeros(layer.d)
+    for e in range(layer.E):
+        o = expert_forward(*layer.expert(e), x)
+        y = y + mw[e] * o
+    return y
+
+
+def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk: bool = True) -> np.ndarray:
+    """Independent formulation: dequantize all experts as one tensor and
+    contract with einsum; chosen experts by a weight vector over all E."""
+    x = bf16_to_f64(x_bits)
+    l = layer.router_w.astype(np.float64) @ x + (0 if layer.router_b is None else layer.router_b.astype(np.float64))
+    p = np.exp(l - l.max())
+    p /= p.sum()
+    # k-subset with the largest total logit, ties by the lexicographically smallest set
+    chosen = np.lexsort((np.arange(layer.E), -p))[:k]
+    wv = np.zeros(layer.E)
+    wv[chosen] = p[chosen] / p[chosen].sum() if norm_topk else p[chosen]
+    Wg = dequant(layer.gate_q, layer.gate_s, layer.d)
+    Wu = dequant(layer.up_q, layer.up_s, layer.d)
+    Wd = dequant(layer.down_q, layer.down_s, layer.f)
+    G = np.einsum("efd,d->ef", Wg, x)
+    U = np.einsum("efd,d->ef", Wu, x)
+    H = G / (1.0 + np.exp(-G)) * U
+    O = np.einsum("edf,ef->ed", Wd, H)
+    return np.einsum("e,ed->d", wv, O)
+
+
+def best_subset_bruteforce(l: np.ndarray, k: int):
+    """All C(E, k) subsets: the one with the largest sum of logits."""
+    best, best_sum = None, -np.inf
+    for c in combinations(range(len(l)), k):
+        s = float(np.sum(l[list(c)]))
+        if s > best_sum:
+            best, best_sum = c, s
+    return np.array(best)
+
+
+def active_weights(E: int, d: int, f: int, k: int) -> int:
+    """Weights a sparse token reads: the router (E*d) and k experts (3*d*f each)."""
+    return E * d + k * 3 * d * f
+
+
+# ------------------------------------------------------------------ stack
+
+
+def rmsnorm_bf16(r: np.ndarray, eps: float) -> np.ndarray:
+    """x = bf16_RNE(r / sqrt(mean(r^2) + eps)), unit weight; returns bf16 bits."""
+    r = np.asarray(r, dtype=np.float64)
+    return f64_to_bf16_bits(r / np.sqrt(np.mean(r * r) + eps))
+
+
+def stack_forward(layers, x0_bits: np.ndarray, k: int, eps: float = 1e-6, norm_topk: bool = True) -> dict:
+    """Pre-norm residual stack: r_0 = x_0; for each layer x_l = RMSNorm(r_l)
+    in bf16, y_l = layer(x_l), r_{l+1} = fp32(r_l + y_l) with y_l in fp32."""
+    r = bf16_to_f64(x0_bits).astype(np.float32)
+    xs, ys, idxs = [], [], []
+    for layer in layers:
+        x = rmsnorm_bf16(r, eps)
+        out = moe_forward(layer, x, k, norm_topk)
+        xs.append(x)
+        ys.append(out["y32"])
+        idxs.append(out["idx"])
+        r = (r.astype(np.float64) + out["y32"].astype(np.float64)).astype(np.float32)
+    return dict(r=r, xs=xs, ys=ys, idx=idxs)

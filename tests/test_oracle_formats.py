@@ -1,0 +1,116 @@
+"""Pins of the oracle's number formats: textbook bit patterns, an exhaustive
+cross-check of the binary16 decoder, the stored int4 layout worked by hand,
+and the quantizer's exact round trip and error bound."""
+import numpy as np
+import pytest
+
+from conftest import golden_lines
+from oracle import formats as F
+
+
+def test_bf16_textbook_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x4049, 0x0001, 0x7F7F], np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, 3.140625, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127]
+    np.testing.assert_array_equal(F.bf16_to_f64(bits), want)
+
+
+def test_f16_textbook_patterns():
+    bits = np.array([0x3C00, 0x0001, 0x7BFF, 0x0400, 0x3555, 0xC000, 0x03FF, 0x2E66], np.uint16)
+    want = [1.0, 2.0 ** -24, 65504.0, 2.0 ** -14, 0.333251953125, -2.0, 1023 * 2.0 ** -24, 0.0999755859375]
+    np.testing.assert_array_equal(F.f16_to_f64(bits), want)
+
+
+def test_f16_decoder_matches_numpy_on_all_finite_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    finite = (bits & 0x7C00) != 0x7C00
+    ours = F.f16_to_f64(bits[finite])
+    ref = bits[finite].view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_f16_encoder_round_trips_every_finite_value():
+    bits = np.arange(65536, dtype=np.uint16)
+    bits = bits[(bits & 0x7C00) != 0x7C00]
+    back = F.f64_to_f16_bits(F.f16_to_f64(bits))
+    # -0.0 and +0.0 keep their sign bit
+    np.testing.assert_array_equal(back, bits)
+
+
+def test_f16_encoder_ties_to_even():
+    one_ulp = 2.0 ** -10
+    assert F.f64_to_f16_bits(1.0 + one_ulp / 2) == 0x3C00          # tie -> even (1.0)
+    assert F.f64_to_f16_bits(1.0 + 3 * one_ulp / 2) == 0x3C02      # tie -> even (1 + 2 ulp)
+    assert F.f64_to_f16_bits(2.0 ** -25) == 0x0000                 # half the smallest subnormal -> 0
+    assert F.f64_to_f16_bits(3 * 2.0 ** -25) == 0x0002
+
+
+def test_bf16_encoder_rounding():
+    assert F.f64_to_bf16_bits(1.0) == 0x3F80
+    assert F.f64_to_bf16_bits(1.0 + 2.0 ** -8) == 0x3F80           # tie -> even
+    assert F.f64_to_bf16_bits(1.0 + 3 * 2.0 ** -8) == 0x3F82       # tie -> even
+    assert F.f64_to_bf16_bits(1.0 + 2.0 ** -8 + 2.0 ** -30) == 0x3F81
+    assert F.f64_to_bf16_bits(-3.140625) == 0xC049
+    x = np.random.default_rng(0).standard_normal(10000)
+    b = F.f64_to_bf16_bits(x)
+    err = np.abs(F.bf16_to_f64(b) - x)
+    assert np.all(err <= np.abs(x) * 2.0 ** -8 * (1 + 1e-12))
+
+
+@pytest.mark.parametrize("pattern", ["A", "B"])
+def test_int4_layout_hand_worked(pattern):
+    rows = {ln[0]: bytes(int(h, 16) for h in ln[1:]) for ln in golden_lines("int4_layout_k128.txt")}
+    k = np.arange(128)
+    u = (k // 8) % 16 if pattern == "A" else k % 8 + 8 * (k // 64)
+    packed = F.pack_codes(u[None, :])[0]
+    assert packed.tobytes() == rows[pattern]
+    np.testing.assert_array_equal(F.unpack_codes(np.frombuffer(rows[pattern], np.uint8)[None], 128)[0], u)
+
+
+def test_int4_positions_are_a_bijection():
+    for K in (128, 256, 2048):
+        byte, shift = F.int4_positions(K)
+        slots = byte * 2 + shift // 4
+        assert sorted(slots.tolist()) == list(range(K))
+
+
+def test_quantize_hand_worked_group():
+    lines = {ln[0]: ln[1:] for ln in golden_lines("quantize_group.txt")}
+    w = np.array([float(v) for v in lines["w"]], np.float32)
+    u, s = F.quantize(w[None, :])
+    assert int(s[0, 0]) == int(lines["scale_bits"][0], 16)
+    np.testing.assert_array_equal(u[0], [int(v) for v in lines["u"]])
+
+
+def test_quantize_round_trip_exact():
+    """quantize(dequant(q, s)) == (q, s) when max|q| = 7 and s is a positive
+    normal binary16: q*s is exact, a = 7s, a/7 = s, so s and q come back."""
+    rng = np.random.default_rng(1)
+    R, K = 64, 256
+    q = rng.integers(-7, 8, size=(R, K))
+    q[:, ::32] = np.where(rng.random((R, K // 32)) < 0.5, 7, -7)  # every group reaches |q| = 7
+    sbits = rng.integers(0x0400, 0x7800, size=(R, K // 32)).astype(np.uint16)  # normal, below 7*s overflow
+    w = (q * np.repeat(F.f16_to_f64(sbits), 32, axis=1)).astype(np.float32)
+    assert np.all(w.astype(np.float64) == q * np.repeat(F.f16_to_f64(sbits), 32, axis=1))
+    u2, s2 = F.quantize(w)
+    np.testing.assert_array_equal(s2, sbits)
+    np.testing.assert_array_equal(u2 - 8, q)
+    # and the packed form decodes back to the same weights
+    np.testing.assert_array_equal(F.dequant(F.pack_codes(u2), s2, K), w.astype(np.float64))
+
+
+def test_quantize_error_bound():
+    """|w - deq(quant(w))| <= s/2 per element (s the group's stored scale),
+    and the scale is within a binary16 rounding of max|w|/7."""
+    rng = np.random.default_rng(2)
+    w = (rng.standard_normal((128, 512)) * 0.02).astype(np.float32)
+    u, s = F.quantize(w)
+    deq = F.dequant(F.pack_codes(u), s, 512)
+    sv = np.repeat(F.f16_to_f64(s), 32, axis=1)
+    assert np.all(np.abs(w - deq) <= sv / 2 * (1 + 1e-12))
+    a = np.abs(w.reshape(128, 16, 32)).max(-1).astype(np.float64)
+    assert np.all(np.abs(F.f16_to_f64(s) - a / 7) <= a / 7 * 2.0 ** -11)
+
+
+def test_quantize_zero_group():
+    u, s = F.quantize(np.zeros((2, 128), np.float32))
+    assert np.all(s == 0) and np.all(u == 8)

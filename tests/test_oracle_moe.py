@@ -1,0 +1,206 @@
+"""Pins of the MoE-layer oracle: closed forms, brute force over tiny inputs,
+a hand-worked single-expert case and invariants.  None of these compute the
+expected value with the function under test."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from conftest import golden_lines
+from oracle import formats as F
+from oracle import moe as M
+
+
+def tiny_layer(seed=1):
+    return M.Layer.from_dict(synth.make_layer(synth.TINY, seed))
+
+
+def tiny_x(layer, seed=1, token=0):
+    from oracle.inputs import pick_token
+    x, _ = pick_token(layer, synth.TINY.k, synth.TINY.margin,
+                      lambda a: synth.draw_x(synth.TINY, seed, 0, token, a))
+    return x
+
+
+def test_router_one_hot_column():
+    L = tiny_layer()
+    for k0 in (0, 7, 255):
+        x = np.zeros(L.d)
+        x[k0] = 1.0
+        np.testing.assert_array_equal(M.router_logits(L, x), L.router_w[:, k0].astype(np.float64))
+
+
+def test_router_integer_exact():
+    rng = np.random.default_rng(3)
+    E, d = 16, 256
+    W = rng.integers(-50, 51, size=(E, d)).astype(np.float32)
+    xi = rng.integers(-8, 9, size=d)
+    b = rng.integers(-5, 6, size=E).astype(np.float32)
+    L = M.Layer(W, b, *[None] * 6)
+    want = [sum(int(W[e, k]) * int(xi[k]) for k in range(d)) + int(b[e]) for e in range(E)]
+    np.testing.assert_array_equal(M.router_logits(L, xi.astype(np.float64)), want)
+
+
+def test_topk_equals_best_subset_bruteforce():
+    for seed in range(1, 6):
+        L = tiny_layer(seed)
+        x = F.bf16_to_f64(tiny_x(L, seed))
+        l = M.router_logits(L, x)
+        S, w = M.route(l, 2)
+        assert sorted(S.tolist()) == sorted(M.best_subset_bruteforce(l, 2).tolist())
+        assert math.isclose(w.sum(), 1.0, rel_tol=1e-15)
+        assert w[0] >= w[1]
+
+
+def test_topk_tie_lower_index_first():
+    p = np.array([0.1, 0.3, 0.3, 0.3])
+    assert M.select_topk(p, 1).tolist() == [1]
+    assert M.select_topk(p, 2).tolist() == [1, 2]
+    assert M.select_topk(p, 4).tolist() == [1, 2, 3, 0]
+
+
+def test_softmax_shift_invariance_and_closed_form():
+    l = np.array([0.0, math.log(2.0), math.log(5.0)])
+    np.testing.assert_allclose(M.softmax(l), [1 / 8, 2 / 8, 5 / 8], rtol=1e-15)
+    np.testing.assert_allclose(M.softmax(l + 123.0), [1 / 8, 2 / 8, 5 / 8], rtol=1e-14)
+
+
+def test_norm_topk_off_keeps_softmax_values():
+    l = np.array([0.0, math.log(2.0), math.log(5.0)])
+    S, w = M.route(l, 2, norm_topk=False)
+    assert S.tolist() == [2, 1]
+    np.testing.assert_allclose(w, [5 / 8, 2 / 8], rtol=1e-15)
+    S, w = M.route(l, 2, norm_topk=True)
+    np.testing.assert_allclose(w, [5 / 7, 2 / 7], rtol=1e-15)
+
+
+def test_margin_values():
+    l = np.array([0.5, 0.2, 0.9, 0.25])
+    assert math.isclose(M.topk_margin(l, 1), 0.4)
+    assert math.isclose(M.topk_margin(l, 2), 0.25)
+    assert math.isclose(M.topk_margin(l, 3), 0.05)
+    assert M.topk_margin(l, 4) == float("inf")
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_sparse_equals_all_experts_then_mask_bit_exact(seed):
+    L = tiny_layer(seed)
+    x = tiny_x(L, seed)
+    y_sparse = M.moe_forward(L, x, 2)["y"]
+    y_masked = M.moe_forward_masked(L, x, 2)
+    assert np.array_equal(y_sparse, y_masked)
+
+
+@pytest.mark.parametrize("norm", [True, False])
+def test_sparse_matches_independent_dense_einsum(norm):
+    L = tiny_layer(4)
+    x = tiny_x(L, 4)
+    y = M.moe_forward(L, x, 2, norm)["y"]
+    y2 = M.moe_forward_dense_einsum(L, x, 2, norm)
+    np.testing.assert_allclose(y, y2, rtol=0, atol=1e-13 * np.abs(y2).max())
+
+
+def test_active_weight_count():
+    L = tiny_layer()
+    x = tiny_x(L)
+    L.weights_read = 0
+    M.moe_forward(L, x, 2)
+    E, d, f, k = 16, 256, 128, 2
+    assert L.weights_read == E * d + k * 3 * d * f == M.active_weights(E, d, f, k)
+    L.weights_read = 0
+    M.moe_forward_masked(L, x, 2)
+    assert L.weights_read == E * d + E * 3 * d * f
+    # the flagship layer shape: 256 experts, top-8, d=2048, f=512
+    assert M.active_weights(256, 2048, 512, 8) == 524288 + 25165824
+
+
+def test_all_experts_selected_is_the_softmax_mixture():
+    L = tiny_layer(5)
+    x = tiny_x(L, 5)
+    out = M.moe_forward(L, x, 16)
+    p = np.exp(out["logits"] - out["logits"].max())
+    p /= p.sum()
+    np.testing.assert_allclose(out["w"], p[out["idx"]], rtol=1e-14)
+    xs = F.bf16_to_f64(x)
+    y = sum(p[e] * M.expert_forward(*L.expert(e), xs) for e in range(16))
+    np.testing.assert_allclose(out["y"], y, rtol=0, atol=1e-14 * np.abs(y).max())
+
+
+def _single_expert_layer():
+    g = {ln[0]: ln[1:] for ln in golden_lines("swiglu_single_expert.txt")}
+    d = f = 128
+    k0 = int(g["k0"][0])
+    ug = np.full((f, d), 8)
+    uu = np.full((f, d), 8)
+    i = np.arange(f)
+    ug[:, k0] = 8 + np.where(i % 3 == 0, 1, np.where(i % 3 == 1, -1, 0))
+    uu[:, k0] = 8 + np.where(i < 64, 1, -1)
+    ud = np.full((d, f), 8)
+    ud[np.arange(d), np.arange(d)] = 9
+    one = np.full((f, d // 32), 0x3C00, np.uint16)
+    L = M.Layer(np.ones((1, d), np.float32), None,
+                F.pack_codes(ug)[None], one[None], F.pack_codes(uu)[None], one[None],
+                F.pack_codes(ud)[None], np.full((d, f // 32), 0x3C00, np.uint16)[None])
+    x = np.zeros(d, np.uint16)
+    x[k0] = 0x3F80
+    return L, x, g, i
+
+
+def test_single_expert_is_plain_swiglu_mlp_hand_worked():
+    L, x, g, i = _single_expert_layer()
+    sp, sm = float(g["silu_plus1"][0]), float(g["silu_minus1"][0])
+    want = np.where(i % 3 == 0, sp, np.where(i % 3 == 1, sm, 0.0)) * np.where(i < 64, 1.0, -1.0)
+    out = M.moe_forward(L, x, 1)
+    assert out["idx"].tolist() == [0] and out["w"].tolist() == [1.0]
+    np.testing.assert_allclose(out["y"], want, rtol=1e-15, atol=0)
+
+
+def test_scale_linearity_exact():
+    """Doubling every down (or every up) scale doubles y exactly: binary16
+    scales times 2 are exact, and so is every product and sum scaled by 2."""
+    L = tiny_layer(6)
+    x = tiny_x(L, 6)
+    y = M.moe_forward(L, x, 2)["y"]
+    for name in ("down_s", "up_s"):
+        L2 = tiny_layer(6)
+        s = getattr(L2, name)
+        setattr(L2, name, F.f64_to_f16_bits(F.f16_to_f64(s) * 2))
+        assert np.array_equal(M.moe_forward(L2, x, 2)["y"], 2 * y)
+
+
+def test_expert_permutation_equivariance():
+    L = tiny_layer(7)
+    x = tiny_x(L, 7)
+    out = M.moe_forward(L, x, 2)
+    perm = np.random.default_rng(7).permutation(16)
+    Lp = M.Layer(L.router_w[perm], None, L.gate_q[perm], L.gate_s[perm], L.up_q[perm], L.up_s[perm],
+                 L.down_q[perm], L.down_s[perm])
+    outp = M.moe_forward(Lp, x, 2)
+    assert sorted(perm[outp["idx"]].tolist()) == sorted(out["idx"].tolist())
+    np.testing.assert_allclose(outp["y"], out["y"], rtol=0, atol=1e-15 * np.abs(out["y"]).max())
+
+
+def test_rmsnorm_closed_forms():
+    eps = 1e-6
+    for c in (0.5, -3.0, 1e-3):
+        x = M.rmsnorm_bf16(np.full(64, c), eps)
+        assert np.all(x == F.f64_to_bf16_bits(c / math.sqrt(c * c + eps)))
+    r = np.random.default_rng(8).standard_normal(2048) * 3
+    xh = r / np.sqrt(np.mean(r * r) + eps)
+    m = np.mean(r * r)
+    assert math.isclose(np.mean(xh * xh), m / (m + eps), rel_tol=1e-12)
+    got = F.bf16_to_f64(M.rmsnorm_bf16(r, eps))
+    assert np.all(np.abs(got - xh) <= np.abs(xh) * 2.0 ** -8)
+
+
+def test_stack_of_zero_experts_keeps_the_residual():
+    """Layers whose expert scales are all zero output y = 0, so the residual
+    stream is unchanged through the whole stack."""
+    L = tiny_layer(9)
+    Z = M.Layer(L.router_w, None, L.gate_q, np.zeros_like(L.gate_s), L.up_q, L.up_s,
+                L.down_q, np.zeros_like(L.down_s))
+    x0 = synth.draw_x(synth.TINY, 9, 0, 0, 0)
+    out = M.stack_forward([Z, Z, Z], x0, 2)
+    np.testing.assert_array_equal(out["r"], F.bf16_to_f64(x0).astype(np.float32))
+    assert all(np.all(y == 0) for y in out["ys"])
