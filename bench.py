@@ -1,0 +1,276 @@
+"""Benchmark: MoE-layer decode tokens/s at 1 token + achieved HBM GB/s.
+
+Workload (one step = one token through one MoE layer: router GEMV, softmax
+and top-k, int4 gate/up GEMVs over the 8 chosen experts, SwiGLU, int4 down
+GEMV and weighted combine): d=2048, f=512, E=256, top-8, int4 weights with
+one fp16 scale per 32, bf16 activations.  The pages give no layer shapes;
+these reproduce their totals (256 routed experts per layer, 40B total, 2.5B
+active, "Flint 40B: Best Mid Sized LLM", transcript 02:35).
+
+So that the 256 MB memory-side cache cannot serve repeats, step i runs layer
+i mod P of a pool of P = 49 independent seeded layers (22.3 GB of weights,
+the 49-layer stack's layers) with a fresh activation: every step reads its
+router and chosen experts from HBM.  Steps run in stream order, replayed as
+one HIP graph (the eager number is reported beside it).
+
+Also reported (not the headline): the 49-layer stack per-token time, the
+LM head (V=131072, d=2048) at B=1 and B=8, and the plain fp64 CPU oracle
+timed on a bounded sample of the same workload.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(d, f, E, k):
+    """Algorithmic bytes of one 1-token layer step: router weights, x, the k
+    chosen experts' int4 nibbles + fp16 scales (each read once), y."""
+    nib = k * (2 * f * d // 2 + d * f // 2)
+    scales = k * (2 * f * (d // 32) * 2 + d * (f // 32) * 2)
+    router = E * d * 4
+    return dict(b_nib=nib, b_q=nib + scales, b_alg=nib + scales + router + d * 2 + d * 4)
+
+
+def lmhead_bytes(V, d, B):
+    return V * d // 2 + V * (d // 32) * 2 + B * d * 2 + B * 8
+
+
+def time_graph(fn, steps, warmup, stream):
+    """Capture `fn(i)` for i in range(steps) into one graph; return seconds per replay."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for i in range(min(warmup, steps)):
+            fn(i)
+    stream.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            fn(i)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    reps = 3
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps, g
+
+
+def time_eager(fn, steps, warmup, stream):
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
+        stream.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            fn(i)
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def cpu_baseline(pool_np, xs_np, cfg, budget_s):
+    """The fp64 oracle as it stands, on a bounded sample of the same steps."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe as OM
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        li = n % len(pool_np)
+        OM.moe_forward(OM.Layer.from_dict(pool_np[li]), xs_np[li][n % len(xs_np[li])], cfg.k)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return dict(value=n / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{n} single-token layer steps over {min(n, len(pool_np))} layers of the pool, "
+                       f"{dt:.1f} s, numpy fp64 (BLAS threads {threads})")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=490)
+    ap.add_argument("--warmup", type=int, default=49)
+    ap.add_argument("--pool", type=int, default=49, help="distinct layers rotated through")
+    ap.add_argument("--tokens", type=int, default=16, help="distinct activations per layer")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip stack, LM head and CPU legs")
+    ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_moe_decode_gemv_amd as M
+
+    M.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.LAYER
+    d, f, E, k = cfg.d, cfg.f, cfg.E, cfg.k
+    P = args.pool
+
+    t0 = time.time()
+    layers, pool_np, xs_np = [], [], []
+    keep_host = 2  # host copies kept for the CPU leg
+    for l in range(P):
+        lay = synth.make_layer(cfg, args.seed, l)
+        layers.append(M.MoELayer.create(M.upload(lay, dev), d, f, E, k, 1, 1))
+        xs = np.stack([synth.draw_x(synth.STACK, args.seed, l, t, 0) for t in range(args.tokens)])
+        xs_np.append(xs)
+        if l < keep_host:
+            pool_np.append(lay)
+        del lay
+    X = torch.from_numpy(np.stack(xs_np).view(np.int16)).to(dev)  # [P][tokens][d]
+    torch.cuda.synchronize()
+    log(f"pool of {P} layers generated and uploaded in {time.time() - t0:.1f} s")
+
+    y = torch.empty((1, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        l = i % P
+        t = (i // P) % args.tokens
+        M.moe_decode_forward(layers[l].handle, X[l, t:t + 1], 1, y, None, None, stream)
+
+    K, W = args.steps, args.warmup
+    eager_s = time_eager(step, K, W, stream)
+    graph_s = None
+    try:
+        graph_s, _g = time_graph(step, K, W, stream)
+        del _g
+    except Exception as e:  # graph capture unavailable: report eager only
+        log(f"graph capture failed: {e!r}")
+    total_s = eager_s if (args.eager or graph_s is None) else graph_s
+    ms_per_step = total_s / K * 1e3
+    value = K / total_s
+
+    by = layer_bytes(d, f, E, k)
+    step_us = ms_per_step * 1e3
+    achieved = by["b_alg"] / (step_us * 1e-6) / 1e9
+    out = {
+        "metric": "MoE-layer decode tokens/s at 1 token + achieved HBM GB/s (% of peak)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4-bf16-f32",
+        "data": "synthetic (seeded N(0,0.02) int4 g32 fp16-scale experts, fp32 router, bf16 N(0,1) x)",
+        "config": {"workload": "1-token MoE layer decode, d=2048 f=512 E=256 top-8, "
+                               f"rotating over {P} distinct layers, fresh x per step",
+                   "d": d, "f": f, "experts": E, "top_k": k, "tokens_per_step": 1, "pool_layers": P,
+                   "launch": "eager" if total_s == eager_s else "hip-graph"},
+        "roofline": {"bound": "hbm", "kernel": "moe layer step (router, gate/up, down kernels)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": by["b_alg"]},
+        "bytes_per_step": by,
+        "gbs_on_int4_weights": round(by["b_q"] / (step_us * 1e-6) / 1e9, 1),
+        "frac_on_int4_weights": round(by["b_q"] / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "eager_ms_per_step": round(eager_s / K * 1e3, 6),
+        "graph_ms_per_step": round(graph_s / K * 1e3, 6) if graph_s else None,
+    }
+
+    if not args.no_extras:
+        # 49-layer stack, 1 token: per-token time (in-stack layer time = / P)
+        # r_0 = fp32 of a bf16 N(0,1) activation, as in the stack's definition
+        x0 = synth.draw_x(synth.STACK, args.seed, 0, 0, 0)
+        base = torch.from_numpy(x0.view(np.int16)[None]).view(torch.bfloat16).float().to(dev)
+        resid = torch.empty((1, d), dtype=torch.float32, device=dev)
+        handles = [L.handle for L in layers]
+
+        def stack_step(i):
+            resid.copy_(base)
+            M.moe_decode_stack_forward(handles, resid, 1, 1e-6, None, None, None, stream)
+
+        st_s = time_eager(stack_step, 10, 2, stream) / 10
+        try:
+            gs, _g = time_graph(stack_step, 10, 2, stream)
+            st_s = gs / 10
+            del _g
+        except Exception as e:
+            log(f"stack graph failed: {e!r}")
+        out["stack"] = {"layers": P, "ms_per_token": round(st_s * 1e3, 4),
+                        "tokens_per_s": round(1 / st_s, 1),
+                        "in_stack_layer_us": round(st_s / P * 1e6, 3),
+                        "achieved_gbs": round(P * by["b_alg"] / st_s / 1e9, 1)}
+
+        # LM head: rotate over 4 copies
+        V = synth.LMHEAD1.V
+        heads = []
+        for c in range(4):
+            q, s = synth.make_lmhead(synth.LMHEAD1, args.seed, c)
+            heads.append((torch.from_numpy(q).to(dev), torch.from_numpy(s.view(np.int16)).to(dev)))
+        del q, s
+        for B in (1, 8):
+            xb = torch.from_numpy(
+                np.stack([synth.draw_hidden(synth.LMHEAD8, args.seed, b, 0) for b in range(B)]).view(np.int16)).to(dev)
+            tok = torch.empty(B, dtype=torch.int32, device=dev)
+            ml = torch.empty(B, dtype=torch.float32, device=dev)
+            wsz = M.lmhead_int4_argmax_workspace_bytes(V, d, B)
+            wsp = torch.zeros(wsz, dtype=torch.uint8, device=dev)
+
+            def lm_step(i, B=B, xb=xb, tok=tok, ml=ml, wsp=wsp):
+                wq, wsc = heads[i % 4]
+                M.lmhead_int4_argmax(wq, wsc, V, d, xb, B, tok, ml, wsp, wsz, stream)
+
+            n = 40
+            try:
+                ls, _g = time_graph(lm_step, n, 4, stream)
+                del _g
+            except Exception as e:
+                log(f"lmhead graph failed: {e!r}")
+                ls = time_eager(lm_step, n, 4, stream)
+            us = ls / n * 1e6
+            gbs = lmhead_bytes(V, d, B) / (us * 1e-6) / 1e9
+            out[f"lmhead_b{B}"] = {"us_per_call": round(us, 3), "rows_per_s": round(B / (us * 1e-6), 1),
+                                   "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del heads
+
+        out["cpu_baseline"] = cpu_baseline(pool_np, xs_np, cfg, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * moe_decode.h -- C ABI of the sparse MoE decode library for MI355X (gfx950).
+ *
+ * One decode step of a 4-bit mixture-of-experts layer (router GEMV, softmax
+ * and top-k expert choice, int4 gate/up GEMVs over the chosen experts only,
+ * SwiGLU, int4 down GEMV, weighted combine), a pre-norm stack of such layers,
+ * and the 4-bit output layer (LM head) GEMV with a fused argmax.
+ *
+ * The pages describe the model these calls serve: every MoE layer holds 256
+ * routed experts of which a small router picks a few per token, and the
+ * output layer, about an eighth of the per-token work, is stored in 4 bits
+ * ("Flint 40B: Best Mid Sized LLM", transcript 02:35-05:39).  The unit of
+ * work follows their statement of the problem, decode speed in tokens per
+ * second: one call advances T tokens through one layer, or B hidden rows
+ * through the LM head.
+ *
+ * Conventions for every call:
+ *   - Pointers marked (device) point to GPU memory that the caller allocated
+ *     and owns; the library never allocates, frees or copies device memory
+ *     except the one-time workspace clear in moe_decode_init.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued on it and the call returns without waiting.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and no output is touched.  Faults inside a
+ *     kernel surface at the caller's next synchronization.
+ *   - No C++ exception crosses this interface.
+ *
+ * Stored int4 weight format (all int4 matrices: experts and LM head):
+ *   A matrix [rows][K] (K a power of two, >= 128) takes K/2 bytes per row,
+ *   rows one after another.  Element k of a row is held in byte
+ *   64*t + 16*q + 4*j + e/2 of the row, with t = k/128, j = (k%128)/32,
+ *   q = (k%32)/8, e = k%8; the low nibble for even e, the high nibble for
+ *   odd e.  The nibble is a code u in 0..15 and the weight is
+ *   (u - 8) * scale[row][k/32], scale an IEEE binary16 bit pattern stored
+ *   row-major [rows][K/32].  (Each 16-byte piece of a row thus holds 8
+ *   elements of each of 4 consecutive groups of 32.)
+ *   The pages say the model ships "integer four" builds and a 4-bit output
+ *   layer but give no group size or layout; this format is the library's.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define MOE_ERR_ALIGN (-3)       /* a device pointer is not 16-byte aligned */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
+#define MOE_ERR_HIP (-5)         /* the HIP runtime refused a launch or copy */
+#define MOE_ERR_UNSUPPORTED (-6) /* a shape the kernels are not built for */
+
+#define MOE_MAX_TOPK 16          /* largest top_k */
+#define MOE_MAX_TOKENS 256       /* largest T per forward call */
+#define MOE_LMHEAD_MAX_B 16      /* largest B per LM-head call */
+
+/* Shape of one MoE layer.
+ *   d          hidden width, a power of two in [256, 8192]
+ *   f          expert FFN width, a power of two in [128, 4096]
+ *   n_experts  E, routed experts, in [1, 1024]
+ *   top_k      k, experts chosen per token, in [1, min(E, MOE_MAX_TOPK)]
+ *   norm_topk  1: the chosen softmax weights are divided by their sum;
+ *              0: they are used as they are
+ *   max_tokens largest T a forward call will pass, in [1, MOE_MAX_TOKENS] */
+typedef struct {
+  int32_t d, f, n_experts, top_k, norm_topk, max_tokens;
+} moe_layer_desc;
+
+/* Weights of one MoE layer (device, read-only, owned by the caller, must
+ * outlive the handle; every pointer 16-byte aligned).
+ *   router_w  fp32 [E][d] row-major
+ *   router_b  fp32 [E], or NULL for no bias
+ *   gate_q    int4 [E][f][d/2] stored format, gate_s binary16 [E][f][d/32]
+ *   up_q      int4 [E][f][d/2],                up_s   binary16 [E][f][d/32]
+ *   down_q    int4 [E][d][f/2],                down_s binary16 [E][d][f/32] */
+typedef struct {
+  const float* router_w;
+  const float* router_b;
+  const uint8_t* gate_q;
+  const uint16_t* gate_s;
+  const uint8_t* up_q;
+  const uint16_t* up_s;
+  const uint8_t* down_q;
+  const uint16_t* down_s;
+} moe_layer_weights;
+
+typedef struct moe_layer* moe_handle;
+
+/* Bytes of device workspace a layer with this shape needs (0 on a bad
+ * shape).  The workspace holds router logits, arrival counters, the chosen
+ * experts and the SwiGLU activations of one call. */
+size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
+
+/* Validate the shape and weights and bind them, with a caller-owned device
+ * workspace of at least moe_decode_workspace_bytes(desc) bytes, into a host
+ * handle.  Clears the workspace once (synchronously, on the null stream).
+ * The handle owns no device memory.  One handle must not run on two streams
+ * at once (its workspace is shared by its calls); distinct handles are
+ * independent. */
+moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                           void* workspace, size_t workspace_bytes, moe_handle* out);
+
+/* One decode step of T tokens through the layer ("a small router selects
+ * [some] of them per token", transcript 02:35):
+ *   logits = W_r x_t + b;  p = softmax(logits) over all E experts;
+ *   S = the k largest p (larger first, lower expert index on ties);
+ *   w_j = p_j / sum_{i in S} p_i (norm_topk) or p_j;
+ *   y_t = sum_{j in S} w_j * W_d[j] (silu(W_g[j] x_t) * (W_u[j] x_t)).
+ * Only the chosen experts' weights are read.
+ *   x         (device) bf16 bit patterns [T][d]
+ *   T         tokens, 1 <= T <= max_tokens
+ *   y         (device) fp32 [T][d], overwritten
+ *   topk_idx  (device) int32 [T][k], chosen experts in the order above, or NULL
+ *   topk_w    (device) fp32 [T][k], their weights, or NULL */
+moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float* y,
+                              int32_t* topk_idx, float* topk_w, void* stream);
+
+/* L layers in sequence on a residual stream, each pre-normed by an RMSNorm
+ * of unit weight (the attention blocks between MoE layers are not part of
+ * this call):
+ *   x_l = bf16_rne(r_l / sqrt(mean(r_l^2) + eps));  r_{l+1} = r_l + layer_l(x_l).
+ *   layers    L handles of equal d and top_k, each with its own workspace
+ *   residual  (device) fp32 [T][d], r_0 in, r_L out
+ *   x_trace   (device) bf16 [L][T][d] receiving every x_l, or NULL
+ *   y_trace   (device) fp32 [L][T][d] receiving every layer output, or NULL
+ *   idx_trace (device) int32 [L][T][k] receiving every chosen set, or NULL */
+moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* residual, int32_t T,
+                                    float eps, uint16_t* x_trace, float* y_trace, int32_t* idx_trace,
+                                    void* stream);
+
+/* Free the host handle (no device memory is touched). NULL is ignored. */
+void moe_decode_destroy(moe_handle h);
+
+/* Bytes of device workspace lmhead_int4_argmax needs for this shape (0 on a
+ * bad shape). */
+size_t lmhead_int4_argmax_workspace_bytes(int32_t V, int32_t d, int32_t B);
+
+/* 4-bit output layer with greedy decoding ("Flint 40B: Best Mid Sized LLM",
+ * transcript 03:36-05:39; mirrorspeed.com page, section "Quantization"):
+ *   z[b][v] = sum_k W[v][k] x[b][k];  token[b] = the smallest v with the
+ *   largest z[b][v];  max_logit[b] = that z (fp32).
+ * The logits are never written to memory.
+ *   w_q, w_s  (device) int4 [V][d/2] stored format and binary16 [V][d/32]
+ *   V         vocabulary rows, 1 <= V <= 2^24
+ *   d         hidden width, a power of two in [256, 8192]
+ *   x         (device) bf16 [B][d]
+ *   B         rows, 1 <= B <= MOE_LMHEAD_MAX_B
+ *   token     (device) int32 [B]
+ *   max_logit (device) fp32 [B], or NULL
+ *   workspace (device) at least lmhead_int4_argmax_workspace_bytes(V, d, B)
+ *             bytes, zero-filled before its first use; every call leaves it
+ *             zero-filled again.  Calls sharing a workspace must not overlap. */
+moe_status lmhead_int4_argmax(const uint8_t* w_q, const uint16_t* w_s, int32_t V, int32_t d,
+                              const uint16_t* x, int32_t B, int32_t* token, float* max_logit,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for a status code (static storage). */
+const char* moe_status_str(moe_status s);
+
+/* Version of this interface (incremented on incompatible changes). */
+int32_t moe_decode_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

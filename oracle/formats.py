@@ -80,10 +80,10 @@ def int4_positions(K: int):
 
 
 def unpack_codes(qbytes: np.ndarray, K: int) -> np.ndarray:
-    """Stored bytes [..., K/2] -> codes u [..., K] in 0..15."""
+    """Stored bytes [..., K/2] -> codes u [..., K] in 0..15 (uint8)."""
     byte, shift = int4_positions(K)
     b = np.asarray(qbytes, dtype=np.uint8)[..., byte]
-    return ((b >> shift.astype(np.uint8)) & 0xF).astype(np.int64)
+    return (b >> shift.astype(np.uint8)) & np.uint8(0xF)
 
 
 def pack_codes(u: np.ndarray) -> np.ndarray:
@@ -99,9 +99,9 @@ def pack_codes(u: np.ndarray) -> np.ndarray:
 
 def dequant(qbytes: np.ndarray, sbits: np.ndarray, K: int) -> np.ndarray:
     """Stored int4 matrix -> fp64 weights [..., K]: w = (u - 8) * s[k // 32]."""
-    u = unpack_codes(qbytes, K)
+    q = unpack_codes(qbytes, K).astype(np.int8) - np.int8(8)
     s = f16_to_f64(sbits)
-    return (u - 8).astype(np.float64) * np.repeat(s, 32, axis=-1)
+    return (q.reshape(q.shape[:-1] + (K // 32, 32)) * s[..., None]).reshape(q.shape)
 
 
 def quantize(w: np.ndarray):

@@ -30,8 +30,24 @@ def pick_token(layer: Layer, k: int, margin: float, draw, max_attempts: int = 10
 
 
 def pick_hidden(w_q: np.ndarray, w_s: np.ndarray, margin: float, draw, max_attempts: int = 100):
+    """One row: first attempt whose top-1/top-2 logit gap is >= margin."""
+    X, A = pick_hidden_rows(w_q, w_s, margin, lambda b, a: draw(a), 1, max_attempts)
+    return X[0], A[0]
+
+
+def pick_hidden_rows(w_q: np.ndarray, w_s: np.ndarray, margin: float, draw, B: int, max_attempts: int = 100):
+    """B rows, row b drawn as draw(b, attempt) until its gap holds; all
+    pending rows are scored together, one pass over the matrix per round."""
+    X = [None] * B
+    A = [0] * B
+    pending = list(range(B))
     for a in range(max_attempts):
-        x = draw(a)
-        if top2_gap(lmhead_logits(w_q, w_s, x))[0] >= margin:
-            return x, a
+        cand = np.stack([draw(b, a) for b in pending])
+        gaps = top2_gap(lmhead_logits(w_q, w_s, cand))
+        for b, x, g in zip(list(pending), cand, gaps):
+            if g >= margin:
+                X[b], A[b] = x, a
+                pending.remove(b)
+        if not pending:
+            return np.stack(X), A
     raise RuntimeError("no draw met the gap")

@@ -1,0 +1,188 @@
+// api.hip -- the C ABI (include/moe_decode.h): validation, workspace layout
+// and kernel dispatch.  All checks run on the host before anything is
+// enqueued; no C++ exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/moe_decode.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+struct Layout {
+  size_t counters, logits, sel_idx, sel_w, h, xnorm, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+moe_status check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->d < 1 || d->f < 1 || d->n_experts < 1 || d->top_k < 1 || d->max_tokens < 1) return MOE_ERR_SHAPE;
+  if (d->top_k > d->n_experts || d->top_k > MOE_MAX_TOPK) return MOE_ERR_SHAPE;
+  if (d->max_tokens > MOE_MAX_TOKENS || d->n_experts > 1024) return MOE_ERR_SHAPE;
+  if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_ERR_SHAPE;
+  if (d->d % 32 || d->f % 32) return MOE_ERR_SHAPE;
+  if (!is_pow2(d->d) || d->d < 256 || d->d > 8192) return MOE_ERR_UNSUPPORTED;
+  if (!is_pow2(d->f) || d->f < 128 || d->f > 4096) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Layout layout_of(const moe_layer_desc* d) {
+  Layout L;
+  const size_t T = (size_t)d->max_tokens, E = (size_t)d->n_experts, k = (size_t)d->top_k;
+  size_t o = 0;
+  L.counters = o, o += align256(T * sizeof(unsigned));
+  L.logits = o, o += align256(T * E * sizeof(float));
+  L.sel_idx = o, o += align256(T * k * sizeof(int32_t));
+  L.sel_w = o, o += align256(T * k * sizeof(float));
+  L.h = o, o += align256(T * k * (size_t)d->f * sizeof(float));
+  L.xnorm = o, o += align256(T * (size_t)d->d * sizeof(uint16_t));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+struct moe_layer {
+  moe_layer_desc desc;
+  moe::LayerArgs args;
+  void* workspace;
+};
+
+extern "C" {
+
+int32_t moe_decode_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_ALIGN: return "a device pointer is not suitably aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "the HIP runtime reported an error";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_decode_workspace_bytes(const moe_layer_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return layout_of(desc).total;
+}
+
+moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* w, void* workspace,
+                           size_t workspace_bytes, moe_handle* out) {
+  if (!out) return MOE_ERR_NULL;
+  *out = nullptr;
+  const moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!w || !w->router_w || !w->gate_q || !w->gate_s || !w->up_q || !w->up_s || !w->down_q || !w->down_s)
+    return MOE_ERR_NULL;
+  const void* ptrs[] = {w->router_w, w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (w->router_b && !aligned4(w->router_b)) return MOE_ERR_ALIGN;
+  const Layout L = layout_of(desc);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
+
+  moe_layer* h = new (std::nothrow) moe_layer;
+  if (!h) return MOE_ERR_HIP;
+  h->desc = *desc;
+  h->workspace = workspace;
+  moe::LayerArgs& a = h->args;
+  a.d = desc->d, a.f = desc->f, a.E = desc->n_experts, a.k = desc->top_k, a.norm_topk = desc->norm_topk;
+  a.router_w = w->router_w, a.router_b = w->router_b;
+  a.gate_q = w->gate_q, a.gate_s = w->gate_s, a.up_q = w->up_q, a.up_s = w->up_s;
+  a.down_q = w->down_q, a.down_s = w->down_s;
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  a.counters = reinterpret_cast<unsigned*>(base + L.counters);
+  a.logits = reinterpret_cast<float*>(base + L.logits);
+  a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
+  a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
+  a.h = reinterpret_cast<float*>(base + L.h);
+  a.xnorm = reinterpret_cast<uint16_t*>(base + L.xnorm);
+  if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    delete h;
+    return MOE_ERR_HIP;
+  }
+  *out = h;
+  return MOE_OK;
+}
+
+void moe_decode_destroy(moe_handle h) { delete h; }
+
+moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float* y, int32_t* topk_idx,
+                              float* topk_w, void* stream) {
+  if (!h || !x || !y) return MOE_ERR_NULL;
+  if (T < 1 || T > h->desc.max_tokens) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y)) return MOE_ERR_ALIGN;
+  if ((topk_idx && !aligned4(topk_idx)) || (topk_w && !aligned4(topk_w))) return MOE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::LayerArgs& a = h->args;
+  if (moe::launch_router(a, x, nullptr, 0.f, T, topk_idx, topk_w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_gateup(a, x, T, s) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_down(a, T, y, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* residual, int32_t T, float eps,
+                                    uint16_t* x_trace, float* y_trace, int32_t* idx_trace, void* stream) {
+  if (!layers || !residual) return MOE_ERR_NULL;
+  if (L < 1 || T < 1) return MOE_ERR_SHAPE;
+  if (!(eps >= 0.f)) return MOE_ERR_SHAPE;
+  for (int l = 0; l < L; ++l) {
+    if (!layers[l]) return MOE_ERR_NULL;
+    if (layers[l]->desc.d != layers[0]->desc.d || layers[l]->desc.top_k != layers[0]->desc.top_k)
+      return MOE_ERR_SHAPE;
+    if (T > layers[l]->desc.max_tokens) return MOE_ERR_SHAPE;
+  }
+  if (!aligned16(residual) || (x_trace && !aligned16(x_trace)) || (y_trace && !aligned16(y_trace)) ||
+      (idx_trace && !aligned4(idx_trace)))
+    return MOE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t d = (size_t)layers[0]->desc.d, k = (size_t)layers[0]->desc.top_k;
+  for (int l = 0; l < L; ++l) {
+    const moe::LayerArgs& a = layers[l]->args;
+    uint16_t* xt = x_trace ? x_trace + (size_t)l * T * d : nullptr;
+    int32_t* it = idx_trace ? idx_trace + (size_t)l * T * k : nullptr;
+    float* yt = y_trace ? y_trace + (size_t)l * T * d : nullptr;
+    if (moe::launch_router(a, nullptr, residual, eps, T, it, nullptr, xt, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup(a, a.xnorm, T, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down(a, T, yt, residual, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+size_t lmhead_int4_argmax_workspace_bytes(int32_t V, int32_t d, int32_t B) {
+  if (V < 1 || V > (1 << 24) || !is_pow2(d) || d < 256 || d > 8192 || B < 1 || B > MOE_LMHEAD_MAX_B) return 0;
+  return moe::lmhead_workspace_bytes(V, d, B);
+}
+
+moe_status lmhead_int4_argmax(const uint8_t* w_q, const uint16_t* w_s, int32_t V, int32_t d, const uint16_t* x,
+                              int32_t B, int32_t* token, float* max_logit, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!w_q || !w_s || !x || !token) return MOE_ERR_NULL;
+  if (V < 1 || V > (1 << 24) || B < 1 || B > MOE_LMHEAD_MAX_B || d < 1 || d % 32) return MOE_ERR_SHAPE;
+  if (!is_pow2(d) || d < 256 || d > 8192) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(w_q) || !aligned16(w_s) || !aligned16(x) || !aligned4(token) ||
+      (max_logit && !aligned4(max_logit)))
+    return MOE_ERR_ALIGN;
+  if (!workspace || workspace_bytes < moe::lmhead_workspace_bytes(V, d, B)) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
+  if (moe::launch_lmhead(w_q, w_s, V, d, x, B, token, max_logit, workspace, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// launch.h -- host-side launchers of the decode kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Device pointers of one MoE layer plus the per-call workspace carve-up.
+struct LayerArgs {
+  int d, f, E, k, norm_topk;
+  const float* router_w;
+  const float* router_b;
+  const uint8_t* gate_q;
+  const uint16_t* gate_s;
+  const uint8_t* up_q;
+  const uint16_t* up_s;
+  const uint8_t* down_q;
+  const uint16_t* down_s;
+  // workspace
+  float* logits;         // [T][E]
+  unsigned* counters;    // [T] arrival counters, zero between calls
+  int32_t* sel_idx;      // [T][k]
+  float* sel_w;          // [T][k]
+  float* h;              // [T][k][f]  w_j * silu(g) * u
+  uint16_t* xnorm;       // [T][d]     normalized activation (stack)
+};
+
+// Router GEMV + softmax + top-k for T tokens.  Activations come either from
+// x (bf16 [T][d]) or, when x is NULL, from the fp32 residual r [T][d]
+// normalized by RMSNorm (eps), in which case x_l is also written to
+// a.xnorm and (if non-NULL) x_trace.
+hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
+                         int32_t* idx_out, float* w_out, uint16_t* x_trace, hipStream_t s);
+
+// h = w_j * silu(W_g[j] x) * (W_u[j] x) for the chosen experts.
+hipError_t launch_gateup(const LayerArgs& a, const uint16_t* x, int T, hipStream_t s);
+
+// y = sum_j W_d[j] h_j; with residual != NULL, residual += y instead of
+// writing y (y_out may still receive y when non-NULL).
+hipError_t launch_down(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
+
+// LM head GEMV + argmax.
+hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,
+                         int32_t* token, float* max_logit, void* workspace, hipStream_t s);
+
+size_t lmhead_workspace_bytes(int V, int d, int B);
+
+}  // namespace moe

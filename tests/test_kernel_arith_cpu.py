@@ -1,0 +1,83 @@
+"""CPU check of the int4 x bf16 dot-product identity the kernels rely on.
+
+The masks, shifts, magic constant, activation scaling and correction
+coefficients are read out of the kernel header (device_common.h) and
+emulated bit for bit in numpy, so a wrong constant there fails here, on the
+CPU, before any GPU run.  Each code u at each of the 8 positions of a dword
+must decode to an exact bf16 value, and the four pair products plus the
+correction must equal sum_e (u_e - 8) x_e exactly (fp64 arithmetic on bf16
+inputs is exact here)."""
+import os
+import re
+
+import numpy as np
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "sparse_moe_decode_gemv_amd", "csrc", "device_common.h")
+
+
+def kernel_constants():
+    src = open(HDR).read()
+    body = src[src.index("float dot8("):]
+    body = body[:body.index("return acc;")]
+    pairs = []
+    for m in re.finditer(r"dot2_bf16\(\(+w(?: >> (\d+)\))? ?& (0x[0-9A-Fa-f]+)u\) \| (0x[0-9A-Fa-f]+)u, s\.p(\d)", body):
+        pairs.append((int(m.group(1) or 0), int(m.group(2), 16), int(m.group(3), 16), int(m.group(4))))
+    mk = src[src.index("make_slice(const float v[8])"):]
+    mk = mk[:mk.index("return s;")]
+    scale = {int(m.group(1)): float(m.group(2)) for m in
+             re.finditer(r"s\.p(\d) = f32_to_bf16_bits\(v\[\d\] \* ([0-9.]+)f\)", mk)}
+    cm = re.search(r"s\.corr = -([0-9.]+)f \* \(\(v\[0\] \+ v\[4\]\) \+ \(v\[2\] \+ v\[6\]\)\) - ([0-9.]+)f \* "
+                   r"\(\(v\[1\] \+ v\[5\]\) \+ \(v\[3\] \+ v\[7\]\)\)", mk)
+    assert len(pairs) == 4 and cm, "kernel header no longer matches the expected form"
+    return pairs, scale, float(cm.group(1)), float(cm.group(2))
+
+
+def bf16_value(bits16):
+    return (np.asarray(bits16, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decode_pairs(w, pairs):
+    """For dwords w: the (low, high) bf16 values each pair instruction sees."""
+    out = {}
+    for shift, mask, magic, p in pairs:
+        v = ((w >> np.uint32(shift)) & np.uint32(mask)) | np.uint32(magic)
+        out[p] = (bf16_value(v & 0xFFFF), bf16_value(v >> 16))
+    return out
+
+
+# which element e each pair register carries in its (low, high) half, as the
+# activation slices are built: p0=(x0,x4), p1=(x1,x5), p2=(x2,x6), p3=(x3,x7)
+ELEMS = {0: (0, 4), 1: (1, 5), 2: (2, 6), 3: (3, 7)}
+
+
+def test_every_code_at_every_position_decodes_exactly():
+    pairs, scale, _, _ = kernel_constants()
+    for e in range(8):
+        u = np.zeros((16, 8), np.uint32)
+        u[:, e] = np.arange(16)
+        w = (u << (4 * np.arange(8, dtype=np.uint32))).sum(axis=1).astype(np.uint32)
+        dec = decode_pairs(w, pairs)
+        p = [q for q, (a, b) in ELEMS.items() if e in (a, b)][0]
+        half = 0 if ELEMS[p][0] == e else 1
+        vals = dec[p][half]
+        # even positions: 128 + u (pair scale 1); odd: 128 + 8u (activation scaled by 1/8)
+        f = scale.get(p, 1.0)
+        np.testing.assert_array_equal(vals, 128 + np.arange(16) / f)
+
+
+def test_identity_on_random_codes_and_activations():
+    pairs, scale, c_even, c_odd = kernel_constants()
+    rng = np.random.default_rng(5)
+    n = 20000
+    u = rng.integers(0, 16, size=(n, 8)).astype(np.uint32)
+    w = (u << (4 * np.arange(8, dtype=np.uint32))).sum(axis=1).astype(np.uint32)
+    x = bf16_value(rng.integers(0, 1 << 16, size=(n, 8)) & 0xBFFF)  # finite bf16, |x| < 2
+    x[np.abs(x) < 1e-30] = 0.0
+    dec = decode_pairs(w, pairs)
+    acc = -c_even * (x[:, 0] + x[:, 4] + x[:, 2] + x[:, 6]) - c_odd * (x[:, 1] + x[:, 5] + x[:, 3] + x[:, 7])
+    for p, (a, b) in ELEMS.items():
+        f = scale.get(p, 1.0)
+        acc = acc + dec[p][0] * (x[:, a] * f) + dec[p][1] * (x[:, b] * f)
+    want = ((u.astype(np.int64) - 8) * x).sum(axis=1)
+    np.testing.assert_allclose(acc, want, rtol=0, atol=1e-9 * np.abs(x).sum(axis=1).max())
