@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_decode.so")
-SOURCES = ["api.hip", "kernels_moe.hip", "kernels_lmhead.hip"]
+SOURCES = ["api.hip", "kernels_moe.hip", "kernels_lmhead.hip", "kernels_layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

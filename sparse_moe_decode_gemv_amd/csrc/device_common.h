@@ -33,12 +33,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) return (b >> 16) | 0x40u;  // quiet NaN
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return b >> 16;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16(f, 0.f) & 0xFFFFu; }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
@@ -55,36 +59,43 @@ struct Slice8 {
 // From 8 fp32 values that are exactly representable in bf16.
 __device__ __forceinline__ Slice8 make_slice(const float v[8]) {
   Slice8 s;
-  s.p0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[4]) << 16);
-  s.p1 = f32_to_bf16_bits(v[1] * 0.125f) | (f32_to_bf16_bits(v[5] * 0.125f) << 16);
-  s.p2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[6]) << 16);
-  s.p3 = f32_to_bf16_bits(v[3] * 0.125f) | (f32_to_bf16_bits(v[7] * 0.125f) << 16);
+  s.p0 = pack_bf16(v[0], v[4]);
+  s.p1 = pack_bf16(v[1] * 0.125f, v[5] * 0.125f);
+  s.p2 = pack_bf16(v[2], v[6]);
+  s.p3 = pack_bf16(v[3] * 0.125f, v[7] * 0.125f);
   s.corr = -136.0f * ((v[0] + v[4]) + (v[2] + v[6])) - 24.0f * ((v[1] + v[5]) + (v[3] + v[7]));
   return s;
 }
 
 // From 8 bf16 values held as 4 dwords (dword i = elements 2i (low), 2i+1 (high)).
 __device__ __forceinline__ Slice8 make_slice_bf16(uint4 q) {
-  float v[8];
-  v[0] = bf16_bits_to_f32(q.x & 0xFFFFu);
-  v[1] = bf16_bits_to_f32(q.x >> 16);
-  v[2] = bf16_bits_to_f32(q.y & 0xFFFFu);
-  v[3] = bf16_bits_to_f32(q.y >> 16);
-  v[4] = bf16_bits_to_f32(q.z & 0xFFFFu);
-  v[5] = bf16_bits_to_f32(q.z >> 16);
-  v[6] = bf16_bits_to_f32(q.w & 0xFFFFu);
-  v[7] = bf16_bits_to_f32(q.w >> 16);
-  return make_slice(v);
+  Slice8 s;
+  s.p0 = (q.x & 0xFFFFu) | (q.z << 16);
+  s.p2 = (q.y & 0xFFFFu) | (q.w << 16);
+  const float x0 = bf16_bits_to_f32(q.x & 0xFFFFu), x1 = __uint_as_float(q.x & 0xFFFF0000u);
+  const float x2 = bf16_bits_to_f32(q.y & 0xFFFFu), x3 = __uint_as_float(q.y & 0xFFFF0000u);
+  const float x4 = bf16_bits_to_f32(q.z & 0xFFFFu), x5 = __uint_as_float(q.z & 0xFFFF0000u);
+  const float x6 = bf16_bits_to_f32(q.w & 0xFFFFu), x7 = __uint_as_float(q.w & 0xFFFF0000u);
+  s.p1 = pack_bf16(x1 * 0.125f, x5 * 0.125f);
+  s.p3 = pack_bf16(x3 * 0.125f, x7 * 0.125f);
+  s.corr = -136.0f * ((x0 + x4) + (x2 + x6)) - 24.0f * ((x1 + x5) + (x3 + x7));
+  return s;
 }
 
 // fp32 activations split as hi = bf16(v), lo = bf16(v - hi): two slices whose
-// sum carries v to about 2^-16 relative.
+// sum carries v to about 2^-16 relative.  Each slice's correction is taken
+// from its own (exactly representable) values, so the 128-offsets cancel
+// exactly and only the split's residual is lost.
 __device__ __forceinline__ void make_slice_hilo(const float v[8], Slice8& hi, Slice8& lo) {
   float h[8], l[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = bf16_bits_to_f32(f32_to_bf16_bits(v[e]));
-    l[e] = bf16_bits_to_f32(f32_to_bf16_bits(v[e] - h[e]));
+  for (int e = 0; e < 8; e += 2) {
+    const uint32_t p = pack_bf16(v[e], v[e + 1]);
+    h[e] = bf16_bits_to_f32(p & 0xFFFFu);
+    h[e + 1] = __uint_as_float(p & 0xFFFF0000u);
+    const uint32_t q = pack_bf16(v[e] - h[e], v[e + 1] - h[e + 1]);
+    l[e] = bf16_bits_to_f32(q & 0xFFFFu);
+    l[e + 1] = __uint_as_float(q & 0xFFFF0000u);
   }
   hi = make_slice(h);
   lo = make_slice(l);
@@ -118,21 +129,123 @@ __device__ __forceinline__ float dot_piece_hilo(uint4 q, const Slice8 hi[4], con
   return p;
 }
 
+// ---- cross-lane reductions (VALU only: DPP and gfx950 permlane swaps) ------
+// Steps pair lanes within growing aligned segments: quad_perm [1,0,3,2] and
+// [2,3,0,1] (segments of 2 and 4), row_half_mirror (8), row_mirror (16),
+// v_permlane16_swap (32: rows 0<->1 and 2<->3) and v_permlane32_swap (64:
+// the two half-waves).  After each step every lane of a segment holds the
+// same value, so the mirror pairings (lane i with 7-i, 15-i) combine the two
+// halves like an xor would.  No step goes through LDS or the scalar unit.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// (value of this lane, value of the lane 16 rows away) for xor-16 pairing
+__device__ __forceinline__ u32x2_t swap16(uint32_t v) { return __builtin_amdgcn_permlane16_swap(v, v, false, false); }
+__device__ __forceinline__ u32x2_t swap32(uint32_t v) { return __builtin_amdgcn_permlane32_swap(v, v, false, false); }
+
 // Sum over aligned segments of SEG lanes (SEG a power of two <= 64); every
 // lane of a segment receives the segment's sum.
 template <int SEG>
 __device__ __forceinline__ float seg_sum(float v) {
-#pragma unroll
-  for (int o = SEG / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if constexpr (SEG >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (SEG >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (SEG >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (SEG >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (SEG >= 32) {
+    const u32x2_t p = swap16(__float_as_uint(v));
+    v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  }
+  if constexpr (SEG >= 64) {
+    const u32x2_t p = swap32(__float_as_uint(v));
+    v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  }
   return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return seg_sum<64>(v); }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  u32x2_t p = swap16(__float_as_uint(v));
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = swap32(__float_as_uint(v));
+  return fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  u32x2_t p = swap16(v);
+  v = max(p.x, p.y);
+  p = swap32(v);
+  return max(p.x, p.y);
+}
+
+// Order-preserving map of a float to an unsigned (larger float, larger key;
+// -0 sorts just below +0).
+__device__ __forceinline__ uint32_t ordered_bits(float z) {
+  const uint32_t b = __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// (value, index) maximum over the wave: larger value, then smaller index.
+// Values must not be NaN.  Every lane receives the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  const float m = wave_max(v);
+  // lowest index among the lanes holding the maximum
+  const int cand = v == m ? i : 0x7FFFFFFF;
+  uint32_t c = (uint32_t)cand;
+  c = min(c, dpp_u<kDppXor1>(c));
+  c = min(c, dpp_u<kDppXor2>(c));
+  c = min(c, dpp_u<kDppHalfMirror>(c));
+  c = min(c, dpp_u<kDppMirror>(c));
+  u32x2_t p = swap16(c);
+  c = min(p.x, p.y);
+  p = swap32(c);
+  c = min(p.x, p.y);
+  v = m;
+  i = (int)c;
+}
+
+// ---- cross-workgroup hand-off without cache maintenance -------------------
+// Data that other workgroups read during the same kernel is written and read
+// with agent-scope relaxed atomics (global_store/load with sc1: coherent
+// across the XCDs' L2s), so no L2 writeback or invalidate is needed.  The
+// writer waits for its stores to complete before bumping the arrival
+// counter; the reader issues its loads only after it has seen the count.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long load_coherent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this wave's outstanding memory operations have completed.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned arrive(unsigned* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -20,14 +20,6 @@
 
 namespace moe {
 
-// Order-preserving map of a float to an unsigned; larger float, larger key.
-__device__ __forceinline__ uint32_t ordered_bits(float z) {
-  const uint32_t b = __float_as_uint(z);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float unordered_bits(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
 // Larger logit first, then the smaller row.
 __device__ __forceinline__ unsigned long long make_key(float z, uint32_t row) {
   return ((unsigned long long)ordered_bits(z) << 32) | (unsigned long long)(0xFFFFFFFFu - row);
@@ -114,45 +106,43 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
 #pragma unroll
   for (int b = 0; b < BP; ++b) {
     float v = best[b];
-    uint32_t r = brow[b];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o, 64);
-      const uint32_t orow = __shfl_xor(r, o, 64);
-      if (ov > v || (ov == v && orow < r)) v = ov, r = orow;
-    }
-    if (lane == 0) s_best[wid][b] = r == 0xFFFFFFFFu ? 0ull : make_key(v, r);
+    int r = (int)brow[b];  // 0xFFFFFFFF (no row) reads as -1 and loses below
+    if (r < 0) v = -INFINITY, r = 0x7FFFFFFF;
+    wave_argmax(v, r);
+    if (lane == 0) s_best[wid][b] = r == 0x7FFFFFFF ? 0ull : make_key(v, (uint32_t)r);
   }
   __syncthreads();
   if (threadIdx.x < BP) {
     unsigned long long kmax = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) kmax = s_best[w][threadIdx.x] > kmax ? s_best[w][threadIdx.x] : kmax;
-    partial[(size_t)blockIdx.x * BP + threadIdx.x] = kmax;
+    store_coherent(partial + (size_t)blockIdx.x * BP + threadIdx.x, kmax);
+    wait_vm();
   }
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1;
+  if (threadIdx.x == 0) s_last = arrive(counter) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   // last workgroup: reduce G keys per x row
   for (int b = 0; b < B; ++b) {
     unsigned long long kmax = 0;
     for (int g = threadIdx.x; g < (int)gridDim.x; g += 256) {
-      const unsigned long long kv = partial[(size_t)g * BP + b];
+      const unsigned long long kv = load_coherent(partial + (size_t)g * BP + b);
       kmax = kv > kmax ? kv : kmax;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long ok = __shfl_xor(kmax, o, 64);
-      kmax = ok > kmax ? ok : kmax;
+    // 64-bit max over the workgroup through LDS
+    __shared__ unsigned long long s_red[256];
+    s_red[threadIdx.x] = kmax;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) s_red[threadIdx.x] = s_red[threadIdx.x + w] > s_red[threadIdx.x] ? s_red[threadIdx.x + w]
+                                                                                            : s_red[threadIdx.x];
+      __syncthreads();
     }
-    if (lane == 0) s_best[wid][0] = kmax;
+    if (threadIdx.x == 0) s_best[0][0] = s_red[0];
     __syncthreads();
     if (threadIdx.x == 0) {
-      unsigned long long m = s_best[0][0];
-      for (int w = 1; w < 4; ++w) m = s_best[w][0] > m ? s_best[w][0] : m;
+      const unsigned long long m = s_best[0][0];
       token[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
       if (max_logit) max_logit[b] = unordered_bits((uint32_t)(m >> 32));
     }

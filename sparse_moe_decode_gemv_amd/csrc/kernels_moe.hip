@@ -20,78 +20,39 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 
 // ----------------------------------------------------------------- top-k
 
-// Softmax over E logits and the k largest, in one wave.  Ties go to the
-// lower expert index, so (value desc, index asc) is a total order and every
-// lane of the butterfly ends with the same winner.  Lane r < k writes
-// selection r.
+// Softmax + top-k of one token's E logits in one wave (topk.h); lane r < k
+// writes choice r.
 template <int EPL>
 __device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int norm, int lane, int32_t* sel_idx,
                                           float* sel_w, int32_t* idx_out, float* w_out) {
   float v[EPL];
-  float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    const float l = e < E ? lg[e] : -INFINITY;
-    v[i] = l == l ? l : -INFINITY;  // a NaN logit never wins; keeps the order total
-    m = fmaxf(m, v[i]);
+    const float l = load_coherent(lg + min(lane + 64 * i, E - 1));
+    v[i] = lane + 64 * i < E && l == l ? l : -INFINITY;
   }
-  m = wave_max(m);
-  float z = 0.f;
-  if (!norm) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i < E) z += expf(v[i] - m);
-    z = wave_sum(z);
-  }
-  int my_idx = 0;
-  float my_l = -INFINITY;
-  for (int r = 0; r < k; ++r) {
-    float best = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i < E && (bi == 0x7FFFFFFF || v[i] > best)) {
-        best = v[i];
-        bi = lane + 64 * i;
-      }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
-      }
-    }
-    if (lane == r) {
-      my_idx = bi;
-      my_l = best;
-    }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
-  }
-  const float p = lane < k ? expf(my_l - m) : 0.f;
-  const float den = norm ? wave_sum(p) : z;
+  int se;
+  float sw;
+  topk_fast<EPL>(v, E, k, norm, lane, se, sw);
   if (lane < k) {
-    const float w = p / den;
-    sel_idx[lane] = my_idx;
-    sel_w[lane] = w;
-    if (idx_out) idx_out[lane] = my_idx;
-    if (w_out) w_out[lane] = w;
+    sel_idx[lane] = se;
+    sel_w[lane] = sw;
+    if (idx_out) idx_out[lane] = se;
+    if (w_out) w_out[lane] = sw;
   }
 }
 
 // ----------------------------------------------------------------- router
 
-// grid (E, T), block 64: wave e of token t computes logit e.
-template <int D>
+// grid (E, T), block 64: wave e of token t computes logit e.  EPL = experts
+// per lane in the top-k wave, ceil(E/64).
+template <int D, int EPL>
 __global__ __launch_bounds__(64) void k_router(const float* __restrict__ Wr, const float* __restrict__ bias,
                                                const uint16_t* __restrict__ x, const float* __restrict__ resid,
                                                float eps, int E, int k, int norm, float* __restrict__ logits,
@@ -157,29 +118,18 @@ __global__ __launch_bounds__(64) void k_router(const float* __restrict__ Wr, con
   }
   acc = wave_sum(acc);
   if (bias) acc += bias[e];
-  if (lane == 0) logits[(size_t)t * E + e] = acc;
+  if (lane == 0) store_coherent(logits + (size_t)t * E + e, acc);
 
   // Arrival: the last wave of token t selects its experts.
-  __threadfence();
+  wait_vm();
   unsigned prev = 0;
-  if (lane == 0) prev = atomicAdd(&counters[t], 1u);
-  prev = __shfl(prev, 0, 64);
+  if (lane == 0) prev = arrive(&counters[t]);
+  prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != (unsigned)(E - 1)) return;
-  __threadfence();
   const float* lg = logits + (size_t)t * E;
   int32_t* io = idx_out ? idx_out + (size_t)t * k : nullptr;
   float* wo = w_out ? w_out + (size_t)t * k : nullptr;
-  const int epl = (E + 63) / 64;
-  if (epl <= 1)
-    topk_wave<1>(lg, E, k, norm, lane, sel_idx + t * k, sel_w + t * k, io, wo);
-  else if (epl <= 2)
-    topk_wave<2>(lg, E, k, norm, lane, sel_idx + t * k, sel_w + t * k, io, wo);
-  else if (epl <= 4)
-    topk_wave<4>(lg, E, k, norm, lane, sel_idx + t * k, sel_w + t * k, io, wo);
-  else if (epl <= 8)
-    topk_wave<8>(lg, E, k, norm, lane, sel_idx + t * k, sel_w + t * k, io, wo);
-  else
-    topk_wave<16>(lg, E, k, norm, lane, sel_idx + t * k, sel_w + t * k, io, wo);
+  topk_wave<EPL>(lg, E, k, norm, lane, sel_idx + t * k, sel_w + t * k, io, wo);
   if (lane == 0) counters[t] = 0u;  // ready for the next call
 }
 
@@ -279,35 +229,20 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
   const int r0 = wave * ROWS_W;
   if (r0 >= d) return;
 
-  int cc[LPR];
+  int cc[LPR], slot[LPR];
   bool act[LPR];
   size_t ebase[LPR];
-  Slice8 hh[LPR][4], hl[LPR][4];
 #pragma unroll
   for (int m = 0; m < LPR; ++m) {
     const int flat = P >= 64 ? 64 * m + lane : lane % P;
-    const int slot = flat / CPRF;
+    slot[m] = flat / CPRF;
     cc[m] = flat % CPRF;
-    act[m] = slot < k;
-    const int e = act[m] ? min(max(sel_idx[t * k + slot], 0), E - 1) : 0;
+    act[m] = slot[m] < k;
+    const int e = act[m] ? min(max(sel_idx[t * k + slot[m]], 0), E - 1) : 0;
     ebase[m] = (size_t)e * d;
-    const int base = 128 * (cc[m] >> 2) + 8 * (cc[m] & 3);
-    const float* hs = h + ((size_t)t * k + (act[m] ? slot : 0)) * F;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v[8];
-      if (act[m]) {
-        const float4 a = *reinterpret_cast<const float4*>(hs + base + 32 * j);
-        const float4 b = *reinterpret_cast<const float4*>(hs + base + 32 * j + 4);
-        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = 0.f;
-      }
-      make_slice_hilo(v, hh[m][j], hl[m][j]);
-    }
   }
 
+  // weight pieces first: their HBM latency overlaps the activation set-up
   uint4 q[NLD];
   uint2 sc[NLD];
 #pragma unroll
@@ -320,6 +255,23 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
     } else {
       q[n] = make_uint4(0, 0, 0, 0);
       sc[n] = make_uint2(0, 0);
+    }
+  }
+
+  Slice8 hh[LPR][4], hl[LPR][4];
+#pragma unroll
+  for (int m = 0; m < LPR; ++m) {
+    const int base = 128 * (cc[m] >> 2) + 8 * (cc[m] & 3);
+    const float* hs = h + ((size_t)t * k + (act[m] ? slot[m] : 0)) * F;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v[8];
+      const float4 a = *reinterpret_cast<const float4*>(hs + base + 32 * j);
+      const float4 b = *reinterpret_cast<const float4*>(hs + base + 32 * j + 4);
+      const bool on = act[m];  // padding slots contribute exact zeros
+      v[0] = on ? a.x : 0.f, v[1] = on ? a.y : 0.f, v[2] = on ? a.z : 0.f, v[3] = on ? a.w : 0.f;
+      v[4] = on ? b.x : 0.f, v[5] = on ? b.y : 0.f, v[6] = on ? b.z : 0.f, v[7] = on ? b.w : 0.f;
+      make_slice_hilo(v, hh[m][j], hl[m][j]);
     }
   }
 
@@ -353,11 +305,27 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
 
 // ----------------------------------------------------------------- launchers
 
+template <int D, int EPL>
+static void router_launch(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, int32_t* io,
+                          float* wo, uint16_t* xt, hipStream_t s) {
+  hipLaunchKernelGGL((k_router<D, EPL>), dim3(a.E, T), dim3(64), 0, s, a.router_w, a.router_b, x, r, eps, a.E,
+                     a.k, a.norm_topk, a.logits, a.counters, a.sel_idx, a.sel_w, io, wo, a.xnorm, xt);
+}
+
 template <int D>
 static void router_inst(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, int32_t* io,
                         float* wo, uint16_t* xt, hipStream_t s) {
-  hipLaunchKernelGGL(k_router<D>, dim3(a.E, T), dim3(64), 0, s, a.router_w, a.router_b, x, r, eps, a.E, a.k,
-                     a.norm_topk, a.logits, a.counters, a.sel_idx, a.sel_w, io, wo, a.xnorm, xt);
+  const int epl = (a.E + 63) / 64;
+  if (epl <= 1)
+    router_launch<D, 1>(a, x, r, eps, T, io, wo, xt, s);
+  else if (epl <= 2)
+    router_launch<D, 2>(a, x, r, eps, T, io, wo, xt, s);
+  else if (epl <= 4)
+    router_launch<D, 4>(a, x, r, eps, T, io, wo, xt, s);
+  else if (epl <= 8)
+    router_launch<D, 8>(a, x, r, eps, T, io, wo, xt, s);
+  else
+    router_launch<D, 16>(a, x, r, eps, T, io, wo, xt, s);
 }
 
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,

@@ -25,7 +25,42 @@ struct LayerArgs {
   float* sel_w;          // [T][k]
   float* h;              // [T][k][f]  w_j * silu(g) * u
   uint16_t* xnorm;       // [T][d]     normalized activation (stack)
+  // single-launch step (T = 1)
+  unsigned long long* tagged_logits;  // [E]  (epoch << 32 | logit bits)
+  unsigned* flags;                    // [kMaxFusedGrid] per-workgroup epoch flags
+  unsigned* epoch;                    // [1]  calls completed
+  unsigned* error;                    // [1]  bit 0/1: a bounded wait timed out
 };
+
+constexpr int kMaxFusedGrid = 1024;
+
+// Arguments of the single-launch 1-token layer kernel.
+struct FusedArgs {
+  const float* router_w;
+  const float* router_b;
+  const uint8_t* gate_q;
+  const uint16_t* gate_s;
+  const uint8_t* up_q;
+  const uint16_t* up_s;
+  const uint8_t* down_q;
+  const uint16_t* down_s;
+  const uint16_t* x;     // [d] bf16
+  float* y;              // [d]
+  int32_t* idx_out;      // [k] or NULL
+  float* w_out;          // [k] or NULL
+  unsigned long long* logits;
+  float* h;
+  unsigned* flags;
+  unsigned* epoch;
+  unsigned* error;
+  int E, k, norm;
+};
+
+// The whole 1-token step in one launch, for the shapes it is built for
+// (d, f) in {(256, 128), (2048, 512)}, E <= 256, k*f*4 <= 64 KiB.
+bool fused_layer_supported(int d, int f, int E, int k, int G);
+int fused_grid();
+hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
 
 // Router GEMV + softmax + top-k for T tokens.  Activations come either from
 // x (bf16 [T][d]) or, when x is NULL, from the fp32 residual r [T][d]

@@ -12,7 +12,9 @@ from oracle import moe as OM
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(layer_np, cfg, X, norm=1, max_tokens=None):
+def run_layer(layer_np, cfg, X, norm=1, max_tokens=None, one_by_one=False):
+    """All T tokens in one call (batched path), or one call per token
+    (the single-launch 1-token path)."""
     import torch
     dev = device()
     T = X.shape[0]
@@ -21,42 +23,53 @@ def run_layer(layer_np, cfg, X, norm=1, max_tokens=None):
     y = torch.full((T, cfg.d), float("nan"), dtype=torch.float32, device=dev)
     idx = torch.full((T, cfg.k), -1, dtype=torch.int32, device=dev)
     w = torch.full((T, cfg.k), float("nan"), dtype=torch.float32, device=dev)
-    L.forward(x, y, idx, w)
+    if one_by_one:
+        for t in range(T):
+            L.forward(x[t:t + 1], y[t:t + 1], idx[t:t + 1], w[t:t + 1])
+    else:
+        L.forward(x, y, idx, w)
     torch.cuda.synchronize()
     return L, y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
 
 
+BOTH = pytest.mark.parametrize("one_by_one", [False, True], ids=["batched", "single-launch"])
+
+
+@BOTH
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
-def test_tiny_layer_parity(seed):
+def test_tiny_layer_parity(seed, one_by_one):
     cfg = synth.TINY
     lay = synth.make_layer(cfg, seed)
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, seed, 4)
-    _, y, idx, w = run_layer(lay, cfg, X, max_tokens=8)
+    _, y, idx, w = run_layer(lay, cfg, X, max_tokens=8, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, f"tiny seed {seed}")
 
 
-def test_tiny_layer_without_renormalization():
+@BOTH
+def test_tiny_layer_without_renormalization(one_by_one):
     cfg = synth.TINY
     lay = synth.make_layer(cfg, 2)
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, 2, 3)
-    _, y, idx, w = run_layer(lay, cfg, X, norm=0)
+    _, y, idx, w = run_layer(lay, cfg, X, norm=0, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k, norm_topk=False), idx, w, y, "tiny norm=0")
 
 
+@BOTH
 @pytest.mark.parametrize("k", [1, 3, 16])
-def test_tiny_layer_other_k(k):
+def test_tiny_layer_other_k(k, one_by_one):
     from dataclasses import replace
     cfg = replace(synth.TINY, k=k)
     lay = synth.make_layer(cfg, 7)
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, 7, 2)
-    _, y, idx, w = run_layer(lay, cfg, X)
+    _, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, k), idx, w, y, f"tiny k={k}")
 
 
-def test_odd_expert_count_and_bias():
+@BOTH
+def test_odd_expert_count_and_bias(one_by_one):
     """E = 100 (not a multiple of the wave width), router bias present."""
     from dataclasses import replace
     cfg = replace(synth.TINY, E=100, k=5)
@@ -64,8 +77,27 @@ def test_odd_expert_count_and_bias():
     lay["router_b"] = (np.arange(100) % 7 - 3).astype(np.float32) * 0.05
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, 8, 3)
-    _, y, idx, w = run_layer(lay, cfg, X)
+    _, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, "E=100")
+
+
+def test_flagship_tied_router_logits_pick_lower_expert():
+    """Router rows 3 and 200 made identical and dominant: their logits tie
+    exactly, and the lower expert index must come first."""
+    cfg = synth.LAYER
+    lay = synth.make_layer(cfg, 4)
+    lay["router_w"] = lay["router_w"].copy()
+    lay["router_w"][3] = lay["router_w"][200] = np.float32(0.05)
+    OL = OM.Layer.from_dict(lay)
+    X = np.full((1, cfg.d), 0x3F80, np.uint16)  # x = 1: both rows give the same fp32 sum
+    out = OM.moe_forward_tokens(OL, X, cfg.k)
+    assert OM.topk_margin(out["logits"][0], cfg.k) > 1e-3  # the rest of the set is unambiguous
+    _, y, idx, w = run_layer(lay, cfg, X, one_by_one=True)
+    assert idx[0][0] == 3 and idx[0][1] == 200, idx[0]
+    assert w[0][0] == w[0][1]
+    assert out["idx"][0][0] == 3 and out["idx"][0][1] == 200
+    err = np.abs(y[0] - out["y"][0]).max()
+    assert err <= 2e-3 * np.abs(out["y"][0]).max()
 
 
 @pytest.mark.parametrize("seed", [1, 2])
@@ -92,6 +124,29 @@ def test_batch_with_zipf_bias_parity():
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, "batch")
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
     assert counts.max() >= 16  # the skew the workload is built to have
+
+
+def test_single_launch_and_batched_calls_interleave_on_one_handle():
+    """T=1 calls (single launch, epoch-tagged hand-offs) and T>1 calls
+    (batched kernels) alternate on the same workspace."""
+    import torch
+    cfg = synth.LAYER
+    lay = synth.make_layer(cfg, 5)
+    OL = OM.Layer.from_dict(lay)
+    X = tokens(cfg, OL, 5, 4)
+    ref = OM.moe_forward_tokens(OL, X, cfg.k)
+    dev = device()
+    L = M.MoELayer.create(M.upload(lay, dev), cfg.d, cfg.f, cfg.E, cfg.k, 1, 4)
+    x = torch.from_numpy(as_i16(X)).to(dev)
+    for rnd in range(3):
+        for T in (1, 4, 1, 1, 2):
+            y = torch.full((T, cfg.d), float("nan"), device=dev)
+            idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+            w = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+            L.forward(x[:T], y, idx, w)
+            torch.cuda.synchronize()
+            compare_layer({k: v[:T] for k, v in ref.items()}, idx.cpu().numpy(), w.cpu().numpy(),
+                          y.cpu().numpy(), f"round {rnd} T={T}")
 
 
 def test_ragged_token_counts_reuse_one_handle():

@@ -23,14 +23,25 @@ def kernel_constants():
     pairs = []
     for m in re.finditer(r"dot2_bf16\(\(+w(?: >> (\d+)\))? ?& (0x[0-9A-Fa-f]+)u\) \| (0x[0-9A-Fa-f]+)u, s\.p(\d)", body):
         pairs.append((int(m.group(1) or 0), int(m.group(2), 16), int(m.group(3), 16), int(m.group(4))))
-    mk = src[src.index("make_slice(const float v[8])"):]
-    mk = mk[:mk.index("return s;")]
-    scale = {int(m.group(1)): float(m.group(2)) for m in
-             re.finditer(r"s\.p(\d) = f32_to_bf16_bits\(v\[\d\] \* ([0-9.]+)f\)", mk)}
-    cm = re.search(r"s\.corr = -([0-9.]+)f \* \(\(v\[0\] \+ v\[4\]\) \+ \(v\[2\] \+ v\[6\]\)\) - ([0-9.]+)f \* "
-                   r"\(\(v\[1\] \+ v\[5\]\) \+ \(v\[3\] \+ v\[7\]\)\)", mk)
-    assert len(pairs) == 4 and cm, "kernel header no longer matches the expected form"
-    return pairs, scale, float(cm.group(1)), float(cm.group(2))
+    consts = []
+    for fn, var in (("make_slice(const float v[8])", "v"), ("make_slice_bf16(uint4 q)", "x")):
+        mk = src[src.index(fn):]
+        mk = mk[:mk.index("return s;")]
+        found = re.findall(r"s\.p(\d) = pack_bf16\(\w+(?:\[\d\])? \* ([0-9.]+)f, \w+(?:\[\d\])? \* ([0-9.]+)f\)", mk)
+        assert all(a == b for _, a, b in found), f"{fn}: the two halves of a pair are scaled differently"
+        scale = {int(p): float(a) for p, a, _ in found}
+        if var == "v":
+            cm = re.search(r"s\.corr = -([0-9.]+)f \* \(\(v\[0\] \+ v\[4\]\) \+ \(v\[2\] \+ v\[6\]\)\) - "
+                           r"([0-9.]+)f \* \(\(v\[1\] \+ v\[5\]\) \+ \(v\[3\] \+ v\[7\]\)\)", mk)
+        else:
+            cm = re.search(r"s\.corr = -([0-9.]+)f \* \(\(x0 \+ x4\) \+ \(x2 \+ x6\)\) - "
+                           r"([0-9.]+)f \* \(\(x1 \+ x5\) \+ \(x3 \+ x7\)\)", mk)
+        assert cm and sorted(scale) == [1, 3], f"{fn} no longer matches the expected form"
+        consts.append((scale, float(cm.group(1)), float(cm.group(2))))
+    assert len(pairs) == 4, "dot8 no longer matches the expected form"
+    assert consts[0] == consts[1], "the two slice builders disagree"
+    scale, c_even, c_odd = consts[0]
+    return pairs, scale, c_even, c_odd
 
 
 def bf16_value(bits16):
