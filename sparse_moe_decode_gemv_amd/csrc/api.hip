@@ -13,7 +13,7 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 struct Layout {
-  size_t counters, logits, sel_idx, sel_w, h, xnorm, tagged, flags, epoch, total;
+  size_t counters, logits, sel_idx, sel_w, h, xnorm, tagged, hrec, epoch, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -45,9 +45,9 @@ Layout layout_of(const moe_layer_desc* d) {
   L.sel_w = o, o += align256(T * k * sizeof(float));
   L.h = o, o += align256(T * k * (size_t)d->f * sizeof(float));
   L.xnorm = o, o += align256(T * (size_t)d->d * sizeof(uint16_t));
-  L.tagged = o, o += align256(E * sizeof(unsigned long long));
-  L.flags = o, o += align256((size_t)moe::kMaxFusedGrid * sizeof(unsigned));
-  L.epoch = o, o += 256;  // epoch word, then the error word
+  L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
+  L.hrec = o, o += align256(k * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
+  L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
   L.total = o;
   return L;
 }
@@ -116,9 +116,9 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.h = reinterpret_cast<float*>(base + L.h);
   a.xnorm = reinterpret_cast<uint16_t*>(base + L.xnorm);
   a.tagged_logits = reinterpret_cast<unsigned long long*>(base + L.tagged);
-  a.flags = reinterpret_cast<unsigned*>(base + L.flags);
+  a.hrec = reinterpret_cast<unsigned long long*>(base + L.hrec);
   a.epoch = reinterpret_cast<unsigned*>(base + L.epoch);
-  a.error = a.epoch + 1;
+  a.error = a.epoch + moe::kMaxFusedGrid;
   if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
@@ -144,7 +144,7 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
     f.gate_q = a.gate_q, f.gate_s = a.gate_s, f.up_q = a.up_q, f.up_s = a.up_s;
     f.down_q = a.down_q, f.down_s = a.down_s;
     f.x = x, f.y = y, f.idx_out = topk_idx, f.w_out = topk_w;
-    f.logits = a.tagged_logits, f.h = a.h, f.flags = a.flags, f.epoch = a.epoch, f.error = a.error;
+    f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error;
     f.E = a.E, f.k = a.k, f.norm = a.norm_topk;
     return moe::launch_layer_fused(f, a.d, a.f, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }

@@ -82,25 +82,6 @@ __device__ __forceinline__ Slice8 make_slice_bf16(uint4 q) {
   return s;
 }
 
-// fp32 activations split as hi = bf16(v), lo = bf16(v - hi): two slices whose
-// sum carries v to about 2^-16 relative.  Each slice's correction is taken
-// from its own (exactly representable) values, so the 128-offsets cancel
-// exactly and only the split's residual is lost.
-__device__ __forceinline__ void make_slice_hilo(const float v[8], Slice8& hi, Slice8& lo) {
-  float h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const uint32_t p = pack_bf16(v[e], v[e + 1]);
-    h[e] = bf16_bits_to_f32(p & 0xFFFFu);
-    h[e + 1] = __uint_as_float(p & 0xFFFF0000u);
-    const uint32_t q = pack_bf16(v[e] - h[e], v[e + 1] - h[e + 1]);
-    l[e] = bf16_bits_to_f32(q & 0xFFFFu);
-    l[e + 1] = __uint_as_float(q & 0xFFFF0000u);
-  }
-  hi = make_slice(h);
-  lo = make_slice(l);
-}
-
 // acc + sum_e (128+u_e or 128+8u_e) * (x_e or x_e/8); started from s.corr
 // this is sum_e (u_e - 8) x_e.
 __device__ __forceinline__ float dot8(uint32_t w, const Slice8& s, float acc) {
@@ -121,11 +102,59 @@ __device__ __forceinline__ float dot_piece(uint4 q, const Slice8 xs[4], uint2 sc
   return p;
 }
 
-__device__ __forceinline__ float dot_piece_hilo(uint4 q, const Slice8 hi[4], const Slice8 lo[4], uint2 sc) {
-  float p = dot8(q.x, lo[0], dot8(q.x, hi[0], hi[0].corr + lo[0].corr)) * f16_bits_to_f32(sc.x & 0xFFFFu);
-  p = fmaf(dot8(q.y, lo[1], dot8(q.y, hi[1], hi[1].corr + lo[1].corr)), f16_bits_to_f32(sc.x >> 16), p);
-  p = fmaf(dot8(q.z, lo[2], dot8(q.z, hi[2], hi[2].corr + lo[2].corr)), f16_bits_to_f32(sc.y & 0xFFFFu), p);
-  p = fmaf(dot8(q.w, lo[3], dot8(q.w, hi[3], hi[3].corr + lo[3].corr)), f16_bits_to_f32(sc.y >> 16), p);
+// ---- fp16 variant for internally produced activations (the SwiGLU output h)
+// fp16 1024.0 is 0x6400: 10 fraction bits worth 1 each, so a nibble in bits
+// 0..3 gives 1024+u and in bits 4..7 gives 1024+16u -- both exact, and only
+// one shift per dword is needed:
+//   (w        & 0x000F000F) | 0x64006400 -> fp16 pair (1024+u0,   1024+u4)
+//   (w        & 0x00F000F0) | 0x64006400 -> fp16 pair (1024+16u1, 1024+16u5)
+//   ((w >> 8) & 0x000F000F) | 0x64006400 -> fp16 pair (1024+u2,   1024+u6)
+//   ((w >> 8) & 0x00F000F0) | 0x64006400 -> fp16 pair (1024+16u3, 1024+16u7)
+// with activations h (even positions) and h/16 (odd), rounded to fp16
+// (|h| < 65504; relative error <= 2^-11).  (1024+u)h = 1024h + uh and
+// (1024+16u)(h/16) = 64h + uh, so the products start from
+//   corr = -1032 * (h0 + h2 + h4 + h6) - 72 * (h1 + h3 + h5 + h7)
+// taken from the rounded values, which cancels the offsets exactly.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+__device__ __forceinline__ float f16_lo(uint32_t p) { return (float)__builtin_bit_cast(f16x2_t, p).x; }
+__device__ __forceinline__ float f16_hi(uint32_t p) { return (float)__builtin_bit_cast(f16x2_t, p).y; }
+
+// From 8 fp32 activations (rounded to fp16 here).
+__device__ __forceinline__ Slice8 make_slice_f16(const float v[8]) {
+  Slice8 s;
+  s.p0 = pack_f16(v[0], v[4]);
+  s.p1 = pack_f16(v[1] * 0.0625f, v[5] * 0.0625f);
+  s.p2 = pack_f16(v[2], v[6]);
+  s.p3 = pack_f16(v[3] * 0.0625f, v[7] * 0.0625f);
+  const float e = (f16_lo(s.p0) + f16_hi(s.p0)) + (f16_lo(s.p2) + f16_hi(s.p2));
+  const float o = (f16_lo(s.p1) + f16_hi(s.p1)) + (f16_lo(s.p3) + f16_hi(s.p3));
+  s.corr = -1032.0f * e - 1152.0f * o;  // odd terms are stored /16: -72 * 16
+  return s;
+}
+
+// acc + sum_e (1024+u_e or 1024+16u_e) * (h_e or h_e/16); started from
+// s.corr this is sum_e (u_e - 8) h_e.
+__device__ __forceinline__ float dot8_f16(uint32_t w, const Slice8& s, float acc) {
+  acc = dot2_f16((w & 0x000F000Fu) | 0x64006400u, s.p0, acc);
+  acc = dot2_f16((w & 0x00F000F0u) | 0x64006400u, s.p1, acc);
+  acc = dot2_f16(((w >> 8) & 0x000F000Fu) | 0x64006400u, s.p2, acc);
+  acc = dot2_f16(((w >> 8) & 0x00F000F0u) | 0x64006400u, s.p3, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float dot_piece_f16(uint4 q, const Slice8 xs[4], uint2 sc) {
+  float p = dot8_f16(q.x, xs[0], xs[0].corr) * f16_bits_to_f32(sc.x & 0xFFFFu);
+  p = fmaf(dot8_f16(q.y, xs[1], xs[1].corr), f16_bits_to_f32(sc.x >> 16), p);
+  p = fmaf(dot8_f16(q.z, xs[2], xs[2].corr), f16_bits_to_f32(sc.y & 0xFFFFu), p);
+  p = fmaf(dot8_f16(q.w, xs[3], xs[3].corr), f16_bits_to_f32(sc.y >> 16), p);
   return p;
 }
 

@@ -4,29 +4,32 @@
 // run ("Flint 40B: Best Mid Sized LLM", transcript 02:35).  The step is a
 // chain of dependent phases -- router GEMV, top-k, expert gate/up + SwiGLU,
 // down + combine -- and at one token each phase moves only a few MB, so the
-// cost is latency, not bandwidth.  On MI355X a kernel boundary in a graph
-// costs about 1.6 us and a counter-based grid barrier over 256 workgroups
-// about 3.7 us (same-address atomics serialize), so this kernel keeps every
-// workgroup resident (grid = one workgroup per CU) and passes data between
-// phases without atomics:
+// cost is latency, not bandwidth.  Measured on MI355X: a kernel boundary in
+// a graph costs about 1.6 us, a counter-based grid barrier over 256
+// workgroups about 3.7 us (same-address atomics serialize), and a coherent
+// store is seen by a polling workgroup about 0.6 us later.  So this kernel
+// keeps every workgroup resident (one per CU) and hands data between phases
+// as self-validating words, with no atomics and no flags:
 //
-//   router   each workgroup computes one router row (its 4 waves take a
-//            quarter each) and publishes the logit as a 64-bit word
-//            (epoch << 32 | value) with a coherent store;
-//   select   wave 0 of every workgroup polls the E tagged words until all
-//            carry this call's epoch, then runs the exact top-k itself (no
-//            second hand-off);
-//   experts  each wave issues its down-projection loads at once (the chosen
-//            experts are known now), then its gate/up rows; h = w_j *
-//            silu(g) * u goes out with coherent stores and the workgroup
-//            raises its flag (= epoch);
-//   down     wave 0 polls the G flags, the workgroup copies h into LDS, and
-//            each wave finishes its output rows from the prefetched weights.
+//   router   workgroup b computes router rows 4b..4b+3 (one per wave) and
+//            writes the 4 logits as (tag << 32 | value) words into its own
+//            128-byte line (one writer per line: words from different XCDs
+//            sharing a line serialize at the memory side);
+//   select   wave 0 of every workgroup polls the tagged logits until all
+//            carry this call's tag; every wave then runs the exact top-k
+//            rounds itself and issues its gate/up loads the moment its own
+//            expert is decided;
+//   experts  the workgroup turns its 16 values h = w_j * silu(g) * u into
+//            two ready-made fp16 dot slices and writes every slice word with
+//            the tag, then prefetches its down pieces;
+//   down     every workgroup polls all slice words straight into LDS until
+//            they all carry the tag (the down pieces arrive meanwhile) and
+//            finishes its output rows.
 //
-// The epoch is read from the workspace at the start and advanced by
-// workgroup 0 once every flag is up (by then every workgroup has read it),
-// so consecutive calls never see each other's tags.  Every wait is bounded:
-// on timeout the kernel sets the error word and finishes anyway.
+// The tag is this workgroup's call count + 1, kept per workgroup in the
+// workspace; all workgroups take part in every call, so their counts agree
+// and consecutive calls never accept each other's words.  Every wait is
+// bounded: on timeout the kernel sets the error word and finishes anyway.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -37,30 +40,29 @@
 namespace moe {
 
 constexpr unsigned kSpinLimit = 1u << 21;
+// Logits are published one 128-byte line per workgroup: words written by
+// workgroups on different XCDs into one line serialize at the memory side
+// (measured: all-to-all detection 2.2 us packed vs 1.3 us one line each).
+constexpr int kLineWords64 = 16;
 
 __device__ __forceinline__ void store_tagged(unsigned long long* p, float v, unsigned tag) {
   store_coherent(p, ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(v));
 }
-__device__ __forceinline__ void store_coherent_u32(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned load_coherent_u32(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Every poll issues all of its coherent loads before looking at any result,
+// so one poll costs one round trip to the coherence point, not one per load.
 
-// Every poll below issues all of its coherent loads before looking at any
-// result, so one poll costs one round trip to the coherence point (about
-// 0.6 us on MI355X), not one per load.
-
-// Wave-wide: wait until the E tagged logits carry `tag`; v receives them
-// (NaN mapped to -inf, entries past E to -inf).
+// Wave-wide: wait until the E tagged logits (4 per line) carry `tag`; v
+// receives them (NaN mapped to -inf, entries past E to -inf).
 template <int EPL>
 __device__ void poll_logits(const unsigned long long* lg, int E, unsigned tag, int lane, float v[EPL],
                             unsigned* error) {
   for (unsigned spin = 0;; ++spin) {
     unsigned long long t[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) t[i] = load_coherent(lg + min(lane + 64 * i, E - 1));
+    for (int i = 0; i < EPL; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+      t[i] = load_coherent(lg + (size_t)(e >> 2) * kLineWords64 + (e & 3));
+    }
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -77,29 +79,15 @@ __device__ void poll_logits(const unsigned long long* lg, int E, unsigned tag, i
   }
 }
 
-// Wave-wide: wait until flags[0..G) all equal `tag` (G even, <= 1024).
-__device__ void poll_flags(const unsigned* flags, int G, unsigned tag, int lane, unsigned* error) {
-  const unsigned long long* f2 = reinterpret_cast<const unsigned long long*>(flags);
-  const unsigned long long want = ((unsigned long long)tag << 32) | tag;
-  const int pairs = G / 2;
-  for (unsigned spin = 0;; ++spin) {
-    unsigned long long f[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) f[m] = load_coherent(f2 + min(lane + 64 * m, pairs - 1));
-    bool ok = true;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) ok = ok & (f[m] == want);
-    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return;
-    if (spin > kSpinLimit) {
-      if (lane == 0) atomicOr(error, 2u);
-      return;
-    }
-  }
+// Slice word j (= 5 * slice + field, slices in h order) sits in the lines of
+// the workgroup that produced it: wpw words per workgroup, lpw lines each.
+__device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
+  return (size_t)(j / wpw) * lpw * 16 + (j % wpw);
 }
 
 // D hidden, F expert width, KP top_k rounded up to a power of two, EPL
-// experts per lane in the top-k wave, RW waves per router row.
-template <int D, int F, int KP, int EPL, int RW>
+// experts per lane in the top-k wave.
+template <int D, int F, int KP, int EPL>
 __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
@@ -111,25 +99,31 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int RPLD = P < 64 ? 64 / P : 1;
   constexpr int NLD = LPRD > 4 ? LPRD : 4;
   constexpr int ROWS_W = (NLD / LPRD) * RPLD;
-  constexpr int NI = D / (RW * 256);  // router float4 per lane
-  static_assert(NL % LPRG == 0 && NI >= 1, "shape");
+  constexpr int NI = D / 256;        // router float4 per lane (one row per wave)
+  constexpr int ROWS_G = 64 * NL / CPR * 4;  // gate/up rows per workgroup (C2: 16)
+  static_assert(NL % LPRG == 0 && NI >= 1 && ROWS_G % 8 == 0, "shape");
 
-  extern __shared__ float s_h[];      // k * F
+  extern __shared__ unsigned s_sl[];  // k*F/8 slices x 5 words
   __shared__ int s_idx[16];
   __shared__ float s_w[16];
   __shared__ float s_part[4];
+  __shared__ float s_hv[ROWS_G];
+  __shared__ float s_lg[64 * EPL];
+  __shared__ unsigned s_pub[ROWS_G / 8 * 5];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int G = gridDim.x, W = 4 * G, wg = blockIdx.x * 4 + wid;
+  const int wg = blockIdx.x * 4 + wid;
   const int E = a.E, k = a.k;
-  const unsigned tag = load_coherent_u32(a.epoch) + 1u;
+  const unsigned tag = a.epoch[blockIdx.x] + 1u;  // this workgroup's own call count
+  const float bias = (a.router_b && wg < E) ? a.router_b[wg] : 0.f;
 
   // ---------------------------------------------------------------- router
-  {
-    const int row = wg / RW, part = wg % RW;
-    if (row < E) {
-      const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)row * D + part * (D / RW));
-      const uint2* xr = reinterpret_cast<const uint2*>(a.x + part * (D / RW));
+  // rows 4*b .. 4*b+3 in workgroup b, one per wave; the 4 logits go out as
+  // (tag, value) words in the workgroup's own 128-byte line.
+  if (blockIdx.x * 4 < E) {
+    if (wg < E) {
+      const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)wg * D);
+      const uint2* xr = reinterpret_cast<const uint2*>(a.x);
       float4 w[NI];
       uint2 q[NI];
 #pragma unroll
@@ -143,45 +137,159 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
         acc = fmaf(w[i].w, __uint_as_float(q[i].y & 0xFFFF0000u), acc);
       }
       acc = wave_sum(acc);
-      if (RW == 1) {
-        if (lane == 0) store_tagged(a.logits + row, acc + (a.router_b ? a.router_b[row] : 0.f), tag);
-      } else if (lane == 0) {
-        s_part[wid] = acc;
-      }
+      if (lane == 0) s_part[wid] = acc + bias;
     }
-    if (RW > 1) {
-      __syncthreads();
-      if (threadIdx.x < 4 / RW) {
-        const int r = (blockIdx.x * 4) / RW + threadIdx.x;
-        if (r < E) {
-          float sum = 0.f;
-#pragma unroll
-          for (int p = 0; p < RW; ++p) sum += s_part[threadIdx.x * RW + p];
-          store_tagged(a.logits + r, sum + (a.router_b ? a.router_b[r] : 0.f), tag);
-        }
-      }
-    }
+    __syncthreads();
+    if (threadIdx.x < 4 && blockIdx.x * 4 + (int)threadIdx.x < E)
+      store_tagged(a.logits + (size_t)blockIdx.x * kLineWords64 + threadIdx.x, s_part[threadIdx.x], tag);
   }
 
   // ---------------------------------------------------------------- select
+  // wave 0 polls the logits and shares them through LDS; then every wave
+  // runs the selection rounds itself and issues its gate/up loads as soon as
+  // its own slot is decided.  The softmax weights follow while the loads
+  // are in flight (they are needed only at the end of gate/up).
   if (wid == 0) {
-    float v[EPL];
-    poll_logits<EPL>(a.logits, E, tag, lane, v, a.error);
-    int se;
-    float sw;
-    topk_fast<EPL>(v, E, k, a.norm, lane, se, sw);
-    if (lane < k) {
-      s_idx[lane] = se;
-      s_w[lane] = sw;
-      if (blockIdx.x == 0) {
-        if (a.idx_out) a.idx_out[lane] = se;
-        if (a.w_out) a.w_out[lane] = sw;
-      }
+    float v0[EPL];
+    poll_logits<EPL>(a.logits, E, tag, lane, v0, a.error);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s_lg[lane + 64 * i] = v0[i];
+  }
+  __syncthreads();
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) v[i] = s_lg[lane + 64 * i];
+
+  const int wpe = (F * CPR) / (64 * NL);  // waves per chosen expert
+  const bool has_gate = wg < k * wpe;
+  const int gslot = has_gate ? wg / wpe : -1;
+  const int c0 = has_gate ? (wg - gslot * wpe) * 64 * NL : 0;
+  uint4 qg[NL], qu[NL];
+  uint2 sg[NL], su[NL];
+  auto load_gate = [&](int e_raw) {
+    const int e = min(max(e_raw, 0), E - 1);
+    const size_t mat = (size_t)F * CPR;
+    const uint4* gp = reinterpret_cast<const uint4*>(a.gate_q) + (size_t)e * mat;
+    const uint4* up = reinterpret_cast<const uint4*>(a.up_q) + (size_t)e * mat;
+    const uint16_t* gsb = a.gate_s + (size_t)e * mat;
+    const uint16_t* usb = a.up_s + (size_t)e * mat;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int c = c0 + 64 * n + lane;
+      qg[n] = gp[c];
+      qu[n] = up[c];
+      const size_t so = (size_t)(c / CPR) * CPR + ((c % CPR) & ~3);
+      sg[n] = *reinterpret_cast<const uint2*>(gsb + so);
+      su[n] = *reinterpret_cast<const uint2*>(usb + so);
+    }
+  };
+
+  int se = 0;
+  bool exact = false;
+  {
+    const int ib = E <= 2 ? 1 : 32 - __clz(E - 1);
+    const uint32_t imask = (1u << ib) - 1u;
+    uint32_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      key[i] = lane + 64 * i < E ? ((ordered_bits(v[i]) & ~imask) | (imask - (uint32_t)(lane + 64 * i))) : 0u;
+    uint32_t prev = 0;
+    bool close = false;
+    for (int r = 0; r <= k && r < E; ++r) {
+      uint32_t loc = key[0];
+#pragma unroll
+      for (int i = 1; i < EPL; ++i) loc = max(loc, key[i]);
+      const uint32_t M = wave_max_u32(loc);
+      close = close || (r > 0 && ((M ^ prev) & ~imask) == 0u);
+      prev = M;
+      if (r == k) break;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) key[i] = key[i] == M ? 0u : key[i];
+      const int e_r = (int)(imask - (M & imask));
+      if (lane == r) se = e_r;
+      if (r == gslot) load_gate(e_r);
+    }
+    if (close) {  // picks that agree in their top bits: redo exactly, reload
+      float sw;
+      topk_exact<EPL>(v, E, k, a.norm, lane, se, sw);
+      if (wid == 0 && lane < k) s_w[lane] = sw;
+      exact = true;
+      const int e_slot = __shfl(se, max(gslot, 0), 64);
+      if (has_gate) load_gate(e_slot);
+    }
+  }
+  if (wid == 0) {
+    if (lane < k) s_idx[lane] = se;
+    if (!exact) {
+      const float sw = topk_weight<EPL>(v, E, k, a.norm, lane, se);
+      if (lane < k) s_w[lane] = sw;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (blockIdx.x == 0 && lane < k) {
+      if (a.idx_out) a.idx_out[lane] = se;
+      if (a.w_out) a.w_out[lane] = s_w[lane];
     }
   }
   __syncthreads();
 
+  // ---------------------------------------------------------------- gate/up + SwiGLU
+  if (has_gate) {
+    const float wj = s_w[gslot];
+    Slice8 xs[XS][4];
+    const uint4* xp = reinterpret_cast<const uint4*>(a.x);
+#pragma unroll
+    for (int s = 0; s < XS; ++s) {
+      const int c = CPR > 64 ? 64 * s + lane : lane % CPR;
+      const int base = 128 * (c >> 2) + 8 * (c & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xs[s][j] = make_slice_bf16(xp[(base + 32 * j) >> 3]);
+    }
+    float ag = 0.f, au = 0.f;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int s = CPR > 64 ? n % XS : 0;
+      ag += dot_piece(qg[n], xs[s], sg[n]);
+      au += dot_piece(qu[n], xs[s], su[n]);
+      if (n % LPRG == LPRG - 1) {
+        // row within this workgroup's ROWS_G consecutive rows of slot gslot
+        if constexpr (CPR >= 64) {
+          const float g = wave_sum(ag), u = wave_sum(au);
+          if (lane == 0) s_hv[(wid * 64 * NL + 64 * n) / CPR] = wj * silu(g) * u;
+        } else {
+          const float g = seg_sum<(CPR < 64 ? CPR : 64)>(ag), u = seg_sum<(CPR < 64 ? CPR : 64)>(au);
+          if (lane % CPR == 0) s_hv[(wid * 64 * NL + 64 * n + lane) / CPR] = wj * silu(g) * u;
+        }
+        ag = au = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // publish this workgroup's rows as ready-made fp16 dot slices, one per 8
+  // consecutive h values, every 64-bit word carrying the tag; the
+  // workgroup's words fill its own 128-byte line(s), written by consecutive
+  // lanes of one store instruction
+  constexpr int SPW = ROWS_G / 8;          // slices per workgroup
+  constexpr int WPW = SPW * 5;             // words per workgroup
+  constexpr int LPW = (WPW + 15) / 16;     // 128-byte lines per workgroup
+  const bool producer = blockIdx.x * 4 < k * wpe;
+  if (producer && threadIdx.x < SPW) {
+    float hv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = s_hv[8 * threadIdx.x + e];
+    const Slice8 sl = make_slice_f16(hv);
+    s_pub[5 * threadIdx.x + 0] = sl.p0, s_pub[5 * threadIdx.x + 1] = sl.p1, s_pub[5 * threadIdx.x + 2] = sl.p2;
+    s_pub[5 * threadIdx.x + 3] = sl.p3, s_pub[5 * threadIdx.x + 4] = __float_as_uint(sl.corr);
+  }
+  __syncthreads();
+  if (producer && wid == 0) {
+    unsigned long long* line = a.hrec + (size_t)blockIdx.x * LPW * 16;  // producer index == workgroup index
+    for (int w0 = 0; w0 < WPW; w0 += 64)
+      if (w0 + lane < WPW) store_coherent(line + w0 + lane, ((unsigned long long)tag << 32) | s_pub[w0 + lane]);
+  }
+
   // ---------------------------------------------------------------- down prefetch
+  // issued now so that the 4.7 MB of down pieces stream in while the h
+  // hand-off is in flight, instead of competing with the gate/up loads
   const bool has_down = wg < D / ROWS_W;
   const int r0 = wg * ROWS_W;
   int cc[LPRD], dslot[LPRD];
@@ -209,109 +317,54 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     }
   }
 
-  // ---------------------------------------------------------------- gate/up
+  // ---------------------------------------------------------------- collect h
+  // all k*F/8 slices straight into LDS; a word is taken once it carries the
+  // tag, and later polls re-read only the words still missing
   {
-    const int wpe = (F * CPR) / (64 * NL);  // waves per chosen expert
-    if (wg < k * wpe) {
-      const int slot = wg / wpe;
-      const int c0 = (wg - slot * wpe) * 64 * NL;
-      const int e = min(max(s_idx[slot], 0), E - 1);
-      const float wj = s_w[slot];
-      const size_t mat = (size_t)F * CPR;
-      const uint4* gp = reinterpret_cast<const uint4*>(a.gate_q) + (size_t)e * mat;
-      const uint4* up = reinterpret_cast<const uint4*>(a.up_q) + (size_t)e * mat;
-      const uint16_t* gsb = a.gate_s + (size_t)e * mat;
-      const uint16_t* usb = a.up_s + (size_t)e * mat;
-      uint4 qg[NL], qu[NL];
-      uint2 sg[NL], su[NL];
+    constexpr int NR = (KP * F / 8 * 5 + 255) / 256;
+    const int nw = k * (F / 8) * 5;  // slice words; word j = 5 * slice + field
+    unsigned missing = 0;
 #pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int c = c0 + 64 * n + lane;
-        qg[n] = gp[c];
-        qu[n] = up[c];
-        const size_t so = (size_t)(c / CPR) * CPR + ((c % CPR) & ~3);
-        sg[n] = *reinterpret_cast<const uint2*>(gsb + so);
-        su[n] = *reinterpret_cast<const uint2*>(usb + so);
-      }
-      Slice8 xs[XS][4];
-      const uint4* xp = reinterpret_cast<const uint4*>(a.x);
+    for (int m = 0; m < NR; ++m) missing |= (threadIdx.x + 256 * m < (unsigned)nw ? 1u : 0u) << m;
+    for (unsigned spin = 0;; ++spin) {
+      unsigned long long r[NR];
 #pragma unroll
-      for (int s = 0; s < XS; ++s) {
-        const int c = CPR > 64 ? 64 * s + lane : lane % CPR;
-        const int base = 128 * (c >> 2) + 8 * (c & 3);
+      for (int m = 0; m < NR; ++m)
+        r[m] = (missing >> m) & 1u ? load_coherent(a.hrec + hrec_index(threadIdx.x + 256 * m, WPW, LPW)) : 0ull;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xs[s][j] = make_slice_bf16(xp[(base + 32 * j) >> 3]);
-      }
-      float* hout = a.h + (size_t)slot * F;
-      float ag = 0.f, au = 0.f;
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int s = CPR > 64 ? n % XS : 0;
-        ag += dot_piece(qg[n], xs[s], sg[n]);
-        au += dot_piece(qu[n], xs[s], su[n]);
-        if (n % LPRG == LPRG - 1) {
-          if constexpr (CPR >= 64) {
-            const float g = wave_sum(ag), u = wave_sum(au);
-            if (lane == 0) store_coherent(hout + (c0 + 64 * n) / CPR, wj * silu(g) * u);
-          } else {
-            const float g = seg_sum<(CPR < 64 ? CPR : 64)>(ag), u = seg_sum<(CPR < 64 ? CPR : 64)>(au);
-            if (lane % CPR == 0) store_coherent(hout + (c0 + 64 * n + lane) / CPR, wj * silu(g) * u);
-          }
-          ag = au = 0.f;
+      for (int m = 0; m < NR; ++m) {
+        if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag) {
+          s_sl[threadIdx.x + 256 * m] = (uint32_t)r[m];
+          missing &= ~(1u << m);
         }
       }
-    }
-  }
-  wait_vm();
-  __syncthreads();
-  if (threadIdx.x == 0) store_coherent_u32(a.flags + blockIdx.x, tag);
-
-  // ---------------------------------------------------------------- down
-  if (wid == 0) {
-    poll_flags(a.flags, G, tag, lane, a.error);
-    if (blockIdx.x == 0 && lane == 0) store_coherent_u32(a.epoch, tag);  // every workgroup has read it
-  }
-  __syncthreads();
-  {
-    // all loads first (one round trip), then the LDS stores
-    constexpr int NH = (KP * F / 2 + 255) / 256;
-    const int nh2 = k * F / 2;
-    const unsigned long long* hsrc = reinterpret_cast<const unsigned long long*>(a.h);
-    unsigned long long hv[NH];
-#pragma unroll
-    for (int m = 0; m < NH; ++m) hv[m] = load_coherent(hsrc + min((int)threadIdx.x + 256 * m, nh2 - 1));
-#pragma unroll
-    for (int m = 0; m < NH; ++m) {
-      const int j = threadIdx.x + 256 * m;
-      if (j < nh2) {
-        s_h[2 * j] = __uint_as_float((uint32_t)hv[m]);
-        s_h[2 * j + 1] = __uint_as_float((uint32_t)(hv[m] >> 32));
+      if (__syncthreads_or(missing != 0) == 0) break;
+      if (spin > kSpinLimit) {
+        if (threadIdx.x == 0) atomicOr(a.error, 2u);
+        break;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
+
+  // ---------------------------------------------------------------- down + combine
   if (has_down) {
-    Slice8 hh[LPRD][4], hl[LPRD][4];
+    Slice8 hs8[LPRD][4];
 #pragma unroll
     for (int m = 0; m < LPRD; ++m) {
-      const int base = 128 * (cc[m] >> 2) + 8 * (cc[m] & 3);
-      const float* hs = s_h + (act[m] ? dslot[m] : 0) * F;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 lo4 = *reinterpret_cast<const float4*>(hs + base + 32 * j);
-        const float4 hi4 = *reinterpret_cast<const float4*>(hs + base + 32 * j + 4);
-        const bool on = act[m];
-        float v[8];
-        v[0] = on ? lo4.x : 0.f, v[1] = on ? lo4.y : 0.f, v[2] = on ? lo4.z : 0.f, v[3] = on ? lo4.w : 0.f;
-        v[4] = on ? hi4.x : 0.f, v[5] = on ? hi4.y : 0.f, v[6] = on ? hi4.z : 0.f, v[7] = on ? hi4.w : 0.f;
-        make_slice_hilo(v, hh[m][j], hl[m][j]);
+        const int c = (act[m] ? dslot[m] : 0) * (F / 8) + 16 * (cc[m] >> 2) + 4 * j + (cc[m] & 3);
+        const unsigned* sp = s_sl + 5 * c;
+        hs8[m][j] = act[m] ? Slice8{sp[0], sp[1], sp[2], sp[3], __uint_as_float(sp[4])}
+                           : Slice8{0u, 0u, 0u, 0u, 0.f};
       }
     }
     float acc = 0.f;
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int m = n % LPRD;
-      acc += dot_piece_hilo(qd[n], hh[m], hl[m], sd[n]);
+      acc += dot_piece_f16(qd[n], hs8[m], sd[n]);
       if (n % LPRD == LPRD - 1) {
         if constexpr (P >= 64) {
           const float v = wave_sum(acc);
@@ -324,44 +377,37 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       }
     }
   }
+  if (threadIdx.x == 0) a.epoch[blockIdx.x] = tag;
 }
 
 // ---------------------------------------------------------------- host side
 
-template <int D, int F, int KP, int EPL, int RW>
+template <int D, int F, int KP, int EPL>
 static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
-  const size_t lds = (size_t)a.k * F * sizeof(float);
-  hipLaunchKernelGGL((k_layer<D, F, KP, EPL, RW>), dim3(G), dim3(256), lds, s, a);
+  const size_t lds = (size_t)a.k * (F / 8) * 5 * sizeof(unsigned);
+  hipLaunchKernelGGL((k_layer<D, F, KP, EPL>), dim3(G), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-template <int D, int F, int KP, int EPL>
-static hipError_t layer_rw(const FusedArgs& a, int G, int rw, hipStream_t s) {
-  if constexpr (D >= 1024) {
-    if (rw == 4) return layer_launch<D, F, KP, EPL, 4>(a, G, s);
-  }
-  return layer_launch<D, F, KP, EPL, 1>(a, G, s);
-}
-
 template <int D, int F, int KP>
-static hipError_t layer_epl(const FusedArgs& a, int G, int rw, hipStream_t s) {
-  if (a.E <= 64) return layer_rw<D, F, KP, 1>(a, G, rw, s);
-  if (a.E <= 128) return layer_rw<D, F, KP, 2>(a, G, rw, s);
-  return layer_rw<D, F, KP, 4>(a, G, rw, s);
+static hipError_t layer_epl(const FusedArgs& a, int G, hipStream_t s) {
+  if (a.E <= 64) return layer_launch<D, F, KP, 1>(a, G, s);
+  if (a.E <= 128) return layer_launch<D, F, KP, 2>(a, G, s);
+  return layer_launch<D, F, KP, 4>(a, G, s);
 }
 
 template <int D, int F>
-static hipError_t layer_kp(const FusedArgs& a, int G, int rw, hipStream_t s) {
+static hipError_t layer_kp(const FusedArgs& a, int G, hipStream_t s) {
   const int k = a.k;
-  if (k <= 1) return layer_epl<D, F, 1>(a, G, rw, s);
-  if (k <= 2) return layer_epl<D, F, 2>(a, G, rw, s);
-  if (k <= 4) return layer_epl<D, F, 4>(a, G, rw, s);
-  if (k <= 8) return layer_epl<D, F, 8>(a, G, rw, s);
-  return layer_epl<D, F, 16>(a, G, rw, s);
+  if (k <= 1) return layer_epl<D, F, 1>(a, G, s);
+  if (k <= 2) return layer_epl<D, F, 2>(a, G, s);
+  if (k <= 4) return layer_epl<D, F, 4>(a, G, s);
+  if (k <= 8) return layer_epl<D, F, 8>(a, G, s);
+  return layer_epl<D, F, 16>(a, G, s);
 }
 
 // Work each wave takes in the fused kernel must fit one unit per wave.
-static bool fits(int d, int f, int E, int k, int G, int& rw) {
+static bool fits(int d, int f, int E, int k, int G) {
   const int W = 4 * G;
   const int cpr = d / 32, cprf = f / 32;
   if ((long)k * f * cpr / 256 > W) return false;  // gate/up units (4 pieces per lane)
@@ -372,17 +418,14 @@ static bool fits(int d, int f, int E, int k, int G, int& rw) {
   const int nld = lprd > 4 ? lprd : 4;
   const int rows_w = (nld / lprd) * rpld;
   if (d / rows_w > W) return false;
-  if ((size_t)k * f * sizeof(float) > 64 * 1024) return false;
-  if (E > 256) return false;
-  rw = (d >= 1024 && E <= G) ? 4 : 1;
-  if (E * rw > W) return false;
+  if ((size_t)k * (f / 8) * 5 * sizeof(unsigned) > 64 * 1024) return false;
+  if (E > 256 || E > W) return false;
   return true;
 }
 
 bool fused_layer_supported(int d, int f, int E, int k, int G) {
-  int rw;
   if (!((d == 256 && f == 128) || (d == 2048 && f == 512))) return false;
-  return fits(d, f, E, k, G, rw);
+  return fits(d, f, E, k, G);
 }
 
 int fused_grid() {
@@ -392,17 +435,16 @@ int fused_grid() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 0;
-    g = cus > kMaxFusedGrid ? kMaxFusedGrid : cus & ~1;  // even: flags are polled in pairs
+    g = cus > kMaxFusedGrid ? kMaxFusedGrid : cus;
   }
   return g;
 }
 
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s) {
   const int G = fused_grid();
-  int rw;
-  if (G <= 0 || !fits(d, f, a.E, a.k, G, rw)) return hipErrorInvalidValue;
-  if (d == 256 && f == 128) return layer_kp<256, 128>(a, G, rw, s);
-  if (d == 2048 && f == 512) return layer_kp<2048, 512>(a, G, rw, s);
+  if (G <= 0 || !fits(d, f, a.E, a.k, G)) return hipErrorInvalidValue;
+  if (d == 256 && f == 128) return layer_kp<256, 128>(a, G, s);
+  if (d == 2048 && f == 512) return layer_kp<2048, 512>(a, G, s);
   return hipErrorInvalidValue;
 }
 

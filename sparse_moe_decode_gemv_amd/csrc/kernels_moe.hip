@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
     }
   }
 
-  Slice8 hh[LPR][4], hl[LPR][4];
+  Slice8 hs8[LPR][4];
 #pragma unroll
   for (int m = 0; m < LPR; ++m) {
     const int base = 128 * (cc[m] >> 2) + 8 * (cc[m] & 3);
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
       const bool on = act[m];  // padding slots contribute exact zeros
       v[0] = on ? a.x : 0.f, v[1] = on ? a.y : 0.f, v[2] = on ? a.z : 0.f, v[3] = on ? a.w : 0.f;
       v[4] = on ? b.x : 0.f, v[5] = on ? b.y : 0.f, v[6] = on ? b.z : 0.f, v[7] = on ? b.w : 0.f;
-      make_slice_hilo(v, hh[m][j], hl[m][j]);
+      hs8[m][j] = make_slice_f16(v);
     }
   }
 
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
     const int m = n % LPR;
-    acc += dot_piece_hilo(q[n], hh[m], hl[m], sc[n]);
+    acc += dot_piece_f16(q[n], hs8[m], sc[n]);
     if (n % LPR == LPR - 1) {
       float v;
       int row;

@@ -26,9 +26,9 @@ struct LayerArgs {
   float* h;              // [T][k][f]  w_j * silu(g) * u
   uint16_t* xnorm;       // [T][d]     normalized activation (stack)
   // single-launch step (T = 1)
-  unsigned long long* tagged_logits;  // [E]  (epoch << 32 | logit bits)
-  unsigned* flags;                    // [kMaxFusedGrid] per-workgroup epoch flags
-  unsigned* epoch;                    // [1]  calls completed
+  unsigned long long* tagged_logits;  // ceil(E/4) lines of 128 B: (epoch << 32 | logit bits)
+  unsigned long long* hrec;           // [k*f/8][5] (epoch << 32 | fp16 slice word)
+  unsigned* epoch;                    // [kMaxFusedGrid] calls completed, per workgroup
   unsigned* error;                    // [1]  bit 0/1: a bounded wait timed out
 };
 
@@ -48,16 +48,15 @@ struct FusedArgs {
   float* y;              // [d]
   int32_t* idx_out;      // [k] or NULL
   float* w_out;          // [k] or NULL
-  unsigned long long* logits;
-  float* h;
-  unsigned* flags;
-  unsigned* epoch;
+  unsigned long long* logits;  // tagged logits, 4 per 128-byte line
+  unsigned long long* hrec;    // tagged fp16 slices of h
+  unsigned* epoch;             // per-workgroup call counts
   unsigned* error;
   int E, k, norm;
 };
 
 // The whole 1-token step in one launch, for the shapes it is built for
-// (d, f) in {(256, 128), (2048, 512)}, E <= 256, k*f*4 <= 64 KiB.
+// (d, f) in {(256, 128), (2048, 512)}, E <= 256.
 bool fused_layer_supported(int d, int f, int E, int k, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);

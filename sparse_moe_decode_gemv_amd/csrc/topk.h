@@ -70,20 +70,13 @@ __device__ __forceinline__ void topk_exact(const float v[EPL], int E, int k, int
   sel_w = p / den;
 }
 
-// Faster selection with the same result as topk_exact (see above).
+// Weights of the chosen experts: lane r < k holds choice e, its logit is
+// fetched from the lane that holds it.
 template <int EPL>
-__device__ __forceinline__ void topk_fast(const float v[EPL], int E, int k, int norm, int lane, int& sel_e,
-                                          float& sel_w) {
-  const int ib = E <= 2 ? 1 : 32 - __clz(E - 1);
-  const uint32_t imask = (1u << ib) - 1u;
-  uint32_t key[EPL];
+__device__ __forceinline__ float topk_weight(const float v[EPL], int E, int k, int norm, int lane, int my_e) {
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const bool valid = lane + 64 * i < E;
-    key[i] = valid ? ((ordered_bits(v[i]) & ~imask) | (imask - (uint32_t)(lane + 64 * i))) : 0u;
-    m = valid ? fmaxf(m, v[i]) : m;
-  }
+  for (int i = 0; i < EPL; ++i) m = lane + 64 * i < E ? fmaxf(m, v[i]) : m;
   m = wave_max(m);
   float z = 0.f;
   if (!norm) {
@@ -91,6 +84,28 @@ __device__ __forceinline__ void topk_fast(const float v[EPL], int E, int k, int 
     for (int i = 0; i < EPL; ++i) z += lane + 64 * i < E ? expf(v[i] - m) : 0.f;
     z = wave_sum(z);
   }
+  float l_sel = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const float c = __shfl(v[i], my_e & 63, 64);
+    l_sel = (my_e >> 6) == i ? c : l_sel;
+  }
+  const float p = lane < k ? expf(l_sel - m) : 0.f;
+  const float den = norm ? wave_sum(p) : z;
+  return p / den;
+}
+
+// The k choices only (lane r < k gets choice r), same result as topk_exact.
+// Returns false when two picks agree in their top bits: the caller must then
+// use topk_exact.
+template <int EPL>
+__device__ __forceinline__ bool topk_select_fast(const float v[EPL], int E, int k, int lane, int& sel_e) {
+  const int ib = E <= 2 ? 1 : 32 - __clz(E - 1);
+  const uint32_t imask = (1u << ib) - 1u;
+  uint32_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    key[i] = lane + 64 * i < E ? ((ordered_bits(v[i]) & ~imask) | (imask - (uint32_t)(lane + 64 * i))) : 0u;
   int my_e = 0;
   uint32_t prev = 0;
   bool close = false;
@@ -106,21 +121,19 @@ __device__ __forceinline__ void topk_fast(const float v[EPL], int E, int k, int 
     for (int i = 0; i < EPL; ++i) key[i] = key[i] == M ? 0u : key[i];
     if (lane == r) my_e = (int)(imask - (M & imask));
   }
-  if (close) {  // logits agreeing in their top bits: compare full values
+  sel_e = my_e;
+  return !close;
+}
+
+// Faster selection with the same result as topk_exact (see above).
+template <int EPL>
+__device__ __forceinline__ void topk_fast(const float v[EPL], int E, int k, int norm, int lane, int& sel_e,
+                                          float& sel_w) {
+  if (!topk_select_fast<EPL>(v, E, k, lane, sel_e)) {
     topk_exact<EPL>(v, E, k, norm, lane, sel_e, sel_w);
     return;
   }
-  // this lane's pick: fetch its exact logit from the lane that holds it
-  float l_sel = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const float c = __shfl(v[i], my_e & 63, 64);
-    l_sel = (my_e >> 6) == i ? c : l_sel;
-  }
-  const float p = lane < k ? expf(l_sel - m) : 0.f;
-  const float den = norm ? wave_sum(p) : z;
-  sel_e = my_e;
-  sel_w = p / den;
+  sel_w = topk_weight<EPL>(v, E, k, norm, lane, sel_e);
 }
 
 }  // namespace moe

@@ -92,3 +92,69 @@ def test_identity_on_random_codes_and_activations():
         acc = acc + dec[p][0] * (x[:, a] * f) + dec[p][1] * (x[:, b] * f)
     want = ((u.astype(np.int64) - 8) * x).sum(axis=1)
     np.testing.assert_allclose(acc, want, rtol=0, atol=1e-9 * np.abs(x).sum(axis=1).max())
+
+
+# ---------------------------------------------------------------- fp16 variant
+
+
+def fp16_constants():
+    src = open(HDR).read()
+    body = src[src.index("float dot8_f16("):]
+    body = body[:body.index("return acc;")]
+    pairs = [(int(m.group(1) or 0), int(m.group(2), 16), int(m.group(3), 16), int(m.group(4))) for m in
+             re.finditer(r"dot2_f16\(\(+w(?: >> (\d+)\))? ?& (0x[0-9A-Fa-f]+)u\) \| (0x[0-9A-Fa-f]+)u, s\.p(\d)", body)]
+    mk = src[src.index("make_slice_f16(const float v[8])"):]
+    mk = mk[:mk.index("return s;")]
+    found = re.findall(r"s\.p(\d) = pack_f16\(v\[\d\] \* ([0-9.]+)f, v\[\d\] \* ([0-9.]+)f\)", mk)
+    assert all(a == b for _, a, b in found)
+    scale = {int(p): float(a) for p, a, _ in found}
+    cm = re.search(r"s\.corr = -([0-9.]+)f \* e - ([0-9.]+)f \* o;", mk)
+    assert len(pairs) == 4 and cm and sorted(scale) == [1, 3], "fp16 helpers no longer match the expected form"
+    return pairs, scale, float(cm.group(1)), float(cm.group(2))
+
+
+def f16_value(bits16):
+    return np.asarray(bits16, np.uint16).view(np.float16).astype(np.float64)
+
+
+def test_fp16_every_code_at_every_position_decodes_exactly():
+    pairs, scale, _, _ = fp16_constants()
+    for e in range(8):
+        u = np.zeros((16, 8), np.uint32)
+        u[:, e] = np.arange(16)
+        w = (u << (4 * np.arange(8, dtype=np.uint32))).sum(axis=1).astype(np.uint32)
+        p = [q for q, (a, b) in ELEMS.items() if e in (a, b)][0]
+        shift, mask, magic, _ = [t for t in pairs if t[3] == p][0]
+        v = ((w >> np.uint32(shift)) & np.uint32(mask)) | np.uint32(magic)
+        half = v & 0xFFFF if ELEMS[p][0] == e else v >> 16
+        np.testing.assert_array_equal(f16_value(half), 1024 + np.arange(16) / scale.get(p, 1.0))
+
+
+def test_fp16_identity_on_random_codes_and_activations():
+    pairs, scale, c_even, c_odd = fp16_constants()
+    rng = np.random.default_rng(6)
+    n = 20000
+    u = rng.integers(0, 16, size=(n, 8)).astype(np.uint32)
+    w = (u << (4 * np.arange(8, dtype=np.uint32))).sum(axis=1).astype(np.uint32)
+    h = rng.standard_normal((n, 8))
+    # activations as the kernel rounds them: fp16 of h (even) and of h*scale (odd)
+    stored = np.empty_like(h)
+    for p, (a, b) in ELEMS.items():
+        f = scale.get(p, 1.0)
+        stored[:, a] = (h[:, a] * f).astype(np.float16).astype(np.float64)
+        stored[:, b] = (h[:, b] * f).astype(np.float16).astype(np.float64)
+    even = stored[:, [0, 2, 4, 6]].sum(axis=1)
+    odd = stored[:, [1, 3, 5, 7]].sum(axis=1)
+    acc = -c_even * even - c_odd * odd
+    for shift, mask, magic, p in pairs:
+        v = ((w >> np.uint32(shift)) & np.uint32(mask)) | np.uint32(magic)
+        a, b = ELEMS[p]
+        acc = acc + f16_value(v & 0xFFFF) * stored[:, a] + f16_value(v >> 16) * stored[:, b]
+    h_eff = stored.copy()
+    for p, (a, b) in ELEMS.items():
+        h_eff[:, a] /= scale.get(p, 1.0)
+        h_eff[:, b] /= scale.get(p, 1.0)
+    want = ((u.astype(np.int64) - 8) * h_eff).sum(axis=1)
+    np.testing.assert_allclose(acc, want, rtol=0, atol=1e-9 * np.abs(h_eff).sum(axis=1).max())
+    # and the fp16 rounding of h stays within 2^-11 relative of the fp32 value
+    assert np.all(np.abs(h_eff - h) <= np.abs(h) * 2.0 ** -11 + 2.0 ** -24 * 16)
