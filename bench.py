@@ -32,6 +32,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCES = ["sparse_moe_decode_gemv_amd/csrc/kernels_layer.hip", "sparse_moe_decode_gemv_amd/csrc/device_common.h",
+                  "sparse_moe_decode_gemv_amd/csrc/topk.h"]
 
 
 def log(*a):
@@ -76,6 +78,62 @@ def time_graph(fn, steps, warmup, stream):
         end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / reps, g
+
+
+def time_launches(fn, steps, stream):
+    """Average duration of the launch each `fn(i)` enqueues, from HIP event
+    pairs recorded around every launch inside one captured graph (no host
+    gaps); None if the runtime rejects event records in a capture."""
+    import torch
+    # external=True makes each record a real event-record node of the graph
+    # (otherwise a record inside a capture only orders streams).
+    starts = [torch.cuda.Event(enable_timing=True, external=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True, external=True) for _ in range(steps)]
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                starts[i].record(stream)
+                fn(i)
+                ends[i].record(stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = [starts[i].elapsed_time(ends[i]) for i in range(steps)]
+    except Exception as e:  # noqa: BLE001
+        log(f"event timing inside a graph unavailable: {e!r}")
+        return None
+    ts.sort()
+    return dict(mean_us=sum(ts) / len(ts) * 1e3, median_us=ts[len(ts) // 2] * 1e3, p10_us=ts[len(ts) // 10] * 1e3,
+                p90_us=ts[len(ts) * 9 // 10] * 1e3)
+
+
+def traffic_from_profile(kernel_sources, name):
+    """HBM bytes per launch measured with rocprofv3 counters and recorded in
+    profiles/<name>; None unless the recorded source hash matches the kernel
+    sources as they are now."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for src in kernel_sources:
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            h.update(fh.read())
+    rec = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def time_eager(fn, steps, warmup, stream):
@@ -125,6 +183,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extras", action="store_true", help="skip stack, LM head and CPU legs")
     ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -141,6 +201,15 @@ def main():
     M.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
     cfg = synth.LAYER
     d, f, E, k = cfg.d, cfg.f, cfg.E, cfg.k
     P = args.pool
@@ -182,7 +251,9 @@ def main():
 
     by = layer_bytes(d, f, E, k)
     step_us = ms_per_step * 1e3
-    achieved = by["b_alg"] / (step_us * 1e-6) / 1e9
+    kt = time_launches(step, min(K, 196), stream)
+    kernel_us = kt["mean_us"] if kt else step_us
+    achieved = by["b_alg"] / (kernel_us * 1e-6) / 1e9
     out = {
         "metric": "MoE-layer decode tokens/s at 1 token + achieved HBM GB/s (% of peak)",
         "value": round(value, 1),
@@ -200,10 +271,14 @@ def main():
                                f"rotating over {P} distinct layers, fresh x per step",
                    "d": d, "f": f, "experts": E, "top_k": k, "tokens_per_step": 1, "pool_layers": P,
                    "launch": "eager" if total_s == eager_s else "hip-graph"},
-        "roofline": {"bound": "hbm", "kernel": "moe layer step (router, gate/up, down kernels)",
+        "roofline": {"bound": "hbm", "kernel": "k_layer (whole 1-token layer step, one launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": by["b_alg"]},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profile(KERNEL_SOURCES, "traffic_k_layer_flagship.txt"),
+                     "bytes_per_launch": by["b_alg"],
+                     "launch_us": round(kernel_us, 3),
+                     "launch_timing": "HIP event pairs around each launch inside a graph" if kt
+                     else "graph replay time / steps (event pairs unavailable)"},
         "bytes_per_step": by,
         "gbs_on_int4_weights": round(by["b_q"] / (step_us * 1e-6) / 1e9, 1),
         "frac_on_int4_weights": round(by["b_q"] / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
