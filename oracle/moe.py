@@ -141,6 +141,21 @@ def moe_forward(layer: Layer, x_bits: np.ndarray, k: int, norm_topk: bool = True
     return dict(y=y, y32=f64_to_f32(y), idx=S, w=w, logits=l)
 
 
+def moe_forward_on_set(layer: Layer, x_bits: np.ndarray, S, norm_topk: bool = True) -> dict:
+    """One token with the chosen set S given instead of selected: the weights
+    are the softmax over all E experts restricted to S (renormalized over S
+    when norm_topk), the rest as in moe_forward.  Used where another
+    selection of equal-to-rounding logits is also correct."""
+    x = bf16_to_f64(x_bits)
+    l = router_logits(layer, x)
+    p = softmax(l)
+    S = np.asarray(S, dtype=np.int64)
+    w = p[S] / p[S].sum() if norm_topk else p[S]
+    outs = {int(e): expert_forward(*layer.expert(int(e)), x) for e in S}
+    y = combine(S, w, outs)
+    return dict(y=y, y32=f64_to_f32(y), idx=S, w=w, logits=l)
+
+
 def moe_forward_tokens(layer: Layer, X_bits: np.ndarray, k: int, norm_topk: bool = True) -> dict:
     """T tokens, each routed on its own (row t of X is token t)."""
     rs = [moe_forward(layer, X_bits[t], k, norm_topk) for t in range(X_bits.shape[0])]

@@ -1,0 +1,118 @@
+"""GPU parity of the pre-norm stack of MoE layers (moe_decode_stack_forward)
+against the fp64 oracle, checked layer by layer with teacher forcing: the
+oracle re-runs layer l from the GPU's own x_l.
+
+Only x_0 is margin-conditioned; deeper layers cannot be.  Where the
+oracle's gap between the k-th and (k+1)-th logit at a layer is at least the
+margin, the chosen experts must match exactly; below it the GPU's set is
+accepted if each of its logits is within 1e-4 of the oracle's k-th, and
+y_l is then checked against the oracle evaluated on the GPU's set."""
+import numpy as np
+import pytest
+
+import synth
+import sparse_moe_decode_gemv_amd as M
+from gpu_common import Y_TOL, as_i16, device, tokens
+from oracle import formats as F
+from oracle import moe as OM
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+CLOSE = 1e-4     # logit slack accepted for a chosen expert below the margin
+
+
+def run_stack(layers_np, cfg, X0):
+    import torch
+    dev = device()
+    T, nl = X0.shape[0], len(layers_np)
+    Ls = [M.MoELayer.create(M.upload(l, dev), cfg.d, cfg.f, cfg.E, cfg.k, 1, T) for l in layers_np]
+    r = torch.from_numpy(F.bf16_to_f64(X0).astype(np.float32)).to(dev)
+    xt = torch.zeros((nl, T, cfg.d), dtype=torch.int16, device=dev)
+    yt = torch.full((nl, T, cfg.d), float("nan"), dtype=torch.float32, device=dev)
+    it = torch.full((nl, T, cfg.k), -1, dtype=torch.int32, device=dev)
+    M.moe_decode_stack_forward([L.handle for L in Ls], r, T, EPS, xt, yt, it)
+    torch.cuda.synchronize()
+    out = r.cpu().numpy(), xt.cpu().numpy().view(np.uint16), yt.cpu().numpy(), it.cpu().numpy()
+    for L in Ls:
+        L.close()
+    return out
+
+
+def check_teacher_forced(layers_o, cfg, X0, r_gpu, xt, yt, it):
+    """Returns the number of (layer, token) pairs below the margin."""
+    T, d, k = X0.shape[0], cfg.d, cfg.k
+    r = F.bf16_to_f64(X0).astype(np.float32)
+    below = 0
+    for l, OL in enumerate(layers_o):
+        for t in range(T):
+            where = f"layer {l} token {t}"
+            # the pre-norm: the GPU normalizes in fp32, the oracle in fp64;
+            # each bf16 code may differ by one unit in the last place
+            xo = OM.rmsnorm_bf16(r[t], EPS)
+            dx = np.abs(xo.astype(np.int32) - xt[l, t].astype(np.int32))
+            assert dx.max() <= 1, f"{where}: x_l differs by {dx.max()} bf16 units"
+            assert np.count_nonzero(dx) <= max(2, d // 64), f"{where}: {np.count_nonzero(dx)} x_l codes differ"
+            ref = OM.moe_forward(OL, xt[l, t], k)
+            gset = np.sort(it[l, t])
+            assert np.all((gset >= 0) & (gset < cfg.E)) and len(np.unique(gset)) == k, f"{where}: set {it[l, t]}"
+            if OM.topk_margin(ref["logits"], k) >= cfg.margin:
+                assert np.array_equal(gset, np.sort(ref["idx"])), f"{where}: experts {gset} vs {np.sort(ref['idx'])}"
+            else:
+                below += 1
+                kth = np.sort(ref["logits"])[::-1][k - 1]
+                assert np.all(ref["logits"][gset] >= kth - CLOSE), f"{where}: {gset} not among the top {k}"
+                ref = OM.moe_forward_on_set(OL, xt[l, t], gset)
+            err = np.abs(yt[l, t].astype(np.float64) - ref["y"]).max()
+            assert err <= Y_TOL * np.abs(ref["y"]).max(), f"{where}: y err {err:.3e}"
+        # residual add in fp32, element by element: reproduced exactly
+        r = (r + yt[l]).astype(np.float32)
+    assert np.array_equal(r, r_gpu), "final residual is not r_0 + sum of the layer outputs in fp32"
+    return below
+
+
+def end_to_end(layers_o, cfg, X0, r_gpu):
+    """Whole-stack oracle from x_0 alone: final residual within Y_TOL of
+    max |r| per token (valid when no layer fell below the margin)."""
+    for t in range(X0.shape[0]):
+        ro = OM.stack_forward(layers_o, X0[t], cfg.k, EPS)["r"].astype(np.float64)
+        err = np.abs(r_gpu[t].astype(np.float64) - ro).max()
+        assert err <= Y_TOL * np.abs(ro).max(), f"token {t}: final residual err {err:.3e}"
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tiny_stack_49_layers(seed):
+    cfg = synth.TINY
+    layers_np = [synth.make_layer(cfg, seed, l) for l in range(49)]
+    layers_o = [OM.Layer.from_dict(l) for l in layers_np]
+    X0 = tokens(cfg, layers_o[0], seed, 3)
+    r, xt, yt, it = run_stack(layers_np, cfg, X0)
+    below = check_teacher_forced(layers_o, cfg, X0, r, xt, yt, it)
+    if below == 0:
+        end_to_end(layers_o, cfg, X0, r)
+
+
+def test_flagship_stack_first_layers():
+    """The first 8 layers of the 49-layer stack at the flagship shape, 2 tokens."""
+    cfg = synth.STACK
+    layers_np = [synth.make_layer(cfg, 1, l) for l in range(8)]
+    layers_o = [OM.Layer.from_dict(l) for l in layers_np]
+    X0 = tokens(cfg, layers_o[0], 1, 2)
+    r, xt, yt, it = run_stack(layers_np, cfg, X0)
+    below = check_teacher_forced(layers_o, cfg, X0, r, xt, yt, it)
+    if below == 0:
+        end_to_end(layers_o, cfg, X0, r)
+
+
+def test_stack_of_zero_layers_keeps_the_residual():
+    """Layers whose down scales are all zero add exact zeros: r_L == r_0."""
+    cfg = synth.TINY
+    layers_np = []
+    for l in range(3):
+        lay = synth.make_layer(cfg, 3, l)
+        lay["down_s"] = np.zeros_like(lay["down_s"])
+        layers_np.append(lay)
+    X0 = tokens(cfg, OM.Layer.from_dict(layers_np[0]), 3, 2)
+    r, _, yt, _ = run_stack(layers_np, cfg, X0)
+    assert np.array_equal(r, F.bf16_to_f64(X0).astype(np.float32))
+    assert np.all(yt == 0)

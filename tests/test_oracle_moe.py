@@ -204,3 +204,29 @@ def test_stack_of_zero_experts_keeps_the_residual():
     out = M.stack_forward([Z, Z, Z], x0, 2)
     np.testing.assert_array_equal(out["r"], F.bf16_to_f64(x0).astype(np.float32))
     assert all(np.all(y == 0) for y in out["ys"])
+
+
+def test_forward_on_given_set():
+    """moe_forward_on_set: on the selected set it is moe_forward exactly; on
+    any set of identical experts it reduces to one expert's output times the
+    sum of the weights (1 with renormalization, sum of the softmax values
+    without); the order in which S is given does not matter."""
+    L = tiny_layer(6)
+    x = tiny_x(L, 6)
+    ref = M.moe_forward(L, x, 2)
+    got = M.moe_forward_on_set(L, x, ref["idx"])
+    assert np.array_equal(got["y"], ref["y"]) and np.array_equal(got["w"], ref["w"])
+    assert np.array_equal(M.moe_forward_on_set(L, x, ref["idx"][::-1])["y"], ref["y"])
+
+    # every expert a copy of expert 0: y over any set is o_0 * sum(w)
+    t = synth.make_layer(synth.TINY, 6)
+    for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"):
+        t[n] = np.repeat(t[n][:1], t[n].shape[0], axis=0)
+    C = M.Layer.from_dict(t)
+    o0 = M.expert_forward(*C.expert(0), F.bf16_to_f64(x))
+    S = np.array([11, 3, 7])      # not the top-3 in general
+    y1 = M.moe_forward_on_set(C, x, S, True)["y"]
+    np.testing.assert_allclose(y1, o0, rtol=0, atol=1e-14 * np.abs(o0).max())
+    p = M.softmax(M.router_logits(C, F.bf16_to_f64(x)))
+    y0 = M.moe_forward_on_set(C, x, S, False)["y"]
+    np.testing.assert_allclose(y0, o0 * p[S].sum(), rtol=0, atol=1e-14 * np.abs(o0).max())
