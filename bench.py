@@ -328,6 +328,42 @@ def main():
                         "in_stack_layer_us": round(st_s / P * 1e6, 3),
                         "achieved_gbs": round(P * by["b_alg"] / st_s / 1e9, 1)}
 
+        # batch: 64 tokens per call through one layer, Zipf(1.1) router bias
+        TB = synth.BATCH.T
+        bias = torch.from_numpy(synth.zipf_bias(synth.BATCH, args.seed)).to(dev)
+        blayers = [M.MoELayer.create(dict(L.tensors, router_b=bias), d, f, E, k, 1, TB) for L in layers]
+        XB = torch.from_numpy(np.stack([np.stack([synth.draw_x(synth.BATCH, args.seed, l, t, 0) for t in range(TB)])
+                                        for l in range(P)]).view(np.int16)).to(dev)  # [P][TB][d]
+        yb = torch.empty((TB, d), dtype=torch.float32, device=dev)
+        ib = torch.empty((P, TB, k), dtype=torch.int32, device=dev)
+        for l in range(P):
+            M.moe_decode_forward(blayers[l].handle, XB[l], TB, yb, ib[l], None, stream)
+        stream.synchronize()
+        distinct = [len(np.unique(a)) for a in ib.cpu().numpy()]
+
+        def batch_step(i):
+            l = i % P
+            M.moe_decode_forward(blayers[l].handle, XB[l], TB, yb, None, None, stream)
+
+        nb = 2 * P
+        try:
+            bs, _g = time_graph(batch_step, nb, P, stream)
+            del _g
+        except Exception as e:
+            log(f"batch graph failed: {e!r}")
+            bs = time_eager(batch_step, nb, P, stream)
+        us = bs / nb * 1e6
+        per_expert = by["b_q"] // k
+        b_batch = E * d * 4 + TB * d * 2 + float(np.mean(distinct)) * per_expert + TB * d * 4
+        out["batch_t64"] = {"us_per_call": round(us, 3), "tokens_per_s": round(TB / (us * 1e-6), 1),
+                            "distinct_experts_mean": round(float(np.mean(distinct)), 2),
+                            "distinct_experts_range": [int(min(distinct)), int(max(distinct))],
+                            "bytes_per_call": int(b_batch), "achieved_gbs": round(b_batch / (us * 1e-6) / 1e9, 1),
+                            "frac": round(b_batch / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        for L in blayers:
+            L.close()
+        del blayers, XB
+
         # LM head: rotate over 4 copies
         V = synth.LMHEAD1.V
         heads = []

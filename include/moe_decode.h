@@ -95,7 +95,9 @@ typedef struct moe_layer* moe_handle;
 
 /* Bytes of device workspace a layer with this shape needs (0 on a bad
  * shape).  The workspace holds router logits, arrival counters, the chosen
- * experts and the SwiGLU activations of one call. */
+ * experts, their grouping by expert, the operand copies of the activations,
+ * the SwiGLU activations and the per-assignment expert outputs of one call
+ * (for max_tokens T: about T*k*(4d + 2f) + 2Td bytes, plus 64 KiB). */
 size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
 
 /* Validate the shape and weights and bind them, with a caller-owned device
@@ -134,6 +136,23 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
 moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* residual, int32_t T,
                                     float eps, uint16_t* x_trace, float* y_trace, int32_t* idx_trace,
                                     void* stream);
+
+/* The grouping of (token, slot) assignments by expert made by the handle's
+ * last forward or stack call that ran the batched kernels (T > 1, or a
+ * shape without the single-launch kernel).  Assignment a = t*k + j is
+ * token t's j-th chosen expert.  Copies, enqueued on `stream` (any output
+ * may be NULL):
+ *   offsets     (device) int32 [E+1]: expert e owns positions
+ *               offsets[e] .. offsets[e+1]-1; offsets[E] = T*k
+ *   assignments (device) int32 [T*k]: the assignments ordered by expert,
+ *               ascending a within an expert
+ *   active      (device) int32 [E]: the experts with at least one
+ *               assignment, ascending (entries past n_active undefined)
+ *   n_active    (device) int32 [1]
+ * T must be the token count of that call.  The batched step reads each
+ * chosen expert's weights once for all its tokens in this order. */
+moe_status moe_decode_expert_groups(moe_handle h, int32_t T, int32_t* offsets, int32_t* assignments,
+                                    int32_t* active, int32_t* n_active, void* stream);
 
 /* Free the host handle (no device memory is touched). NULL is ignored. */
 void moe_decode_destroy(moe_handle h);

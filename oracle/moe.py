@@ -200,6 +200,21 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     return np.einsum("e,ed->d", wv, O)
 
 
+def group_by_expert(idx: np.ndarray, E: int):
+    """The T*k assignments a = t*k + j (token t's j-th chosen expert idx[t][j])
+    grouped by expert: offsets [E+1] (expert e owns positions offsets[e] ..
+    offsets[e+1]-1), the assignments in that order (ascending a within an
+    expert), and the experts that own any (ascending)."""
+    flat = np.asarray(idx).reshape(-1)
+    lists = [[a for a in range(flat.size) if flat[a] == e] for e in range(E)]
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + len(lists[e])
+    order = np.array([a for e in range(E) for a in lists[e]], dtype=np.int64)
+    active = np.array([e for e in range(E) if lists[e]], dtype=np.int64)
+    return offsets, order, active
+
+
 def best_subset_bruteforce(l: np.ndarray, k: int):
     """All C(E, k) subsets: the one with the largest sum of logits."""
     best, best_sum = None, -np.inf

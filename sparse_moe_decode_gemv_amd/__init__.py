@@ -31,7 +31,7 @@ MOE_LMHEAD_MAX_B = 16
 
 EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
-    "moe_decode_destroy", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
+    "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
     "moe_decode_abi_version",
 )
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_forward.argtypes = [p, p, i32, p, p, p, p]
         L.moe_decode_stack_forward.restype = i32
         L.moe_decode_stack_forward.argtypes = [ctypes.POINTER(p), i32, p, i32, f32, p, p, p, p]
+        L.moe_decode_expert_groups.restype = i32
+        L.moe_decode_expert_groups.argtypes = [p, i32, p, p, p, p, p]
         L.moe_decode_destroy.restype = None
         L.moe_decode_destroy.argtypes = [p]
         L.lmhead_int4_argmax_workspace_bytes.restype = sz
@@ -139,6 +141,12 @@ def moe_decode_stack_forward(handles, residual, T: int, eps: float, x_trace=None
     arr = (ctypes.c_void_p * len(handles))(*handles)
     _check(lib().moe_decode_stack_forward(arr, len(handles), _ptr(residual), T, eps, _ptr(x_trace), _ptr(y_trace),
                                           _ptr(idx_trace), _stream(stream)), "moe_decode_stack_forward")
+
+
+def moe_decode_expert_groups(handle: int, T: int, offsets=None, assignments=None, active=None, n_active=None,
+                             stream=None) -> None:
+    _check(lib().moe_decode_expert_groups(handle, T, _ptr(offsets), _ptr(assignments), _ptr(active),
+                                          _ptr(n_active), _stream(stream)), "moe_decode_expert_groups")
 
 
 def moe_decode_destroy(handle: int) -> None:

@@ -13,7 +13,8 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 struct Layout {
-  size_t counters, logits, sel_idx, sel_w, h, xnorm, tagged, hrec, epoch, total;
+  size_t counters, logits, sel_idx, sel_w, xp, corr_x, off, act, asg, h16, corr_h, obuf, tagged, hrec, epoch,
+      total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -39,12 +40,19 @@ Layout layout_of(const moe_layer_desc* d) {
   Layout L;
   const size_t T = (size_t)d->max_tokens, E = (size_t)d->n_experts, k = (size_t)d->top_k;
   size_t o = 0;
-  L.counters = o, o += align256(T * sizeof(unsigned));
+  const size_t Tk = T * k, d_ = (size_t)d->d, f_ = (size_t)d->f;
+  L.counters = o, o += align256((T + 1) * sizeof(unsigned));  // per token, then tokens_done
   L.logits = o, o += align256(T * E * sizeof(float));
-  L.sel_idx = o, o += align256(T * k * sizeof(int32_t));
-  L.sel_w = o, o += align256(T * k * sizeof(float));
-  L.h = o, o += align256(T * k * (size_t)d->f * sizeof(float));
-  L.xnorm = o, o += align256(T * (size_t)d->d * sizeof(uint16_t));
+  L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
+  L.sel_w = o, o += align256(Tk * sizeof(float));
+  L.xp = o, o += align256(T * d_ * sizeof(uint16_t));
+  L.corr_x = o, o += align256(T * (d_ / 32) * sizeof(float));
+  L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
+  L.act = o, o += align256(E * sizeof(int32_t));
+  L.asg = o, o += align256(Tk * sizeof(int32_t));
+  L.h16 = o, o += align256(Tk * f_ * sizeof(uint16_t));
+  L.corr_h = o, o += align256(Tk * (f_ / 32) * sizeof(float));
+  L.obuf = o, o += align256(Tk * d_ * sizeof(float));
   L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
   L.hrec = o, o += align256(k * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
@@ -110,11 +118,19 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.down_q = w->down_q, a.down_s = w->down_s;
   unsigned char* base = static_cast<unsigned char*>(workspace);
   a.counters = reinterpret_cast<unsigned*>(base + L.counters);
+  a.tokens_done = a.counters + desc->max_tokens;
   a.logits = reinterpret_cast<float*>(base + L.logits);
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
-  a.h = reinterpret_cast<float*>(base + L.h);
-  a.xnorm = reinterpret_cast<uint16_t*>(base + L.xnorm);
+  a.xp = reinterpret_cast<uint16_t*>(base + L.xp);
+  a.corr_x = reinterpret_cast<float*>(base + L.corr_x);
+  a.off = reinterpret_cast<int32_t*>(base + L.off);
+  a.meta = a.off + desc->n_experts + 1;
+  a.act = reinterpret_cast<int32_t*>(base + L.act);
+  a.asg = reinterpret_cast<int32_t*>(base + L.asg);
+  a.h16 = reinterpret_cast<uint16_t*>(base + L.h16);
+  a.corr_h = reinterpret_cast<float*>(base + L.corr_h);
+  a.obuf = reinterpret_cast<float*>(base + L.obuf);
   a.tagged_logits = reinterpret_cast<unsigned long long*>(base + L.tagged);
   a.hrec = reinterpret_cast<unsigned long long*>(base + L.hrec);
   a.epoch = reinterpret_cast<unsigned*>(base + L.epoch);
@@ -129,6 +145,24 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
 }
 
 void moe_decode_destroy(moe_handle h) { delete h; }
+
+moe_status moe_decode_expert_groups(moe_handle h, int32_t T, int32_t* offsets, int32_t* assignments,
+                                    int32_t* active, int32_t* n_active, void* stream) {
+  if (!h) return MOE_ERR_NULL;
+  if (T < 1 || T > h->desc.max_tokens) return MOE_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::LayerArgs& a = h->args;
+  const size_t E = (size_t)a.E, Tk = (size_t)T * a.k;
+  struct {
+    void* dst;
+    const void* src;
+    size_t n;
+  } cp[] = {{offsets, a.off, (E + 1) * 4}, {assignments, a.asg, Tk * 4}, {active, a.act, E * 4},
+            {n_active, a.meta, 4}};
+  for (const auto& c : cp)
+    if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
 
 moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float* y, int32_t* topk_idx,
                               float* topk_w, void* stream) {
@@ -149,8 +183,9 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
     return moe::launch_layer_fused(f, a.d, a.f, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   if (moe::launch_router(a, x, nullptr, 0.f, T, topk_idx, topk_w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
-  if (moe::launch_gateup(a, x, T, s) != hipSuccess) return MOE_ERR_HIP;
-  if (moe::launch_down(a, T, y, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_gateup(a, T, s) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_down(a, T, s) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_combine(a, T, y, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -176,8 +211,9 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
     int32_t* it = idx_trace ? idx_trace + (size_t)l * T * k : nullptr;
     float* yt = y_trace ? y_trace + (size_t)l * T * d : nullptr;
     if (moe::launch_router(a, nullptr, residual, eps, T, it, nullptr, xt, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_gateup(a, a.xnorm, T, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_down(a, T, yt, residual, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup(a, T, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down(a, T, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_combine(a, T, yt, residual, s) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
 }

@@ -18,13 +18,21 @@ struct LayerArgs {
   const uint16_t* up_s;
   const uint8_t* down_q;
   const uint16_t* down_s;
-  // workspace
-  float* logits;         // [T][E]
-  unsigned* counters;    // [T] arrival counters, zero between calls
-  int32_t* sel_idx;      // [T][k]
-  float* sel_w;          // [T][k]
-  float* h;              // [T][k][f]  w_j * silu(g) * u
-  uint16_t* xnorm;       // [T][d]     normalized activation (stack)
+  // workspace of the batched path
+  float* logits;          // [T][E]
+  unsigned* counters;     // [T] arrival counters, zero between calls
+  unsigned* tokens_done;  // [1] tokens whose top-k is done, zero between calls
+  int32_t* sel_idx;       // [T][k] chosen experts of assignment t*k + j
+  float* sel_w;           // [T][k] their weights
+  uint16_t* xp;           // [T][d] activations in MFMA operand order (bf16)
+  float* corr_x;          // [T][d/32] their per-group offset corrections
+  int32_t* off;           // [E+1] first position of each expert in asg
+  int32_t* act;           // [E] experts with assignments, ascending
+  int32_t* meta;          // [0]: number of such experts
+  int32_t* asg;           // [T*k] assignments grouped by expert
+  uint16_t* h16;          // [T*k][f] w_j silu(g) u per position, fp16 operand order
+  float* corr_h;          // [T*k][f/32] their per-group offset corrections
+  float* obuf;            // [T*k][d] o_{t,j} per assignment
   // single-launch step (T = 1)
   unsigned long long* tagged_logits;  // ceil(E/4) lines of 128 B: (epoch << 32 | logit bits)
   unsigned long long* hrec;           // [k*f/8][5] (epoch << 32 | fp16 slice word)
@@ -33,6 +41,7 @@ struct LayerArgs {
 };
 
 constexpr int kMaxFusedGrid = 1024;
+constexpr int kMaxGroupedGrid = 1024;  // persistent grid of the expert-grouped kernels
 
 // Arguments of the single-launch 1-token layer kernel.
 struct FusedArgs {
@@ -61,19 +70,21 @@ bool fused_layer_supported(int d, int f, int E, int k, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
 
-// Router GEMV + softmax + top-k for T tokens.  Activations come either from
-// x (bf16 [T][d]) or, when x is NULL, from the fp32 residual r [T][d]
-// normalized by RMSNorm (eps), in which case x_l is also written to
-// a.xnorm and (if non-NULL) x_trace.
+// Router GEMV + softmax + top-k for T tokens, then the assignments grouped
+// by expert.  Activations come either from x (bf16 [T][d]) or, when x is
+// NULL, from the fp32 residual r [T][d] normalized by RMSNorm (eps), in
+// which case x_l is also written to x_trace when it is non-NULL.
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
                          int32_t* idx_out, float* w_out, uint16_t* x_trace, hipStream_t s);
 
-// h = w_j * silu(W_g[j] x) * (W_u[j] x) for the chosen experts.
-hipError_t launch_gateup(const LayerArgs& a, const uint16_t* x, int T, hipStream_t s);
+// Per chosen expert, over all its tokens: h = w_j * silu(W_g x) * (W_u x).
+hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s);
 
-// y = sum_j W_d[j] h_j; with residual != NULL, residual += y instead of
-// writing y (y_out may still receive y when non-NULL).
-hipError_t launch_down(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
+// Per chosen expert, over all its tokens: o_{t,j} = W_d h.
+hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s);
+
+// y_t = sum_j o_{t,j} into y_out (if non-NULL); residual_t += y_t (if non-NULL).
+hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
 
 // LM head GEMV + argmax.
 hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,

@@ -53,8 +53,8 @@ def test_workspace_bytes_layout():
     n1 = M.moe_decode_workspace_bytes(desc())
     n64 = M.moe_decode_workspace_bytes(desc(max_tokens=64))
     assert n1 > 0 and n64 > n1
-    # h alone is T*k*f floats; the total includes it
-    assert n64 >= 64 * 8 * 512 * 4
+    # the per-assignment expert outputs alone are T*k*d floats
+    assert n64 >= 64 * 8 * 2048 * 4
     assert n1 % 256 == 0
 
 
@@ -99,6 +99,7 @@ def test_forward_and_stack_reject_null_handles():
     assert L.moe_decode_stack_forward(arr, 2, FAKE, 1, 1e-6, None, None, None, None) == M.MOE_ERR_NULL
     assert L.moe_decode_stack_forward(arr, 0, FAKE, 1, 1e-6, None, None, None, None) == M.MOE_ERR_SHAPE
     assert L.moe_decode_stack_forward(None, 1, FAKE, 1, 1e-6, None, None, None, None) == M.MOE_ERR_NULL
+    assert L.moe_decode_expert_groups(None, 1, FAKE, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
     M.moe_decode_destroy(None)  # ignored
 
 

@@ -35,6 +35,24 @@ def run_layer(layer_np, cfg, X, norm=1, max_tokens=None, one_by_one=False):
 BOTH = pytest.mark.parametrize("one_by_one", [False, True], ids=["batched", "single-launch"])
 
 
+def check_groups(L, T, idx_gpu):
+    """The batched path's grouping of assignments by expert, bit-exact
+    against the definition applied to the chosen experts the GPU returned."""
+    import torch
+    dev = device()
+    off = torch.full((L.E + 1,), -1, dtype=torch.int32, device=dev)
+    asg = torch.full((T * L.k,), -1, dtype=torch.int32, device=dev)
+    act = torch.full((L.E,), -1, dtype=torch.int32, device=dev)
+    na = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    M.moe_decode_expert_groups(L.handle, T, off, asg, act, na)
+    torch.cuda.synchronize()
+    e_off, e_asg, e_act = OM.group_by_expert(idx_gpu[:T], L.E)
+    assert np.array_equal(off.cpu().numpy(), e_off), "offsets"
+    assert np.array_equal(asg.cpu().numpy(), e_asg), "assignment order"
+    n = int(na.item())
+    assert n == len(e_act) and np.array_equal(act.cpu().numpy()[:n], e_act), "active experts"
+
+
 @BOTH
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
 def test_tiny_layer_parity(seed, one_by_one):
@@ -42,8 +60,10 @@ def test_tiny_layer_parity(seed, one_by_one):
     lay = synth.make_layer(cfg, seed)
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, seed, 4)
-    _, y, idx, w = run_layer(lay, cfg, X, max_tokens=8, one_by_one=one_by_one)
+    L, y, idx, w = run_layer(lay, cfg, X, max_tokens=8, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, f"tiny seed {seed}")
+    if not one_by_one:
+        check_groups(L, 4, idx)
 
 
 @BOTH
@@ -64,8 +84,10 @@ def test_tiny_layer_other_k(k, one_by_one):
     lay = synth.make_layer(cfg, 7)
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, 7, 2)
-    _, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
+    L, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, k), idx, w, y, f"tiny k={k}")
+    if not one_by_one:
+        check_groups(L, 2, idx)
 
 
 @BOTH
@@ -77,8 +99,10 @@ def test_odd_expert_count_and_bias(one_by_one):
     lay["router_b"] = (np.arange(100) % 7 - 3).astype(np.float32) * 0.05
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, 8, 3)
-    _, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
+    L, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, "E=100")
+    if not one_by_one:
+        check_groups(L, 3, idx)
 
 
 def test_flagship_tied_router_logits_pick_lower_expert():
@@ -120,10 +144,59 @@ def test_batch_with_zipf_bias_parity():
     lay = synth.make_layer(cfg, 1)
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, 1, cfg.T)
-    _, y, idx, w = run_layer(lay, cfg, X)
+    L, y, idx, w = run_layer(lay, cfg, X)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, "batch")
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
-    assert counts.max() >= 16  # the skew the workload is built to have
+    assert counts.max() > 32  # the skew the workload is built to have: several 32-token chunks
+    check_groups(L, cfg.T, idx)
+
+
+def test_batch_repeat_calls_are_bit_identical():
+    """The batched path has no atomics in its arithmetic: same input, same bits."""
+    import torch
+    cfg = synth.BATCH
+    lay = synth.make_layer(cfg, 2)
+    OL = OM.Layer.from_dict(lay)
+    X = tokens(cfg, OL, 2, cfg.T)
+    dev = device()
+    L = M.MoELayer.create(M.upload(lay, dev), cfg.d, cfg.f, cfg.E, cfg.k, 1, cfg.T)
+    x = torch.from_numpy(as_i16(X)).to(dev)
+    outs = []
+    for _ in range(5):
+        y = torch.empty((cfg.T, cfg.d), device=dev)
+        L.forward(x, y)
+        outs.append(y.cpu().numpy())
+    for y in outs[1:]:
+        assert np.array_equal(y, outs[0])
+
+
+@pytest.mark.parametrize("T,k", [(256, 4), (64, 16)])
+def test_max_tokens_and_hot_experts(T, k):
+    """Up to the largest T: with 16 experts every expert takes many 32-token
+    chunks (k=16: all 16 experts chosen by every token)."""
+    from dataclasses import replace
+    cfg = replace(synth.TINY, k=k)
+    lay = synth.make_layer(cfg, 9)
+    OL = OM.Layer.from_dict(lay)
+    X = tokens(cfg, OL, 9, T)
+    L, y, idx, w = run_layer(lay, cfg, X)
+    compare_layer(OM.moe_forward_tokens(OL, X, k), idx, w, y, f"T={T} k={k}")
+    check_groups(L, T, idx)
+
+
+@pytest.mark.parametrize("d,f,E,k,T", [(512, 256, 8, 2, 5), (1024, 1024, 4, 2, 3), (4096, 1024, 4, 2, 3),
+                                       (256, 4096, 3, 1, 4), (8192, 128, 2, 1, 2)])
+def test_other_shapes_batched(d, f, E, k, T):
+    """Every template of the grouped kernels: K split 1, 2 or 4 ways, one or
+    several passes over K."""
+    from dataclasses import replace
+    cfg = replace(synth.LAYER, d=d, f=f, E=E, k=k)
+    lay = synth.make_layer(cfg, 11)
+    OL = OM.Layer.from_dict(lay)
+    X = tokens(cfg, OL, 11, T)
+    L, y, idx, w = run_layer(lay, cfg, X)
+    compare_layer(OM.moe_forward_tokens(OL, X, k), idx, w, y, f"d={d} f={f}")
+    check_groups(L, T, idx)
 
 
 def test_single_launch_and_batched_calls_interleave_on_one_handle():

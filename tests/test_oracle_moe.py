@@ -230,3 +230,21 @@ def test_forward_on_given_set():
     p = M.softmax(M.router_logits(C, F.bf16_to_f64(x)))
     y0 = M.moe_forward_on_set(C, x, S, False)["y"]
     np.testing.assert_allclose(y0, o0 * p[S].sum(), rtol=0, atol=1e-14 * np.abs(o0).max())
+
+
+def test_group_by_expert_hand_example_and_invariants():
+    """Tokens (0: experts 2,0), (1: 2,3), (2: 0,2) with E = 5: expert 0 owns
+    assignments 1 and 4, expert 2 owns 0, 2 and 5, expert 3 owns 3."""
+    off, order, active = M.group_by_expert(np.array([[2, 0], [2, 3], [0, 2]]), 5)
+    assert off.tolist() == [0, 2, 2, 5, 6, 6]
+    assert order.tolist() == [1, 4, 0, 2, 5, 3]
+    assert active.tolist() == [0, 2, 3]
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(40, 6, replace=False) for _ in range(33)])
+    off, order, active = M.group_by_expert(idx, 40)
+    assert sorted(order.tolist()) == list(range(idx.size))          # each assignment once
+    assert np.array_equal(np.diff(off), np.bincount(idx.ravel(), minlength=40))
+    for e in range(40):
+        seg = order[off[e]:off[e + 1]]
+        assert np.all(idx.ravel()[seg] == e) and np.all(np.diff(seg) > 0)
+    assert active.tolist() == [e for e in range(40) if off[e + 1] > off[e]]
