@@ -5,7 +5,7 @@
 
 #include <new>
 
-#include "../../include/moe_decode.h"
+#include "moe_decode.h"
 #include "launch.h"
 
 namespace {
@@ -13,8 +13,8 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 struct Layout {
-  size_t counters, logits, sel_idx, sel_w, xp, corr_x, off, act, asg, h16, corr_h, obuf, tagged, hrec, epoch,
-      total;
+  size_t counters, logits, sel_idx, sel_w, xp, corr_x, off, act, chunk_off, asg, h16, obuf, resid, tagged, hrec,
+      epoch, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -41,7 +41,7 @@ Layout layout_of(const moe_layer_desc* d) {
   const size_t T = (size_t)d->max_tokens, E = (size_t)d->n_experts, k = (size_t)d->top_k;
   size_t o = 0;
   const size_t Tk = T * k, d_ = (size_t)d->d, f_ = (size_t)d->f;
-  L.counters = o, o += align256((T + 1) * sizeof(unsigned));  // per token, then tokens_done
+  L.counters = o, o += align256(((T + 3) / 4 + 1) * 128);  // one line per 4-token block, then tokens_done
   L.logits = o, o += align256(T * E * sizeof(float));
   L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
   L.sel_w = o, o += align256(Tk * sizeof(float));
@@ -49,10 +49,11 @@ Layout layout_of(const moe_layer_desc* d) {
   L.corr_x = o, o += align256(T * (d_ / 32) * sizeof(float));
   L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
   L.act = o, o += align256(E * sizeof(int32_t));
+  L.chunk_off = o, o += align256((E + 1) * sizeof(int32_t));
   L.asg = o, o += align256(Tk * sizeof(int32_t));
   L.h16 = o, o += align256(Tk * f_ * sizeof(uint16_t));
-  L.corr_h = o, o += align256(Tk * (f_ / 32) * sizeof(float));
   L.obuf = o, o += align256(Tk * d_ * sizeof(float));
+  L.resid = o, o += align256(T * d_ * sizeof(float));  // second residual buffer of a stack
   L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
   L.hrec = o, o += align256(k * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
@@ -66,8 +67,24 @@ struct moe_layer {
   moe_layer_desc desc;
   moe::LayerArgs args;
   void* workspace;
-  bool fused;  // the 1-token step runs as one launch
+  float* resid_tmp;  // [max_tokens][d]: the other residual buffer when this layer leads a stack
+  bool fused;        // the 1-token step runs as one launch
 };
+
+namespace {
+
+moe::FusedArgs fused_args(const moe_layer* h) {
+  const moe::LayerArgs& a = h->args;
+  moe::FusedArgs f{};
+  f.router_w = a.router_w, f.router_b = a.router_b;
+  f.gate_q = a.gate_q, f.gate_s = a.gate_s, f.up_q = a.up_q, f.up_s = a.up_s;
+  f.down_q = a.down_q, f.down_s = a.down_s;
+  f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error;
+  f.E = a.E, f.k = a.k, f.norm = a.norm_topk;
+  return f;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -118,7 +135,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.down_q = w->down_q, a.down_s = w->down_s;
   unsigned char* base = static_cast<unsigned char*>(workspace);
   a.counters = reinterpret_cast<unsigned*>(base + L.counters);
-  a.tokens_done = a.counters + desc->max_tokens;
+  a.tokens_done = a.counters + 32 * ((desc->max_tokens + 3) / 4);
   a.logits = reinterpret_cast<float*>(base + L.logits);
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
@@ -127,10 +144,11 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.off = reinterpret_cast<int32_t*>(base + L.off);
   a.meta = a.off + desc->n_experts + 1;
   a.act = reinterpret_cast<int32_t*>(base + L.act);
+  a.chunk_off = reinterpret_cast<int32_t*>(base + L.chunk_off);
   a.asg = reinterpret_cast<int32_t*>(base + L.asg);
   a.h16 = reinterpret_cast<uint16_t*>(base + L.h16);
-  a.corr_h = reinterpret_cast<float*>(base + L.corr_h);
   a.obuf = reinterpret_cast<float*>(base + L.obuf);
+  h->resid_tmp = reinterpret_cast<float*>(base + L.resid);
   a.tagged_logits = reinterpret_cast<unsigned long long*>(base + L.tagged);
   a.hrec = reinterpret_cast<unsigned long long*>(base + L.hrec);
   a.epoch = reinterpret_cast<unsigned*>(base + L.epoch);
@@ -173,13 +191,8 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe::LayerArgs& a = h->args;
   if (T == 1 && h->fused) {
-    moe::FusedArgs f;
-    f.router_w = a.router_w, f.router_b = a.router_b;
-    f.gate_q = a.gate_q, f.gate_s = a.gate_s, f.up_q = a.up_q, f.up_s = a.up_s;
-    f.down_q = a.down_q, f.down_s = a.down_s;
+    moe::FusedArgs f = fused_args(h);
     f.x = x, f.y = y, f.idx_out = topk_idx, f.w_out = topk_w;
-    f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error;
-    f.E = a.E, f.k = a.k, f.norm = a.norm_topk;
     return moe::launch_layer_fused(f, a.d, a.f, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   if (moe::launch_router(a, x, nullptr, 0.f, T, topk_idx, topk_w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
@@ -205,6 +218,27 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
     return MOE_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t d = (size_t)layers[0]->desc.d, k = (size_t)layers[0]->desc.top_k;
+  bool fused = T == 1;
+  for (int l = 0; l < L; ++l) fused = fused && layers[l]->fused;
+  if (fused) {
+    // One launch per layer.  The residual alternates between the caller's
+    // buffer and the first layer's spare one, arranged so that r_L lands in
+    // the caller's buffer, except for odd L, which ends with one copy.
+    float* buf[2] = {residual, layers[0]->resid_tmp};
+    for (int l = 0; l < L; ++l) {
+      moe::FusedArgs f = fused_args(layers[l]);
+      f.resid_in = buf[l & 1];
+      f.resid_out = buf[(l + 1) & 1];
+      f.eps = eps;
+      f.y = y_trace ? y_trace + (size_t)l * d : nullptr;
+      f.x_trace = x_trace ? x_trace + (size_t)l * d : nullptr;
+      f.idx_out = idx_trace ? idx_trace + (size_t)l * k : nullptr;
+      if (moe::launch_layer_fused(f, layers[l]->args.d, layers[l]->args.f, s) != hipSuccess) return MOE_ERR_HIP;
+    }
+    if ((L & 1) && hipMemcpyAsync(residual, buf[1], d * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  }
   for (int l = 0; l < L; ++l) {
     const moe::LayerArgs& a = layers[l]->args;
     uint16_t* xt = x_trace ? x_trace + (size_t)l * T * d : nullptr;

@@ -26,6 +26,12 @@
 //            they all carry the tag (the down pieces arrive meanwhile) and
 //            finishes its output rows.
 //
+// In a pre-norm stack (NORM) the activation is not an input: every
+// workgroup normalizes the fp32 residual itself (identical code and data,
+// so identical bits) into LDS, and the output rows are added to the
+// residual, read from one buffer and written to another so that no
+// workgroup can see a row that another has already updated.
+//
 // The tag is this workgroup's call count + 1, kept per workgroup in the
 // workspace; all workgroups take part in every call, so their counts agree
 // and consecutive calls never accept each other's words.  Every wait is
@@ -87,7 +93,7 @@ __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
 
 // D hidden, F expert width, KP top_k rounded up to a power of two, EPL
 // experts per lane in the top-k wave.
-template <int D, int F, int KP, int EPL>
+template <int D, int F, int KP, int EPL, bool NORM>
 __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
@@ -111,11 +117,53 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   __shared__ float s_lg[64 * EPL];
   __shared__ unsigned s_pub[ROWS_G / 8 * 5];
 
+  __shared__ __align__(16) uint16_t s_x[NORM ? D : 8];
+  __shared__ float s_ss[4];
+
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wg = blockIdx.x * 4 + wid;
   const int E = a.E, k = a.k;
   const unsigned tag = a.epoch[blockIdx.x] + 1u;  // this workgroup's own call count
   const float bias = (a.router_b && wg < E) ? a.router_b[wg] : 0.f;
+
+  // the activation: bf16 from the caller, or the normalized residual in LDS
+  auto x2 = [&](int i) -> uint2 {  // bf16 elements 4i .. 4i+3
+    if constexpr (NORM) return reinterpret_cast<const uint2*>(s_x)[i];
+    else return reinterpret_cast<const uint2*>(a.x)[i];
+  };
+  auto x4 = [&](int i) -> uint4 {  // bf16 elements 8i .. 8i+7
+    if constexpr (NORM) return reinterpret_cast<const uint4*>(s_x)[i];
+    else return reinterpret_cast<const uint4*>(a.x)[i];
+  };
+  if constexpr (NORM) {
+    // x = bf16(r / sqrt(mean(r^2) + eps)), the same in every workgroup
+    constexpr int NR = (D / 4 + 255) / 256;
+    float4 rv[NR];
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int c = threadIdx.x + 256 * m;
+      rv[m] = c < D / 4 ? reinterpret_cast<const float4*>(a.resid_in)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      ss = fmaf(rv[m].x, rv[m].x, ss);
+      ss = fmaf(rv[m].y, rv[m].y, ss);
+      ss = fmaf(rv[m].z, rv[m].z, ss);
+      ss = fmaf(rv[m].w, rv[m].w, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) s_ss[wid] = ss;
+    __syncthreads();
+    const float den = sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)D + a.eps);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int c = threadIdx.x + 256 * m;
+      if (c < D / 4) {
+        const uint2 pk = make_uint2(pack_bf16(rv[m].x / den, rv[m].y / den), pack_bf16(rv[m].z / den, rv[m].w / den));
+        reinterpret_cast<uint2*>(s_x)[c] = pk;
+        if (a.x_trace && blockIdx.x == 0) reinterpret_cast<uint2*>(a.x_trace)[c] = pk;
+      }
+    }
+    __syncthreads();
+  }
 
   // ---------------------------------------------------------------- router
   // rows 4*b .. 4*b+3 in workgroup b, one per wave; the 4 logits go out as
@@ -123,11 +171,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   if (blockIdx.x * 4 < E) {
     if (wg < E) {
       const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)wg * D);
-      const uint2* xr = reinterpret_cast<const uint2*>(a.x);
       float4 w[NI];
       uint2 q[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane], q[i] = xr[64 * i + lane];
+      for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane], q[i] = x2(64 * i + lane);
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -236,13 +283,12 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   if (has_gate) {
     const float wj = s_w[gslot];
     Slice8 xs[XS][4];
-    const uint4* xp = reinterpret_cast<const uint4*>(a.x);
 #pragma unroll
     for (int s = 0; s < XS; ++s) {
       const int c = CPR > 64 ? 64 * s + lane : lane % CPR;
       const int base = 128 * (c >> 2) + 8 * (c & 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xs[s][j] = make_slice_bf16(xp[(base + 32 * j) >> 3]);
+      for (int j = 0; j < 4; ++j) xs[s][j] = make_slice_bf16(x4((base + 32 * j) >> 3));
     }
     float ag = 0.f, au = 0.f;
 #pragma unroll
@@ -303,6 +349,15 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     cc[m] = flat % CPRF;
     act[m] = has_down && dslot[m] < k;
   }
+  float radd[NLD];  // residual rows this lane will update (stack)
+#pragma unroll
+  for (int n = 0; n < NLD; ++n) {
+    const int row = r0 + (P >= 64 ? n / LPRD : n * RPLD + lane / P);
+    const bool writer = has_down && (P >= 64 ? lane == 0 : lane % P == 0) && n % LPRD == LPRD - 1;
+    radd[n] = 0.f;
+    if constexpr (NORM)
+      if (writer) radd[n] = a.resid_in[row];
+  }
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
     const int m = n % LPRD;
@@ -348,6 +403,14 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   }
 
   // ---------------------------------------------------------------- down + combine
+  auto put_y = [&](int row, float v, float r) {
+    if constexpr (NORM) {
+      a.resid_out[row] = r + v;
+      if (a.y) a.y[row] = v;
+    } else {
+      a.y[row] = v;
+    }
+  };
   if (has_down) {
     Slice8 hs8[LPRD][4];
 #pragma unroll
@@ -368,10 +431,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       if (n % LPRD == LPRD - 1) {
         if constexpr (P >= 64) {
           const float v = wave_sum(acc);
-          if (lane == 0) a.y[r0 + n / LPRD] = v;
+          if (lane == 0) put_y(r0 + n / LPRD, v, radd[n]);
         } else {
           const float v = seg_sum<(P < 64 ? P : 64)>(acc);
-          if (lane % P == 0) a.y[r0 + n * RPLD + lane / P] = v;
+          if (lane % P == 0) put_y(r0 + n * RPLD + lane / P, v, radd[n]);
         }
         acc = 0.f;
       }
@@ -385,7 +448,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 template <int D, int F, int KP, int EPL>
 static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
   const size_t lds = (size_t)a.k * (F / 8) * 5 * sizeof(unsigned);
-  hipLaunchKernelGGL((k_layer<D, F, KP, EPL>), dim3(G), dim3(256), lds, s, a);
+  if (a.resid_in)
+    hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true>), dim3(G), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false>), dim3(G), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

@@ -1,19 +1,22 @@
 // kernels_moe.hip -- the decode step of a 4-bit MoE layer for T tokens on gfx950.
 //
 // Four kernels per call:
-//   router  : logits = W_r x (+b), one router row per wave, four rows per
-//             workgroup.  The last workgroup to finish a token does that
-//             token's softmax + top-k in one wave; the last token to finish
-//             sorts the T*k (token, slot) assignments by expert (a stable
-//             counting sort built from wave ballots).  Workgroup 0 of each
-//             token also writes the token's activations in MFMA operand
-//             order, with their per-group offset corrections.  In the stack
-//             the router applies the pre-norm (RMSNorm) to the residual.
-//   gate/up : per chosen expert, int4 x bf16 MFMA tiles over all the
-//             tokens routed to it, so each chosen expert's weights are read
-//             once per call however many tokens chose it; SwiGLU; h = w_j
-//             silu(g) u stored as fp16 operands of the down step.
-//   down    : the same over W_d; each assignment's o_{t,j} in fp32.
+//   router  : logits = W_r x (+b), one router row per wave, held in
+//             registers across a block of 4 tokens.  The last workgroup to
+//             finish a token block does its 4 softmax + top-k selections,
+//             one wave each; the last token to finish sorts the T*k (token,
+//             slot) assignments by expert (a stable counting sort built from
+//             wave ballots).  Workgroup 0 also writes each token's
+//             activations in MFMA operand order with their per-group offset
+//             corrections.  In the stack the router applies the pre-norm
+//             (RMSNorm) to the residual.
+//   gate/up : one wave per (chosen expert, 16 rows, chunk of up to 32 of its
+//             tokens): int4 x bf16 MFMA tiles, so each chosen expert's
+//             weights are read once per call however many tokens chose it;
+//             SwiGLU in registers; h = w_j silu(g) u stored as fp16 operands
+//             of the down step.
+//   down    : the same shape of work over W_d with int4 x fp16 MFMA; each
+//             assignment's o_{t,j} in fp32.
 //   combine : y_t = sum_j o_{t,j} in slot order (deterministic); in the
 //             stack the residual add is folded in.
 // The pages describe the step: per token a small router picks a few of 256
@@ -27,11 +30,12 @@
 // activations, B 16 weight rows, so every lane ends with one weight row and
 // four tokens, and one group scale per lane applies to all four.  One dword
 // of stored codes is the 8 elements of one chunk; its 8 operand values come
-// out of the magic-number conversion in the order e = 0,4,1,5,2,6,3,7 with
-// the odd e scaled (see device_common.h), and the activation operands are
-// stored in that same order, odd e divided by 8 (bf16) or 16 (fp16).  The
-// per-group offset correction times the scale is added by one fp32 MFMA
-// (16x16x4) per four groups.
+// out of the magic-number conversion in the order e = 0,4,1,5,2,6,3,7 (see
+// device_common.h) and the activation operands are stored in that order.
+// gate/up: bf16 128+u / 128+8u against x / x/8, the offsets removed by the
+// per-group correction times the scale, one fp32 MFMA (16x16x4) per four
+// groups.  down: the codes become exact signed fp16 q = u - 8 with packed
+// fp16 arithmetic, so h needs no correction.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -97,52 +101,73 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 // grouped by expert, ascending a within an expert:
 //   off[e] .. off[e+1]-1  positions of expert e in asg (off[E] = Tk)
 //   asg[p]                the assignment at position p
-//   act[0 .. meta[0]-1]   the experts with at least one assignment, ascending
-// cnt: LDS [E]; sums: LDS [128].
-__device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int* sums, int32_t* off,
-                               int32_t* act, int32_t* meta, int32_t* asg, int lane) {
+//   act[i], i < meta[0]   the experts with at least one assignment, ascending
+//   chunk_off[i]          32-token chunks of the active experts before act[i]
+//                         (chunk_off[meta[0]] = all chunks)
+// cnt: LDS [E]; ssel: LDS [Tk]; sums: LDS [192].
+__device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int* ssel, int* sums, int32_t* off,
+                               int32_t* act, int32_t* chunk_off, int32_t* meta, int32_t* asg, int lane) {
+  // the chosen experts into LDS, 8 loads in flight per lane
+  for (int c0 = 0; c0 < Tk; c0 += 512) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = load_coherent_i32(sel + min(c0 + 64 * i + lane, Tk - 1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (c0 + 64 * i + lane < Tk) ssel[c0 + 64 * i + lane] = min(max(v[i], 0), E - 1);
+  }
   for (int i = lane; i < E; i += 64) cnt[i] = 0;
   lds_wait();
   for (int c = 0; c < Tk; c += 64) {  // counts
     const int a = c + lane;
     const bool v = a < Tk;
-    const int e = v ? min(max(load_coherent_i32(sel + a), 0), E - 1) : 0;
+    const int e = v ? ssel[a] : 0;
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     if (v && lane == __builtin_ctzll(same)) cnt[e] += __builtin_popcountll(same);
     lds_wait();
   }
-  // exclusive scans over experts of the counts and of the active flags
+  // exclusive scans over experts: counts, active flags, chunks
   const int per = (E + 63) / 64;
   const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
-  int s = 0, na = 0;
+  int s = 0, na = 0, nc = 0;
   for (int e = e0; e < e1; ++e) {
-    s += cnt[e];
-    na += cnt[e] > 0;
+    const int n = cnt[e];
+    s += n;
+    na += n > 0;
+    nc += (n + 31) >> 5;
   }
   sums[lane] = s;
   sums[64 + lane] = na;
+  sums[128 + lane] = nc;
   lds_wait();
-  int base = 0, abase = 0;
+  int base = 0, abase = 0, cbase = 0;
   for (int l = 0; l < lane; ++l) {
     base += sums[l];
     abase += sums[64 + l];
+    cbase += sums[128 + l];
   }
   for (int e = e0; e < e1; ++e) {
     const int n = cnt[e];
     off[e] = base;
-    if (n > 0) act[abase++] = e;
+    if (n > 0) {
+      act[abase] = e;
+      chunk_off[abase] = cbase;
+      ++abase;
+      cbase += (n + 31) >> 5;
+    }
     cnt[e] = base;  // from here on: the next free position of expert e
     base += n;
   }
   if (lane == 63) {
     off[E] = base;
+    chunk_off[abase] = cbase;
     meta[0] = abase;
   }
   lds_wait();
   for (int c = 0; c < Tk; c += 64) {  // placement, stable in a
     const int a = c + lane;
     const bool v = a < Tk;
-    const int e = v ? min(max(load_coherent_i32(sel + a), 0), E - 1) : 0;
+    const int e = v ? ssel[a] : 0;
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
     const int pos = v ? cnt[e] : 0;
@@ -155,8 +180,14 @@ __device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int*
 
 // ----------------------------------------------------------------- router
 
-// grid (ceil(E/4), T), block 256: wave w of workgroup b computes logit
-// 4b + w of token t.  EPL = experts per lane in the top-k wave, ceil(E/64).
+constexpr int kRouterTokens = 4;  // tokens per router workgroup
+constexpr int kCounterStride = 32;  // one arrival counter per 128-byte line
+
+// grid (ceil(E/4), ceil(T/4)), block 256: wave w of workgroup (b, c) holds
+// router row 4b + w in registers and computes its logit for tokens 4c ..
+// 4c+3.  One arrival per workgroup on the token block's counter (own cache
+// line); the last workgroup of a block does the top-k of its 4 tokens, one
+// per wave; the last token overall runs the sort.  EPL = ceil(E/64).
 template <int D, int EPL>
 __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_t* __restrict__ x,
                                                 const float* __restrict__ resid, float eps, int T,
@@ -165,99 +196,107 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
   constexpr int NI = D / 256;  // float4 columns per lane: 4*lane + 256*i
   constexpr int G = D / 32;
   __shared__ int s_cnt[1024];
-  __shared__ int s_sums[128];
+  __shared__ int s_sel[kMaxAssignments];
+  __shared__ int s_sums[192];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave, t = blockIdx.y;
+  const int e = blockIdx.x * 4 + wave;
   const bool row_ok = e < a.E;
   const float4* wrow = reinterpret_cast<const float4*>(a.router_w + (size_t)min(e, a.E - 1) * D);
   float4 w[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) w[i] = wrow[64 * i + lane];
+  const float bias = row_ok && a.router_b ? a.router_b[e] : 0.f;
 
-  float xv[NI][4];
-  if (x) {
-    const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)t * D);
+  for (int tb = 0; tb < kRouterTokens; ++tb) {
+    const int t = blockIdx.y * kRouterTokens + tb;
+    if (t >= T) break;
+    float xv[NI][4];
+    if (x) {
+      const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)t * D);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint2 q = xr[64 * i + lane];
-      xv[i][0] = bf16_bits_to_f32(q.x & 0xFFFFu);
-      xv[i][1] = bf16_bits_to_f32(q.x >> 16);
-      xv[i][2] = bf16_bits_to_f32(q.y & 0xFFFFu);
-      xv[i][3] = bf16_bits_to_f32(q.y >> 16);
-    }
-  } else {
-    // pre-norm: x = bf16(r / sqrt(mean(r^2) + eps))
-    const float4* rr = reinterpret_cast<const float4*>(resid + (size_t)t * D);
-    float4 rv[NI];
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      rv[i] = rr[64 * i + lane];
-      ss = fmaf(rv[i].x, rv[i].x, ss);
-      ss = fmaf(rv[i].y, rv[i].y, ss);
-      ss = fmaf(rv[i].z, rv[i].z, ss);
-      ss = fmaf(rv[i].w, rv[i].w, ss);
-    }
-    ss = wave_sum(ss);
-    const float den = sqrtf(ss / (float)D + eps);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint32_t b0 = f32_to_bf16_bits(rv[i].x / den), b1 = f32_to_bf16_bits(rv[i].y / den);
-      const uint32_t b2 = f32_to_bf16_bits(rv[i].z / den), b3 = f32_to_bf16_bits(rv[i].w / den);
-      xv[i][0] = bf16_bits_to_f32(b0);
-      xv[i][1] = bf16_bits_to_f32(b1);
-      xv[i][2] = bf16_bits_to_f32(b2);
-      xv[i][3] = bf16_bits_to_f32(b3);
-      if (x_trace && blockIdx.x == 0 && wave == 0)
-        reinterpret_cast<uint2*>(x_trace + (size_t)t * D)[64 * i + lane] =
-            make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    }
-  }
-
-  if (blockIdx.x == 0 && wave == 0) {
-    // The token's MFMA operand row: chunk of 8 elements stored as
-    // (x0, x4, x1/8, x5/8, x2, x6, x3/8, x7/8); lane 2m holds x0..x3 of a
-    // chunk and lane 2m+1 holds x4..x7, so neighbours trade halves.  Per
-    // group of 32 (8 lanes): corr = -136 * sum(even e) - 24 * sum(odd e).
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float o0 = dpp_f<kDppXor1>(xv[i][0]), o1 = dpp_f<kDppXor1>(xv[i][1]);
-      const float o2 = dpp_f<kDppXor1>(xv[i][2]), o3 = dpp_f<kDppXor1>(xv[i][3]);
-      uint2 pk;
-      if ((lane & 1) == 0) {
-        pk.x = pack_bf16(xv[i][0], o0);
-        pk.y = pack_bf16(xv[i][1] * 0.125f, o1 * 0.125f);
-      } else {
-        pk.x = pack_bf16(o2, xv[i][2]);
-        pk.y = pack_bf16(o3 * 0.125f, xv[i][3] * 0.125f);
+      for (int i = 0; i < NI; ++i) {
+        const uint2 q = xr[64 * i + lane];
+        xv[i][0] = bf16_bits_to_f32(q.x & 0xFFFFu);
+        xv[i][1] = bf16_bits_to_f32(q.x >> 16);
+        xv[i][2] = bf16_bits_to_f32(q.y & 0xFFFFu);
+        xv[i][3] = bf16_bits_to_f32(q.y >> 16);
       }
-      reinterpret_cast<uint2*>(a.xp + (size_t)t * D)[64 * i + lane] = pk;
-      const float cr = seg_sum<8>(-136.0f * (xv[i][0] + xv[i][2]) - 24.0f * (xv[i][1] + xv[i][3]));
-      if ((lane & 7) == 0) a.corr_x[(size_t)t * G + (256 * i + 4 * lane) / 32] = cr;
-    }
-  }
-
-  if (row_ok) {
-    float acc = 0.f;
+    } else {
+      // pre-norm: x = bf16(r / sqrt(mean(r^2) + eps))
+      const float4* rr = reinterpret_cast<const float4*>(resid + (size_t)t * D);
+      float4 rv[NI];
+      float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      acc = fmaf(w[i].x, xv[i][0], acc);
-      acc = fmaf(w[i].y, xv[i][1], acc);
-      acc = fmaf(w[i].z, xv[i][2], acc);
-      acc = fmaf(w[i].w, xv[i][3], acc);
+      for (int i = 0; i < NI; ++i) {
+        rv[i] = rr[64 * i + lane];
+        ss = fmaf(rv[i].x, rv[i].x, ss);
+        ss = fmaf(rv[i].y, rv[i].y, ss);
+        ss = fmaf(rv[i].z, rv[i].z, ss);
+        ss = fmaf(rv[i].w, rv[i].w, ss);
+      }
+      ss = wave_sum(ss);
+      const float den = sqrtf(ss / (float)D + eps);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint32_t b0 = f32_to_bf16_bits(rv[i].x / den), b1 = f32_to_bf16_bits(rv[i].y / den);
+        const uint32_t b2 = f32_to_bf16_bits(rv[i].z / den), b3 = f32_to_bf16_bits(rv[i].w / den);
+        xv[i][0] = bf16_bits_to_f32(b0);
+        xv[i][1] = bf16_bits_to_f32(b1);
+        xv[i][2] = bf16_bits_to_f32(b2);
+        xv[i][3] = bf16_bits_to_f32(b3);
+        if (x_trace && blockIdx.x == 0 && wave == tb)
+          reinterpret_cast<uint2*>(x_trace + (size_t)t * D)[64 * i + lane] =
+              make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      }
     }
-    acc = wave_sum(acc);
-    if (a.router_b) acc += a.router_b[e];
-    if (lane == 0) store_coherent(a.logits + (size_t)t * a.E + e, acc);
+
+    if (blockIdx.x == 0 && wave == tb) {
+      // The token's MFMA operand row: chunk of 8 elements stored as
+      // (x0, x4, x1/8, x5/8, x2, x6, x3/8, x7/8); lane 2m holds x0..x3 of a
+      // chunk and lane 2m+1 holds x4..x7, so neighbours trade halves.  Per
+      // group of 32 (8 lanes): corr = -136 * sum(even e) - 24 * sum(odd e).
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float o0 = dpp_f<kDppXor1>(xv[i][0]), o1 = dpp_f<kDppXor1>(xv[i][1]);
+        const float o2 = dpp_f<kDppXor1>(xv[i][2]), o3 = dpp_f<kDppXor1>(xv[i][3]);
+        uint2 pk;
+        if ((lane & 1) == 0) {
+          pk.x = pack_bf16(xv[i][0], o0);
+          pk.y = pack_bf16(xv[i][1] * 0.125f, o1 * 0.125f);
+        } else {
+          pk.x = pack_bf16(o2, xv[i][2]);
+          pk.y = pack_bf16(o3 * 0.125f, xv[i][3] * 0.125f);
+        }
+        reinterpret_cast<uint2*>(a.xp + (size_t)t * D)[64 * i + lane] = pk;
+        const float cr = seg_sum<8>(-136.0f * (xv[i][0] + xv[i][2]) - 24.0f * (xv[i][1] + xv[i][3]));
+        if ((lane & 7) == 0) a.corr_x[(size_t)t * G + (256 * i + 4 * lane) / 32] = cr;
+      }
+    }
+
+    if (row_ok) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        acc = fmaf(w[i].x, xv[i][0], acc);
+        acc = fmaf(w[i].y, xv[i][1], acc);
+        acc = fmaf(w[i].z, xv[i][2], acc);
+        acc = fmaf(w[i].w, xv[i][3], acc);
+      }
+      acc = wave_sum(acc) + bias;
+      if (lane == 0) store_coherent(a.logits + (size_t)t * a.E + e, acc);
+    }
   }
 
-  // Arrival: the last workgroup of token t selects its experts.
+  // Arrival: the last workgroup of this token block selects its experts.
+  unsigned* counter = a.counters + blockIdx.y * kCounterStride;
   wait_vm();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive(&a.counters[t]) == gridDim.x - 1;
+  if (threadIdx.x == 0) s_last = arrive(counter) == gridDim.x - 1;
   __syncthreads();
-  if (!s_last || wave != 0) return;
+  if (!s_last) return;
+  const int t = blockIdx.y * kRouterTokens + wave;
+  if (t >= T) return;
   int32_t* io = idx_out ? idx_out + (size_t)t * a.k : nullptr;
   float* wo = w_out ? w_out + (size_t)t * a.k : nullptr;
   topk_wave<EPL>(a.logits + (size_t)t * a.E, a.E, a.k, a.norm_topk, lane, a.sel_idx + t * a.k,
@@ -265,29 +304,39 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
   wait_vm();
   unsigned prev = 0;
   if (lane == 0) {
-    a.counters[t] = 0u;  // ready for the next call
+    if (wave == 0) *counter = 0u;  // every workgroup of the block has arrived
     prev = arrive(a.tokens_done);
   }
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != (unsigned)(T - 1)) return;
   // the last token: group the assignments by expert
-  sort_by_expert(a.sel_idx, T * a.k, a.E, s_cnt, s_sums, a.off, a.act, a.meta, a.asg, lane);
+  sort_by_expert(a.sel_idx, T * a.k, a.E, s_cnt, s_sel, s_sums, a.off, a.act, a.chunk_off, a.meta, a.asg, lane);
   if (lane == 0) *a.tokens_done = 0u;
 }
 
 // ----------------------------------------------------------------- MFMA tiles
 
-// B operand of one MFMA from one dword of codes (8 elements of a chunk):
-// bf16 128+u (even e) / 128+8u (odd e), or fp16 1024+u / 1024+16u.
+// B operand of one MFMA from one dword of codes (8 elements of a chunk).
+// bf16: 128+u (even e) / 128+8u (odd e), offsets removed afterwards with
+// the activations' per-group correction.
 __device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w) {
   const uint4 v = make_uint4((w & 0x000F000Fu) | 0x43004300u, ((w >> 1) & 0x00780078u) | 0x43004300u,
                              ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 9) & 0x00780078u) | 0x43004300u);
   return __builtin_bit_cast(bf16x8_t, v);
 }
-__device__ __forceinline__ f16x8_t codes_f16(uint32_t w) {
+// fp16 signed codes q = u - 8, exact: (1024+u) - 1032 for even e and
+// (1024+16u)/16 - 72 for odd e, with packed fp16 add / fma.
+__device__ __forceinline__ f16x8_t codes_f16_signed(uint32_t w) {
+  const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2_t sx = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2_t so = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t w8 = w >> 8;
-  const uint4 v = make_uint4((w & 0x000F000Fu) | 0x64006400u, (w & 0x00F000F0u) | 0x64006400u,
-                             (w8 & 0x000F000Fu) | 0x64006400u, (w8 & 0x00F000F0u) | 0x64006400u);
+  const f16x2_t p0 = __builtin_bit_cast(f16x2_t, (w & 0x000F000Fu) | 0x64006400u) + off;
+  const f16x2_t p1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w & 0x00F000F0u) | 0x64006400u), sx, so);
+  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, (w8 & 0x000F000Fu) | 0x64006400u) + off;
+  const f16x2_t p3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w8 & 0x00F000F0u) | 0x64006400u), sx, so);
+  const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
   return __builtin_bit_cast(f16x8_t, v);
 }
 
@@ -297,232 +346,228 @@ __device__ __forceinline__ float scale_of(uint2 sc, int j) {
   const uint32_t d = (j & 2) ? sc.y : sc.x;
   return f16_bits_to_f32((j & 1) ? (d >> 16) : (d & 0xFFFFu));
 }
-
-template <bool HALF>
-__device__ __forceinline__ f32x4_t mfma_group(uint4 act, uint32_t codes) {
-  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (HALF)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, act), codes_f16(codes), z, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, act), codes_bf16(codes), z, 0, 0,
-                                                   0);
+__device__ __forceinline__ void fma4(f32x4_t& acc, float s, f32x4_t c) {
+  acc[0] = fmaf(s, c[0], acc[0]);
+  acc[1] = fmaf(s, c[1], acc[1]);
+  acc[2] = fmaf(s, c[2], acc[2]);
+  acc[3] = fmaf(s, c[3], acc[3]);
 }
 
-// Contraction of one wave's share of K for TPW weight tiles (16 rows each)
-// against up to two token tiles.
-//   K      contraction length (elements); KSPLIT waves share it, each taking
-//          GW = K/32/KSPLIT consecutive groups (a multiple of 4)
-//   wrow   per tile: this lane's weight row (stored codes) and its scales
-//   opnd   operand rows ([row][K] in operand order) and corr ([row][K/32]);
-//          the lane's token of tile tt is row orow[tt], used when ov[tt]
-template <int K, int KSPLIT, bool HALF>
-__device__ __forceinline__ void contract(f32x4_t (&acc)[KSPLIT][2], const uint8_t* const (&wrow)[KSPLIT],
-                                         const uint16_t* const (&srow)[KSPLIT], const uint16_t* __restrict__ opnd,
-                                         const float* __restrict__ corr, const int (&orow)[2], const bool (&ov)[2],
-                                         int ntt, int kpart, int lane) {
-  constexpr int G = K / 32;
-  constexpr int BW = G / KSPLIT / 4;  // 128-element blocks per wave
-  constexpr int NB = BW < 2 ? BW : 2; // blocks per pass
-  static_assert(BW >= 1 && BW % NB == 0, "each wave takes whole blocks");
-  const int q = lane >> 4;
-  for (int ps = 0; ps < BW / NB; ++ps) {
-    const int kb0 = kpart * BW + ps * NB;
-    uint4 wq[KSPLIT][NB];
-    uint2 sc[KSPLIT][NB];
-#pragma unroll
-    for (int i = 0; i < KSPLIT; ++i)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        wq[i][b] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)(kb0 + b) * 64 + 16 * q);
-        sc[i][b] = *reinterpret_cast<const uint2*>(srow[i] + 4 * (kb0 + b));
-      }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt >= ntt) break;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint16_t* op = opnd + (size_t)orow[tt] * K + (kb0 + b) * 128 + 8 * q;
-        uint4 xf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xf[j] = ov[tt] ? *reinterpret_cast<const uint4*>(op + 32 * j) : make_uint4(0u, 0u, 0u, 0u);
-        const float cx = ov[tt] ? corr[(size_t)orow[tt] * G + 4 * (kb0 + b) + q] : 0.f;
-#pragma unroll
-        for (int i = 0; i < KSPLIT; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4_t c = mfma_group<HALF>(xf[j], dword_of(wq[i][b], j));
-            const float s = scale_of(sc[i][b], j);
-            acc[i][tt][0] = fmaf(s, c[0], acc[i][tt][0]);
-            acc[i][tt][1] = fmaf(s, c[1], acc[i][tt][1]);
-            acc[i][tt][2] = fmaf(s, c[2], acc[i][tt][2]);
-            acc[i][tt][3] = fmaf(s, c[3], acc[i][tt][3]);
-          }
-          // sum over the block's 4 groups of corr(token, g) * scale(row, g)
-          acc[i][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cx, scale_of(sc[i][b], q), acc[i][tt], 0, 0, 0);
-        }
-      }
-    }
+// Work item of one wave: (active expert, 16 weight rows, chunk of up to 32
+// tokens).  Item w of an expert-major enumeration: the expert is the last
+// active index i with rows * chunk_off[i] <= w (binary search in LDS);
+// within it, chunks vary fastest so that the waves of a workgroup usually
+// share their weight rows.
+struct WaveItem {
+  int e, rt, tc, p0, n;
+};
+__device__ __forceinline__ WaveItem wave_item(const LayerArgs& a, const int* s_cp, int nact, int rts, int w) {
+  int lo = 0, hi = nact - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rts * s_cp[mid] <= w) lo = mid; else hi = mid - 1;
   }
+  const int nch = s_cp[lo + 1] - s_cp[lo];
+  const int local = w - rts * s_cp[lo];
+  WaveItem it;
+  it.e = a.act[lo];
+  it.rt = local / nch;
+  it.tc = (local - it.rt * nch) * 32;
+  it.p0 = a.off[it.e];
+  it.n = a.off[it.e + 1] - it.p0;
+  return it;
 }
 
 // ----------------------------------------------------------------- gate/up
 
-// Work item: (active expert, 32 rows of f).  KSPLIT waves share K = d and
-// 4/KSPLIT share the 4 weight tiles (gate rows 0-15, 16-31, up rows 0-15,
-// 16-31); tokens in chunks of 32.  Partial tiles meet in LDS, then 128
-// threads form h for (token, 8 rows) each and store it as an fp16 operand
-// chunk, with the group's offset correction.
+// One wave: gate and up rows 16*rt .. 16*rt+15 of expert e for up to 32
+// tokens (two token tiles), the whole of K = d streamed in 128-element
+// blocks with one block of loads in flight ahead of the MFMAs.  Epilogue in
+// registers: h = w_j * silu(g) * u, written as fp16 in operand order
+// (0,4,1,5,2,6,3,7 within each 8 rows) for the down step.
+struct GUStage {
+  uint4 g, u;
+  uint2 sg, su;
+  uint4 x[2][4];
+  float cx[2];
+};
+
+// Every load is unconditional (rows of absent tokens are clamped to a real
+// one and their output rows discarded), so the compiler's count of loads in
+// flight stays exact and a wait never drains the next block's loads.
+template <int D>
+__device__ __forceinline__ void gu_load(GUStage& st, int b, const uint8_t* gr, const uint8_t* ur,
+                                        const uint16_t* gsr, const uint16_t* usr, const uint16_t* xp,
+                                        const float* corr_x, const int (&trow)[2], int q) {
+  st.g = *reinterpret_cast<const uint4*>(gr + b * 64 + 16 * q);
+  st.u = *reinterpret_cast<const uint4*>(ur + b * 64 + 16 * q);
+  st.sg = *reinterpret_cast<const uint2*>(gsr + 4 * b);
+  st.su = *reinterpret_cast<const uint2*>(usr + 4 * b);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint16_t* op = xp + (size_t)trow[tt] * D + b * 128 + 8 * q;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.x[tt][j] = *reinterpret_cast<const uint4*>(op + 32 * j);
+    st.cx[tt] = corr_x[(size_t)trow[tt] * (D / 32) + 4 * b + q];
+  }
+}
+
+__device__ __forceinline__ void gu_compute(const GUStage& st, f32x4_t (&acc)[2][2], int ntt, int q) {
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    if (tt >= ntt) break;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, st.x[tt][j]);
+      const f32x4_t cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, codes_bf16(dword_of(st.g, j)), z, 0, 0, 0);
+      const f32x4_t cu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, codes_bf16(dword_of(st.u, j)), z, 0, 0, 0);
+      fma4(acc[0][tt], scale_of(st.sg, j), cg);
+      fma4(acc[1][tt], scale_of(st.su, j), cu);
+    }
+    // sum over the block's 4 groups of corr(token, g) * scale(row, g)
+    acc[0][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.cx[tt], scale_of(st.sg, q), acc[0][tt], 0, 0, 0);
+    acc[1][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.cx[tt], scale_of(st.su, q), acc[1][tt], 0, 0, 0);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_gateup(const LayerArgs a) {
+  constexpr int NBLK = D / 128;
   constexpr int G = D / 32;
-  constexpr int KSPLIT = G / 4 >= 4 ? 4 : G / 4;
-  constexpr int TPW = KSPLIT;  // tiles per wave
-  __shared__ float P[KSPLIT][4][2][16][16];
-  const int f = a.f, k = a.k;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15;
-  const int kpart = wave % KSPLIT, rpart = wave / KSPLIT;
-  const int rbs = f / 32;
-  const int nitems = a.meta[0] * rbs;
+  __shared__ int s_cp[1025];
+  const int nact = a.meta[0];
+  for (int i = threadIdx.x; i <= nact; i += 256) s_cp[i] = a.chunk_off[i];
+  __syncthreads();
+  const int f = a.f, k = a.k, rts = f / 16;
+  const int total = rts * s_cp[nact];
+  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
   const size_t mq = (size_t)f * (D / 2), ms = (size_t)f * G;
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int ai = item / rbs, rb = item - ai * rbs;
-    const int e = a.act[ai];
-    const int p0 = a.off[e], n = a.off[e + 1] - p0;
-    const uint8_t* wrow[TPW];
-    const uint16_t* srow[TPW];
+  for (int w = blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += gridDim.x * 4) {
+    const WaveItem it = wave_item(a, s_cp, nact, rts, w);
+    const int row = it.rt * 16 + r16;
+    const uint8_t* gr = a.gate_q + it.e * mq + (size_t)row * (D / 2);
+    const uint8_t* ur = a.up_q + it.e * mq + (size_t)row * (D / 2);
+    const uint16_t* gsr = a.gate_s + it.e * ms + (size_t)row * G;
+    const uint16_t* usr = a.up_s + it.e * ms + (size_t)row * G;
+    const int ntt = it.n - it.tc > 16 ? 2 : 1;
+    int trow[2];  // token of this lane's A-operand row (a real one for absent rows)
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int wt = rpart * TPW + i;
-      const int row = rb * 32 + 16 * (wt & 1) + r16;
-      wrow[i] = (wt < 2 ? a.gate_q : a.up_q) + e * mq + (size_t)row * (D / 2);
-      srow[i] = (wt < 2 ? a.gate_s : a.up_s) + e * ms + (size_t)row * G;
+    for (int tt = 0; tt < 2; ++tt) trow[tt] = a.asg[it.p0 + min(it.tc + 16 * tt + r16, it.n - 1)] / k;
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Two stages; the loads past the last block repeat it (unconditional
+    // loads keep the compiler's wait counts exact, so a wait for one block
+    // never drains the next block's loads).
+    GUStage s0, s1;
+    gu_load<D>(s0, 0, gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
+    gu_load<D>(s1, 1, gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
+    for (int b = 0; b < NBLK; b += 2) {
+      gu_compute(s0, acc, ntt, q);
+      gu_load<D>(s0, min(b + 2, NBLK - 1), gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
+      gu_compute(s1, acc, ntt, q);
+      gu_load<D>(s1, min(b + 3, NBLK - 1), gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
     }
-    for (int tc = 0; tc < n; tc += 32) {
-      const int ntt = n - tc > 16 ? 2 : 1;
-      int orow[2];
-      bool ov[2];
+    // lane: weight row r16, tokens 4q+v of each tile
+    const int e8 = r16 & 7;
+    const int col = it.rt * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int pt = tc + 16 * tt + r16;
-        ov[tt] = pt < n;
-        orow[tt] = ov[tt] ? a.asg[p0 + pt] / k : 0;
-      }
-      f32x4_t acc[TPW][2];
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt >= ntt) break;
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      contract<D, KSPLIT, false>(acc, wrow, srow, a.xp, a.corr_x, orow, ov, ntt, kpart, lane);
-#pragma unroll
-      for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          *reinterpret_cast<f32x4_t*>(&P[kpart][rpart * TPW + i][tt][r16][4 * (lane >> 4)]) = acc[i][tt];
-      __syncthreads();
-      if (threadIdx.x < 128) {
-        const int c = threadIdx.x >> 2, m = threadIdx.x & 3;  // token of the chunk, 8-row chunk
-        const int tt = c >> 4, cc = c & 15;
-        const int pt = tc + c;
-        const bool valid = pt < n;
-        const float wj = valid ? a.sel_w[a.asg[p0 + pt]] : 0.f;
-        float hv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * m + i, wt = r >> 4, rr = r & 15;
-          float g = 0.f, u = 0.f;
-#pragma unroll
-          for (int kp = 0; kp < KSPLIT; ++kp) {
-            g += P[kp][wt][tt][rr][cc];
-            u += P[kp][2 + wt][tt][rr][cc];
-          }
-          hv[i] = wj * silu(g) * u;
-        }
-        uint4 o;
-        o.x = pack_f16(hv[0], hv[4]);
-        o.y = pack_f16(hv[1] * 0.0625f, hv[5] * 0.0625f);
-        o.z = pack_f16(hv[2], hv[6]);
-        o.w = pack_f16(hv[3] * 0.0625f, hv[7] * 0.0625f);
-        const float ev = (f16_lo(o.x) + f16_hi(o.x)) + (f16_lo(o.z) + f16_hi(o.z));
-        const float od = (f16_lo(o.y) + f16_hi(o.y)) + (f16_lo(o.w) + f16_hi(o.w));
-        const float cr = seg_sum<4>(-1032.0f * ev - 1152.0f * od);
-        if (valid) {
-          *reinterpret_cast<uint4*>(a.h16 + (size_t)(p0 + pt) * f + rb * 32 + 8 * m) = o;
-          if (m == 0) a.corr_h[(size_t)(p0 + pt) * (f / 32) + rb] = cr;
+      for (int v = 0; v < 4; ++v) {
+        const int pt = it.tc + 16 * tt + 4 * q + v;
+        if (pt < it.n) {
+          const float wj = a.sel_w[a.asg[it.p0 + pt]];
+          const float h = wj * silu(acc[0][tt][v]) * acc[1][tt][v];
+          a.h16[(size_t)(it.p0 + pt) * f + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
       }
-      __syncthreads();
     }
   }
 }
 
 // ----------------------------------------------------------------- down
 
-// Work item: (active expert, 64 rows of d) = 4 weight tiles; K = f.  The
-// summed tiles give o_{t,j} for every assignment of the expert, written to
+// One wave: rows 16*rt .. 16*rt+15 of W_d[e] for up to 32 tokens, K = f;
+// signed fp16 codes against the fp16 h operands.  o_{t,j} goes to
 // obuf[t*k + j][row].
+struct DStage {
+  uint4 w;
+  uint2 s;
+  uint4 h[2][4];
+};
+
+template <int F>
+__device__ __forceinline__ void dn_load(DStage& st, int b, const uint8_t* wr, const uint16_t* sr,
+                                        const uint16_t* h16, const int (&prow)[2], int q) {
+  st.w = *reinterpret_cast<const uint4*>(wr + b * 64 + 16 * q);
+  st.s = *reinterpret_cast<const uint2*>(sr + 4 * b);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint16_t* op = h16 + (size_t)prow[tt] * F + b * 128 + 8 * q;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.h[tt][j] = *reinterpret_cast<const uint4*>(op + 32 * j);
+  }
+}
+
+__device__ __forceinline__ void dn_compute(const DStage& st, f32x4_t (&acc)[2], int ntt) {
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x8_t wb = codes_f16_signed(dword_of(st.w, j));
+    const float s = scale_of(st.s, j);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt >= ntt) break;
+      const f32x4_t c =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, st.h[tt][j]), wb, z, 0, 0, 0);
+      fma4(acc[tt], s, c);
+    }
+  }
+}
+
 template <int F>
 __global__ __launch_bounds__(256) void k_down(const LayerArgs a) {
+  constexpr int NBLK = F / 128;
   constexpr int G = F / 32;
-  constexpr int KSPLIT = G / 4 >= 4 ? 4 : G / 4;
-  constexpr int TPW = KSPLIT;
-  __shared__ float P[KSPLIT][4][2][16][16];
-  const int d = a.d;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15;
-  const int kpart = wave % KSPLIT, rpart = wave / KSPLIT;
-  const int rbs = d / 64;
-  const int nitems = a.meta[0] * rbs;
+  __shared__ int s_cp[1025];
+  const int nact = a.meta[0];
+  for (int i = threadIdx.x; i <= nact; i += 256) s_cp[i] = a.chunk_off[i];
+  __syncthreads();
+  const int d = a.d, rts = d / 16;
+  const int total = rts * s_cp[nact];
+  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
   const size_t mq = (size_t)d * (F / 2), ms = (size_t)d * G;
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int ai = item / rbs, rb = item - ai * rbs;
-    const int e = a.act[ai];
-    const int p0 = a.off[e], n = a.off[e + 1] - p0;
-    const uint8_t* wrow[TPW];
-    const uint16_t* srow[TPW];
+  for (int w = blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += gridDim.x * 4) {
+    const WaveItem it = wave_item(a, s_cp, nact, rts, w);
+    const int row = it.rt * 16 + r16;
+    const uint8_t* wr = a.down_q + it.e * mq + (size_t)row * (F / 2);
+    const uint16_t* sr = a.down_s + it.e * ms + (size_t)row * G;
+    const int ntt = it.n - it.tc > 16 ? 2 : 1;
+    int prow[2];  // position of this lane's A-operand row (a real one for absent rows)
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int row = rb * 64 + 16 * (rpart * TPW + i) + r16;
-      wrow[i] = a.down_q + e * mq + (size_t)row * (F / 2);
-      srow[i] = a.down_s + e * ms + (size_t)row * G;
+    for (int tt = 0; tt < 2; ++tt) prow[tt] = it.p0 + min(it.tc + 16 * tt + r16, it.n - 1);
+    f32x4_t acc[2];
+    acc[0] = acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    DStage s0, s1;
+    dn_load<F>(s0, 0, wr, sr, a.h16, prow, q);
+    dn_load<F>(s1, min(1, NBLK - 1), wr, sr, a.h16, prow, q);
+    for (int b = 0; b < NBLK; b += 2) {
+      dn_compute(s0, acc, ntt);
+      dn_load<F>(s0, min(b + 2, NBLK - 1), wr, sr, a.h16, prow, q);
+      if (b + 1 < NBLK) dn_compute(s1, acc, ntt);
+      dn_load<F>(s1, min(b + 3, NBLK - 1), wr, sr, a.h16, prow, q);
     }
-    for (int tc = 0; tc < n; tc += 32) {
-      const int ntt = n - tc > 16 ? 2 : 1;
-      int orow[2];
-      bool ov[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int pt = tc + 16 * tt + r16;
-        ov[tt] = pt < n;
-        orow[tt] = ov[tt] ? p0 + pt : 0;
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt >= ntt) break;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int pt = it.tc + 16 * tt + 4 * q + v;
+        if (pt < it.n) a.obuf[(size_t)a.asg[it.p0 + pt] * d + row] = acc[tt][v];
       }
-      f32x4_t acc[TPW][2];
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      contract<F, KSPLIT, true>(acc, wrow, srow, a.h16, a.corr_h, orow, ov, ntt, kpart, lane);
-#pragma unroll
-      for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          *reinterpret_cast<f32x4_t*>(&P[kpart][rpart * TPW + i][tt][r16][4 * (lane >> 4)]) = acc[i][tt];
-      __syncthreads();
-      {
-        const int c = threadIdx.x >> 3, m = threadIdx.x & 7;  // token of the chunk, 8 rows
-        const int tt = c >> 4, cc = c & 15;
-        const int pt = tc + c;
-        if (pt < n) {
-          float v[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int r = 8 * m + i, wt = r >> 4, rr = r & 15;
-            float s = 0.f;
-#pragma unroll
-            for (int kp = 0; kp < KSPLIT; ++kp) s += P[kp][wt][tt][rr][cc];
-            v[i] = s;
-          }
-          float4* dst = reinterpret_cast<float4*>(a.obuf + (size_t)a.asg[p0 + pt] * d + rb * 64 + 8 * m);
-          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
-      }
-      __syncthreads();
     }
   }
 }
@@ -560,7 +605,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf,
 template <int D, int EPL>
 static void router_launch(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, int32_t* io,
                           float* wo, uint16_t* xt, hipStream_t s) {
-  hipLaunchKernelGGL((k_router<D, EPL>), dim3((a.E + 3) / 4, T), dim3(256), 0, s, a, x, r, eps, T, io, wo, xt);
+  hipLaunchKernelGGL((k_router<D, EPL>), dim3((a.E + 3) / 4, (T + kRouterTokens - 1) / kRouterTokens), dim3(256), 0,
+                     s, a, x, r, eps, T, io, wo, xt);
 }
 
 template <int D>
@@ -593,11 +639,17 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
   return hipGetLastError();
 }
 
-static int grid_for(int items) { return items < kMaxGroupedGrid ? items : kMaxGroupedGrid; }
+// Wave items: (active expert, 16-row tile, 32-token chunk); at most
+// min(E, T*k) active experts and T*k/32 extra chunks.
+static int grid_for(const LayerArgs& a, int T, int rows) {
+  const int Tk = T * a.k;
+  const int chunks = (a.E < Tk ? a.E : Tk) + Tk / 32;
+  const int wgs = (chunks * (rows / 16) + 3) / 4;
+  return wgs < kMaxGroupedGrid ? wgs : kMaxGroupedGrid;
+}
 
 hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
-  const int items = (a.E < T * a.k ? a.E : T * a.k) * (a.f / 32);
-  const dim3 g(grid_for(items)), b(256);
+  const dim3 g(grid_for(a, T, a.f)), b(256);
   switch (a.d) {
     case 256: hipLaunchKernelGGL((k_gateup<256>), g, b, 0, s, a); break;
     case 512: hipLaunchKernelGGL((k_gateup<512>), g, b, 0, s, a); break;
@@ -611,8 +663,7 @@ hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
 }
 
 hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
-  const int items = (a.E < T * a.k ? a.E : T * a.k) * (a.d / 64);
-  const dim3 g(grid_for(items)), b(256);
+  const dim3 g(grid_for(a, T, a.d)), b(256);
   switch (a.f) {
     case 128: hipLaunchKernelGGL((k_down<128>), g, b, 0, s, a); break;
     case 256: hipLaunchKernelGGL((k_down<256>), g, b, 0, s, a); break;

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_decode.h"
+
 namespace moe {
 
 // Device pointers of one MoE layer plus the per-call workspace carve-up.
@@ -20,7 +22,7 @@ struct LayerArgs {
   const uint16_t* down_s;
   // workspace of the batched path
   float* logits;          // [T][E]
-  unsigned* counters;     // [T] arrival counters, zero between calls
+  unsigned* counters;     // arrival counter per block of 4 tokens, one per 128 B line; zero between calls
   unsigned* tokens_done;  // [1] tokens whose top-k is done, zero between calls
   int32_t* sel_idx;       // [T][k] chosen experts of assignment t*k + j
   float* sel_w;           // [T][k] their weights
@@ -28,10 +30,10 @@ struct LayerArgs {
   float* corr_x;          // [T][d/32] their per-group offset corrections
   int32_t* off;           // [E+1] first position of each expert in asg
   int32_t* act;           // [E] experts with assignments, ascending
+  int32_t* chunk_off;     // [E+1] 32-token chunks of the active experts before each
   int32_t* meta;          // [0]: number of such experts
   int32_t* asg;           // [T*k] assignments grouped by expert
   uint16_t* h16;          // [T*k][f] w_j silu(g) u per position, fp16 operand order
-  float* corr_h;          // [T*k][f/32] their per-group offset corrections
   float* obuf;            // [T*k][d] o_{t,j} per assignment
   // single-launch step (T = 1)
   unsigned long long* tagged_logits;  // ceil(E/4) lines of 128 B: (epoch << 32 | logit bits)
@@ -41,7 +43,8 @@ struct LayerArgs {
 };
 
 constexpr int kMaxFusedGrid = 1024;
-constexpr int kMaxGroupedGrid = 1024;  // persistent grid of the expert-grouped kernels
+constexpr int kMaxGroupedGrid = 1024;
+constexpr int kMaxAssignments = MOE_MAX_TOKENS * MOE_MAX_TOPK;  // largest T*k  // persistent grid of the expert-grouped kernels
 
 // Arguments of the single-launch 1-token layer kernel.
 struct FusedArgs {
@@ -53,8 +56,12 @@ struct FusedArgs {
   const uint16_t* up_s;
   const uint8_t* down_q;
   const uint16_t* down_s;
-  const uint16_t* x;     // [d] bf16
-  float* y;              // [d]
+  const uint16_t* x;     // [d] bf16 (unused when resid_in is set)
+  float* y;              // [d], or NULL in a stack
+  const float* resid_in; // stack: fp32 residual r_l [d]; x = bf16(r / rms(r)); NULL otherwise
+  float* resid_out;      // stack: r_{l+1} = r_l + y (a different buffer from resid_in)
+  float eps;
+  uint16_t* x_trace;     // stack: x_l [d], or NULL
   int32_t* idx_out;      // [k] or NULL
   float* w_out;          // [k] or NULL
   unsigned long long* logits;  // tagged logits, 4 per 128-byte line

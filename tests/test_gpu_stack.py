@@ -80,28 +80,47 @@ def end_to_end(layers_o, cfg, X0, r_gpu):
         assert err <= Y_TOL * np.abs(ro).max(), f"token {t}: final residual err {err:.3e}"
 
 
-@pytest.mark.parametrize("seed", [1, 2])
-def test_tiny_stack_49_layers(seed):
+@pytest.mark.parametrize("seed,T", [(1, 3), (2, 1), (3, 1)], ids=["T3-batched", "T1-fused-a", "T1-fused-b"])
+def test_tiny_stack_49_layers(seed, T):
+    """49 layers (odd: the single-launch stack ends with one residual copy)."""
     cfg = synth.TINY
     layers_np = [synth.make_layer(cfg, seed, l) for l in range(49)]
     layers_o = [OM.Layer.from_dict(l) for l in layers_np]
-    X0 = tokens(cfg, layers_o[0], seed, 3)
+    X0 = tokens(cfg, layers_o[0], seed, T)
     r, xt, yt, it = run_stack(layers_np, cfg, X0)
     below = check_teacher_forced(layers_o, cfg, X0, r, xt, yt, it)
     if below == 0:
         end_to_end(layers_o, cfg, X0, r)
 
 
-def test_flagship_stack_first_layers():
-    """The first 8 layers of the 49-layer stack at the flagship shape, 2 tokens."""
+@pytest.mark.parametrize("L,T", [(8, 2), (8, 1), (7, 1)], ids=["L8-T2-batched", "L8-T1-fused", "L7-T1-fused"])
+def test_flagship_stack_first_layers(L, T):
+    """The first layers of the 49-layer stack at the flagship shape."""
     cfg = synth.STACK
-    layers_np = [synth.make_layer(cfg, 1, l) for l in range(8)]
+    layers_np = [synth.make_layer(cfg, 1, l) for l in range(L)]
     layers_o = [OM.Layer.from_dict(l) for l in layers_np]
-    X0 = tokens(cfg, layers_o[0], 1, 2)
+    X0 = tokens(cfg, layers_o[0], 1, T)
     r, xt, yt, it = run_stack(layers_np, cfg, X0)
     below = check_teacher_forced(layers_o, cfg, X0, r, xt, yt, it)
     if below == 0:
         end_to_end(layers_o, cfg, X0, r)
+
+
+def test_fused_and_batched_stacks_agree():
+    """The same 6 flagship layers and token through the single-launch stack
+    (T=1) and the batched one (the token twice, T=2): same experts, outputs
+    within the tolerance of each other."""
+    import torch
+    cfg = synth.STACK
+    layers_np = [synth.make_layer(cfg, 2, l) for l in range(6)]
+    X0 = tokens(cfg, OM.Layer.from_dict(layers_np[0]), 2, 1)
+    r1, x1, y1, i1 = run_stack(layers_np, cfg, X0)
+    r2, x2, y2, i2 = run_stack(layers_np, cfg, np.concatenate([X0, X0]))
+    for l in range(6):
+        assert np.array_equal(np.sort(i1[l, 0]), np.sort(i2[l, 0])), f"layer {l}"
+        assert np.array_equal(np.sort(i2[l, 0]), np.sort(i2[l, 1]))
+    assert np.abs(r1[0] - r2[0]).max() <= Y_TOL * np.abs(r2[0]).max()
+    assert np.array_equal(r2[0], r2[1])
 
 
 def test_stack_of_zero_layers_keeps_the_residual():
