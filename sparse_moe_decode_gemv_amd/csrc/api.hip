@@ -13,8 +13,8 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 struct Layout {
-  size_t counters, logits, sel_idx, sel_w, xp, corr_x, off, act, chunk_off, asg, h16, obuf, resid, tagged, hrec,
-      epoch, total;
+  size_t counters, logits, sel_idx, sel_w, xp, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
+      hrec, epoch, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -46,10 +46,10 @@ Layout layout_of(const moe_layer_desc* d) {
   L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
   L.sel_w = o, o += align256(Tk * sizeof(float));
   L.xp = o, o += align256(T * d_ * sizeof(uint16_t));
-  L.corr_x = o, o += align256(T * (d_ / 32) * sizeof(float));
   L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
   L.act = o, o += align256(E * sizeof(int32_t));
   L.chunk_off = o, o += align256((E + 1) * sizeof(int32_t));
+  L.chunks = o, o += align256(((E < Tk ? E : Tk) + Tk / 32) * 4 * sizeof(int32_t));
   L.asg = o, o += align256(Tk * sizeof(int32_t));
   L.h16 = o, o += align256(Tk * f_ * sizeof(uint16_t));
   L.obuf = o, o += align256(Tk * d_ * sizeof(float));
@@ -140,11 +140,11 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
   a.xp = reinterpret_cast<uint16_t*>(base + L.xp);
-  a.corr_x = reinterpret_cast<float*>(base + L.corr_x);
   a.off = reinterpret_cast<int32_t*>(base + L.off);
   a.meta = a.off + desc->n_experts + 1;
   a.act = reinterpret_cast<int32_t*>(base + L.act);
   a.chunk_off = reinterpret_cast<int32_t*>(base + L.chunk_off);
+  a.chunks = reinterpret_cast<int4*>(base + L.chunks);
   a.asg = reinterpret_cast<int32_t*>(base + L.asg);
   a.h16 = reinterpret_cast<uint16_t*>(base + L.h16);
   a.obuf = reinterpret_cast<float*>(base + L.obuf);

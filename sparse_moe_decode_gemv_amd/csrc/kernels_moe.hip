@@ -7,15 +7,15 @@
 //             one wave each; the last token to finish sorts the T*k (token,
 //             slot) assignments by expert (a stable counting sort built from
 //             wave ballots).  Workgroup 0 also writes each token's
-//             activations in MFMA operand order with their per-group offset
-//             corrections.  In the stack the router applies the pre-norm
-//             (RMSNorm) to the residual.
-//   gate/up : one wave per (chosen expert, 16 rows, chunk of up to 32 of its
-//             tokens): int4 x bf16 MFMA tiles, so each chosen expert's
-//             weights are read once per call however many tokens chose it;
-//             SwiGLU in registers; h = w_j silu(g) u stored as fp16 operands
-//             of the down step.
-//   down    : the same shape of work over W_d with int4 x fp16 MFMA; each
+//             activations in MFMA operand order (fp16).  In the stack the
+//             router applies the pre-norm (RMSNorm) to the residual.
+//   gate/up : one workgroup per (chunk of up to 32 tokens of one chosen
+//             expert, 64 rows of f): the chunk's activations staged in LDS,
+//             int4 weights dequantized into MFMA operands, so each chosen
+//             expert's weights are read once per call however many tokens
+//             chose it; SwiGLU in registers; h = w_j silu(g) u stored as
+//             fp16 operands of the down step.
+//   down    : the same over W_d (128 rows of d per workgroup); each
 //             assignment's o_{t,j} in fp32.
 //   combine : y_t = sum_j o_{t,j} in slot order (deterministic); in the
 //             stack the residual add is folded in.
@@ -24,18 +24,19 @@
 // transcript 02:35); kernels for low-bit projections, MoE routing and
 // prompt processing are named in the same source (06:11).
 //
-// MFMA operands.  v_mfma_f32_16x16x32_{bf16,f16}: lane l supplies row l%16
-// of A and column l%16 of B, each with the 8 consecutive k of chunk l/16;
-// lane l receives D[4*(l/16)+v][l%16], v = 0..3.  A holds 16 tokens'
-// activations, B 16 weight rows, so every lane ends with one weight row and
-// four tokens, and one group scale per lane applies to all four.  One dword
-// of stored codes is the 8 elements of one chunk; its 8 operand values come
-// out of the magic-number conversion in the order e = 0,4,1,5,2,6,3,7 (see
-// device_common.h) and the activation operands are stored in that order.
-// gate/up: bf16 128+u / 128+8u against x / x/8, the offsets removed by the
-// per-group correction times the scale, one fp32 MFMA (16x16x4) per four
-// groups.  down: the codes become exact signed fp16 q = u - 8 with packed
-// fp16 arithmetic, so h needs no correction.
+// MFMA operands.  v_mfma_f32_16x16x32_f16: lane l supplies row l%16 of A
+// and column l%16 of B, each with the 8 consecutive k of chunk l/16; lane l
+// receives D[4*(l/16)+v][l%16], v = 0..3.  A holds 16 tokens' activations
+// (or h), B 16 weight rows, so every lane holds one weight row: the 8 codes
+// of one chunk of one group (one stored dword) with that group's scale.
+// The lane turns them into fp16 q*s (q = u - 8 exact via the magic number
+// 1024, times the scale: one rounding, relative error <= 2^-11), in the
+// order e = 0,4,1,5,2,6,3,7 that the magic-number extraction yields (see
+// device_common.h); the activation operands are stored in that same order.
+// The MFMAs then accumulate over all of K in their C operand.  The
+// activations are fp16 here (finite bf16 activations below 65504 in
+// magnitude convert exactly, except that magnitudes under 2^-14 lose low
+// bits, an absolute error below 2^-25).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -103,10 +104,12 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 //   asg[p]                the assignment at position p
 //   act[i], i < meta[0]   the experts with at least one assignment, ascending
 //   chunk_off[i]          32-token chunks of the active experts before act[i]
-//                         (chunk_off[meta[0]] = all chunks)
-// cnt: LDS [E]; ssel: LDS [Tk]; sums: LDS [192].
-__device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int* ssel, int* sums, int32_t* off,
-                               int32_t* act, int32_t* chunk_off, int32_t* meta, int32_t* asg, int lane) {
+//                         (chunk_off[meta[0]] = all chunks = meta[1])
+//   chunks[c]             chunk c: (expert, first position, positions <= 32)
+// cnt: LDS [E]; ssel: LDS [Tk].
+__device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int* ssel, int32_t* off,
+                               int32_t* act, int32_t* chunk_off, int4* chunks, int32_t* meta, int32_t* asg,
+                               int lane) {
   // the chosen experts into LDS, 8 loads in flight per lane
   for (int c0 = 0; c0 < Tk; c0 += 512) {
     int v[8];
@@ -136,16 +139,20 @@ __device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int*
     na += n > 0;
     nc += (n + 31) >> 5;
   }
-  sums[lane] = s;
-  sums[64 + lane] = na;
-  sums[128 + lane] = nc;
-  lds_wait();
-  int base = 0, abase = 0, cbase = 0;
-  for (int l = 0; l < lane; ++l) {
-    base += sums[l];
-    abase += sums[64 + l];
-    cbase += sums[128 + l];
+  // exclusive prefix sums over lanes, log steps
+  int base = s, abase = na, cbase = nc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int b1 = __shfl_up(base, o, 64), b2 = __shfl_up(abase, o, 64), b3 = __shfl_up(cbase, o, 64);
+    if (lane >= o) {
+      base += b1;
+      abase += b2;
+      cbase += b3;
+    }
   }
+  base -= s;
+  abase -= na;
+  cbase -= nc;
   for (int e = e0; e < e1; ++e) {
     const int n = cnt[e];
     off[e] = base;
@@ -153,7 +160,7 @@ __device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int*
       act[abase] = e;
       chunk_off[abase] = cbase;
       ++abase;
-      cbase += (n + 31) >> 5;
+      for (int tc = 0; tc < n; tc += 32) chunks[cbase++] = make_int4(e, base + tc, min(32, n - tc), 0);
     }
     cnt[e] = base;  // from here on: the next free position of expert e
     base += n;
@@ -162,6 +169,7 @@ __device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int*
     off[E] = base;
     chunk_off[abase] = cbase;
     meta[0] = abase;
+    meta[1] = cbase;
   }
   lds_wait();
   for (int c = 0; c < Tk; c += 64) {  // placement, stable in a
@@ -194,10 +202,8 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
                                                 int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                 uint16_t* __restrict__ x_trace) {
   constexpr int NI = D / 256;  // float4 columns per lane: 4*lane + 256*i
-  constexpr int G = D / 32;
   __shared__ int s_cnt[1024];
   __shared__ int s_sel[kMaxAssignments];
-  __shared__ int s_sums[192];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
@@ -208,6 +214,22 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
   for (int i = 0; i < NI; ++i) w[i] = wrow[64 * i + lane];
   const float bias = row_ok && a.router_b ? a.router_b[e] : 0.f;
 
+  // the block's bf16 activations, all loads issued before any is used
+  constexpr bool XPRE = NI * kRouterTokens <= 32;
+  uint2 xq[XPRE ? kRouterTokens : 1][XPRE ? NI : 1];
+  if constexpr (XPRE) {
+    if (x) {
+#pragma unroll
+      for (int tb = 0; tb < kRouterTokens; ++tb) {
+        const uint2* xr =
+            reinterpret_cast<const uint2*>(x + (size_t)min(blockIdx.y * kRouterTokens + tb, T - 1) * D);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) xq[tb][i] = xr[64 * i + lane];
+      }
+    }
+  }
+
+#pragma unroll
   for (int tb = 0; tb < kRouterTokens; ++tb) {
     const int t = blockIdx.y * kRouterTokens + tb;
     if (t >= T) break;
@@ -216,7 +238,9 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
       const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)t * D);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const uint2 q = xr[64 * i + lane];
+        uint2 q;
+        if constexpr (XPRE) q = xq[tb][i];
+        else q = xr[64 * i + lane];
         xv[i][0] = bf16_bits_to_f32(q.x & 0xFFFFu);
         xv[i][1] = bf16_bits_to_f32(q.x >> 16);
         xv[i][2] = bf16_bits_to_f32(q.y & 0xFFFFu);
@@ -252,25 +276,22 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
     }
 
     if (blockIdx.x == 0 && wave == tb) {
-      // The token's MFMA operand row: chunk of 8 elements stored as
-      // (x0, x4, x1/8, x5/8, x2, x6, x3/8, x7/8); lane 2m holds x0..x3 of a
-      // chunk and lane 2m+1 holds x4..x7, so neighbours trade halves.  Per
-      // group of 32 (8 lanes): corr = -136 * sum(even e) - 24 * sum(odd e).
+      // The token's MFMA operand row: fp16, each chunk of 8 elements stored
+      // as (x0, x4, x1, x5, x2, x6, x3, x7); lane 2m holds x0..x3 of a chunk
+      // and lane 2m+1 holds x4..x7, so neighbours trade halves.
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const float o0 = dpp_f<kDppXor1>(xv[i][0]), o1 = dpp_f<kDppXor1>(xv[i][1]);
         const float o2 = dpp_f<kDppXor1>(xv[i][2]), o3 = dpp_f<kDppXor1>(xv[i][3]);
         uint2 pk;
         if ((lane & 1) == 0) {
-          pk.x = pack_bf16(xv[i][0], o0);
-          pk.y = pack_bf16(xv[i][1] * 0.125f, o1 * 0.125f);
+          pk.x = pack_f16(xv[i][0], o0);
+          pk.y = pack_f16(xv[i][1], o1);
         } else {
-          pk.x = pack_bf16(o2, xv[i][2]);
-          pk.y = pack_bf16(o3 * 0.125f, xv[i][3] * 0.125f);
+          pk.x = pack_f16(o2, xv[i][2]);
+          pk.y = pack_f16(o3, xv[i][3]);
         }
         reinterpret_cast<uint2*>(a.xp + (size_t)t * D)[64 * i + lane] = pk;
-        const float cr = seg_sum<8>(-136.0f * (xv[i][0] + xv[i][2]) - 24.0f * (xv[i][1] + xv[i][3]));
-        if ((lane & 7) == 0) a.corr_x[(size_t)t * G + (256 * i + 4 * lane) / 32] = cr;
       }
     }
 
@@ -310,174 +331,223 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != (unsigned)(T - 1)) return;
   // the last token: group the assignments by expert
-  sort_by_expert(a.sel_idx, T * a.k, a.E, s_cnt, s_sel, s_sums, a.off, a.act, a.chunk_off, a.meta, a.asg, lane);
+  sort_by_expert(a.sel_idx, T * a.k, a.E, s_cnt, s_sel, a.off, a.act, a.chunk_off, a.chunks, a.meta, a.asg,
+                 lane);
   if (lane == 0) *a.tokens_done = 0u;
 }
 
 // ----------------------------------------------------------------- MFMA tiles
 
-// B operand of one MFMA from one dword of codes (8 elements of a chunk).
-// bf16: 128+u (even e) / 128+8u (odd e), offsets removed afterwards with
-// the activations' per-group correction.
-__device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w) {
-  const uint4 v = make_uint4((w & 0x000F000Fu) | 0x43004300u, ((w >> 1) & 0x00780078u) | 0x43004300u,
-                             ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 9) & 0x00780078u) | 0x43004300u);
-  return __builtin_bit_cast(bf16x8_t, v);
+__device__ __forceinline__ uint32_t dword_of(uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+
+// 0x64006400 held in a VGPR the compiler cannot see into, so that each
+// (mask, magic) pair is one 3-input bitwise instruction (a VALU instruction
+// takes at most one literal).
+__device__ __forceinline__ uint32_t magic_f16x2() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
 }
-// fp16 signed codes q = u - 8, exact: (1024+u) - 1032 for even e and
-// (1024+16u)/16 - 72 for odd e, with packed fp16 add / fma.
-__device__ __forceinline__ f16x8_t codes_f16_signed(uint32_t w) {
+
+// B operand of one MFMA: the 8 codes of one dword as fp16 q * s, with s2
+// the group's binary16 scale in both halves and magic = 0x64006400.
+__device__ __forceinline__ f16x8_t dequant_f16(uint32_t w, f16x2_t s2, uint32_t magic) {
   const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const f16x2_t sx = {(_Float16)0.0625f, (_Float16)0.0625f};
   const f16x2_t so = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t w8 = w >> 8;
-  const f16x2_t p0 = __builtin_bit_cast(f16x2_t, (w & 0x000F000Fu) | 0x64006400u) + off;
-  const f16x2_t p1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w & 0x00F000F0u) | 0x64006400u), sx, so);
-  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, (w8 & 0x000F000Fu) | 0x64006400u) + off;
-  const f16x2_t p3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w8 & 0x00F000F0u) | 0x64006400u), sx, so);
-  const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+  // exact q: (1024+u) - 1032 for even e, (1024+16u)/16 - 72 for odd e
+  const f16x2_t q0 = __builtin_bit_cast(f16x2_t, (w & 0x000F000Fu) | magic) + off;
+  const f16x2_t q1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w & 0x00F000F0u) | magic), sx, so);
+  const f16x2_t q2 = __builtin_bit_cast(f16x2_t, (w8 & 0x000F000Fu) | magic) + off;
+  const f16x2_t q3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w8 & 0x00F000F0u) | magic), sx, so);
+  const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, q0 * s2), __builtin_bit_cast(uint32_t, q1 * s2),
+                             __builtin_bit_cast(uint32_t, q2 * s2), __builtin_bit_cast(uint32_t, q3 * s2));
   return __builtin_bit_cast(f16x8_t, v);
 }
 
-__device__ __forceinline__ uint32_t dword_of(uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
-// binary16 scale j (0..3) of the four packed in sc
-__device__ __forceinline__ float scale_of(uint2 sc, int j) {
+// scale j (0..3) of the four binary16 scales in sc, in both halves
+__device__ __forceinline__ f16x2_t scale2(uint2 sc, int j) {
   const uint32_t d = (j & 2) ? sc.y : sc.x;
-  return f16_bits_to_f32((j & 1) ? (d >> 16) : (d & 0xFFFFu));
-}
-__device__ __forceinline__ void fma4(f32x4_t& acc, float s, f32x4_t c) {
-  acc[0] = fmaf(s, c[0], acc[0]);
-  acc[1] = fmaf(s, c[1], acc[1]);
-  acc[2] = fmaf(s, c[2], acc[2]);
-  acc[3] = fmaf(s, c[3], acc[3]);
+  return __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d, d, (j & 1) ? 0x03020302u : 0x01000100u));
 }
 
-// Work item of one wave: (active expert, 16 weight rows, chunk of up to 32
-// tokens).  Item w of an expert-major enumeration: the expert is the last
-// active index i with rows * chunk_off[i] <= w (binary search in LDS);
-// within it, chunks vary fastest so that the waves of a workgroup usually
-// share their weight rows.
-struct WaveItem {
-  int e, rt, tc, p0, n;
+// ----------------------------------------------------------------- grouped items
+
+// Work item of one workgroup: (chunk of up to 32 positions of one expert,
+// group of weight rows); item w is chunk w / ngroups, row group w % ngroups,
+// so the row groups of a chunk are consecutive.  The chunk table is read
+// directly (one round trip from the start of the kernel to the operand
+// loads' addresses).
+struct Item {
+  int e, rg, p0, n;
 };
-__device__ __forceinline__ WaveItem wave_item(const LayerArgs& a, const int* s_cp, int nact, int rts, int w) {
-  int lo = 0, hi = nact - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (rts * s_cp[mid] <= w) lo = mid; else hi = mid - 1;
-  }
-  const int nch = s_cp[lo + 1] - s_cp[lo];
-  const int local = w - rts * s_cp[lo];
-  WaveItem it;
-  it.e = a.act[lo];
-  it.rt = local / nch;
-  it.tc = (local - it.rt * nch) * 32;
-  it.p0 = a.off[it.e];
-  it.n = a.off[it.e + 1] - it.p0;
+__device__ __forceinline__ Item item_of(const LayerArgs& a, int ngroups, int w) {
+  const int c = w / ngroups;
+  const int4 cd = a.chunks[c];
+  Item it;
+  it.e = cd.x;
+  it.p0 = cd.y;
+  it.n = cd.z;
+  it.rg = w - c * ngroups;
   return it;
+}
+
+// The operand rows of one 128-element block of K for the item's (up to) 32
+// rows (tokens or positions), in LDS in fragment order: v[tt][j][q][slot]
+// is chunk q of group j of row 16*tt + r, at slot r ^ swz(j, q), so that
+// the 64 lanes of a wave read one (tt, j) as 1 KB with every 16 lanes
+// covering all banks, and the staging stores (8 rows x 8 parts per wave)
+// hit distinct banks too.
+struct OpTile {
+  uint4 v[2][4][4][16];
+};
+__device__ __forceinline__ int swz(int j, int q) { return (4 * j + 2 * (q >> 1)) & 15; }
+
+// Thread i stages 32 bytes (16 elements: group p/2, chunks 2(p%2) and
+// 2(p%2)+1) of row c = i/8, part p = i%8.
+struct StageRegs {
+  uint4 a, b;
+};
+__device__ __forceinline__ StageRegs stage_load(int blk, const uint16_t* row_c, int tid) {
+  const uint4* src = reinterpret_cast<const uint4*>(row_c + blk * 128 + 16 * (tid & 7));
+  StageRegs r;
+  r.a = src[0];
+  r.b = src[1];
+  return r;
+}
+__device__ __forceinline__ void stage_store(OpTile& t, const StageRegs& r, int tid) {
+  const int c = tid >> 3, p = tid & 7;
+  const int j = p >> 1, q0 = 2 * (p & 1), r16 = c & 15;
+  t.v[c >> 4][j][q0][r16 ^ swz(j, q0)] = r.a;
+  t.v[c >> 4][j][q0 + 1][r16 ^ swz(j, q0 + 1)] = r.b;
+}
+
+// Weights of one block for one 16-row tile: this lane's row, chunk q of the
+// block's 4 groups, and the 4 group scales.
+struct WBlk {
+  uint4 q;
+  uint2 s;
+};
+__device__ __forceinline__ WBlk wload(const uint8_t* row, const uint16_t* srow, int blk, int q) {
+  WBlk w;
+  w.q = *reinterpret_cast<const uint4*>(row + blk * 64 + 16 * q);
+  w.s = *reinterpret_cast<const uint2*>(srow + 4 * blk);
+  return w;
+}
+
+// One block of K for two weight tiles against NTT (1 or 2) staged token tiles.
+template <int NTT>
+__device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][2], const OpTile& t, const WBlk (&w)[2], int lane,
+                                           uint32_t magic) {
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f16x8_t wb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wb[i] = dequant_f16(dword_of(w[i].q, j), scale2(w[i].s, j), magic);
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const f16x8_t xa = __builtin_bit_cast(f16x8_t, t.v[tt][j][q][r16 ^ swz(j, q)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, wb[i], acc[i][tt], 0, 0, 0);
+    }
+  }
+}
+
+// The K loop shared by both kernels: NBLK blocks; the operand tile is
+// double-buffered in LDS (one barrier per block) and fed from a ring of up
+// to 2 blocks of staging loads in registers.  Each wave's two weight tiles
+// come in groups of G = 4 consecutive blocks, double-buffered: the loads of
+// group g+1 are issued together when group g starts, so that every row is
+// requested as 256 contiguous bytes in one burst (a row's 64-byte pieces
+// fetched one block at a time, far apart in time, leave most of each DRAM
+// page unused).  Every global load is unconditional (rows past the chunk
+// are clamped to a real one and their outputs dropped), so the compiler's
+// wait counts stay exact.
+template <int K, int NTT>
+__device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, const uint16_t* op_row,
+                                       const uint8_t* const (&wrow)[2], const uint16_t* const (&srow)[2], int tid,
+                                       int lane, uint32_t magic) {
+  constexpr int NBLK = K / 128;
+  constexpr int G = NBLK < 4 ? NBLK : 4;    // weight blocks per burst
+  constexpr int SX = NBLK < 2 ? NBLK : 2;   // operand blocks in flight
+  const int q = lane >> 4;
+  StageRegs sx[SX];
+#pragma unroll
+  for (int i = 0; i < SX; ++i) sx[i] = stage_load(i, op_row, tid);
+  WBlk w[2][G][2];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) w[0][i][m] = wload(wrow[m], srow[m], i, q);
+  stage_store(tiles[0], sx[0], tid);
+  sx[0] = stage_load(min(SX, NBLK - 1), op_row, tid);
+  __syncthreads();
+  for (int b0 = 0; b0 < NBLK; b0 += 2 * G) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g0 = b0 + h * G;  // first block of this group
+      if (NBLK > G) {
+        // the next group's burst (clamped past the end: repeats the last group)
+        const int n0 = min(g0 + G, NBLK - G);
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) w[h ^ 1][i][m] = wload(wrow[m], srow[m], n0 + i, q);
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const int b = g0 + i;
+        if (b < NBLK) {
+          block_mfma<NTT>(acc, tiles[b & 1], w[h][i], lane, magic);
+          // slot (b+1) % SX holds block b+1: into the other LDS buffer, then refill
+          stage_store(tiles[(b + 1) & 1], sx[(b + 1) % SX], tid);
+          sx[(b + 1) % SX] = stage_load(min(b + 1 + SX, NBLK - 1), op_row, tid);
+          __syncthreads();
+        }
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------------------- gate/up
 
-// One wave: gate and up rows 16*rt .. 16*rt+15 of expert e for up to 32
-// tokens (two token tiles), the whole of K = d streamed in 128-element
-// blocks with one block of loads in flight ahead of the MFMAs.  Epilogue in
-// registers: h = w_j * silu(g) * u, written as fp16 in operand order
-// (0,4,1,5,2,6,3,7 within each 8 rows) for the down step.
-struct GUStage {
-  uint4 g, u;
-  uint2 sg, su;
-  uint4 x[2][4];
-  float cx[2];
-};
-
-// Every load is unconditional (rows of absent tokens are clamped to a real
-// one and their output rows discarded), so the compiler's count of loads in
-// flight stays exact and a wait never drains the next block's loads.
+// Item: (chosen expert, 64 rows of f, up to 32 tokens).  Wave w takes gate
+// and up rows 16w .. 16w+15 of the group; K = d.  Epilogue in registers: h =
+// w_j * silu(g) * u, written as fp16 in operand order (0,4,1,5,2,6,3,7
+// within each 8 rows) for the down step.
 template <int D>
-__device__ __forceinline__ void gu_load(GUStage& st, int b, const uint8_t* gr, const uint8_t* ur,
-                                        const uint16_t* gsr, const uint16_t* usr, const uint16_t* xp,
-                                        const float* corr_x, const int (&trow)[2], int q) {
-  st.g = *reinterpret_cast<const uint4*>(gr + b * 64 + 16 * q);
-  st.u = *reinterpret_cast<const uint4*>(ur + b * 64 + 16 * q);
-  st.sg = *reinterpret_cast<const uint2*>(gsr + 4 * b);
-  st.su = *reinterpret_cast<const uint2*>(usr + 4 * b);
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const uint16_t* op = xp + (size_t)trow[tt] * D + b * 128 + 8 * q;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) st.x[tt][j] = *reinterpret_cast<const uint4*>(op + 32 * j);
-    st.cx[tt] = corr_x[(size_t)trow[tt] * (D / 32) + 4 * b + q];
-  }
-}
-
-__device__ __forceinline__ void gu_compute(const GUStage& st, f32x4_t (&acc)[2][2], int ntt, int q) {
-  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    if (tt >= ntt) break;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, st.x[tt][j]);
-      const f32x4_t cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, codes_bf16(dword_of(st.g, j)), z, 0, 0, 0);
-      const f32x4_t cu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, codes_bf16(dword_of(st.u, j)), z, 0, 0, 0);
-      fma4(acc[0][tt], scale_of(st.sg, j), cg);
-      fma4(acc[1][tt], scale_of(st.su, j), cu);
-    }
-    // sum over the block's 4 groups of corr(token, g) * scale(row, g)
-    acc[0][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.cx[tt], scale_of(st.sg, q), acc[0][tt], 0, 0, 0);
-    acc[1][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.cx[tt], scale_of(st.su, q), acc[1][tt], 0, 0, 0);
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void k_gateup(const LayerArgs a) {
-  constexpr int NBLK = D / 128;
+__global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
   constexpr int G = D / 32;
-  __shared__ int s_cp[1025];
-  const int nact = a.meta[0];
-  for (int i = threadIdx.x; i <= nact; i += 256) s_cp[i] = a.chunk_off[i];
-  __syncthreads();
-  const int f = a.f, k = a.k, rts = f / 16;
-  const int total = rts * s_cp[nact];
-  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+  __shared__ OpTile s_tile[2];
+  const int f = a.f, k = a.k, ngroups = f / 64;
+  const int total = ngroups * a.meta[1];
+  const uint32_t magic = magic_f16x2();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
   const size_t mq = (size_t)f * (D / 2), ms = (size_t)f * G;
-  for (int w = blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += gridDim.x * 4) {
-    const WaveItem it = wave_item(a, s_cp, nact, rts, w);
-    const int row = it.rt * 16 + r16;
-    const uint8_t* gr = a.gate_q + it.e * mq + (size_t)row * (D / 2);
-    const uint8_t* ur = a.up_q + it.e * mq + (size_t)row * (D / 2);
-    const uint16_t* gsr = a.gate_s + it.e * ms + (size_t)row * G;
-    const uint16_t* usr = a.up_s + it.e * ms + (size_t)row * G;
-    const int ntt = it.n - it.tc > 16 ? 2 : 1;
-    int trow[2];  // token of this lane's A-operand row (a real one for absent rows)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) trow[tt] = a.asg[it.p0 + min(it.tc + 16 * tt + r16, it.n - 1)] / k;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const Item it = item_of(a, ngroups, w);
+    const int ntt = it.n > 16 ? 2 : 1;
+    const int row = it.rg * 64 + wave * 16 + r16;
+    const uint8_t* wrow[2] = {a.gate_q + it.e * mq + (size_t)row * (D / 2), a.up_q + it.e * mq + (size_t)row * (D / 2)};
+    const uint16_t* srow[2] = {a.gate_s + it.e * ms + (size_t)row * G, a.up_s + it.e * ms + (size_t)row * G};
+    // the operand row this thread stages: token of chunk row tid/8
+    const int tok = a.asg[it.p0 + min(tid >> 3, it.n - 1)] / k;
     f32x4_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // Two stages; the loads past the last block repeat it (unconditional
-    // loads keep the compiler's wait counts exact, so a wait for one block
-    // never drains the next block's loads).
-    GUStage s0, s1;
-    gu_load<D>(s0, 0, gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
-    gu_load<D>(s1, 1, gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
-    for (int b = 0; b < NBLK; b += 2) {
-      gu_compute(s0, acc, ntt, q);
-      gu_load<D>(s0, min(b + 2, NBLK - 1), gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
-      gu_compute(s1, acc, ntt, q);
-      gu_load<D>(s1, min(b + 3, NBLK - 1), gr, ur, gsr, usr, a.xp, a.corr_x, trow, q);
-    }
+    acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // both token tiles always (for a chunk of up to 16 rows the second tile
+    // repeats a real row and its outputs are dropped): one code path
+    k_loop<D, 2>(acc, s_tile, a.xp + (size_t)tok * D, wrow, srow, tid, lane, magic);
     // lane: weight row r16, tokens 4q+v of each tile
     const int e8 = r16 & 7;
-    const int col = it.rt * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);
+    const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt >= ntt) break;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int pt = it.tc + 16 * tt + 4 * q + v;
+        const int pt = 16 * tt + 4 * q + v;
         if (pt < it.n) {
           const float wj = a.sel_w[a.asg[it.p0 + pt]];
           const float h = wj * silu(acc[0][tt][v]) * acc[1][tt][v];
@@ -490,83 +560,46 @@ __global__ __launch_bounds__(256) void k_gateup(const LayerArgs a) {
 
 // ----------------------------------------------------------------- down
 
-// One wave: rows 16*rt .. 16*rt+15 of W_d[e] for up to 32 tokens, K = f;
-// signed fp16 codes against the fp16 h operands.  o_{t,j} goes to
-// obuf[t*k + j][row].
-struct DStage {
-  uint4 w;
-  uint2 s;
-  uint4 h[2][4];
-};
-
+// Item: (chosen expert, 128 rows of d, up to 32 tokens).  Wave w takes rows
+// 32w .. 32w+31 of the group as two tiles; K = f, against the fp16 h
+// operands.  o_{t,j} goes to obuf[t*k + j][row].
 template <int F>
-__device__ __forceinline__ void dn_load(DStage& st, int b, const uint8_t* wr, const uint16_t* sr,
-                                        const uint16_t* h16, const int (&prow)[2], int q) {
-  st.w = *reinterpret_cast<const uint4*>(wr + b * 64 + 16 * q);
-  st.s = *reinterpret_cast<const uint2*>(sr + 4 * b);
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const uint16_t* op = h16 + (size_t)prow[tt] * F + b * 128 + 8 * q;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) st.h[tt][j] = *reinterpret_cast<const uint4*>(op + 32 * j);
-  }
-}
-
-__device__ __forceinline__ void dn_compute(const DStage& st, f32x4_t (&acc)[2], int ntt) {
-  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16x8_t wb = codes_f16_signed(dword_of(st.w, j));
-    const float s = scale_of(st.s, j);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt >= ntt) break;
-      const f32x4_t c =
-          __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, st.h[tt][j]), wb, z, 0, 0, 0);
-      fma4(acc[tt], s, c);
-    }
-  }
-}
-
-template <int F>
-__global__ __launch_bounds__(256) void k_down(const LayerArgs a) {
-  constexpr int NBLK = F / 128;
+__global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
   constexpr int G = F / 32;
-  __shared__ int s_cp[1025];
-  const int nact = a.meta[0];
-  for (int i = threadIdx.x; i <= nact; i += 256) s_cp[i] = a.chunk_off[i];
-  __syncthreads();
-  const int d = a.d, rts = d / 16;
-  const int total = rts * s_cp[nact];
-  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+  __shared__ OpTile s_tile[2];
+  const int d = a.d, ngroups = d / 128;
+  const int total = ngroups * a.meta[1];
+  const uint32_t magic = magic_f16x2();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
   const size_t mq = (size_t)d * (F / 2), ms = (size_t)d * G;
-  for (int w = blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += gridDim.x * 4) {
-    const WaveItem it = wave_item(a, s_cp, nact, rts, w);
-    const int row = it.rt * 16 + r16;
-    const uint8_t* wr = a.down_q + it.e * mq + (size_t)row * (F / 2);
-    const uint16_t* sr = a.down_s + it.e * ms + (size_t)row * G;
-    const int ntt = it.n - it.tc > 16 ? 2 : 1;
-    int prow[2];  // position of this lane's A-operand row (a real one for absent rows)
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const Item it = item_of(a, ngroups, w);
+    const int ntt = it.n > 16 ? 2 : 1;
+    const int row0 = it.rg * 128 + wave * 32 + r16;
+    const uint8_t* wrow[2] = {a.down_q + it.e * mq + (size_t)row0 * (F / 2),
+                              a.down_q + it.e * mq + (size_t)(row0 + 16) * (F / 2)};
+    const uint16_t* srow[2] = {a.down_s + it.e * ms + (size_t)row0 * G, a.down_s + it.e * ms + (size_t)(row0 + 16) * G};
+    const int pos = it.p0 + min(tid >> 3, it.n - 1);
+    // the assignments this lane's outputs go to, fetched while the K loop runs
+    int dst[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) prow[tt] = it.p0 + min(it.tc + 16 * tt + r16, it.n - 1);
-    f32x4_t acc[2];
-    acc[0] = acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    DStage s0, s1;
-    dn_load<F>(s0, 0, wr, sr, a.h16, prow, q);
-    dn_load<F>(s1, min(1, NBLK - 1), wr, sr, a.h16, prow, q);
-    for (int b = 0; b < NBLK; b += 2) {
-      dn_compute(s0, acc, ntt);
-      dn_load<F>(s0, min(b + 2, NBLK - 1), wr, sr, a.h16, prow, q);
-      if (b + 1 < NBLK) dn_compute(s1, acc, ntt);
-      dn_load<F>(s1, min(b + 3, NBLK - 1), wr, sr, a.h16, prow, q);
-    }
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[tt][v] = a.asg[it.p0 + min(16 * tt + 4 * q + v, it.n - 1)];
+    f32x4_t acc[2][2];
+    acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    k_loop<F, 2>(acc, s_tile, a.h16 + (size_t)pos * F, wrow, srow, tid, lane, magic);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt >= ntt) break;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int pt = it.tc + 16 * tt + 4 * q + v;
-        if (pt < it.n) a.obuf[(size_t)a.asg[it.p0 + pt] * d + row] = acc[tt][v];
+        const int pt = 16 * tt + 4 * q + v;
+        if (pt < it.n) {
+          float* o = a.obuf + (size_t)dst[tt][v] * d + row0;
+          o[0] = acc[0][tt][v];
+          o[16] = acc[1][tt][v];
+        }
       }
     }
   }
@@ -639,17 +672,18 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
   return hipGetLastError();
 }
 
-// Wave items: (active expert, 16-row tile, 32-token chunk); at most
-// min(E, T*k) active experts and T*k/32 extra chunks.
-static int grid_for(const LayerArgs& a, int T, int rows) {
+// Workgroup items: (chunk, row group); at most min(E, T*k) + T*k/32 chunks.
+static int max_chunks(const LayerArgs& a, int T) {
   const int Tk = T * a.k;
-  const int chunks = (a.E < Tk ? a.E : Tk) + Tk / 32;
-  const int wgs = (chunks * (rows / 16) + 3) / 4;
-  return wgs < kMaxGroupedGrid ? wgs : kMaxGroupedGrid;
+  return (a.E < Tk ? a.E : Tk) + Tk / 32;
+}
+static int grid_for(const LayerArgs& a, int T, int groups) {
+  const int items = max_chunks(a, T) * groups;
+  return items < kMaxGroupedGrid ? items : kMaxGroupedGrid;
 }
 
 hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
-  const dim3 g(grid_for(a, T, a.f)), b(256);
+  const dim3 g(grid_for(a, T, a.f / 64)), b(256);
   switch (a.d) {
     case 256: hipLaunchKernelGGL((k_gateup<256>), g, b, 0, s, a); break;
     case 512: hipLaunchKernelGGL((k_gateup<512>), g, b, 0, s, a); break;
@@ -663,7 +697,7 @@ hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
 }
 
 hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
-  const dim3 g(grid_for(a, T, a.d)), b(256);
+  const dim3 g(grid_for(a, T, a.d / 128)), b(256);
   switch (a.f) {
     case 128: hipLaunchKernelGGL((k_down<128>), g, b, 0, s, a); break;
     case 256: hipLaunchKernelGGL((k_down<256>), g, b, 0, s, a); break;

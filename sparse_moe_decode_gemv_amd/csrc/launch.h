@@ -26,12 +26,12 @@ struct LayerArgs {
   unsigned* tokens_done;  // [1] tokens whose top-k is done, zero between calls
   int32_t* sel_idx;       // [T][k] chosen experts of assignment t*k + j
   float* sel_w;           // [T][k] their weights
-  uint16_t* xp;           // [T][d] activations in MFMA operand order (bf16)
-  float* corr_x;          // [T][d/32] their per-group offset corrections
+  uint16_t* xp;           // [T][d] activations in MFMA operand order (fp16)
   int32_t* off;           // [E+1] first position of each expert in asg
   int32_t* act;           // [E] experts with assignments, ascending
   int32_t* chunk_off;     // [E+1] 32-token chunks of the active experts before each
-  int32_t* meta;          // [0]: number of such experts
+  int4* chunks;           // [min(E, T*k) + T*k/32] (expert, first position, count <= 32)
+  int32_t* meta;          // [0]: number of active experts, [1]: number of chunks
   int32_t* asg;           // [T*k] assignments grouped by expert
   uint16_t* h16;          // [T*k][f] w_j silu(g) u per position, fp16 operand order
   float* obuf;            // [T*k][d] o_{t,j} per assignment
