@@ -13,8 +13,10 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 struct Layout {
-  size_t counters, logits, sel_idx, sel_w, xp, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
-      hrec, epoch, total;
+  size_t logits, sel_idx, sel_w, xp, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
+      hrec, epoch, cleared;                      // [0, cleared) is zeroed at init
+  size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
+  size_t total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -36,12 +38,18 @@ moe_status check_desc(const moe_layer_desc* d) {
   return MOE_OK;
 }
 
+// The batched kernels read a tile-major copy of the expert matrices, made
+// at init; a layer gets one if it may run them: T > 1 allowed, or a shape
+// without the single-launch kernel (which reads the caller's matrices).
+bool needs_tiled_copy(const moe_layer_desc* d) {
+  return d->max_tokens > 1 || !moe::fused_layer_supported(d->d, d->f, d->n_experts, d->top_k, moe::kFusedGridCUs);
+}
+
 Layout layout_of(const moe_layer_desc* d) {
   Layout L;
   const size_t T = (size_t)d->max_tokens, E = (size_t)d->n_experts, k = (size_t)d->top_k;
   size_t o = 0;
   const size_t Tk = T * k, d_ = (size_t)d->d, f_ = (size_t)d->f;
-  L.counters = o, o += align256(((T + 3) / 4 + 1) * 128);  // one line per 4-token block, then tokens_done
   L.logits = o, o += align256(T * E * sizeof(float));
   L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
   L.sel_w = o, o += align256(Tk * sizeof(float));
@@ -57,6 +65,15 @@ Layout layout_of(const moe_layer_desc* d) {
   L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
   L.hrec = o, o += align256(k * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
+  L.cleared = o;
+  const bool copy = needs_tiled_copy(d);
+  const size_t cq = copy ? E * f_ * d_ / 2 : 0, cs = copy ? E * f_ * (d_ / 32) * 2 : 0;
+  L.gate_t = o, o += align256(cq);
+  L.gate_ts = o, o += align256(cs);
+  L.up_t = o, o += align256(cq);
+  L.up_ts = o, o += align256(cs);
+  L.down_t = o, o += align256(cq);  // E*d*f/2 bytes as well
+  L.down_ts = o, o += align256(cs);
   L.total = o;
   return L;
 }
@@ -134,8 +151,6 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.gate_q = w->gate_q, a.gate_s = w->gate_s, a.up_q = w->up_q, a.up_s = w->up_s;
   a.down_q = w->down_q, a.down_s = w->down_s;
   unsigned char* base = static_cast<unsigned char*>(workspace);
-  a.counters = reinterpret_cast<unsigned*>(base + L.counters);
-  a.tokens_done = a.counters + 32 * ((desc->max_tokens + 3) / 4);
   a.logits = reinterpret_cast<float*>(base + L.logits);
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
@@ -153,11 +168,23 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.hrec = reinterpret_cast<unsigned long long*>(base + L.hrec);
   a.epoch = reinterpret_cast<unsigned*>(base + L.epoch);
   a.error = a.epoch + moe::kMaxFusedGrid;
-  if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+  const bool copy = needs_tiled_copy(desc);
+  a.gate_t = copy ? base + L.gate_t : nullptr;
+  a.gate_ts = copy ? reinterpret_cast<uint16_t*>(base + L.gate_ts) : nullptr;
+  a.up_t = copy ? base + L.up_t : nullptr;
+  a.up_ts = copy ? reinterpret_cast<uint16_t*>(base + L.up_ts) : nullptr;
+  a.down_t = copy ? base + L.down_t : nullptr;
+  a.down_ts = copy ? reinterpret_cast<uint16_t*>(base + L.down_ts) : nullptr;
+  h->fused = moe::fused_layer_supported(desc->d, desc->f, desc->n_experts, desc->top_k, moe::fused_grid());
+  if (!h->fused && !copy) {  // a GPU with fewer CUs than the single-launch kernel assumes
+    delete h;
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (hipMemset(workspace, 0, L.cleared) != hipSuccess || (copy && moe::launch_tile_weights(a, nullptr) != hipSuccess) ||
+      hipDeviceSynchronize() != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
   }
-  h->fused = moe::fused_layer_supported(desc->d, desc->f, desc->n_experts, desc->top_k, moe::fused_grid());
   *out = h;
   return MOE_OK;
 }

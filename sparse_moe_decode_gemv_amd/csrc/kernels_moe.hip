@@ -1,14 +1,14 @@
 // kernels_moe.hip -- the decode step of a 4-bit MoE layer for T tokens on gfx950.
 //
-// Four kernels per call:
+// Five kernels per call:
 //   router  : logits = W_r x (+b), one router row per wave, held in
-//             registers across a block of 4 tokens.  The last workgroup to
-//             finish a token block does its 4 softmax + top-k selections,
-//             one wave each; the last token to finish sorts the T*k (token,
-//             slot) assignments by expert (a stable counting sort built from
-//             wave ballots).  Workgroup 0 also writes each token's
-//             activations in MFMA operand order (fp16).  In the stack the
-//             router applies the pre-norm (RMSNorm) to the residual.
+//             registers across a block of 4 tokens; workgroup 0 also writes
+//             each token's activations in MFMA operand order (fp16).  In the
+//             stack the router applies the pre-norm (RMSNorm) to the
+//             residual.
+//   select  : one workgroup: every token's softmax + top-k (16 waves in
+//             parallel), then the T*k (token, slot) assignments sorted by
+//             expert (a stable counting sort built from wave ballots).
 //   gate/up : one workgroup per (chunk of up to 32 tokens of one chosen
 //             expert, 64 rows of f): the chunk's activations staged in LDS,
 //             int4 weights dequantized into MFMA operands, so each chosen
@@ -52,35 +52,33 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------- top-k
 
-__device__ __forceinline__ void store_coherent_i32(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t load_coherent_i32(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // This wave's LDS operations have completed (and act as a compiler barrier).
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Softmax + top-k of one token's E logits in one wave (topk.h); lane r < k
-// writes choice r.  The chosen indices are read by another workgroup of the
-// same launch (the sort), so they are written coherently.
+// Softmax + top-k of one token's E logits (already loaded, v) in one wave
+// (topk.h); lane r < k writes choice r, also into the LDS list of chosen
+// experts that the sort reads.
 template <int EPL>
-__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int norm, int lane, int32_t* sel_idx,
-                                          float* sel_w, int32_t* idx_out, float* w_out) {
-  float v[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const float l = load_coherent(lg + min(lane + 64 * i, E - 1));
-    v[i] = lane + 64 * i < E && l == l ? l : -INFINITY;
-  }
+__device__ __forceinline__ void topk_wave(const float (&v)[EPL], int E, int k, int norm, int lane, int32_t* sel_idx,
+                                          float* sel_w, int* s_sel, int32_t* idx_out, float* w_out) {
   int se;
   float sw;
   topk_fast<EPL>(v, E, k, norm, lane, se, sw);
   if (lane < k) {
-    store_coherent_i32(sel_idx + lane, se);
+    sel_idx[lane] = se;
     sel_w[lane] = sw;
+    s_sel[lane] = se;
     if (idx_out) idx_out[lane] = se;
     if (w_out) w_out[lane] = sw;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_logits(float (&v)[EPL], const float* lg, int E, int lane) {
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const float l = lg[min(lane + 64 * i, E - 1)];
+    v[i] = lane + 64 * i < E && l == l ? l : -INFINITY;
   }
 }
 
@@ -106,25 +104,15 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 //   chunk_off[i]          32-token chunks of the active experts before act[i]
 //                         (chunk_off[meta[0]] = all chunks = meta[1])
 //   chunks[c]             chunk c: (expert, first position, positions <= 32)
-// cnt: LDS [E]; ssel: LDS [Tk].
-__device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int* ssel, int32_t* off,
-                               int32_t* act, int32_t* chunk_off, int4* chunks, int32_t* meta, int32_t* asg,
-                               int lane) {
-  // the chosen experts into LDS, 8 loads in flight per lane
-  for (int c0 = 0; c0 < Tk; c0 += 512) {
-    int v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = load_coherent_i32(sel + min(c0 + 64 * i + lane, Tk - 1));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (c0 + 64 * i + lane < Tk) ssel[c0 + 64 * i + lane] = min(max(v[i], 0), E - 1);
-  }
+// ssel: LDS [Tk], the chosen experts; cnt: LDS [E].
+__device__ void sort_by_expert(const int* ssel, int Tk, int E, int* cnt, int32_t* off, int32_t* act,
+                               int32_t* chunk_off, int4* chunks, int32_t* meta, int32_t* asg, int lane) {
   for (int i = lane; i < E; i += 64) cnt[i] = 0;
   lds_wait();
   for (int c = 0; c < Tk; c += 64) {  // counts
     const int a = c + lane;
     const bool v = a < Tk;
-    const int e = v ? ssel[a] : 0;
+    const int e = v ? min(max(ssel[a], 0), E - 1) : 0;
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     if (v && lane == __builtin_ctzll(same)) cnt[e] += __builtin_popcountll(same);
     lds_wait();
@@ -175,7 +163,7 @@ __device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int*
   for (int c = 0; c < Tk; c += 64) {  // placement, stable in a
     const int a = c + lane;
     const bool v = a < Tk;
-    const int e = v ? ssel[a] : 0;
+    const int e = v ? min(max(ssel[a], 0), E - 1) : 0;
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
     const int pos = v ? cnt[e] : 0;
@@ -189,22 +177,15 @@ __device__ void sort_by_expert(const int32_t* sel, int Tk, int E, int* cnt, int*
 // ----------------------------------------------------------------- router
 
 constexpr int kRouterTokens = 4;  // tokens per router workgroup
-constexpr int kCounterStride = 32;  // one arrival counter per 128-byte line
 
 // grid (ceil(E/4), ceil(T/4)), block 256: wave w of workgroup (b, c) holds
 // router row 4b + w in registers and computes its logit for tokens 4c ..
-// 4c+3.  One arrival per workgroup on the token block's counter (own cache
-// line); the last workgroup of a block does the top-k of its 4 tokens, one
-// per wave; the last token overall runs the sort.  EPL = ceil(E/64).
-template <int D, int EPL>
+// 4c+3.
+template <int D>
 __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_t* __restrict__ x,
                                                 const float* __restrict__ resid, float eps, int T,
-                                                int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                 uint16_t* __restrict__ x_trace) {
   constexpr int NI = D / 256;  // float4 columns per lane: 4*lane + 256*i
-  __shared__ int s_cnt[1024];
-  __shared__ int s_sel[kMaxAssignments];
-  __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
   const bool row_ok = e < a.E;
@@ -305,35 +286,33 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
         acc = fmaf(w[i].w, xv[i][3], acc);
       }
       acc = wave_sum(acc) + bias;
-      if (lane == 0) store_coherent(a.logits + (size_t)t * a.E + e, acc);
+      if (lane == 0) a.logits[(size_t)t * a.E + e] = acc;
     }
   }
 
-  // Arrival: the last workgroup of this token block selects its experts.
-  unsigned* counter = a.counters + blockIdx.y * kCounterStride;
-  wait_vm();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive(counter) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  const int t = blockIdx.y * kRouterTokens + wave;
-  if (t >= T) return;
-  int32_t* io = idx_out ? idx_out + (size_t)t * a.k : nullptr;
-  float* wo = w_out ? w_out + (size_t)t * a.k : nullptr;
-  topk_wave<EPL>(a.logits + (size_t)t * a.E, a.E, a.k, a.norm_topk, lane, a.sel_idx + t * a.k,
-                 a.sel_w + t * a.k, io, wo);
-  wait_vm();
-  unsigned prev = 0;
-  if (lane == 0) {
-    if (wave == 0) *counter = 0u;  // every workgroup of the block has arrived
-    prev = arrive(a.tokens_done);
+}
+
+// One workgroup of 16 waves: the softmax + top-k of every token (wave w
+// takes tokens w, w+16, ...; the next token's logits are loaded before the
+// current one is selected), then wave 0 groups the assignments by expert.
+template <int EPL>
+__global__ __launch_bounds__(1024) void k_select(const LayerArgs a, int T, int32_t* __restrict__ idx_out,
+                                                 float* __restrict__ w_out) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_sel[kMaxAssignments];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  float v[EPL], vn[EPL];
+  if (wave < T) load_logits<EPL>(v, a.logits + (size_t)wave * E, E, lane);
+  for (int t = wave; t < T; t += 16) {
+    if (t + 16 < T) load_logits<EPL>(vn, a.logits + (size_t)(t + 16) * E, E, lane);
+    topk_wave<EPL>(v, E, k, a.norm_topk, lane, a.sel_idx + t * k, a.sel_w + t * k, s_sel + t * k,
+                   idx_out ? idx_out + (size_t)t * k : nullptr, w_out ? w_out + (size_t)t * k : nullptr);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = vn[i];
   }
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev != (unsigned)(T - 1)) return;
-  // the last token: group the assignments by expert
-  sort_by_expert(a.sel_idx, T * a.k, a.E, s_cnt, s_sel, a.off, a.act, a.chunk_off, a.chunks, a.meta, a.asg,
-                 lane);
-  if (lane == 0) *a.tokens_done = 0u;
+  __syncthreads();
+  if (wave == 0) sort_by_expert(s_sel, T * k, E, s_cnt, a.off, a.act, a.chunk_off, a.chunks, a.meta, a.asg, lane);
 }
 
 // ----------------------------------------------------------------- MFMA tiles
@@ -423,16 +402,42 @@ __device__ __forceinline__ void stage_store(OpTile& t, const StageRegs& r, int t
   t.v[c >> 4][j][q0 + 1][r16 ^ swz(j, q0 + 1)] = r.b;
 }
 
+// Tile-major copy of an expert matrix [R rows][K] (made once at init for
+// the batched step): unit (tile of 16 rows, block of 128 k) holds, at
+// 16-byte word 16*q + r, piece q of that block of row 16*tile + r -- the
+// lane order of an MFMA operand -- so one wave load reads 1 KB contiguous
+// and a tile streams sequentially; its scales sit at 8-byte word r of a
+// 128-byte unit (the block's 4 group scales of row r).
+__global__ __launch_bounds__(256) void k_tile_codes(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                    long long rows, int K) {
+  const int ppr = K / 32;  // pieces per row
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * ppr) return;
+  const long long row = i / ppr;
+  const int c = (int)(i - row * ppr), kb = c >> 2, q = c & 3;
+  const long long tile = row >> 4;
+  dst[(tile * (K / 128) + kb) * 64 + q * 16 + (row & 15)] = src[i];
+}
+__global__ __launch_bounds__(256) void k_tile_scales(const uint2* __restrict__ src, uint2* __restrict__ dst,
+                                                     long long rows, int K) {
+  const int upr = K / 128;  // 4-scale units per row
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * upr) return;
+  const long long row = i / upr;
+  const int kb = (int)(i - row * upr);
+  dst[((row >> 4) * upr + kb) * 16 + (row & 15)] = src[i];
+}
+
 // Weights of one block for one 16-row tile: this lane's row, chunk q of the
-// block's 4 groups, and the 4 group scales.
+// block's 4 groups, and the 4 group scales, from the tile-major copy.
 struct WBlk {
   uint4 q;
   uint2 s;
 };
-__device__ __forceinline__ WBlk wload(const uint8_t* row, const uint16_t* srow, int blk, int q) {
+__device__ __forceinline__ WBlk wload(const uint4* tq, const uint2* ts, int blk, int lane) {
   WBlk w;
-  w.q = *reinterpret_cast<const uint4*>(row + blk * 64 + 16 * q);
-  w.s = *reinterpret_cast<const uint2*>(srow + 4 * blk);
+  w.q = tq[blk * 64 + lane];
+  w.s = ts[blk * 16 + (lane & 15)];
   return w;
 }
 
@@ -458,17 +463,15 @@ __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][2], const OpTile& t
 // The K loop shared by both kernels: NBLK blocks; the operand tile is
 // double-buffered in LDS (one barrier per block) and fed from a ring of up
 // to 2 blocks of staging loads in registers.  Each wave's two weight tiles
-// come in groups of G = 4 consecutive blocks, double-buffered: the loads of
-// group g+1 are issued together when group g starts, so that every row is
-// requested as 256 contiguous bytes in one burst (a row's 64-byte pieces
-// fetched one block at a time, far apart in time, leave most of each DRAM
-// page unused).  Every global load is unconditional (rows past the chunk
+// come in groups of G = 4 consecutive blocks (4 KB of the tile-major copy
+// each), double-buffered: the loads of group g+1 are issued when group g
+// starts.  Every global load is unconditional (rows past the chunk
 // are clamped to a real one and their outputs dropped), so the compiler's
 // wait counts stay exact.
 template <int K, int NTT>
 __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, const uint16_t* op_row,
-                                       const uint8_t* const (&wrow)[2], const uint16_t* const (&srow)[2], int tid,
-                                       int lane, uint32_t magic) {
+                                       const uint4* const (&wtq)[2], const uint2* const (&wts)[2], int tid, int lane,
+                                       uint32_t magic) {
   constexpr int NBLK = K / 128;
   constexpr int G = NBLK < 4 ? NBLK : 4;    // weight blocks per burst
   constexpr int SX = NBLK < 2 ? NBLK : 2;   // operand blocks in flight
@@ -480,7 +483,7 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, cons
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) w[0][i][m] = wload(wrow[m], srow[m], i, q);
+    for (int m = 0; m < 2; ++m) w[0][i][m] = wload(wtq[m], wts[m], i, lane);
   stage_store(tiles[0], sx[0], tid);
   sx[0] = stage_load(min(SX, NBLK - 1), op_row, tid);
   __syncthreads();
@@ -494,7 +497,7 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, cons
 #pragma unroll
         for (int i = 0; i < G; ++i)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) w[h ^ 1][i][m] = wload(wrow[m], srow[m], n0 + i, q);
+          for (int m = 0; m < 2; ++m) w[h ^ 1][i][m] = wload(wtq[m], wts[m], n0 + i, lane);
       }
 #pragma unroll
       for (int i = 0; i < G; ++i) {
@@ -525,23 +528,24 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
   const int total = ngroups * a.meta[1];
   const uint32_t magic = magic_f16x2();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
-  const size_t mq = (size_t)f * (D / 2), ms = (size_t)f * G;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const Item it = item_of(a, ngroups, w);
     const int ntt = it.n > 16 ? 2 : 1;
-    const int row = it.rg * 64 + wave * 16 + r16;
-    const uint8_t* wrow[2] = {a.gate_q + it.e * mq + (size_t)row * (D / 2), a.up_q + it.e * mq + (size_t)row * (D / 2)};
-    const uint16_t* srow[2] = {a.gate_s + it.e * ms + (size_t)row * G, a.up_s + it.e * ms + (size_t)row * G};
+    const size_t tile = (size_t)it.e * (f / 16) + it.rg * 4 + wave;  // 16-row tile of gate and of up
+    const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.gate_t) + tile * (D / 128) * 64,
+                           reinterpret_cast<const uint4*>(a.up_t) + tile * (D / 128) * 64};
+    const uint2* wts[2] = {reinterpret_cast<const uint2*>(a.gate_ts) + tile * (D / 128) * 16,
+                           reinterpret_cast<const uint2*>(a.up_ts) + tile * (D / 128) * 16};
     // the operand row this thread stages: token of chunk row tid/8
     const int tok = a.asg[it.p0 + min(tid >> 3, it.n - 1)] / k;
     f32x4_t acc[2][2];
     acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // both token tiles always (for a chunk of up to 16 rows the second tile
     // repeats a real row and its outputs are dropped): one code path
-    k_loop<D, 2>(acc, s_tile, a.xp + (size_t)tok * D, wrow, srow, tid, lane, magic);
+    k_loop<D, 2>(acc, s_tile, a.xp + (size_t)tok * D, wtq, wts, tid, lane, magic);
     // lane: weight row r16, tokens 4q+v of each tile
     const int e8 = r16 & 7;
-    const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);
+    const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);  // h in operand order
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt >= ntt) break;
@@ -571,14 +575,15 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
   const int total = ngroups * a.meta[1];
   const uint32_t magic = magic_f16x2();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
-  const size_t mq = (size_t)d * (F / 2), ms = (size_t)d * G;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const Item it = item_of(a, ngroups, w);
     const int ntt = it.n > 16 ? 2 : 1;
     const int row0 = it.rg * 128 + wave * 32 + r16;
-    const uint8_t* wrow[2] = {a.down_q + it.e * mq + (size_t)row0 * (F / 2),
-                              a.down_q + it.e * mq + (size_t)(row0 + 16) * (F / 2)};
-    const uint16_t* srow[2] = {a.down_s + it.e * ms + (size_t)row0 * G, a.down_s + it.e * ms + (size_t)(row0 + 16) * G};
+    const size_t tile = (size_t)it.e * (d / 16) + it.rg * 8 + wave * 2;  // two 16-row tiles of W_d
+    const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.down_t) + tile * (F / 128) * 64,
+                           reinterpret_cast<const uint4*>(a.down_t) + (tile + 1) * (F / 128) * 64};
+    const uint2* wts[2] = {reinterpret_cast<const uint2*>(a.down_ts) + tile * (F / 128) * 16,
+                           reinterpret_cast<const uint2*>(a.down_ts) + (tile + 1) * (F / 128) * 16};
     const int pos = it.p0 + min(tid >> 3, it.n - 1);
     // the assignments this lane's outputs go to, fetched while the K loop runs
     int dst[2][4];
@@ -588,7 +593,7 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
       for (int v = 0; v < 4; ++v) dst[tt][v] = a.asg[it.p0 + min(16 * tt + 4 * q + v, it.n - 1)];
     f32x4_t acc[2][2];
     acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    k_loop<F, 2>(acc, s_tile, a.h16 + (size_t)pos * F, wrow, srow, tid, lane, magic);
+    k_loop<F, 2>(acc, s_tile, a.h16 + (size_t)pos * F, wtq, wts, tid, lane, magic);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt >= ntt) break;
@@ -635,40 +640,36 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf,
 
 // ----------------------------------------------------------------- launchers
 
-template <int D, int EPL>
-static void router_launch(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, int32_t* io,
-                          float* wo, uint16_t* xt, hipStream_t s) {
-  hipLaunchKernelGGL((k_router<D, EPL>), dim3((a.E + 3) / 4, (T + kRouterTokens - 1) / kRouterTokens), dim3(256), 0,
-                     s, a, x, r, eps, T, io, wo, xt);
-}
-
 template <int D>
-static void router_inst(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, int32_t* io,
-                        float* wo, uint16_t* xt, hipStream_t s) {
-  const int epl = (a.E + 63) / 64;
-  if (epl <= 1)
-    router_launch<D, 1>(a, x, r, eps, T, io, wo, xt, s);
-  else if (epl <= 2)
-    router_launch<D, 2>(a, x, r, eps, T, io, wo, xt, s);
-  else if (epl <= 4)
-    router_launch<D, 4>(a, x, r, eps, T, io, wo, xt, s);
-  else if (epl <= 8)
-    router_launch<D, 8>(a, x, r, eps, T, io, wo, xt, s);
-  else
-    router_launch<D, 16>(a, x, r, eps, T, io, wo, xt, s);
+static void router_inst(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, uint16_t* xt,
+                        hipStream_t s) {
+  hipLaunchKernelGGL((k_router<D>), dim3((a.E + 3) / 4, (T + kRouterTokens - 1) / kRouterTokens), dim3(256), 0, s,
+                     a, x, r, eps, T, xt);
 }
 
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
                          int32_t* idx_out, float* w_out, uint16_t* x_trace, hipStream_t s) {
   switch (a.d) {
-    case 256: router_inst<256>(a, x, r, eps, T, idx_out, w_out, x_trace, s); break;
-    case 512: router_inst<512>(a, x, r, eps, T, idx_out, w_out, x_trace, s); break;
-    case 1024: router_inst<1024>(a, x, r, eps, T, idx_out, w_out, x_trace, s); break;
-    case 2048: router_inst<2048>(a, x, r, eps, T, idx_out, w_out, x_trace, s); break;
-    case 4096: router_inst<4096>(a, x, r, eps, T, idx_out, w_out, x_trace, s); break;
-    case 8192: router_inst<8192>(a, x, r, eps, T, idx_out, w_out, x_trace, s); break;
+    case 256: router_inst<256>(a, x, r, eps, T, x_trace, s); break;
+    case 512: router_inst<512>(a, x, r, eps, T, x_trace, s); break;
+    case 1024: router_inst<1024>(a, x, r, eps, T, x_trace, s); break;
+    case 2048: router_inst<2048>(a, x, r, eps, T, x_trace, s); break;
+    case 4096: router_inst<4096>(a, x, r, eps, T, x_trace, s); break;
+    case 8192: router_inst<8192>(a, x, r, eps, T, x_trace, s); break;
     default: return hipErrorInvalidValue;
   }
+  const int epl = (a.E + 63) / 64;
+  const dim3 g(1), b(1024);
+  if (epl <= 1)
+    hipLaunchKernelGGL((k_select<1>), g, b, 0, s, a, T, idx_out, w_out);
+  else if (epl <= 2)
+    hipLaunchKernelGGL((k_select<2>), g, b, 0, s, a, T, idx_out, w_out);
+  else if (epl <= 4)
+    hipLaunchKernelGGL((k_select<4>), g, b, 0, s, a, T, idx_out, w_out);
+  else if (epl <= 8)
+    hipLaunchKernelGGL((k_select<8>), g, b, 0, s, a, T, idx_out, w_out);
+  else
+    hipLaunchKernelGGL((k_select<16>), g, b, 0, s, a, T, idx_out, w_out);
   return hipGetLastError();
 }
 
@@ -708,6 +709,29 @@ hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq, uint16_t* ts, long long rows, int K,
+                              hipStream_t s) {
+  const long long np = rows * (K / 32), ns = rows * (K / 128);
+  hipLaunchKernelGGL(k_tile_codes, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(q), reinterpret_cast<uint4*>(tq), rows, K);
+  hipLaunchKernelGGL(k_tile_scales, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint2*>(sc), reinterpret_cast<uint2*>(ts), rows, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
+  const long long E = a.E;
+  hipError_t e;
+  if ((e = tile_matrix(a.gate_q, a.gate_s, const_cast<uint8_t*>(a.gate_t), const_cast<uint16_t*>(a.gate_ts),
+                       E * a.f, a.d, s)) != hipSuccess)
+    return e;
+  if ((e = tile_matrix(a.up_q, a.up_s, const_cast<uint8_t*>(a.up_t), const_cast<uint16_t*>(a.up_ts), E * a.f,
+                       a.d, s)) != hipSuccess)
+    return e;
+  return tile_matrix(a.down_q, a.down_s, const_cast<uint8_t*>(a.down_t), const_cast<uint16_t*>(a.down_ts),
+                     E * a.d, a.f, s);
 }
 
 hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s) {

@@ -20,10 +20,15 @@ struct LayerArgs {
   const uint16_t* up_s;
   const uint8_t* down_q;
   const uint16_t* down_s;
+  // tile-major copies of the expert matrices (batched path; max_tokens > 1)
+  const uint8_t* gate_t;
+  const uint16_t* gate_ts;
+  const uint8_t* up_t;
+  const uint16_t* up_ts;
+  const uint8_t* down_t;
+  const uint16_t* down_ts;
   // workspace of the batched path
   float* logits;          // [T][E]
-  unsigned* counters;     // arrival counter per block of 4 tokens, one per 128 B line; zero between calls
-  unsigned* tokens_done;  // [1] tokens whose top-k is done, zero between calls
   int32_t* sel_idx;       // [T][k] chosen experts of assignment t*k + j
   float* sel_w;           // [T][k] their weights
   uint16_t* xp;           // [T][d] activations in MFMA operand order (fp16)
@@ -43,6 +48,7 @@ struct LayerArgs {
 };
 
 constexpr int kMaxFusedGrid = 1024;
+constexpr int kFusedGridCUs = 256;  // compute units the single-launch kernel is sized for (MI355X)
 constexpr int kMaxGroupedGrid = 1024;
 constexpr int kMaxAssignments = MOE_MAX_TOKENS * MOE_MAX_TOPK;  // largest T*k  // persistent grid of the expert-grouped kernels
 
@@ -77,8 +83,8 @@ bool fused_layer_supported(int d, int f, int E, int k, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
 
-// Router GEMV + softmax + top-k for T tokens, then the assignments grouped
-// by expert.  Activations come either from x (bf16 [T][d]) or, when x is
+// Router GEMV for T tokens, then (a second kernel) softmax + top-k of
+// every token and the assignments grouped by expert.  Activations come either from x (bf16 [T][d]) or, when x is
 // NULL, from the fp32 residual r [T][d] normalized by RMSNorm (eps), in
 // which case x_l is also written to x_trace when it is non-NULL.
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
@@ -89,6 +95,9 @@ hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s);
 
 // Per chosen expert, over all its tokens: o_{t,j} = W_d h.
 hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s);
+
+// The tile-major copies of gate, up and down (from the canonical matrices).
+hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s);
 
 // y_t = sum_j o_{t,j} into y_out (if non-NULL); residual_t += y_t (if non-NULL).
 hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
