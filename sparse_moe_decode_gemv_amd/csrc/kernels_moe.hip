@@ -1,14 +1,15 @@
 // kernels_moe.hip -- the decode step of a 4-bit MoE layer for T tokens on gfx950.
 //
-// Five kernels per call:
+// Six kernels per call:
 //   router  : logits = W_r x (+b), one router row per wave, held in
 //             registers across a block of 4 tokens; workgroup 0 also writes
 //             each token's activations in MFMA operand order (fp16).  In the
 //             stack the router applies the pre-norm (RMSNorm) to the
 //             residual.
-//   select  : one workgroup: every token's softmax + top-k (16 waves in
-//             parallel), then the T*k (token, slot) assignments sorted by
-//             expert (a stable counting sort built from wave ballots).
+//   top-k   : one wave per token: softmax + top-k.
+//   sort    : one workgroup of 16 waves: the T*k (token, slot) assignments
+//             grouped by expert (a stable counting sort built from wave
+//             ballots).
 //   gate/up : one workgroup per (chunk of up to 32 tokens of one chosen
 //             expert, 64 rows of f): the chunk's activations staged in LDS,
 //             int4 weights dequantized into MFMA operands, so each chosen
@@ -55,30 +56,27 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // This wave's LDS operations have completed (and act as a compiler barrier).
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Softmax + top-k of one token's E logits (already loaded, v) in one wave
-// (topk.h); lane r < k writes choice r, also into the LDS list of chosen
-// experts that the sort reads.
+// Softmax + top-k of one token's E logits in one wave (topk.h): grid T,
+// block 64, one token per workgroup (one wave per SIMD of its own: a wave64
+// VALU instruction takes 4 cycles, so waves sharing a SIMD would serialize).
 template <int EPL>
-__device__ __forceinline__ void topk_wave(const float (&v)[EPL], int E, int k, int norm, int lane, int32_t* sel_idx,
-                                          float* sel_w, int* s_sel, int32_t* idx_out, float* w_out) {
-  int se;
-  float sw;
-  topk_fast<EPL>(v, E, k, norm, lane, se, sw);
-  if (lane < k) {
-    sel_idx[lane] = se;
-    sel_w[lane] = sw;
-    s_sel[lane] = se;
-    if (idx_out) idx_out[lane] = se;
-    if (w_out) w_out[lane] = sw;
-  }
-}
-
-template <int EPL>
-__device__ __forceinline__ void load_logits(float (&v)[EPL], const float* lg, int E, int lane) {
+__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int32_t* __restrict__ idx_out,
+                                             float* __restrict__ w_out) {
+  const int t = blockIdx.x, lane = threadIdx.x, E = a.E, k = a.k;
+  float v[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const float l = lg[min(lane + 64 * i, E - 1)];
+    const float l = a.logits[(size_t)t * E + min(lane + 64 * i, E - 1)];
     v[i] = lane + 64 * i < E && l == l ? l : -INFINITY;
+  }
+  int se;
+  float sw;
+  topk_fast<EPL>(v, E, k, a.norm_topk, lane, se, sw);
+  if (lane < k) {
+    a.sel_idx[t * k + lane] = se;
+    a.sel_w[t * k + lane] = sw;
+    if (idx_out) idx_out[(size_t)t * k + lane] = se;
+    if (w_out) w_out[(size_t)t * k + lane] = sw;
   }
 }
 
@@ -96,91 +94,118 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
   return m;
 }
 
-// One wave: the Tk = T*k assignments a = t*k + j (chosen expert sel[a])
-// grouped by expert, ascending a within an expert:
+// One workgroup of 16 waves: the Tk = T*k assignments a = t*k + j (chosen
+// expert sel[a]) grouped by expert, ascending a within an expert:
 //   off[e] .. off[e+1]-1  positions of expert e in asg (off[E] = Tk)
 //   asg[p]                the assignment at position p
 //   act[i], i < meta[0]   the experts with at least one assignment, ascending
 //   chunk_off[i]          32-token chunks of the active experts before act[i]
 //                         (chunk_off[meta[0]] = all chunks = meta[1])
 //   chunks[c]             chunk c: (expert, first position, positions <= 32)
-// ssel: LDS [Tk], the chosen experts; cnt: LDS [E].
-__device__ void sort_by_expert(const int* ssel, int Tk, int E, int* cnt, int32_t* off, int32_t* act,
-                               int32_t* chunk_off, int4* chunks, int32_t* meta, int32_t* asg, int lane) {
-  for (int i = lane; i < E; i += 64) cnt[i] = 0;
-  lds_wait();
-  for (int c = 0; c < Tk; c += 64) {  // counts
-    const int a = c + lane;
-    const bool v = a < Tk;
-    const int e = v ? min(max(ssel[a], 0), E - 1) : 0;
+// Wave w owns the w-th sixteenth of the assignments: it counts them per
+// expert (lanes with equal experts found by wave ballots), a prefix over
+// waves gives each (wave, expert) its base, and each wave places its own
+// assignments in order: stable, deterministic, no atomics.
+// LDS (dynamic): sel [Tk], cnt [16][E], tot [E].
+__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
+  extern __shared__ int sm[];
+  const int E = a.E, Tk = T * a.k;
+  int* ssel = sm;
+  int* cnt = sm + ((Tk + 3) & ~3);
+  int* tot = cnt + 16 * E;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < Tk; i += 1024) ssel[i] = min(max(a.sel_idx[i], 0), E - 1);
+  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int per = (Tk + 15) / 16, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
+  int* cw = cnt + wave * E;
+  for (int c = a0; c < a1; c += 64) {  // this wave's counts
+    const int i = c + lane;
+    const bool v = i < a1;
+    const int e = v ? ssel[i] : 0;
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
-    if (v && lane == __builtin_ctzll(same)) cnt[e] += __builtin_popcountll(same);
+    if (v && lane == __builtin_ctzll(same)) cw[e] += __builtin_popcountll(same);
     lds_wait();
   }
-  // exclusive scans over experts: counts, active flags, chunks
-  const int per = (E + 63) / 64;
-  const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
-  int s = 0, na = 0, nc = 0;
-  for (int e = e0; e < e1; ++e) {
-    const int n = cnt[e];
-    s += n;
-    na += n > 0;
-    nc += (n + 31) >> 5;
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {  // base of each wave within expert e, and e's total
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int n = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += n;
+    }
+    tot[e] = run;
   }
-  // exclusive prefix sums over lanes, log steps
-  int base = s, abase = na, cbase = nc;
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scans over experts: counts, active flags, chunks
+    const int pe = (E + 63) / 64;
+    const int e0 = min(lane * pe, E), e1 = min(e0 + pe, E);
+    int s = 0, na = 0, nc = 0;
+    for (int e = e0; e < e1; ++e) {
+      const int n = tot[e];
+      s += n;
+      na += n > 0;
+      nc += (n + 31) >> 5;
+    }
+    int base = s, abase = na, cbase = nc;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int b1 = __shfl_up(base, o, 64), b2 = __shfl_up(abase, o, 64), b3 = __shfl_up(cbase, o, 64);
-    if (lane >= o) {
-      base += b1;
-      abase += b2;
-      cbase += b3;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int b1 = __shfl_up(base, o, 64), b2 = __shfl_up(abase, o, 64), b3 = __shfl_up(cbase, o, 64);
+      if (lane >= o) {
+        base += b1;
+        abase += b2;
+        cbase += b3;
+      }
+    }
+    base -= s;
+    abase -= na;
+    cbase -= nc;
+    for (int e = e0; e < e1; ++e) {
+      const int n = tot[e];
+      a.off[e] = base;
+      if (n > 0) {
+        a.act[abase] = e;
+        a.chunk_off[abase] = cbase;
+        ++abase;
+        for (int tc = 0; tc < n; tc += 32) a.chunks[cbase++] = make_int4(e, base + tc, min(32, n - tc), 0);
+      }
+      tot[e] = base;  // from here on: the first position of expert e
+      base += n;
+    }
+    if (lane == 63) {
+      a.off[E] = base;
+      a.chunk_off[abase] = cbase;
+      a.meta[0] = abase;
+      a.meta[1] = cbase;
     }
   }
-  base -= s;
-  abase -= na;
-  cbase -= nc;
-  for (int e = e0; e < e1; ++e) {
-    const int n = cnt[e];
-    off[e] = base;
-    if (n > 0) {
-      act[abase] = e;
-      chunk_off[abase] = cbase;
-      ++abase;
-      for (int tc = 0; tc < n; tc += 32) chunks[cbase++] = make_int4(e, base + tc, min(32, n - tc), 0);
-    }
-    cnt[e] = base;  // from here on: the next free position of expert e
-    base += n;
-  }
-  if (lane == 63) {
-    off[E] = base;
-    chunk_off[abase] = cbase;
-    meta[0] = abase;
-    meta[1] = cbase;
-  }
-  lds_wait();
-  for (int c = 0; c < Tk; c += 64) {  // placement, stable in a
-    const int a = c + lane;
-    const bool v = a < Tk;
-    const int e = v ? min(max(ssel[a], 0), E - 1) : 0;
+  __syncthreads();
+  for (int c = a0; c < a1; c += 64) {  // placement, stable in a
+    const int i = c + lane;
+    const bool v = i < a1;
+    const int e = v ? ssel[i] : 0;
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
-    const int pos = v ? cnt[e] : 0;
+    const int pos = v ? tot[e] + cw[e] : 0;
     lds_wait();
-    if (v) asg[pos + rank] = a;
-    if (v && lane == __builtin_ctzll(same)) cnt[e] = pos + __builtin_popcountll(same);
+    if (v) a.asg[pos + rank] = i;
+    if (v && lane == __builtin_ctzll(same)) cw[e] += __builtin_popcountll(same);
     lds_wait();
   }
 }
 
+size_t sort_lds_bytes(int E, int Tk) { return (size_t)(((Tk + 3) & ~3) + 17 * E) * sizeof(int); }
+
 // ----------------------------------------------------------------- router
 
-constexpr int kRouterTokens = 4;  // tokens per router workgroup
+constexpr int kRouterTokens = 4;  // tokens per router workgroup (16 measured slower)
+constexpr int kRouterSub = 4;     // tokens per activation prefetch group
 
 // grid (ceil(E/4), ceil(T/4)), block 256: wave w of workgroup (b, c) holds
 // router row 4b + w in registers and computes its logit for tokens 4c ..
-// 4c+3.
+// 4c+3, all 4 tokens' activations loaded before any is used.
 template <int D>
 __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_t* __restrict__ x,
                                                 const float* __restrict__ resid, float eps, int T,
@@ -195,24 +220,31 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
   for (int i = 0; i < NI; ++i) w[i] = wrow[64 * i + lane];
   const float bias = row_ok && a.router_b ? a.router_b[e] : 0.f;
 
-  // the block's bf16 activations, all loads issued before any is used
-  constexpr bool XPRE = NI * kRouterTokens <= 32;
-  uint2 xq[XPRE ? kRouterTokens : 1][XPRE ? NI : 1];
-  if constexpr (XPRE) {
-    if (x) {
+  // bf16 activations in groups of 4 tokens, one group ahead (clamped to
+  // real tokens, so the loads are unconditional)
+  constexpr bool XPRE = NI <= 8;
+  uint2 xq[2][XPRE ? kRouterSub : 1][XPRE ? NI : 1];
+  const int t0 = blockIdx.y * kRouterTokens;
+  auto load_group = [&](uint2 (&dst)[XPRE ? kRouterSub : 1][XPRE ? NI : 1], int g) {
+    if constexpr (XPRE) {
 #pragma unroll
-      for (int tb = 0; tb < kRouterTokens; ++tb) {
-        const uint2* xr =
-            reinterpret_cast<const uint2*>(x + (size_t)min(blockIdx.y * kRouterTokens + tb, T - 1) * D);
+      for (int tb = 0; tb < kRouterSub; ++tb) {
+        const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)min(t0 + g * kRouterSub + tb, T - 1) * D);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) xq[tb][i] = xr[64 * i + lane];
+        for (int i = 0; i < NI; ++i) dst[tb][i] = xr[64 * i + lane];
       }
     }
-  }
+  };
+  if (x) load_group(xq[0], 0);
 
 #pragma unroll
-  for (int tb = 0; tb < kRouterTokens; ++tb) {
-    const int t = blockIdx.y * kRouterTokens + tb;
+  for (int g = 0; g < kRouterTokens / kRouterSub; ++g) {
+    if (t0 + g * kRouterSub >= T) break;
+    if (x && g + 1 < kRouterTokens / kRouterSub) load_group(xq[(g + 1) & 1], g + 1);
+#pragma unroll
+  for (int tq = 0; tq < kRouterSub; ++tq) {
+    const int tb = g * kRouterSub + tq;
+    const int t = t0 + tb;
     if (t >= T) break;
     float xv[NI][4];
     if (x) {
@@ -220,7 +252,7 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         uint2 q;
-        if constexpr (XPRE) q = xq[tb][i];
+        if constexpr (XPRE) q = xq[g & 1][tq][i];
         else q = xr[64 * i + lane];
         xv[i][0] = bf16_bits_to_f32(q.x & 0xFFFFu);
         xv[i][1] = bf16_bits_to_f32(q.x >> 16);
@@ -250,13 +282,13 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
         xv[i][1] = bf16_bits_to_f32(b1);
         xv[i][2] = bf16_bits_to_f32(b2);
         xv[i][3] = bf16_bits_to_f32(b3);
-        if (x_trace && blockIdx.x == 0 && wave == tb)
+        if (x_trace && blockIdx.x == 0 && wave == tq)
           reinterpret_cast<uint2*>(x_trace + (size_t)t * D)[64 * i + lane] =
               make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
       }
     }
 
-    if (blockIdx.x == 0 && wave == tb) {
+    if (blockIdx.x == 0 && wave == tq) {
       // The token's MFMA operand row: fp16, each chunk of 8 elements stored
       // as (x0, x4, x1, x5, x2, x6, x3, x7); lane 2m holds x0..x3 of a chunk
       // and lane 2m+1 holds x4..x7, so neighbours trade halves.
@@ -289,30 +321,7 @@ __global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_
       if (lane == 0) a.logits[(size_t)t * a.E + e] = acc;
     }
   }
-
-}
-
-// One workgroup of 16 waves: the softmax + top-k of every token (wave w
-// takes tokens w, w+16, ...; the next token's logits are loaded before the
-// current one is selected), then wave 0 groups the assignments by expert.
-template <int EPL>
-__global__ __launch_bounds__(1024) void k_select(const LayerArgs a, int T, int32_t* __restrict__ idx_out,
-                                                 float* __restrict__ w_out) {
-  __shared__ int s_cnt[1024];
-  __shared__ int s_sel[kMaxAssignments];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
-  float v[EPL], vn[EPL];
-  if (wave < T) load_logits<EPL>(v, a.logits + (size_t)wave * E, E, lane);
-  for (int t = wave; t < T; t += 16) {
-    if (t + 16 < T) load_logits<EPL>(vn, a.logits + (size_t)(t + 16) * E, E, lane);
-    topk_wave<EPL>(v, E, k, a.norm_topk, lane, a.sel_idx + t * k, a.sel_w + t * k, s_sel + t * k,
-                   idx_out ? idx_out + (size_t)t * k : nullptr, w_out ? w_out + (size_t)t * k : nullptr);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = vn[i];
   }
-  __syncthreads();
-  if (wave == 0) sort_by_expert(s_sel, T * k, E, s_cnt, a.off, a.act, a.chunk_off, a.chunks, a.meta, a.asg, lane);
 }
 
 // ----------------------------------------------------------------- MFMA tiles
@@ -659,17 +668,28 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
     default: return hipErrorInvalidValue;
   }
   const int epl = (a.E + 63) / 64;
-  const dim3 g(1), b(1024);
+  const dim3 g(T), b(64);
   if (epl <= 1)
-    hipLaunchKernelGGL((k_select<1>), g, b, 0, s, a, T, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<1>), g, b, 0, s, a, idx_out, w_out);
   else if (epl <= 2)
-    hipLaunchKernelGGL((k_select<2>), g, b, 0, s, a, T, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<2>), g, b, 0, s, a, idx_out, w_out);
   else if (epl <= 4)
-    hipLaunchKernelGGL((k_select<4>), g, b, 0, s, a, T, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<4>), g, b, 0, s, a, idx_out, w_out);
   else if (epl <= 8)
-    hipLaunchKernelGGL((k_select<8>), g, b, 0, s, a, T, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<8>), g, b, 0, s, a, idx_out, w_out);
   else
-    hipLaunchKernelGGL((k_select<16>), g, b, 0, s, a, T, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<16>), g, b, 0, s, a, idx_out, w_out);
+  const size_t lds = sort_lds_bytes(a.E, T * a.k);
+  if (lds > 64 * 1024) {
+    static bool raised = false;
+    if (!raised) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sort_lds_bytes(1024, kMaxAssignments)) != hipSuccess)
+        return hipErrorInvalidValue;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), lds, s, a, T);
   return hipGetLastError();
 }
 
