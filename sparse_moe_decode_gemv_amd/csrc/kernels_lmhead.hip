@@ -151,6 +151,235 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   if (threadIdx.x == 0) *counter = 0u;
 }
 
+// ---------------------------------------------------------------- MFMA path (3 <= B <= 16)
+//
+// Logits of 16 vocabulary rows x up to 16 x rows per group of 32 elements
+// with one v_mfma_f32_16x16x32_f16 (A = x rows, zero past B; B operand = 16
+// weight rows: lane l holds row l%16, chunk l/16 of the group).  A group of
+// 32 is exactly one scale group, so the operand holds the codes q = u - 8
+// (small integers, exact in fp16) and the scale is applied to the MFMA's
+// fp32 result, accumulated in fp32: the weights enter exactly.  x enters as
+// fp16 after multiplying each row by a power of two that brings its largest
+// magnitude into [2^14, 2^15) (bf16 values are then exact in fp16 down to
+// 2^-24 of the row maximum); the argmax of a row is unchanged by that
+// factor and its maximum logit is scaled back at the end.
+// The 4 waves of a workgroup split K into quarters; each keeps its quarter
+// of x as fragments in registers (elements in the order 0,4,1,5,2,6,3,7 of
+// every 8, the order the magic-number extraction yields) and streams 16-row
+// tiles of W with loads that are contiguous along each row (256 bytes of a
+// row per quarter for d = 2048), two tiles ahead; a small wave-private LDS
+// block, XOR-swizzled so that its stores and its fragment reads are free of
+// bank conflicts, turns them into MFMA lane order.  The 4 quarter sums meet
+// in LDS, one barrier per tile; wave 0 keeps the running (value, row)
+// maximum per x row, and the workgroup results are reduced as in the VALU
+// path.
+typedef _Float16 lm_f16x8 __attribute__((ext_vector_type(8)));
+typedef float lm_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lm_magic() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
+// 8 codes of one dword (elements e = 0..7, nibble e of the stored format) as
+// fp16 q = u - 8 in the order e0,e4,e1,e5,e2,e6,e3,e7: the nibbles are
+// placed in the mantissa of 1024 (even: 1024 + u; odd: 1024 + 16u) and the
+// offset removed exactly
+__device__ __forceinline__ lm_f16x8 lm_codes(uint32_t w, uint32_t magic) {
+  const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2_t sx = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2_t so = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = w >> 8;
+  const f16x2_t q0 = __builtin_bit_cast(f16x2_t, (w & 0x000F000Fu) | magic) + off;
+  const f16x2_t q1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w & 0x00F000F0u) | magic), sx, so);
+  const f16x2_t q2 = __builtin_bit_cast(f16x2_t, (w8 & 0x000F000Fu) | magic) + off;
+  const f16x2_t q3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, (w8 & 0x00F000F0u) | magic), sx, so);
+  const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+                             __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3));
+  return __builtin_bit_cast(lm_f16x8, v);
+}
+__device__ __forceinline__ uint32_t lm_dword(uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restrict__ wq,
+                                                        const uint16_t* __restrict__ ws, int V,
+                                                        const uint16_t* __restrict__ x, int B,
+                                                        unsigned long long* __restrict__ partial,
+                                                        unsigned* __restrict__ counter, int32_t* __restrict__ token,
+                                                        float* __restrict__ max_logit) {
+  constexpr int KQ = D / 4;          // K elements per wave
+  constexpr int NBQ = KQ / 128;      // 128-element blocks per wave
+  constexpr int PPR = KQ / 32;       // 16-byte pieces of a row in the quarter
+  constexpr int RPI = 64 / PPR;      // rows per load instruction
+  constexpr int NI = 16 / RPI;       // load instructions per 16-row tile
+  constexpr int SH = 16 / PPR > 1 ? (16 / PPR == 2 ? 1 : 2) : 0;  // log2(16 / PPR)
+  static_assert(NBQ >= 1 && PPR <= 64 && 64 % PPR == 0, "d = 512, 1024 or 2048");
+  __shared__ uint4 s_w[4][16 * PPR];
+  __shared__ uint2 s_s[4][16 * NBQ];
+  __shared__ lm_f32x4 s_acc[2][4][64];
+  __shared__ unsigned long long s_key[16];
+  __shared__ uint32_t s_xm[4][16];
+  __shared__ bool s_last;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  const uint32_t magic = lm_magic();
+  const int ntiles = (V + 15) >> 4;
+
+  // this wave's quarter of x: row r16 (< B), block b, group j, chunk q
+  uint4 xr[NBQ][4];
+  uint32_t xm = 0;  // largest |x| as a bf16 magnitude pattern (ordered like the values)
+#pragma unroll
+  for (int b = 0; b < NBQ; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = wave * KQ + 128 * b + 32 * j + 8 * q;
+      xr[b][j] = r16 < B ? *reinterpret_cast<const uint4*>(x + (size_t)r16 * D + k0) : make_uint4(0, 0, 0, 0);
+      const uint32_t c[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xm = max(xm, max(c[e] & 0x7FFFu, (c[e] >> 16) & 0x7FFFu));
+    }
+  xm = max(xm, (uint32_t)__shfl_xor((int)xm, 16, 64));
+  xm = max(xm, (uint32_t)__shfl_xor((int)xm, 32, 64));
+  if (lane < 16) s_xm[wave][lane] = xm;
+  __syncthreads();
+  xm = max(max(s_xm[0][r16], s_xm[1][r16]), max(s_xm[2][r16], s_xm[3][r16]));
+  // row r16 is multiplied by 2^-sh, sh = (exponent of its maximum) - 14
+  const int sh = max((int)(xm >> 7) - 141, -126);
+  const float fx = __uint_as_float((uint32_t)(127 - sh) << 23);
+  uint4 xf[NBQ][4];
+#pragma unroll
+  for (int b = 0; b < NBQ; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = xr[b][j];
+      const float e0 = bf16_bits_to_f32(v.x & 0xFFFFu) * fx, e1 = __uint_as_float(v.x & 0xFFFF0000u) * fx;
+      const float e2 = bf16_bits_to_f32(v.y & 0xFFFFu) * fx, e3 = __uint_as_float(v.y & 0xFFFF0000u) * fx;
+      const float e4 = bf16_bits_to_f32(v.z & 0xFFFFu) * fx, e5 = __uint_as_float(v.z & 0xFFFF0000u) * fx;
+      const float e6 = bf16_bits_to_f32(v.w & 0xFFFFu) * fx, e7 = __uint_as_float(v.w & 0xFFFF0000u) * fx;
+      xf[b][j] = make_uint4(pack_f16(e0, e4), pack_f16(e1, e5), pack_f16(e2, e6), pack_f16(e3, e7));
+    }
+
+  // weight loads of one tile: instruction i, lane l -> row RPI*i + l/PPR of the tile, piece l%PPR
+  struct TileRegs {
+    uint4 w[NI];
+    uint2 s;
+  };
+  auto load_tile = [&](int tt) {
+    TileRegs r;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = min(16 * tt + RPI * i + lane / PPR, V - 1);
+      r.w[i] = *reinterpret_cast<const uint4*>(wq + (size_t)row * (D / 2) + wave * (KQ / 2) + 16 * (lane % PPR));
+    }
+    const int srow = min(16 * tt + min(lane / NBQ, 15), V - 1);
+    r.s = *reinterpret_cast<const uint2*>(ws + (size_t)srow * (D / 32) + wave * (KQ / 32) + 4 * (lane % NBQ));
+    return r;
+  };
+  int t = blockIdx.x;
+  TileRegs tr0 = load_tile(min(t, ntiles - 1));
+  TileRegs tr1 = load_tile(min(t + (int)gridDim.x, ntiles - 1));
+
+  float best[4];
+  uint32_t brow[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) best[v] = -INFINITY, brow[v] = 0xFFFFFFFFu;
+
+  // one tile per step: its weights (tr0 or tr1) through the wave's LDS block
+  // into MFMAs, then the next-but-one tile's loads into the same registers;
+  // par also selects the accumulator buffer, so one barrier per tile suffices
+  bool more = t < ntiles;
+  while (more) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      if (more) {
+        TileRegs& tr = par ? tr1 : tr0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r = RPI * i + lane / PPR, p = lane % PPR;
+          s_w[wave][r * PPR + (p ^ ((r >> SH) & (PPR - 1)))] = tr.w[i];  // piece p of row r at slot p ^ (r >> SH)
+        }
+        if (lane < 16 * NBQ) s_s[wave][lane] = tr.s;
+        // other lanes of this wave read these slots: keep the compiler from
+        // moving the reads above the stores (the wave's LDS operations run in order)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        tr = load_tile(min(t + 2 * (int)gridDim.x, ntiles - 1));
+        lm_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NBQ; ++b) {
+          const int p = 4 * b + q;
+          const uint4 wc = s_w[wave][r16 * PPR + (p ^ ((r16 >> SH) & (PPR - 1)))];
+          const uint2 sc = s_s[wave][r16 * NBQ + b];
+          const float sg[4] = {f16_lo(sc.x), f16_hi(sc.x), f16_lo(sc.y), f16_hi(sc.y)};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const lm_f32x4 g = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(lm_f16x8, xf[b][j]), lm_codes(lm_dword(wc, j), magic),
+                lm_f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sg[j], g[v], acc[v]);
+          }
+        }
+        s_acc[par][wave][lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+          // lane: vocabulary row 16t + r16, x rows 4q + v
+          const lm_f32x4 z =
+              (s_acc[par][0][lane] + s_acc[par][1][lane]) + (s_acc[par][2][lane] + s_acc[par][3][lane]);
+          const uint32_t row = 16u * t + r16;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (row < (uint32_t)V && z[v] > best[v]) best[v] = z[v], brow[v] = row;
+        }
+        t += gridDim.x;
+        more = t < ntiles;
+      }
+    }
+  }
+
+  // per x row: maximum over the 16 lanes of its group (rows in increasing order per lane)
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      unsigned long long key = brow[v] == 0xFFFFFFFFu ? 0ull : make_key(best[v], brow[v]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const unsigned long long other = __shfl_xor(key, o, 64);
+        key = other > key ? other : key;
+      }
+      if (r16 == 0) s_key[4 * q + v] = key;
+    }
+  }
+  __syncthreads();
+  if (tid < B) {
+    store_coherent(partial + (size_t)blockIdx.x * 16 + tid, s_key[tid]);
+    wait_vm();
+  }
+  __syncthreads();
+  if (tid == 0) s_last = arrive(counter) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // last workgroup: one wave per x row reduces the workgroup keys
+  for (int b = wave; b < B; b += 4) {
+    unsigned long long kmax = 0;
+    for (int g = lane; g < (int)gridDim.x; g += 64) {
+      const unsigned long long kv = load_coherent(partial + (size_t)g * 16 + b);
+      kmax = kv > kmax ? kv : kmax;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long other = __shfl_xor(kmax, o, 64);
+      kmax = other > kmax ? other : kmax;
+    }
+    if (lane == 0) {
+      token[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(kmax & 0xFFFFFFFFull));
+      if (max_logit) {
+        const uint32_t m = max(max(s_xm[0][b], s_xm[1][b]), max(s_xm[2][b], s_xm[3][b]));
+        max_logit[b] = ldexpf(unordered_bits((uint32_t)(kmax >> 32)), max((int)(m >> 7) - 141, -126));
+      }
+    }
+  }
+  if (tid == 0) *counter = 0u;
+}
+
 size_t lmhead_workspace_bytes(int V, int d, int B) {
   (void)V;
   (void)d;
@@ -196,9 +425,27 @@ static void lm_b(const uint8_t* wq, const uint16_t* ws, int V, const uint16_t* x
     lm_inst<CPR, 8>(wq, ws, V, x, B, wsp, token, max_logit, s);
 }
 
+template <int D>
+static hipError_t lm_mfma(const uint8_t* wq, const uint16_t* ws, int V, const uint16_t* x, int B, unsigned char* wsp,
+                          int32_t* token, float* max_logit, hipStream_t s) {
+  unsigned* counter = reinterpret_cast<unsigned*>(wsp);
+  unsigned long long* partial = reinterpret_cast<unsigned long long*>(wsp + 256);
+  const int ntiles = (V + 15) / 16;
+  int grid = 2 * (lm_grid() / 4);  // two workgroups per compute unit
+  if (grid > ntiles) grid = ntiles;
+  hipLaunchKernelGGL((k_lmhead_mfma<D>), dim3(grid), dim3(256), 0, s, wq, ws, V, x, B, partial, counter, token,
+                     max_logit);
+  return hipGetLastError();
+}
+
 hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,
                          int32_t* token, float* max_logit, void* workspace, hipStream_t s) {
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
+  if (B >= 3 && B <= 16) {  // MFMA tiles (one 16-row x tile) for the shapes they are built for
+    if (d == 512) return lm_mfma<512>(wq, ws, V, x, B, wsp, token, max_logit, s);
+    if (d == 1024) return lm_mfma<1024>(wq, ws, V, x, B, wsp, token, max_logit, s);
+    if (d == 2048) return lm_mfma<2048>(wq, ws, V, x, B, wsp, token, max_logit, s);
+  }
   const size_t per = 256 + (size_t)kLmMaxGrid * 8 * sizeof(unsigned long long);
   for (int b0 = 0; b0 < B; b0 += 8) {
     const int nb = B - b0 < 8 ? B - b0 : 8;

@@ -32,9 +32,12 @@ def check(q, s, X, what):
     assert np.all(np.abs(ml - oml) <= tol), f"{what}: max logit {ml} vs {oml}"
 
 
-def test_v16_hand_worked_tie_goes_to_lower_row():
+@pytest.mark.parametrize("d,B", [(256, 1), (512, 4), (2048, 16)], ids=["valu", "mfma-d512", "mfma-d2048"])
+def test_v16_hand_worked_tie_goes_to_lower_row(d, B):
+    """The hand-worked 16-row head (zero weights past k = 1), the same x in
+    every one of B rows: the 1-2 row kernel and the 16-row MFMA tiles."""
     rows = golden_lines("lmhead_v16.txt")
-    V, d = 16, 256
+    V = 16
     u = np.full((V, d), 8)
     s = np.full((V, d // 32), 0x3C00, np.uint16)
     for r in rows:
@@ -43,14 +46,54 @@ def test_v16_hand_worked_tie_goes_to_lower_row():
         v = int(r[0])
         u[v, 0], u[v, 1] = int(r[1]) + 8, int(r[2]) + 8
         s[v, 0] = F.f64_to_f16_bits(float(r[3]))
-    X = np.zeros((1, d), np.uint16)
-    X[0, 0], X[0, 1] = 0x3F80, 0x4000
+    X = np.zeros((B, d), np.uint16)
+    X[:, 0], X[:, 1] = 0x3F80, 0x4000
     tok, ml = run(F.pack_codes(u), s, X)
-    assert tok[0] == 3 and ml[0] == 21.0
+    assert np.all(tok == 3) and np.all(ml == 21.0), (tok, ml)
+
+
+@pytest.mark.parametrize("d,B", [(2048, 6), (1024, 5), (4096, 6)], ids=["mfma-d2048", "mfma-d1024", "valu-d4096"])
+def test_extreme_magnitudes_of_x(d, B):
+    """Rows of x scaled by 2^100 and 2^-100 (exact in bf16): the same
+    tokens as the unscaled rows and maximum logits scaled by the same power
+    of two, checked against the fp64 oracle on the scaled rows."""
+    V = 5000
+    q, s = synth.int4_matrix(V, d, synth.key(23, "lm-scale", V, d), 0.02)
+    X, _ = pick_hidden_rows(q, s, 1e-2, lambda b, a: synth.bf16(d, synth.key(23, "h", d, b, a)), 2)
+    up, down = X.copy(), X.copy()
+    nz = (X & 0x7FFF) != 0
+    up[nz] += np.uint16(100 << 7)      # exponent field + 100
+    down[nz] -= np.uint16(100 << 7)    # exponent field - 100 (no draw is that small)
+    assert np.all(((X[nz] & 0x7F80) >> 7) > 100) and np.all(((X[nz] & 0x7F80) >> 7) < 155)
+    Xs = np.concatenate([X, up, down] * 2)[:B]
+    check(q, s, Xs, f"scaled rows d={d} B={B}")
+    tok, _ = run(q, s, Xs)
+    assert np.array_equal(tok[2:4], tok[0:2]) and np.array_equal(tok[4:6], tok[0:2][: len(tok) - 4])
+
+
+@pytest.mark.parametrize("d,B", [(2048, 4), (2048, 2), (512, 9)], ids=["mfma", "valu", "mfma-d512"])
+def test_equal_rows_far_apart_lowest_index_wins(d, B):
+    """The winning row of each x copied to rows in other tiles and
+    workgroups, one of them below it: every copy ties bit for bit and the
+    lowest index is returned."""
+    V = 40000
+    q, s = synth.int4_matrix(V, d, synth.key(24, "lm-tie", V, d), 0.02)
+    X, _ = pick_hidden_rows(q, s, 1e-2, lambda b, a: synth.bf16(d, synth.key(24, "h", d, b, a)), B)
+    otok, _, _ = OH.lmhead_argmax(q, s, X)
+    for i, a in enumerate(otok):
+        for c in (a // 2, (a + 12345) % V, V - 1 - i):
+            if c not in otok:
+                q[c], s[c] = q[a], s[a]
+    tok2, _, z = OH.lmhead_argmax(q, s, X)
+    assert np.all(tok2 <= otok) and np.any(tok2 < otok)
+    for b in range(B):   # apart from exact copies, the gap still holds
+        m = z[b].max()
+        assert m - z[b][z[b] < m].max() >= 1e-2
+    check(q, s, X, f"copied rows d={d} B={B}")
 
 
 @pytest.mark.parametrize("V,d,B", [(1000, 256, 1), (4099, 512, 3), (20000, 2048, 8), (3000, 4096, 2),
-                                   (777, 2048, 16)])
+                                   (777, 2048, 16), (6007, 1024, 7), (33, 2048, 3), (50001, 1024, 12)])
 def test_small_heads_ragged_rows(V, d, B):
     q, s = synth.int4_matrix(V, d, synth.key(21, "lm-small", V, d), 0.02)
     X, _ = pick_hidden_rows(q, s, 1e-2, lambda b, a: synth.bf16(d, synth.key(21, "h", V, d, b, a)), B)
