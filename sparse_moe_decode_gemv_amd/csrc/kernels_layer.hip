@@ -17,8 +17,8 @@
 //            sharing a line serialize at the memory side);
 //   select   wave 0 of every workgroup polls the tagged logits until all
 //            carry this call's tag; every wave then runs the exact top-k
-//            rounds itself and issues its gate/up loads the moment its own
-//            expert is decided;
+//            itself (lists of the largest keys merged across lanes in
+//            registers, no serial rounds) and issues its gate/up loads;
 //   experts  the workgroup turns its 16 values h = w_j * silu(g) * u into
 //            two ready-made fp16 dot slices and writes every slice word with
 //            the tag, then prefetches its down pieces;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   __shared__ float s_lg[64 * EPL];
   __shared__ unsigned s_pub[ROWS_G / 8 * 5];
 
-  __shared__ __align__(16) uint16_t s_x[NORM ? D : 8];
+  __shared__ __align__(16) uint16_t s_x[D];
   __shared__ float s_ss[4];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -126,16 +126,25 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   const unsigned tag = a.epoch[blockIdx.x] + 1u;  // this workgroup's own call count
   const float bias = (a.router_b && wg < E) ? a.router_b[wg] : 0.f;
 
-  // the activation: bf16 from the caller, or the normalized residual in LDS
-  auto x2 = [&](int i) -> uint2 {  // bf16 elements 4i .. 4i+3
-    if constexpr (NORM) return reinterpret_cast<const uint2*>(s_x)[i];
-    else return reinterpret_cast<const uint2*>(a.x)[i];
-  };
-  auto x4 = [&](int i) -> uint4 {  // bf16 elements 8i .. 8i+7
-    if constexpr (NORM) return reinterpret_cast<const uint4*>(s_x)[i];
-    else return reinterpret_cast<const uint4*>(a.x)[i];
-  };
-  if constexpr (NORM) {
+  // the activation in LDS: bf16 from the caller, or the normalized
+  // residual.  Copied once at the start, so that no later phase issues a
+  // global load behind the expert weight loads and waits for all of them.
+  auto x2 = [&](int i) -> uint2 { return reinterpret_cast<const uint2*>(s_x)[i]; };  // elements 4i .. 4i+3
+  auto x4 = [&](int i) -> uint4 { return reinterpret_cast<const uint4*>(s_x)[i]; };  // elements 8i .. 8i+7
+  // router row wg (one per wave): its weight loads go out first and stay in
+  // flight while the activation is staged
+  const bool router_row = blockIdx.x * 4 < E && wg < E;
+  float4 w[NI];
+  if (router_row) {
+    const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)wg * D);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane];
+  }
+  if constexpr (!NORM) {
+#pragma unroll
+    for (int c = threadIdx.x; c < D / 8; c += 256) reinterpret_cast<uint4*>(s_x)[c] = reinterpret_cast<const uint4*>(a.x)[c];
+    __syncthreads();
+  } else {
     // x = bf16(r / sqrt(mean(r^2) + eps)), the same in every workgroup
     constexpr int NR = (D / 4 + 255) / 256;
     float4 rv[NR];
@@ -169,12 +178,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   // rows 4*b .. 4*b+3 in workgroup b, one per wave; the 4 logits go out as
   // (tag, value) words in the workgroup's own 128-byte line.
   if (blockIdx.x * 4 < E) {
-    if (wg < E) {
-      const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)wg * D);
-      float4 w[NI];
+    if (router_row) {
       uint2 q[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane], q[i] = x2(64 * i + lane);
+      for (int i = 0; i < NI; ++i) q[i] = x2(64 * i + lane);
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -193,8 +200,8 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
   // ---------------------------------------------------------------- select
   // wave 0 polls the logits and shares them through LDS; then every wave
-  // runs the selection rounds itself and issues its gate/up loads as soon as
-  // its own slot is decided.  The softmax weights follow while the loads
+  // runs the selection itself and issues its gate/up loads as soon as its
+  // own slot is decided.  The softmax weights follow while the loads
   // are in flight (they are needed only at the end of gate/up).
   if (wid == 0) {
     float v0[EPL];
@@ -233,37 +240,16 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
   int se = 0;
   bool exact = false;
-  {
-    const int ib = E <= 2 ? 1 : 32 - __clz(E - 1);
-    const uint32_t imask = (1u << ib) - 1u;
-    uint32_t key[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      key[i] = lane + 64 * i < E ? ((ordered_bits(v[i]) & ~imask) | (imask - (uint32_t)(lane + 64 * i))) : 0u;
-    uint32_t prev = 0;
-    bool close = false;
-    for (int r = 0; r <= k && r < E; ++r) {
-      uint32_t loc = key[0];
-#pragma unroll
-      for (int i = 1; i < EPL; ++i) loc = max(loc, key[i]);
-      const uint32_t M = wave_max_u32(loc);
-      close = close || (r > 0 && ((M ^ prev) & ~imask) == 0u);
-      prev = M;
-      if (r == k) break;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) key[i] = key[i] == M ? 0u : key[i];
-      const int e_r = (int)(imask - (M & imask));
-      if (lane == r) se = e_r;
-      if (r == gslot) load_gate(e_r);
-    }
-    if (close) {  // picks that agree in their top bits: redo exactly, reload
-      float sw;
-      topk_exact<EPL>(v, E, k, a.norm, lane, se, sw);
-      if (wid == 0 && lane < k) s_w[lane] = sw;
-      exact = true;
-      const int e_slot = __shfl(se, max(gslot, 0), 64);
-      if (has_gate) load_gate(e_slot);
-    }
+  if (topk_select_merge<EPL, KP>(v, E, k, lane, se)) {
+    const int e_slot = __shfl(se, max(gslot, 0), 64);
+    if (has_gate) load_gate(e_slot);
+  } else {  // picks that agree in their top bits: redo exactly
+    float sw;
+    topk_exact<EPL>(v, E, k, a.norm, lane, se, sw);
+    if (wid == 0 && lane < k) s_w[lane] = sw;
+    exact = true;
+    const int e_slot = __shfl(se, max(gslot, 0), 64);
+    if (has_gate) load_gate(e_slot);
   }
   if (wid == 0) {
     if (lane < k) s_idx[lane] = se;

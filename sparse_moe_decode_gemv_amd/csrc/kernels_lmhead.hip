@@ -276,6 +276,9 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
   };
   int t = blockIdx.x;
   TileRegs tr0 = load_tile(min(t, ntiles - 1));
+  // tile t's loads issue before tile t + G's, the order the loop consumes
+  // them in, so the waits before each step leave the later tile in flight
+  __builtin_amdgcn_sched_barrier(0);
   TileRegs tr1 = load_tile(min(t + (int)gridDim.x, ntiles - 1));
 
   float best[4];
@@ -283,57 +286,55 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
 #pragma unroll
   for (int v = 0; v < 4; ++v) best[v] = -INFINITY, brow[v] = 0xFFFFFFFFu;
 
-  // one tile per step: its weights (tr0 or tr1) through the wave's LDS block
-  // into MFMAs, then the next-but-one tile's loads into the same registers;
-  // par also selects the accumulator buffer, so one barrier per tile suffices
-  bool more = t < ntiles;
-  while (more) {
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      if (more) {
-        TileRegs& tr = par ? tr1 : tr0;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int r = RPI * i + lane / PPR, p = lane % PPR;
-          s_w[wave][r * PPR + (p ^ ((r >> SH) & (PPR - 1)))] = tr.w[i];  // piece p of row r at slot p ^ (r >> SH)
-        }
-        if (lane < 16 * NBQ) s_s[wave][lane] = tr.s;
-        // other lanes of this wave read these slots: keep the compiler from
-        // moving the reads above the stores (the wave's LDS operations run in order)
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        tr = load_tile(min(t + 2 * (int)gridDim.x, ntiles - 1));
-        lm_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < NBQ; ++b) {
-          const int p = 4 * b + q;
-          const uint4 wc = s_w[wave][r16 * PPR + (p ^ ((r16 >> SH) & (PPR - 1)))];
-          const uint2 sc = s_s[wave][r16 * NBQ + b];
-          const float sg[4] = {f16_lo(sc.x), f16_hi(sc.x), f16_lo(sc.y), f16_hi(sc.y)};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const lm_f32x4 g = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(lm_f16x8, xf[b][j]), lm_codes(lm_dword(wc, j), magic),
-                lm_f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sg[j], g[v], acc[v]);
-          }
-        }
-        s_acc[par][wave][lane] = acc;
-        __syncthreads();
-        if (wave == 0) {
-          // lane: vocabulary row 16t + r16, x rows 4q + v
-          const lm_f32x4 z =
-              (s_acc[par][0][lane] + s_acc[par][1][lane]) + (s_acc[par][2][lane] + s_acc[par][3][lane]);
-          const uint32_t row = 16u * t + r16;
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (row < (uint32_t)V && z[v] > best[v]) best[v] = z[v], brow[v] = row;
-        }
-        t += gridDim.x;
-        more = t < ntiles;
-      }
-    }
+  // one tile per step: its weights (TR = tr0 or tr1) through the wave's LDS
+  // block into MFMAs, then the next-but-one tile's loads into the same
+  // registers; PAR also selects the accumulator buffer, so one barrier per
+  // tile suffices.  The two steps are written out so that each register set
+  // stays in place and the next tile's loads stay in flight.
+#define LM_MFMA_STEP(TR, PAR)                                                                                   \
+  {                                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                                           \
+      const int r = RPI * i + lane / PPR, p = lane % PPR;                                                      \
+      s_w[wave][r * PPR + (p ^ ((r >> SH) & (PPR - 1)))] = TR.w[i]; /* piece p of row r at slot p ^ (r >> SH) */ \
+    }                                                                                                          \
+    if (lane < 16 * NBQ) s_s[wave][lane] = TR.s;                                                               \
+    /* other lanes of this wave read these slots: keep the compiler from moving   */                          \
+    /* the reads above the stores (the wave's LDS operations run in order)        */                          \
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");                                                     \
+    TR = load_tile(min(t + 2 * (int)gridDim.x, ntiles - 1));                                                   \
+    lm_f32x4 acc = {0.f, 0.f, 0.f, 0.f};                                                                       \
+    _Pragma("unroll") for (int b = 0; b < NBQ; ++b) {                                                          \
+      const int p = 4 * b + q;                                                                                 \
+      const uint4 wc = s_w[wave][r16 * PPR + (p ^ ((r16 >> SH) & (PPR - 1)))];                                 \
+      const uint2 sc = s_s[wave][r16 * NBQ + b];                                                               \
+      const float sg[4] = {f16_lo(sc.x), f16_hi(sc.x), f16_lo(sc.y), f16_hi(sc.y)};                            \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                          \
+        const lm_f32x4 g = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                             \
+            __builtin_bit_cast(lm_f16x8, xf[b][j]), lm_codes(lm_dword(wc, j), magic),                          \
+            lm_f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);                                                            \
+        _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sg[j], g[v], acc[v]);            \
+      }                                                                                                        \
+    }                                                                                                          \
+    s_acc[PAR][wave][lane] = acc;                                                                              \
+    __syncthreads();                                                                                           \
+    if (wave == 0) {                                                                                           \
+      /* lane: vocabulary row 16t + r16, x rows 4q + v */                                                      \
+      const lm_f32x4 z =                                                                                       \
+          (s_acc[PAR][0][lane] + s_acc[PAR][1][lane]) + (s_acc[PAR][2][lane] + s_acc[PAR][3][lane]);           \
+      const uint32_t row = 16u * t + r16;                                                                      \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) if (row < (uint32_t)V && z[v] > best[v]) best[v] = z[v],   \
+          brow[v] = row;                                                                                       \
+    }                                                                                                          \
+    t += gridDim.x;                                                                                            \
   }
+  // steps in pairs (a step past the last tile reads a clamped tile and
+  // updates nothing), so that the loop has a single exit
+  const int nsteps = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  for (int n = 0; n < nsteps; n += 2) {
+    LM_MFMA_STEP(tr0, 0)
+    LM_MFMA_STEP(tr1, 1)
+  }
+#undef LM_MFMA_STEP
 
   // per x row: maximum over the 16 lanes of its group (rows in increasing order per lane)
   if (wave == 0) {

@@ -59,7 +59,7 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // Softmax + top-k of one token's E logits in one wave (topk.h): grid T,
 // block 64, one token per workgroup (one wave per SIMD of its own: a wave64
 // VALU instruction takes 4 cycles, so waves sharing a SIMD would serialize).
-template <int EPL>
+template <int EPL, int KP>
 __global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int32_t* __restrict__ idx_out,
                                              float* __restrict__ w_out) {
   const int t = blockIdx.x, lane = threadIdx.x, E = a.E, k = a.k;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int32_t* __restr
   }
   int se;
   float sw;
-  topk_fast<EPL>(v, E, k, a.norm_topk, lane, se, sw);
+  topk_fast<EPL, KP>(v, E, k, a.norm_topk, lane, se, sw);
   if (lane < k) {
     a.sel_idx[t * k + lane] = se;
     a.sel_w[t * k + lane] = sw;
@@ -656,6 +656,14 @@ static void router_inst(const LayerArgs& a, const uint16_t* x, const float* r, f
                      a, x, r, eps, T, xt);
 }
 
+template <int EPL>
+static void topk_inst(const LayerArgs& a, int T, int32_t* idx_out, float* w_out, hipStream_t s) {
+  if (a.k <= 8)
+    hipLaunchKernelGGL((k_topk<EPL, 8>), dim3(T), dim3(64), 0, s, a, idx_out, w_out);
+  else
+    hipLaunchKernelGGL((k_topk<EPL, 16>), dim3(T), dim3(64), 0, s, a, idx_out, w_out);
+}
+
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
                          int32_t* idx_out, float* w_out, uint16_t* x_trace, hipStream_t s) {
   switch (a.d) {
@@ -668,17 +676,16 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
     default: return hipErrorInvalidValue;
   }
   const int epl = (a.E + 63) / 64;
-  const dim3 g(T), b(64);
   if (epl <= 1)
-    hipLaunchKernelGGL((k_topk<1>), g, b, 0, s, a, idx_out, w_out);
+    topk_inst<1>(a, T, idx_out, w_out, s);
   else if (epl <= 2)
-    hipLaunchKernelGGL((k_topk<2>), g, b, 0, s, a, idx_out, w_out);
+    topk_inst<2>(a, T, idx_out, w_out, s);
   else if (epl <= 4)
-    hipLaunchKernelGGL((k_topk<4>), g, b, 0, s, a, idx_out, w_out);
+    topk_inst<4>(a, T, idx_out, w_out, s);
   else if (epl <= 8)
-    hipLaunchKernelGGL((k_topk<8>), g, b, 0, s, a, idx_out, w_out);
+    topk_inst<8>(a, T, idx_out, w_out, s);
   else
-    hipLaunchKernelGGL((k_topk<16>), g, b, 0, s, a, idx_out, w_out);
+    topk_inst<16>(a, T, idx_out, w_out, s);
   const size_t lds = sort_lds_bytes(a.E, T * a.k);
   if (lds > 64 * 1024) {
     static bool raised = false;

@@ -9,14 +9,13 @@
 // exp(l_j - max l) over the chosen set, divided by their sum (renormalized)
 // or by the sum over all experts.
 //
-// topk_fast: every round is one wave maximum (DPP + permlane, VALU only) of
-// 32-bit keys holding the top bits of the order-preserving logit bits and,
-// in the low bits, the inverted expert index, so the maximum names its
-// owner.  The truncation can only mis-order logits that agree in their top
-// bits; one extra round checks every consecutive pair of picks (the k-th
-// against the best unpicked included) and, if any agree, the selection is
-// redone by topk_exact, which compares full values and breaks exact ties by
-// ballot.
+// topk_fast selects with 32-bit keys holding the top bits of the
+// order-preserving logit bits and, in the low bits, the inverted expert
+// index, so keys are distinct and the largest names its owner.  The
+// truncation can only mis-order logits that agree in their top bits; every
+// consecutive pair of the k + 1 largest keys is checked and, if any agree,
+// the selection is redone by topk_exact, which compares full values and
+// breaks exact ties by ballot.
 #pragma once
 
 #include "device_common.h"
@@ -95,41 +94,114 @@ __device__ __forceinline__ float topk_weight(const float v[EPL], int E, int k, i
   return p / den;
 }
 
-// The k choices only (lane r < k gets choice r), same result as topk_exact.
-// Returns false when two picks agree in their top bits: the caller must then
-// use topk_exact.
-template <int EPL>
-__device__ __forceinline__ bool topk_select_fast(const float v[EPL], int E, int k, int lane, int& sel_e) {
+// Bitonic compare-exchange network sorting N registers in descending order
+// (N a power of two), all indices compile-time.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint32_t (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;  // direction of this run
+          const uint32_t hi = max(a[i], a[j]), lo = min(a[i], a[j]);
+          a[i] = desc ? hi : lo;
+          a[j] = desc ? lo : hi;
+        }
+      }
+}
+
+// a: descending; b: descending.  a receives the KP largest of both, descending.
+template <int KP>
+__device__ __forceinline__ void merge_top(uint32_t (&a)[KP], const uint32_t (&b)[KP]) {
+#pragma unroll
+  for (int i = 0; i < KP; ++i) a[i] = max(a[i], b[KP - 1 - i]);  // bitonic: falls, then rises
+#pragma unroll
+  for (int stride = KP >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int j = i ^ stride;
+      if (j > i) {
+        const uint32_t hi = max(a[i], a[j]), lo = min(a[i], a[j]);
+        a[i] = hi;
+        a[j] = lo;
+      }
+    }
+}
+
+// The k choices (lane r < k gets choice r, every lane gets its own slot's
+// expert through slot_e), the same as topk_exact unless it returns false
+// (two of the k + 1 largest keys agree in their top bits; the caller must
+// then use topk_exact).  k <= KP (a power of two <= 16).
+// Selection by k rounds of wave maxima would chain k times about ten
+// dependent DPP/permlane steps.  Here every lane sorts its EPL keys and the
+// lanes merge their lists of the KP largest along the six pairing steps of
+// a wave reduction (each step: the partner's list through DPP or a permlane
+// swap, then a bitonic merge in registers), so every lane ends with the
+// global KP largest, in order.
+template <int EPL, int KP>
+__device__ __forceinline__ bool topk_select_merge(const float v[EPL], int E, int k, int lane, int& sel_e) {
   const int ib = E <= 2 ? 1 : 32 - __clz(E - 1);
   const uint32_t imask = (1u << ib) - 1u;
-  uint32_t key[EPL];
+  constexpr int N0 = EPL > KP ? EPL : KP;
+  uint32_t a0[N0];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    key[i] = lane + 64 * i < E ? ((ordered_bits(v[i]) & ~imask) | (imask - (uint32_t)(lane + 64 * i))) : 0u;
-  int my_e = 0;
-  uint32_t prev = 0;
-  bool close = false;
-  for (int r = 0; r <= k && r < E; ++r) {
-    uint32_t loc = key[0];
+  for (int i = 0; i < N0; ++i)
+    a0[i] = i < EPL && lane + 64 * i < E ? ((ordered_bits(v[i]) & ~imask) | (imask - (uint32_t)(lane + 64 * i))) : 0u;
+  sort_desc<N0>(a0);
+  uint32_t L[KP];
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) loc = max(loc, key[i]);
-    const uint32_t M = wave_max_u32(loc);
-    close = close || (r > 0 && ((M ^ prev) & ~imask) == 0u);
-    prev = M;
-    if (r == k) break;
+  for (int i = 0; i < KP; ++i) L[i] = a0[i];
+  uint32_t P[KP];
+#define TOPK_DPP_LEVEL(CTRL)                                \
+  _Pragma("unroll") for (int i = 0; i < KP; ++i) P[i] = dpp_u<CTRL>(L[i]); \
+  merge_top<KP>(L, P);
+  TOPK_DPP_LEVEL(kDppXor1)
+  TOPK_DPP_LEVEL(kDppXor2)
+  TOPK_DPP_LEVEL(kDppHalfMirror)
+  TOPK_DPP_LEVEL(kDppMirror)
+#undef TOPK_DPP_LEVEL
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) key[i] = key[i] == M ? 0u : key[i];
-    if (lane == r) my_e = (int)(imask - (M & imask));
+  for (int i = 0; i < KP; ++i) {
+    const u32x2_t p = swap16(L[i]);
+    L[i] = p.x, P[i] = p.y;
   }
-  sel_e = my_e;
+  merge_top<KP>(L, P);
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const u32x2_t p = swap32(L[i]);
+    L[i] = p.x, P[i] = p.y;
+  }
+  merge_top<KP>(L, P);
+  // every lane: L = the KP largest keys, descending
+  uint32_t mine = 0, kth = 0, next = 0;
+  bool close = false;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    mine = lane == i ? L[i] : mine;
+    kth = i == k - 1 ? L[i] : kth;
+    next = i == k ? L[i] : next;
+    if (i >= 1) close = close || (i < k && ((L[i - 1] ^ L[i]) & ~imask) == 0u);
+  }
+  if (k == KP && k < E) {  // the best unchosen key is not in the lists
+    uint32_t rest = 0;
+#pragma unroll
+    for (int i = 0; i < N0; ++i) rest = max(rest, a0[i] < kth ? a0[i] : 0u);
+    next = wave_max_u32(rest);
+  }
+  close = close || (k < E && ((kth ^ next) & ~imask) == 0u);
+  sel_e = lane < k ? (int)(imask - (mine & imask)) : 0;
   return !close;
 }
 
-// Faster selection with the same result as topk_exact (see above).
-template <int EPL>
+// Faster selection with the same result as topk_exact (see above); k <= KP.
+template <int EPL, int KP>
 __device__ __forceinline__ void topk_fast(const float v[EPL], int E, int k, int norm, int lane, int& sel_e,
                                           float& sel_w) {
-  if (!topk_select_fast<EPL>(v, E, k, lane, sel_e)) {
+  if (!topk_select_merge<EPL, KP>(v, E, k, lane, sel_e)) {
     topk_exact<EPL>(v, E, k, norm, lane, sel_e, sel_w);
     return;
   }

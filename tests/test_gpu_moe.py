@@ -124,6 +124,28 @@ def test_flagship_tied_router_logits_pick_lower_expert():
     assert err <= 2e-3 * np.abs(out["y"][0]).max()
 
 
+@pytest.mark.parametrize("one_by_one", [True, False], ids=["single-launch", "batched"])
+def test_flagship_near_tied_router_logits_keep_their_order(one_by_one):
+    """Rows 3 and 200 dominant and equal but for one element of row 200,
+    larger by 1e-4: the two logits agree in their leading bits (the part the
+    selection keys keep) and row 200 must come first, by value."""
+    cfg = synth.LAYER
+    lay = synth.make_layer(cfg, 4)
+    lay["router_w"] = lay["router_w"].copy()
+    lay["router_w"][3] = lay["router_w"][200] = np.float32(0.05)
+    lay["router_w"][200, 0] = np.float32(0.05 + 1e-4)
+    OL = OM.Layer.from_dict(lay)
+    X = np.full((2, cfg.d), 0x3F80, np.uint16)
+    out = OM.moe_forward_tokens(OL, X, cfg.k)
+    assert OM.topk_margin(out["logits"][0], cfg.k) > 1e-3
+    assert out["idx"][0][0] == 200 and out["idx"][0][1] == 3
+    _, y, idx, w = run_layer(lay, cfg, X, one_by_one=one_by_one)
+    for t in range(2):
+        assert idx[t][0] == 200 and idx[t][1] == 3, idx[t]
+        assert w[t][0] > w[t][1]
+        compare_layer({k: v[t:t + 1] for k, v in out.items()}, idx[t:t + 1], w[t:t + 1], y[t:t + 1], f"token {t}")
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_flagship_layer_parity(seed):
     """d=2048, f=512, E=256, top-8: every output of 3 tokens against the oracle."""
