@@ -97,7 +97,8 @@ typedef struct moe_layer* moe_handle;
  * shape).  The workspace holds router logits, the chosen experts, their
  * grouping by expert, the operand copies of the activations, the SwiGLU
  * activations and the per-assignment expert outputs of one call (for
- * max_tokens T: about T*k*(4d + 2f) + 6Td bytes, plus 64 KiB) and, for a
+ * max_tokens T: about T*k*(4d + 2f) + 6Td bytes, plus 32*E + 10*k*f bytes of
+ * single-launch hand-off words and 6 KiB) and, for a
  * layer that may run the batched kernels (max_tokens > 1, or a shape the
  * single-launch kernel does not take), a tile-major copy of the gate, up and
  * down matrices (their size: 3*E*d*f/2 bytes of codes + 3*E*d*f/16 of
