@@ -163,16 +163,22 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
 // magnitude into [2^14, 2^15) (bf16 values are then exact in fp16 down to
 // 2^-24 of the row maximum); the argmax of a row is unchanged by that
 // factor and its maximum logit is scaled back at the end.
-// The 4 waves of a workgroup split K into quarters; each keeps its quarter
+// One workgroup of 8 waves per compute unit: two groups of 4 waves, each
+// group on its own sequence of tiles, the 4 waves of a group splitting K
+// into quarters.  (Two 4-wave workgroups per compute unit would share it
+// unevenly -- the older one's waves win arbitration and finish first, the
+// other then runs alone at half the memory parallelism; the groups here
+// step together, one barrier per tile pair.)  Each wave keeps its quarter
 // of x as fragments in registers (elements in the order 0,4,1,5,2,6,3,7 of
 // every 8, the order the magic-number extraction yields) and streams 16-row
 // tiles of W with loads that are contiguous along each row (256 bytes of a
-// row per quarter for d = 2048), two tiles ahead; a small wave-private LDS
-// block, XOR-swizzled so that its stores and its fragment reads are free of
-// bank conflicts, turns them into MFMA lane order.  The 4 quarter sums meet
-// in LDS, one barrier per tile; wave 0 keeps the running (value, row)
-// maximum per x row, and the workgroup results are reduced as in the VALU
-// path.
+// row per quarter for d = 2048), two tiles ahead, the first two issued
+// before x is read; a small wave-private LDS block, XOR-swizzled so that
+// its stores and its fragment reads are free of bank conflicts, turns them
+// into MFMA lane order.  The quarter sums meet in LDS; the first wave of
+// each group keeps the running (value, row) maximum per x row.  Workgroup
+// keys are stored row-major and the last workgroup to arrive reduces them
+// with all its threads, every load issued before any is waited for.
 typedef _Float16 lm_f16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_f32x4 __attribute__((ext_vector_type(4)));
 
@@ -201,7 +207,7 @@ __device__ __forceinline__ lm_f16x8 lm_codes(uint32_t w, uint32_t magic) {
 __device__ __forceinline__ uint32_t lm_dword(uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restrict__ wq,
+__global__ __launch_bounds__(512, 1) void k_lmhead_mfma(const uint8_t* __restrict__ wq,
                                                         const uint16_t* __restrict__ ws, int V,
                                                         const uint16_t* __restrict__ x, int B,
                                                         unsigned long long* __restrict__ partial,
@@ -214,49 +220,18 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
   constexpr int NI = 16 / RPI;       // load instructions per 16-row tile
   constexpr int SH = 16 / PPR > 1 ? (16 / PPR == 2 ? 1 : 2) : 0;  // log2(16 / PPR)
   static_assert(NBQ >= 1 && PPR <= 64 && 64 % PPR == 0, "d = 512, 1024 or 2048");
-  __shared__ uint4 s_w[4][16 * PPR];
-  __shared__ uint2 s_s[4][16 * NBQ];
-  __shared__ lm_f32x4 s_acc[2][4][64];
-  __shared__ unsigned long long s_key[16];
-  __shared__ uint32_t s_xm[4][16];
+  __shared__ uint4 s_w[8][16 * PPR];
+  __shared__ uint2 s_s[8][16 * NBQ];
+  __shared__ lm_f32x4 s_acc[2][8][64];
+  __shared__ unsigned long long s_key[2][16];
+  __shared__ uint4 s_x[16 * (D / 8 + 1)];
+  __shared__ uint32_t s_xm2[16];
   __shared__ bool s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  const int grp = wave >> 2, kq = wave & 3;  // tile group, K quarter
   const uint32_t magic = lm_magic();
   const int ntiles = (V + 15) >> 4;
-
-  // this wave's quarter of x: row r16 (< B), block b, group j, chunk q
-  uint4 xr[NBQ][4];
-  uint32_t xm = 0;  // largest |x| as a bf16 magnitude pattern (ordered like the values)
-#pragma unroll
-  for (int b = 0; b < NBQ; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k0 = wave * KQ + 128 * b + 32 * j + 8 * q;
-      xr[b][j] = r16 < B ? *reinterpret_cast<const uint4*>(x + (size_t)r16 * D + k0) : make_uint4(0, 0, 0, 0);
-      const uint32_t c[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xm = max(xm, max(c[e] & 0x7FFFu, (c[e] >> 16) & 0x7FFFu));
-    }
-  xm = max(xm, (uint32_t)__shfl_xor((int)xm, 16, 64));
-  xm = max(xm, (uint32_t)__shfl_xor((int)xm, 32, 64));
-  if (lane < 16) s_xm[wave][lane] = xm;
-  __syncthreads();
-  xm = max(max(s_xm[0][r16], s_xm[1][r16]), max(s_xm[2][r16], s_xm[3][r16]));
-  // row r16 is multiplied by 2^-sh, sh = (exponent of its maximum) - 14
-  const int sh = max((int)(xm >> 7) - 141, -126);
-  const float fx = __uint_as_float((uint32_t)(127 - sh) << 23);
-  uint4 xf[NBQ][4];
-#pragma unroll
-  for (int b = 0; b < NBQ; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 v = xr[b][j];
-      const float e0 = bf16_bits_to_f32(v.x & 0xFFFFu) * fx, e1 = __uint_as_float(v.x & 0xFFFF0000u) * fx;
-      const float e2 = bf16_bits_to_f32(v.y & 0xFFFFu) * fx, e3 = __uint_as_float(v.y & 0xFFFF0000u) * fx;
-      const float e4 = bf16_bits_to_f32(v.z & 0xFFFFu) * fx, e5 = __uint_as_float(v.z & 0xFFFF0000u) * fx;
-      const float e6 = bf16_bits_to_f32(v.w & 0xFFFFu) * fx, e7 = __uint_as_float(v.w & 0xFFFF0000u) * fx;
-      xf[b][j] = make_uint4(pack_f16(e0, e4), pack_f16(e1, e5), pack_f16(e2, e6), pack_f16(e3, e7));
-    }
+  const int G2 = 2 * (int)gridDim.x;  // tiles of group grp: 2 * blockIdx + grp + n * G2
 
   // weight loads of one tile: instruction i, lane l -> row RPI*i + l/PPR of the tile, piece l%PPR
   struct TileRegs {
@@ -268,29 +243,88 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = min(16 * tt + RPI * i + lane / PPR, V - 1);
-      r.w[i] = *reinterpret_cast<const uint4*>(wq + (size_t)row * (D / 2) + wave * (KQ / 2) + 16 * (lane % PPR));
+      r.w[i] = *reinterpret_cast<const uint4*>(wq + (size_t)row * (D / 2) + kq * (KQ / 2) + 16 * (lane % PPR));
     }
     const int srow = min(16 * tt + min(lane / NBQ, 15), V - 1);
-    r.s = *reinterpret_cast<const uint2*>(ws + (size_t)srow * (D / 32) + wave * (KQ / 32) + 4 * (lane % NBQ));
+    r.s = *reinterpret_cast<const uint2*>(ws + (size_t)srow * (D / 32) + kq * (KQ / 32) + 4 * (lane % NBQ));
     return r;
   };
-  int t = blockIdx.x;
+  // x, staged once per workgroup: the 512 threads copy the B rows into LDS
+  // (16 bytes each per pass; a row padded by 16 bytes so that the 16 rows
+  // one fragment read touches fall in different banks) and take each row's
+  // largest magnitude with LDS atomics
+  constexpr int XC = D / 8;            // 16-byte chunks per row
+  constexpr int XP = 16 * XC / 512;    // passes for 16 rows
+  static_assert(XC % 64 == 0, "a wave's chunks of one pass in one row");
+  if (tid < 16) s_xm2[tid] = 0u;
+  uint4 xv[XP];
+  // pass m reads chunk block (m + rot) % XP: the workgroups of one XCD
+  // (every 8th) start on different blocks, so that 32 compute units do not
+  // all miss on the same lines at once
+  const int rot = (int)(blockIdx.x >> 3) % XP;
+#pragma unroll
+  for (int m = 0; m < XP; ++m) {
+    const int mb = m + rot < XP ? m + rot : m + rot - XP;
+    const int c = min(tid + 512 * mb, B * XC - 1);  // past the B rows: reread the last chunk, not stored
+    xv[m] = *reinterpret_cast<const uint4*>(x + (size_t)c * 8);
+  }
+  __syncthreads();  // s_xm2 cleared
+#pragma unroll
+  for (int m = 0; m < XP; ++m) {
+    // a wave's 64 chunks lie in one row (64 divides XC): one LDS atomic per wave
+    const int mb = m + rot < XP ? m + rot : m + rot - XP;
+    const int c = tid + 512 * mb, row = c / XC;
+    uint32_t mm = 0;
+    if (c < B * XC) {
+      s_x[row * (XC + 1) + c % XC] = xv[m];
+      const uint32_t cw[4] = {xv[m].x, xv[m].y, xv[m].z, xv[m].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mm = max(mm, max(cw[e] & 0x7FFFu, (cw[e] >> 16) & 0x7FFFu));
+    }
+    mm = wave_max_u32(mm);  // largest |x| of the row as a bf16 magnitude pattern (ordered like the values)
+    if (lane == 0 && row < B) atomicMax(&s_xm2[row], mm);
+  }
+  __syncthreads();
+  const uint32_t xm = r16 < B ? s_xm2[r16] : 0u;
+  // row r16 is multiplied by 2^-sh, sh = (exponent of its maximum) - 14
+  const int sh = max((int)(xm >> 7) - 141, -126);
+  const float fx = __uint_as_float((uint32_t)(127 - sh) << 23);
+  // this wave's quarter of x as fp16 fragments: row r16 (zero past B), block b, group j, chunk q
+  uint4 xf[NBQ][4];
+#pragma unroll
+  for (int b = 0; b < NBQ; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = kq * KQ + 128 * b + 32 * j + 8 * q;
+      uint4 v = s_x[min(r16, 15) * (XC + 1) + k0 / 8];
+      if (r16 >= B) v = make_uint4(0, 0, 0, 0);
+      const float e0 = bf16_bits_to_f32(v.x & 0xFFFFu) * fx, e1 = __uint_as_float(v.x & 0xFFFF0000u) * fx;
+      const float e2 = bf16_bits_to_f32(v.y & 0xFFFFu) * fx, e3 = __uint_as_float(v.y & 0xFFFF0000u) * fx;
+      const float e4 = bf16_bits_to_f32(v.z & 0xFFFFu) * fx, e5 = __uint_as_float(v.z & 0xFFFF0000u) * fx;
+      const float e6 = bf16_bits_to_f32(v.w & 0xFFFFu) * fx, e7 = __uint_as_float(v.w & 0xFFFF0000u) * fx;
+      xf[b][j] = make_uint4(pack_f16(e0, e4), pack_f16(e1, e5), pack_f16(e2, e6), pack_f16(e3, e7));
+    }
+
+  // only now the first two tiles: a compute unit's memory pipeline takes
+  // requests in order, and the tiles' requests (20 MB across the chip)
+  // would hold up the issue of everything behind them for microseconds.
+  // Tile t's loads issue before tile t + G2's, the order the loop consumes
+  // them in, so the waits before each step leave the later tile in flight.
+  int t = 2 * (int)blockIdx.x + grp;
   TileRegs tr0 = load_tile(min(t, ntiles - 1));
-  // tile t's loads issue before tile t + G's, the order the loop consumes
-  // them in, so the waits before each step leave the later tile in flight
   __builtin_amdgcn_sched_barrier(0);
-  TileRegs tr1 = load_tile(min(t + (int)gridDim.x, ntiles - 1));
+  TileRegs tr1 = load_tile(min(t + G2, ntiles - 1));
 
   float best[4];
   uint32_t brow[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) best[v] = -INFINITY, brow[v] = 0xFFFFFFFFu;
 
-  // one tile per step: its weights (TR = tr0 or tr1) through the wave's LDS
-  // block into MFMAs, then the next-but-one tile's loads into the same
-  // registers; PAR also selects the accumulator buffer, so one barrier per
-  // tile suffices.  The two steps are written out so that each register set
-  // stays in place and the next tile's loads stay in flight.
+  // one tile per group and step: its weights (TR = tr0 or tr1) through the
+  // wave's LDS block into MFMAs, then the next-but-one tile's loads into the
+  // same registers; PAR also selects the accumulator buffer, so one barrier
+  // per step suffices.  The two steps are written out so that each register
+  // set stays in place and the next tile's loads stay in flight.
 #define LM_MFMA_STEP(TR, PAR)                                                                                   \
   {                                                                                                            \
     _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                                           \
@@ -301,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
     /* other lanes of this wave read these slots: keep the compiler from moving   */                          \
     /* the reads above the stores (the wave's LDS operations run in order)        */                          \
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");                                                     \
-    TR = load_tile(min(t + 2 * (int)gridDim.x, ntiles - 1));                                                   \
+    TR = load_tile(min(t + 2 * G2, ntiles - 1));                                                               \
     lm_f32x4 acc = {0.f, 0.f, 0.f, 0.f};                                                                       \
     _Pragma("unroll") for (int b = 0; b < NBQ; ++b) {                                                          \
       const int p = 4 * b + q;                                                                                 \
@@ -317,27 +351,28 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
     }                                                                                                          \
     s_acc[PAR][wave][lane] = acc;                                                                              \
     __syncthreads();                                                                                           \
-    if (wave == 0) {                                                                                           \
+    if (kq == 0) {                                                                                             \
       /* lane: vocabulary row 16t + r16, x rows 4q + v */                                                      \
-      const lm_f32x4 z =                                                                                       \
-          (s_acc[PAR][0][lane] + s_acc[PAR][1][lane]) + (s_acc[PAR][2][lane] + s_acc[PAR][3][lane]);           \
+      const lm_f32x4 z = (s_acc[PAR][4 * grp][lane] + s_acc[PAR][4 * grp + 1][lane]) +                         \
+                         (s_acc[PAR][4 * grp + 2][lane] + s_acc[PAR][4 * grp + 3][lane]);                      \
       const uint32_t row = 16u * t + r16;                                                                      \
       _Pragma("unroll") for (int v = 0; v < 4; ++v) if (row < (uint32_t)V && z[v] > best[v]) best[v] = z[v],   \
           brow[v] = row;                                                                                       \
     }                                                                                                          \
-    t += gridDim.x;                                                                                            \
+    t += G2;                                                                                                   \
   }
-  // steps in pairs (a step past the last tile reads a clamped tile and
-  // updates nothing), so that the loop has a single exit
-  const int nsteps = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // steps in pairs, as many as group 0 has tiles (group 1 has as many or one
+  // fewer): a step past a group's last tile reads a clamped tile and updates
+  // nothing; a single loop exit keeps the waits precise
+  const int nsteps = (ntiles - 2 * (int)blockIdx.x + G2 - 1) / G2;
   for (int n = 0; n < nsteps; n += 2) {
     LM_MFMA_STEP(tr0, 0)
     LM_MFMA_STEP(tr1, 1)
   }
 #undef LM_MFMA_STEP
 
-  // per x row: maximum over the 16 lanes of its group (rows in increasing order per lane)
-  if (wave == 0) {
+  // per group and x row: maximum over the 16 lanes of its group (rows in increasing order per lane)
+  if (kq == 0) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       unsigned long long key = brow[v] == 0xFFFFFFFFu ? 0ull : make_key(best[v], brow[v]);
@@ -346,35 +381,44 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_mfma(const uint8_t* __restric
         const unsigned long long other = __shfl_xor(key, o, 64);
         key = other > key ? other : key;
       }
-      if (r16 == 0) s_key[4 * q + v] = key;
+      if (r16 == 0) s_key[grp][4 * q + v] = key;
     }
   }
   __syncthreads();
+  const int G = gridDim.x;
   if (tid < B) {
-    store_coherent(partial + (size_t)blockIdx.x * 16 + tid, s_key[tid]);
+    const unsigned long long k0 = s_key[0][tid], k1 = s_key[1][tid];
+    store_coherent(partial + (size_t)tid * G + blockIdx.x, k0 > k1 ? k0 : k1);  // row-major [B][G]
     wait_vm();
   }
   __syncthreads();
   if (tid == 0) s_last = arrive(counter) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  // last workgroup: one wave per x row reduces the workgroup keys
-  for (int b = wave; b < B; b += 4) {
+  // last workgroup: 32 threads per x row, each loading its keys at once
+  {
+    const int b = tid >> 5, l32 = tid & 31;
     unsigned long long kmax = 0;
-    for (int g = lane; g < (int)gridDim.x; g += 64) {
-      const unsigned long long kv = load_coherent(partial + (size_t)g * 16 + b);
-      kmax = kv > kmax ? kv : kmax;
+    if (b < B) {
+      constexpr int KL = 16;  // keys per thread, G <= 512
+      unsigned long long kv[KL];
+#pragma unroll
+      for (int m = 0; m < KL; ++m) {
+        const int g = l32 + 32 * m;
+        kv[m] = g < G ? load_coherent(partial + (size_t)b * G + g) : 0ull;
+      }
+#pragma unroll
+      for (int m = 0; m < KL; ++m) kmax = kv[m] > kmax ? kv[m] : kmax;
     }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
+    for (int o = 1; o < 32; o <<= 1) {
       const unsigned long long other = __shfl_xor(kmax, o, 64);
       kmax = other > kmax ? other : kmax;
     }
-    if (lane == 0) {
+    if (b < B && l32 == 0) {
       token[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(kmax & 0xFFFFFFFFull));
       if (max_logit) {
-        const uint32_t m = max(max(s_xm[0][b], s_xm[1][b]), max(s_xm[2][b], s_xm[3][b]));
-        max_logit[b] = ldexpf(unordered_bits((uint32_t)(kmax >> 32)), max((int)(m >> 7) - 141, -126));
+        max_logit[b] = ldexpf(unordered_bits((uint32_t)(kmax >> 32)), max((int)(s_xm2[b] >> 7) - 141, -126));
       }
     }
   }
@@ -432,9 +476,10 @@ static hipError_t lm_mfma(const uint8_t* wq, const uint16_t* ws, int V, const ui
   unsigned* counter = reinterpret_cast<unsigned*>(wsp);
   unsigned long long* partial = reinterpret_cast<unsigned long long*>(wsp + 256);
   const int ntiles = (V + 15) / 16;
-  int grid = 2 * (lm_grid() / 4);  // two workgroups per compute unit
-  if (grid > ntiles) grid = ntiles;
-  hipLaunchKernelGGL((k_lmhead_mfma<D>), dim3(grid), dim3(256), 0, s, wq, ws, V, x, B, partial, counter, token,
+  int grid = lm_grid() / 4;  // one 8-wave workgroup per compute unit, at most kLmMaxGrid / 8
+  if (grid > kLmMaxGrid / 8) grid = kLmMaxGrid / 8;
+  if (grid > (ntiles + 1) / 2) grid = (ntiles + 1) / 2;
+  hipLaunchKernelGGL((k_lmhead_mfma<D>), dim3(grid), dim3(512), 0, s, wq, ws, V, x, B, partial, counter, token,
                      max_logit);
   return hipGetLastError();
 }
