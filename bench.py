@@ -193,7 +193,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=16, help="distinct activations per layer")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-extras", action="store_true", help="skip stack, LM head and CPU legs")
+    ap.add_argument("--no-extras", action="store_true", help="skip stack, batch, LM head and CPU legs")
+    ap.add_argument("--extras", default="stack,batch,lmhead,cpu",
+                    help="comma list of the legs run after the headline (stack, batch, lmhead, cpu)")
     ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (reference for HBM byte counters)")
@@ -307,7 +309,8 @@ def main():
         "graph_ms_per_step": round(graph_s / K * 1e3, 6) if graph_s else None,
     }
 
-    if not args.no_extras:
+    extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    if "stack" in extras:
         # 49-layer stack, 1 token: per-token time (in-stack layer time = / P)
         # r_0 = fp32 of a bf16 N(0,1) activation, as in the stack's definition
         x0 = synth.draw_x(synth.STACK, args.seed, 0, 0, 0)
@@ -331,6 +334,7 @@ def main():
                         "in_stack_layer_us": round(st_s / P * 1e6, 3),
                         "achieved_gbs": round(P * by["b_alg"] / st_s / 1e9, 1)}
 
+    if "batch" in extras:
         # batch: 64 tokens per call through one layer, Zipf(1.1) router bias
         TB = synth.BATCH.T
         bias = torch.from_numpy(synth.zipf_bias(synth.BATCH, args.seed)).to(dev)
@@ -367,6 +371,7 @@ def main():
             L.close()
         del blayers, XB
 
+    if "lmhead" in extras:
         # LM head: rotate over 4 copies
         V = synth.LMHEAD1.V
         heads = []
@@ -399,6 +404,7 @@ def main():
                                    "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
         del heads
 
+    if "cpu" in extras:
         out["cpu_baseline"] = cpu_baseline(pool_np, xs_np, cfg, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)

@@ -52,10 +52,11 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
       const int base = 128 * (cc >> 2) + 8 * (cc & 3);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (b < B)
-          xs[b][s][j] = make_slice_bf16(reinterpret_cast<const uint4*>(x + (size_t)b * D)[(base + 32 * j) >> 3]);
-        else
-          xs[b][s][j] = Slice8{0u, 0u, 0u, 0u, 0.f};
+        // rows past B read row B-1 and are zeroed once loaded (a load in
+        // one arm of a branch makes the other arm's write of its registers
+        // wait for it: the loads would run one at a time)
+        const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)min(b, B - 1) * D)[(base + 32 * j) >> 3];
+        xs[b][s][j] = make_slice_bf16(b < B ? v : make_uint4(0u, 0u, 0u, 0u));
       }
     }
 
@@ -123,13 +124,19 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   if (threadIdx.x == 0) s_last = arrive(counter) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  // last workgroup: reduce G keys per x row
+  // last workgroup: reduce G keys per x row, every load issued before any
+  // is waited for
   for (int b = 0; b < B; ++b) {
-    unsigned long long kmax = 0;
-    for (int g = threadIdx.x; g < (int)gridDim.x; g += 256) {
-      const unsigned long long kv = load_coherent(partial + (size_t)g * BP + b);
-      kmax = kv > kmax ? kv : kmax;
+    constexpr int KL = kLmMaxGrid / 256;
+    unsigned long long kv[KL];
+#pragma unroll
+    for (int m = 0; m < KL; ++m) {
+      const int g = min(threadIdx.x + 256 * m, gridDim.x - 1);  // repeats past G: harmless for a maximum
+      kv[m] = load_coherent(partial + (size_t)g * BP + b);
     }
+    unsigned long long kmax = 0;
+#pragma unroll
+    for (int m = 0; m < KL; ++m) kmax = kv[m] > kmax ? kv[m] : kmax;
     // 64-bit max over the workgroup through LDS
     __shared__ unsigned long long s_red[256];
     s_red[threadIdx.x] = kmax;
@@ -404,8 +411,8 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_mfma(const uint8_t* __restric
       unsigned long long kv[KL];
 #pragma unroll
       for (int m = 0; m < KL; ++m) {
-        const int g = l32 + 32 * m;
-        kv[m] = g < G ? load_coherent(partial + (size_t)b * G + g) : 0ull;
+        const int g = min(l32 + 32 * m, G - 1);  // repeats past G: harmless for a maximum
+        kv[m] = load_coherent(partial + (size_t)b * G + g);
       }
 #pragma unroll
       for (int m = 0; m < KL; ++m) kmax = kv[m] > kmax ? kv[m] : kmax;
