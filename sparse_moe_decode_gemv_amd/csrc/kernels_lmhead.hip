@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   if (threadIdx.x == 0) *counter = 0u;
 }
 
-// ---------------------------------------------------------------- MFMA path (3 <= B <= 16)
+// ---------------------------------------------------------------- MFMA path (2 <= B <= 16)
 //
 // Logits of 16 vocabulary rows x up to 16 x rows per group of 32 elements
 // with one v_mfma_f32_16x16x32_f16 (A = x rows, zero past B; B operand = 16
@@ -494,7 +494,7 @@ static hipError_t lm_mfma(const uint8_t* wq, const uint16_t* ws, int V, const ui
 hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,
                          int32_t* token, float* max_logit, void* workspace, hipStream_t s) {
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
-  if (B >= 3 && B <= 16) {  // MFMA tiles (one 16-row x tile) for the shapes they are built for
+  if (B >= 2 && B <= 16) {  // MFMA tiles (one 16-row x tile) for the shapes they are built for
     if (d == 512) return lm_mfma<512>(wq, ws, V, x, B, wsp, token, max_logit, s);
     if (d == 1024) return lm_mfma<1024>(wq, ws, V, x, B, wsp, token, max_logit, s);
     if (d == 2048) return lm_mfma<2048>(wq, ws, V, x, B, wsp, token, max_logit, s);

@@ -71,7 +71,7 @@ def test_extreme_magnitudes_of_x(d, B):
     assert np.array_equal(tok[2:4], tok[0:2]) and np.array_equal(tok[4:6], tok[0:2][: len(tok) - 4])
 
 
-@pytest.mark.parametrize("d,B", [(2048, 4), (2048, 2), (512, 9)], ids=["mfma", "valu", "mfma-d512"])
+@pytest.mark.parametrize("d,B", [(2048, 4), (2048, 2), (512, 9), (4096, 2)], ids=["mfma", "mfma-b2", "mfma-d512", "valu"])
 def test_equal_rows_far_apart_lowest_index_wins(d, B):
     """The winning row of each x copied to rows in other tiles and
     workgroups, one of them below it: every copy ties bit for bit and the
@@ -93,7 +93,8 @@ def test_equal_rows_far_apart_lowest_index_wins(d, B):
 
 
 @pytest.mark.parametrize("V,d,B", [(1000, 256, 1), (4099, 512, 3), (20000, 2048, 8), (3000, 4096, 2),
-                                   (777, 2048, 16), (6007, 1024, 7), (33, 2048, 3), (50001, 1024, 12)])
+                                   (777, 2048, 16), (6007, 1024, 7), (33, 2048, 3), (50001, 1024, 12),
+                                   (9001, 1024, 2), (300, 512, 2)])
 def test_small_heads_ragged_rows(V, d, B):
     q, s = synth.int4_matrix(V, d, synth.key(21, "lm-small", V, d), 0.02)
     X, _ = pick_hidden_rows(q, s, 1e-2, lambda b, a: synth.bf16(d, synth.key(21, "h", V, d, b, a)), B)
