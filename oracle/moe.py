@@ -16,7 +16,12 @@ follows (each reading is also listed in the design notes):
 * expert: SwiGLU, h = silu(W_g x) * (W_u x) with silu(z) = z / (1 + e^-z),
   then o = W_d h, all on dequantized int4 weights in fp64;
 * combine: y = sum over chosen experts of w_j o_j, added in ascending expert
-  index, rounded once to fp32 for comparison.
+  index, rounded once to fp32 for comparison;
+* shared expert (the pages' layer adds one always-on expert to the routed
+  ones, "Flint 40B: Best Mid Sized LLM", transcript 02:35): when a layer has
+  one, its output o_s, same SwiGLU form and shape, is added with weight 1
+  after the routed sum (it takes no part in the softmax or the
+  renormalization).
 
 Functions take host numpy arrays in the stored formats (see formats.py) and
 never share code with the GPU path.
@@ -43,12 +48,16 @@ class Layer:
     up_s: np.ndarray
     down_q: np.ndarray              # uint8 [E][d][f/2]
     down_s: np.ndarray              # uint16 [E][d][f/32]
+    shared: tuple | None = None     # (gate_q, gate_s, up_q, up_s, down_q, down_s) of the shared expert, or None
     weights_read: int = field(default=0)
 
     @classmethod
     def from_dict(cls, t: dict) -> "Layer":
+        sh = None
+        if t.get("shared_gate_q") is not None:
+            sh = tuple(t["shared_" + n] for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"))
         return cls(t["router_w"], t.get("router_b"), t["gate_q"], t["gate_s"], t["up_q"], t["up_s"],
-                   t["down_q"], t["down_s"])
+                   t["down_q"], t["down_s"], sh)
 
     @property
     def E(self) -> int:
@@ -68,6 +77,13 @@ class Layer:
         Wg = dequant(self.gate_q[e], self.gate_s[e], d)
         Wu = dequant(self.up_q[e], self.up_s[e], d)
         Wd = dequant(self.down_q[e], self.down_s[e], f)
+        self.weights_read += Wg.size + Wu.size + Wd.size
+        return Wg, Wu, Wd
+
+    def shared_expert(self):
+        """Dequantized (W_g, W_u, W_d) of the shared expert, counted as read."""
+        gq, gs, uq, us, dq, ds = self.shared
+        Wg, Wu, Wd = dequant(gq, gs, self.d), dequant(uq, us, self.d), dequant(dq, ds, self.f)
         self.weights_read += Wg.size + Wu.size + Wd.size
         return Wg, Wu, Wd
 
@@ -122,6 +138,13 @@ def combine(S: np.ndarray, w: np.ndarray, outs: dict) -> np.ndarray:
     return y
 
 
+def add_shared(layer: Layer, y: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y + o_s, the shared expert's output with weight 1 (y unchanged without one)."""
+    if layer.shared is None:
+        return y
+    return y + expert_forward(*layer.shared_expert(), x)
+
+
 def topk_margin(l: np.ndarray, k: int) -> float:
     """Gap between the k-th and (k+1)-th largest logit (inf when k == E)."""
     s = np.sort(l)[::-1]
@@ -137,7 +160,7 @@ def moe_forward(layer: Layer, x_bits: np.ndarray, k: int, norm_topk: bool = True
     l = router_logits(layer, x)
     S, w = route(l, k, norm_topk)
     outs = {int(e): expert_forward(*layer.expert(int(e)), x) for e in S}
-    y = combine(S, w, outs)
+    y = add_shared(layer, combine(S, w, outs), x)
     return dict(y=y, y32=f64_to_f32(y), idx=S, w=w, logits=l)
 
 
@@ -152,7 +175,7 @@ def moe_forward_on_set(layer: Layer, x_bits: np.ndarray, S, norm_topk: bool = Tr
     S = np.asarray(S, dtype=np.int64)
     w = p[S] / p[S].sum() if norm_topk else p[S]
     outs = {int(e): expert_forward(*layer.expert(int(e)), x) for e in S}
-    y = combine(S, w, outs)
+    y = add_shared(layer, combine(S, w, outs), x)
     return dict(y=y, y32=f64_to_f32(y), idx=S, w=w, logits=l)
 
 
@@ -176,6 +199,8 @@ def moe_forward_masked(layer: Layer, x_bits: np.ndarray, k: int, norm_topk: bool
     for e in range(layer.E):
         o = expert_forward(*layer.expert(e), x)
         y = y + mw[e] * o
+    if layer.shared is not None:  # mask 1 for the always-on expert
+        y = y + 1.0 * expert_forward(*layer.shared_expert(), x)
     return y
 
 
@@ -197,7 +222,13 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     U = np.einsum("efd,d->ef", Wu, x)
     H = G / (1.0 + np.exp(-G)) * U
     O = np.einsum("edf,ef->ed", Wd, H)
-    return np.einsum("e,ed->d", wv, O)
+    y = np.einsum("e,ed->d", wv, O)
+    if layer.shared is not None:
+        gq, gs, uq, us, dq, ds = layer.shared
+        Ws = [dequant(gq, gs, layer.d), dequant(uq, us, layer.d), dequant(dq, ds, layer.f)]
+        gs_, us_ = np.einsum("fd,d->f", Ws[0], x), np.einsum("fd,d->f", Ws[1], x)
+        y = y + np.einsum("df,f->d", Ws[2], gs_ / (1.0 + np.exp(-gs_)) * us_)
+    return y
 
 
 def group_by_expert(idx: np.ndarray, E: int):
@@ -225,9 +256,10 @@ def best_subset_bruteforce(l: np.ndarray, k: int):
     return np.array(best)
 
 
-def active_weights(E: int, d: int, f: int, k: int) -> int:
-    """Weights a sparse token reads: the router (E*d) and k experts (3*d*f each)."""
-    return E * d + k * 3 * d * f
+def active_weights(E: int, d: int, f: int, k: int, shared: int = 0) -> int:
+    """Weights a sparse token reads: the router (E*d) and k routed plus the
+    shared experts (3*d*f each)."""
+    return E * d + (k + shared) * 3 * d * f
 
 
 # ------------------------------------------------------------------ stack

@@ -170,6 +170,7 @@ class MoEConfig:
     zipf_s: float = 0.0      # >0: router bias b_e = ln p_e, p_e ~ rank^-s
     layers: int = 1
     margin: float = 1e-2
+    shared: int = 0          # always-on experts (0 or 1), same shape, weight 1
 
 
 @dataclass(frozen=True)
@@ -186,6 +187,10 @@ TINY = MoEConfig("tiny", d=256, f=128, E=16, k=2, router_sigma=0.05)
 LAYER = MoEConfig("layer", d=2048, f=512, E=256, k=8)
 BATCH = replace(LAYER, name="batch", T=64, zipf_s=1.1)
 STACK = replace(LAYER, name="stack", layers=49)
+# the pages' own routing: top-6 of the 256 routed experts plus one shared expert
+FLINT = replace(LAYER, name="flint", k=6, shared=1)
+FLINT_BATCH = replace(FLINT, name="flint_batch", T=64, zipf_s=1.1)
+TINY_SHARED = replace(TINY, shared=1)
 LMHEAD1 = LMHeadConfig("lmhead", V=131072, d=2048, B=1)
 LMHEAD8 = replace(LMHEAD1, B=8)
 
@@ -209,7 +214,13 @@ def make_layer(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
     uq, us = int4_experts(E, f, d, key(*base, "up"), cfg.expert_sigma)
     dq, ds = int4_experts(E, d, f, key(*base, "down"), cfg.expert_sigma)
     rb = zipf_bias(cfg, seed) if cfg.zipf_s > 0 else None
-    return dict(router_w=rw, router_b=rb, gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+    out = dict(router_w=rw, router_b=rb, gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+    if cfg.shared:
+        # the shared expert: streams of its own, the routed experts' distribution
+        for name, rows, K in (("gate", f, d), ("up", f, d), ("down", d, f)):
+            q, sc = int4_experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
+            out["shared_" + name + "_q"], out["shared_" + name + "_s"] = q[0], sc[0]
+    return out
 
 
 def draw_x(cfg: MoEConfig, seed: int, layer: int, token: int, attempt: int) -> np.ndarray:

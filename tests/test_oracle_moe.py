@@ -248,3 +248,72 @@ def test_group_by_expert_hand_example_and_invariants():
         seg = order[off[e]:off[e + 1]]
         assert np.all(idx.ravel()[seg] == e) and np.all(np.diff(seg) > 0)
     assert active.tolist() == [e for e in range(40) if off[e + 1] > off[e]]
+
+
+# ------------------------------------------------------------------ shared expert
+
+
+def _shared_alone_layer():
+    """Routed experts that read as exact zeros (code 8, scale 1) and the
+    hand-worked single expert as the shared one."""
+    L1, x, g, i = _single_expert_layer()
+    d = f = 128
+    zeros_q = F.pack_codes(np.full((f, d), 8))
+    one = np.full((f, d // 32), 0x3C00, np.uint16)
+    E = 2
+    L = M.Layer(np.ones((E, d), np.float32), None,
+                np.stack([zeros_q] * E), np.stack([one] * E), np.stack([zeros_q] * E), np.stack([one] * E),
+                np.stack([zeros_q] * E), np.stack([one] * E),
+                shared=(L1.gate_q[0], L1.gate_s[0], L1.up_q[0], L1.up_s[0], L1.down_q[0], L1.down_s[0]))
+    return L, x, g, i
+
+
+def test_shared_expert_alone_is_the_hand_worked_swiglu():
+    """With routed experts of zero weight the output is the shared expert's:
+    the hand-worked SwiGLU values, added with weight 1."""
+    L, x, g, i = _shared_alone_layer()
+    sp, sm = float(g["silu_plus1"][0]), float(g["silu_minus1"][0])
+    want = np.where(i % 3 == 0, sp, np.where(i % 3 == 1, sm, 0.0)) * np.where(i < 64, 1.0, -1.0)
+    out = M.moe_forward(L, x, 1)
+    np.testing.assert_allclose(out["y"], want, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(M.moe_forward_masked(L, x, 1), want, rtol=1e-15, atol=0)
+
+
+def test_shared_expert_weight_one_and_routing_untouched():
+    """The shared expert changes neither the chosen set nor its weights, and
+    enters with weight 1: doubling its down scales adds its output once more."""
+    lay = synth.make_layer(synth.TINY_SHARED, 3)
+    Ls = M.Layer.from_dict(lay)
+    L0 = M.Layer.from_dict({k: v for k, v in lay.items() if not k.startswith("shared")})
+    x = tiny_x(L0, 3)
+    a, b = M.moe_forward(Ls, x, 2), M.moe_forward(L0, x, 2)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["w"], b["w"])
+    assert np.array_equal(a["logits"], b["logits"])
+    lay2 = dict(lay, shared_down_s=F.f64_to_f16_bits(F.f16_to_f64(lay["shared_down_s"]) * 2))
+    c = M.moe_forward(M.Layer.from_dict(lay2), x, 2)
+    s = a["y"] - b["y"]
+    assert np.abs(s).max() > 1e-3
+    np.testing.assert_allclose(c["y"] - a["y"], s, rtol=0, atol=1e-15 * np.abs(a["y"]).max())
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_shared_sparse_equals_all_experts_then_mask_and_dense(seed):
+    lay = synth.make_layer(synth.TINY_SHARED, seed)
+    L = M.Layer.from_dict(lay)
+    x = tiny_x(M.Layer.from_dict({k: v for k, v in lay.items() if not k.startswith("shared")}), seed)
+    y = M.moe_forward(L, x, 2)["y"]
+    assert np.array_equal(y, M.moe_forward_masked(M.Layer.from_dict(lay), x, 2))
+    yd = M.moe_forward_dense_einsum(M.Layer.from_dict(lay), x, 2)
+    np.testing.assert_allclose(y, yd, rtol=0, atol=1e-13 * np.abs(y).max())
+
+
+def test_shared_active_weight_count():
+    lay = synth.make_layer(synth.TINY_SHARED, 1)
+    L = M.Layer.from_dict(lay)
+    x = tiny_x(L, 1)
+    L.weights_read = 0
+    M.moe_forward(L, x, 2)
+    E, d, f, k = 16, 256, 128, 2
+    assert L.weights_read == E * d + (k + 1) * 3 * d * f == M.active_weights(E, d, f, k, 1)
+    # the pages' layer: 256 routed experts, top-6 plus one shared, d=2048, f=512
+    assert M.active_weights(256, 2048, 512, 6, 1) == 524288 + 7 * 3 * 2048 * 512
