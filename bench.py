@@ -194,8 +194,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extras", action="store_true", help="skip stack, batch, LM head and CPU legs")
-    ap.add_argument("--extras", default="stack,batch,lmhead,cpu",
-                    help="comma list of the legs run after the headline (stack, batch, lmhead, cpu)")
+    ap.add_argument("--extras", default="stack,batch,flint,lmhead,cpu",
+                    help="comma list of the legs run after the headline (stack, batch, flint, lmhead, cpu)")
     ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (reference for HBM byte counters)")
@@ -370,6 +370,37 @@ def main():
         for L in blayers:
             L.close()
         del blayers, XB
+
+    if "flint" in extras:
+        # the pages' own routing: top-6 of the 256 routed experts plus one
+        # shared expert, 1-token steps over the same pool (each layer gets its
+        # shared expert), graph-timed like the headline
+        fk = synth.FLINT.k
+        fl = []
+        for l, L in enumerate(layers):
+            sh = M.upload(synth.make_shared(synth.FLINT, args.seed, l), dev)
+            fl.append(M.MoELayer.create(dict(L.tensors, **sh), d, f, E, fk, 1, 1))
+        yf = torch.empty((1, d), dtype=torch.float32, device=dev)
+
+        def flint_step(i):
+            l = i % P
+            t = (i // P) % args.tokens
+            M.moe_decode_forward(fl[l].handle, X[l, t:t + 1], 1, yf, None, None, stream)
+
+        try:
+            fs, _g = time_graph(flint_step, 2 * P * 5, P, stream)
+            del _g
+        except Exception as e:
+            log(f"flint graph failed: {e!r}")
+            fs = time_eager(flint_step, 2 * P * 5, P, stream)
+        us = fs / (2 * P * 5) * 1e6
+        bf = E * d * 4 + d * 2 + (fk + 1) * (by["b_q"] // k) + d * 4
+        out["flint_top6_shared"] = {"us_per_step": round(us, 3), "tokens_per_s": round(1 / (us * 1e-6), 1),
+                                    "bytes_per_step": int(bf), "achieved_gbs": round(bf / (us * 1e-6) / 1e9, 1),
+                                    "frac": round(bf / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        for L in fl:
+            L.close()
+        del fl
 
     if "lmhead" in extras:
         # LM head: rotate over 4 copies

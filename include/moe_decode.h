@@ -68,9 +68,14 @@ typedef int32_t moe_status;
  *   top_k      k, experts chosen per token, in [1, min(E, MOE_MAX_TOPK)]
  *   norm_topk  1: the chosen softmax weights are divided by their sum;
  *              0: they are used as they are
- *   max_tokens largest T a forward call will pass, in [1, MOE_MAX_TOKENS] */
+ *   max_tokens largest T a forward call will pass, in [1, MOE_MAX_TOKENS]
+ *   n_shared   0, or 1 for an always-on shared expert of the routed experts'
+ *              shape whose output is added with weight 1 (the pages' layer
+ *              has six routed experts plus one shared, "Flint 40B: Best Mid
+ *              Sized LLM", transcript 02:35); it takes no part in the
+ *              softmax or the renormalization */
 typedef struct {
-  int32_t d, f, n_experts, top_k, norm_topk, max_tokens;
+  int32_t d, f, n_experts, top_k, norm_topk, max_tokens, n_shared;
 } moe_layer_desc;
 
 /* Weights of one MoE layer (device, read-only, owned by the caller, must
@@ -79,7 +84,10 @@ typedef struct {
  *   router_b  fp32 [E], or NULL for no bias
  *   gate_q    int4 [E][f][d/2] stored format, gate_s binary16 [E][f][d/32]
  *   up_q      int4 [E][f][d/2],                up_s   binary16 [E][f][d/32]
- *   down_q    int4 [E][d][f/2],                down_s binary16 [E][d][f/32] */
+ *   down_q    int4 [E][d][f/2],                down_s binary16 [E][d][f/32]
+ *   shared_*  the shared expert's matrices in the same formats without the
+ *             expert dimension ([f][d/2], [f][d/32], [d][f/2], [d][f/32]);
+ *             required when n_shared = 1, ignored (may be NULL) otherwise */
 typedef struct {
   const float* router_w;
   const float* router_b;
@@ -89,6 +97,12 @@ typedef struct {
   const uint16_t* up_s;
   const uint8_t* down_q;
   const uint16_t* down_s;
+  const uint8_t* shared_gate_q;
+  const uint16_t* shared_gate_s;
+  const uint8_t* shared_up_q;
+  const uint16_t* shared_up_s;
+  const uint8_t* shared_down_q;
+  const uint16_t* shared_down_s;
 } moe_layer_weights;
 
 typedef struct moe_layer* moe_handle;
@@ -101,8 +115,8 @@ typedef struct moe_layer* moe_handle;
  * single-launch hand-off words and 6 KiB) and, for a
  * layer that may run the batched kernels (max_tokens > 1, or a shape the
  * single-launch kernel does not take), a tile-major copy of the gate, up and
- * down matrices (their size: 3*E*d*f/2 bytes of codes + 3*E*d*f/16 of
- * scales). */
+ * down matrices, the shared expert's included (their size: 3*(E+n_shared)*
+ * d*f/2 bytes of codes + 3*(E+n_shared)*d*f/16 of scales). */
 size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
 
 /* Validate the shape and weights and bind them, with a caller-owned device
@@ -122,13 +136,15 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
  *   logits = W_r x_t + b;  p = softmax(logits) over all E experts;
  *   S = the k largest p (larger first, lower expert index on ties);
  *   w_j = p_j / sum_{i in S} p_i (norm_topk) or p_j;
- *   y_t = sum_{j in S} w_j * W_d[j] (silu(W_g[j] x_t) * (W_u[j] x_t)).
- * Only the chosen experts' weights are read.
+ *   y_t = sum_{j in S} w_j * W_d[j] (silu(W_g[j] x_t) * (W_u[j] x_t))
+ *         [+ W_d^s (silu(W_g^s x_t) * (W_u^s x_t)) with a shared expert].
+ * Only the chosen experts' (and the shared expert's) weights are read.
  *   x         (device) bf16 bit patterns [T][d]
  *   T         tokens, 1 <= T <= max_tokens
  *   y         (device) fp32 [T][d], overwritten
  *   topk_idx  (device) int32 [T][k], chosen experts in the order above, or NULL
- *   topk_w    (device) fp32 [T][k], their weights, or NULL */
+ *   topk_w    (device) fp32 [T][k], their weights, or NULL (routed experts
+ *             only: the shared expert's weight is always 1) */
 moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float* y,
                               int32_t* topk_idx, float* topk_w, void* stream);
 
@@ -145,7 +161,7 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
                                     float eps, uint16_t* x_trace, float* y_trace, int32_t* idx_trace,
                                     void* stream);
 
-/* The grouping of (token, slot) assignments by expert made by the handle's
+/* The grouping of (token, slot) assignments to routed experts made by the handle's
  * last forward or stack call that ran the batched kernels (T > 1, or a
  * shape without the single-launch kernel).  Assignment a = t*k + j is
  * token t's j-th chosen expert.  Copies, enqueued on `stream` (any output

@@ -44,12 +44,16 @@ class MoEError(RuntimeError):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("f", ctypes.c_int32), ("n_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("norm_topk", ctypes.c_int32), ("max_tokens", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("norm_topk", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32)]
+
+
+WEIGHT_NAMES = ("router_w", "router_b", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
+                "shared_gate_q", "shared_gate_s", "shared_up_q", "shared_up_s", "shared_down_q", "shared_down_s")
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("router_w", "router_b", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
 
 
 _lib = None
@@ -183,15 +187,16 @@ class MoELayer:
 
     @classmethod
     def create(cls, tensors: dict, d: int, f: int, E: int, k: int, norm_topk: int = 1, max_tokens: int = 1):
-        """tensors: device tensors router_w, router_b (or None), gate_q, gate_s, up_q, up_s, down_q, down_s."""
+        """tensors: device tensors router_w, router_b (or None), gate_q, gate_s, up_q, up_s, down_q, down_s,
+        and shared_gate_q ... shared_down_s when the layer has a shared expert."""
         import torch
-        desc = LayerDesc(d, f, E, k, norm_topk, max_tokens)
+        n_shared = 1 if tensors.get("shared_gate_q") is not None else 0
+        desc = LayerDesc(d, f, E, k, norm_topk, max_tokens, n_shared)
         nbytes = moe_decode_workspace_bytes(desc)
         if nbytes == 0:
             raise MoEError(MOE_ERR_SHAPE, "moe_decode_workspace_bytes")
         ws = torch.empty(nbytes, dtype=torch.uint8, device=tensors["router_w"].device)
-        w = LayerWeights(*[_ptr(tensors.get(n)) for n in
-                           ("router_w", "router_b", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")])
+        w = LayerWeights(*[_ptr(tensors.get(n)) for n in WEIGHT_NAMES])
         h = moe_decode_init(desc, w, ws)
         return cls(d, f, E, k, norm_topk, max_tokens, tensors, ws, h)
 

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
@@ -32,6 +32,7 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->top_k > d->n_experts || d->top_k > MOE_MAX_TOPK) return MOE_ERR_SHAPE;
   if (d->max_tokens > MOE_MAX_TOKENS || d->n_experts > 1024) return MOE_ERR_SHAPE;
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_ERR_SHAPE;
+  if (d->n_shared != 0 && d->n_shared != 1) return MOE_ERR_SHAPE;
   if (d->d % 32 || d->f % 32) return MOE_ERR_SHAPE;
   if (!is_pow2(d->d) || d->d < 256 || d->d > 8192) return MOE_ERR_UNSUPPORTED;
   if (!is_pow2(d->f) || d->f < 128 || d->f > 4096) return MOE_ERR_UNSUPPORTED;
@@ -42,14 +43,17 @@ moe_status check_desc(const moe_layer_desc* d) {
 // at init; a layer gets one if it may run them: T > 1 allowed, or a shape
 // without the single-launch kernel (which reads the caller's matrices).
 bool needs_tiled_copy(const moe_layer_desc* d) {
-  return d->max_tokens > 1 || !moe::fused_layer_supported(d->d, d->f, d->n_experts, d->top_k, moe::kFusedGridCUs);
+  return d->max_tokens > 1 ||
+         !moe::fused_layer_supported(d->d, d->f, d->n_experts, d->top_k, d->n_shared, moe::kFusedGridCUs);
 }
 
 Layout layout_of(const moe_layer_desc* d) {
   Layout L;
   const size_t T = (size_t)d->max_tokens, E = (size_t)d->n_experts, k = (size_t)d->top_k;
+  const size_t ns = (size_t)d->n_shared;
   size_t o = 0;
   const size_t Tk = T * k, d_ = (size_t)d->d, f_ = (size_t)d->f;
+  const size_t Ta = Tk + ns * T;  // assignments, the shared expert's last
   L.logits = o, o += align256(T * E * sizeof(float));
   L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
   L.sel_w = o, o += align256(Tk * sizeof(float));
@@ -57,17 +61,17 @@ Layout layout_of(const moe_layer_desc* d) {
   L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
   L.act = o, o += align256(E * sizeof(int32_t));
   L.chunk_off = o, o += align256((E + 1) * sizeof(int32_t));
-  L.chunks = o, o += align256(((E < Tk ? E : Tk) + Tk / 32) * 4 * sizeof(int32_t));
-  L.asg = o, o += align256(Tk * sizeof(int32_t));
-  L.h16 = o, o += align256(Tk * f_ * sizeof(uint16_t));
-  L.obuf = o, o += align256(Tk * d_ * sizeof(float));
+  L.chunks = o, o += align256(((E < Tk ? E : Tk) + Tk / 32 + ns * ((T + 31) / 32)) * 4 * sizeof(int32_t));
+  L.asg = o, o += align256(Ta * sizeof(int32_t));
+  L.h16 = o, o += align256(Ta * f_ * sizeof(uint16_t));
+  L.obuf = o, o += align256(Ta * d_ * sizeof(float));
   L.resid = o, o += align256(T * d_ * sizeof(float));  // second residual buffer of a stack
   L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
-  L.hrec = o, o += align256(k * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
+  L.hrec = o, o += align256((k + ns) * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
   L.cleared = o;
   const bool copy = needs_tiled_copy(d);
-  const size_t cq = copy ? E * f_ * d_ / 2 : 0, cs = copy ? E * f_ * (d_ / 32) * 2 : 0;
+  const size_t cq = copy ? (E + ns) * f_ * d_ / 2 : 0, cs = copy ? (E + ns) * f_ * (d_ / 32) * 2 : 0;
   L.gate_t = o, o += align256(cq);
   L.gate_ts = o, o += align256(cs);
   L.up_t = o, o += align256(cq);
@@ -97,7 +101,9 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.gate_q = a.gate_q, f.gate_s = a.gate_s, f.up_q = a.up_q, f.up_s = a.up_s;
   f.down_q = a.down_q, f.down_s = a.down_s;
   f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error;
-  f.E = a.E, f.k = a.k, f.norm = a.norm_topk;
+  f.sh_gate_q = a.sh_gate_q, f.sh_gate_s = a.sh_gate_s, f.sh_up_q = a.sh_up_q, f.sh_up_s = a.sh_up_s;
+  f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
+  f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
   return f;
 }
 
@@ -137,6 +143,15 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
   if (w->router_b && !aligned4(w->router_b)) return MOE_ERR_ALIGN;
+  if (desc->n_shared) {
+    if (!w->shared_gate_q || !w->shared_gate_s || !w->shared_up_q || !w->shared_up_s || !w->shared_down_q ||
+        !w->shared_down_s)
+      return MOE_ERR_NULL;
+    const void* sp[] = {w->shared_gate_q, w->shared_gate_s, w->shared_up_q, w->shared_up_s, w->shared_down_q,
+                        w->shared_down_s};
+    for (const void* p : sp)
+      if (!aligned16(p)) return MOE_ERR_ALIGN;
+  }
   const Layout L = layout_of(desc);
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
@@ -147,9 +162,13 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   h->workspace = workspace;
   moe::LayerArgs& a = h->args;
   a.d = desc->d, a.f = desc->f, a.E = desc->n_experts, a.k = desc->top_k, a.norm_topk = desc->norm_topk;
+  a.ns = desc->n_shared;
   a.router_w = w->router_w, a.router_b = w->router_b;
   a.gate_q = w->gate_q, a.gate_s = w->gate_s, a.up_q = w->up_q, a.up_s = w->up_s;
   a.down_q = w->down_q, a.down_s = w->down_s;
+  a.sh_gate_q = a.ns ? w->shared_gate_q : nullptr, a.sh_gate_s = a.ns ? w->shared_gate_s : nullptr;
+  a.sh_up_q = a.ns ? w->shared_up_q : nullptr, a.sh_up_s = a.ns ? w->shared_up_s : nullptr;
+  a.sh_down_q = a.ns ? w->shared_down_q : nullptr, a.sh_down_s = a.ns ? w->shared_down_s : nullptr;
   unsigned char* base = static_cast<unsigned char*>(workspace);
   a.logits = reinterpret_cast<float*>(base + L.logits);
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
@@ -175,7 +194,8 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.up_ts = copy ? reinterpret_cast<uint16_t*>(base + L.up_ts) : nullptr;
   a.down_t = copy ? base + L.down_t : nullptr;
   a.down_ts = copy ? reinterpret_cast<uint16_t*>(base + L.down_ts) : nullptr;
-  h->fused = moe::fused_layer_supported(desc->d, desc->f, desc->n_experts, desc->top_k, moe::fused_grid());
+  h->fused = moe::fused_layer_supported(desc->d, desc->f, desc->n_experts, desc->top_k, desc->n_shared,
+                                        moe::fused_grid());
   if (!h->fused && !copy) {  // a GPU with fewer CUs than the single-launch kernel assumes
     delete h;
     return MOE_ERR_UNSUPPORTED;

@@ -91,9 +91,10 @@ __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
   return (size_t)(j / wpw) * lpw * 16 + (j % wpw);
 }
 
-// D hidden, F expert width, KP top_k rounded up to a power of two, EPL
+// D hidden, F expert width, KP expert slots (top_k, plus one with a shared
+// expert, SH) rounded up to a power of two, EPL
 // experts per lane in the top-k wave.
-template <int D, int F, int KP, int EPL, bool NORM>
+template <int D, int F, int KP, int EPL, bool NORM, bool SH>
 __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
@@ -140,6 +141,39 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane];
   }
+  // gate/up slots: the k chosen experts, then the shared one (ns = 1), wpe
+  // waves each
+  const int wpe = (F * CPR) / (64 * NL);  // waves per expert slot
+  const int nslots = k + (SH ? 1 : 0);
+  const bool has_gate = wg < nslots * wpe;
+  const int gslot = has_gate ? wg / wpe : -1;
+  const bool shared_slot = SH && gslot >= k;
+  const int c0 = has_gate ? (wg - gslot * wpe) * 64 * NL : 0;
+  uint4 qg[NL], qu[NL];
+  uint2 sg[NL], su[NL];
+  auto load_mats = [&](const uint8_t* gq8, const uint16_t* gsb, const uint8_t* uq8, const uint16_t* usb) {
+    const uint4* gp = reinterpret_cast<const uint4*>(gq8);
+    const uint4* up = reinterpret_cast<const uint4*>(uq8);
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int c = c0 + 64 * n + lane;
+      qg[n] = gp[c];
+      qu[n] = up[c];
+      const size_t so = (size_t)(c / CPR) * CPR + ((c % CPR) & ~3);
+      sg[n] = *reinterpret_cast<const uint2*>(gsb + so);
+      su[n] = *reinterpret_cast<const uint2*>(usb + so);
+    }
+  };
+  auto load_gate = [&](int e_raw) {
+    const int e = min(max(e_raw, 0), E - 1);
+    const size_t mat = (size_t)F * CPR;
+    load_mats(a.gate_q + (size_t)e * mat * 16, a.gate_s + (size_t)e * mat, a.up_q + (size_t)e * mat * 16,
+              a.up_s + (size_t)e * mat);
+  };
+  // the shared expert needs no routing: its slot's loads go out now, behind
+  // the router rows, and land while the logits are exchanged
+  if constexpr (SH)
+    if (shared_slot) load_mats(a.sh_gate_q, a.sh_gate_s, a.sh_up_q, a.sh_up_s);
   if constexpr (!NORM) {
 #pragma unroll
     for (int c = threadIdx.x; c < D / 8; c += 256) reinterpret_cast<uint4*>(s_x)[c] = reinterpret_cast<const uint4*>(a.x)[c];
@@ -214,42 +248,18 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 #pragma unroll
   for (int i = 0; i < EPL; ++i) v[i] = s_lg[lane + 64 * i];
 
-  const int wpe = (F * CPR) / (64 * NL);  // waves per chosen expert
-  const bool has_gate = wg < k * wpe;
-  const int gslot = has_gate ? wg / wpe : -1;
-  const int c0 = has_gate ? (wg - gslot * wpe) * 64 * NL : 0;
-  uint4 qg[NL], qu[NL];
-  uint2 sg[NL], su[NL];
-  auto load_gate = [&](int e_raw) {
-    const int e = min(max(e_raw, 0), E - 1);
-    const size_t mat = (size_t)F * CPR;
-    const uint4* gp = reinterpret_cast<const uint4*>(a.gate_q) + (size_t)e * mat;
-    const uint4* up = reinterpret_cast<const uint4*>(a.up_q) + (size_t)e * mat;
-    const uint16_t* gsb = a.gate_s + (size_t)e * mat;
-    const uint16_t* usb = a.up_s + (size_t)e * mat;
-#pragma unroll
-    for (int n = 0; n < NL; ++n) {
-      const int c = c0 + 64 * n + lane;
-      qg[n] = gp[c];
-      qu[n] = up[c];
-      const size_t so = (size_t)(c / CPR) * CPR + ((c % CPR) & ~3);
-      sg[n] = *reinterpret_cast<const uint2*>(gsb + so);
-      su[n] = *reinterpret_cast<const uint2*>(usb + so);
-    }
-  };
-
   int se = 0;
   bool exact = false;
   if (topk_select_merge<EPL, KP>(v, E, k, lane, se)) {
-    const int e_slot = __shfl(se, max(gslot, 0), 64);
-    if (has_gate) load_gate(e_slot);
+    const int e_slot = __shfl(se, max(gslot, 0) & 63, 64);
+    if (has_gate && !shared_slot) load_gate(e_slot);
   } else {  // picks that agree in their top bits: redo exactly
     float sw;
     topk_exact<EPL>(v, E, k, a.norm, lane, se, sw);
     if (wid == 0 && lane < k) s_w[lane] = sw;
     exact = true;
-    const int e_slot = __shfl(se, max(gslot, 0), 64);
-    if (has_gate) load_gate(e_slot);
+    const int e_slot = __shfl(se, max(gslot, 0) & 63, 64);
+    if (has_gate && !shared_slot) load_gate(e_slot);
   }
   if (wid == 0) {
     if (lane < k) s_idx[lane] = se;
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
   // ---------------------------------------------------------------- gate/up + SwiGLU
   if (has_gate) {
-    const float wj = s_w[gslot];
+    const float wj = shared_slot ? 1.f : s_w[gslot];
     Slice8 xs[XS][4];
 #pragma unroll
     for (int s = 0; s < XS; ++s) {
@@ -303,7 +313,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int SPW = ROWS_G / 8;          // slices per workgroup
   constexpr int WPW = SPW * 5;             // words per workgroup
   constexpr int LPW = (WPW + 15) / 16;     // 128-byte lines per workgroup
-  const bool producer = blockIdx.x * 4 < k * wpe;
+  const bool producer = blockIdx.x * 4 < nslots * wpe;
   if (producer && threadIdx.x < SPW) {
     float hv[8];
 #pragma unroll
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     const int flat = P >= 64 ? 64 * m + lane : lane % P;
     dslot[m] = flat / CPRF;
     cc[m] = flat % CPRF;
-    act[m] = has_down && dslot[m] < k;
+    act[m] = has_down && dslot[m] < nslots;
   }
   float radd[NLD];  // residual rows this lane will update (stack)
 #pragma unroll
@@ -349,9 +359,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     const int m = n % LPRD;
     const int row = r0 + (P >= 64 ? n / LPRD : n * RPLD + lane / P);
     if (act[m]) {
-      const size_t eb = (size_t)min(max(s_idx[dslot[m]], 0), E - 1) * D + row;
-      qd[n] = *reinterpret_cast<const uint4*>(a.down_q + piece_offset(eb, CPRF, cc[m]));
-      sd[n] = *reinterpret_cast<const uint2*>(a.down_s + eb * CPRF + (cc[m] & ~3));
+      const bool shd = SH && dslot[m] >= k;  // the shared expert's slot
+      const size_t eb = shd ? (size_t)row : (size_t)min(max(s_idx[dslot[m]], 0), E - 1) * D + row;
+      qd[n] = *reinterpret_cast<const uint4*>((shd ? a.sh_down_q : a.down_q) + piece_offset(eb, CPRF, cc[m]));
+      sd[n] = *reinterpret_cast<const uint2*>((shd ? a.sh_down_s : a.down_s) + eb * CPRF + (cc[m] & ~3));
     } else {
       qd[n] = make_uint4(0, 0, 0, 0);
       sd[n] = make_uint2(0, 0);
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   // tag, and later polls re-read only the words still missing
   {
     constexpr int NR = (KP * F / 8 * 5 + 255) / 256;
-    const int nw = k * (F / 8) * 5;  // slice words; word j = 5 * slice + field
+    const int nw = nslots * (F / 8) * 5;  // slice words; word j = 5 * slice + field
     unsigned missing = 0;
 #pragma unroll
     for (int m = 0; m < NR; ++m) missing |= (threadIdx.x + 256 * m < (unsigned)nw ? 1u : 0u) << m;
@@ -433,11 +444,18 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
 template <int D, int F, int KP, int EPL>
 static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
-  const size_t lds = (size_t)a.k * (F / 8) * 5 * sizeof(unsigned);
-  if (a.resid_in)
-    hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true>), dim3(G), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false>), dim3(G), dim3(256), lds, s, a);
+  const size_t lds = (size_t)(a.k + a.ns) * (F / 8) * 5 * sizeof(unsigned);
+  if (a.ns) {
+    if (a.resid_in)
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true>), dim3(G), dim3(256), lds, s, a);
+    else
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, true>), dim3(G), dim3(256), lds, s, a);
+  } else {
+    if (a.resid_in)
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, false>), dim3(G), dim3(256), lds, s, a);
+    else
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, false>), dim3(G), dim3(256), lds, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -450,7 +468,7 @@ static hipError_t layer_epl(const FusedArgs& a, int G, hipStream_t s) {
 
 template <int D, int F>
 static hipError_t layer_kp(const FusedArgs& a, int G, hipStream_t s) {
-  const int k = a.k;
+  const int k = a.k + a.ns;  // expert slots
   if (k <= 1) return layer_epl<D, F, 1>(a, G, s);
   if (k <= 2) return layer_epl<D, F, 2>(a, G, s);
   if (k <= 4) return layer_epl<D, F, 4>(a, G, s);
@@ -458,9 +476,11 @@ static hipError_t layer_kp(const FusedArgs& a, int G, hipStream_t s) {
   return layer_epl<D, F, 16>(a, G, s);
 }
 
-// Work each wave takes in the fused kernel must fit one unit per wave.
+// Work each wave takes in the fused kernel must fit one unit per wave; k
+// counts the expert slots (chosen plus shared).
 static bool fits(int d, int f, int E, int k, int G) {
   const int W = 4 * G;
+  if (k > 16) return false;
   const int cpr = d / 32, cprf = f / 32;
   if ((long)k * f * cpr / 256 > W) return false;  // gate/up units (4 pieces per lane)
   int kp = 1;
@@ -475,9 +495,9 @@ static bool fits(int d, int f, int E, int k, int G) {
   return true;
 }
 
-bool fused_layer_supported(int d, int f, int E, int k, int G) {
+bool fused_layer_supported(int d, int f, int E, int k, int ns, int G) {
   if (!((d == 256 && f == 128) || (d == 2048 && f == 512))) return false;
-  return fits(d, f, E, k, G);
+  return fits(d, f, E, k + ns, G);
 }
 
 int fused_grid() {
@@ -494,7 +514,7 @@ int fused_grid() {
 
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s) {
   const int G = fused_grid();
-  if (G <= 0 || !fits(d, f, a.E, a.k, G)) return hipErrorInvalidValue;
+  if (G <= 0 || !fits(d, f, a.E, a.k + a.ns, G)) return hipErrorInvalidValue;
   if (d == 256 && f == 128) return layer_kp<256, 128>(a, G, s);
   if (d == 2048 && f == 512) return layer_kp<2048, 512>(a, G, s);
   return hipErrorInvalidValue;

@@ -100,8 +100,11 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 //   asg[p]                the assignment at position p
 //   act[i], i < meta[0]   the experts with at least one assignment, ascending
 //   chunk_off[i]          32-token chunks of the active experts before act[i]
-//                         (chunk_off[meta[0]] = all chunks = meta[1])
+//                         (chunk_off[meta[0]] = all routed chunks)
 //   chunks[c]             chunk c: (expert, first position, positions <= 32)
+//   meta[1], meta[2]      all chunks, Tk
+// With a shared expert, its T assignments Tk + t sit at positions Tk + t and
+// its chunks (expert index E) follow the routed ones.
 // Wave w owns the w-th sixteenth of the assignments: it counts them per
 // expert (lanes with equal experts found by wave ballots), a prefix over
 // waves gives each (wave, expert) its base, and each wave places its own
@@ -115,6 +118,7 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
   int* tot = cnt + 16 * E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < Tk; i += 1024) ssel[i] = min(max(a.sel_idx[i], 0), E - 1);
+  for (int i = tid; i < a.ns * T; i += 1024) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
   for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
   __syncthreads();
   const int per = (Tk + 15) / 16, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
@@ -178,7 +182,11 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
       a.off[E] = base;
       a.chunk_off[abase] = cbase;
       a.meta[0] = abase;
+      // the shared expert (expert index E of the tile-major copies) takes
+      // every token, in chunks after the routed ones
+      for (int tc = 0; tc < a.ns * T; tc += 32) a.chunks[cbase++] = make_int4(E, Tk + tc, min(32, T - tc), 0);
       a.meta[1] = cbase;
+      a.meta[2] = Tk;
     }
   }
   __syncthreads();
@@ -546,7 +554,9 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
     const uint2* wts[2] = {reinterpret_cast<const uint2*>(a.gate_ts) + tile * (D / 128) * 16,
                            reinterpret_cast<const uint2*>(a.up_ts) + tile * (D / 128) * 16};
     // the operand row this thread stages: token of chunk row tid/8
-    const int tok = a.asg[it.p0 + min(tid >> 3, it.n - 1)] / k;
+    const int Tk = a.meta[2];
+    const int asg0 = a.asg[it.p0 + min(tid >> 3, it.n - 1)];
+    const int tok = asg0 < Tk ? asg0 / k : asg0 - Tk;  // shared-expert assignments: Tk + token
     f32x4_t acc[2][2];
     acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // both token tiles always (for a chunk of up to 16 rows the second tile
@@ -562,7 +572,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int pt = 16 * tt + 4 * q + v;
         if (pt < it.n) {
-          const float wj = a.sel_w[a.asg[it.p0 + pt]];
+          const int asg = a.asg[it.p0 + pt];
+          const float wj = asg < Tk ? a.sel_w[asg] : 1.f;
           const float h = wj * silu(acc[0][tt][v]) * acc[1][tt][v];
           a.h16[(size_t)(it.p0 + pt) * f + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
@@ -622,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
 // ----------------------------------------------------------------- combine
 
 // y_t = sum_{j<k} o_{t,j} (slot order); with resid, resid_t += y_t.
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf, int T, int d, int k,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf, int T, int d, int k, int ns,
                                                  float* __restrict__ y_out, float* __restrict__ resid) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // float4 index over [T][d]
   if (i >= T * d / 4) return;
@@ -630,6 +641,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf,
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const float4 o = *reinterpret_cast<const float4*>(obuf + ((size_t)t * k + j) * d + r);
+    s.x += o.x;
+    s.y += o.y;
+    s.z += o.z;
+    s.w += o.w;
+  }
+  if (ns) {  // the shared expert's output, weight 1
+    const float4 o = *reinterpret_cast<const float4*>(obuf + ((size_t)T * k + t) * d + r);
     s.x += o.x;
     s.y += o.y;
     s.z += o.z;
@@ -703,7 +721,7 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
 // Workgroup items: (chunk, row group); at most min(E, T*k) + T*k/32 chunks.
 static int max_chunks(const LayerArgs& a, int T) {
   const int Tk = T * a.k;
-  return (a.E < Tk ? a.E : Tk) + Tk / 32;
+  return (a.E < Tk ? a.E : Tk) + Tk / 32 + a.ns * ((T + 31) / 32);
 }
 static int grid_for(const LayerArgs& a, int T, int groups) {
   const int items = max_chunks(a, T) * groups;
@@ -757,13 +775,27 @@ hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
   if ((e = tile_matrix(a.up_q, a.up_s, const_cast<uint8_t*>(a.up_t), const_cast<uint16_t*>(a.up_ts), E * a.f,
                        a.d, s)) != hipSuccess)
     return e;
-  return tile_matrix(a.down_q, a.down_s, const_cast<uint8_t*>(a.down_t), const_cast<uint16_t*>(a.down_ts),
-                     E * a.d, a.f, s);
+  if ((e = tile_matrix(a.down_q, a.down_s, const_cast<uint8_t*>(a.down_t), const_cast<uint16_t*>(a.down_ts),
+                       E * a.d, a.f, s)) != hipSuccess)
+    return e;
+  if (!a.ns) return hipSuccess;
+  // the shared expert as expert E of the copies
+  const size_t gq = (size_t)E * a.f * a.d / 2, gs = (size_t)E * a.f * (a.d / 32);
+  const size_t dq = (size_t)E * a.d * a.f / 2, ds = (size_t)E * a.d * (a.f / 32);
+  if ((e = tile_matrix(a.sh_gate_q, a.sh_gate_s, const_cast<uint8_t*>(a.gate_t) + gq,
+                       const_cast<uint16_t*>(a.gate_ts) + gs, a.f, a.d, s)) != hipSuccess)
+    return e;
+  if ((e = tile_matrix(a.sh_up_q, a.sh_up_s, const_cast<uint8_t*>(a.up_t) + gq, const_cast<uint16_t*>(a.up_ts) + gs,
+                       a.f, a.d, s)) != hipSuccess)
+    return e;
+  return tile_matrix(a.sh_down_q, a.sh_down_s, const_cast<uint8_t*>(a.down_t) + dq,
+                     const_cast<uint16_t*>(a.down_ts) + ds, a.d, a.f, s);
 }
 
 hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s) {
   const int n4 = T * a.d / 4;
-  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, T, a.d, a.k, y_out, residual);
+  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, T, a.d, a.k, a.ns, y_out,
+                     residual);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ namespace moe {
 // Device pointers of one MoE layer plus the per-call workspace carve-up.
 struct LayerArgs {
   int d, f, E, k, norm_topk;
+  int ns;  // shared experts, 0 or 1: expert index E of the tile-major copies, assignments T*k + t
   const float* router_w;
   const float* router_b;
   const uint8_t* gate_q;
@@ -20,7 +21,13 @@ struct LayerArgs {
   const uint16_t* up_s;
   const uint8_t* down_q;
   const uint16_t* down_s;
-  // tile-major copies of the expert matrices (batched path; max_tokens > 1)
+  const uint8_t* sh_gate_q;  // the shared expert (ns = 1), formats as one expert of the above
+  const uint16_t* sh_gate_s;
+  const uint8_t* sh_up_q;
+  const uint16_t* sh_up_s;
+  const uint8_t* sh_down_q;
+  const uint16_t* sh_down_s;
+  // tile-major copies of the expert matrices, [E + ns] (batched path; max_tokens > 1)
   const uint8_t* gate_t;
   const uint16_t* gate_ts;
   const uint8_t* up_t;
@@ -35,11 +42,12 @@ struct LayerArgs {
   int32_t* off;           // [E+1] first position of each expert in asg
   int32_t* act;           // [E] experts with assignments, ascending
   int32_t* chunk_off;     // [E+1] 32-token chunks of the active experts before each
-  int4* chunks;           // [min(E, T*k) + T*k/32] (expert, first position, count <= 32)
-  int32_t* meta;          // [0]: number of active experts, [1]: number of chunks
-  int32_t* asg;           // [T*k] assignments grouped by expert
-  uint16_t* h16;          // [T*k][f] w_j silu(g) u per position, fp16 operand order
-  float* obuf;            // [T*k][d] o_{t,j} per assignment
+  int4* chunks;           // [min(E, T*k) + T*k/32 + ns*ceil(T/32)] (expert, first position, count <= 32);
+                          // the shared expert's chunks (expert E) come last
+  int32_t* meta;          // [0]: active routed experts, [1]: chunks, [2]: T*k
+  int32_t* asg;           // [T*k + ns*T] assignments grouped by expert (shared: T*k + t, last)
+  uint16_t* h16;          // [T*k + ns*T][f] w_j silu(g) u per position, fp16 operand order
+  float* obuf;            // [T*k + ns*T][d] o_{t,j} per assignment
   // single-launch step (T = 1)
   unsigned long long* tagged_logits;  // ceil(E/4) lines of 128 B: (epoch << 32 | logit bits)
   unsigned long long* hrec;           // [k*f/8][5] (epoch << 32 | fp16 slice word)
@@ -74,12 +82,19 @@ struct FusedArgs {
   unsigned long long* hrec;    // tagged fp16 slices of h
   unsigned* epoch;             // per-workgroup call counts
   unsigned* error;
-  int E, k, norm;
+  const uint8_t* sh_gate_q;    // the shared expert (ns = 1): slot k of the step, weight 1
+  const uint16_t* sh_gate_s;
+  const uint8_t* sh_up_q;
+  const uint16_t* sh_up_s;
+  const uint8_t* sh_down_q;
+  const uint16_t* sh_down_s;
+  int E, k, norm, ns;
 };
 
 // The whole 1-token step in one launch, for the shapes it is built for
-// (d, f) in {(256, 128), (2048, 512)}, E <= 256.
-bool fused_layer_supported(int d, int f, int E, int k, int G);
+// (d, f) in {(256, 128), (2048, 512)}, E <= 256; ns shared experts take
+// slots k .. k+ns-1.
+bool fused_layer_supported(int d, int f, int E, int k, int ns, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
 
@@ -99,7 +114,7 @@ hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s);
 // The tile-major copies of gate, up and down (from the canonical matrices).
 hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s);
 
-// y_t = sum_j o_{t,j} into y_out (if non-NULL); residual_t += y_t (if non-NULL).
+// y_t = sum_j o_{t,j} (+ o_{t,shared}) into y_out (if non-NULL); residual_t += y_t (if non-NULL).
 hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
 
 // LM head GEMV + argmax.

@@ -216,10 +216,19 @@ def make_layer(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
     rb = zipf_bias(cfg, seed) if cfg.zipf_s > 0 else None
     out = dict(router_w=rw, router_b=rb, gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
     if cfg.shared:
-        # the shared expert: streams of its own, the routed experts' distribution
-        for name, rows, K in (("gate", f, d), ("up", f, d), ("down", d, f)):
-            q, sc = int4_experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
-            out["shared_" + name + "_q"], out["shared_" + name + "_s"] = q[0], sc[0]
+        out.update(make_shared(cfg, seed, layer))
+    return out
+
+
+def make_shared(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
+    """The shared expert of a layer (streams of its own, the routed experts'
+    distribution): shared_{gate,up,down}_{q,s}."""
+    d, f = cfg.d, cfg.f
+    base = (seed, "tiny" if cfg.d == TINY.d and cfg.E == TINY.E else "layer", layer)
+    out = {}
+    for name, rows, K in (("gate", f, d), ("up", f, d), ("down", d, f)):
+        q, sc = int4_experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
+        out["shared_" + name + "_q"], out["shared_" + name + "_s"] = q[0], sc[0]
     return out
 
 

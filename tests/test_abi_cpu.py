@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert L.moe_decode_abi_version() == 1
+    assert L.moe_decode_abi_version() == 2
 
 
 def test_status_strings():
@@ -60,7 +60,7 @@ def test_workspace_bytes_layout():
 
 @pytest.mark.parametrize("kw", [dict(top_k=0), dict(top_k=17), dict(top_k=300, n_experts=256), dict(max_tokens=0),
                                 dict(max_tokens=257), dict(d=2040), dict(f=500), dict(norm_topk=2),
-                                dict(n_experts=2000), dict(d=0)])
+                                dict(n_experts=2000), dict(d=0), dict(n_shared=2), dict(n_shared=-1)])
 def test_bad_shapes_have_no_workspace(kw):
     assert M.moe_decode_workspace_bytes(desc(**kw)) == 0
 
@@ -90,6 +90,22 @@ def test_init_validation_codes():
     assert init_status(desc(), weights(), None, need)[0] == M.MOE_ERR_WORKSPACE
     assert init_status(desc(), weights(), FAKE + 16, need)[0] == M.MOE_ERR_ALIGN
     assert M.lib().moe_decode_init(None, ctypes.byref(weights()), FAKE, need, None) == M.MOE_ERR_NULL
+
+
+def test_shared_expert_validation_and_workspace():
+    """n_shared = 1 needs all six shared matrices, 16-byte aligned; the
+    batched workspace grows by the shared expert's assignments and copy."""
+    sh = {n: FAKE for n in ("shared_gate_q", "shared_gate_s", "shared_up_q", "shared_up_s", "shared_down_q",
+                            "shared_down_s")}
+    need = M.moe_decode_workspace_bytes(desc(n_shared=1, top_k=6))
+    assert need > 0
+    assert init_status(desc(n_shared=1, top_k=6), weights())[0] == M.MOE_ERR_NULL
+    assert init_status(desc(n_shared=1, top_k=6), weights(**dict(sh, shared_down_s=None)))[0] == M.MOE_ERR_NULL
+    assert init_status(desc(n_shared=1, top_k=6), weights(**dict(sh, shared_up_q=FAKE + 8)))[0] == M.MOE_ERR_ALIGN
+    n64 = M.moe_decode_workspace_bytes(desc(max_tokens=64, top_k=6))
+    s64 = M.moe_decode_workspace_bytes(desc(max_tokens=64, top_k=6, n_shared=1))
+    # 64 more assignments (fp32 outputs and fp16 h) and one more expert in the tile-major copies
+    assert s64 - n64 >= 64 * 2048 * 4 + 64 * 512 * 2 + 3 * 2048 * 512 // 2
 
 
 def test_forward_and_stack_reject_null_handles():
