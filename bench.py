@@ -194,8 +194,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extras", action="store_true", help="skip stack, batch, LM head and CPU legs")
-    ap.add_argument("--extras", default="stack,batch,flint,lmhead,cpu",
-                    help="comma list of the legs run after the headline (stack, batch, flint, lmhead, cpu)")
+    ap.add_argument("--extras", default="stack,batch,prefill,flint,lmhead,cpu",
+                    help="comma list of the legs run after the headline (stack, batch, prefill, flint, lmhead, cpu)")
     ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (reference for HBM byte counters)")
@@ -370,6 +370,43 @@ def main():
         for L in blayers:
             L.close()
         del blayers, XB
+
+    if "prefill" in extras:
+        # prompt processing: 2048 tokens per call through one layer (no
+        # router bias), rotating over 8 layers of the pool (4.7 GB with their
+        # tile-major copies, more than the memory-side cache)
+        TP, PL = 2048, 8
+        pl = [M.MoELayer.create(layers[l].tensors, d, f, E, k, 1, TP) for l in range(PL)]
+        XP = torch.from_numpy(np.stack([np.stack([synth.draw_x(synth.LAYER, args.seed, l, 4096 + t, 0)
+                                                  for t in range(TP)]) for l in range(PL)]).view(np.int16)).to(dev)
+        yp = torch.empty((TP, d), dtype=torch.float32, device=dev)
+        ipf = torch.empty((PL, TP, k), dtype=torch.int32, device=dev)
+        for l in range(PL):
+            M.moe_decode_forward(pl[l].handle, XP[l], TP, yp, ipf[l], None, stream)
+        stream.synchronize()
+        dpf = [len(np.unique(a)) for a in ipf.cpu().numpy()]
+
+        def prefill_step(i):
+            M.moe_decode_forward(pl[i % PL].handle, XP[i % PL], TP, yp, None, None, stream)
+
+        try:
+            ps, _g = time_graph(prefill_step, 4 * PL, PL, stream)
+            del _g
+        except Exception as e:
+            log(f"prefill graph failed: {e!r}")
+            ps = time_eager(prefill_step, 4 * PL, PL, stream)
+        us = ps / (4 * PL) * 1e6
+        per_expert = by["b_q"] // k
+        bp = E * d * 4 + TP * d * 2 + float(np.mean(dpf)) * per_expert + TP * d * 4
+        flop = TP * (2 * E * d + k * 3 * 2 * d * f)
+        out["prefill_t2048"] = {"us_per_call": round(us, 3), "tokens_per_s": round(TP / (us * 1e-6), 1),
+                                "distinct_experts_mean": round(float(np.mean(dpf)), 2),
+                                "bytes_per_call": int(bp), "achieved_gbs": round(bp / (us * 1e-6) / 1e9, 1),
+                                "frac": round(bp / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                "tflops": round(flop / (us * 1e-6) / 1e12, 1)}
+        for L in pl:
+            L.close()
+        del pl, XP
 
     if "flint" in extras:
         # the pages' own routing: top-6 of the 256 routed experts plus one

@@ -58,7 +58,7 @@ typedef int32_t moe_status;
 #define MOE_ERR_UNSUPPORTED (-6) /* a shape the kernels are not built for */
 
 #define MOE_MAX_TOPK 16          /* largest top_k */
-#define MOE_MAX_TOKENS 256       /* largest T per forward call */
+#define MOE_MAX_TOKENS 4096      /* largest T per forward call (prompt processing included) */
 #define MOE_LMHEAD_MAX_B 16      /* largest B per LM-head call */
 
 /* Shape of one MoE layer.

@@ -26,7 +26,7 @@ MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
 MOE_ERR_UNSUPPORTED = -6
 MOE_MAX_TOPK = 16
-MOE_MAX_TOKENS = 256
+MOE_MAX_TOKENS = 4096
 MOE_LMHEAD_MAX_B = 16
 
 EXPORTED = (

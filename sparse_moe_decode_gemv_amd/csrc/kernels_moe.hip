@@ -113,11 +113,11 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
   extern __shared__ int sm[];
   const int E = a.E, Tk = T * a.k;
-  int* ssel = sm;
-  int* cnt = sm + ((Tk + 3) & ~3);
+  int* cnt = sm;
   int* tot = cnt + 16 * E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < Tk; i += 1024) ssel[i] = min(max(a.sel_idx[i], 0), E - 1);
+  // the chosen experts are read where they are (T*k of them may exceed LDS at prefill sizes)
+  auto sel = [&](int i) { return min(max(a.sel_idx[i], 0), E - 1); };
   for (int i = tid; i < a.ns * T; i += 1024) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
   for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
   __syncthreads();
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
   for (int c = a0; c < a1; c += 64) {  // this wave's counts
     const int i = c + lane;
     const bool v = i < a1;
-    const int e = v ? ssel[i] : 0;
+    const int e = sel(min(i, Tk - 1));
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     if (v && lane == __builtin_ctzll(same)) cw[e] += __builtin_popcountll(same);
     lds_wait();
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
   for (int c = a0; c < a1; c += 64) {  // placement, stable in a
     const int i = c + lane;
     const bool v = i < a1;
-    const int e = v ? ssel[i] : 0;
+    const int e = sel(min(i, Tk - 1));
     const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
     const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
     const int pos = v ? tot[e] + cw[e] : 0;
@@ -204,7 +204,10 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
   }
 }
 
-size_t sort_lds_bytes(int E, int Tk) { return (size_t)(((Tk + 3) & ~3) + 17 * E) * sizeof(int); }
+size_t sort_lds_bytes(int E, int Tk) {
+  (void)Tk;
+  return (size_t)(17 * E) * sizeof(int);
+}
 
 // ----------------------------------------------------------------- router
 

@@ -59,7 +59,7 @@ def test_workspace_bytes_layout():
 
 
 @pytest.mark.parametrize("kw", [dict(top_k=0), dict(top_k=17), dict(top_k=300, n_experts=256), dict(max_tokens=0),
-                                dict(max_tokens=257), dict(d=2040), dict(f=500), dict(norm_topk=2),
+                                dict(max_tokens=4097), dict(d=2040), dict(f=500), dict(norm_topk=2),
                                 dict(n_experts=2000), dict(d=0), dict(n_shared=2), dict(n_shared=-1)])
 def test_bad_shapes_have_no_workspace(kw):
     assert M.moe_decode_workspace_bytes(desc(**kw)) == 0
