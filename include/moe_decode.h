@@ -108,24 +108,27 @@ typedef struct {
 typedef struct moe_layer* moe_handle;
 
 /* Bytes of device workspace a layer with this shape needs (0 on a bad
- * shape).  The workspace holds router logits, the chosen experts, their
- * grouping by expert, the operand copies of the activations, the SwiGLU
- * activations and the per-assignment expert outputs of one call (for
- * max_tokens T: about T*k*(4d + 2f) + 6Td bytes, plus 32*E + 10*k*f bytes of
- * single-launch hand-off words and 6 KiB) and, for a
+ * shape).  The workspace holds the router's partial sums (at most about
+ * max(4*T*E bytes, 8 MiB)), the chosen experts, their grouping by expert,
+ * the operand copies of the activations, the SwiGLU activations and the
+ * per-assignment expert outputs of one call (for max_tokens T: about
+ * T*k*(4d + 2f) + 8Td bytes, plus 32*E + 10*k*f bytes of single-launch
+ * hand-off words and 6 KiB) and, for a
  * layer that may run the batched kernels (max_tokens > 1, or a shape the
  * single-launch kernel does not take), a tile-major copy of the gate, up and
  * down matrices, the shared expert's included (their size: 3*(E+n_shared)*
- * d*f/2 bytes of codes + 3*(E+n_shared)*d*f/16 of scales). */
+ * d*f/2 bytes of codes + 3*(E+n_shared)*d*f/16 of scales), and the router
+ * matrix as three bfloat16 terms whose sum is exactly W_r (6*E*d bytes, E
+ * rounded up to 16). */
 size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
 
 /* Validate the shape and weights and bind them, with a caller-owned device
  * workspace of at least moe_decode_workspace_bytes(desc) bytes, into a host
  * handle.  Clears the workspace once and, when the layer may run the
- * batched kernels, writes the tile-major copy of the expert matrices
- * (synchronously, on the null stream); batched calls read that copy, so
- * expert weights changed after init reach only the single-launch 1-token
- * step.  The handle owns no device memory.  One handle must not run on two streams
+ * batched kernels, writes the tile-major copy of the expert matrices and
+ * the router's bf16 terms (synchronously, on the null stream); batched
+ * calls read those copies, so router or expert weights changed after init
+ * reach only the single-launch 1-token step.  The handle owns no device memory.  One handle must not run on two streams
  * at once (its workspace is shared by its calls); distinct handles are
  * independent. */
 moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* weights,

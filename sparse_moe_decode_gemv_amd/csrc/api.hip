@@ -13,9 +13,10 @@ namespace {
 constexpr int kAbiVersion = 2;
 
 struct Layout {
-  size_t logits, sel_idx, sel_w, xp, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
+  size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
       hrec, epoch, cleared;                      // [0, cleared) is zeroed at init
   size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
+  size_t router_t;                                       // bf16 terms of the router matrix (same)
   size_t total;
 };
 
@@ -54,10 +55,16 @@ Layout layout_of(const moe_layer_desc* d) {
   size_t o = 0;
   const size_t Tk = T * k, d_ = (size_t)d->d, f_ = (size_t)d->f;
   const size_t Ta = Tk + ns * T;  // assignments, the shared expert's last
-  L.logits = o, o += align256(T * E * sizeof(float));
+  size_t part = 0;  // router partial sums: the most any T <= max_tokens needs
+  for (int t = 1; t <= d->max_tokens; ++t) {
+    const size_t n = moe::router_partial_floats(t, d->n_experts, d->d);
+    part = n > part ? n : part;
+  }
+  L.logits = o, o += align256(part * sizeof(float));
   L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
   L.sel_w = o, o += align256(Tk * sizeof(float));
   L.xp = o, o += align256(T * d_ * sizeof(uint16_t));
+  L.xn = o, o += align256(T * d_ * sizeof(uint16_t));
   L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
   L.act = o, o += align256(E * sizeof(int32_t));
   L.chunk_off = o, o += align256((E + 1) * sizeof(int32_t));
@@ -78,6 +85,7 @@ Layout layout_of(const moe_layer_desc* d) {
   L.up_ts = o, o += align256(cs);
   L.down_t = o, o += align256(cq);  // E*d*f/2 bytes as well
   L.down_ts = o, o += align256(cs);
+  L.router_t = o, o += align256(copy ? (E + 15) / 16 * 16 * d_ * 3 * sizeof(uint16_t) : 0);
   L.total = o;
   return L;
 }
@@ -174,6 +182,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
   a.xp = reinterpret_cast<uint16_t*>(base + L.xp);
+  a.xn = reinterpret_cast<uint16_t*>(base + L.xn);
   a.off = reinterpret_cast<int32_t*>(base + L.off);
   a.meta = a.off + desc->n_experts + 1;
   a.act = reinterpret_cast<int32_t*>(base + L.act);
@@ -194,6 +203,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.up_ts = copy ? reinterpret_cast<uint16_t*>(base + L.up_ts) : nullptr;
   a.down_t = copy ? base + L.down_t : nullptr;
   a.down_ts = copy ? reinterpret_cast<uint16_t*>(base + L.down_ts) : nullptr;
+  a.router_t = copy ? reinterpret_cast<uint16_t*>(base + L.router_t) : nullptr;
   h->fused = moe::fused_layer_supported(desc->d, desc->f, desc->n_experts, desc->top_k, desc->n_shared,
                                         moe::fused_grid());
   if (!h->fused && !copy) {  // a GPU with fewer CUs than the single-launch kernel assumes

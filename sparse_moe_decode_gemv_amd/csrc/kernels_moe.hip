@@ -1,12 +1,13 @@
 // kernels_moe.hip -- the decode step of a 4-bit MoE layer for T tokens on gfx950.
 //
-// Six kernels per call:
-//   router  : logits = W_r x (+b), one router row per wave, held in
-//             registers across a block of 4 tokens; workgroup 0 also writes
-//             each token's activations in MFMA operand order (fp16).  In the
-//             stack the router applies the pre-norm (RMSNorm) to the
-//             residual.
-//   top-k   : one wave per token: softmax + top-k.
+// Six kernels per call (seven in the stack, whose pre-norm kernel first
+// turns the residual into x):
+//   router  : logits = W_r x as a matrix product on the matrix cores (x
+//             against three exact bf16 terms of W_r), split over K into
+//             partial sums; the workgroups of expert tile 0 also write each
+//             token's activations in MFMA operand order (fp16).
+//   top-k   : one wave per token: the partial sums and bias added in a
+//             fixed order, then softmax + top-k.
 //   sort    : one workgroup of 16 waves: the T*k (token, slot) assignments
 //             grouped by expert (a stable counting sort built from wave
 //             ballots).
@@ -59,15 +60,35 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // Softmax + top-k of one token's E logits in one wave (topk.h): grid T,
 // block 64, one token per workgroup (one wave per SIMD of its own: a wave64
 // VALU instruction takes 4 cycles, so waves sharing a SIMD would serialize).
+// The logits are the S partial sums of the router (slice order) plus the
+// bias.
 template <int EPL, int KP>
-__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int32_t* __restrict__ idx_out,
+__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int T, int S, int32_t* __restrict__ idx_out,
                                              float* __restrict__ w_out) {
-  const int t = blockIdx.x, lane = threadIdx.x, E = a.E, k = a.k;
+  const int t = blockIdx.x, lane = threadIdx.x, E = a.E, k = a.k, E16 = (E + 15) & ~15;
+  constexpr int SU = EPL <= 4 ? 8 : 2;  // slices loaded at a time (all EPL * SU loads in flight)
+  const float* p = a.logits + (size_t)t * E16;
+  float l[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) l[i] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += SU) {
+    float q[EPL][SU];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+#pragma unroll
+      for (int u = 0; u < SU; ++u) q[i][u] = p[(size_t)min(s0 + u, S - 1) * T * E16 + min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if (s0 + u < S) l[i] += q[i][u];  // slice order
+  }
   float v[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const float l = a.logits[(size_t)t * E + min(lane + 64 * i, E - 1)];
-    v[i] = lane + 64 * i < E && l == l ? l : -INFINITY;
+    const int e = min(lane + 64 * i, E - 1);
+    const float li = a.router_b ? l[i] + a.router_b[e] : l[i];
+    v[i] = lane + 64 * i < E && li == li ? li : -INFINITY;
   }
   int se;
   float sw;
@@ -211,127 +232,203 @@ size_t sort_lds_bytes(int E, int Tk) {
 
 // ----------------------------------------------------------------- router
 
-constexpr int kRouterTokens = 4;  // tokens per router workgroup (16 measured slower)
-constexpr int kRouterSub = 4;     // tokens per activation prefetch group
+// Router logits of T tokens as one matrix product on the matrix cores:
+// logits[t][e] = sum_k x[t][k] W_r[e][k].  The fp32 router matrix is held
+// (from init) as three bfloat16 terms per weight, w = h + m + l exactly
+// (each term takes the next 8 significant bits of what the previous ones
+// left; exact for |w| >= 2^-100), so the three bf16 MFMAs per tile form
+// every product x * w exactly in fp32 and the only rounding is the fp32
+// accumulation, as in an fp32 dot product.  A workgroup computes 64 experts
+// (16 per wave) x 16*NB tokens over one slice of K (split K: enough
+// workgroups to fill the chip at any T); each slice's sums go to its own
+// partial array and the top-k kernel adds the slices and the bias in a
+// fixed order, so the result does not depend on timing.
+constexpr int kRtE = 64;       // experts per workgroup
+constexpr int kRtGrid = 256;   // workgroups aimed for (one per CU)
+constexpr int kRtMinK = 128;   // smallest K slice of one workgroup
+constexpr int kRtRow = 5;      // uint4 per staged token row: 4 of x (32 bf16) + 1 of padding
 
-// grid (ceil(E/4), ceil(T/4)), block 256: wave w of workgroup (b, c) holds
-// router row 4b + w in registers and computes its logit for tokens 4c ..
-// 4c+3, all 4 tokens' activations loaded before any is used.
+// 16-token blocks per workgroup: up to 8 (128 tokens), fewer for small T.
+int router_nb(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8; }
+
+int router_splits(int T, int E, int d) {
+  const int tt = 16 * router_nb(T);
+  const int tiles = ((T + tt - 1) / tt) * ((E + kRtE - 1) / kRtE);
+  int S = 1;
+  while (2 * S * tiles <= kRtGrid && 2 * S <= d / kRtMinK) S *= 2;
+  return S;
+}
+
+size_t router_partial_floats(int T, int E, int d) {
+  return (size_t)router_splits(T, E, d) * T * ((E + 15) & ~15);
+}
+
+// One thread per (16-row block eb, 32-column block kb, lane l): the weights
+// W_r[16eb + l%16][32kb + 8(l/16) + i], i = 0..7 (zero past row E), as their
+// three bf16 terms, stored as tiles [eb][kb][term][64 lanes] of uint4 (the
+// MFMA A-operand of lane l).
+__global__ __launch_bounds__(256) void k_router_terms(const float* __restrict__ w, int E, int d,
+                                                      uint4* __restrict__ out) {
+  const int nkb = d / 32;
+  const size_t n = (size_t)((E + 15) / 16) * nkb * 64;
+  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n) return;
+  const int l = (int)(g & 63);
+  const size_t tile = g >> 6;
+  const int kb = (int)(tile % nkb), eb = (int)(tile / nkb);
+  const int e = eb * 16 + (l & 15), k0 = kb * 32 + 8 * (l >> 4);
+  float v[8];
+  const float4* src = reinterpret_cast<const float4*>(w + (size_t)min(e, E - 1) * d + k0);
+  const float4 v0 = src[0], v1 = src[1];
+  v[0] = v0.x, v[1] = v0.y, v[2] = v0.z, v[3] = v0.w, v[4] = v1.x, v[5] = v1.y, v[6] = v1.z, v[7] = v1.w;
+  uint32_t th[4], tm[4], tl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = e < E ? v[2 * j] : 0.f, b = e < E ? v[2 * j + 1] : 0.f;
+    th[j] = pack_bf16(a, b);
+    const float ra = a - bf16_bits_to_f32(th[j] & 0xFFFFu), rb = b - __uint_as_float(th[j] & 0xFFFF0000u);
+    tm[j] = pack_bf16(ra, rb);
+    const float sa = ra - bf16_bits_to_f32(tm[j] & 0xFFFFu), sb = rb - __uint_as_float(tm[j] & 0xFFFF0000u);
+    tl[j] = pack_bf16(sa, sb);
+  }
+  out[(tile * 3 + 0) * 64 + l] = make_uint4(th[0], th[1], th[2], th[3]);
+  out[(tile * 3 + 1) * 64 + l] = make_uint4(tm[0], tm[1], tm[2], tm[3]);
+  out[(tile * 3 + 2) * 64 + l] = make_uint4(tl[0], tl[1], tl[2], tl[3]);
+}
+
+// Pre-norm of the stack: x_t = bf16(r_t / sqrt(mean(r_t^2) + eps)), one wave
+// per token.
 template <int D>
-__global__ __launch_bounds__(256) void k_router(const LayerArgs a, const uint16_t* __restrict__ x,
-                                                const float* __restrict__ resid, float eps, int T,
-                                                uint16_t* __restrict__ x_trace) {
-  constexpr int NI = D / 256;  // float4 columns per lane: 4*lane + 256*i
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
-  const bool row_ok = e < a.E;
-  const float4* wrow = reinterpret_cast<const float4*>(a.router_w + (size_t)min(e, a.E - 1) * D);
-  float4 w[NI];
+__global__ __launch_bounds__(64) void k_prenorm(const float* __restrict__ resid, float eps,
+                                                uint16_t* __restrict__ xn) {
+  constexpr int NI = D / 256;  // float4 per lane: columns 4*lane + 256*i
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float4* rr = reinterpret_cast<const float4*>(resid + (size_t)t * D);
+  float4 rv[NI];
+  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) w[i] = wrow[64 * i + lane];
-  const float bias = row_ok && a.router_b ? a.router_b[e] : 0.f;
+  for (int i = 0; i < NI; ++i) {
+    rv[i] = rr[64 * i + lane];
+    ss = fmaf(rv[i].x, rv[i].x, ss);
+    ss = fmaf(rv[i].y, rv[i].y, ss);
+    ss = fmaf(rv[i].z, rv[i].z, ss);
+    ss = fmaf(rv[i].w, rv[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  const float den = sqrtf(ss / (float)D + eps);
+  uint2* xr = reinterpret_cast<uint2*>(xn + (size_t)t * D);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    xr[64 * i + lane] = make_uint2(pack_bf16(rv[i].x / den, rv[i].y / den), pack_bf16(rv[i].z / den, rv[i].w / den));
+}
 
-  // bf16 activations in groups of 4 tokens, one group ahead (clamped to
-  // real tokens, so the loads are unconditional)
-  constexpr bool XPRE = NI <= 8;
-  uint2 xq[2][XPRE ? kRouterSub : 1][XPRE ? NI : 1];
-  const int t0 = blockIdx.y * kRouterTokens;
-  auto load_group = [&](uint2 (&dst)[XPRE ? kRouterSub : 1][XPRE ? NI : 1], int g) {
-    if constexpr (XPRE) {
+// One token's 8 activations of one chunk (bf16) as the fp16 MFMA operand
+// of the expert kernels, in the order (x0, x4, x1, x5, x2, x6, x3, x7).
+__device__ __forceinline__ uint4 operand_chunk(uint4 q) {
+  const float x0 = bf16_bits_to_f32(q.x & 0xFFFFu), x1 = __uint_as_float(q.x & 0xFFFF0000u);
+  const float x2 = bf16_bits_to_f32(q.y & 0xFFFFu), x3 = __uint_as_float(q.y & 0xFFFF0000u);
+  const float x4 = bf16_bits_to_f32(q.z & 0xFFFFu), x5 = __uint_as_float(q.z & 0xFFFF0000u);
+  const float x6 = bf16_bits_to_f32(q.w & 0xFFFFu), x7 = __uint_as_float(q.w & 0xFFFF0000u);
+  return make_uint4(pack_f16(x0, x4), pack_f16(x1, x5), pack_f16(x2, x6), pack_f16(x3, x7));
+}
+
+// grid = ceil(E/64) * ceil(T/(16 NB)) * S workgroups of 256.  Wave w holds
+// the A operands (16 experts x 32 k, three terms) of its expert block; the
+// workgroup stages its 16 NB tokens' x (32 k per step) in LDS, double
+// buffered, and each wave reads its B operands (16 tokens x 32 k) there.
+// Rows past T hold token T-1 again (loads clamped); their sums are not
+// stored.  Lane l ends with the logits of token 16j + l%16, experts
+// 4(l/16) .. +3 of its block.  The workgroups of expert tile 0 also write
+// each token's fp16 operand row xp for the expert kernels.
+template <int NB>
+__global__ __launch_bounds__(256) void k_router_mm(const LayerArgs a, const uint16_t* __restrict__ x, int T,
+                                                   int S) {
+  constexpr int TT = 16 * NB;                  // tokens per workgroup
+  constexpr int NC = (4 * TT + 255) / 256;     // staged 16-byte chunks per thread and step
+  __shared__ uint4 s_x[2][TT * kRtRow];
+  const int d = a.d, E16 = (a.E + 15) & ~15, nkb = d / 32;
+  const int NET = (a.E + kRtE - 1) / kRtE, NTT = (T + TT - 1) / TT;
+  // consecutive work items on one XCD (blocks go round-robin over the 8 XCDs)
+  const int N = gridDim.x, bi = blockIdx.x;
+  const int w = (N & 7) == 0 ? (bi & 7) * (N >> 3) + (bi >> 3) : bi;
+  const int et = w % NET, tt = (w / NET) % NTT, sk = w / (NET * NTT);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool eb_ok = et * 4 + wave < E16 / 16;
+  const int eb = min(et * 4 + wave, E16 / 16 - 1);
+  const int nk = nkb / S, kb0 = sk * nk;
+  const int t0 = tt * TT;
+
+  const uint4* wa = reinterpret_cast<const uint4*>(a.router_t) + ((size_t)eb * nkb + kb0) * 192 + lane;
+  // staging: chunk c = threadIdx.x + 256 i is chunk c%4 of token row c/4
+  const bool st_ok = 4 * TT >= 256 || (int)threadIdx.x < 4 * TT;
+  const uint4* xs[NC];
+  uint4* ps[NC];
+  bool pw[NC];
 #pragma unroll
-      for (int tb = 0; tb < kRouterSub; ++tb) {
-        const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)min(t0 + g * kRouterSub + tb, T - 1) * D);
+  for (int i = 0; i < NC; ++i) {
+    const int c = threadIdx.x + 256 * i, t = t0 + c / 4;
+    xs[i] = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * d + kb0 * 32) + (c & 3);
+    ps[i] = reinterpret_cast<uint4*>(a.xp + (size_t)min(t, T - 1) * d + kb0 * 32) + (c & 3);
+    pw[i] = et == 0 && st_ok && t < T;
+  }
+
+  // operands of 4 steps in flight (a ring of register slots; nk is a
+  // multiple of 4): step ks + 4 is loaded into the slot step ks has used.
+  // Past the end the loads repeat the last step (unconditional loads).
+  uint4 Ar[4][3], Xr[4][NC];
+  auto load = [&](uint4 (&A)[3], uint4 (&X)[NC], int ks) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) dst[tb][i] = xr[64 * i + lane];
-      }
+    for (int i = 0; i < NC; ++i) X[i] = xs[i][ks * 4];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) A[p] = wa[(size_t)ks * 192 + p * 64];
+  };
+  auto stage = [&](int buf, const uint4 (&X)[NC], int ks) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      if (st_ok) s_x[buf][(c >> 2) * kRtRow + (c & 3)] = X[i];
+      if (pw[i]) ps[i][ks * 4] = operand_chunk(X[i]);
     }
   };
-  if (x) load_group(xq[0], 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load(Ar[u], Xr[u], u);
+  stage(0, Xr[0], 0);
+  __syncthreads();
 
+  f32x4_t acc[NB];
 #pragma unroll
-  for (int g = 0; g < kRouterTokens / kRouterSub; ++g) {
-    if (t0 + g * kRouterSub >= T) break;
-    if (x && g + 1 < kRouterTokens / kRouterSub) load_group(xq[(g + 1) & 1], g + 1);
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ks0 = 0; ks0 < nk; ks0 += 4) {
 #pragma unroll
-  for (int tq = 0; tq < kRouterSub; ++tq) {
-    const int tb = g * kRouterSub + tq;
-    const int t = t0 + tb;
-    if (t >= T) break;
-    float xv[NI][4];
-    if (x) {
-      const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)t * D);
+    for (int u = 0; u < 4; ++u) {
+      const int ks = ks0 + u;
+      const uint4* sb = s_x[u & 1];
+      uint4 B[NB];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        uint2 q;
-        if constexpr (XPRE) q = xq[g & 1][tq][i];
-        else q = xr[64 * i + lane];
-        xv[i][0] = bf16_bits_to_f32(q.x & 0xFFFFu);
-        xv[i][1] = bf16_bits_to_f32(q.x >> 16);
-        xv[i][2] = bf16_bits_to_f32(q.y & 0xFFFFu);
-        xv[i][3] = bf16_bits_to_f32(q.y >> 16);
-      }
-    } else {
-      // pre-norm: x = bf16(r / sqrt(mean(r^2) + eps))
-      const float4* rr = reinterpret_cast<const float4*>(resid + (size_t)t * D);
-      float4 rv[NI];
-      float ss = 0.f;
+      for (int j = 0; j < NB; ++j) B[j] = sb[(16 * j + (lane & 15)) * kRtRow + (lane >> 4)];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        rv[i] = rr[64 * i + lane];
-        ss = fmaf(rv[i].x, rv[i].x, ss);
-        ss = fmaf(rv[i].y, rv[i].y, ss);
-        ss = fmaf(rv[i].z, rv[i].z, ss);
-        ss = fmaf(rv[i].w, rv[i].w, ss);
-      }
-      ss = wave_sum(ss);
-      const float den = sqrtf(ss / (float)D + eps);
+      for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const uint32_t b0 = f32_to_bf16_bits(rv[i].x / den), b1 = f32_to_bf16_bits(rv[i].y / den);
-        const uint32_t b2 = f32_to_bf16_bits(rv[i].z / den), b3 = f32_to_bf16_bits(rv[i].w / den);
-        xv[i][0] = bf16_bits_to_f32(b0);
-        xv[i][1] = bf16_bits_to_f32(b1);
-        xv[i][2] = bf16_bits_to_f32(b2);
-        xv[i][3] = bf16_bits_to_f32(b3);
-        if (x_trace && blockIdx.x == 0 && wave == tq)
-          reinterpret_cast<uint2*>(x_trace + (size_t)t * D)[64 * i + lane] =
-              make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-      }
-    }
-
-    if (blockIdx.x == 0 && wave == tq) {
-      // The token's MFMA operand row: fp16, each chunk of 8 elements stored
-      // as (x0, x4, x1, x5, x2, x6, x3, x7); lane 2m holds x0..x3 of a chunk
-      // and lane 2m+1 holds x4..x7, so neighbours trade halves.
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float o0 = dpp_f<kDppXor1>(xv[i][0]), o1 = dpp_f<kDppXor1>(xv[i][1]);
-        const float o2 = dpp_f<kDppXor1>(xv[i][2]), o3 = dpp_f<kDppXor1>(xv[i][3]);
-        uint2 pk;
-        if ((lane & 1) == 0) {
-          pk.x = pack_f16(xv[i][0], o0);
-          pk.y = pack_f16(xv[i][1], o1);
-        } else {
-          pk.x = pack_f16(o2, xv[i][2]);
-          pk.y = pack_f16(o3, xv[i][3]);
-        }
-        reinterpret_cast<uint2*>(a.xp + (size_t)t * D)[64 * i + lane] = pk;
-      }
-    }
-
-    if (row_ok) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        acc = fmaf(w[i].x, xv[i][0], acc);
-        acc = fmaf(w[i].y, xv[i][1], acc);
-        acc = fmaf(w[i].z, xv[i][2], acc);
-        acc = fmaf(w[i].w, xv[i][3], acc);
-      }
-      acc = wave_sum(acc) + bias;
-      if (lane == 0) a.logits[(size_t)t * a.E + e] = acc;
+        for (int j = 0; j < NB; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Ar[u][p]),
+                                                           __builtin_bit_cast(bf16x8_t, B[j]), acc[j], 0, 0, 0);
+      // the next step's x into the other buffer (the last step restages its own)
+      stage((u + 1) & 1, Xr[(u + 1) & 3], min(ks + 1, nk - 1));
+      __syncthreads();
+      load(Ar[u], Xr[u], min(ks + 4, nk - 1));
     }
   }
+
+  if (eb_ok) {
+    float* part = a.logits + (size_t)sk * T * E16 + eb * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = t0 + 16 * j + (lane & 15);
+      if (t < T) {
+        const f32x4_t v = acc[j];
+        *reinterpret_cast<float4*>(part + (size_t)t * E16) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
   }
 }
 
@@ -671,42 +768,52 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf,
 // ----------------------------------------------------------------- launchers
 
 template <int D>
-static void router_inst(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T, uint16_t* xt,
-                        hipStream_t s) {
-  hipLaunchKernelGGL((k_router<D>), dim3((a.E + 3) / 4, (T + kRouterTokens - 1) / kRouterTokens), dim3(256), 0, s,
-                     a, x, r, eps, T, xt);
+static void prenorm_inst(const float* r, float eps, int T, uint16_t* xn, hipStream_t s) {
+  hipLaunchKernelGGL((k_prenorm<D>), dim3(T), dim3(64), 0, s, r, eps, xn);
 }
 
 template <int EPL>
-static void topk_inst(const LayerArgs& a, int T, int32_t* idx_out, float* w_out, hipStream_t s) {
+static void topk_inst(const LayerArgs& a, int T, int S, int32_t* idx_out, float* w_out, hipStream_t s) {
   if (a.k <= 8)
-    hipLaunchKernelGGL((k_topk<EPL, 8>), dim3(T), dim3(64), 0, s, a, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<EPL, 8>), dim3(T), dim3(64), 0, s, a, T, S, idx_out, w_out);
   else
-    hipLaunchKernelGGL((k_topk<EPL, 16>), dim3(T), dim3(64), 0, s, a, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<EPL, 16>), dim3(T), dim3(64), 0, s, a, T, S, idx_out, w_out);
 }
 
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
                          int32_t* idx_out, float* w_out, uint16_t* x_trace, hipStream_t s) {
-  switch (a.d) {
-    case 256: router_inst<256>(a, x, r, eps, T, x_trace, s); break;
-    case 512: router_inst<512>(a, x, r, eps, T, x_trace, s); break;
-    case 1024: router_inst<1024>(a, x, r, eps, T, x_trace, s); break;
-    case 2048: router_inst<2048>(a, x, r, eps, T, x_trace, s); break;
-    case 4096: router_inst<4096>(a, x, r, eps, T, x_trace, s); break;
-    case 8192: router_inst<8192>(a, x, r, eps, T, x_trace, s); break;
-    default: return hipErrorInvalidValue;
+  if (!x) {  // the stack: pre-norm of the residual first
+    uint16_t* xn = x_trace ? x_trace : a.xn;
+    switch (a.d) {
+      case 256: prenorm_inst<256>(r, eps, T, xn, s); break;
+      case 512: prenorm_inst<512>(r, eps, T, xn, s); break;
+      case 1024: prenorm_inst<1024>(r, eps, T, xn, s); break;
+      case 2048: prenorm_inst<2048>(r, eps, T, xn, s); break;
+      case 4096: prenorm_inst<4096>(r, eps, T, xn, s); break;
+      case 8192: prenorm_inst<8192>(r, eps, T, xn, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    x = xn;
+  }
+  const int S = router_splits(T, a.E, a.d), nb = router_nb(T);
+  const int grid = ((a.E + kRtE - 1) / kRtE) * ((T + 16 * nb - 1) / (16 * nb)) * S;
+  switch (nb) {
+    case 1: hipLaunchKernelGGL((k_router_mm<1>), dim3(grid), dim3(256), 0, s, a, x, T, S); break;
+    case 2: hipLaunchKernelGGL((k_router_mm<2>), dim3(grid), dim3(256), 0, s, a, x, T, S); break;
+    case 4: hipLaunchKernelGGL((k_router_mm<4>), dim3(grid), dim3(256), 0, s, a, x, T, S); break;
+    default: hipLaunchKernelGGL((k_router_mm<8>), dim3(grid), dim3(256), 0, s, a, x, T, S); break;
   }
   const int epl = (a.E + 63) / 64;
   if (epl <= 1)
-    topk_inst<1>(a, T, idx_out, w_out, s);
+    topk_inst<1>(a, T, S, idx_out, w_out, s);
   else if (epl <= 2)
-    topk_inst<2>(a, T, idx_out, w_out, s);
+    topk_inst<2>(a, T, S, idx_out, w_out, s);
   else if (epl <= 4)
-    topk_inst<4>(a, T, idx_out, w_out, s);
+    topk_inst<4>(a, T, S, idx_out, w_out, s);
   else if (epl <= 8)
-    topk_inst<8>(a, T, idx_out, w_out, s);
+    topk_inst<8>(a, T, S, idx_out, w_out, s);
   else
-    topk_inst<16>(a, T, idx_out, w_out, s);
+    topk_inst<16>(a, T, S, idx_out, w_out, s);
   const size_t lds = sort_lds_bytes(a.E, T * a.k);
   if (lds > 64 * 1024) {
     static bool raised = false;
@@ -772,6 +879,10 @@ static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq,
 hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
   const long long E = a.E;
   hipError_t e;
+  const size_t nt = (size_t)((E + 15) / 16) * (a.d / 32) * 64;
+  hipLaunchKernelGGL(k_router_terms, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a.router_w, a.E, a.d,
+                     reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.router_t)));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = tile_matrix(a.gate_q, a.gate_s, const_cast<uint8_t*>(a.gate_t), const_cast<uint16_t*>(a.gate_ts),
                        E * a.f, a.d, s)) != hipSuccess)
     return e;

@@ -34,8 +34,12 @@ struct LayerArgs {
   const uint16_t* up_ts;
   const uint8_t* down_t;
   const uint16_t* down_ts;
+  // three bf16 terms of the router matrix (h + m + l = W_r), MFMA tiles
+  // [ceil(E/16)][d/32][term][64 lanes][8] (batched path)
+  const uint16_t* router_t;
   // workspace of the batched path
-  float* logits;          // [T][E]
+  float* logits;          // [S][T][E16] router partial sums of S slices of K, E16 = E rounded up to 16
+  uint16_t* xn;           // [T][d] pre-normed activations of a stack layer (bf16), unless x_trace holds them
   int32_t* sel_idx;       // [T][k] chosen experts of assignment t*k + j
   float* sel_w;           // [T][k] their weights
   uint16_t* xp;           // [T][d] activations in MFMA operand order (fp16)
@@ -98,12 +102,18 @@ bool fused_layer_supported(int d, int f, int E, int k, int ns, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
 
-// Router GEMV for T tokens, then (a second kernel) softmax + top-k of
-// every token and the assignments grouped by expert.  Activations come either from x (bf16 [T][d]) or, when x is
-// NULL, from the fp32 residual r [T][d] normalized by RMSNorm (eps), in
-// which case x_l is also written to x_trace when it is non-NULL.
+// Router logits of T tokens (a matrix product), then softmax + top-k of
+// every token and the assignments grouped by expert.  Activations come
+// either from x (bf16 [T][d]) or, when x is NULL, from the fp32 residual
+// r [T][d] normalized by RMSNorm (eps), written to x_trace when it is
+// non-NULL (else to the workspace).
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
                          int32_t* idx_out, float* w_out, uint16_t* x_trace, hipStream_t s);
+
+// Slices of K the router splits its sum into for T tokens, and the floats
+// of its partial sums (logits workspace).
+int router_splits(int T, int E, int d);
+size_t router_partial_floats(int T, int E, int d);
 
 // Per chosen expert, over all its tokens: h = w_j * silu(W_g x) * (W_u x).
 hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s);
@@ -111,7 +121,8 @@ hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s);
 // Per chosen expert, over all its tokens: o_{t,j} = W_d h.
 hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s);
 
-// The tile-major copies of gate, up and down (from the canonical matrices).
+// The tile-major copies of gate, up and down (from the canonical matrices)
+// and the router's bf16 terms.
 hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s);
 
 // y_t = sum_j o_{t,j} (+ o_{t,shared}) into y_out (if non-NULL); residual_t += y_t (if non-NULL).
