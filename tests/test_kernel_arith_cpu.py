@@ -6,7 +6,9 @@ emulated bit for bit in numpy, so a wrong constant there fails here, on the
 CPU, before any GPU run.  Each code u at each of the 8 positions of a dword
 must decode to an exact bf16 value, and the four pair products plus the
 correction must equal sum_e (u_e - 8) x_e exactly (fp64 arithmetic on bf16
-inputs is exact here)."""
+inputs is exact here).  The batched router's three bf16 terms of each fp32
+router weight must sum to it exactly, and their products with bf16
+activations must be exact in fp32."""
 import os
 import re
 
@@ -158,3 +160,58 @@ def test_fp16_identity_on_random_codes_and_activations():
     np.testing.assert_allclose(acc, want, rtol=0, atol=1e-9 * np.abs(h_eff).sum(axis=1).max())
     # and the fp16 rounding of h stays within 2^-11 relative of the fp32 value
     assert np.all(np.abs(h_eff - h) <= np.abs(h) * 2.0 ** -11 + 2.0 ** -24 * 16)
+
+
+def _bf16_rne(a):
+    """fp32 -> bf16 (as fp32 values), round to nearest even, as v_cvt_pk_bf16_f32 (finite inputs)."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _router_terms(w):
+    """The batched router's three bf16 terms of an fp32 weight, each from what the
+    previous ones left, every step in fp32 as in k_router_terms."""
+    w = np.asarray(w, dtype=np.float32)
+    h = _bf16_rne(w)
+    r1 = (w - h).astype(np.float32)
+    m = _bf16_rne(r1)
+    r2 = (r1 - m).astype(np.float32)
+    lo = _bf16_rne(r2)
+    return h, m, lo, r2
+
+
+def test_router_terms_sum_exactly_to_the_weight():
+    """h + m + l == w exactly (so the three bf16 MFMAs see every router weight
+    whole) over router-like N(0, 0.02) weights, a wide exponent range, and
+    weights at bf16 rounding ties; and each term is a bf16 value."""
+    rng = np.random.default_rng(7)
+    w = np.concatenate([
+        rng.normal(0, 0.02, 200000),
+        rng.choice([-1.0, 1.0], 50000) * rng.uniform(1, 2, 50000) * 2.0 ** rng.integers(-100, 100, 50000),
+        # ties: a bf16 value plus exactly half of its last place (and neighbours)
+        (_bf16_rne(rng.normal(0, 1, 20000).astype(np.float32)).astype(np.float64)
+         * (1 + 2.0 ** -8 * np.array([1.0, 1 + 2.0 ** -15, 1 - 2.0 ** -15]).repeat(20000)[:20000])),
+    ]).astype(np.float32)
+    h, m, lo, r2 = _router_terms(w)
+    for t in (h, m, lo):
+        assert np.all((t.view(np.uint32) & 0xFFFF) == 0)
+    assert np.array_equal(lo, r2), "the third term must take the remainder whole"
+    assert np.array_equal(h.astype(np.float64) + m.astype(np.float64) + lo.astype(np.float64), w.astype(np.float64))
+    # below 2^-100 the last term can fall under bf16's normal range: an
+    # absolute error below 2^-133, far under any logit's rounding
+    tiny = (rng.uniform(1, 2, 10000) * 2.0 ** rng.integers(-126, -100, 10000)).astype(np.float32)
+    h, m, lo, _ = _router_terms(tiny)
+    err = np.abs(h.astype(np.float64) + m + lo - tiny.astype(np.float64))
+    assert err.max() < 2.0 ** -133
+
+
+def test_router_term_products_are_exact_in_fp32():
+    """x (bf16) times a bf16 term has at most 16 significant bits: exact in fp32,
+    so the MFMA's only rounding is its fp32 accumulation."""
+    rng = np.random.default_rng(8)
+    x = _bf16_rne(rng.normal(0, 1, 100000).astype(np.float32))
+    h, m, lo, _ = _router_terms(rng.normal(0, 0.02, 100000).astype(np.float32))
+    for t in (h, m, lo):
+        p64 = x.astype(np.float64) * t.astype(np.float64)
+        assert np.array_equal(p64.astype(np.float32).astype(np.float64), p64)
