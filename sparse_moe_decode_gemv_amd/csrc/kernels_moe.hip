@@ -120,9 +120,9 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 //   off[e] .. off[e+1]-1  positions of expert e in asg (off[E] = Tk)
 //   asg[p]                the assignment at position p
 //   act[i], i < meta[0]   the experts with at least one assignment, ascending
-//   chunk_off[i]          32-token chunks of the active experts before act[i]
-//                         (chunk_off[meta[0]] = all routed chunks)
-//   chunks[c]             chunk c: (expert, first position, positions <= 32)
+//   chunk_off[i]          CS-token chunks of the active experts before act[i]
+//                         (chunk_off[meta[0]] = all routed chunks), CS = 32 or 64
+//   chunks[c]             chunk c: (expert, first position, positions <= CS)
 //   meta[1], meta[2]      all chunks, Tk
 // With a shared expert, its T assignments Tk + t sit at positions Tk + t and
 // its chunks (expert index E) follow the routed ones.
@@ -131,7 +131,7 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 // waves gives each (wave, expert) its base, and each wave places its own
 // assignments in order: stable, deterministic, no atomics.
 // LDS (dynamic): sel [Tk], cnt [16][E], tot [E].
-__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
+__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS) {
   extern __shared__ int sm[];
   const int E = a.E, Tk = T * a.k;
   int* cnt = sm;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
       const int n = tot[e];
       s += n;
       na += n > 0;
-      nc += (n + 31) >> 5;
+      nc += (n + CS - 1) / CS;
     }
     int base = s, abase = na, cbase = nc;
 #pragma unroll
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
         a.act[abase] = e;
         a.chunk_off[abase] = cbase;
         ++abase;
-        for (int tc = 0; tc < n; tc += 32) a.chunks[cbase++] = make_int4(e, base + tc, min(32, n - tc), 0);
+        for (int tc = 0; tc < n; tc += CS) a.chunks[cbase++] = make_int4(e, base + tc, min(CS, n - tc), 0);
       }
       tot[e] = base;  // from here on: the first position of expert e
       base += n;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
       a.meta[0] = abase;
       // the shared expert (expert index E of the tile-major copies) takes
       // every token, in chunks after the routed ones
-      for (int tc = 0; tc < a.ns * T; tc += 32) a.chunks[cbase++] = make_int4(E, Tk + tc, min(32, T - tc), 0);
+      for (int tc = 0; tc < a.ns * T; tc += CS) a.chunks[cbase++] = make_int4(E, Tk + tc, min(CS, T - tc), 0);
       a.meta[1] = cbase;
       a.meta[2] = Tk;
     }
@@ -224,6 +224,10 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T) {
     lds_wait();
   }
 }
+
+// Tokens per chunk of the expert kernels: 64 once the experts average 32
+// or more assignments (each weight dequantized once per 64 tokens), else 32.
+int chunk_rows(const LayerArgs& a, int T) { return (long long)T * a.k >= 32LL * a.E ? 64 : 32; }
 
 size_t sort_lds_bytes(int E, int Tk) {
   (void)Tk;
@@ -470,53 +474,75 @@ __device__ __forceinline__ f16x2_t scale2(uint2 sc, int j) {
 
 // ----------------------------------------------------------------- grouped items
 
-// Work item of one workgroup: (chunk of up to 32 positions of one expert,
-// group of weight rows); item w is chunk w / ngroups, row group w % ngroups,
-// so the row groups of a chunk are consecutive.  The chunk table is read
+// Work item of one workgroup: (chunk of up to 32 or 64 positions of one
+// expert, group of weight rows).  The chunk list (grouped by expert) is cut
+// into 8 contiguous ranges, one per XCD (workgroups go round-robin over the
+// 8 XCDs, and the grid is a multiple of 8), so the row groups of a chunk
+// share one L2 for its activations, and the chunks of an expert share it
+// for the weights (but at the 7 cuts).  Within an XCD, item i is chunk
+// i / ngroups of the range, row group i % ngroups.  The chunk table is read
 // directly (one round trip from the start of the kernel to the operand
 // loads' addresses).
 struct Item {
   int e, rg, p0, n;
 };
-__device__ __forceinline__ Item item_of(const LayerArgs& a, int ngroups, int w) {
-  const int c = w / ngroups;
-  const int4 cd = a.chunks[c];
+struct ItemRange {
+  int c0, n, step;  // first chunk, items, item stride of this workgroup
+};
+__device__ __forceinline__ ItemRange xcd_items(const LayerArgs& a, int ngroups) {
+  const int C = a.meta[1], x = blockIdx.x & 7;
+  const int c0 = x * C / 8, c1 = (x + 1) * C / 8;
+  return ItemRange{c0, (c1 - c0) * ngroups, (int)gridDim.x >> 3};
+}
+__device__ __forceinline__ Item item_of(const LayerArgs& a, const ItemRange& r, int ngroups, int i) {
+  const int c = i / ngroups;
+  const int4 cd = a.chunks[r.c0 + c];
   Item it;
   it.e = cd.x;
   it.p0 = cd.y;
   it.n = cd.z;
-  it.rg = w - c * ngroups;
+  it.rg = i - c * ngroups;
   return it;
 }
 
-// The operand rows of one 128-element block of K for the item's (up to) 32
-// rows (tokens or positions), in LDS in fragment order: v[tt][j][q][slot]
-// is chunk q of group j of row 16*tt + r, at slot r ^ swz(j, q), so that
-// the 64 lanes of a wave read one (tt, j) as 1 KB with every 16 lanes
-// covering all banks, and the staging stores (8 rows x 8 parts per wave)
-// hit distinct banks too.
+// The operand rows of one 128-element block of K for the item's (up to)
+// 16*NTT rows (tokens or positions), in LDS in fragment order:
+// v[tt][j][q][slot] is chunk q of group j of row 16*tt + r, at slot
+// r ^ swz(j, q), so that the 64 lanes of a wave read one (tt, j) as 1 KB
+// with every 16 lanes covering all banks, and the staging stores (8 rows x
+// 8 parts per wave) hit distinct banks too.
+template <int NTT>
 struct OpTile {
-  uint4 v[2][4][4][16];
+  uint4 v[NTT][4][4][16];
 };
 __device__ __forceinline__ int swz(int j, int q) { return (4 * j + 2 * (q >> 1)) & 15; }
 
 // Thread i stages 32 bytes (16 elements: group p/2, chunks 2(p%2) and
-// 2(p%2)+1) of row c = i/8, part p = i%8.
+// 2(p%2)+1) of row c = i/8 + 32 m, part p = i%8, for each pass m < NTT/2.
+template <int NP>
 struct StageRegs {
-  uint4 a, b;
+  uint4 a[NP], b[NP];
 };
-__device__ __forceinline__ StageRegs stage_load(int blk, const uint16_t* row_c, int tid) {
-  const uint4* src = reinterpret_cast<const uint4*>(row_c + blk * 128 + 16 * (tid & 7));
-  StageRegs r;
-  r.a = src[0];
-  r.b = src[1];
+template <int NP>
+__device__ __forceinline__ StageRegs<NP> stage_load(int blk, const uint16_t* const (&rows)[NP], int tid) {
+  StageRegs<NP> r;
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    const uint4* src = reinterpret_cast<const uint4*>(rows[m] + blk * 128 + 16 * (tid & 7));
+    r.a[m] = src[0];
+    r.b[m] = src[1];
+  }
   return r;
 }
-__device__ __forceinline__ void stage_store(OpTile& t, const StageRegs& r, int tid) {
-  const int c = tid >> 3, p = tid & 7;
-  const int j = p >> 1, q0 = 2 * (p & 1), r16 = c & 15;
-  t.v[c >> 4][j][q0][r16 ^ swz(j, q0)] = r.a;
-  t.v[c >> 4][j][q0 + 1][r16 ^ swz(j, q0 + 1)] = r.b;
+template <int NTT>
+__device__ __forceinline__ void stage_store(OpTile<NTT>& t, const StageRegs<NTT / 2>& r, int tid) {
+  const int p = tid & 7, j = p >> 1, q0 = 2 * (p & 1);
+#pragma unroll
+  for (int m = 0; m < NTT / 2; ++m) {
+    const int c = (tid >> 3) + 32 * m, r16 = c & 15;
+    t.v[c >> 4][j][q0][r16 ^ swz(j, q0)] = r.a[m];
+    t.v[c >> 4][j][q0 + 1][r16 ^ swz(j, q0 + 1)] = r.b[m];
+  }
 }
 
 // Tile-major copy of an expert matrix [R rows][K] (made once at init for
@@ -558,10 +584,11 @@ __device__ __forceinline__ WBlk wload(const uint4* tq, const uint2* ts, int blk,
   return w;
 }
 
-// One block of K for two weight tiles against NTT (1 or 2) staged token tiles.
+// One block of K for two weight tiles against the NTT staged token tiles:
+// each weight dword is dequantized once and used by NTT MFMAs.
 template <int NTT>
-__device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][2], const OpTile& t, const WBlk (&w)[2], int lane,
-                                           uint32_t magic) {
+__device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<NTT>& t, const WBlk (&w)[2],
+                                           int lane, uint32_t magic) {
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -586,23 +613,22 @@ __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][2], const OpTile& t
 // are clamped to a real one and their outputs dropped), so the compiler's
 // wait counts stay exact.
 template <int K, int NTT>
-__device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, const uint16_t* op_row,
-                                       const uint4* const (&wtq)[2], const uint2* const (&wts)[2], int tid, int lane,
-                                       uint32_t magic) {
+__device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tiles,
+                                       const uint16_t* const (&op_rows)[NTT / 2], const uint4* const (&wtq)[2],
+                                       const uint2* const (&wts)[2], int tid, int lane, uint32_t magic) {
   constexpr int NBLK = K / 128;
   constexpr int G = NBLK < 4 ? NBLK : 4;    // weight blocks per burst
   constexpr int SX = NBLK < 2 ? NBLK : 2;   // operand blocks in flight
-  const int q = lane >> 4;
-  StageRegs sx[SX];
+  StageRegs<NTT / 2> sx[SX];
 #pragma unroll
-  for (int i = 0; i < SX; ++i) sx[i] = stage_load(i, op_row, tid);
+  for (int i = 0; i < SX; ++i) sx[i] = stage_load(i, op_rows, tid);
   WBlk w[2][G][2];
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
     for (int m = 0; m < 2; ++m) w[0][i][m] = wload(wtq[m], wts[m], i, lane);
   stage_store(tiles[0], sx[0], tid);
-  sx[0] = stage_load(min(SX, NBLK - 1), op_row, tid);
+  sx[0] = stage_load(min(SX, NBLK - 1), op_rows, tid);
   __syncthreads();
   for (int b0 = 0; b0 < NBLK; b0 += 2 * G) {
 #pragma unroll
@@ -623,7 +649,7 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, cons
           block_mfma<NTT>(acc, tiles[b & 1], w[h][i], lane, magic);
           // slot (b+1) % SX holds block b+1: into the other LDS buffer, then refill
           stage_store(tiles[(b + 1) & 1], sx[(b + 1) % SX], tid);
-          sx[(b + 1) % SX] = stage_load(min(b + 1 + SX, NBLK - 1), op_row, tid);
+          sx[(b + 1) % SX] = stage_load(min(b + 1 + SX, NBLK - 1), op_rows, tid);
           __syncthreads();
         }
       }
@@ -633,41 +659,45 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][2], OpTile* tiles, cons
 
 // ----------------------------------------------------------------- gate/up
 
-// Item: (chosen expert, 64 rows of f, up to 32 tokens).  Wave w takes gate
-// and up rows 16w .. 16w+15 of the group; K = d.  Epilogue in registers: h =
-// w_j * silu(g) * u, written as fp16 in operand order (0,4,1,5,2,6,3,7
-// within each 8 rows) for the down step.
-template <int D>
+// Item: (chosen expert, 64 rows of f, up to 16*NTT tokens).  Wave w takes
+// gate and up rows 16w .. 16w+15 of the group; K = d.  Epilogue in
+// registers: h = w_j * silu(g) * u, written as fp16 in operand order
+// (0,4,1,5,2,6,3,7 within each 8 rows) for the down step.
+template <int D, int NTT>
 __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
-  constexpr int G = D / 32;
-  __shared__ OpTile s_tile[2];
+  __shared__ OpTile<NTT> s_tile[2];
   const int f = a.f, k = a.k, ngroups = f / 64;
-  const int total = ngroups * a.meta[1];
+  const ItemRange ir = xcd_items(a, ngroups);
   const uint32_t magic = magic_f16x2();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const Item it = item_of(a, ngroups, w);
-    const int ntt = it.n > 16 ? 2 : 1;
+  for (int i = blockIdx.x >> 3; i < ir.n; i += ir.step) {
+    const Item it = item_of(a, ir, ngroups, i);
     const size_t tile = (size_t)it.e * (f / 16) + it.rg * 4 + wave;  // 16-row tile of gate and of up
     const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.gate_t) + tile * (D / 128) * 64,
                            reinterpret_cast<const uint4*>(a.up_t) + tile * (D / 128) * 64};
     const uint2* wts[2] = {reinterpret_cast<const uint2*>(a.gate_ts) + tile * (D / 128) * 16,
                            reinterpret_cast<const uint2*>(a.up_ts) + tile * (D / 128) * 16};
-    // the operand row this thread stages: token of chunk row tid/8
+    // the operand rows this thread stages: tokens of chunk rows tid/8 + 32m
     const int Tk = a.meta[2];
-    const int asg0 = a.asg[it.p0 + min(tid >> 3, it.n - 1)];
-    const int tok = asg0 < Tk ? asg0 / k : asg0 - Tk;  // shared-expert assignments: Tk + token
-    f32x4_t acc[2][2];
-    acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // both token tiles always (for a chunk of up to 16 rows the second tile
-    // repeats a real row and its outputs are dropped): one code path
-    k_loop<D, 2>(acc, s_tile, a.xp + (size_t)tok * D, wtq, wts, tid, lane, magic);
+    const uint16_t* rows[NTT / 2];
+#pragma unroll
+    for (int m = 0; m < NTT / 2; ++m) {
+      const int asg0 = a.asg[it.p0 + min((tid >> 3) + 32 * m, it.n - 1)];
+      const int tok = asg0 < Tk ? asg0 / k : asg0 - Tk;  // shared-expert assignments: Tk + token
+      rows[m] = a.xp + (size_t)tok * D;
+    }
+    f32x4_t acc[2][NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // all token tiles always (rows past the chunk repeat a real row and
+    // their outputs are dropped): one code path
+    k_loop<D, NTT>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
     // lane: weight row r16, tokens 4q+v of each tile
     const int e8 = r16 & 7;
     const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);  // h in operand order
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt >= ntt) break;
+    for (int tt = 0; tt < NTT; ++tt) {
+      if (16 * tt >= it.n) break;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int pt = 16 * tt + 4 * q + v;
@@ -684,39 +714,40 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
 
 // ----------------------------------------------------------------- down
 
-// Item: (chosen expert, 128 rows of d, up to 32 tokens).  Wave w takes rows
-// 32w .. 32w+31 of the group as two tiles; K = f, against the fp16 h
+// Item: (chosen expert, 128 rows of d, up to 16*NTT tokens).  Wave w takes
+// rows 32w .. 32w+31 of the group as two tiles; K = f, against the fp16 h
 // operands.  o_{t,j} goes to obuf[t*k + j][row].
-template <int F>
+template <int F, int NTT>
 __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
-  constexpr int G = F / 32;
-  __shared__ OpTile s_tile[2];
+  __shared__ OpTile<NTT> s_tile[2];
   const int d = a.d, ngroups = d / 128;
-  const int total = ngroups * a.meta[1];
+  const ItemRange ir = xcd_items(a, ngroups);
   const uint32_t magic = magic_f16x2();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const Item it = item_of(a, ngroups, w);
-    const int ntt = it.n > 16 ? 2 : 1;
+  for (int i = blockIdx.x >> 3; i < ir.n; i += ir.step) {
+    const Item it = item_of(a, ir, ngroups, i);
     const int row0 = it.rg * 128 + wave * 32 + r16;
     const size_t tile = (size_t)it.e * (d / 16) + it.rg * 8 + wave * 2;  // two 16-row tiles of W_d
     const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.down_t) + tile * (F / 128) * 64,
                            reinterpret_cast<const uint4*>(a.down_t) + (tile + 1) * (F / 128) * 64};
     const uint2* wts[2] = {reinterpret_cast<const uint2*>(a.down_ts) + tile * (F / 128) * 16,
                            reinterpret_cast<const uint2*>(a.down_ts) + (tile + 1) * (F / 128) * 16};
-    const int pos = it.p0 + min(tid >> 3, it.n - 1);
-    // the assignments this lane's outputs go to, fetched while the K loop runs
-    int dst[2][4];
+    const uint16_t* rows[NTT / 2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int m = 0; m < NTT / 2; ++m) rows[m] = a.h16 + (size_t)(it.p0 + min((tid >> 3) + 32 * m, it.n - 1)) * F;
+    // the assignments this lane's outputs go to, fetched while the K loop runs
+    int dst[NTT][4];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[tt][v] = a.asg[it.p0 + min(16 * tt + 4 * q + v, it.n - 1)];
-    f32x4_t acc[2][2];
-    acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    k_loop<F, 2>(acc, s_tile, a.h16 + (size_t)pos * F, wtq, wts, tid, lane, magic);
+    f32x4_t acc[2][NTT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt >= ntt) break;
+    for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    k_loop<F, NTT>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      if (16 * tt >= it.n) break;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int pt = 16 * tt + 4 * q + v;
@@ -824,46 +855,59 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
       raised = true;
     }
   }
-  hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), lds, s, a, T);
+  hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), lds, s, a, T, chunk_rows(a, T));
   return hipGetLastError();
 }
 
-// Workgroup items: (chunk, row group); at most min(E, T*k) + T*k/32 chunks.
+// Workgroup items: (chunk, row group); at most min(E, T*k) + T*k/CS chunks.
 static int max_chunks(const LayerArgs& a, int T) {
-  const int Tk = T * a.k;
-  return (a.E < Tk ? a.E : Tk) + Tk / 32 + a.ns * ((T + 31) / 32);
+  const int Tk = T * a.k, cs = chunk_rows(a, T);
+  return (a.E < Tk ? a.E : Tk) + Tk / cs + a.ns * ((T + cs - 1) / cs);
 }
+// A multiple of 8 (one share per XCD), at most what stays resident.
 static int grid_for(const LayerArgs& a, int T, int groups) {
-  const int items = max_chunks(a, T) * groups;
+  const int items = (max_chunks(a, T) * groups + 7) & ~7;
   return items < kMaxGroupedGrid ? items : kMaxGroupedGrid;
 }
 
-hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
-  const dim3 g(grid_for(a, T, a.f / 64)), b(256);
+template <int NTT>
+static hipError_t gateup_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
+  const dim3 b(256);
   switch (a.d) {
-    case 256: hipLaunchKernelGGL((k_gateup<256>), g, b, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((k_gateup<512>), g, b, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((k_gateup<1024>), g, b, 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((k_gateup<2048>), g, b, 0, s, a); break;
-    case 4096: hipLaunchKernelGGL((k_gateup<4096>), g, b, 0, s, a); break;
-    case 8192: hipLaunchKernelGGL((k_gateup<8192>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((k_gateup<256, NTT>), g, b, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((k_gateup<512, NTT>), g, b, 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((k_gateup<1024, NTT>), g, b, 0, s, a); break;
+    case 2048: hipLaunchKernelGGL((k_gateup<2048, NTT>), g, b, 0, s, a); break;
+    case 4096: hipLaunchKernelGGL((k_gateup<4096, NTT>), g, b, 0, s, a); break;
+    case 8192: hipLaunchKernelGGL((k_gateup<8192, NTT>), g, b, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
+  const dim3 g(grid_for(a, T, a.f / 64));
+  return chunk_rows(a, T) == 64 ? gateup_inst<4>(a, g, s) : gateup_inst<2>(a, g, s);
+}
+
+template <int NTT>
+static hipError_t down_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
+  const dim3 b(256);
+  switch (a.f) {
+    case 128: hipLaunchKernelGGL((k_down<128, NTT>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((k_down<256, NTT>), g, b, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((k_down<512, NTT>), g, b, 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((k_down<1024, NTT>), g, b, 0, s, a); break;
+    case 2048: hipLaunchKernelGGL((k_down<2048, NTT>), g, b, 0, s, a); break;
+    case 4096: hipLaunchKernelGGL((k_down<4096, NTT>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
-  const dim3 g(grid_for(a, T, a.d / 128)), b(256);
-  switch (a.f) {
-    case 128: hipLaunchKernelGGL((k_down<128>), g, b, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((k_down<256>), g, b, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((k_down<512>), g, b, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((k_down<1024>), g, b, 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((k_down<2048>), g, b, 0, s, a); break;
-    case 4096: hipLaunchKernelGGL((k_down<4096>), g, b, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  const dim3 g(grid_for(a, T, a.d / 128));
+  return chunk_rows(a, T) == 64 ? down_inst<4>(a, g, s) : down_inst<2>(a, g, s);
 }
 
 static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq, uint16_t* ts, long long rows, int K,

@@ -46,7 +46,8 @@ struct LayerArgs {
   int32_t* off;           // [E+1] first position of each expert in asg
   int32_t* act;           // [E] experts with assignments, ascending
   int32_t* chunk_off;     // [E+1] 32-token chunks of the active experts before each
-  int4* chunks;           // [min(E, T*k) + T*k/32 + ns*ceil(T/32)] (expert, first position, count <= 32);
+  int4* chunks;           // [min(E, T*k) + T*k/32 + ns*ceil(T/32)] (expert, first position, count <= CS),
+                          // CS = 32, or 64 when T*k >= 32*E;
                           // the shared expert's chunks (expert E) come last
   int32_t* meta;          // [0]: active routed experts, [1]: chunks, [2]: T*k
   int32_t* asg;           // [T*k + ns*T] assignments grouped by expert (shared: T*k + t, last)
@@ -61,8 +62,8 @@ struct LayerArgs {
 
 constexpr int kMaxFusedGrid = 1024;
 constexpr int kFusedGridCUs = 256;  // compute units the single-launch kernel is sized for (MI355X)
-constexpr int kMaxGroupedGrid = 1024;
-constexpr int kMaxAssignments = MOE_MAX_TOKENS * MOE_MAX_TOPK;  // largest T*k  // persistent grid of the expert-grouped kernels
+constexpr int kMaxGroupedGrid = 512;  // expert kernels: 2 resident workgroups on each of 256 CUs
+constexpr int kMaxAssignments = MOE_MAX_TOKENS * MOE_MAX_TOPK;  // largest T*k
 
 // Arguments of the single-launch 1-token layer kernel.
 struct FusedArgs {
