@@ -14,7 +14,7 @@ constexpr int kAbiVersion = 2;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
-      hrec, epoch, rwords, fargs, cleared;       // [0, cleared) is zeroed at init
+      hrec, epoch, cleared;                      // [0, cleared) is zeroed at init
   size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
   size_t router_t;                                       // bf16 terms of the router matrix (same)
   size_t total;
@@ -76,8 +76,6 @@ Layout layout_of(const moe_layer_desc* d) {
   L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
   L.hrec = o, o += align256((k + ns) * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
-  L.rwords = o, o += align256(4 * d_ * sizeof(unsigned long long));  // stack launch: tagged residual words
-  L.fargs = o, o += align256(sizeof(moe::FusedArgs));                 // stack launch: this layer's arguments
   L.cleared = o;
   const bool copy = needs_tiled_copy(d);
   const size_t cq = copy ? (E + ns) * f_ * d_ / 2 : 0, cs = copy ? (E + ns) * f_ * (d_ / 32) * 2 : 0;
@@ -99,8 +97,6 @@ struct moe_layer {
   moe::LayerArgs args;
   void* workspace;
   float* resid_tmp;  // [max_tokens][d]: the other residual buffer when this layer leads a stack
-  moe::FusedArgs* fargs_dev;  // this layer's single-launch arguments in its workspace (stack launch)
-  unsigned long long* rwords;  // stack launch: this layer's tagged output residual words
   bool fused;        // the 1-token step runs as one launch
 };
 
@@ -115,25 +111,8 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error;
   f.sh_gate_q = a.sh_gate_q, f.sh_gate_s = a.sh_gate_s, f.sh_up_q = a.sh_up_q, f.sh_up_s = a.sh_up_s;
   f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
-  f.rwords = h->rwords;
   f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
   return f;
-}
-
-// One stack launch needs layers of one shape (one kernel instance) and no
-// handle twice (each layer's hand-off words live in its own workspace).
-bool stack_launchable(const moe_handle* layers, int L) {
-  if (L < 2) return false;
-  const moe_layer_desc& d0 = layers[0]->desc;
-  for (int l = 0; l < L; ++l) {
-    const moe_layer_desc& dl = layers[l]->desc;
-    if (dl.d != d0.d || dl.f != d0.f || dl.n_experts != d0.n_experts || dl.top_k != d0.top_k ||
-        dl.n_shared != d0.n_shared)
-      return false;
-    for (int m = 0; m < l; ++m)
-      if (layers[m] == layers[l]) return false;
-  }
-  return true;
 }
 
 }  // namespace
@@ -213,8 +192,6 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.h16 = reinterpret_cast<uint16_t*>(base + L.h16);
   a.obuf = reinterpret_cast<float*>(base + L.obuf);
   h->resid_tmp = reinterpret_cast<float*>(base + L.resid);
-  h->rwords = reinterpret_cast<unsigned long long*>(base + L.rwords);
-  h->fargs_dev = reinterpret_cast<moe::FusedArgs*>(base + L.fargs);
   a.tagged_logits = reinterpret_cast<unsigned long long*>(base + L.tagged);
   a.hrec = reinterpret_cast<unsigned long long*>(base + L.hrec);
   a.epoch = reinterpret_cast<unsigned*>(base + L.epoch);
@@ -237,13 +214,6 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
       hipDeviceSynchronize() != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
-  }
-  if (h->fused) {  // the arguments a stack launch reads for this layer
-    const moe::FusedArgs fa = fused_args(h);
-    if (hipMemcpy(h->fargs_dev, &fa, sizeof(fa), hipMemcpyHostToDevice) != hipSuccess) {
-      delete h;
-      return MOE_ERR_HIP;
-    }
   }
   *out = h;
   return MOE_OK;
@@ -307,30 +277,6 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
   const size_t d = (size_t)layers[0]->desc.d, k = (size_t)layers[0]->desc.top_k;
   bool fused = T == 1;
   for (int l = 0; l < L; ++l) fused = fused && layers[l]->fused;
-  if (fused && stack_launchable(layers, L)) {
-    // The whole stack in one launch per (at most kMaxStackLayers) layers:
-    // the residual crosses layers inside the kernel; each segment reads its
-    // r from the previous segment's buffer (first: the caller's) and leaves
-    // r_L in its first layer's spare buffer, copied back at the end.
-    const float* r = residual;
-    for (int l0 = 0; l0 < L; l0 += moe::kMaxStackLayers) {
-      const int n = L - l0 < moe::kMaxStackLayers ? L - l0 : moe::kMaxStackLayers;
-      moe::StackArgs st{};
-      for (int i = 0; i < n; ++i) st.layer[i] = layers[l0 + i]->fargs_dev;
-      st.L = n;
-      st.eps = eps;
-      st.r0 = r;
-      st.r_last = layers[l0]->resid_tmp;
-      st.x_trace = x_trace ? x_trace + (size_t)l0 * d : nullptr;
-      st.y_trace = y_trace ? y_trace + (size_t)l0 * d : nullptr;
-      st.idx_trace = idx_trace ? idx_trace + (size_t)l0 * k : nullptr;
-      if (moe::launch_stack_fused(st, fused_args(layers[l0]), layers[0]->args.d, layers[0]->args.f, s) != hipSuccess)
-        return MOE_ERR_HIP;
-      r = st.r_last;
-    }
-    if (hipMemcpyAsync(residual, r, d * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess) return MOE_ERR_HIP;
-    return MOE_OK;
-  }
   if (fused) {
     // One launch per layer.  The residual alternates between the caller's
     // buffer and the first layer's spare one, arranged so that r_L lands in

@@ -91,26 +91,11 @@ __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
   return (size_t)(j / wpw) * lpw * 16 + (j % wpw);
 }
 
-// The residual between the layers of one persistent stack launch (HOP):
-// layer l publishes r_{l+1} as tagged words, one 128-byte line set per
-// producing workgroup, and layer l+1 polls them instead of reading memory.
-struct StackHop {
-  const unsigned long long* rin;  // r_l words of the previous layer (its tag), or NULL: a.resid_in
-  unsigned rin_tag;
-  unsigned long long* rout;       // this layer's r_{l+1} words, or NULL: a.resid_out
-};
-
-// Word of output row `row`: rows of one workgroup (RPG) in their own lines.
-template <int RPG>
-__device__ __forceinline__ size_t rword_index(int row) {
-  return (size_t)(row / RPG) * (16 * ((RPG + 15) / 16)) + row % RPG;
-}
-
 // D hidden, F expert width, KP expert slots (top_k, plus one with a shared
 // expert, SH) rounded up to a power of two, EPL
-// experts per lane in the top-k wave.  Returns this layer's tag.
-template <int D, int F, int KP, int EPL, bool NORM, bool SH, bool HOP>
-__device__ __forceinline__ unsigned layer_body(const FusedArgs& a, const StackHop& hop) {
+// experts per lane in the top-k wave.
+template <int D, int F, int KP, int EPL, bool NORM, bool SH>
+__global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
   constexpr int NL = 4;              // gate (and up) loads per lane
@@ -135,8 +120,6 @@ __device__ __forceinline__ unsigned layer_body(const FusedArgs& a, const StackHo
 
   __shared__ __align__(16) uint16_t s_x[D];
   __shared__ float s_ss[4];
-  __shared__ float s_r[HOP ? D : 1];  // r_l (stack launch): the rows this workgroup adds to
-  constexpr int RPG = 4 * ROWS_W;  // output rows per workgroup
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wg = blockIdx.x * 4 + wid;
@@ -200,45 +183,10 @@ __device__ __forceinline__ unsigned layer_body(const FusedArgs& a, const StackHo
     constexpr int NR = (D / 4 + 255) / 256;
     float4 rv[NR];
     float ss = 0.f;
-    if constexpr (HOP) {
-      if (hop.rin) {
-        // the previous layer's r words, polled until all carry its tag
-        for (unsigned spin = 0;; ++spin) {
-          bool ok = true;
-#pragma unroll
-          for (int m = 0; m < NR; ++m) {
-            const int c = min((int)threadIdx.x + 256 * m, D / 4 - 1);
-            unsigned long long t[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) t[j] = load_coherent(hop.rin + rword_index<RPG>(4 * c + j));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ok = ok & ((uint32_t)(t[j] >> 32) == hop.rin_tag);
-            rv[m] = make_float4(__uint_as_float((uint32_t)t[0]), __uint_as_float((uint32_t)t[1]),
-                                __uint_as_float((uint32_t)t[2]), __uint_as_float((uint32_t)t[3]));
-          }
-          if (__syncthreads_or(!ok) == 0) break;
-          if (spin > kSpinLimit) {
-            if (threadIdx.x == 0) atomicOr(a.error, 4u);
-            break;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < NR; ++m)
-          rv[m] = reinterpret_cast<const float4*>(a.resid_in)[min((int)threadIdx.x + 256 * m, D / 4 - 1)];
-      }
-#pragma unroll
-      for (int m = 0; m < NR; ++m) {
-        const int c = threadIdx.x + 256 * m;
-        if (c >= D / 4) rv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        else reinterpret_cast<float4*>(s_r)[c] = rv[m];
-      }
-    }
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
       const int c = threadIdx.x + 256 * m;
-      if constexpr (!HOP)
-        rv[m] = c < D / 4 ? reinterpret_cast<const float4*>(a.resid_in)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      rv[m] = c < D / 4 ? reinterpret_cast<const float4*>(a.resid_in)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
       ss = fmaf(rv[m].x, rv[m].x, ss);
       ss = fmaf(rv[m].y, rv[m].y, ss);
       ss = fmaf(rv[m].z, rv[m].z, ss);
@@ -403,13 +351,8 @@ __device__ __forceinline__ unsigned layer_body(const FusedArgs& a, const StackHo
     const int row = r0 + (P >= 64 ? n / LPRD : n * RPLD + lane / P);
     const bool writer = has_down && (P >= 64 ? lane == 0 : lane % P == 0) && n % LPRD == LPRD - 1;
     radd[n] = 0.f;
-    if constexpr (NORM) {
-      if constexpr (HOP) {
-        if (writer) radd[n] = s_r[row];
-      } else {
-        if (writer) radd[n] = a.resid_in[row];
-      }
-    }
+    if constexpr (NORM)
+      if (writer) radd[n] = a.resid_in[row];
   }
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
@@ -459,12 +402,7 @@ __device__ __forceinline__ unsigned layer_body(const FusedArgs& a, const StackHo
   // ---------------------------------------------------------------- down + combine
   auto put_y = [&](int row, float v, float r) {
     if constexpr (NORM) {
-      if constexpr (HOP) {
-        if (hop.rout) store_tagged(hop.rout + rword_index<RPG>(row), r + v, tag);
-        else a.resid_out[row] = r + v;
-      } else {
-        a.resid_out[row] = r + v;
-      }
+      a.resid_out[row] = r + v;
       if (a.y) a.y[row] = v;
     } else {
       a.y[row] = v;
@@ -500,51 +438,14 @@ __device__ __forceinline__ unsigned layer_body(const FusedArgs& a, const StackHo
     }
   }
   if (threadIdx.x == 0) a.epoch[blockIdx.x] = tag;
-  return tag;
-}
-
-template <int D, int F, int KP, int EPL, bool NORM, bool SH>
-__global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
-  layer_body<D, F, KP, EPL, NORM, SH, false>(a, StackHop{nullptr, 0u, nullptr});
-}
-
-// A whole pre-norm stack of L layers of one shape in one launch: every
-// workgroup runs the layers in turn; the residual crosses from layer to
-// layer as tagged words (so layer l+1's router rows are already loading
-// while it waits for them), r_0 is read from memory and r_L written to
-// memory (a buffer other than r_0's).
-template <int D, int F, int KP, int EPL, bool SH>
-__global__ __launch_bounds__(256) void k_stack(const StackArgs s) {
-  const unsigned long long* prev = nullptr;
-  unsigned prev_tag = 0;
-  for (int l = 0; l < s.L; ++l) {
-    FusedArgs a = *s.layer[l];
-    a.eps = s.eps;
-    a.resid_in = s.r0;
-    a.resid_out = s.r_last;
-    a.x_trace = s.x_trace ? s.x_trace + (size_t)l * D : nullptr;
-    a.y = s.y_trace ? s.y_trace + (size_t)l * D : nullptr;
-    a.idx_out = s.idx_trace ? s.idx_trace + (size_t)l * a.k : nullptr;
-    a.w_out = nullptr;
-    const StackHop hop{l == 0 ? nullptr : prev, prev_tag, l + 1 < s.L ? a.rwords : nullptr};
-    prev_tag = layer_body<D, F, KP, EPL, true, SH, true>(a, hop);
-    prev = a.rwords;
-    __syncthreads();  // LDS is reused by the next layer
-  }
 }
 
 // ---------------------------------------------------------------- host side
 
-// st == NULL: one layer (k_layer); else the whole stack (k_stack)
 template <int D, int F, int KP, int EPL>
-static hipError_t layer_launch(const FusedArgs& a, const StackArgs* st, int G, hipStream_t s) {
+static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
   const size_t lds = (size_t)(a.k + a.ns) * (F / 8) * 5 * sizeof(unsigned);
-  if (st) {
-    if (a.ns)
-      hipLaunchKernelGGL((k_stack<D, F, KP, EPL, true>), dim3(G), dim3(256), lds, s, *st);
-    else
-      hipLaunchKernelGGL((k_stack<D, F, KP, EPL, false>), dim3(G), dim3(256), lds, s, *st);
-  } else if (a.ns) {
+  if (a.ns) {
     if (a.resid_in)
       hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true>), dim3(G), dim3(256), lds, s, a);
     else
@@ -559,20 +460,20 @@ static hipError_t layer_launch(const FusedArgs& a, const StackArgs* st, int G, h
 }
 
 template <int D, int F, int KP>
-static hipError_t layer_epl(const FusedArgs& a, const StackArgs* st, int G, hipStream_t s) {
-  if (a.E <= 64) return layer_launch<D, F, KP, 1>(a, st, G, s);
-  if (a.E <= 128) return layer_launch<D, F, KP, 2>(a, st, G, s);
-  return layer_launch<D, F, KP, 4>(a, st, G, s);
+static hipError_t layer_epl(const FusedArgs& a, int G, hipStream_t s) {
+  if (a.E <= 64) return layer_launch<D, F, KP, 1>(a, G, s);
+  if (a.E <= 128) return layer_launch<D, F, KP, 2>(a, G, s);
+  return layer_launch<D, F, KP, 4>(a, G, s);
 }
 
 template <int D, int F>
-static hipError_t layer_kp(const FusedArgs& a, const StackArgs* st, int G, hipStream_t s) {
+static hipError_t layer_kp(const FusedArgs& a, int G, hipStream_t s) {
   const int k = a.k + a.ns;  // expert slots
-  if (k <= 1) return layer_epl<D, F, 1>(a, st, G, s);
-  if (k <= 2) return layer_epl<D, F, 2>(a, st, G, s);
-  if (k <= 4) return layer_epl<D, F, 4>(a, st, G, s);
-  if (k <= 8) return layer_epl<D, F, 8>(a, st, G, s);
-  return layer_epl<D, F, 16>(a, st, G, s);
+  if (k <= 1) return layer_epl<D, F, 1>(a, G, s);
+  if (k <= 2) return layer_epl<D, F, 2>(a, G, s);
+  if (k <= 4) return layer_epl<D, F, 4>(a, G, s);
+  if (k <= 8) return layer_epl<D, F, 8>(a, G, s);
+  return layer_epl<D, F, 16>(a, G, s);
 }
 
 // Work each wave takes in the fused kernel must fit one unit per wave; k
@@ -614,16 +515,8 @@ int fused_grid() {
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s) {
   const int G = fused_grid();
   if (G <= 0 || !fits(d, f, a.E, a.k + a.ns, G)) return hipErrorInvalidValue;
-  if (d == 256 && f == 128) return layer_kp<256, 128>(a, nullptr, G, s);
-  if (d == 2048 && f == 512) return layer_kp<2048, 512>(a, nullptr, G, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_stack_fused(const StackArgs& st, const FusedArgs& a, int d, int f, hipStream_t s) {
-  const int G = fused_grid();
-  if (G <= 0 || !fits(d, f, a.E, a.k + a.ns, G) || st.L < 1 || st.L > kMaxStackLayers) return hipErrorInvalidValue;
-  if (d == 256 && f == 128) return layer_kp<256, 128>(a, &st, G, s);
-  if (d == 2048 && f == 512) return layer_kp<2048, 512>(a, &st, G, s);
+  if (d == 256 && f == 128) return layer_kp<256, 128>(a, G, s);
+  if (d == 2048 && f == 512) return layer_kp<2048, 512>(a, G, s);
   return hipErrorInvalidValue;
 }
 

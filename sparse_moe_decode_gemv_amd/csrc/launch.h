@@ -93,23 +93,7 @@ struct FusedArgs {
   const uint16_t* sh_up_s;
   const uint8_t* sh_down_q;
   const uint16_t* sh_down_s;
-  unsigned long long* rwords;  // stack launch: this layer's tagged output residual words (4*d)
   int E, k, norm, ns;
-};
-
-// One launch for a pre-norm stack of layers of one shape (T = 1): the
-// per-layer arguments are read from device memory (each layer's own copy,
-// written at init).
-constexpr int kMaxStackLayers = 64;
-struct StackArgs {
-  const FusedArgs* layer[kMaxStackLayers];
-  int L;
-  float eps;
-  const float* r0;     // r_0 [d]
-  float* r_last;       // r_L [d] (not r0's buffer)
-  uint16_t* x_trace;   // [L][d] or NULL
-  float* y_trace;      // [L][d] or NULL
-  int32_t* idx_trace;  // [L][k] or NULL
 };
 
 // The whole 1-token step in one launch, for the shapes it is built for
@@ -118,8 +102,6 @@ struct StackArgs {
 bool fused_layer_supported(int d, int f, int E, int k, int ns, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
-// a: any layer of the stack (all share d, f, E, k, ns)
-hipError_t launch_stack_fused(const StackArgs& st, const FusedArgs& a, int d, int f, hipStream_t s);
 
 // Router logits of T tokens (a matrix product), then softmax + top-k of
 // every token and the assignments grouped by expert.  Activations come

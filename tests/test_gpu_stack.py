@@ -135,48 +135,3 @@ def test_stack_of_zero_layers_keeps_the_residual():
     r, _, yt, _ = run_stack(layers_np, cfg, X0)
     assert np.array_equal(r, F.bf16_to_f64(X0).astype(np.float32))
     assert np.all(yt == 0)
-
-
-def _stack_outputs(handles, cfg, X0, nl):
-    import torch
-    dev = device()
-    T = X0.shape[0]
-    r = torch.from_numpy(F.bf16_to_f64(X0).astype(np.float32)).to(dev)
-    xt = torch.zeros((nl, T, cfg.d), dtype=torch.int16, device=dev)
-    yt = torch.full((nl, T, cfg.d), float("nan"), dtype=torch.float32, device=dev)
-    it = torch.full((nl, T, cfg.k), -1, dtype=torch.int32, device=dev)
-    M.moe_decode_stack_forward(handles, r, T, EPS, xt, yt, it)
-    torch.cuda.synchronize()
-    return r.cpu().numpy(), xt.cpu().numpy(), yt.cpu().numpy(), it.cpu().numpy()
-
-
-@pytest.mark.parametrize("cfg_name", ["STACK", "TINY"])
-def test_stack_launch_matches_per_layer_launches(cfg_name):
-    """Layers A B C D A: with A's handle twice the stack runs one launch per
-    layer; with a second handle on A's weights it runs as one launch.  Both
-    compute each layer with the same arithmetic, so every output (residual,
-    x_l, y_l, chosen experts) is bit-identical."""
-    cfg = getattr(synth, cfg_name)
-    dev = device()
-    layers_np = [synth.make_layer(cfg, 4, l) for l in range(4)]
-    X0 = tokens(cfg, OM.Layer.from_dict(layers_np[0]), 4, 1)
-    Ls = [M.MoELayer.create(M.upload(l, dev), cfg.d, cfg.f, cfg.E, cfg.k, 1, 1) for l in layers_np]
-    A2 = M.MoELayer.create(M.upload(layers_np[0], dev), cfg.d, cfg.f, cfg.E, cfg.k, 1, 1)
-    per_layer = _stack_outputs([L.handle for L in Ls] + [Ls[0].handle], cfg, X0, 5)
-    one_launch = _stack_outputs([L.handle for L in Ls] + [A2.handle], cfg, X0, 5)
-    for L in Ls + [A2]:
-        L.close()
-    for name, a, b in zip(("r", "x_l", "y_l", "experts"), per_layer, one_launch):
-        assert np.array_equal(a, b), f"{name} differs between per-layer launches and the stack launch"
-    assert np.all(one_launch[3] >= 0)
-
-
-def test_tiny_stack_70_layers_two_launches():
-    """70 layers: more than one stack launch holds (64), so the residual
-    crosses from the first launch to the second through memory."""
-    cfg = synth.TINY
-    layers_np = [synth.make_layer(cfg, 5, l) for l in range(70)]
-    layers_o = [OM.Layer.from_dict(l) for l in layers_np]
-    X0 = tokens(cfg, layers_o[0], 5, 1)
-    r, xt, yt, it = run_stack(layers_np, cfg, X0)
-    check_teacher_forced(layers_o, cfg, X0, r, xt, yt, it)
