@@ -19,6 +19,25 @@ format is a stated choice:
 Quantizer (offline, produces stored weights): per group a = max|w|,
 s = fp16_RNE(a/7) with a/7 in fp64; s == 0 gives all codes 8, otherwise
 q = clamp(round_half_even(w/s), -7, 7) and u = q + 8.
+
+The pages name NVFP4 as the released model's 4-bit format ("Recursive
+Releases Flint...", section "Quantization"; noticiai.com.br page, section "O
+papel da quantização e dos kernels") without defining it.  The FP4 variant
+here is MXFP4, the OCP Microscaling (MX) v1.0 format, whose block scale the
+target hardware decodes natively:
+
+* element: FP4 E2M1, 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit;
+  exponent field e > 0 gives (-1)^s 2^(e-1) (1 + m/2), e = 0 gives (-1)^s m/2;
+  no infinities or NaN (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6);
+* scale: E8M0, an unsigned byte b standing for 2^(b-127) (b = 255 is NaN);
+  one scale per 32 consecutive elements along K;
+* stored: codes at the int4 nibble positions above, scale bytes [rows][K/32].
+
+MXFP4 quantizer (the MX specification's conversion): per block a = max|w|;
+a == 0 gives scale byte 127 and all codes 0; otherwise the shared exponent is
+X = floor(log2 a) - 2 (2 = the largest E2M1 exponent), the scale byte X + 127
+(clamped to 0..254), and every element w / 2^X goes to the nearest E2M1
+value, ties to the even mantissa, magnitudes above 6 to 6.
 """
 from __future__ import annotations
 
@@ -117,3 +136,54 @@ def quantize(w: np.ndarray):
     q = np.where(s == 0.0, 0.0, q)
     u = (q + 8).astype(np.int64).reshape(w.shape)
     return u, sbits
+
+
+# ------------------------------------------------------------------ MXFP4
+
+
+def fp4_e2m1_to_f64(codes) -> np.ndarray:
+    """FP4 E2M1 codes (0..15) -> fp64 from the bit fields."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    normal = np.exp2(e.astype(np.float64) - 1.0) * (1.0 + m / 2.0)
+    return sign * np.where(e == 0, m / 2.0, normal)
+
+
+def e8m0_to_f64(b) -> np.ndarray:
+    """E8M0 scale bytes -> fp64: 2^(b - 127), NaN for b = 255."""
+    b = np.asarray(b, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b.astype(np.float64) - 127.0))
+
+
+def dequant_mxfp4(qbytes: np.ndarray, sbytes: np.ndarray, K: int) -> np.ndarray:
+    """Stored MXFP4 matrix -> fp64 weights [..., K]: w = e2m1(c) * 2^(b[k // 32] - 127)."""
+    v = fp4_e2m1_to_f64(unpack_codes(qbytes, K))
+    s = e8m0_to_f64(sbytes)
+    return (v.reshape(v.shape[:-1] + (K // 32, 32)) * s[..., None]).reshape(v.shape)
+
+
+E2M1_MAGNITUDES = fp4_e2m1_to_f64(np.arange(8))
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """fp32 weights [..., K] -> (E2M1 codes [..., K], E8M0 scale bytes [..., K/32])."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    K = w.shape[-1]
+    g = w.reshape(w.shape[:-1] + (K // 32, 32))
+    a = np.abs(g).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        X = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0))) - 2, 0)
+    b = np.clip(X + 127, 0, 254).astype(np.int64)
+    v = np.abs(g) / np.exp2(b - 127.0)[..., None]
+    # nearest magnitude; on a tie the even code (even mantissa) wins
+    dist = np.abs(v[..., None] - E2M1_MAGNITUDES)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = np.where(dist == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))
+    code = np.where((g < 0) & (code > 0), code | 8, code)
+    code = np.where(a[..., None] > 0, code, 0)
+    b = np.where(a > 0, b, 127)
+    return code.reshape(w.shape).astype(np.int64), b.astype(np.uint8)

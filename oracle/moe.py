@@ -14,7 +14,9 @@ follows (each reading is also listed in the design notes):
   expert index first), then the weights renormalized over the chosen set
   (norm_topk=True) or kept as the softmax values (norm_topk=False);
 * expert: SwiGLU, h = silu(W_g x) * (W_u x) with silu(z) = z / (1 + e^-z),
-  then o = W_d h, all on dequantized int4 weights in fp64;
+  then o = W_d h, all on dequantized 4-bit weights in fp64 (int4 with fp16
+  scales, or MXFP4 -- E2M1 codes with E8M0 scales -- when the scale arrays
+  hold bytes; formats.py);
 * combine: y = sum over chosen experts of w_j o_j, added in ascending expert
   index, rounded once to fp32 for comparison;
 * shared expert (the pages' layer adds one always-on expert to the routed
@@ -33,7 +35,14 @@ from itertools import combinations
 
 import numpy as np
 
-from .formats import bf16_to_f64, dequant, f64_to_bf16_bits, f64_to_f32
+from .formats import bf16_to_f64, dequant, dequant_mxfp4, f64_to_bf16_bits, f64_to_f32
+
+
+def dequant_4bit(q: np.ndarray, s: np.ndarray, K: int) -> np.ndarray:
+    """A stored 4-bit matrix in either format: byte scales mean MXFP4 (E8M0),
+    16-bit scales int4 (binary16)."""
+    s = np.asarray(s)
+    return dequant_mxfp4(q, s, K) if s.dtype == np.uint8 else dequant(q, s, K)
 
 
 @dataclass
@@ -43,7 +52,7 @@ class Layer:
     router_w: np.ndarray            # fp32 [E][d]
     router_b: np.ndarray | None     # fp32 [E] or None
     gate_q: np.ndarray              # uint8 [E][f][d/2]
-    gate_s: np.ndarray              # uint16 [E][f][d/32]
+    gate_s: np.ndarray              # uint16 [E][f][d/32] (int4), or uint8 (MXFP4)
     up_q: np.ndarray
     up_s: np.ndarray
     down_q: np.ndarray              # uint8 [E][d][f/2]
@@ -74,16 +83,16 @@ class Layer:
     def expert(self, e: int):
         """Dequantized (W_g [f][d], W_u [f][d], W_d [d][f]) of expert e, counted as read."""
         d, f = self.d, self.f
-        Wg = dequant(self.gate_q[e], self.gate_s[e], d)
-        Wu = dequant(self.up_q[e], self.up_s[e], d)
-        Wd = dequant(self.down_q[e], self.down_s[e], f)
+        Wg = dequant_4bit(self.gate_q[e], self.gate_s[e], d)
+        Wu = dequant_4bit(self.up_q[e], self.up_s[e], d)
+        Wd = dequant_4bit(self.down_q[e], self.down_s[e], f)
         self.weights_read += Wg.size + Wu.size + Wd.size
         return Wg, Wu, Wd
 
     def shared_expert(self):
         """Dequantized (W_g, W_u, W_d) of the shared expert, counted as read."""
         gq, gs, uq, us, dq, ds = self.shared
-        Wg, Wu, Wd = dequant(gq, gs, self.d), dequant(uq, us, self.d), dequant(dq, ds, self.f)
+        Wg, Wu, Wd = dequant_4bit(gq, gs, self.d), dequant_4bit(uq, us, self.d), dequant_4bit(dq, ds, self.f)
         self.weights_read += Wg.size + Wu.size + Wd.size
         return Wg, Wu, Wd
 
@@ -215,9 +224,9 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     chosen = np.lexsort((np.arange(layer.E), -p))[:k]
     wv = np.zeros(layer.E)
     wv[chosen] = p[chosen] / p[chosen].sum() if norm_topk else p[chosen]
-    Wg = dequant(layer.gate_q, layer.gate_s, layer.d)
-    Wu = dequant(layer.up_q, layer.up_s, layer.d)
-    Wd = dequant(layer.down_q, layer.down_s, layer.f)
+    Wg = dequant_4bit(layer.gate_q, layer.gate_s, layer.d)
+    Wu = dequant_4bit(layer.up_q, layer.up_s, layer.d)
+    Wd = dequant_4bit(layer.down_q, layer.down_s, layer.f)
     G = np.einsum("efd,d->ef", Wg, x)
     U = np.einsum("efd,d->ef", Wu, x)
     H = G / (1.0 + np.exp(-G)) * U
@@ -225,7 +234,7 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     y = np.einsum("e,ed->d", wv, O)
     if layer.shared is not None:
         gq, gs, uq, us, dq, ds = layer.shared
-        Ws = [dequant(gq, gs, layer.d), dequant(uq, us, layer.d), dequant(dq, ds, layer.f)]
+        Ws = [dequant_4bit(gq, gs, layer.d), dequant_4bit(uq, us, layer.d), dequant_4bit(dq, ds, layer.f)]
         gs_, us_ = np.einsum("fd,d->f", Ws[0], x), np.einsum("fd,d->f", Ws[1], x)
         y = y + np.einsum("df,f->d", Ws[2], gs_ / (1.0 + np.exp(-gs_)) * us_)
     return y

@@ -2,7 +2,7 @@
 
 This module holds the input recipe only: shapes of the five workloads, the
 counter-based random streams, normal draws, bf16 activations, the offline int4
-quantize-and-pack step that produces stored weights, and the Zipf popularity
+(and MXFP4) quantize-and-pack steps that produce stored weights, and the Zipf popularity
 bias of the batched workload.  It contains none of the decode step's
 arithmetic, and it imports neither the oracle nor the GPU library.
 
@@ -68,6 +68,8 @@ def lib():
         L.synth_int4.argtypes = [p, p, i64, i64, u64, d, p]
         L.synth_int4_experts.argtypes = [p, p, i64, i64, i64, u64, d]
         L.synth_quantize_pack.argtypes = [p, i64, i64, p, p]
+        L.synth_mxfp4_experts.argtypes = [p, p, i64, i64, i64, u64, d]
+        L.synth_quantize_pack_mxfp4.argtypes = [p, i64, i64, p, p]
         L.synth_pack_codes.argtypes = [p, i64, i64, p]
         L.synth_permutation.argtypes = [p, ctypes.c_int32, u64]
         _lib = L
@@ -127,6 +129,25 @@ def int4_experts(E: int, rows: int, K: int, k: int, sigma: float):
     return q, s
 
 
+def mxfp4_experts(E: int, rows: int, K: int, k: int, sigma: float):
+    """MXFP4 counterpart of int4_experts (same draws): codes uint8 [E][rows][K/2], E8M0 bytes [E][rows][K/32]."""
+    q = np.empty((E, rows, K // 2), np.uint8)
+    s = np.empty((E, rows, K // 32), np.uint8)
+    lib().synth_mxfp4_experts(_ptr(q), _ptr(s), E, rows, K, k, sigma)
+    return q, s
+
+
+def quantize_pack_mxfp4(w: np.ndarray):
+    """Quantize caller-given fp32 weights [rows][K] into stored MXFP4."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, K = w.shape
+    assert K % 128 == 0
+    q = np.empty((rows, K // 2), np.uint8)
+    s = np.empty((rows, K // 32), np.uint8)
+    lib().synth_quantize_pack_mxfp4(_ptr(w), rows, K, _ptr(q), _ptr(s))
+    return q, s
+
+
 def quantize_pack(w: np.ndarray):
     """Quantize caller-given fp32 weights [rows][K] into the stored format."""
     w = np.ascontiguousarray(w, np.float32)
@@ -171,6 +192,7 @@ class MoEConfig:
     layers: int = 1
     margin: float = 1e-2
     shared: int = 0          # always-on experts (0 or 1), same shape, weight 1
+    fmt: str = "int4"        # expert weights: "int4" (fp16 scales) or "mxfp4" (E2M1, E8M0 scales)
 
 
 @dataclass(frozen=True)
@@ -191,6 +213,10 @@ STACK = replace(LAYER, name="stack", layers=49)
 FLINT = replace(LAYER, name="flint", k=6, shared=1)
 FLINT_BATCH = replace(FLINT, name="flint_batch", T=64, zipf_s=1.1)
 TINY_SHARED = replace(TINY, shared=1)
+# the same draws quantized to MXFP4 (the pages' released model is FP4)
+TINY_FP4 = replace(TINY, name="tiny_fp4", fmt="mxfp4")
+LAYER_FP4 = replace(LAYER, name="layer_fp4", fmt="mxfp4")
+FLINT_FP4 = replace(FLINT, name="flint_fp4", fmt="mxfp4")
 LMHEAD1 = LMHeadConfig("lmhead", V=131072, d=2048, B=1)
 LMHEAD8 = replace(LMHEAD1, B=8)
 
@@ -210,9 +236,10 @@ def make_layer(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
     # the same layer, and layer 0 of the stack is that layer.
     base = (seed, "tiny" if cfg.d == TINY.d and cfg.E == TINY.E else "layer", layer)
     rw = normal_f32(E * d, key(*base, "router"), 0.0, cfg.router_sigma).reshape(E, d)
-    gq, gs = int4_experts(E, f, d, key(*base, "gate"), cfg.expert_sigma)
-    uq, us = int4_experts(E, f, d, key(*base, "up"), cfg.expert_sigma)
-    dq, ds = int4_experts(E, d, f, key(*base, "down"), cfg.expert_sigma)
+    experts = mxfp4_experts if cfg.fmt == "mxfp4" else int4_experts
+    gq, gs = experts(E, f, d, key(*base, "gate"), cfg.expert_sigma)
+    uq, us = experts(E, f, d, key(*base, "up"), cfg.expert_sigma)
+    dq, ds = experts(E, d, f, key(*base, "down"), cfg.expert_sigma)
     rb = zipf_bias(cfg, seed) if cfg.zipf_s > 0 else None
     out = dict(router_w=rw, router_b=rb, gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
     if cfg.shared:
@@ -227,7 +254,8 @@ def make_shared(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
     base = (seed, "tiny" if cfg.d == TINY.d and cfg.E == TINY.E else "layer", layer)
     out = {}
     for name, rows, K in (("gate", f, d), ("up", f, d), ("down", d, f)):
-        q, sc = int4_experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
+        experts = mxfp4_experts if cfg.fmt == "mxfp4" else int4_experts
+        q, sc = experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
         out["shared_" + name + "_q"], out["shared_" + name + "_s"] = q[0], sc[0]
     return out
 

@@ -115,6 +115,42 @@ static uint16_t quantize_group(const float* w, uint8_t* u) {
   return sb;
 }
 
+/* MXFP4 block of 32 (the OCP MX v1.0 conversion): shared exponent
+ * X = floor(log2 amax) - 2 (2: the largest E2M1 exponent), scale byte
+ * X + 127 kept in 0..254; each |w| / 2^X goes to the nearest E2M1 magnitude
+ * (0, 0.5, 1, 1.5, 2, 3, 4, 6), a tie to the even code, anything above 6 to
+ * 6, the sign into bit 3 (zero stays code 0).  An all-zero block gets scale
+ * byte 127 and codes 0.  Writes codes u[32], returns the scale byte. */
+static uint8_t quantize_group_mxfp4(const float* w, uint8_t* u) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  float a = 0.f;
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(w[i]));
+  if (a == 0.f) {
+    memset(u, 0, 32);
+    return 127;
+  }
+  int e;
+  frexp((double)a, &e); /* a = m 2^e, 0.5 <= m < 1: floor(log2 a) = e - 1 */
+  int b = e - 1 - 2 + 127;
+  if (b < 0) b = 0;
+  if (b > 254) b = 254;
+  const double sc = ldexp(1.0, b - 127);
+  for (int i = 0; i < 32; ++i) {
+    const double v = fabs((double)w[i]) / sc;
+    int best = 0;
+    double bd = v;
+    for (int c = 1; c < 8; ++c) {
+      const double dd = fabs(v - mag[c]);
+      if (dd < bd || (dd == bd && (c & 1) == 0 && (best & 1) != 0)) {
+        best = c;
+        bd = dd;
+      }
+    }
+    u[i] = (uint8_t)(best | (w[i] < 0.f && best > 0 ? 8 : 0));
+  }
+  return (uint8_t)b;
+}
+
 static void pack_row(const uint8_t* u, int64_t K, uint8_t* row) {
   memset(row, 0, (size_t)(K / 2));
   for (int64_t k = 0; k < K; ++k) {
@@ -227,5 +263,52 @@ void synth_permutation(int32_t* out, int32_t n, uint64_t key) {
     int32_t t = out[i];
     out[i] = out[j];
     out[j] = t;
+  }
+}
+
+/* MXFP4 counterparts: E matrices [rows][K] from the same streams as
+ * synth_int4_experts, E2M1 codes packed at the same nibble positions, one
+ * E8M0 scale byte per 32 elements. */
+void synth_mxfp4_experts(uint8_t* q, uint8_t* s, int64_t E, int64_t rows, int64_t K, uint64_t key, double sigma) {
+#pragma omp parallel
+  {
+    float w[32];
+    uint8_t u[32];
+#pragma omp for schedule(static) collapse(2)
+    for (int64_t e = 0; e < E; ++e)
+      for (int64_t r = 0; r < rows; ++r) {
+        uint64_t ek = synth_key(key, (uint64_t)e);
+        int64_t rr = e * rows + r;
+        uint8_t* row = q + rr * (K / 2);
+        memset(row, 0, (size_t)(K / 2));
+        for (int64_t g = 0; g < K / 32; ++g) {
+          normal_block32(ek, (uint64_t)(r * (K / 32) + g), w);
+          for (int i = 0; i < 32; ++i) w[i] = (float)(sigma * (double)w[i]);
+          s[rr * (K / 32) + g] = quantize_group_mxfp4(w, u);
+          for (int i = 0; i < 32; ++i) {
+            int64_t k = g * 32 + i;
+            row[packed_offset(k)] |= (uint8_t)((k & 1) ? (u[i] << 4) : u[i]);
+          }
+        }
+      }
+  }
+}
+
+void synth_quantize_pack_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* q, uint8_t* s) {
+#pragma omp parallel
+  {
+    uint8_t u[32];
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      uint8_t* row = q + r * (K / 2);
+      memset(row, 0, (size_t)(K / 2));
+      for (int64_t g = 0; g < K / 32; ++g) {
+        s[r * (K / 32) + g] = quantize_group_mxfp4(w + r * K + g * 32, u);
+        for (int i = 0; i < 32; ++i) {
+          int64_t k = g * 32 + i;
+          row[packed_offset(k)] |= (uint8_t)((k & 1) ? (u[i] << 4) : u[i]);
+        }
+      }
+    }
   }
 }

@@ -114,3 +114,88 @@ def test_quantize_error_bound():
 def test_quantize_zero_group():
     u, s = F.quantize(np.zeros((2, 128), np.float32))
     assert np.all(s == 0) and np.all(u == 8)
+
+
+# ------------------------------------------------------------------ MXFP4
+
+
+def test_fp4_e2m1_every_code_against_the_spec_table():
+    """All 16 codes against the E2M1 table written out from the MX
+    specification (tests/golden/fp4_e2m1.txt), signed zero included."""
+    rows = golden_lines("fp4_e2m1.txt")
+    codes = np.array([int(r[0]) for r in rows])
+    want = np.array([float(r[1]) for r in rows])
+    got = F.fp4_e2m1_to_f64(codes)
+    assert len(codes) == 16 and np.array_equal(np.sort(codes), np.arange(16))
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_e8m0_scales_match_fp32_exponent_patterns():
+    """2^(b-127) for every byte: b = 1..254 is the fp32 pattern b << 23, b = 0
+    the subnormal 0x00400000 (2^-127), b = 255 NaN."""
+    b = np.arange(256)
+    got = F.e8m0_to_f64(b)
+    want = np.empty(256)
+    want[1:255] = (b[1:255].astype(np.uint32) << 23).view(np.float32)
+    want[0] = np.array([0x00400000], np.uint32).view(np.float32)[0]
+    assert np.array_equal(got[:255], want[:255]) and np.isnan(got[255])
+
+
+def test_mxfp4_dequant_hand_worked_row():
+    """One 128-element row: code 7 (6.0) at element 37 with scale byte 125
+    (1/4) in its block 1, code 9 (-0.5) at element 100 with scale byte 130 (8)
+    in block 3: w[37] = 1.5, w[100] = -4, every other element 0."""
+    u = np.zeros((1, 128), np.int64)
+    u[0, 37], u[0, 100] = 7, 9
+    s = np.array([[127, 125, 127, 130]], np.uint8)
+    w = F.dequant_mxfp4(F.pack_codes(u), s, 128)[0]
+    want = np.zeros(128)
+    want[37], want[100] = 1.5, -4.0
+    assert np.array_equal(w, want)
+
+
+def test_mxfp4_quantize_matches_brute_force():
+    """Shared exponent floor(log2 amax) - 2 (computed here with frexp) and
+    every element the nearest of the 16 codes' values at that scale, ties
+    to the even code, over random blocks of many magnitudes."""
+    rng = np.random.default_rng(11)
+    w = (rng.normal(0, 1, (64, 128)) * 2.0 ** rng.integers(-20, 10, (64, 1))).astype(np.float32)
+    w[3, :32] = 0.0  # one all-zero block
+    codes, sb = F.quantize_mxfp4(w)
+    vals = F.fp4_e2m1_to_f64(np.arange(16))
+    for r in range(w.shape[0]):
+        for g in range(4):
+            blk = w[r, 32 * g:32 * g + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert sb[r, g] == 127 and np.all(codes[r, 32 * g:32 * g + 32] == 0)
+                continue
+            _, e = np.frexp(amax)          # amax = m 2^e, 0.5 <= m < 1: floor(log2 amax) = e - 1
+            assert sb[r, g] == e - 1 - 2 + 127
+            scale = 2.0 ** (int(sb[r, g]) - 127)
+            for i, x in enumerate(blk):
+                d = np.abs(x - vals * scale)
+                d[8] = np.inf  # -0 is never chosen
+                best = np.flatnonzero(d == d.min())
+                pick = best[best % 2 == 0][0] if np.any(best % 2 == 0) else best[0]
+                assert F.fp4_e2m1_to_f64(codes[r, 32 * g + i]) == vals[pick], (r, g, i, x)
+
+
+def test_mxfp4_representable_values_round_trip():
+    """Weights that are MXFP4 values already come back unchanged (possibly
+    with another code/scale pair of equal value)."""
+    rng = np.random.default_rng(12)
+    u = rng.integers(0, 16, (32, 256))
+    s = rng.integers(100, 140, (32, 8)).astype(np.uint8)
+    w = F.dequant_mxfp4(F.pack_codes(u), s, 256)
+    c2, s2 = F.quantize_mxfp4(w.astype(np.float32))
+    assert np.array_equal(F.dequant_mxfp4(F.pack_codes(c2), s2, 256), w)
+
+
+def test_mxfp4_quantize_saturates_at_six():
+    """amax / 2^X lies in [4, 8): a block whose largest element is 7.9 * 2^X
+    stores it as 6 * 2^X (the largest E2M1 magnitude)."""
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0], w[0, 1] = 7.9, -7.9
+    c, s = F.quantize_mxfp4(w)
+    assert s[0, 0] == 127 and c[0, 0] == 7 and c[0, 1] == 15

@@ -317,3 +317,40 @@ def test_shared_active_weight_count():
     assert L.weights_read == E * d + (k + 1) * 3 * d * f == M.active_weights(E, d, f, k, 1)
     # the pages' layer: 256 routed experts, top-6 plus one shared, d=2048, f=512
     assert M.active_weights(256, 2048, 512, 6, 1) == 524288 + 7 * 3 * 2048 * 512
+
+
+# ------------------------------------------------------------------ MXFP4 layers
+
+
+def tiny_fp4_layer(seed=1):
+    return M.Layer.from_dict(synth.make_layer(synth.TINY_FP4, seed))
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_fp4_sparse_equals_mask_and_dense(seed):
+    """An MXFP4 layer: the sparse step equals all experts then mask (bit for
+    bit) and the independent dense einsum."""
+    L = tiny_fp4_layer(seed)
+    x = tiny_x(L, seed)
+    y = M.moe_forward(L, x, 2)["y"]
+    assert np.array_equal(y, M.moe_forward_masked(L, x, 2))
+    y2 = M.moe_forward_dense_einsum(L, x, 2)
+    np.testing.assert_allclose(y, y2, rtol=0, atol=1e-13 * np.abs(y2).max())
+
+
+def test_fp4_layer_reads_e2m1_values_times_power_of_two_scales():
+    """The MXFP4 layer's expert matrices are exactly the E2M1 table values
+    (tests/golden/fp4_e2m1.txt) times 2^(b-127): every weight divided by its
+    block's scale is one of the 15 distinct table values; and raising every
+    down scale byte by one doubles y exactly."""
+    L = tiny_fp4_layer(3)
+    table = {float(r[1]) for r in golden_lines("fp4_e2m1.txt")}
+    Wg, _, Wd = L.expert(0)
+    s = 2.0 ** (L.gate_s[0].astype(np.float64) - 127.0)
+    v = Wg.reshape(Wg.shape[0], -1, 32) / s[..., None]
+    assert set(np.unique(v).tolist()) <= table
+    x = tiny_x(L, 3)
+    y = M.moe_forward(L, x, 2)["y"]
+    L2 = tiny_fp4_layer(3)
+    L2.down_s = (L2.down_s.astype(np.int64) + 1).astype(np.uint8)
+    assert np.array_equal(M.moe_forward(L2, x, 2)["y"], 2 * y)

@@ -59,3 +59,30 @@ def test_zipf_bias_is_a_log_probability_vector():
     assert abs(p.sum() - 1) < 1e-5
     ranks = np.argsort(-p)
     assert np.allclose(p[ranks[0]] / p[ranks[1]], 2 ** 1.1, rtol=1e-5)
+
+
+def test_mxfp4_quantizer_agrees_with_oracle():
+    """The generator's MXFP4 quantizer (C) and the oracle's (numpy), written
+    independently from the MX conversion rule, agree bit for bit: on
+    N(0, 0.02) draws, on wide-range values, on exact ties and on zero blocks;
+    and an MXFP4 layer draws the same normals as the int4 one."""
+    rng = np.random.default_rng(5)
+    w = np.concatenate([
+        synth.normal_f32(64 * 256, synth.key(7, "fp4"), 0.0, 0.02).reshape(64, 256),
+        (rng.normal(0, 1, (64, 256)) * 2.0 ** rng.integers(-30, 30, (64, 1))),
+        # exact ties between neighbouring E2M1 values at scale 1 (block max 4)
+        np.tile(np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4), (8, 8)),
+        np.zeros((8, 256)),
+    ]).astype(np.float32)
+    q, s = synth.quantize_pack_mxfp4(w)
+    u, s2 = F.quantize_mxfp4(w)
+    np.testing.assert_array_equal(s, s2)
+    np.testing.assert_array_equal(q, F.pack_codes(u))
+    a = synth.make_layer(synth.TINY, 3)
+    b = synth.make_layer(synth.TINY_FP4, 3)
+    assert b["gate_s"].dtype == np.uint8 and b["gate_q"].shape == a["gate_q"].shape
+    np.testing.assert_array_equal(a["router_w"], b["router_w"])
+    # same draws: the MXFP4 weights are within half a step of the int4 ones' source values
+    Wi = F.dequant(a["gate_q"][0], a["gate_s"][0], 256)
+    Wf = F.dequant_mxfp4(b["gate_q"][0], b["gate_s"][0], 256)
+    assert np.corrcoef(Wi.ravel(), Wf.ravel())[0, 1] > 0.95
