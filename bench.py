@@ -194,8 +194,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extras", action="store_true", help="skip stack, batch, LM head and CPU legs")
-    ap.add_argument("--extras", default="stack,batch,prefill,flint,lmhead,cpu",
-                    help="comma list of the legs run after the headline (stack, batch, prefill, flint, lmhead, cpu)")
+    ap.add_argument("--extras", default="stack,batch,prefill,flint,fp4,lmhead,cpu",
+                    help="comma list of the legs run after the headline (stack, batch, prefill, flint, fp4, lmhead, cpu)")
     ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (reference for HBM byte counters)")
@@ -438,6 +438,36 @@ def main():
         for L in fl:
             L.close()
         del fl
+
+    if "fp4" in extras:
+        # MXFP4 experts (E2M1 codes, E8M0 scale per 32): the same draws as the
+        # pool's first 16 layers quantized to FP4 (6.7 GB, beyond the
+        # memory-side cache), 1-token steps graph-timed like the headline
+        PF = min(16, P)
+        f4 = [M.MoELayer.create(M.upload(synth.make_layer(synth.LAYER_FP4, args.seed, l), dev), d, f, E, k, 1, 1)
+              for l in range(PF)]
+        y4 = torch.empty((1, d), dtype=torch.float32, device=dev)
+
+        def fp4_step(i):
+            l = i % PF
+            t = (i // PF) % args.tokens
+            M.moe_decode_forward(f4[l].handle, X[l, t:t + 1], 1, y4, None, None, stream)
+
+        try:
+            f4s, _g = time_graph(fp4_step, 30 * PF, PF, stream)
+            del _g
+        except Exception as e:
+            log(f"fp4 graph failed: {e!r}")
+            f4s = time_eager(fp4_step, 30 * PF, PF, stream)
+        us = f4s / (30 * PF) * 1e6
+        per_expert4 = 3 * f * d // 2 + 3 * f * (d // 32)  # codes + one E8M0 byte per 32
+        b4 = E * d * 4 + d * 2 + k * per_expert4 + d * 4
+        out["mxfp4_layer"] = {"us_per_step": round(us, 3), "tokens_per_s": round(1 / (us * 1e-6), 1),
+                              "bytes_per_step": int(b4), "achieved_gbs": round(b4 / (us * 1e-6) / 1e9, 1),
+                              "frac": round(b4 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "pool_layers": PF}
+        for L in f4:
+            L.close()
+        del f4
 
     if "lmhead" in extras:
         # LM head: rotate over 4 copies

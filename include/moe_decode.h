@@ -73,9 +73,20 @@ typedef int32_t moe_status;
  *              shape whose output is added with weight 1 (the pages' layer
  *              has six routed experts plus one shared, "Flint 40B: Best Mid
  *              Sized LLM", transcript 02:35); it takes no part in the
- *              softmax or the renormalization */
+ *              softmax or the renormalization
+ *   weight_format  MOE_WEIGHTS_INT4 or MOE_WEIGHTS_MXFP4 (the pages name an
+ *              FP4 format for the released model, "Recursive Releases
+ *              Flint...", section "Quantization"): MXFP4 expert matrices
+ *              hold FP4 E2M1 codes at the int4 nibble positions with one
+ *              E8M0 scale byte 2^(b-127) per 32 elements (OCP MX v1.0).
+ *              MXFP4 layers run the single-launch 1-token step only:
+ *              max_tokens must be 1 and (d, f) one of its shapes, else
+ *              MOE_ERR_UNSUPPORTED; scale byte 255 (NaN) is not supported */
+#define MOE_WEIGHTS_INT4 0
+#define MOE_WEIGHTS_MXFP4 1
 typedef struct {
   int32_t d, f, n_experts, top_k, norm_topk, max_tokens, n_shared;
+  int32_t weight_format;
 } moe_layer_desc;
 
 /* Weights of one MoE layer (device, read-only, owned by the caller, must
@@ -85,6 +96,9 @@ typedef struct {
  *   gate_q    int4 [E][f][d/2] stored format, gate_s binary16 [E][f][d/32]
  *   up_q      int4 [E][f][d/2],                up_s   binary16 [E][f][d/32]
  *   down_q    int4 [E][d][f/2],                down_s binary16 [E][d][f/32]
+ *   with weight_format MOE_WEIGHTS_MXFP4 each *_q holds E2M1 codes and each
+ *             *_s points to E8M0 bytes [...][K/32] (same shapes, one byte
+ *             per scale; pass the byte array's address in the field)
  *   shared_*  the shared expert's matrices in the same formats without the
  *             expert dimension ([f][d/2], [f][d/32], [d][f/2], [d][f/32]);
  *             required when n_shared = 1, ignored (may be NULL) otherwise */

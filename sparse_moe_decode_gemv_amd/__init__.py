@@ -28,6 +28,8 @@ MOE_ERR_UNSUPPORTED = -6
 MOE_MAX_TOPK = 16
 MOE_MAX_TOKENS = 4096
 MOE_LMHEAD_MAX_B = 16
+WEIGHTS_INT4 = 0    # int4 codes, binary16 scales per 32
+WEIGHTS_MXFP4 = 1   # FP4 E2M1 codes, E8M0 scale bytes per 32
 
 EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
@@ -45,7 +47,7 @@ class MoEError(RuntimeError):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("f", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("norm_topk", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 WEIGHT_NAMES = ("router_w", "router_b", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
@@ -191,7 +193,9 @@ class MoELayer:
         and shared_gate_q ... shared_down_s when the layer has a shared expert."""
         import torch
         n_shared = 1 if tensors.get("shared_gate_q") is not None else 0
-        desc = LayerDesc(d, f, E, k, norm_topk, max_tokens, n_shared)
+        # byte scales: MXFP4 (E8M0); 16-bit scales: int4 (binary16)
+        fmt = WEIGHTS_MXFP4 if tensors["gate_s"].dtype == torch.uint8 else WEIGHTS_INT4
+        desc = LayerDesc(d, f, E, k, norm_topk, max_tokens, n_shared, fmt)
         nbytes = moe_decode_workspace_bytes(desc)
         if nbytes == 0:
             raise MoEError(MOE_ERR_SHAPE, "moe_decode_workspace_bytes")

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
@@ -34,9 +34,15 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->max_tokens > MOE_MAX_TOKENS || d->n_experts > 1024) return MOE_ERR_SHAPE;
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_ERR_SHAPE;
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_ERR_SHAPE;
+  if (d->weight_format != MOE_WEIGHTS_INT4 && d->weight_format != MOE_WEIGHTS_MXFP4) return MOE_ERR_SHAPE;
   if (d->d % 32 || d->f % 32) return MOE_ERR_SHAPE;
   if (!is_pow2(d->d) || d->d < 256 || d->d > 8192) return MOE_ERR_UNSUPPORTED;
   if (!is_pow2(d->f) || d->f < 128 || d->f > 4096) return MOE_ERR_UNSUPPORTED;
+  // MXFP4: the single-launch 1-token step only
+  if (d->weight_format == MOE_WEIGHTS_MXFP4 &&
+      (d->max_tokens != 1 ||
+       !moe::fused_layer_supported(d->d, d->f, d->n_experts, d->top_k, d->n_shared, moe::kFusedGridCUs)))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -112,6 +118,7 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.sh_gate_q = a.sh_gate_q, f.sh_gate_s = a.sh_gate_s, f.sh_up_q = a.sh_up_q, f.sh_up_s = a.sh_up_s;
   f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
   f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
+  f.fp4 = h->desc.weight_format == MOE_WEIGHTS_MXFP4;
   return f;
 }
 

@@ -158,6 +158,67 @@ __device__ __forceinline__ float dot_piece_f16(uint4 q, const Slice8 xs[4], uint
   return p;
 }
 
+// ---------------------------------------------------------------- MXFP4
+// FP4 E2M1 codes at the int4 nibble positions (byte b of a dword holds the
+// elements 2b, low nibble, and 2b+1), one E8M0 scale byte 2^(b-127) per 32
+// elements.  gfx950 turns a byte's two codes into a bf16 or fp16 pair in one
+// instruction (exact: E2M1 values have two significant bits, so products
+// with bf16 or fp16 activations are exact in fp32), and the block scale
+// multiplies the block's fp32 sum through ldexp (exact).  Activation slices
+// hold their 8 values as they are, pairs (v0,v1) .. (v6,v7).
+
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair_f16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
+}
+
+// 8 bf16 activations as stored (4 pairs).
+__device__ __forceinline__ Slice8 make_slice_raw(uint4 q) { return Slice8{q.x, q.y, q.z, q.w, 0.f}; }
+
+// From 8 fp32 activations, rounded to fp16, in pairs.
+__device__ __forceinline__ Slice8 make_slice_f16_raw(const float v[8]) {
+  return Slice8{pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]), pack_f16(v[6], v[7]), 0.f};
+}
+
+__device__ __forceinline__ float e8m0_scaled(float v, uint32_t sc, int j) {
+  return ldexpf(v, (int)((sc >> (8 * j)) & 0xFFu) - 127);
+}
+
+// sum_e e2m1(c_e) x_e over one dword's 8 codes
+__device__ __forceinline__ float dot8_fp4(uint32_t w, const Slice8& s) {
+  float acc = dot2_bf16(fp4_pair_bf16<0>(w), s.p0, 0.f);
+  acc = dot2_bf16(fp4_pair_bf16<1>(w), s.p1, acc);
+  acc = dot2_bf16(fp4_pair_bf16<2>(w), s.p2, acc);
+  return dot2_bf16(fp4_pair_bf16<3>(w), s.p3, acc);
+}
+__device__ __forceinline__ float dot8_fp4_f16(uint32_t w, const Slice8& s) {
+  float acc = dot2_f16(fp4_pair_f16<0>(w), s.p0, 0.f);
+  acc = dot2_f16(fp4_pair_f16<1>(w), s.p1, acc);
+  acc = dot2_f16(fp4_pair_f16<2>(w), s.p2, acc);
+  return dot2_f16(fp4_pair_f16<3>(w), s.p3, acc);
+}
+
+// One 16-byte piece (dword j in scale block j of the four) against bf16
+// (dot_piece_fp4) or fp16 (dot_piece_fp4_f16) slices; sc = the 4 scale bytes.
+__device__ __forceinline__ float dot_piece_fp4(uint4 q, const Slice8 xs[4], uint32_t sc) {
+  float p = e8m0_scaled(dot8_fp4(q.x, xs[0]), sc, 0);
+  p += e8m0_scaled(dot8_fp4(q.y, xs[1]), sc, 1);
+  p += e8m0_scaled(dot8_fp4(q.z, xs[2]), sc, 2);
+  p += e8m0_scaled(dot8_fp4(q.w, xs[3]), sc, 3);
+  return p;
+}
+__device__ __forceinline__ float dot_piece_fp4_f16(uint4 q, const Slice8 xs[4], uint32_t sc) {
+  float p = e8m0_scaled(dot8_fp4_f16(q.x, xs[0]), sc, 0);
+  p += e8m0_scaled(dot8_fp4_f16(q.y, xs[1]), sc, 1);
+  p += e8m0_scaled(dot8_fp4_f16(q.z, xs[2]), sc, 2);
+  p += e8m0_scaled(dot8_fp4_f16(q.w, xs[3]), sc, 3);
+  return p;
+}
+
 // ---- cross-lane reductions (VALU only: DPP and gfx950 permlane swaps) ------
 // Steps pair lanes within growing aligned segments: quad_perm [1,0,3,2] and
 // [2,3,0,1] (segments of 2 and 4), row_half_mirror (8), row_mirror (16),

@@ -93,8 +93,9 @@ __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
 
 // D hidden, F expert width, KP expert slots (top_k, plus one with a shared
 // expert, SH) rounded up to a power of two, EPL
-// experts per lane in the top-k wave.
-template <int D, int F, int KP, int EPL, bool NORM, bool SH>
+// experts per lane in the top-k wave; FP4: MXFP4 expert weights (E2M1 codes,
+// one E8M0 scale byte per 32) instead of int4 with binary16 scales.
+template <int D, int F, int KP, int EPL, bool NORM, bool SH, bool FP4>
 __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
@@ -151,6 +152,16 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   const int c0 = has_gate ? (wg - gslot * wpe) * 64 * NL : 0;
   uint4 qg[NL], qu[NL];
   uint2 sg[NL], su[NL];
+  // the 4 scales of a piece: 4 binary16 (int4) or 4 E8M0 bytes (FP4, in .x)
+  auto load_scales = [&](const uint16_t* base, size_t i) -> uint2 {
+    if constexpr (FP4) return make_uint2(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + i), 0u);
+    else return *reinterpret_cast<const uint2*>(base + i);
+  };
+  // scale array of expert e (scales counted in elements of either size)
+  auto scales_of = [&](const uint16_t* base, size_t e_off) -> const uint16_t* {
+    if constexpr (FP4) return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + e_off);
+    else return base + e_off;
+  };
   auto load_mats = [&](const uint8_t* gq8, const uint16_t* gsb, const uint8_t* uq8, const uint16_t* usb) {
     const uint4* gp = reinterpret_cast<const uint4*>(gq8);
     const uint4* up = reinterpret_cast<const uint4*>(uq8);
@@ -160,15 +171,15 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       qg[n] = gp[c];
       qu[n] = up[c];
       const size_t so = (size_t)(c / CPR) * CPR + ((c % CPR) & ~3);
-      sg[n] = *reinterpret_cast<const uint2*>(gsb + so);
-      su[n] = *reinterpret_cast<const uint2*>(usb + so);
+      sg[n] = load_scales(gsb, so);
+      su[n] = load_scales(usb, so);
     }
   };
   auto load_gate = [&](int e_raw) {
     const int e = min(max(e_raw, 0), E - 1);
     const size_t mat = (size_t)F * CPR;
-    load_mats(a.gate_q + (size_t)e * mat * 16, a.gate_s + (size_t)e * mat, a.up_q + (size_t)e * mat * 16,
-              a.up_s + (size_t)e * mat);
+    load_mats(a.gate_q + (size_t)e * mat * 16, scales_of(a.gate_s, (size_t)e * mat), a.up_q + (size_t)e * mat * 16,
+              scales_of(a.up_s, (size_t)e * mat));
   };
   // the shared expert needs no routing: its slot's loads go out now, behind
   // the router rows, and land while the logits are exchanged
@@ -284,14 +295,22 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       const int c = CPR > 64 ? 64 * s + lane : lane % CPR;
       const int base = 128 * (c >> 2) + 8 * (c & 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xs[s][j] = make_slice_bf16(x4((base + 32 * j) >> 3));
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (FP4) xs[s][j] = make_slice_raw(x4((base + 32 * j) >> 3));
+        else xs[s][j] = make_slice_bf16(x4((base + 32 * j) >> 3));
+      }
     }
     float ag = 0.f, au = 0.f;
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
       const int s = CPR > 64 ? n % XS : 0;
-      ag += dot_piece(qg[n], xs[s], sg[n]);
-      au += dot_piece(qu[n], xs[s], su[n]);
+      if constexpr (FP4) {
+        ag += dot_piece_fp4(qg[n], xs[s], sg[n].x);
+        au += dot_piece_fp4(qu[n], xs[s], su[n].x);
+      } else {
+        ag += dot_piece(qg[n], xs[s], sg[n]);
+        au += dot_piece(qu[n], xs[s], su[n]);
+      }
       if (n % LPRG == LPRG - 1) {
         // row within this workgroup's ROWS_G consecutive rows of slot gslot
         if constexpr (CPR >= 64) {
@@ -318,7 +337,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     float hv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) hv[e] = s_hv[8 * threadIdx.x + e];
-    const Slice8 sl = make_slice_f16(hv);
+    const Slice8 sl = FP4 ? make_slice_f16_raw(hv) : make_slice_f16(hv);
     s_pub[5 * threadIdx.x + 0] = sl.p0, s_pub[5 * threadIdx.x + 1] = sl.p1, s_pub[5 * threadIdx.x + 2] = sl.p2;
     s_pub[5 * threadIdx.x + 3] = sl.p3, s_pub[5 * threadIdx.x + 4] = __float_as_uint(sl.corr);
   }
@@ -362,7 +381,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       const bool shd = SH && dslot[m] >= k;  // the shared expert's slot
       const size_t eb = shd ? (size_t)row : (size_t)min(max(s_idx[dslot[m]], 0), E - 1) * D + row;
       qd[n] = *reinterpret_cast<const uint4*>((shd ? a.sh_down_q : a.down_q) + piece_offset(eb, CPRF, cc[m]));
-      sd[n] = *reinterpret_cast<const uint2*>((shd ? a.sh_down_s : a.down_s) + eb * CPRF + (cc[m] & ~3));
+      sd[n] = load_scales(shd ? a.sh_down_s : a.down_s, eb * CPRF + (cc[m] & ~3));
     } else {
       qd[n] = make_uint4(0, 0, 0, 0);
       sd[n] = make_uint2(0, 0);
@@ -424,7 +443,8 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int m = n % LPRD;
-      acc += dot_piece_f16(qd[n], hs8[m], sd[n]);
+      if constexpr (FP4) acc += dot_piece_fp4_f16(qd[n], hs8[m], sd[n].x);
+      else acc += dot_piece_f16(qd[n], hs8[m], sd[n]);
       if (n % LPRD == LPRD - 1) {
         if constexpr (P >= 64) {
           const float v = wave_sum(acc);
@@ -442,21 +462,26 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
 // ---------------------------------------------------------------- host side
 
-template <int D, int F, int KP, int EPL>
-static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
+template <int D, int F, int KP, int EPL, bool FP4>
+static hipError_t layer_launch_fmt(const FusedArgs& a, int G, hipStream_t s) {
   const size_t lds = (size_t)(a.k + a.ns) * (F / 8) * 5 * sizeof(unsigned);
   if (a.ns) {
     if (a.resid_in)
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true, FP4>), dim3(G), dim3(256), lds, s, a);
     else
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, true>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, true, FP4>), dim3(G), dim3(256), lds, s, a);
   } else {
     if (a.resid_in)
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, false>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, false, FP4>), dim3(G), dim3(256), lds, s, a);
     else
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, false>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, false, FP4>), dim3(G), dim3(256), lds, s, a);
   }
   return hipGetLastError();
+}
+
+template <int D, int F, int KP, int EPL>
+static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
+  return a.fp4 ? layer_launch_fmt<D, F, KP, EPL, true>(a, G, s) : layer_launch_fmt<D, F, KP, EPL, false>(a, G, s);
 }
 
 template <int D, int F, int KP>

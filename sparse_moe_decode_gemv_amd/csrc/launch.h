@@ -94,6 +94,7 @@ struct FusedArgs {
   const uint8_t* sh_down_q;
   const uint16_t* sh_down_s;
   int E, k, norm, ns;
+  int fp4;  // 1: MXFP4 expert weights (the *_s pointers hold E8M0 bytes)
 };
 
 // The whole 1-token step in one launch, for the shapes it is built for

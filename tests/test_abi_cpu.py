@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert L.moe_decode_abi_version() == 2
+    assert L.moe_decode_abi_version() == 3
 
 
 def test_status_strings():
@@ -60,7 +60,8 @@ def test_workspace_bytes_layout():
 
 @pytest.mark.parametrize("kw", [dict(top_k=0), dict(top_k=17), dict(top_k=300, n_experts=256), dict(max_tokens=0),
                                 dict(max_tokens=4097), dict(d=2040), dict(f=500), dict(norm_topk=2),
-                                dict(n_experts=2000), dict(d=0), dict(n_shared=2), dict(n_shared=-1)])
+                                dict(n_experts=2000), dict(d=0), dict(n_shared=2), dict(n_shared=-1),
+                                dict(weight_format=2), dict(weight_format=-1)])
 def test_bad_shapes_have_no_workspace(kw):
     assert M.moe_decode_workspace_bytes(desc(**kw)) == 0
 
@@ -146,3 +147,14 @@ def test_python_errors_are_raised():
     with pytest.raises(M.MoEError) as ei:
         M.lmhead_int4_argmax(None, FAKE, 16, 256, FAKE, 1, FAKE, None, FAKE, 1 << 20, stream=0)
     assert ei.value.status == M.MOE_ERR_NULL
+
+
+def test_mxfp4_layers_are_single_launch_only():
+    """MXFP4 layers: accepted on the single-launch shapes at max_tokens = 1
+    (no tile-major copy in the workspace); max_tokens > 1 or another shape is
+    MOE_ERR_UNSUPPORTED."""
+    fp4 = dict(weight_format=M.WEIGHTS_MXFP4)
+    assert 0 < M.moe_decode_workspace_bytes(desc(**fp4)) <= M.moe_decode_workspace_bytes(desc())
+    assert M.moe_decode_workspace_bytes(desc(**fp4)) < M.moe_decode_workspace_bytes(desc(max_tokens=2))
+    assert init_status(desc(max_tokens=2, **fp4), weights())[0] == M.MOE_ERR_UNSUPPORTED
+    assert init_status(desc(d=1024, f=256, **fp4), weights())[0] == M.MOE_ERR_UNSUPPORTED
