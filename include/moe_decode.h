@@ -78,10 +78,10 @@ typedef int32_t moe_status;
  *              FP4 format for the released model, "Recursive Releases
  *              Flint...", section "Quantization"): MXFP4 expert matrices
  *              hold FP4 E2M1 codes at the int4 nibble positions with one
- *              E8M0 scale byte 2^(b-127) per 32 elements (OCP MX v1.0).
- *              MXFP4 layers run the single-launch 1-token step only:
- *              max_tokens must be 1 and (d, f) one of its shapes, else
- *              MOE_ERR_UNSUPPORTED; scale byte 255 (NaN) is not supported */
+ *              E8M0 scale byte 2^(b-127) per 32 elements (OCP MX v1.0);
+ *              scale byte 255 (NaN) is not supported, and the batched
+ *              (T > 1) kernels, which round each weight to fp16, are exact
+ *              for scale bytes 104..140 */
 #define MOE_WEIGHTS_INT4 0
 #define MOE_WEIGHTS_MXFP4 1
 typedef struct {

@@ -38,11 +38,6 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->d % 32 || d->f % 32) return MOE_ERR_SHAPE;
   if (!is_pow2(d->d) || d->d < 256 || d->d > 8192) return MOE_ERR_UNSUPPORTED;
   if (!is_pow2(d->f) || d->f < 128 || d->f > 4096) return MOE_ERR_UNSUPPORTED;
-  // MXFP4: the single-launch 1-token step only
-  if (d->weight_format == MOE_WEIGHTS_MXFP4 &&
-      (d->max_tokens != 1 ||
-       !moe::fused_layer_supported(d->d, d->f, d->n_experts, d->top_k, d->n_shared, moe::kFusedGridCUs)))
-    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -118,7 +113,7 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.sh_gate_q = a.sh_gate_q, f.sh_gate_s = a.sh_gate_s, f.sh_up_q = a.sh_up_q, f.sh_up_s = a.sh_up_s;
   f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
   f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
-  f.fp4 = h->desc.weight_format == MOE_WEIGHTS_MXFP4;
+  f.fp4 = a.fp4;
   return f;
 }
 
@@ -178,6 +173,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   moe::LayerArgs& a = h->args;
   a.d = desc->d, a.f = desc->f, a.E = desc->n_experts, a.k = desc->top_k, a.norm_topk = desc->norm_topk;
   a.ns = desc->n_shared;
+  a.fp4 = desc->weight_format == MOE_WEIGHTS_MXFP4;
   a.router_w = w->router_w, a.router_b = w->router_b;
   a.gate_q = w->gate_q, a.gate_s = w->gate_s, a.up_q = w->up_q, a.up_s = w->up_s;
   a.down_q = w->down_q, a.down_s = w->down_s;

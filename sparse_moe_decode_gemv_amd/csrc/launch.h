@@ -13,6 +13,7 @@ namespace moe {
 struct LayerArgs {
   int d, f, E, k, norm_topk;
   int ns;  // shared experts, 0 or 1: expert index E of the tile-major copies, assignments T*k + t
+  int fp4;  // 1: MXFP4 experts (codes E2M1, the *_s pointers and the tile scale copies hold E8M0 bytes)
   const float* router_w;
   const float* router_b;
   const uint8_t* gate_q;

@@ -217,6 +217,7 @@ TINY_SHARED = replace(TINY, shared=1)
 TINY_FP4 = replace(TINY, name="tiny_fp4", fmt="mxfp4")
 LAYER_FP4 = replace(LAYER, name="layer_fp4", fmt="mxfp4")
 FLINT_FP4 = replace(FLINT, name="flint_fp4", fmt="mxfp4")
+BATCH_FP4 = replace(BATCH, name="batch_fp4", fmt="mxfp4")
 LMHEAD1 = LMHeadConfig("lmhead", V=131072, d=2048, B=1)
 LMHEAD8 = replace(LMHEAD1, B=8)
 
