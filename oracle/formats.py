@@ -33,6 +33,17 @@ target hardware decodes natively:
   one scale per 32 consecutive elements along K;
 * stored: codes at the int4 nibble positions above, scale bytes [rows][K/32].
 
+NVFP4 (the format the pages name; its public definition): the same E2M1
+codes at the same positions, one FP8 E4M3 scale per 16 elements along K
+(OCP E4M3FN: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+448, S.1111.111 is NaN, no infinity) and one fp32 scale per tensor (here per
+expert matrix); w = e2m1(c) * e4m3(s_block) * s_tensor.  Stored: codes as
+above, scale bytes [rows][K/16], tensor scales fp32 [E].  Its two-level
+quantizer: s_tensor = amax(matrix) / (6 * 448); per block the E4M3 value
+nearest to amax(block) / 6 / s_tensor (ties to even, at most 448); then each
+element w / (e4m3(s_block) * s_tensor) to the nearest E2M1 value as for
+MXFP4; a zero block (or matrix) gets scale 0 and codes 0.
+
 MXFP4 quantizer (the MX specification's conversion): per block a = max|w|;
 a == 0 gives scale byte 127 and all codes 0; otherwise the shared exponent is
 X = floor(log2 a) - 2 (2 = the largest E2M1 exponent), the scale byte X + 127
@@ -187,3 +198,64 @@ def quantize_mxfp4(w: np.ndarray):
     code = np.where(a[..., None] > 0, code, 0)
     b = np.where(a > 0, b, 127)
     return code.reshape(w.shape).astype(np.int64), b.astype(np.uint8)
+
+
+# ------------------------------------------------------------------ NVFP4
+
+
+def e4m3_to_f64(b) -> np.ndarray:
+    """FP8 E4M3 (OCP E4M3FN) bytes -> fp64 from the bit fields; S.1111.111 is NaN."""
+    b = np.asarray(b, dtype=np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * val)
+
+
+E4M3_POSITIVE = e4m3_to_f64(np.arange(0x7F))  # codes 0x00..0x7E, ascending
+
+
+def f64_to_e4m3(x) -> np.ndarray:
+    """Non-negative fp64 -> nearest E4M3 byte (ties to the even code), saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    dist = np.abs(x[..., None] - E4M3_POSITIVE)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = np.where(dist == best, np.arange(0x7F), 999)
+    even = np.where(cand % 2 == 0, cand, 999).min(axis=-1)
+    return np.where(even < 999, even, cand.min(axis=-1)).astype(np.uint8)
+
+
+def dequant_nvfp4(qbytes: np.ndarray, sbytes: np.ndarray, tscale, K: int) -> np.ndarray:
+    """Stored NVFP4 matrix -> fp64 weights [..., K]: e2m1(c) * e4m3(s[k // 16]) * tscale."""
+    v = fp4_e2m1_to_f64(unpack_codes(qbytes, K))
+    s = e4m3_to_f64(sbytes)
+    w = (v.reshape(v.shape[:-1] + (K // 16, 16)) * s[..., None]).reshape(v.shape)
+    t = np.asarray(tscale, dtype=np.float32).astype(np.float64)
+    return w * t.reshape(t.shape + (1,) * (w.ndim - t.ndim))
+
+
+def nearest_e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """Signed values -> nearest E2M1 code (ties to the even code, |v| > 6 to 6, zero -> code 0)."""
+    a = np.abs(v)
+    dist = np.abs(a[..., None] - E2M1_MAGNITUDES)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = np.where(dist == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))
+    return np.where((v < 0) & (code > 0), code | 8, code).astype(np.int64)
+
+
+def quantize_nvfp4(w: np.ndarray):
+    """fp32 matrix [rows][K] -> (E2M1 codes [rows][K], E4M3 scale bytes [rows][K/16], fp32 tensor scale)."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    rows, K = w.shape
+    t = np.float32(np.abs(w).max() / (6.0 * 448.0))
+    if t == 0:
+        return np.zeros((rows, K), np.int64), np.zeros((rows, K // 16), np.uint8), np.float32(0.0)
+    g = w.reshape(rows, K // 16, 16)
+    sb = f64_to_e4m3(np.abs(g).max(axis=-1) / 6.0 / np.float64(t))
+    s = e4m3_to_f64(sb) * np.float64(t)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s[..., None] > 0, g / s[..., None], 0.0)
+    return nearest_e2m1_codes(v).reshape(rows, K), sb, t

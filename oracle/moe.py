@@ -15,8 +15,9 @@ follows (each reading is also listed in the design notes):
   (norm_topk=True) or kept as the softmax values (norm_topk=False);
 * expert: SwiGLU, h = silu(W_g x) * (W_u x) with silu(z) = z / (1 + e^-z),
   then o = W_d h, all on dequantized 4-bit weights in fp64 (int4 with fp16
-  scales, or MXFP4 -- E2M1 codes with E8M0 scales -- when the scale arrays
-  hold bytes; formats.py);
+  scales; MXFP4 -- E2M1 codes with E8M0 scales -- when the scale arrays
+  hold bytes; NVFP4 -- E2M1 codes, E4M3 scales per 16, an fp32 scale per
+  matrix -- when the layer carries tensor scales; formats.py);
 * combine: y = sum over chosen experts of w_j o_j, added in ascending expert
   index, rounded once to fp32 for comparison;
 * shared expert (the pages' layer adds one always-on expert to the routed
@@ -35,13 +36,16 @@ from itertools import combinations
 
 import numpy as np
 
-from .formats import bf16_to_f64, dequant, dequant_mxfp4, f64_to_bf16_bits, f64_to_f32
+from .formats import bf16_to_f64, dequant, dequant_mxfp4, dequant_nvfp4, f64_to_bf16_bits, f64_to_f32
 
 
-def dequant_4bit(q: np.ndarray, s: np.ndarray, K: int) -> np.ndarray:
-    """A stored 4-bit matrix in either format: byte scales mean MXFP4 (E8M0),
-    16-bit scales int4 (binary16)."""
+def dequant_4bit(q: np.ndarray, s: np.ndarray, K: int, t=None) -> np.ndarray:
+    """A stored 4-bit matrix in any of the formats: a tensor scale t means
+    NVFP4 (E4M3 per 16), else byte scales MXFP4 (E8M0 per 32), else int4
+    (binary16 per 32)."""
     s = np.asarray(s)
+    if t is not None:
+        return dequant_nvfp4(q, s, t, K)
     return dequant_mxfp4(q, s, K) if s.dtype == np.uint8 else dequant(q, s, K)
 
 
@@ -59,14 +63,26 @@ class Layer:
     down_s: np.ndarray              # uint16 [E][d][f/32]
     shared: tuple | None = None     # (gate_q, gate_s, up_q, up_s, down_q, down_s) of the shared expert, or None
     weights_read: int = field(default=0)
+    tscales: dict | None = None     # NVFP4: fp32 tensor scales gate_ts/up_ts/down_ts [E] (+ shared_*_ts scalars)
 
     @classmethod
     def from_dict(cls, t: dict) -> "Layer":
         sh = None
         if t.get("shared_gate_q") is not None:
             sh = tuple(t["shared_" + n] for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s"))
+        ts = None
+        if t.get("gate_ts") is not None:
+            ts = {n: t[n] for n in ("gate_ts", "up_ts", "down_ts", "shared_gate_ts", "shared_up_ts",
+                                    "shared_down_ts") if t.get(n) is not None}
         return cls(t["router_w"], t.get("router_b"), t["gate_q"], t["gate_s"], t["up_q"], t["up_s"],
-                   t["down_q"], t["down_s"], sh)
+                   t["down_q"], t["down_s"], sh, tscales=ts)
+
+    def _t(self, name: str, e=None):
+        """Tensor scale of a matrix (NVFP4), or None."""
+        if self.tscales is None:
+            return None
+        v = np.asarray(self.tscales[name])
+        return v if e is None else v[e]
 
     @property
     def E(self) -> int:
@@ -83,16 +99,18 @@ class Layer:
     def expert(self, e: int):
         """Dequantized (W_g [f][d], W_u [f][d], W_d [d][f]) of expert e, counted as read."""
         d, f = self.d, self.f
-        Wg = dequant_4bit(self.gate_q[e], self.gate_s[e], d)
-        Wu = dequant_4bit(self.up_q[e], self.up_s[e], d)
-        Wd = dequant_4bit(self.down_q[e], self.down_s[e], f)
+        Wg = dequant_4bit(self.gate_q[e], self.gate_s[e], d, self._t("gate_ts", e))
+        Wu = dequant_4bit(self.up_q[e], self.up_s[e], d, self._t("up_ts", e))
+        Wd = dequant_4bit(self.down_q[e], self.down_s[e], f, self._t("down_ts", e))
         self.weights_read += Wg.size + Wu.size + Wd.size
         return Wg, Wu, Wd
 
     def shared_expert(self):
         """Dequantized (W_g, W_u, W_d) of the shared expert, counted as read."""
         gq, gs, uq, us, dq, ds = self.shared
-        Wg, Wu, Wd = dequant_4bit(gq, gs, self.d), dequant_4bit(uq, us, self.d), dequant_4bit(dq, ds, self.f)
+        Wg = dequant_4bit(gq, gs, self.d, self._t("shared_gate_ts"))
+        Wu = dequant_4bit(uq, us, self.d, self._t("shared_up_ts"))
+        Wd = dequant_4bit(dq, ds, self.f, self._t("shared_down_ts"))
         self.weights_read += Wg.size + Wu.size + Wd.size
         return Wg, Wu, Wd
 
@@ -224,9 +242,9 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     chosen = np.lexsort((np.arange(layer.E), -p))[:k]
     wv = np.zeros(layer.E)
     wv[chosen] = p[chosen] / p[chosen].sum() if norm_topk else p[chosen]
-    Wg = dequant_4bit(layer.gate_q, layer.gate_s, layer.d)
-    Wu = dequant_4bit(layer.up_q, layer.up_s, layer.d)
-    Wd = dequant_4bit(layer.down_q, layer.down_s, layer.f)
+    Wg = dequant_4bit(layer.gate_q, layer.gate_s, layer.d, layer._t("gate_ts"))
+    Wu = dequant_4bit(layer.up_q, layer.up_s, layer.d, layer._t("up_ts"))
+    Wd = dequant_4bit(layer.down_q, layer.down_s, layer.f, layer._t("down_ts"))
     G = np.einsum("efd,d->ef", Wg, x)
     U = np.einsum("efd,d->ef", Wu, x)
     H = G / (1.0 + np.exp(-G)) * U
@@ -234,7 +252,8 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     y = np.einsum("e,ed->d", wv, O)
     if layer.shared is not None:
         gq, gs, uq, us, dq, ds = layer.shared
-        Ws = [dequant_4bit(gq, gs, layer.d), dequant_4bit(uq, us, layer.d), dequant_4bit(dq, ds, layer.f)]
+        Ws = [dequant_4bit(gq, gs, layer.d, layer._t("shared_gate_ts")), dequant_4bit(uq, us, layer.d, layer._t("shared_up_ts")),
+              dequant_4bit(dq, ds, layer.f, layer._t("shared_down_ts"))]
         gs_, us_ = np.einsum("fd,d->f", Ws[0], x), np.einsum("fd,d->f", Ws[1], x)
         y = y + np.einsum("df,f->d", Ws[2], gs_ / (1.0 + np.exp(-gs_)) * us_)
     return y

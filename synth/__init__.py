@@ -70,6 +70,9 @@ def lib():
         L.synth_quantize_pack.argtypes = [p, i64, i64, p, p]
         L.synth_mxfp4_experts.argtypes = [p, p, i64, i64, i64, u64, d]
         L.synth_quantize_pack_mxfp4.argtypes = [p, i64, i64, p, p]
+        L.synth_nvfp4_experts.argtypes = [p, p, p, i64, i64, i64, u64, d]
+        L.synth_quantize_nvfp4.restype = ctypes.c_float
+        L.synth_quantize_nvfp4.argtypes = [p, i64, i64, p, p]
         L.synth_pack_codes.argtypes = [p, i64, i64, p]
         L.synth_permutation.argtypes = [p, ctypes.c_int32, u64]
         _lib = L
@@ -137,6 +140,27 @@ def mxfp4_experts(E: int, rows: int, K: int, k: int, sigma: float):
     return q, s
 
 
+def nvfp4_experts(E: int, rows: int, K: int, k: int, sigma: float):
+    """NVFP4 counterpart of int4_experts (same draws): codes uint8 [E][rows][K/2],
+    E4M3 bytes [E][rows][K/16], fp32 tensor scales [E]."""
+    q = np.empty((E, rows, K // 2), np.uint8)
+    s = np.empty((E, rows, K // 16), np.uint8)
+    t = np.empty(E, np.float32)
+    lib().synth_nvfp4_experts(_ptr(q), _ptr(s), _ptr(t), E, rows, K, k, sigma)
+    return q, s, t
+
+
+def quantize_nvfp4(w: np.ndarray):
+    """Quantize a caller-given fp32 matrix [rows][K] into stored NVFP4 (codes, scale bytes, tensor scale)."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, K = w.shape
+    assert K % 128 == 0
+    q = np.empty((rows, K // 2), np.uint8)
+    s = np.empty((rows, K // 16), np.uint8)
+    t = lib().synth_quantize_nvfp4(_ptr(w), rows, K, _ptr(q), _ptr(s))
+    return q, s, np.float32(t)
+
+
 def quantize_pack_mxfp4(w: np.ndarray):
     """Quantize caller-given fp32 weights [rows][K] into stored MXFP4."""
     w = np.ascontiguousarray(w, np.float32)
@@ -192,7 +216,7 @@ class MoEConfig:
     layers: int = 1
     margin: float = 1e-2
     shared: int = 0          # always-on experts (0 or 1), same shape, weight 1
-    fmt: str = "int4"        # expert weights: "int4" (fp16 scales) or "mxfp4" (E2M1, E8M0 scales)
+    fmt: str = "int4"        # expert weights: "int4" (fp16 scales), "mxfp4" (E2M1, E8M0 scales) or "nvfp4"
 
 
 @dataclass(frozen=True)
@@ -218,6 +242,10 @@ TINY_FP4 = replace(TINY, name="tiny_fp4", fmt="mxfp4")
 LAYER_FP4 = replace(LAYER, name="layer_fp4", fmt="mxfp4")
 FLINT_FP4 = replace(FLINT, name="flint_fp4", fmt="mxfp4")
 BATCH_FP4 = replace(BATCH, name="batch_fp4", fmt="mxfp4")
+TINY_NV = replace(TINY, name="tiny_nv", fmt="nvfp4")
+LAYER_NV = replace(LAYER, name="layer_nv", fmt="nvfp4")
+FLINT_NV = replace(FLINT, name="flint_nv", fmt="nvfp4")
+BATCH_NV = replace(BATCH, name="batch_nv", fmt="nvfp4")
 LMHEAD1 = LMHeadConfig("lmhead", V=131072, d=2048, B=1)
 LMHEAD8 = replace(LMHEAD1, B=8)
 
@@ -237,12 +265,15 @@ def make_layer(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
     # the same layer, and layer 0 of the stack is that layer.
     base = (seed, "tiny" if cfg.d == TINY.d and cfg.E == TINY.E else "layer", layer)
     rw = normal_f32(E * d, key(*base, "router"), 0.0, cfg.router_sigma).reshape(E, d)
-    experts = mxfp4_experts if cfg.fmt == "mxfp4" else int4_experts
-    gq, gs = experts(E, f, d, key(*base, "gate"), cfg.expert_sigma)
-    uq, us = experts(E, f, d, key(*base, "up"), cfg.expert_sigma)
-    dq, ds = experts(E, d, f, key(*base, "down"), cfg.expert_sigma)
     rb = zipf_bias(cfg, seed) if cfg.zipf_s > 0 else None
-    out = dict(router_w=rw, router_b=rb, gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+    out = dict(router_w=rw, router_b=rb)
+    for name, rows, K in (("gate", f, d), ("up", f, d), ("down", d, f)):
+        if cfg.fmt == "nvfp4":
+            out[name + "_q"], out[name + "_s"], out[name + "_ts"] = nvfp4_experts(E, rows, K, key(*base, name),
+                                                                                  cfg.expert_sigma)
+        else:
+            experts = mxfp4_experts if cfg.fmt == "mxfp4" else int4_experts
+            out[name + "_q"], out[name + "_s"] = experts(E, rows, K, key(*base, name), cfg.expert_sigma)
     if cfg.shared:
         out.update(make_shared(cfg, seed, layer))
     return out
@@ -255,8 +286,12 @@ def make_shared(cfg: MoEConfig, seed: int, layer: int = 0) -> dict:
     base = (seed, "tiny" if cfg.d == TINY.d and cfg.E == TINY.E else "layer", layer)
     out = {}
     for name, rows, K in (("gate", f, d), ("up", f, d), ("down", d, f)):
-        experts = mxfp4_experts if cfg.fmt == "mxfp4" else int4_experts
-        q, sc = experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
+        if cfg.fmt == "nvfp4":
+            q, sc, ts = nvfp4_experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
+            out["shared_" + name + "_ts"] = ts
+        else:
+            experts = mxfp4_experts if cfg.fmt == "mxfp4" else int4_experts
+            q, sc = experts(1, rows, K, key(*base, "shared_" + name), cfg.expert_sigma)
         out["shared_" + name + "_q"], out["shared_" + name + "_s"] = q[0], sc[0]
     return out
 

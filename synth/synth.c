@@ -29,6 +29,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#include <stdlib.h>
 
 #define GAMMA 0x9E3779B97F4A7C15ull
 
@@ -311,4 +312,95 @@ void synth_quantize_pack_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t*
       }
     }
   }
+}
+
+/* Nearest E2M1 code of a magnitude v >= 0 (ties to the even code, above 6
+ * to 6). */
+static int e2m1_nearest(double v) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  int best = 0;
+  double bd = v;
+  for (int c = 1; c < 8; ++c) {
+    const double dd = fabs(v - mag[c]);
+    if (dd < bd || (dd == bd && (c & 1) == 0 && (best & 1) != 0)) {
+      best = c;
+      bd = dd;
+    }
+  }
+  return best;
+}
+
+/* Nearest OCP E4M3FN byte of x >= 0 (ties to even, at most 448 = 0x7E):
+ * x = m 2^e with 0.5 <= m < 1 has exponent field e + 6 when that is >= 1
+ * (mantissa (2m - 1) * 8 rounded), else it is a subnormal x / 2^-9. */
+static uint8_t e4m3_nearest(double x) {
+  if (!(x > 0.0)) return 0;
+  if (x >= 448.0) return 0x7E;
+  int e;
+  const double m = frexp(x, &e);
+  int E = e + 6;
+  if (E < 1) return (uint8_t)nearbyint(x * 512.0); /* 0..8; 8 is the smallest normal */
+  double mant = nearbyint((2.0 * m - 1.0) * 8.0);
+  if (mant >= 8.0) {
+    mant = 0.0;
+    ++E;
+  }
+  if (E > 15 || (E == 15 && mant >= 7.0)) return 0x7E;
+  return (uint8_t)((E << 3) | (int)mant);
+}
+
+static double e4m3_value(uint8_t b) {
+  const int E = (b >> 3) & 15, m = b & 7;
+  return E == 0 ? m * ldexp(1.0, -9) : (1.0 + m / 8.0) * ldexp(1.0, E - 7);
+}
+
+/* NVFP4 of one matrix [rows][K] (two-level: an fp32 tensor scale
+ * amax / (6 * 448), an E4M3 scale per 16 elements nearest to
+ * amax(block) / 6 / t, E2M1 codes nearest to w / (e4m3 * t)); returns t. */
+static float quantize_matrix_nvfp4(const float* w, int64_t rows, int64_t K, uint8_t* q, uint8_t* s) {
+  float amax = 0.f;
+  for (int64_t i = 0; i < rows * K; ++i) amax = fmaxf(amax, fabsf(w[i]));
+  const float t = (float)((double)amax / (6.0 * 448.0));
+  memset(q, 0, (size_t)(rows * K / 2));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < K / 16; ++b) {
+      const float* x = w + r * K + b * 16;
+      float ab = 0.f;
+      for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(x[i]));
+      const uint8_t sb = t > 0.f ? e4m3_nearest((double)ab / 6.0 / (double)t) : 0;
+      s[r * (K / 16) + b] = sb;
+      const double sc = e4m3_value(sb) * (double)t;
+      for (int i = 0; i < 16; ++i) {
+        const int c0 = sc > 0.0 ? e2m1_nearest(fabs((double)x[i]) / sc) : 0;
+        const int c = c0 | (x[i] < 0.f && c0 > 0 ? 8 : 0);
+        const int64_t k = b * 16 + i;
+        q[r * (K / 2) + packed_offset(k)] |= (uint8_t)((k & 1) ? (c << 4) : c);
+      }
+    }
+  return t;
+}
+
+/* E NVFP4 matrices [rows][K] from the same streams as synth_int4_experts. */
+void synth_nvfp4_experts(uint8_t* q, uint8_t* s, float* t, int64_t E, int64_t rows, int64_t K, uint64_t key,
+                         double sigma) {
+#pragma omp parallel
+  {
+    float* w = (float*)malloc((size_t)(rows * K) * sizeof(float));
+#pragma omp for schedule(static)
+    for (int64_t e = 0; e < E; ++e) {
+      const uint64_t ek = synth_key(key, (uint64_t)e);
+      for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < K / 32; ++g) {
+          float z[32];
+          normal_block32(ek, (uint64_t)(r * (K / 32) + g), z);
+          for (int i = 0; i < 32; ++i) w[r * K + g * 32 + i] = (float)(sigma * (double)z[i]);
+        }
+      t[e] = quantize_matrix_nvfp4(w, rows, K, q + e * rows * (K / 2), s + e * rows * (K / 16));
+    }
+    free(w);
+  }
+}
+
+float synth_quantize_nvfp4(const float* w, int64_t rows, int64_t K, uint8_t* q, uint8_t* s) {
+  return quantize_matrix_nvfp4(w, rows, K, q, s);
 }

@@ -199,3 +199,73 @@ def test_mxfp4_quantize_saturates_at_six():
     w[0, 0], w[0, 1] = 7.9, -7.9
     c, s = F.quantize_mxfp4(w)
     assert s[0, 0] == 127 and c[0, 0] == 7 and c[0, 1] == 15
+
+
+# ------------------------------------------------------------------ NVFP4
+
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn():
+    """All 256 E4M3 bytes against torch's float8_e4m3fn (the OCP E4M3FN
+    type): equal values and signs, NaN exactly at S.1111.111."""
+    import torch
+    b = np.arange(256)
+    got = F.e4m3_to_f64(b)
+    want = torch.from_numpy(b.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    nan = (b & 0x7F) == 0x7F
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(np.isnan(want), nan)
+    assert np.array_equal(got[~nan], want[~nan]) and np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_e4m3_encoder_matches_torch_rounding():
+    """The quantizer's E4M3 rounding (nearest, ties to even) against torch's
+    float -> float8_e4m3fn cast on values in [0, 448], ties included."""
+    import torch
+    rng = np.random.default_rng(13)
+    vals = F.e4m3_to_f64(np.arange(0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([rng.uniform(0, 448, 4000), rng.uniform(0, 2 ** -5, 2000), mids, vals])
+    got = F.e4m3_to_f64(F.f64_to_e4m3(x))
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(got, want)
+
+
+def test_nvfp4_dequant_hand_worked_row():
+    """One 128-element row: code 5 (3.0) at element 20 in block 1 with scale
+    byte 0x40 (E4M3 2.0), code 14 (-4.0) at element 71 in block 4 with scale
+    byte 0x31 (1.125 * 2^-1 = 0.5625), tensor scale 0.25:
+    w[20] = 3 * 2 * 0.25 = 1.5, w[71] = -4 * 0.5625 * 0.25 = -0.5625."""
+    u = np.zeros((1, 128), np.int64)
+    u[0, 20], u[0, 71] = 5, 14
+    s = np.zeros((1, 8), np.uint8)
+    s[0, 1], s[0, 4] = 0x40, 0x31
+    w = F.dequant_nvfp4(F.pack_codes(u), s, np.float32(0.25), 128)[0]
+    want = np.zeros(128)
+    want[20], want[71] = 1.5, -0.5625
+    assert np.array_equal(w, want)
+
+
+def test_nvfp4_quantize_matches_brute_force():
+    """Tensor scale amax / (6 * 448) in fp32; every block's scale the E4M3
+    value nearest to amax(block) / 6 / t; every element the nearest E2M1
+    value at that scale (ties to the even code)."""
+    rng = np.random.default_rng(14)
+    w = (rng.normal(0, 1, (16, 128)) * 2.0 ** rng.integers(-6, 3, (16, 8)).repeat(16, axis=1)).astype(np.float32)
+    codes, sb, t = F.quantize_nvfp4(w)
+    assert t == np.float32(np.abs(w.astype(np.float64)).max() / (6 * 448))
+    e4 = F.e4m3_to_f64(np.arange(0x7F))
+    vals = F.fp4_e2m1_to_f64(np.arange(16))
+    for r in range(16):
+        for g in range(8):
+            blk = w[r, 16 * g:16 * g + 16].astype(np.float64)
+            target = np.abs(blk).max() / 6.0 / np.float64(t)
+            dd = np.abs(e4 - target)
+            best = np.flatnonzero(dd == dd.min())
+            pick = best[best % 2 == 0][0] if np.any(best % 2 == 0) else best[0]
+            assert sb[r, g] == pick, (r, g)
+            scale = e4[pick] * np.float64(t)
+            for i, x in enumerate(blk):
+                d = np.abs(x - vals * scale)
+                d[8] = np.inf
+                b2 = np.flatnonzero(d == d.min())
+                p2 = b2[b2 % 2 == 0][0] if np.any(b2 % 2 == 0) else b2[0]
+                assert F.fp4_e2m1_to_f64(codes[r, 16 * g + i]) == vals[p2], (r, g, i)

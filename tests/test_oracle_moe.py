@@ -354,3 +354,35 @@ def test_fp4_layer_reads_e2m1_values_times_power_of_two_scales():
     L2 = tiny_fp4_layer(3)
     L2.down_s = (L2.down_s.astype(np.int64) + 1).astype(np.uint8)
     assert np.array_equal(M.moe_forward(L2, x, 2)["y"], 2 * y)
+
+
+# ------------------------------------------------------------------ NVFP4 layers
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_nvfp4_sparse_equals_mask_and_dense(seed):
+    """An NVFP4 layer (E4M3 per 16, fp32 per matrix): sparse == all experts
+    then mask (bit for bit) == the independent dense einsum."""
+    L = M.Layer.from_dict(synth.make_layer(synth.TINY_NV, seed))
+    x = tiny_x(L, seed)
+    y = M.moe_forward(L, x, 2)["y"]
+    assert np.array_equal(y, M.moe_forward_masked(L, x, 2))
+    y2 = M.moe_forward_dense_einsum(L, x, 2)
+    np.testing.assert_allclose(y, y2, rtol=0, atol=1e-13 * np.abs(y2).max())
+
+
+def test_nvfp4_tensor_scale_is_linear_and_weights_are_table_values():
+    """Every NVFP4 weight is an E2M1 table value times an E4M3 value times
+    the matrix's fp32 scale, and doubling every down tensor scale doubles y
+    exactly."""
+    lay = synth.make_layer(synth.TINY_NV, 3)
+    L = M.Layer.from_dict(lay)
+    table = {float(r[1]) for r in golden_lines("fp4_e2m1.txt")}
+    Wg, _, _ = L.expert(1)
+    s = F.e4m3_to_f64(lay["gate_s"][1]) * np.float64(lay["gate_ts"][1])
+    v = Wg.reshape(Wg.shape[0], -1, 16) / np.where(s == 0, 1, s)[..., None]
+    assert set(np.unique(v).tolist()) <= table
+    x = tiny_x(L, 3)
+    y = M.moe_forward(L, x, 2)["y"]
+    L2 = M.Layer.from_dict(dict(lay, down_ts=(lay["down_ts"] * 2).astype(np.float32)))
+    assert np.array_equal(M.moe_forward(L2, x, 2)["y"], 2 * y)

@@ -86,3 +86,26 @@ def test_mxfp4_quantizer_agrees_with_oracle():
     Wi = F.dequant(a["gate_q"][0], a["gate_s"][0], 256)
     Wf = F.dequant_mxfp4(b["gate_q"][0], b["gate_s"][0], 256)
     assert np.corrcoef(Wi.ravel(), Wf.ravel())[0, 1] > 0.95
+
+
+def test_nvfp4_quantizer_agrees_with_oracle():
+    """The generator's NVFP4 quantizer (C: direct E4M3 rounding through
+    frexp) and the oracle's (numpy: nearest of all E4M3 values) agree bit for
+    bit, tensor scale included, on N(0, 0.02) draws, on blocks of very
+    different magnitudes and on a zero matrix."""
+    rng = np.random.default_rng(15)
+    mats = [
+        synth.normal_f32(64 * 256, synth.key(8, "nv"), 0.0, 0.02).reshape(64, 256),
+        (rng.normal(0, 1, (32, 256)) * 2.0 ** rng.integers(-12, 4, (32, 16)).repeat(16, axis=1)).astype(np.float32),
+        np.zeros((4, 128), np.float32),
+    ]
+    for w in mats:
+        q, s, t = synth.quantize_nvfp4(w)
+        u, s2, t2 = F.quantize_nvfp4(w)
+        assert t == t2
+        np.testing.assert_array_equal(s, s2)
+        np.testing.assert_array_equal(q, F.pack_codes(u))
+    lay = synth.make_layer(synth.TINY_NV, 3)
+    assert lay["gate_ts"].shape == (synth.TINY.E,) and lay["gate_s"].shape[-1] == synth.TINY.d // 16
+    q, s, t = synth.quantize_nvfp4(np.asarray(synth.normal_f32(128 * 256, synth.key(9, "nv"), 0.0, 0.02)).reshape(128, 256))
+    assert t > 0
