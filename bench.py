@@ -440,65 +440,69 @@ def main():
         del fl
 
     if "fp4" in extras:
-        # MXFP4 experts (E2M1 codes, E8M0 scale per 32): the same draws as the
-        # pool's first 16 layers quantized to FP4 (6.7 GB, beyond the
-        # memory-side cache), 1-token steps graph-timed like the headline
+        # FP4 experts, MXFP4 (E2M1 codes, E8M0 scale per 32) and NVFP4 (E4M3
+        # scale per 16 + fp32 per matrix): the same draws as the pool's first
+        # 16 layers quantized to FP4 (6.7 GB, beyond the memory-side cache);
+        # 1-token steps graph-timed like the headline, then the batched call
+        # at T = 64 with the Zipf bias on the same layers
         PF = min(16, P)
-        f4 = [M.MoELayer.create(M.upload(synth.make_layer(synth.LAYER_FP4, args.seed, l), dev), d, f, E, k, 1, 1)
-              for l in range(PF)]
-        y4 = torch.empty((1, d), dtype=torch.float32, device=dev)
-
-        def fp4_step(i):
-            l = i % PF
-            t = (i // PF) % args.tokens
-            M.moe_decode_forward(f4[l].handle, X[l, t:t + 1], 1, y4, None, None, stream)
-
-        try:
-            f4s, _g = time_graph(fp4_step, 30 * PF, PF, stream)
-            del _g
-        except Exception as e:
-            log(f"fp4 graph failed: {e!r}")
-            f4s = time_eager(fp4_step, 30 * PF, PF, stream)
-        us = f4s / (30 * PF) * 1e6
-        per_expert4 = 3 * f * d // 2 + 3 * f * (d // 32)  # codes + one E8M0 byte per 32
-        b4 = E * d * 4 + d * 2 + k * per_expert4 + d * 4
-        out["mxfp4_layer"] = {"us_per_step": round(us, 3), "tokens_per_s": round(1 / (us * 1e-6), 1),
-                              "bytes_per_step": int(b4), "achieved_gbs": round(b4 / (us * 1e-6) / 1e9, 1),
-                              "frac": round(b4 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "pool_layers": PF}
-        # the batched call at T = 64 with the Zipf bias, on the same MXFP4 layers
         TB = synth.BATCH.T
         bias = torch.from_numpy(synth.zipf_bias(synth.BATCH, args.seed)).to(dev)
-        fb = [M.MoELayer.create(dict(L.tensors, router_b=bias), d, f, E, k, 1, TB) for L in f4]
-        for L in f4:
-            L.close()
-        del f4
         XB4 = torch.from_numpy(np.stack([np.stack([synth.draw_x(synth.BATCH, args.seed, l, t, 0) for t in range(TB)])
                                          for l in range(PF)]).view(np.int16)).to(dev)
-        yb4 = torch.empty((TB, d), dtype=torch.float32, device=dev)
-        ib4 = torch.empty((PF, TB, k), dtype=torch.int32, device=dev)
-        for l in range(PF):
-            M.moe_decode_forward(fb[l].handle, XB4[l], TB, yb4, ib4[l], None, stream)
-        stream.synchronize()
-        d4 = [len(np.unique(a)) for a in ib4.cpu().numpy()]
+        for fname, fcfg, sbytes in (("mxfp4", synth.LAYER_FP4, 3 * f * (d // 32)),
+                                    ("nvfp4", synth.LAYER_NV, 3 * f * (d // 16) + 12)):
+            f4 = [M.MoELayer.create(M.upload(synth.make_layer(fcfg, args.seed, l), dev), d, f, E, k, 1, 1)
+                  for l in range(PF)]
+            y4 = torch.empty((1, d), dtype=torch.float32, device=dev)
 
-        def fp4_batch_step(i):
-            M.moe_decode_forward(fb[i % PF].handle, XB4[i % PF], TB, yb4, None, None, stream)
+            def fp4_step(i, f4=f4, y4=y4):
+                l = i % PF
+                t = (i // PF) % args.tokens
+                M.moe_decode_forward(f4[l].handle, X[l, t:t + 1], 1, y4, None, None, stream)
 
-        try:
-            f4b, _g = time_graph(fp4_batch_step, 4 * PF, PF, stream)
-            del _g
-        except Exception as e:
-            log(f"fp4 batch graph failed: {e!r}")
-            f4b = time_eager(fp4_batch_step, 4 * PF, PF, stream)
-        us = f4b / (4 * PF) * 1e6
-        b4b = E * d * 4 + TB * d * 2 + float(np.mean(d4)) * per_expert4 + TB * d * 4
-        out["mxfp4_batch_t64"] = {"us_per_call": round(us, 3), "tokens_per_s": round(TB / (us * 1e-6), 1),
-                                  "distinct_experts_mean": round(float(np.mean(d4)), 2),
-                                  "bytes_per_call": int(b4b), "achieved_gbs": round(b4b / (us * 1e-6) / 1e9, 1),
-                                  "frac": round(b4b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-        for L in fb:
-            L.close()
-        del fb, XB4
+            try:
+                f4s, _g = time_graph(fp4_step, 30 * PF, PF, stream)
+                del _g
+            except Exception as e:
+                log(f"{fname} graph failed: {e!r}")
+                f4s = time_eager(fp4_step, 30 * PF, PF, stream)
+            us = f4s / (30 * PF) * 1e6
+            per_expert4 = 3 * f * d // 2 + sbytes  # codes + scales
+            b4 = E * d * 4 + d * 2 + k * per_expert4 + d * 4
+            out[f"{fname}_layer"] = {"us_per_step": round(us, 3), "tokens_per_s": round(1 / (us * 1e-6), 1),
+                                     "bytes_per_step": int(b4), "achieved_gbs": round(b4 / (us * 1e-6) / 1e9, 1),
+                                     "frac": round(b4 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "pool_layers": PF}
+            fb = [M.MoELayer.create(dict(L.tensors, router_b=bias), d, f, E, k, 1, TB) for L in f4]
+            for L in f4:
+                L.close()
+            del f4
+            yb4 = torch.empty((TB, d), dtype=torch.float32, device=dev)
+            ib4 = torch.empty((PF, TB, k), dtype=torch.int32, device=dev)
+            for l in range(PF):
+                M.moe_decode_forward(fb[l].handle, XB4[l], TB, yb4, ib4[l], None, stream)
+            stream.synchronize()
+            d4 = [len(np.unique(a)) for a in ib4.cpu().numpy()]
+
+            def fp4_batch_step(i, fb=fb, yb4=yb4):
+                M.moe_decode_forward(fb[i % PF].handle, XB4[i % PF], TB, yb4, None, None, stream)
+
+            try:
+                f4b, _g = time_graph(fp4_batch_step, 4 * PF, PF, stream)
+                del _g
+            except Exception as e:
+                log(f"{fname} batch graph failed: {e!r}")
+                f4b = time_eager(fp4_batch_step, 4 * PF, PF, stream)
+            us = f4b / (4 * PF) * 1e6
+            b4b = E * d * 4 + TB * d * 2 + float(np.mean(d4)) * per_expert4 + TB * d * 4
+            out[f"{fname}_batch_t64"] = {"us_per_call": round(us, 3), "tokens_per_s": round(TB / (us * 1e-6), 1),
+                                         "distinct_experts_mean": round(float(np.mean(d4)), 2),
+                                         "bytes_per_call": int(b4b), "achieved_gbs": round(b4b / (us * 1e-6) / 1e9, 1),
+                                         "frac": round(b4b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            for L in fb:
+                L.close()
+            del fb
+        del XB4
 
     if "lmhead" in extras:
         # LM head: rotate over 4 copies

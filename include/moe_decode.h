@@ -74,16 +74,19 @@ typedef int32_t moe_status;
  *              has six routed experts plus one shared, "Flint 40B: Best Mid
  *              Sized LLM", transcript 02:35); it takes no part in the
  *              softmax or the renormalization
- *   weight_format  MOE_WEIGHTS_INT4 or MOE_WEIGHTS_MXFP4 (the pages name an
- *              FP4 format for the released model, "Recursive Releases
- *              Flint...", section "Quantization"): MXFP4 expert matrices
- *              hold FP4 E2M1 codes at the int4 nibble positions with one
- *              E8M0 scale byte 2^(b-127) per 32 elements (OCP MX v1.0);
- *              scale byte 255 (NaN) is not supported, and the batched
- *              (T > 1) kernels, which round each weight to fp16, are exact
- *              for scale bytes 104..140 */
+ *   weight_format  MOE_WEIGHTS_INT4, MOE_WEIGHTS_MXFP4 or MOE_WEIGHTS_NVFP4
+ *              (the pages name NVFP4 as the released model's format,
+ *              "Recursive Releases Flint...", section "Quantization").  Both
+ *              FP4 formats hold FP4 E2M1 codes at the int4 nibble positions.
+ *              MXFP4: one E8M0 scale byte 2^(b-127) per 32 elements (OCP MX
+ *              v1.0; byte 255, NaN, is not supported; the batched kernels,
+ *              which round each weight to fp16, are exact for bytes
+ *              104..140).  NVFP4: one FP8 E4M3 scale byte per 16 elements
+ *              (OCP E4M3FN) and one fp32 scale per expert matrix
+ *              (moe_layer_weights.*_tscale) */
 #define MOE_WEIGHTS_INT4 0
 #define MOE_WEIGHTS_MXFP4 1
+#define MOE_WEIGHTS_NVFP4 2
 typedef struct {
   int32_t d, f, n_experts, top_k, norm_topk, max_tokens, n_shared;
   int32_t weight_format;
@@ -98,7 +101,11 @@ typedef struct {
  *   down_q    int4 [E][d][f/2],                down_s binary16 [E][d][f/32]
  *   with weight_format MOE_WEIGHTS_MXFP4 each *_q holds E2M1 codes and each
  *             *_s points to E8M0 bytes [...][K/32] (same shapes, one byte
- *             per scale; pass the byte array's address in the field)
+ *             per scale; pass the byte array's address in the field);
+ *             with MOE_WEIGHTS_NVFP4 each *_s points to E4M3 bytes
+ *             [...][K/16] and gate_tscale, up_tscale, down_tscale are fp32
+ *             [E] (shared_*_tscale fp32 [1]), 4-byte aligned; they are
+ *             ignored (may be NULL) for the other formats
  *   shared_*  the shared expert's matrices in the same formats without the
  *             expert dimension ([f][d/2], [f][d/32], [d][f/2], [d][f/32]);
  *             required when n_shared = 1, ignored (may be NULL) otherwise */
@@ -117,6 +124,12 @@ typedef struct {
   const uint16_t* shared_up_s;
   const uint8_t* shared_down_q;
   const uint16_t* shared_down_s;
+  const float* gate_tscale;
+  const float* up_tscale;
+  const float* down_tscale;
+  const float* shared_gate_tscale;
+  const float* shared_up_tscale;
+  const float* shared_down_tscale;
 } moe_layer_weights;
 
 typedef struct moe_layer* moe_handle;

@@ -30,6 +30,7 @@ MOE_MAX_TOKENS = 4096
 MOE_LMHEAD_MAX_B = 16
 WEIGHTS_INT4 = 0    # int4 codes, binary16 scales per 32
 WEIGHTS_MXFP4 = 1   # FP4 E2M1 codes, E8M0 scale bytes per 32
+WEIGHTS_NVFP4 = 2   # FP4 E2M1 codes, E4M3 scale bytes per 16, fp32 scale per matrix
 
 EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
@@ -51,7 +52,9 @@ class LayerDesc(ctypes.Structure):
 
 
 WEIGHT_NAMES = ("router_w", "router_b", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
-                "shared_gate_q", "shared_gate_s", "shared_up_q", "shared_up_s", "shared_down_q", "shared_down_s")
+                "shared_gate_q", "shared_gate_s", "shared_up_q", "shared_up_s", "shared_down_q", "shared_down_s",
+                "gate_tscale", "up_tscale", "down_tscale",
+                "shared_gate_tscale", "shared_up_tscale", "shared_down_tscale")
 
 
 class LayerWeights(ctypes.Structure):
@@ -193,8 +196,15 @@ class MoELayer:
         and shared_gate_q ... shared_down_s when the layer has a shared expert."""
         import torch
         n_shared = 1 if tensors.get("shared_gate_q") is not None else 0
-        # byte scales: MXFP4 (E8M0); 16-bit scales: int4 (binary16)
-        fmt = WEIGHTS_MXFP4 if tensors["gate_s"].dtype == torch.uint8 else WEIGHTS_INT4
+        # matrix scales: NVFP4; byte scales: MXFP4 (E8M0); 16-bit scales: int4 (binary16)
+        if tensors.get("gate_ts") is not None:
+            fmt = WEIGHTS_NVFP4
+            tensors = dict(tensors, gate_tscale=tensors["gate_ts"], up_tscale=tensors["up_ts"],
+                           down_tscale=tensors["down_ts"], shared_gate_tscale=tensors.get("shared_gate_ts"),
+                           shared_up_tscale=tensors.get("shared_up_ts"),
+                           shared_down_tscale=tensors.get("shared_down_ts"))
+        else:
+            fmt = WEIGHTS_MXFP4 if tensors["gate_s"].dtype == torch.uint8 else WEIGHTS_INT4
         desc = LayerDesc(d, f, E, k, norm_topk, max_tokens, n_shared, fmt)
         nbytes = moe_decode_workspace_bytes(desc)
         if nbytes == 0:

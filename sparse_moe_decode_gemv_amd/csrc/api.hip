@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
@@ -34,7 +34,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->max_tokens > MOE_MAX_TOKENS || d->n_experts > 1024) return MOE_ERR_SHAPE;
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_ERR_SHAPE;
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_ERR_SHAPE;
-  if (d->weight_format != MOE_WEIGHTS_INT4 && d->weight_format != MOE_WEIGHTS_MXFP4) return MOE_ERR_SHAPE;
+  if (d->weight_format != MOE_WEIGHTS_INT4 && d->weight_format != MOE_WEIGHTS_MXFP4 &&
+      d->weight_format != MOE_WEIGHTS_NVFP4)
+    return MOE_ERR_SHAPE;
   if (d->d % 32 || d->f % 32) return MOE_ERR_SHAPE;
   if (!is_pow2(d->d) || d->d < 256 || d->d > 8192) return MOE_ERR_UNSUPPORTED;
   if (!is_pow2(d->f) || d->f < 128 || d->f > 4096) return MOE_ERR_UNSUPPORTED;
@@ -113,7 +115,9 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.sh_gate_q = a.sh_gate_q, f.sh_gate_s = a.sh_gate_s, f.sh_up_q = a.sh_up_q, f.sh_up_s = a.sh_up_s;
   f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
   f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
-  f.fp4 = a.fp4;
+  f.fmt = a.fmt;
+  f.gate_tscale = a.gate_tscale, f.up_tscale = a.up_tscale, f.down_tscale = a.down_tscale;
+  f.sh_gate_tscale = a.sh_gate_tscale, f.sh_up_tscale = a.sh_up_tscale, f.sh_down_tscale = a.sh_down_tscale;
   return f;
 }
 
@@ -162,6 +166,15 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
     for (const void* p : sp)
       if (!aligned16(p)) return MOE_ERR_ALIGN;
   }
+  if (desc->weight_format == MOE_WEIGHTS_NVFP4) {  // the matrices' fp32 scales
+    if (!w->gate_tscale || !w->up_tscale || !w->down_tscale) return MOE_ERR_NULL;
+    if (desc->n_shared && (!w->shared_gate_tscale || !w->shared_up_tscale || !w->shared_down_tscale))
+      return MOE_ERR_NULL;
+    const void* tp[] = {w->gate_tscale, w->up_tscale, w->down_tscale, w->shared_gate_tscale, w->shared_up_tscale,
+                        w->shared_down_tscale};
+    for (const void* p : tp)
+      if (p && !aligned4(p)) return MOE_ERR_ALIGN;
+  }
   const Layout L = layout_of(desc);
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
@@ -173,7 +186,10 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   moe::LayerArgs& a = h->args;
   a.d = desc->d, a.f = desc->f, a.E = desc->n_experts, a.k = desc->top_k, a.norm_topk = desc->norm_topk;
   a.ns = desc->n_shared;
-  a.fp4 = desc->weight_format == MOE_WEIGHTS_MXFP4;
+  a.fmt = desc->weight_format;
+  a.gate_tscale = w->gate_tscale, a.up_tscale = w->up_tscale, a.down_tscale = w->down_tscale;
+  a.sh_gate_tscale = w->shared_gate_tscale, a.sh_up_tscale = w->shared_up_tscale;
+  a.sh_down_tscale = w->shared_down_tscale;
   a.router_w = w->router_w, a.router_b = w->router_b;
   a.gate_q = w->gate_q, a.gate_s = w->gate_s, a.up_q = w->up_q, a.up_s = w->up_s;
   a.down_q = w->down_q, a.down_s = w->down_s;

@@ -93,10 +93,12 @@ __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
 
 // D hidden, F expert width, KP expert slots (top_k, plus one with a shared
 // expert, SH) rounded up to a power of two, EPL
-// experts per lane in the top-k wave; FP4: MXFP4 expert weights (E2M1 codes,
-// one E8M0 scale byte per 32) instead of int4 with binary16 scales.
-template <int D, int F, int KP, int EPL, bool NORM, bool SH, bool FP4>
+// experts per lane in the top-k wave; FMT: expert weights int4 with binary16
+// scales (0), MXFP4 (1: E2M1 codes, an E8M0 scale byte per 32) or NVFP4 (2:
+// E2M1 codes, an E4M3 scale byte per 16, an fp32 scale per matrix).
+template <int D, int F, int KP, int EPL, bool NORM, bool SH, int FMT>
 __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
+  constexpr bool FP4 = FMT != 0, NV = FMT == 2;
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
   constexpr int NL = 4;              // gate (and up) loads per lane
@@ -152,16 +154,30 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   const int c0 = has_gate ? (wg - gslot * wpe) * 64 * NL : 0;
   uint4 qg[NL], qu[NL];
   uint2 sg[NL], su[NL];
-  // the 4 scales of a piece: 4 binary16 (int4) or 4 E8M0 bytes (FP4, in .x)
-  auto load_scales = [&](const uint16_t* base, size_t i) -> uint2 {
-    if constexpr (FP4) return make_uint2(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + i), 0u);
-    else return *reinterpret_cast<const uint2*>(base + i);
+  // The 4 scales of piece c of row `row` (CP pieces per row): 4 binary16
+  // (int4), 4 E8M0 bytes (MXFP4, in .x), or the piece's NVFP4 E4M3 bytes
+  // at bytes 0, 2, 4, 6 (its 8-byte group shifted by the piece's half).
+  auto load_scales = [&](const uint16_t* base, size_t row, int CP, int c) -> uint2 {
+    if constexpr (NV) {
+      const uint64_t v = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(base) + row * 2 * CP +
+                                                            8 * (c >> 2));
+      const uint64_t s = v >> (8 * ((c & 3) >> 1));
+      return make_uint2((uint32_t)s, (uint32_t)(s >> 32));
+    } else if constexpr (FP4) {
+      return make_uint2(
+          *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + row * CP + (c & ~3)), 0u);
+    } else {
+      return *reinterpret_cast<const uint2*>(base + row * CP + (c & ~3));
+    }
   };
-  // scale array of expert e (scales counted in elements of either size)
+  // scale array of expert e: e_off scales of 2 bytes (int4), 1 (MXFP4) or 2
+  // per 32 elements (NVFP4)
   auto scales_of = [&](const uint16_t* base, size_t e_off) -> const uint16_t* {
-    if constexpr (FP4) return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + e_off);
+    if constexpr (NV) return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + 2 * e_off);
+    else if constexpr (FP4) return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + e_off);
     else return base + e_off;
   };
+  float tg = 1.f, tu = 1.f;  // NVFP4 matrix scales of this wave's slot
   auto load_mats = [&](const uint8_t* gq8, const uint16_t* gsb, const uint8_t* uq8, const uint16_t* usb) {
     const uint4* gp = reinterpret_cast<const uint4*>(gq8);
     const uint4* up = reinterpret_cast<const uint4*>(uq8);
@@ -170,9 +186,8 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       const int c = c0 + 64 * n + lane;
       qg[n] = gp[c];
       qu[n] = up[c];
-      const size_t so = (size_t)(c / CPR) * CPR + ((c % CPR) & ~3);
-      sg[n] = load_scales(gsb, so);
-      su[n] = load_scales(usb, so);
+      sg[n] = load_scales(gsb, (size_t)(c / CPR), CPR, c % CPR);
+      su[n] = load_scales(usb, (size_t)(c / CPR), CPR, c % CPR);
     }
   };
   auto load_gate = [&](int e_raw) {
@@ -180,11 +195,21 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     const size_t mat = (size_t)F * CPR;
     load_mats(a.gate_q + (size_t)e * mat * 16, scales_of(a.gate_s, (size_t)e * mat), a.up_q + (size_t)e * mat * 16,
               scales_of(a.up_s, (size_t)e * mat));
+    if constexpr (NV) {
+      tg = a.gate_tscale[e];
+      tu = a.up_tscale[e];
+    }
   };
   // the shared expert needs no routing: its slot's loads go out now, behind
   // the router rows, and land while the logits are exchanged
   if constexpr (SH)
-    if (shared_slot) load_mats(a.sh_gate_q, a.sh_gate_s, a.sh_up_q, a.sh_up_s);
+    if (shared_slot) {
+      load_mats(a.sh_gate_q, a.sh_gate_s, a.sh_up_q, a.sh_up_s);
+      if constexpr (NV) {
+        tg = a.sh_gate_tscale[0];
+        tu = a.sh_up_tscale[0];
+      }
+    }
   if constexpr (!NORM) {
 #pragma unroll
     for (int c = threadIdx.x; c < D / 8; c += 256) reinterpret_cast<uint4*>(s_x)[c] = reinterpret_cast<const uint4*>(a.x)[c];
@@ -304,7 +329,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
       const int s = CPR > 64 ? n % XS : 0;
-      if constexpr (FP4) {
+      if constexpr (NV) {
+        ag += dot_piece_nv(qg[n], xs[s], sg[n]);
+        au += dot_piece_nv(qu[n], xs[s], su[n]);
+      } else if constexpr (FP4) {
         ag += dot_piece_fp4(qg[n], xs[s], sg[n].x);
         au += dot_piece_fp4(qu[n], xs[s], su[n].x);
       } else {
@@ -314,10 +342,10 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       if (n % LPRG == LPRG - 1) {
         // row within this workgroup's ROWS_G consecutive rows of slot gslot
         if constexpr (CPR >= 64) {
-          const float g = wave_sum(ag), u = wave_sum(au);
+          const float g = wave_sum(ag) * tg, u = wave_sum(au) * tu;
           if (lane == 0) s_hv[(wid * 64 * NL + 64 * n) / CPR] = wj * silu(g) * u;
         } else {
-          const float g = seg_sum<(CPR < 64 ? CPR : 64)>(ag), u = seg_sum<(CPR < 64 ? CPR : 64)>(au);
+          const float g = seg_sum<(CPR < 64 ? CPR : 64)>(ag) * tg, u = seg_sum<(CPR < 64 ? CPR : 64)>(au) * tu;
           if (lane % CPR == 0) s_hv[(wid * 64 * NL + 64 * n + lane) / CPR] = wj * silu(g) * u;
         }
         ag = au = 0.f;
@@ -364,6 +392,14 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     cc[m] = flat % CPRF;
     act[m] = has_down && dslot[m] < nslots;
   }
+  float td[LPRD];  // NVFP4: the matrix scale of each piece's expert (1 otherwise)
+#pragma unroll
+  for (int m = 0; m < LPRD; ++m) {
+    td[m] = 1.f;
+    if constexpr (NV) {
+      if (act[m]) td[m] = (SH && dslot[m] >= k) ? a.sh_down_tscale[0] : a.down_tscale[min(max(s_idx[dslot[m]], 0), E - 1)];
+    }
+  }
   float radd[NLD];  // residual rows this lane will update (stack)
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
@@ -381,7 +417,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       const bool shd = SH && dslot[m] >= k;  // the shared expert's slot
       const size_t eb = shd ? (size_t)row : (size_t)min(max(s_idx[dslot[m]], 0), E - 1) * D + row;
       qd[n] = *reinterpret_cast<const uint4*>((shd ? a.sh_down_q : a.down_q) + piece_offset(eb, CPRF, cc[m]));
-      sd[n] = load_scales(shd ? a.sh_down_s : a.down_s, eb * CPRF + (cc[m] & ~3));
+      sd[n] = load_scales(shd ? a.sh_down_s : a.down_s, eb, CPRF, cc[m]);
     } else {
       qd[n] = make_uint4(0, 0, 0, 0);
       sd[n] = make_uint2(0, 0);
@@ -443,7 +479,8 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int m = n % LPRD;
-      if constexpr (FP4) acc += dot_piece_fp4_f16(qd[n], hs8[m], sd[n].x);
+      if constexpr (NV) acc = fmaf(dot_piece_nv_f16(qd[n], hs8[m], sd[n]), td[m], acc);
+      else if constexpr (FP4) acc += dot_piece_fp4_f16(qd[n], hs8[m], sd[n].x);
       else acc += dot_piece_f16(qd[n], hs8[m], sd[n]);
       if (n % LPRD == LPRD - 1) {
         if constexpr (P >= 64) {
@@ -462,26 +499,28 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
 // ---------------------------------------------------------------- host side
 
-template <int D, int F, int KP, int EPL, bool FP4>
+template <int D, int F, int KP, int EPL, int FMT>
 static hipError_t layer_launch_fmt(const FusedArgs& a, int G, hipStream_t s) {
   const size_t lds = (size_t)(a.k + a.ns) * (F / 8) * 5 * sizeof(unsigned);
   if (a.ns) {
     if (a.resid_in)
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true, FP4>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true, FMT>), dim3(G), dim3(256), lds, s, a);
     else
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, true, FP4>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, true, FMT>), dim3(G), dim3(256), lds, s, a);
   } else {
     if (a.resid_in)
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, false, FP4>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, false, FMT>), dim3(G), dim3(256), lds, s, a);
     else
-      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, false, FP4>), dim3(G), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((k_layer<D, F, KP, EPL, false, false, FMT>), dim3(G), dim3(256), lds, s, a);
   }
   return hipGetLastError();
 }
 
 template <int D, int F, int KP, int EPL>
 static hipError_t layer_launch(const FusedArgs& a, int G, hipStream_t s) {
-  return a.fp4 ? layer_launch_fmt<D, F, KP, EPL, true>(a, G, s) : layer_launch_fmt<D, F, KP, EPL, false>(a, G, s);
+  if (a.fmt == 2) return layer_launch_fmt<D, F, KP, EPL, 2>(a, G, s);
+  if (a.fmt == 1) return layer_launch_fmt<D, F, KP, EPL, 1>(a, G, s);
+  return layer_launch_fmt<D, F, KP, EPL, 0>(a, G, s);
 }
 
 template <int D, int F, int KP>

@@ -597,33 +597,36 @@ struct WBlk {
   uint4 q;
   uint2 s;
 };
-template <bool FP4>
+// FMT: 0 int4 (4 binary16 scales per row and block: 8 bytes), 1 MXFP4 (4
+// E8M0 bytes), 2 NVFP4 (8 E4M3 bytes, one per 16 elements)
+template <int FMT>
 __device__ __forceinline__ WBlk wload(const uint4* tq, const uint2* ts, int blk, int lane) {
   WBlk w;
   w.q = tq[blk * 64 + lane];
-  if constexpr (FP4) w.s = make_uint2(reinterpret_cast<const uint32_t*>(ts)[blk * 16 + (lane & 15)], 0u);
+  if constexpr (FMT == 1) w.s = make_uint2(reinterpret_cast<const uint32_t*>(ts)[blk * 16 + (lane & 15)], 0u);
   else w.s = ts[blk * 16 + (lane & 15)];
   return w;
 }
 
-// Scales of tile unit `off` (units of one row's 4 block scales) of a
+// Scales of tile unit `off` (units of one row's block scales) of a
 // tile-major scale copy.
-template <bool FP4>
+template <int FMT>
 __device__ __forceinline__ const uint2* tile_scales(const uint16_t* base, size_t off) {
-  if constexpr (FP4) return reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(base) + off);
+  if constexpr (FMT == 1) return reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(base) + off);
   else return reinterpret_cast<const uint2*>(base) + off;
 }
 
-// MXFP4 B operand of one MFMA: the 8 E2M1 codes of one dword times the
-// block scale 2^(b-127), as fp16 (one v_cvt_scalef32_pk_f16_fp4 per code
-// pair; exact for scale bytes 104..140), reordered into the int4 operand
-// order (e0,e4), (e1,e5), (e2,e6), (e3,e7) that the activation rows use.
+// FP4 B operand of one MFMA: the 8 E2M1 codes of one dword times `scale`,
+// a power of two (the conversion's scale operand is an MX block scale: only
+// its exponent counts; exact for E8M0 bytes 104..140), as fp16 (one
+// v_cvt_scalef32_pk_f16_fp4 per code pair), reordered into the int4
+// operand order (e0,e4), (e1,e5), (e2,e6), (e3,e7) that the activation rows
+// use.
 template <int B>
 __device__ __forceinline__ uint32_t fp4_pair_f16s(uint32_t w, float scale) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, B));
 }
-__device__ __forceinline__ f16x8_t dequant_fp4_f16(uint32_t w, uint32_t sc, int j) {
-  const float scale = ldexpf(1.0f, (int)((sc >> (8 * j)) & 0xFFu) - 127);
+__device__ __forceinline__ f16x8_t dequant_fp4_f16(uint32_t w, float scale) {
   const uint32_t p01 = fp4_pair_f16s<0>(w, scale), p23 = fp4_pair_f16s<1>(w, scale);
   const uint32_t p45 = fp4_pair_f16s<2>(w, scale), p67 = fp4_pair_f16s<3>(w, scale);
   const uint4 v = make_uint4(__builtin_amdgcn_perm(p45, p01, 0x05040100u), __builtin_amdgcn_perm(p45, p01, 0x07060302u),
@@ -633,17 +636,35 @@ __device__ __forceinline__ f16x8_t dequant_fp4_f16(uint32_t w, uint32_t sc, int 
 
 // One block of K for two weight tiles against the NTT staged token tiles:
 // each weight dword is dequantized once and used by NTT MFMAs.
-template <int NTT, bool FP4>
+// NVFP4 B operand: the codes converted exactly (scale 1), then one fp16
+// multiply by the block's E4M3 value times the matrix scale (that product
+// rounded to fp16 first): two roundings of 2^-11, like int4's q * s.
+__device__ __forceinline__ f16x8_t dequant_nv_f16(uint32_t w, float scale) {
+  const _Float16 h = (_Float16)scale;
+  const f16x8_t s8 = {h, h, h, h, h, h, h, h};
+  return dequant_fp4_f16(w, 1.0f) * s8;
+}
+
+// tsc: NVFP4 matrix scale of each weight tile
+template <int NTT, int FMT>
 __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<NTT>& t, const WBlk (&w)[2],
-                                           int lane, uint32_t magic) {
+                                           int lane, uint32_t magic, const float (&tsc)[2]) {
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     f16x8_t wb[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if constexpr (FP4) wb[i] = dequant_fp4_f16(dword_of(w[i].q, j), w[i].s.x, j);
-      else wb[i] = dequant_f16(dword_of(w[i].q, j), scale2(w[i].s, j), magic);
+      if constexpr (FMT == 2) {
+        // dword j of piece q spans elements 32j + 8q .. +7: 16-block 2j + q/2
+        const int b = 2 * j + (q >> 1);
+        const uint32_t sb = ((b < 4 ? w[i].s.x : w[i].s.y) >> (8 * (b & 3))) & 0xFFu;
+        wb[i] = dequant_nv_f16(dword_of(w[i].q, j), e4m3_f32(sb) * tsc[i]);
+      } else if constexpr (FMT == 1) {
+        wb[i] = dequant_fp4_f16(dword_of(w[i].q, j), ldexpf(1.0f, (int)((w[i].s.x >> (8 * j)) & 0xFFu) - 127));
+      } else {
+        wb[i] = dequant_f16(dword_of(w[i].q, j), scale2(w[i].s, j), magic);
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
@@ -663,10 +684,11 @@ __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<
 // T = 2048.)  Every global load is unconditional (rows past the chunk
 // are clamped to a real one and their outputs dropped), so the compiler's
 // wait counts stay exact.
-template <int K, int NTT, bool FP4>
+template <int K, int NTT, int FMT>
 __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tiles,
                                        const uint16_t* const (&op_rows)[NTT / 2], const uint4* const (&wtq)[2],
-                                       const uint2* const (&wts)[2], int tid, int lane, uint32_t magic) {
+                                       const uint2* const (&wts)[2], int tid, int lane, uint32_t magic,
+                                       const float (&tsc)[2]) {
   constexpr int NBLK = K / 128;
   constexpr int G = NBLK < 2 ? NBLK : 2;    // weight blocks per burst
   constexpr int SX = NBLK < 4 ? NBLK : 4;   // operand blocks in flight
@@ -677,7 +699,7 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tile
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) w[0][i][m] = wload<FP4>(wtq[m], wts[m], i, lane);
+    for (int m = 0; m < 2; ++m) w[0][i][m] = wload<FMT>(wtq[m], wts[m], i, lane);
   stage_store(tiles[0], sx[0], tid);
   sx[0] = stage_load(min(SX, NBLK - 1), op_rows, tid);
   __syncthreads();
@@ -691,13 +713,13 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tile
 #pragma unroll
         for (int i = 0; i < G; ++i)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) w[h ^ 1][i][m] = wload<FP4>(wtq[m], wts[m], n0 + i, lane);
+          for (int m = 0; m < 2; ++m) w[h ^ 1][i][m] = wload<FMT>(wtq[m], wts[m], n0 + i, lane);
       }
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         const int b = g0 + i;
         if (b < NBLK) {
-          block_mfma<NTT, FP4>(acc, tiles[b & 1], w[h][i], lane, magic);
+          block_mfma<NTT, FMT>(acc, tiles[b & 1], w[h][i], lane, magic, tsc);
           // slot (b+1) % SX holds block b+1: into the other LDS buffer, then refill
           stage_store(tiles[(b + 1) & 1], sx[(b + 1) % SX], tid);
           sx[(b + 1) % SX] = stage_load(min(b + 1 + SX, NBLK - 1), op_rows, tid);
@@ -714,7 +736,7 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tile
 // gate and up rows 16w .. 16w+15 of the group; K = d.  Epilogue in
 // registers: h = w_j * silu(g) * u, written as fp16 in operand order
 // (0,4,1,5,2,6,3,7 within each 8 rows) for the down step.
-template <int D, int NTT, bool FP4>
+template <int D, int NTT, int FMT>
 __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
   __shared__ OpTile<NTT> s_tile[2];
   const int f = a.f, k = a.k, ngroups = f / 64;
@@ -726,8 +748,13 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
     const size_t tile = (size_t)it.e * (f / 16) + it.rg * 4 + wave;  // 16-row tile of gate and of up
     const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.gate_t) + tile * (D / 128) * 64,
                            reinterpret_cast<const uint4*>(a.up_t) + tile * (D / 128) * 64};
-    const uint2* wts[2] = {tile_scales<FP4>(a.gate_ts, tile * (D / 128) * 16),
-                           tile_scales<FP4>(a.up_ts, tile * (D / 128) * 16)};
+    const uint2* wts[2] = {tile_scales<FMT>(a.gate_ts, tile * (D / 128) * 16),
+                           tile_scales<FMT>(a.up_ts, tile * (D / 128) * 16)};
+    float tsc[2] = {1.f, 1.f};
+    if constexpr (FMT == 2) {  // the matrix scales of this item's expert (index E: the shared one)
+      tsc[0] = it.e < a.E ? a.gate_tscale[it.e] : a.sh_gate_tscale[0];
+      tsc[1] = it.e < a.E ? a.up_tscale[it.e] : a.sh_up_tscale[0];
+    }
     // the operand rows this thread stages: tokens of chunk rows tid/8 + 32m
     const int Tk = a.meta[2];
     const uint16_t* rows[NTT / 2];
@@ -742,7 +769,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // all token tiles always (rows past the chunk repeat a real row and
     // their outputs are dropped): one code path
-    k_loop<D, NTT, FP4>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
+    k_loop<D, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic, tsc);
     // lane: weight row r16, tokens 4q+v of each tile
     const int e8 = r16 & 7;
     const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);  // h in operand order
@@ -768,7 +795,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
 // Item: (chosen expert, 128 rows of d, up to 16*NTT tokens).  Wave w takes
 // rows 32w .. 32w+31 of the group as two tiles; K = f, against the fp16 h
 // operands.  o_{t,j} goes to obuf[t*k + j][row].
-template <int F, int NTT, bool FP4>
+template <int F, int NTT, int FMT>
 __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
   __shared__ OpTile<NTT> s_tile[2];
   const int d = a.d, ngroups = d / 128;
@@ -781,8 +808,10 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
     const size_t tile = (size_t)it.e * (d / 16) + it.rg * 8 + wave * 2;  // two 16-row tiles of W_d
     const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.down_t) + tile * (F / 128) * 64,
                            reinterpret_cast<const uint4*>(a.down_t) + (tile + 1) * (F / 128) * 64};
-    const uint2* wts[2] = {tile_scales<FP4>(a.down_ts, tile * (F / 128) * 16),
-                           tile_scales<FP4>(a.down_ts, (tile + 1) * (F / 128) * 16)};
+    const uint2* wts[2] = {tile_scales<FMT>(a.down_ts, tile * (F / 128) * 16),
+                           tile_scales<FMT>(a.down_ts, (tile + 1) * (F / 128) * 16)};
+    float tsc[2] = {1.f, 1.f};
+    if constexpr (FMT == 2) tsc[0] = tsc[1] = it.e < a.E ? a.down_tscale[it.e] : a.sh_down_tscale[0];
     const uint16_t* rows[NTT / 2];
 #pragma unroll
     for (int m = 0; m < NTT / 2; ++m) rows[m] = a.h16 + (size_t)(it.p0 + min((tid >> 3) + 32 * m, it.n - 1)) * F;
@@ -795,7 +824,7 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
     f32x4_t acc[2][NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    k_loop<F, NTT, FP4>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
+    k_loop<F, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic, tsc);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       if (16 * tt >= it.n) break;
@@ -921,16 +950,16 @@ static int grid_for(const LayerArgs& a, int T, int groups) {
   return items < kMaxGroupedGrid ? items : kMaxGroupedGrid;
 }
 
-template <int NTT, bool FP4>
+template <int NTT, int FMT>
 static hipError_t gateup_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
   const dim3 b(256);
   switch (a.d) {
-    case 256: hipLaunchKernelGGL((k_gateup<256, NTT, FP4>), g, b, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((k_gateup<512, NTT, FP4>), g, b, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((k_gateup<1024, NTT, FP4>), g, b, 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((k_gateup<2048, NTT, FP4>), g, b, 0, s, a); break;
-    case 4096: hipLaunchKernelGGL((k_gateup<4096, NTT, FP4>), g, b, 0, s, a); break;
-    case 8192: hipLaunchKernelGGL((k_gateup<8192, NTT, FP4>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((k_gateup<256, NTT, FMT>), g, b, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((k_gateup<512, NTT, FMT>), g, b, 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((k_gateup<1024, NTT, FMT>), g, b, 0, s, a); break;
+    case 2048: hipLaunchKernelGGL((k_gateup<2048, NTT, FMT>), g, b, 0, s, a); break;
+    case 4096: hipLaunchKernelGGL((k_gateup<4096, NTT, FMT>), g, b, 0, s, a); break;
+    case 8192: hipLaunchKernelGGL((k_gateup<8192, NTT, FMT>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -939,20 +968,21 @@ static hipError_t gateup_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
 hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s) {
   const dim3 g(grid_for(a, T, a.f / 64));
   const bool c64 = chunk_rows(a, T) == 64;
-  if (a.fp4) return c64 ? gateup_inst<4, true>(a, g, s) : gateup_inst<2, true>(a, g, s);
-  return c64 ? gateup_inst<4, false>(a, g, s) : gateup_inst<2, false>(a, g, s);
+  if (a.fmt == 2) return c64 ? gateup_inst<4, 2>(a, g, s) : gateup_inst<2, 2>(a, g, s);
+  if (a.fmt == 1) return c64 ? gateup_inst<4, 1>(a, g, s) : gateup_inst<2, 1>(a, g, s);
+  return c64 ? gateup_inst<4, 0>(a, g, s) : gateup_inst<2, 0>(a, g, s);
 }
 
-template <int NTT, bool FP4>
+template <int NTT, int FMT>
 static hipError_t down_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
   const dim3 b(256);
   switch (a.f) {
-    case 128: hipLaunchKernelGGL((k_down<128, NTT, FP4>), g, b, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((k_down<256, NTT, FP4>), g, b, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((k_down<512, NTT, FP4>), g, b, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((k_down<1024, NTT, FP4>), g, b, 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((k_down<2048, NTT, FP4>), g, b, 0, s, a); break;
-    case 4096: hipLaunchKernelGGL((k_down<4096, NTT, FP4>), g, b, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_down<128, NTT, FMT>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((k_down<256, NTT, FMT>), g, b, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((k_down<512, NTT, FMT>), g, b, 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((k_down<1024, NTT, FMT>), g, b, 0, s, a); break;
+    case 2048: hipLaunchKernelGGL((k_down<2048, NTT, FMT>), g, b, 0, s, a); break;
+    case 4096: hipLaunchKernelGGL((k_down<4096, NTT, FMT>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -961,8 +991,9 @@ static hipError_t down_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
 hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
   const dim3 g(grid_for(a, T, a.d / 128));
   const bool c64 = chunk_rows(a, T) == 64;
-  if (a.fp4) return c64 ? down_inst<4, true>(a, g, s) : down_inst<2, true>(a, g, s);
-  return c64 ? down_inst<4, false>(a, g, s) : down_inst<2, false>(a, g, s);
+  if (a.fmt == 2) return c64 ? down_inst<4, 2>(a, g, s) : down_inst<2, 2>(a, g, s);
+  if (a.fmt == 1) return c64 ? down_inst<4, 1>(a, g, s) : down_inst<2, 1>(a, g, s);
+  return c64 ? down_inst<4, 0>(a, g, s) : down_inst<2, 0>(a, g, s);
 }
 
 static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq, uint16_t* ts, long long rows, int K,
@@ -979,7 +1010,8 @@ static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq,
   return hipGetLastError();
 }
 
-// n scales into a scale array of either element size
+// n scales (of 32 elements) into a scale array: 1 byte each for MXFP4, 2
+// for int4 (binary16) and NVFP4 (two E4M3)
 static uint16_t* scales_at(const uint16_t* base, size_t n, bool fp4) {
   return const_cast<uint16_t*>(fp4 ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + n)
                                    : base + n);
@@ -992,7 +1024,7 @@ hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_router_terms, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a.router_w, a.E, a.d,
                      reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.router_t)));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const bool fp4 = a.fp4 != 0;
+  const bool fp4 = a.fmt == 1;  // 4-byte scale units (MXFP4); int4 and NVFP4 have 8-byte units
   if ((e = tile_matrix(a.gate_q, a.gate_s, const_cast<uint8_t*>(a.gate_t), const_cast<uint16_t*>(a.gate_ts),
                        E * a.f, a.d, fp4, s)) != hipSuccess)
     return e;

@@ -13,7 +13,13 @@ namespace moe {
 struct LayerArgs {
   int d, f, E, k, norm_topk;
   int ns;  // shared experts, 0 or 1: expert index E of the tile-major copies, assignments T*k + t
-  int fp4;  // 1: MXFP4 experts (codes E2M1, the *_s pointers and the tile scale copies hold E8M0 bytes)
+  int fmt;  // 0 int4; 1 MXFP4 (the *_s pointers and scale copies hold E8M0 bytes); 2 NVFP4 (E4M3 bytes per 16)
+  const float* gate_tscale;  // NVFP4: fp32 scale of each expert matrix [E] (shared: [1])
+  const float* up_tscale;
+  const float* down_tscale;
+  const float* sh_gate_tscale;
+  const float* sh_up_tscale;
+  const float* sh_down_tscale;
   const float* router_w;
   const float* router_b;
   const uint8_t* gate_q;
@@ -94,8 +100,14 @@ struct FusedArgs {
   const uint16_t* sh_up_s;
   const uint8_t* sh_down_q;
   const uint16_t* sh_down_s;
+  const float* gate_tscale;  // NVFP4: fp32 scale of each expert matrix [E] (shared: [1])
+  const float* up_tscale;
+  const float* down_tscale;
+  const float* sh_gate_tscale;
+  const float* sh_up_tscale;
+  const float* sh_down_tscale;
   int E, k, norm, ns;
-  int fp4;  // 1: MXFP4 expert weights (the *_s pointers hold E8M0 bytes)
+  int fmt;  // expert weights: 0 int4, 1 MXFP4 (E8M0 bytes per 32), 2 NVFP4 (E4M3 bytes per 16 + gate_ts ...)
 };
 
 // The whole 1-token step in one launch, for the shapes it is built for

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert L.moe_decode_abi_version() == 3
+    assert L.moe_decode_abi_version() == 4
 
 
 def test_status_strings():
@@ -61,7 +61,7 @@ def test_workspace_bytes_layout():
 @pytest.mark.parametrize("kw", [dict(top_k=0), dict(top_k=17), dict(top_k=300, n_experts=256), dict(max_tokens=0),
                                 dict(max_tokens=4097), dict(d=2040), dict(f=500), dict(norm_topk=2),
                                 dict(n_experts=2000), dict(d=0), dict(n_shared=2), dict(n_shared=-1),
-                                dict(weight_format=2), dict(weight_format=-1)])
+                                dict(weight_format=3), dict(weight_format=-1)])
 def test_bad_shapes_have_no_workspace(kw):
     assert M.moe_decode_workspace_bytes(desc(**kw)) == 0
 
@@ -157,3 +157,12 @@ def test_mxfp4_layer_workspace():
     fp4 = dict(weight_format=M.WEIGHTS_MXFP4)
     assert M.moe_decode_workspace_bytes(desc(**fp4)) == M.moe_decode_workspace_bytes(desc())
     assert M.moe_decode_workspace_bytes(desc(max_tokens=64, **fp4)) == M.moe_decode_workspace_bytes(desc(max_tokens=64))
+
+
+def test_nvfp4_needs_matrix_scales():
+    """NVFP4 layers need the fp32 matrix scales (NULL -> MOE_ERR_NULL,
+    misaligned -> MOE_ERR_ALIGN, checked before any device work)."""
+    nv = desc(weight_format=M.WEIGHTS_NVFP4)
+    assert init_status(nv, weights())[0] == M.MOE_ERR_NULL
+    ts = dict(gate_tscale=FAKE, up_tscale=FAKE, down_tscale=FAKE)
+    assert init_status(nv, weights(**dict(ts, up_tscale=FAKE + 2)))[0] == M.MOE_ERR_ALIGN
