@@ -155,14 +155,13 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   uint4 qg[NL], qu[NL];
   uint2 sg[NL], su[NL];
   // The 4 scales of piece c of row `row` (CP pieces per row): 4 binary16
-  // (int4), 4 E8M0 bytes (MXFP4, in .x), or the piece's NVFP4 E4M3 bytes
-  // at bytes 0, 2, 4, 6 (its 8-byte group shifted by the piece's half).
+  // (int4), 4 E8M0 bytes (MXFP4, in .x), or the 8 NVFP4 E4M3 bytes of the
+  // piece's group (nv_scales picks the piece's 4 where they are used: no
+  // arithmetic on a loaded value before the dot, which would make the wave
+  // wait for it -- and for every load issued before it -- right away).
   auto load_scales = [&](const uint16_t* base, size_t row, int CP, int c) -> uint2 {
     if constexpr (NV) {
-      const uint64_t v = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(base) + row * 2 * CP +
-                                                            8 * (c >> 2));
-      const uint64_t s = v >> (8 * ((c & 3) >> 1));
-      return make_uint2((uint32_t)s, (uint32_t)(s >> 32));
+      return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + row * 2 * CP + 8 * (c >> 2));
     } else if constexpr (FP4) {
       return make_uint2(
           *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + row * CP + (c & ~3)), 0u);
@@ -178,6 +177,11 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     else return base + e_off;
   };
   float tg = 1.f, tu = 1.f;  // NVFP4 matrix scales of this wave's slot
+  // NVFP4: piece c's E4M3 bytes of its group's 8 at bytes 0, 2, 4, 6
+  auto nv_scales = [](uint2 v, int c) -> uint2 {
+    const uint64_t s = (((uint64_t)v.y << 32) | v.x) >> (8 * ((c & 3) >> 1));
+    return make_uint2((uint32_t)s, (uint32_t)(s >> 32));
+  };
   auto load_mats = [&](const uint8_t* gq8, const uint16_t* gsb, const uint8_t* uq8, const uint16_t* usb) {
     const uint4* gp = reinterpret_cast<const uint4*>(gq8);
     const uint4* up = reinterpret_cast<const uint4*>(uq8);
@@ -330,8 +334,9 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     for (int n = 0; n < NL; ++n) {
       const int s = CPR > 64 ? n % XS : 0;
       if constexpr (NV) {
-        ag += dot_piece_nv(qg[n], xs[s], sg[n]);
-        au += dot_piece_nv(qu[n], xs[s], su[n]);
+        const int c = (c0 + 64 * n + lane) % CPR;
+        ag += dot_piece_nv(qg[n], xs[s], nv_scales(sg[n], c));
+        au += dot_piece_nv(qu[n], xs[s], nv_scales(su[n], c));
       } else if constexpr (FP4) {
         ag += dot_piece_fp4(qg[n], xs[s], sg[n].x);
         au += dot_piece_fp4(qu[n], xs[s], su[n].x);
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int m = n % LPRD;
-      if constexpr (NV) acc = fmaf(dot_piece_nv_f16(qd[n], hs8[m], sd[n]), td[m], acc);
+      if constexpr (NV) acc = fmaf(dot_piece_nv_f16(qd[n], hs8[m], nv_scales(sd[n], cc[m])), td[m], acc);
       else if constexpr (FP4) acc += dot_piece_fp4_f16(qd[n], hs8[m], sd[n].x);
       else acc += dot_piece_f16(qd[n], hs8[m], sd[n]);
       if (n % LPRD == LPRD - 1) {
