@@ -14,7 +14,7 @@ constexpr int kAbiVersion = 4;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
-      hrec, epoch, cleared;                      // [0, cleared) is zeroed at init
+      hrec, epoch, sort_wc, cleared;             // [0, cleared) is zeroed at init
   size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
   size_t router_t;                                       // bf16 terms of the router matrix (same)
   size_t total;
@@ -79,6 +79,7 @@ Layout layout_of(const moe_layer_desc* d) {
   L.tagged = o, o += align256((E + 3) / 4 * 128);                          // 4 logits per line
   L.hrec = o, o += align256((k + ns) * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
+  L.sort_wc = o, o += align256(T > 1 ? (size_t)64 * E * sizeof(int32_t) : 0);      // per-wave counts of the wide sort
   L.cleared = o;
   const bool copy = needs_tiled_copy(d);
   const size_t cq = copy ? (E + ns) * f_ * d_ / 2 : 0, cs = copy ? (E + ns) * f_ * (d_ / 32) * 2 : 0;
@@ -202,6 +203,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
   a.xp = reinterpret_cast<uint16_t*>(base + L.xp);
   a.xn = reinterpret_cast<uint16_t*>(base + L.xn);
+  a.sort_wc = reinterpret_cast<int32_t*>(base + L.sort_wc);
   a.off = reinterpret_cast<int32_t*>(base + L.off);
   a.meta = a.off + desc->n_experts + 1;
   a.act = reinterpret_cast<int32_t*>(base + L.act);

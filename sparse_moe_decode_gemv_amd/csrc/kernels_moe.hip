@@ -115,8 +115,8 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
   return m;
 }
 
-// One workgroup of 16 waves: the Tk = T*k assignments a = t*k + j (chosen
-// expert sel[a]) grouped by expert, ascending a within an expert:
+// The Tk = T*k assignments a = t*k + j (chosen expert sel[a]) grouped by
+// expert, ascending a within an expert:
 //   off[e] .. off[e+1]-1  positions of expert e in asg (off[E] = Tk)
 //   asg[p]                the assignment at position p
 //   act[i], i < meta[0]   the experts with at least one assignment, ascending
@@ -126,33 +126,29 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, uint64_t valid) {
 //   meta[1], meta[2]      all chunks, Tk
 // With a shared expert, its T assignments Tk + t sit at positions Tk + t and
 // its chunks (expert index E) follow the routed ones.
-// Wave w owns the w-th sixteenth of the assignments: it counts them per
+// Each wave owns a contiguous slice of the assignments: it counts them per
 // expert (lanes with equal experts found by wave ballots), a prefix over
 // waves gives each (wave, expert) its base, and each wave places its own
-// assignments in order: stable, deterministic, no atomics.
-// LDS (dynamic): sel [Tk], cnt [16][E], tot [E].
-__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS) {
-  extern __shared__ int sm[];
-  const int E = a.E, Tk = T * a.k;
-  int* cnt = sm;
-  int* tot = cnt + 16 * E;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // the chosen experts are read where they are (T*k of them may exceed LDS at prefill sizes)
-  auto sel = [&](int i) { return min(max(a.sel_idx[i], 0), E - 1); };
-  for (int i = tid; i < a.ns * T; i += 1024) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
-  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
-  __syncthreads();
-  const int per = (Tk + 15) / 16, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
-  int* cw = cnt + wave * E;
-  // this wave's chosen experts are read SB chunks of 64 at a time (all loads
-  // in flight together), in both passes
-  constexpr int SB = 16;
-  for (int cb = a0; cb < a1; cb += 64 * SB) {  // this wave's counts
-    int eb[SB];
+// assignments in order: stable, deterministic, no atomics.  Up to 4096
+// assignments one workgroup of 16 waves does all of it (k_sort); beyond,
+// 64 waves in 16 workgroups count and place, with one workgroup scanning
+// between them (k_sort_count, k_sort_scan, k_sort_place).
+
+constexpr int kSortSB = 16;          // chunks of 64 whose expert loads are in flight together
+constexpr int kSortWideWaves = 64;   // waves of the three-kernel sort
+constexpr int kSortWideMin = 4096;   // assignments from which it is used
+
+__device__ __forceinline__ int sel_of(const LayerArgs& a, int i, int E) { return min(max(a.sel_idx[i], 0), E - 1); }
+
+// Counts of the wave's slice [a0, a1) into cw[e] (zeroed).
+__device__ void sort_count(const LayerArgs& a, int Tk, int a0, int a1, int lane, int* cw) {
+  const int E = a.E;
+  for (int cb = a0; cb < a1; cb += 64 * kSortSB) {
+    int eb[kSortSB];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) eb[u] = sel(min(cb + 64 * u + lane, Tk - 1));
+    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of(a, min(cb + 64 * u + lane, Tk - 1), E);
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
+    for (int u = 0; u < kSortSB; ++u) {
       const int i = cb + 64 * u + lane;
       if (cb + 64 * u >= a1) break;
       const bool v = i < a1;
@@ -162,6 +158,96 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS)
       lds_wait();
     }
   }
+}
+
+// Places the wave's slice: cw[e] holds the next position of expert e.
+__device__ void sort_place(const LayerArgs& a, int Tk, int a0, int a1, int lane, int* cw) {
+  const int E = a.E;
+  for (int cb = a0; cb < a1; cb += 64 * kSortSB) {
+    int eb[kSortSB];
+#pragma unroll
+    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of(a, min(cb + 64 * u + lane, Tk - 1), E);
+#pragma unroll
+    for (int u = 0; u < kSortSB; ++u) {
+      const int i = cb + 64 * u + lane;
+      if (cb + 64 * u >= a1) break;
+      const bool v = i < a1;
+      const int e = eb[u];
+      const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
+      const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+      const int pos = v ? cw[e] : 0;
+      lds_wait();
+      if (v) a.asg[pos + rank] = i;
+      if (v && lane == __builtin_ctzll(same)) cw[e] += __builtin_popcountll(same);
+      lds_wait();
+    }
+  }
+}
+
+// One wave: from the totals tot[e], the tables off, act, chunk_off, chunks
+// and meta; tot[e] becomes the first position of expert e.
+__device__ void sort_tables(const LayerArgs& a, int T, int Tk, int CS, int lane, int* tot) {
+  const int E = a.E;
+  const int pe = (E + 63) / 64;
+  const int e0 = min(lane * pe, E), e1 = min(e0 + pe, E);
+  int s = 0, na = 0, nc = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int n = tot[e];
+    s += n;
+    na += n > 0;
+    nc += (n + CS - 1) / CS;
+  }
+  int base = s, abase = na, cbase = nc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int b1 = __shfl_up(base, o, 64), b2 = __shfl_up(abase, o, 64), b3 = __shfl_up(cbase, o, 64);
+    if (lane >= o) {
+      base += b1;
+      abase += b2;
+      cbase += b3;
+    }
+  }
+  base -= s;
+  abase -= na;
+  cbase -= nc;
+  for (int e = e0; e < e1; ++e) {
+    const int n = tot[e];
+    a.off[e] = base;
+    if (n > 0) {
+      a.act[abase] = e;
+      a.chunk_off[abase] = cbase;
+      ++abase;
+      for (int tc = 0; tc < n; tc += CS) a.chunks[cbase++] = make_int4(e, base + tc, min(CS, n - tc), 0);
+    }
+    tot[e] = base;  // from here on: the first position of expert e
+    base += n;
+  }
+  if (lane == 63) {
+    a.off[E] = base;
+    a.chunk_off[abase] = cbase;
+    a.meta[0] = abase;
+    // the shared expert (expert index E of the tile-major copies) takes
+    // every token, in chunks after the routed ones
+    for (int tc = 0; tc < a.ns * T; tc += CS) a.chunks[cbase++] = make_int4(E, Tk + tc, min(CS, T - tc), 0);
+    a.meta[1] = cbase;
+    a.meta[2] = Tk;
+  }
+}
+
+// One workgroup of 16 waves (up to kSortWideMin assignments).
+// LDS (dynamic): cnt [16][E], tot [E].
+__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS) {
+  extern __shared__ int sm[];
+  const int E = a.E, Tk = T * a.k;
+  int* cnt = sm;
+  int* tot = cnt + 16 * E;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < a.ns * T; i += 1024) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
+  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int per = (Tk + 15) / 16, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
+  int* cw = cnt + wave * E;
+  sort_count(a, Tk, a0, a1, lane, cw);
   __syncthreads();
   for (int e = tid; e < E; e += 1024) {  // base of each wave within expert e, and e's total
     int run = 0;
@@ -173,73 +259,63 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS)
     tot[e] = run;
   }
   __syncthreads();
-  if (wave == 0) {
-    // exclusive scans over experts: counts, active flags, chunks
-    const int pe = (E + 63) / 64;
-    const int e0 = min(lane * pe, E), e1 = min(e0 + pe, E);
-    int s = 0, na = 0, nc = 0;
-    for (int e = e0; e < e1; ++e) {
-      const int n = tot[e];
-      s += n;
-      na += n > 0;
-      nc += (n + CS - 1) / CS;
-    }
-    int base = s, abase = na, cbase = nc;
+  if (wave == 0) sort_tables(a, T, Tk, CS, lane, tot);
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) cw[e] += tot[e];  // absolute next positions of this wave
+  lds_wait();
+  sort_place(a, Tk, a0, a1, lane, cw);
+}
+
+// Three-kernel sort for many assignments: wave w of kSortWideWaves (16
+// workgroups of 4) owns slice w; its counts go to wc[w][E] in the workspace,
+// k_sort_scan turns them into per-wave bases and builds the tables, and the
+// waves then place their slices.
+__global__ __launch_bounds__(256) void k_sort_count(const LayerArgs a, int T) {
+  extern __shared__ int sm[];  // [4][E]
+  const int E = a.E, Tk = T * a.k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, w = blockIdx.x * 4 + wave;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < a.ns * T; i += gridDim.x * 256) a.asg[Tk + i] = Tk + i;
+  int* cw = sm + wave * E;
+  for (int e = lane; e < E; e += 64) cw[e] = 0;
+  lds_wait();
+  const int per = (Tk + kSortWideWaves - 1) / kSortWideWaves, a0 = min(w * per, Tk), a1 = min(a0 + per, Tk);
+  sort_count(a, Tk, a0, a1, lane, cw);
+  for (int e = lane; e < E; e += 64) a.sort_wc[(size_t)w * E + e] = cw[e];
+}
+
+// One workgroup: per expert, the exclusive prefix of the wave counts (the
+// wave bases, written back), the totals, then the tables.  LDS: tot [E].
+__global__ __launch_bounds__(1024) void k_sort_scan(const LayerArgs a, int T, int CS) {
+  extern __shared__ int sm[];
+  const int E = a.E, Tk = T * a.k;
+  int* tot = sm;
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int run = 0;
+    for (int w0 = 0; w0 < kSortWideWaves; w0 += 16) {  // 16 loads in flight at a time
+      int c[16];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int b1 = __shfl_up(base, o, 64), b2 = __shfl_up(abase, o, 64), b3 = __shfl_up(cbase, o, 64);
-      if (lane >= o) {
-        base += b1;
-        abase += b2;
-        cbase += b3;
+      for (int u = 0; u < 16; ++u) c[u] = a.sort_wc[(size_t)(w0 + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        a.sort_wc[(size_t)(w0 + u) * E + e] = run;
+        run += c[u];
       }
     }
-    base -= s;
-    abase -= na;
-    cbase -= nc;
-    for (int e = e0; e < e1; ++e) {
-      const int n = tot[e];
-      a.off[e] = base;
-      if (n > 0) {
-        a.act[abase] = e;
-        a.chunk_off[abase] = cbase;
-        ++abase;
-        for (int tc = 0; tc < n; tc += CS) a.chunks[cbase++] = make_int4(e, base + tc, min(CS, n - tc), 0);
-      }
-      tot[e] = base;  // from here on: the first position of expert e
-      base += n;
-    }
-    if (lane == 63) {
-      a.off[E] = base;
-      a.chunk_off[abase] = cbase;
-      a.meta[0] = abase;
-      // the shared expert (expert index E of the tile-major copies) takes
-      // every token, in chunks after the routed ones
-      for (int tc = 0; tc < a.ns * T; tc += CS) a.chunks[cbase++] = make_int4(E, Tk + tc, min(CS, T - tc), 0);
-      a.meta[1] = cbase;
-      a.meta[2] = Tk;
-    }
+    tot[e] = run;
   }
   __syncthreads();
-  for (int cb = a0; cb < a1; cb += 64 * SB) {  // placement, stable in a
-    int eb[SB];
-#pragma unroll
-    for (int u = 0; u < SB; ++u) eb[u] = sel(min(cb + 64 * u + lane, Tk - 1));
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const int i = cb + 64 * u + lane;
-      if (cb + 64 * u >= a1) break;
-      const bool v = i < a1;
-      const int e = eb[u];
-      const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
-      const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
-      const int pos = v ? tot[e] + cw[e] : 0;
-      lds_wait();
-      if (v) a.asg[pos + rank] = i;
-      if (v && lane == __builtin_ctzll(same)) cw[e] += __builtin_popcountll(same);
-      lds_wait();
-    }
-  }
+  if (threadIdx.x < 64) sort_tables(a, T, Tk, CS, threadIdx.x, tot);
+}
+
+__global__ __launch_bounds__(256) void k_sort_place(const LayerArgs a, int T) {
+  extern __shared__ int sm[];  // [4][E]
+  const int E = a.E, Tk = T * a.k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, w = blockIdx.x * 4 + wave;
+  int* cw = sm + wave * E;
+  for (int e = lane; e < E; e += 64) cw[e] = a.off[e] + a.sort_wc[(size_t)w * E + e];
+  lds_wait();
+  const int per = (Tk + kSortWideWaves - 1) / kSortWideWaves, a0 = min(w * per, Tk), a1 = min(a0 + per, Tk);
+  sort_place(a, Tk, a0, a1, lane, cw);
 }
 
 // Tokens per chunk of the expert kernels: 64 once the experts average 32
@@ -934,6 +1010,13 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
         return hipErrorInvalidValue;
       raised = true;
     }
+  }
+  if (T * a.k >= kSortWideMin) {
+    const size_t l4 = (size_t)4 * a.E * sizeof(int);
+    hipLaunchKernelGGL(k_sort_count, dim3(kSortWideWaves / 4), dim3(256), l4, s, a, T);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(1024), (size_t)a.E * sizeof(int), s, a, T, chunk_rows(a, T));
+    hipLaunchKernelGGL(k_sort_place, dim3(kSortWideWaves / 4), dim3(256), l4, s, a, T);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), lds, s, a, T, chunk_rows(a, T));
   return hipGetLastError();

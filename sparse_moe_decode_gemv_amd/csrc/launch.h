@@ -57,6 +57,7 @@ struct LayerArgs {
                           // CS = 32, or 64 when T*k >= 32*E;
                           // the shared expert's chunks (expert E) come last
   int32_t* meta;          // [0]: active routed experts, [1]: chunks, [2]: T*k
+  int32_t* sort_wc;       // [64][E] per-wave expert counts, then bases (the many-assignment sort)
   int32_t* asg;           // [T*k + ns*T] assignments grouped by expert (shared: T*k + t, last)
   uint16_t* h16;          // [T*k + ns*T][f] w_j silu(g) u per position, fp16 operand order
   float* obuf;            // [T*k + ns*T][d] o_{t,j} per assignment
