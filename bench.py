@@ -32,8 +32,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCES = ["sparse_moe_decode_gemv_amd/csrc/kernels_layer.hip", "sparse_moe_decode_gemv_amd/csrc/device_common.h",
-                  "sparse_moe_decode_gemv_amd/csrc/topk.h"]
+KERNEL_SOURCES = ["sparse_moe_decode_gemv_amd/csrc/layer_kernel.h", "sparse_moe_decode_gemv_amd/csrc/kernels_layer.hip",
+                  "sparse_moe_decode_gemv_amd/csrc/device_common.h", "sparse_moe_decode_gemv_amd/csrc/topk.h"]
 
 
 def log(*a):

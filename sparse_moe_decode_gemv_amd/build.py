@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_decode.so")
-SOURCES = ["api.hip", "kernels_moe.hip", "kernels_lmhead.hip", "kernels_layer.hip"]
+SOURCES = ["api.hip", "kernels_moe.hip", "kernels_lmhead.hip", "kernels_layer.hip", "kernels_layer_mxfp4.hip",
+           "kernels_layer_nvfp4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

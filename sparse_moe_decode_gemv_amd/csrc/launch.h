@@ -117,6 +117,10 @@ struct FusedArgs {
 bool fused_layer_supported(int d, int f, int E, int k, int ns, int G);
 int fused_grid();
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
+// the per-format instances (grid G), in their own translation units
+hipError_t launch_layer_int4(const FusedArgs& a, int d, int f, int G, hipStream_t s);
+hipError_t launch_layer_mxfp4(const FusedArgs& a, int d, int f, int G, hipStream_t s);
+hipError_t launch_layer_nvfp4(const FusedArgs& a, int d, int f, int G, hipStream_t s);
 
 // Router logits of T tokens (a matrix product), then softmax + top-k of
 // every token and the assignments grouped by expert.  Activations come
