@@ -82,7 +82,9 @@ Layout layout_of(const moe_layer_desc* d) {
   L.sort_wc = o, o += align256(T > 1 ? (size_t)64 * E * sizeof(int32_t) : 0);      // per-wave counts of the wide sort
   L.cleared = o;
   const bool copy = needs_tiled_copy(d);
-  const size_t cq = copy ? (E + ns) * f_ * d_ / 2 : 0, cs = copy ? (E + ns) * f_ * (d_ / 32) * 2 : 0;
+  // scale copy: 2 bytes per 32 elements (int4, MXFP4 uses half), 4 for NVFP4 (fp16 per 16 elements)
+  const size_t sb = d->weight_format == MOE_WEIGHTS_NVFP4 ? 4 : 2;
+  const size_t cq = copy ? (E + ns) * f_ * d_ / 2 : 0, cs = copy ? (E + ns) * f_ * (d_ / 32) * sb : 0;
   L.gate_t = o, o += align256(cq);
   L.gate_ts = o, o += align256(cs);
   L.up_t = o, o += align256(cq);

@@ -667,6 +667,32 @@ __global__ __launch_bounds__(256) void k_tile_scales(const U* __restrict__ src, 
   dst[((row >> 4) * upr + kb) * 16 + (row & 15)] = src[i];
 }
 
+// NVFP4 scales into the tile-major order with the matrix scale folded in:
+// thread (row, block kb, half h) writes the fp16 values of the row's E4M3
+// scales h, h+2, h+4, h+6 of that 128-element block times the row's matrix
+// scale (rounded once to fp16) -- the 4 scales a lane of piece q, h = q/2,
+// uses -- at unit ((row/16) * K/128 + kb) * 32 + 16 h + row % 16.
+__global__ __launch_bounds__(256) void k_tile_scales_nv(const uint8_t* __restrict__ src, const float* __restrict__ tsc,
+                                                        long long rows_per_mat, long long rows, int K,
+                                                        uint2* __restrict__ dst) {
+  const int upr = K / 128;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * upr * 2) return;
+  const int h = (int)(i & 1);
+  const long long ru = i >> 1, row = ru / upr;
+  const int kb = (int)(ru - row * upr);
+  const uint2 b = *reinterpret_cast<const uint2*>(src + row * (K / 16) + 8 * kb);
+  const float t = tsc[row / rows_per_mat];
+  uint32_t f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bi = 2 * j + h;
+    const uint32_t byte = ((bi < 4 ? b.x : b.y) >> (8 * (bi & 3))) & 0xFFu;
+    f[j] = __builtin_bit_cast(uint16_t, (_Float16)(e4m3_f32(byte) * t));
+  }
+  dst[((row >> 4) * upr + kb) * 32 + 16 * h + (row & 15)] = make_uint2(f[0] | (f[1] << 16), f[2] | (f[3] << 16));
+}
+
 // Weights of one block for one 16-row tile: this lane's row, chunk q of the
 // block's 4 groups, and the 4 group scales, from the tile-major copy.
 struct WBlk {
@@ -674,21 +700,24 @@ struct WBlk {
   uint2 s;
 };
 // FMT: 0 int4 (4 binary16 scales per row and block: 8 bytes), 1 MXFP4 (4
-// E8M0 bytes), 2 NVFP4 (8 E4M3 bytes, one per 16 elements)
+// E8M0 bytes), 2 NVFP4 (per row and block two sets of 4 fp16 scales, the
+// matrix scale folded in; a lane takes the set of its piece's half)
 template <int FMT>
 __device__ __forceinline__ WBlk wload(const uint4* tq, const uint2* ts, int blk, int lane) {
   WBlk w;
   w.q = tq[blk * 64 + lane];
   if constexpr (FMT == 1) w.s = make_uint2(reinterpret_cast<const uint32_t*>(ts)[blk * 16 + (lane & 15)], 0u);
+  else if constexpr (FMT == 2) w.s = ts[blk * 32 + 16 * (lane >> 5) + (lane & 15)];
   else w.s = ts[blk * 16 + (lane & 15)];
   return w;
 }
 
-// Scales of tile unit `off` (units of one row's block scales) of a
-// tile-major scale copy.
+// Scales of tile unit `off` (units of one row's block scales: 16 per tile
+// and block) of a tile-major scale copy.
 template <int FMT>
 __device__ __forceinline__ const uint2* tile_scales(const uint16_t* base, size_t off) {
   if constexpr (FMT == 1) return reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(base) + off);
+  else if constexpr (FMT == 2) return reinterpret_cast<const uint2*>(base) + 2 * off;
   else return reinterpret_cast<const uint2*>(base) + off;
 }
 
@@ -713,18 +742,16 @@ __device__ __forceinline__ f16x8_t dequant_fp4_f16(uint32_t w, float scale) {
 // One block of K for two weight tiles against the NTT staged token tiles:
 // each weight dword is dequantized once and used by NTT MFMAs.
 // NVFP4 B operand: the codes converted exactly (scale 1), then one fp16
-// multiply by the block's E4M3 value times the matrix scale (that product
-// rounded to fp16 first): two roundings of 2^-11, like int4's q * s.
-__device__ __forceinline__ f16x8_t dequant_nv_f16(uint32_t w, float scale) {
-  const _Float16 h = (_Float16)scale;
-  const f16x8_t s8 = {h, h, h, h, h, h, h, h};
+// multiply by s2, the block's E4M3 value times the matrix scale (rounded to
+// fp16 once, at init): two roundings of 2^-11, like int4's q * s.
+__device__ __forceinline__ f16x8_t dequant_nv_f16(uint32_t w, f16x2_t s2) {
+  const f16x8_t s8 = {s2.x, s2.y, s2.x, s2.y, s2.x, s2.y, s2.x, s2.y};
   return dequant_fp4_f16(w, 1.0f) * s8;
 }
 
-// tsc: NVFP4 matrix scale of each weight tile
 template <int NTT, int FMT>
 __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<NTT>& t, const WBlk (&w)[2],
-                                           int lane, uint32_t magic, const float (&tsc)[2]) {
+                                           int lane, uint32_t magic) {
   const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -732,10 +759,9 @@ __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if constexpr (FMT == 2) {
-        // dword j of piece q spans elements 32j + 8q .. +7: 16-block 2j + q/2
-        const int b = 2 * j + (q >> 1);
-        const uint32_t sb = ((b < 4 ? w[i].s.x : w[i].s.y) >> (8 * (b & 3))) & 0xFFu;
-        wb[i] = dequant_nv_f16(dword_of(w[i].q, j), e4m3_f32(sb) * tsc[i]);
+        // dword j of piece q spans elements 32j + 8q .. +7: 16-block 2j + q/2,
+        // scale j of the lane's set
+        wb[i] = dequant_nv_f16(dword_of(w[i].q, j), scale2(w[i].s, j));
       } else if constexpr (FMT == 1) {
         wb[i] = dequant_fp4_f16(dword_of(w[i].q, j), ldexpf(1.0f, (int)((w[i].s.x >> (8 * j)) & 0xFFu) - 127));
       } else {
@@ -763,8 +789,7 @@ __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<
 template <int K, int NTT, int FMT>
 __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tiles,
                                        const uint16_t* const (&op_rows)[NTT / 2], const uint4* const (&wtq)[2],
-                                       const uint2* const (&wts)[2], int tid, int lane, uint32_t magic,
-                                       const float (&tsc)[2]) {
+                                       const uint2* const (&wts)[2], int tid, int lane, uint32_t magic) {
   constexpr int NBLK = K / 128;
   constexpr int G = NBLK < 2 ? NBLK : 2;    // weight blocks per burst
   constexpr int SX = NBLK < 4 ? NBLK : 4;   // operand blocks in flight
@@ -795,7 +820,7 @@ __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tile
       for (int i = 0; i < G; ++i) {
         const int b = g0 + i;
         if (b < NBLK) {
-          block_mfma<NTT, FMT>(acc, tiles[b & 1], w[h][i], lane, magic, tsc);
+          block_mfma<NTT, FMT>(acc, tiles[b & 1], w[h][i], lane, magic);
           // slot (b+1) % SX holds block b+1: into the other LDS buffer, then refill
           stage_store(tiles[(b + 1) & 1], sx[(b + 1) % SX], tid);
           sx[(b + 1) % SX] = stage_load(min(b + 1 + SX, NBLK - 1), op_rows, tid);
@@ -826,11 +851,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
                            reinterpret_cast<const uint4*>(a.up_t) + tile * (D / 128) * 64};
     const uint2* wts[2] = {tile_scales<FMT>(a.gate_ts, tile * (D / 128) * 16),
                            tile_scales<FMT>(a.up_ts, tile * (D / 128) * 16)};
-    float tsc[2] = {1.f, 1.f};
-    if constexpr (FMT == 2) {  // the matrix scales of this item's expert (index E: the shared one)
-      tsc[0] = it.e < a.E ? a.gate_tscale[it.e] : a.sh_gate_tscale[0];
-      tsc[1] = it.e < a.E ? a.up_tscale[it.e] : a.sh_up_tscale[0];
-    }
+
     // the operand rows this thread stages: tokens of chunk rows tid/8 + 32m
     const int Tk = a.meta[2];
     const uint16_t* rows[NTT / 2];
@@ -845,7 +866,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // all token tiles always (rows past the chunk repeat a real row and
     // their outputs are dropped): one code path
-    k_loop<D, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic, tsc);
+    k_loop<D, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
     // lane: weight row r16, tokens 4q+v of each tile
     const int e8 = r16 & 7;
     const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);  // h in operand order
@@ -886,8 +907,7 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
                            reinterpret_cast<const uint4*>(a.down_t) + (tile + 1) * (F / 128) * 64};
     const uint2* wts[2] = {tile_scales<FMT>(a.down_ts, tile * (F / 128) * 16),
                            tile_scales<FMT>(a.down_ts, (tile + 1) * (F / 128) * 16)};
-    float tsc[2] = {1.f, 1.f};
-    if constexpr (FMT == 2) tsc[0] = tsc[1] = it.e < a.E ? a.down_tscale[it.e] : a.sh_down_tscale[0];
+
     const uint16_t* rows[NTT / 2];
 #pragma unroll
     for (int m = 0; m < NTT / 2; ++m) rows[m] = a.h16 + (size_t)(it.p0 + min((tid >> 3) + 32 * m, it.n - 1)) * F;
@@ -900,7 +920,7 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
     f32x4_t acc[2][NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    k_loop<F, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic, tsc);
+    k_loop<F, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       if (16 * tt >= it.n) break;
@@ -1079,12 +1099,16 @@ hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
   return c64 ? down_inst<4, 0>(a, g, s) : down_inst<2, 0>(a, g, s);
 }
 
+// fmt: 0 int4, 1 MXFP4, 2 NVFP4 (tsc: its matrix scales, rows_per_mat rows each)
 static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq, uint16_t* ts, long long rows, int K,
-                              bool fp4, hipStream_t s) {
+                              int fmt, const float* tsc, long long rows_per_mat, hipStream_t s) {
   const long long np = rows * (K / 32), ns = rows * (K / 128);
   hipLaunchKernelGGL(k_tile_codes, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(q), reinterpret_cast<uint4*>(tq), rows, K);
-  if (fp4)
+  if (fmt == 2)
+    hipLaunchKernelGGL(k_tile_scales_nv, dim3((unsigned)((2 * ns + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint8_t*>(sc), tsc, rows_per_mat, rows, K, reinterpret_cast<uint2*>(ts));
+  else if (fmt == 1)
     hipLaunchKernelGGL((k_tile_scales<uint32_t>), dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<const uint32_t*>(sc), reinterpret_cast<uint32_t*>(ts), rows, K);
   else
@@ -1093,11 +1117,12 @@ static hipError_t tile_matrix(const uint8_t* q, const uint16_t* sc, uint8_t* tq,
   return hipGetLastError();
 }
 
-// n scales (of 32 elements) into a scale array: 1 byte each for MXFP4, 2
-// for int4 (binary16) and NVFP4 (two E4M3)
-static uint16_t* scales_at(const uint16_t* base, size_t n, bool fp4) {
-  return const_cast<uint16_t*>(fp4 ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + n)
-                                   : base + n);
+// Bytes per 32 elements of the tile-major scale copy: 2 (int4 binary16), 1
+// (MXFP4 E8M0), 4 (NVFP4: two fp16 per 32 elements).
+static size_t copy_scale_bytes(int fmt) { return fmt == 1 ? 1 : fmt == 2 ? 4 : 2; }
+static uint16_t* scales_at(const uint16_t* base, size_t n, int fmt) {
+  return const_cast<uint16_t*>(
+      reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + n * copy_scale_bytes(fmt)));
 }
 
 hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
@@ -1107,28 +1132,29 @@ hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_router_terms, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, a.router_w, a.E, a.d,
                      reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.router_t)));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const bool fp4 = a.fmt == 1;  // 4-byte scale units (MXFP4); int4 and NVFP4 have 8-byte units
+  const int fmt = a.fmt;
+  const long long F = a.f, Dd = a.d;
   if ((e = tile_matrix(a.gate_q, a.gate_s, const_cast<uint8_t*>(a.gate_t), const_cast<uint16_t*>(a.gate_ts),
-                       E * a.f, a.d, fp4, s)) != hipSuccess)
+                       E * a.f, a.d, fmt, a.gate_tscale, F, s)) != hipSuccess)
     return e;
   if ((e = tile_matrix(a.up_q, a.up_s, const_cast<uint8_t*>(a.up_t), const_cast<uint16_t*>(a.up_ts), E * a.f,
-                       a.d, fp4, s)) != hipSuccess)
+                       a.d, fmt, a.up_tscale, F, s)) != hipSuccess)
     return e;
   if ((e = tile_matrix(a.down_q, a.down_s, const_cast<uint8_t*>(a.down_t), const_cast<uint16_t*>(a.down_ts),
-                       E * a.d, a.f, fp4, s)) != hipSuccess)
+                       E * a.d, a.f, fmt, a.down_tscale, Dd, s)) != hipSuccess)
     return e;
   if (!a.ns) return hipSuccess;
-  // the shared expert as expert E of the copies (scale offsets in scales)
+  // the shared expert as expert E of the copies (scale offsets in scales of 32 elements)
   const size_t gq = (size_t)E * a.f * a.d / 2, gs = (size_t)E * a.f * (a.d / 32);
   const size_t dq = (size_t)E * a.d * a.f / 2, ds = (size_t)E * a.d * (a.f / 32);
-  if ((e = tile_matrix(a.sh_gate_q, a.sh_gate_s, const_cast<uint8_t*>(a.gate_t) + gq, scales_at(a.gate_ts, gs, fp4),
-                       a.f, a.d, fp4, s)) != hipSuccess)
+  if ((e = tile_matrix(a.sh_gate_q, a.sh_gate_s, const_cast<uint8_t*>(a.gate_t) + gq, scales_at(a.gate_ts, gs, fmt),
+                       a.f, a.d, fmt, a.sh_gate_tscale, F, s)) != hipSuccess)
     return e;
-  if ((e = tile_matrix(a.sh_up_q, a.sh_up_s, const_cast<uint8_t*>(a.up_t) + gq, scales_at(a.up_ts, gs, fp4), a.f,
-                       a.d, fp4, s)) != hipSuccess)
+  if ((e = tile_matrix(a.sh_up_q, a.sh_up_s, const_cast<uint8_t*>(a.up_t) + gq, scales_at(a.up_ts, gs, fmt), a.f,
+                       a.d, fmt, a.sh_up_tscale, F, s)) != hipSuccess)
     return e;
-  return tile_matrix(a.sh_down_q, a.sh_down_s, const_cast<uint8_t*>(a.down_t) + dq, scales_at(a.down_ts, ds, fp4),
-                     a.d, a.f, fp4, s);
+  return tile_matrix(a.sh_down_q, a.sh_down_s, const_cast<uint8_t*>(a.down_t) + dq, scales_at(a.down_ts, ds, fmt),
+                     a.d, a.f, fmt, a.sh_down_tscale, Dd, s);
 }
 
 hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s) {

@@ -26,9 +26,10 @@ def test_prefill_512_tokens_every_output():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfgname,T", [("LAYER", 2048), ("FLINT", 1024)], ids=["top8-2048", "top6-shared-1024"])
+@pytest.mark.parametrize("cfgname,T", [("LAYER", 2048), ("FLINT", 1024), ("LAYER", 4096)],
+                         ids=["top8-2048", "top6-shared-1024", "top8-4096-max"])
 def test_prefill_large_sampled(cfgname, T):
-    """T up to 2048 in one call: the chosen experts of every token and the
+    """T up to 4096 (MOE_MAX_TOKENS) in one call: the chosen experts of every token and the
     grouping are checked in full (bit-exact sets), the outputs of 96 tokens
     spread over the call against the oracle (it evaluates each token on its
     own, so a sample bounds its time)."""
