@@ -144,7 +144,9 @@ typedef struct moe_layer* moe_handle;
  * layer that may run the batched kernels (max_tokens > 1, or a shape the
  * single-launch kernel does not take), a tile-major copy of the gate, up and
  * down matrices, the shared expert's included (their size: 3*(E+n_shared)*
- * d*f/2 bytes of codes + 3*(E+n_shared)*d*f/16 of scales), and the router
+ * d*f/2 bytes of codes + 3*(E+n_shared)*d*f/16 of scales, twice that for
+ * NVFP4, whose copy holds binary16 block scales with the matrix scale folded
+ * in), and the router
  * matrix as three bfloat16 terms whose sum is exactly W_r (6*E*d bytes, E
  * rounded up to 16). */
 size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
