@@ -230,8 +230,10 @@ size_t lmhead_int4_argmax_workspace_bytes(int32_t V, int32_t d, int32_t B);
  *   token     (device) int32 [B]
  *   max_logit (device) fp32 [B], or NULL
  *   workspace (device) at least lmhead_int4_argmax_workspace_bytes(V, d, B)
- *             bytes, zero-filled before its first use; every call leaves it
- *             zero-filled again.  Calls sharing a workspace must not overlap. */
+ *             bytes, 256-byte aligned, zero-filled before its first use:
+ *             it holds arrival counters, which every call leaves at zero
+ *             again, and per-workgroup partial results, which need no
+ *             clearing.  Calls sharing a workspace must not overlap. */
 moe_status lmhead_int4_argmax(const uint8_t* w_q, const uint16_t* w_s, int32_t V, int32_t d,
                               const uint16_t* x, int32_t B, int32_t* token, float* max_logit,
                               void* workspace, size_t workspace_bytes, void* stream);

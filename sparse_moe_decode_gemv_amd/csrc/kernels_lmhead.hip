@@ -10,8 +10,8 @@
 // tiles of 64*NL consecutive 16-byte pieces per wave (one piece per lane per
 // load, activations of up to BP rows of x in registers).  Each workgroup
 // writes its best (value, row) per x row as a 64-bit key; the last workgroup
-// to arrive reduces the G keys, writes token and max logit, and clears the
-// arrival counter so the next call starts from zero.
+// to arrive (a two-level count, below) reduces the G keys, writes token and
+// max logit, and clears the top counter so the next call starts from zero.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -26,6 +26,25 @@ __device__ __forceinline__ unsigned long long make_key(float z, uint32_t row) {
 }
 
 constexpr int kLmMaxGrid = 4096;
+
+// Arrival.  Same-address atomics are serialized (about 14 ns each here), so
+// G workgroups finishing together on one counter would end the kernel with G
+// of them in a row.  Instead groups of kLmArr workgroups count on counters
+// of their own, each on its own 128-byte line, and the last of each group
+// counts on the top counter (line 0).  Every counter is zeroed by the last
+// to arrive on it.  Called by one thread after the workgroup's partial
+// results were stored and waited for; true in the last workgroup to arrive.
+constexpr int kLmArr = 32;
+constexpr int kLmLine = 32;  // counters are kLmLine unsigned apart
+constexpr size_t kLmCtrBytes = ((1 + kLmMaxGrid / kLmArr) * 128 + 255) / 256 * 256;
+__device__ __forceinline__ bool lm_arrive_last(unsigned* ctr) {
+  const int G = gridDim.x, g = blockIdx.x / kLmArr, ng = (G + kLmArr - 1) / kLmArr;
+  const unsigned gsize = (unsigned)min(kLmArr, G - g * kLmArr);
+  unsigned* mine = ctr + (size_t)(1 + g) * kLmLine;
+  if (arrive(mine) != gsize - 1) return false;
+  __hip_atomic_store(mine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return arrive(ctr) == (unsigned)ng - 1;
+}
 
 template <int CPR, int BP, int NL>
 __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
@@ -65,23 +84,20 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
 #pragma unroll
   for (int b = 0; b < BP; ++b) best[b] = -INFINITY, brow[b] = 0xFFFFFFFFu;
 
-  for (size_t tile = (size_t)blockIdx.x * 4 + wid; tile * 64 * NL < total; tile += (size_t)gridDim.x * 4) {
-    const size_t c0 = tile * 64 * NL;
-    uint4 q[NL];
-    uint2 sc[NL];
+  // Tiles are dealt round-robin to the waves.  Every load is unconditional,
+  // so the compiler's wait counts stay exact: pieces past the matrix read
+  // its last piece (their rows are >= V and are dropped below).
+  const size_t ntiles = (total + 64 * NL - 1) / (64 * NL), stride = (size_t)gridDim.x * 4;
+  auto load_tile = [&](size_t t, uint4 (&q)[NL], uint2 (&sc)[NL]) {
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
-      const size_t c = c0 + 64 * n + lane;
-      if (c < total) {
-        q[n] = wp[c];
-        const size_t row = c / CPR;
-        const int cc = (int)(c % CPR);
-        sc[n] = *reinterpret_cast<const uint2*>(ws + row * CPR + (cc & ~3));
-      } else {
-        q[n] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        sc[n] = make_uint2(0, 0);
-      }
+      const size_t c = min(t * 64 * NL + 64 * n + lane, total - 1);
+      q[n] = wp[c];
+      sc[n] = *reinterpret_cast<const uint2*>(ws + (c / CPR) * CPR + ((int)(c % CPR) & ~3));
     }
+  };
+  auto dot_tile = [&](size_t t, const uint4 (&q)[NL], const uint2 (&sc)[NL]) {
+    const size_t c0 = t * 64 * NL;
     float acc[BP];
 #pragma unroll
     for (int b = 0; b < BP; ++b) acc[b] = 0.f;
@@ -101,6 +117,14 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
         }
       }
     }
+  };
+  // The wave index goes through readfirstlane so that the tile sequence is
+  // known to be uniform (scalar loop control).
+  uint4 q[NL];
+  uint2 sc[NL];
+  for (size_t t = (size_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wid); t < ntiles; t += stride) {
+    load_tile(t, q, sc);
+    dot_tile(t, q, sc);
   }
 
   // wave argmax, then across the 4 waves through LDS
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
     wait_vm();
   }
   __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive(counter) == gridDim.x - 1;
+  if (threadIdx.x == 0) s_last = lm_arrive_last(counter);
   __syncthreads();
   if (!s_last) return;
   // last workgroup: reduce G keys per x row, every load issued before any
@@ -399,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void k_lmhead_mfma(const uint8_t* __restric
     wait_vm();
   }
   __syncthreads();
-  if (tid == 0) s_last = arrive(counter) == gridDim.x - 1;
+  if (tid == 0) s_last = lm_arrive_last(counter);
   __syncthreads();
   if (!s_last) return;
   // last workgroup: 32 threads per x row, each loading its keys at once
@@ -436,7 +460,7 @@ size_t lmhead_workspace_bytes(int V, int d, int B) {
   (void)V;
   (void)d;
   const int launches = (B + 7) / 8;
-  return (size_t)launches * (256 + (size_t)kLmMaxGrid * 8 * sizeof(unsigned long long));
+  return (size_t)launches * (kLmCtrBytes + (size_t)kLmMaxGrid * 8 * sizeof(unsigned long long));
 }
 
 static int lm_grid() {
@@ -456,7 +480,7 @@ static void lm_inst(const uint8_t* wq, const uint16_t* ws, int V, const uint16_t
                     int32_t* token, float* max_logit, hipStream_t s) {
   constexpr int NL = BP <= 2 ? 8 : 4;
   unsigned* counter = reinterpret_cast<unsigned*>(wsp);
-  unsigned long long* partial = reinterpret_cast<unsigned long long*>(wsp + 256);
+  unsigned long long* partial = reinterpret_cast<unsigned long long*>(wsp + kLmCtrBytes);
   const size_t tiles = ((size_t)V * CPR + 64 * NL - 1) / (64 * NL);
   int grid = lm_grid();
   if ((size_t)grid * 4 > tiles) grid = (int)((tiles + 3) / 4);
@@ -481,7 +505,7 @@ template <int D>
 static hipError_t lm_mfma(const uint8_t* wq, const uint16_t* ws, int V, const uint16_t* x, int B, unsigned char* wsp,
                           int32_t* token, float* max_logit, hipStream_t s) {
   unsigned* counter = reinterpret_cast<unsigned*>(wsp);
-  unsigned long long* partial = reinterpret_cast<unsigned long long*>(wsp + 256);
+  unsigned long long* partial = reinterpret_cast<unsigned long long*>(wsp + kLmCtrBytes);
   const int ntiles = (V + 15) / 16;
   int grid = lm_grid() / 4;  // one 8-wave workgroup per compute unit, at most kLmMaxGrid / 8
   if (grid > kLmMaxGrid / 8) grid = kLmMaxGrid / 8;
@@ -499,7 +523,7 @@ hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, co
     if (d == 1024) return lm_mfma<1024>(wq, ws, V, x, B, wsp, token, max_logit, s);
     if (d == 2048) return lm_mfma<2048>(wq, ws, V, x, B, wsp, token, max_logit, s);
   }
-  const size_t per = 256 + (size_t)kLmMaxGrid * 8 * sizeof(unsigned long long);
+  const size_t per = kLmCtrBytes + (size_t)kLmMaxGrid * 8 * sizeof(unsigned long long);
   for (int b0 = 0; b0 < B; b0 += 8) {
     const int nb = B - b0 < 8 ? B - b0 : 8;
     const uint16_t* xb = x + (size_t)b0 * d;
