@@ -245,6 +245,7 @@ def test_single_launch_and_batched_calls_interleave_on_one_handle():
 
 
 def test_ragged_token_counts_reuse_one_handle():
+    """T = 7, 1, 3 on one handle sized for 7; T = 8 and T = 0 are rejected."""
     import torch
     cfg = synth.TINY
     lay = synth.make_layer(cfg, 3)
@@ -264,6 +265,13 @@ def test_ragged_token_counts_reuse_one_handle():
     with pytest.raises(M.MoEError) as ei:
         L.forward(torch.zeros((8, cfg.d), dtype=torch.int16, device=dev))
     assert ei.value.status == M.MOE_ERR_SHAPE
+    # an empty call (T = 0) is a shape error too, and launches nothing
+    y0 = torch.full((1, cfg.d), 7.0, device=dev)
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_decode_forward(L.handle, torch.zeros((1, cfg.d), dtype=torch.int16, device=dev), 0, y0)
+    assert ei.value.status == M.MOE_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert torch.all(y0 == 7.0)
 
 
 def test_zero_scale_experts_give_zero_output_and_every_element_is_written():
