@@ -34,7 +34,10 @@ struct LayerArgs {
   const uint16_t* sh_up_s;
   const uint8_t* sh_down_q;
   const uint16_t* sh_down_s;
-  // tile-major copies of the expert matrices, [E + ns] (batched path; max_tokens > 1)
+  // tile-major copies of the expert matrices, [E + ns] (batched path; max_tokens > 1):
+  // codes in MFMA lane order (1 KB per 16 rows x 128 k); scales per (16 rows x 128 k)
+  // as 16 rows of 4 binary16 (int4), 4 E8M0 bytes (MXFP4), or two sets of 4
+  // binary16 block scales with the matrix scale folded in (NVFP4)
   const uint8_t* gate_t;
   const uint16_t* gate_ts;
   const uint8_t* up_t;
