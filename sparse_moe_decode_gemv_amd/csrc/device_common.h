@@ -204,24 +204,32 @@ __device__ __forceinline__ float dot8_fp4_f16(uint32_t w, const Slice8& s) {
 
 // NVFP4: an OCP E4M3 scale per 16 elements; the 4 dwords of a piece take
 // the bytes 0, 2, 4, 6 of `sc` (the piece's 8 scale bytes shifted so that
-// its own come first); products rounded once in fp32.
+// its own come first); products rounded once in fp32.  e4m3_f32 decodes
+// with integer operations (used at init); the dot products use gfx950's
+// fp8 conversion, which on this target decodes the OCP E4M3 format exactly
+// (every byte in every byte position compared on the device) in one
+// instruction with a byte select.
 __device__ __forceinline__ float e4m3_f32(uint32_t b) {
   const uint32_t em = b & 0x7Fu;
   const float mag = em >= 8u ? __uint_as_float((em + (120u << 3)) << 20) : (float)em * 0.001953125f;
   return (b & 0x80u) ? -mag : mag;
 }
+template <int BYTE>
+__device__ __forceinline__ float e4m3_byte(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, BYTE);
+}
 __device__ __forceinline__ float dot_piece_nv(uint4 q, const Slice8 xs[4], uint2 sc) {
-  float p = dot8_fp4(q.x, xs[0]) * e4m3_f32(sc.x & 0xFFu);
-  p = fmaf(dot8_fp4(q.y, xs[1]), e4m3_f32((sc.x >> 16) & 0xFFu), p);
-  p = fmaf(dot8_fp4(q.z, xs[2]), e4m3_f32(sc.y & 0xFFu), p);
-  p = fmaf(dot8_fp4(q.w, xs[3]), e4m3_f32((sc.y >> 16) & 0xFFu), p);
+  float p = dot8_fp4(q.x, xs[0]) * e4m3_byte<0>(sc.x);
+  p = fmaf(dot8_fp4(q.y, xs[1]), e4m3_byte<2>(sc.x), p);
+  p = fmaf(dot8_fp4(q.z, xs[2]), e4m3_byte<0>(sc.y), p);
+  p = fmaf(dot8_fp4(q.w, xs[3]), e4m3_byte<2>(sc.y), p);
   return p;
 }
 __device__ __forceinline__ float dot_piece_nv_f16(uint4 q, const Slice8 xs[4], uint2 sc) {
-  float p = dot8_fp4_f16(q.x, xs[0]) * e4m3_f32(sc.x & 0xFFu);
-  p = fmaf(dot8_fp4_f16(q.y, xs[1]), e4m3_f32((sc.x >> 16) & 0xFFu), p);
-  p = fmaf(dot8_fp4_f16(q.z, xs[2]), e4m3_f32(sc.y & 0xFFu), p);
-  p = fmaf(dot8_fp4_f16(q.w, xs[3]), e4m3_f32((sc.y >> 16) & 0xFFu), p);
+  float p = dot8_fp4_f16(q.x, xs[0]) * e4m3_byte<0>(sc.x);
+  p = fmaf(dot8_fp4_f16(q.y, xs[1]), e4m3_byte<2>(sc.x), p);
+  p = fmaf(dot8_fp4_f16(q.z, xs[2]), e4m3_byte<0>(sc.y), p);
+  p = fmaf(dot8_fp4_f16(q.w, xs[3]), e4m3_byte<2>(sc.y), p);
   return p;
 }
 
