@@ -206,9 +206,8 @@ __device__ __forceinline__ float dot8_fp4_f16(uint32_t w, const Slice8& s) {
 // the bytes 0, 2, 4, 6 of `sc` (the piece's 8 scale bytes shifted so that
 // its own come first); products rounded once in fp32.  e4m3_f32 decodes
 // with integer operations (used at init); the dot products use gfx950's
-// fp8 conversion, which on this target decodes the OCP E4M3 format exactly
-// (every byte in every byte position compared on the device) in one
-// instruction with a byte select.
+// fp8 conversion, which on this target decodes the OCP E4M3 format exactly,
+// in one instruction with a byte select.
 __device__ __forceinline__ float e4m3_f32(uint32_t b) {
   const uint32_t em = b & 0x7Fu;
   const float mag = em >= 8u ? __uint_as_float((em + (120u << 3)) << 20) : (float)em * 0.001953125f;
