@@ -53,8 +53,10 @@ def lmhead_bytes(V, d, B):
     return V * d // 2 + V * (d // 32) * 2 + B * d * 2 + B * 8
 
 
-def time_graph(fn, steps, warmup, stream):
-    """Capture `fn(i)` for i in range(steps) into one graph; return seconds per replay."""
+def time_graph(fn, steps, warmup, stream, warm_s=0.0):
+    """Capture `fn(i)` for i in range(steps) into one graph; return seconds per replay.
+    warm_s: keep replaying for at least this long before timing (a leg that
+    follows seconds of host-side setup otherwise starts on an idle GPU)."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -68,6 +70,10 @@ def time_graph(fn, steps, warmup, stream):
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
+    t0 = time.time()
+    while time.time() - t0 < warm_s:
+        g.replay()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     reps = 3
@@ -505,7 +511,8 @@ def main():
         del XB4
 
     if "lmhead" in extras:
-        # LM head: rotate over 4 copies
+        # LM head: rotate over 4 copies; 0.1 s of replays before timing (the
+        # heads are generated on the host first, leaving the GPU idle)
         V = synth.LMHEAD1.V
         heads = []
         for c in range(4):
@@ -526,7 +533,7 @@ def main():
 
             n = 40
             try:
-                ls, _g = time_graph(lm_step, n, 4, stream)
+                ls, _g = time_graph(lm_step, n, 4, stream, warm_s=0.1)
                 del _g
             except Exception as e:
                 log(f"lmhead graph failed: {e!r}")
