@@ -163,8 +163,9 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
 moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* weights,
                            void* workspace, size_t workspace_bytes, moe_handle* out);
 
-/* One decode step of T tokens through the layer ("a small router selects
- * [some] of them per token", transcript 02:35):
+/* One decode step of T tokens through the layer (per token a router picks a
+ * few of the routed experts and only those run, "Flint 40B: Best Mid Sized
+ * LLM", transcript 02:35):
  *   logits = W_r x_t + b;  p = softmax(logits) over all E experts;
  *   S = the k largest p (larger first, lower expert index on ties);
  *   w_j = p_j / sum_{i in S} p_i (norm_topk) or p_j;
@@ -176,7 +177,20 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
  *   y         (device) fp32 [T][d], overwritten
  *   topk_idx  (device) int32 [T][k], chosen experts in the order above, or NULL
  *   topk_w    (device) fp32 [T][k], their weights, or NULL (routed experts
- *             only: the shared expert's weight is always 1) */
+ *             only: the shared expert's weight is always 1)
+ * T = 1 on a shape the single-launch kernel is built for ((d, f) = (256,
+ * 128) or (2048, 512), E <= 256, k + n_shared <= 16) runs as one launch of
+ * one workgroup per compute unit that hands data between its phases through
+ * memory; it needs all of its workgroups resident at once.  Its waits are
+ * bounded: if other work on the GPU keeps some workgroups from starting
+ * until a wait gives up, the call still ends but its outputs are not valid,
+ * and moe_decode_error_flags reports it.
+ * Intermediate precision: the router, gate/up and down sums accumulate in
+ * fp32; the SwiGLU activations h = w_j silu(g) u reach the down projection
+ * in binary16 (relative rounding 2^-11), so |h| must stay below 65504 and
+ * values below 2^-14 of it keep fewer bits; the batched kernels (T > 1)
+ * also round each dequantized weight q*s and each activation to binary16
+ * (|x| < 65504; elements below 2^-14 lose low bits). */
 moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float* y,
                               int32_t* topk_idx, float* topk_w, void* stream);
 
@@ -184,6 +198,9 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
  * of unit weight (the attention blocks between MoE layers are not part of
  * this call):
  *   x_l = bf16_rne(r_l / sqrt(mean(r_l^2) + eps));  r_{l+1} = r_l + layer_l(x_l).
+ * Each layer runs as forward would run it for T tokens (one launch at T = 1
+ * where its shape allows, else the batched kernels), so layers of different
+ * shapes and max_tokens may be mixed.
  *   layers    L handles of equal d and top_k, each with its own workspace
  *   residual  (device) fp32 [T][d], r_0 in, r_L out
  *   x_trace   (device) bf16 [L][T][d] receiving every x_l, or NULL
@@ -209,6 +226,23 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
  * chosen expert's weights once for all its tokens in this order. */
 moe_status moe_decode_expert_groups(moe_handle h, int32_t T, int32_t* offsets, int32_t* assignments,
                                     int32_t* active, int32_t* n_active, void* stream);
+
+/* Flags the layer's single-launch kernel raised since they were last
+ * cleared: bit 0, a wait for the other workgroups' router logits gave up;
+ * bit 1, a wait for the SwiGLU activations gave up.  Either means that the
+ * call's outputs are not valid (see moe_decode_forward).  Enqueues on
+ * `stream` a copy of the flags to `flags` (device uint32 [1], or NULL) and,
+ * when clear != 0, resets them, so the copy is ordered after every call
+ * enqueued before it on that stream. */
+moe_status moe_decode_error_flags(moe_handle h, uint32_t* flags, int32_t clear, void* stream);
+
+/* Diagnostic setting of the single-launch kernel's bounded waits, for tests
+ * of the error path: each wait gives up after `polls` rounds (>= 1; the
+ * default, restored by passing 1u << 21, is about 2 s), and with
+ * unreachable = 1 every wait looks for a tag no workgroup writes, so every
+ * wait gives up and the call ends with both flags set.  Host-side only; it
+ * applies to calls enqueued afterwards. */
+moe_status moe_decode_set_wait_limit(moe_handle h, uint32_t polls, int32_t unreachable);
 
 /* Free the host handle (no device memory is touched). NULL is ignored. */
 void moe_decode_destroy(moe_handle h);

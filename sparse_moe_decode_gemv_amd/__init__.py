@@ -35,8 +35,9 @@ WEIGHTS_NVFP4 = 2   # FP4 E2M1 codes, E4M3 scale bytes per 16, fp32 scale per ma
 EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
     "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
-    "moe_decode_abi_version",
+    "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit",
 )
+DEFAULT_WAIT_POLLS = 1 << 21
 
 
 class MoEError(RuntimeError):
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.argtypes = [i32]
         L.moe_decode_abi_version.restype = i32
         L.moe_decode_abi_version.argtypes = []
+        L.moe_decode_error_flags.restype = i32
+        L.moe_decode_error_flags.argtypes = [p, p, i32, p]
+        L.moe_decode_set_wait_limit.restype = i32
+        L.moe_decode_set_wait_limit.argtypes = [p, ctypes.c_uint32, i32]
         _lib = L
     return _lib
 
@@ -156,6 +161,14 @@ def moe_decode_expert_groups(handle: int, T: int, offsets=None, assignments=None
                              stream=None) -> None:
     _check(lib().moe_decode_expert_groups(handle, T, _ptr(offsets), _ptr(assignments), _ptr(active),
                                           _ptr(n_active), _stream(stream)), "moe_decode_expert_groups")
+
+
+def moe_decode_error_flags(handle: int, flags=None, clear: int = 1, stream=None) -> None:
+    _check(lib().moe_decode_error_flags(handle, _ptr(flags), int(clear), _stream(stream)), "moe_decode_error_flags")
+
+
+def moe_decode_set_wait_limit(handle: int, polls: int, unreachable: int = 0) -> None:
+    _check(lib().moe_decode_set_wait_limit(handle, int(polls), int(unreachable)), "moe_decode_set_wait_limit")
 
 
 def moe_decode_destroy(handle: int) -> None:
@@ -222,6 +235,15 @@ class MoELayer:
             y = torch.empty((T, self.d), dtype=torch.float32, device=dev)
         moe_decode_forward(self.handle, x, T, y, topk_idx, topk_w, stream)
         return y
+
+    def error_flags(self, clear: bool = True, stream=None) -> int:
+        """The single-launch kernel's error flags (0 when every wait
+        completed); synchronizes the stream."""
+        import torch
+        out = torch.full((1,), -1, dtype=torch.int32, device=self.workspace.device)
+        moe_decode_error_flags(self.handle, out, 1 if clear else 0, stream)
+        torch.cuda.current_stream().synchronize() if stream is None else torch.cuda.synchronize()
+        return int(out.item())
 
     def close(self) -> None:
         if self.handle:

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
@@ -104,6 +104,8 @@ struct moe_layer {
   void* workspace;
   float* resid_tmp;  // [max_tokens][d]: the other residual buffer when this layer leads a stack
   bool fused;        // the 1-token step runs as one launch
+  unsigned spin_limit = moe::kSpinLimit;  // polls of the single-launch kernel's bounded waits
+  unsigned tag_skew = 0;                  // 1: the waits look for a tag nobody writes (error-path tests)
 };
 
 namespace {
@@ -119,9 +121,17 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
   f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
   f.fmt = a.fmt;
+  f.spin_limit = h->spin_limit, f.tag_skew = h->tag_skew;
   f.gate_tscale = a.gate_tscale, f.up_tscale = a.up_tscale, f.down_tscale = a.down_tscale;
   f.sh_gate_tscale = a.sh_gate_tscale, f.sh_up_tscale = a.sh_up_tscale, f.sh_down_tscale = a.sh_down_tscale;
   return f;
+}
+
+// The error word of a layer: copied to `out` and, with clear, reset (one
+// thread; device atomics, so it is ordered with the kernels on the stream).
+__global__ void k_take_flags(unsigned* err, uint32_t* out, int clear) {
+  const unsigned v = clear ? atomicExch(err, 0u) : __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (out) *out = v;
 }
 
 }  // namespace
@@ -298,37 +308,56 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
     return MOE_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t d = (size_t)layers[0]->desc.d, k = (size_t)layers[0]->desc.top_k;
-  bool fused = T == 1;
-  for (int l = 0; l < L; ++l) fused = fused && layers[l]->fused;
-  if (fused) {
-    // One launch per layer.  The residual alternates between the caller's
-    // buffer and the first layer's spare one, arranged so that r_L lands in
-    // the caller's buffer, except for odd L, which ends with one copy.
-    float* buf[2] = {residual, layers[0]->resid_tmp};
-    for (int l = 0; l < L; ++l) {
-      moe::FusedArgs f = fused_args(layers[l]);
-      f.resid_in = buf[l & 1];
-      f.resid_out = buf[(l + 1) & 1];
-      f.eps = eps;
-      f.y = y_trace ? y_trace + (size_t)l * d : nullptr;
-      f.x_trace = x_trace ? x_trace + (size_t)l * d : nullptr;
-      f.idx_out = idx_trace ? idx_trace + (size_t)l * k : nullptr;
-      if (moe::launch_layer_fused(f, layers[l]->args.d, layers[l]->args.f, s) != hipSuccess) return MOE_ERR_HIP;
-    }
-    if ((L & 1) && hipMemcpyAsync(residual, buf[1], d * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return MOE_ERR_HIP;
-    return MOE_OK;
-  }
+  // Each layer runs as one launch when T = 1 and its shape has the
+  // single-launch kernel, else through the batched kernels (which every
+  // such layer can run: init gave it the tile-major copies).  The
+  // single-launch kernel reads the residual from one buffer and writes
+  // r + y to the other (the caller's buffer and the first layer's spare
+  // one, alternately); the batched kernels add y in place.  r_L ends in the
+  // caller's buffer, with one copy when it ends in the spare one.
+  float* buf[2] = {residual, layers[0]->resid_tmp};
+  int cur = 0;
   for (int l = 0; l < L; ++l) {
-    const moe::LayerArgs& a = layers[l]->args;
+    const moe_layer* h = layers[l];
+    const moe::LayerArgs& a = h->args;
     uint16_t* xt = x_trace ? x_trace + (size_t)l * T * d : nullptr;
     int32_t* it = idx_trace ? idx_trace + (size_t)l * T * k : nullptr;
     float* yt = y_trace ? y_trace + (size_t)l * T * d : nullptr;
-    if (moe::launch_router(a, nullptr, residual, eps, T, it, nullptr, xt, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_gateup(a, T, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_down(a, T, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_combine(a, T, yt, residual, s) != hipSuccess) return MOE_ERR_HIP;
+    if (T == 1 && h->fused) {
+      moe::FusedArgs f = fused_args(h);
+      f.resid_in = buf[cur];
+      f.resid_out = buf[cur ^ 1];
+      f.eps = eps;
+      f.y = yt, f.x_trace = xt, f.idx_out = it;
+      if (moe::launch_layer_fused(f, a.d, a.f, s) != hipSuccess) return MOE_ERR_HIP;
+      cur ^= 1;
+    } else {
+      if (!a.gate_t || !a.router_t) return MOE_ERR_UNSUPPORTED;  // unreachable: init guarantees the copies
+      float* r = buf[cur];
+      if (moe::launch_router(a, nullptr, r, eps, T, it, nullptr, xt, s) != hipSuccess) return MOE_ERR_HIP;
+      if (moe::launch_gateup(a, T, s) != hipSuccess) return MOE_ERR_HIP;
+      if (moe::launch_down(a, T, s) != hipSuccess) return MOE_ERR_HIP;
+      if (moe::launch_combine(a, T, yt, r, s) != hipSuccess) return MOE_ERR_HIP;
+    }
   }
+  if (cur && hipMemcpyAsync(residual, buf[1], (size_t)T * d * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_decode_error_flags(moe_handle h, uint32_t* flags, int32_t clear, void* stream) {
+  if (!h) return MOE_ERR_NULL;
+  if (flags && !aligned4(flags)) return MOE_ERR_ALIGN;
+  hipLaunchKernelGGL(k_take_flags, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), h->args.error, flags,
+                     clear ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_decode_set_wait_limit(moe_handle h, uint32_t polls, int32_t unreachable) {
+  if (!h) return MOE_ERR_NULL;
+  if (polls < 1 || (unreachable != 0 && unreachable != 1)) return MOE_ERR_SHAPE;
+  h->spin_limit = polls;
+  h->tag_skew = (unsigned)unreachable;
   return MOE_OK;
 }
 

@@ -112,7 +112,11 @@ struct FusedArgs {
   const float* sh_down_tscale;
   int E, k, norm, ns;
   int fmt;  // expert weights: 0 int4, 1 MXFP4 (E8M0 bytes per 32), 2 NVFP4 (E4M3 bytes per 16 + gate_ts ...)
+  unsigned spin_limit;  // polls of a bounded wait before it gives up (>= 1)
+  unsigned tag_skew;    // 0; 1 makes every wait look for a tag no workgroup writes (tests of the error path)
 };
+
+constexpr unsigned kSpinLimit = 1u << 21;  // default polls of a bounded wait (about 2 s)
 
 // The whole 1-token step in one launch, for the shapes it is built for
 // (d, f) in {(256, 128), (2048, 512)}, E <= 256; ns shared experts take

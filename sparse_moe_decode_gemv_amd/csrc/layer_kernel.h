@@ -19,9 +19,10 @@
 //            128-byte line (one writer per line: words from different XCDs
 //            sharing a line serialize at the memory side);
 //   select   wave 0 of every workgroup polls the tagged logits until all
-//            carry this call's tag; every wave then runs the exact top-k
-//            itself (lists of the largest keys merged across lanes in
-//            registers, no serial rounds) and issues its gate/up loads;
+//            carry this call's tag; the workgroup's threads then key one
+//            expert each and sort the 16 largest keys across lanes and
+//            waves (topk.h, block_top16), so every wave knows the chosen
+//            experts and issues its gate/up loads;
 //   experts  the workgroup turns its 16 values h = w_j * silu(g) * u into
 //            two ready-made fp16 dot slices and writes every slice word with
 //            the tag, then prefetches its down pieces;
@@ -38,7 +39,11 @@
 // The tag is this workgroup's call count + 1, kept per workgroup in the
 // workspace; all workgroups take part in every call, so their counts agree
 // and consecutive calls never accept each other's words.  Every wait is
-// bounded: on timeout the kernel sets the error word and finishes anyway.
+// bounded (a.spin_limit polls): on timeout the kernel sets a bit of the
+// error word, which the host reads through the library's error-flag call,
+// and finishes anyway.  The waits assume that all G workgroups are resident
+// at once (one per CU); if other work keeps some from starting, the waits
+// time out instead of hanging.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,7 +55,6 @@
 
 namespace moe {
 
-constexpr unsigned kSpinLimit = 1u << 21;
 // Logits are published one 128-byte line per workgroup: words written by
 // workgroups on different XCDs into one line serialize at the memory side
 // (measured: all-to-all detection 2.2 us packed vs 1.3 us one line each).
@@ -66,7 +70,7 @@ __device__ __forceinline__ void store_tagged(unsigned long long* p, float v, uns
 // receives them (NaN mapped to -inf, entries past E to -inf).
 template <int EPL>
 __device__ void poll_logits(const unsigned long long* lg, int E, unsigned tag, int lane, float v[EPL],
-                            unsigned* error) {
+                            unsigned* error, unsigned spin_limit) {
   for (unsigned spin = 0;; ++spin) {
     unsigned long long t[EPL];
 #pragma unroll
@@ -83,7 +87,7 @@ __device__ void poll_logits(const unsigned long long* lg, int E, unsigned tag, i
       ok = ok & (!valid | ((uint32_t)(t[i] >> 32) == tag));
     }
     if (__builtin_amdgcn_ballot_w64(!ok) == 0) return;
-    if (spin > kSpinLimit) {
+    if (spin + 1 >= spin_limit) {
       if (lane == 0) atomicOr(error, 1u);
       return;
     }
@@ -124,6 +128,8 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   __shared__ float s_part[4];
   __shared__ float s_hv[ROWS_G];
   __shared__ float s_lg[64 * EPL];
+  __shared__ uint32_t s_top[64];
+  __shared__ float s_z[4];
   __shared__ unsigned s_pub[ROWS_G / 8 * 5];
 
   __shared__ __align__(16) uint16_t s_x[D];
@@ -284,38 +290,66 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   // are in flight (they are needed only at the end of gate/up).
   if (wid == 0) {
     float v0[EPL];
-    poll_logits<EPL>(a.logits, E, tag, lane, v0, a.error);
+    poll_logits<EPL>(a.logits, E, tag + a.tag_skew, lane, v0, a.error, a.spin_limit);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) s_lg[lane + 64 * i] = v0[i];
   }
   __syncthreads();
-  float v[EPL];
+  int se = 0;     // lanes 0..k-1: the chosen experts, larger logit first
+  float sw = 0.f; // their weights
+  const int gsl = __builtin_amdgcn_readfirstlane(max(gslot, 0));  // this wave's slot (uniform)
+  bool fast = false;
+  if (k < 16) {
+    // every thread keys its expert; the 16 largest keys reach every wave
+    const int ib = E <= 2 ? 1 : 32 - __clz(E - 1);
+    const uint32_t imask = (1u << ib) - 1u;
+    const int t = threadIdx.x;
+    const float lt = t < E ? s_lg[t] : -INFINITY;
+    const uint32_t key = t < E ? ((ordered_bits(lt) & ~imask) | (imask - (uint32_t)t)) : 0u;
+    const uint32_t top = block_top16(key, lane, wid, s_top);
+    // two of the k + 1 largest keys that agree above the index bits may be
+    // out of order: then the exact selection below decides
+    const uint32_t prev = dpp_u<kDppShr1>(top);
+    fast = __builtin_amdgcn_ballot_w64(lane >= 1 && lane <= k && ((prev ^ top) & ~imask) == 0u) == 0ull;
+    if (fast) {
+      se = lane < k ? (int)(imask - (top & imask)) : 0;
+      if (has_gate && !shared_slot) load_gate(__builtin_amdgcn_readlane(se, gsl));
+      // weights while the loads fly: lane 0 holds the largest logit
+      const float l = s_lg[se];
+      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 0));
+      const float pe = lane < k ? expf(l - m) : 0.f;
+      float den;
+      if (a.norm) {
+        den = seg_sum<16>(pe);  // lanes 0..15 (k <= 15)
+      } else {  // the softmax's sum over all E experts
+        const float z = wave_sum(t < E ? expf(lt - m) : 0.f);
+        if (lane == 0) s_z[wid] = z;
+        __syncthreads();
+        den = (s_z[0] + s_z[1]) + (s_z[2] + s_z[3]);
+      }
+      sw = pe / den;
+    }
+  }
+  if (!fast) {
+    float v[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) v[i] = s_lg[lane + 64 * i];
-
-  int se = 0;
-  bool exact = false;
-  if (topk_select_merge<EPL, KP>(v, E, k, lane, se)) {
-    const int e_slot = __shfl(se, max(gslot, 0) & 63, 64);
-    if (has_gate && !shared_slot) load_gate(e_slot);
-  } else {  // picks that agree in their top bits: redo exactly
-    float sw;
-    topk_exact<EPL>(v, E, k, a.norm, lane, se, sw);
-    if (wid == 0 && lane < k) s_w[lane] = sw;
-    exact = true;
-    const int e_slot = __shfl(se, max(gslot, 0) & 63, 64);
-    if (has_gate && !shared_slot) load_gate(e_slot);
+    for (int i = 0; i < EPL; ++i) v[i] = s_lg[lane + 64 * i];
+    if (k < 16 || !topk_select_merge<EPL, KP>(v, E, k, lane, se)) {  // picks that agree in their top bits: redo exactly
+      topk_exact<EPL>(v, E, k, a.norm, lane, se, sw);
+      if (has_gate && !shared_slot) load_gate(__builtin_amdgcn_readlane(se, gsl));
+    } else {
+      if (has_gate && !shared_slot) load_gate(__builtin_amdgcn_readlane(se, gsl));
+      sw = topk_weight<EPL>(v, E, k, a.norm, lane, se);
+    }
   }
   if (wid == 0) {
-    if (lane < k) s_idx[lane] = se;
-    if (!exact) {
-      const float sw = topk_weight<EPL>(v, E, k, a.norm, lane, se);
-      if (lane < k) s_w[lane] = sw;
+    if (lane < k) {
+      s_idx[lane] = se;
+      s_w[lane] = sw;
     }
-    __builtin_amdgcn_wave_barrier();
     if (blockIdx.x == 0 && lane < k) {
       if (a.idx_out) a.idx_out[lane] = se;
-      if (a.w_out) a.w_out[lane] = s_w[lane];
+      if (a.w_out) a.w_out[lane] = sw;
     }
   }
   __syncthreads();
@@ -450,13 +484,13 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
         r[m] = (missing >> m) & 1u ? load_coherent(a.hrec + hrec_index(threadIdx.x + 256 * m, WPW, LPW)) : 0ull;
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
-        if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag) {
+        if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag + a.tag_skew) {
           s_sl[threadIdx.x + 256 * m] = (uint32_t)r[m];
           missing &= ~(1u << m);
         }
       }
       if (__syncthreads_or(missing != 0) == 0) break;
-      if (spin > kSpinLimit) {
+      if (spin + 1 >= a.spin_limit) {
         if (threadIdx.x == 0) atomicOr(a.error, 2u);
         break;
       }

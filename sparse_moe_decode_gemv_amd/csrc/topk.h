@@ -197,6 +197,88 @@ __device__ __forceinline__ bool topk_select_merge(const float v[EPL], int E, int
   return !close;
 }
 
+// ---------------------------------------------------------------- block top-k
+// The 256 threads of a workgroup hold one key each (expert e = thread,
+// E <= 256).  Each wave sorts the 16 largest of its 64 keys across its
+// lanes with a bitonic network (compare-exchange steps whose partner lane
+// is i ^ M, reached by DPP or a permlane swap), the four lists meet in LDS,
+// and two merge levels give every wave the 16 largest of all E, in lanes
+// 0..15, descending.  About 30 steps of 3-4 VALU instructions each, instead
+// of every wave merging lists of all 256 keys.
+
+enum : int { kDppRev4 = 0x1B, kDppShr1 = 0x111 };
+
+// The value of lane i ^ 16 (or i ^ 32): one of the pair a permlane swap
+// returns is this lane's own value, the other the partner's.
+__device__ __forceinline__ uint32_t partner16(uint32_t v) {
+  const u32x2_t p = swap16(v);
+  return p.x != v ? p.x : p.y;
+}
+__device__ __forceinline__ uint32_t partner32(uint32_t v) {
+  const u32x2_t p = swap32(v);
+  return p.x != v ? p.x : p.y;
+}
+// The value of lane i ^ M.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (M == 1) return dpp_u<kDppXor1>(v);
+  else if constexpr (M == 2) return dpp_u<kDppXor2>(v);
+  else if constexpr (M == 3) return dpp_u<kDppRev4>(v);
+  else if constexpr (M == 4) return dpp_u<kDppRev4>(dpp_u<kDppHalfMirror>(v));  // (i ^ 7) ^ 3
+  else if constexpr (M == 7) return dpp_u<kDppHalfMirror>(v);
+  else if constexpr (M == 8) return dpp_u<kDppHalfMirror>(dpp_u<kDppMirror>(v));  // (i ^ 15) ^ 7
+  else if constexpr (M == 15) return dpp_u<kDppMirror>(v);
+  else if constexpr (M == 31) return dpp_u<kDppMirror>(partner16(v));  // (i ^ 16) ^ 15
+  else {
+    static_assert(M == 47, "lane pattern");
+    return dpp_u<kDppMirror>(partner32(v));  // (i ^ 32) ^ 15
+  }
+}
+// Compare-exchange with lane i ^ M: the lane whose bit B is clear keeps the
+// larger key, the other the smaller.
+template <int M, int B>
+__device__ __forceinline__ uint32_t cx(uint32_t v, int lane) {
+  const uint32_t p = lane_xor<M>(v);
+  return (lane >> B) & 1 ? min(v, p) : max(v, p);
+}
+// Lanes 0..15 of every 32: the 16 largest keys of the two sorted 16-lane
+// groups 0..15 and 16..31 (M = 31, B = 4); or of lanes 0..15 and 32..47
+// (M = 47, B = 5).  Bitonic: mirror step, then half-cleaners.
+template <int M, int B>
+__device__ __forceinline__ uint32_t merge16(uint32_t v, int lane) {
+  v = cx<M, B>(v, lane);
+  v = cx<8, 3>(v, lane);
+  v = cx<4, 2>(v, lane);
+  v = cx<2, 1>(v, lane);
+  return cx<1, 0>(v, lane);
+}
+// key: this thread's key (0 for none).  s_top: 64 words of LDS.  Returns,
+// in every wave, the 16 largest keys of the workgroup in lanes 0..15
+// (descending; lanes 16..63 undefined).  Contains a barrier: every thread
+// of the workgroup must call it.
+__device__ __forceinline__ uint32_t block_top16(uint32_t key, int lane, int wid, uint32_t* s_top) {
+  uint32_t v = key;
+  // sorted runs of 2, 4, 8, 16 lanes
+  v = cx<1, 0>(v, lane);
+  v = cx<3, 1>(v, lane);
+  v = cx<1, 0>(v, lane);
+  v = cx<7, 2>(v, lane);
+  v = cx<2, 1>(v, lane);
+  v = cx<1, 0>(v, lane);
+  v = cx<15, 3>(v, lane);
+  v = cx<4, 2>(v, lane);
+  v = cx<2, 1>(v, lane);
+  v = cx<1, 0>(v, lane);
+  // the wave's 16 largest in lanes 0..15
+  v = merge16<31, 4>(v, lane);
+  v = merge16<47, 5>(v, lane);
+  if (lane < 16) s_top[16 * wid + lane] = v;
+  __syncthreads();
+  v = s_top[lane];  // the four waves' lists in lanes 0..15, 16..31, 32..47, 48..63
+  v = merge16<31, 4>(v, lane);
+  return merge16<47, 5>(v, lane);
+}
+
 // Faster selection with the same result as topk_exact (see above); k <= KP.
 template <int EPL, int KP>
 __device__ __forceinline__ void topk_fast(const float v[EPL], int E, int k, int norm, int lane, int& sel_e,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert L.moe_decode_abi_version() == 4
+    assert L.moe_decode_abi_version() == 5
 
 
 def test_status_strings():
@@ -117,6 +117,8 @@ def test_forward_and_stack_reject_null_handles():
     assert L.moe_decode_stack_forward(arr, 0, FAKE, 1, 1e-6, None, None, None, None) == M.MOE_ERR_SHAPE
     assert L.moe_decode_stack_forward(None, 1, FAKE, 1, 1e-6, None, None, None, None) == M.MOE_ERR_NULL
     assert L.moe_decode_expert_groups(None, 1, FAKE, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
+    assert L.moe_decode_error_flags(None, FAKE, 1, None) == M.MOE_ERR_NULL
+    assert L.moe_decode_set_wait_limit(None, 1, 0) == M.MOE_ERR_NULL
     M.moe_decode_destroy(None)  # ignored
 
 

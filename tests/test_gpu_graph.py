@@ -81,7 +81,9 @@ def test_headline_steps_in_a_graph():
         assert np.array_equal(np.sort(idx[i]), np.sort(out["idx"][0])), f"step {i}: experts"
         err = np.abs(y[i].astype(np.float64) - out["y"][0]).max()
         assert err <= Y_TOL * np.abs(out["y"][0]).max(), f"step {i}: y err {err:.3e}"
+    # every bounded wait of every replayed step completed
     for L in Ls:
+        assert L.error_flags() == 0
         L.close()
 
 

@@ -206,6 +206,46 @@ def test_stack_of_zero_experts_keeps_the_residual():
     assert all(np.all(y == 0) for y in out["ys"])
 
 
+def _one_entry_layer(gate, up, down):
+    """E = 1, d = f = 128, every weight 0 except gate/up entries (row, col,
+    code) with a binary16 scale of 1/8 on their group and down entries with
+    scale 1."""
+    d = f = 128
+    codes = {n: np.full(shape, 8) for n, shape in (("g", (f, d)), ("u", (f, d)), ("d", (d, f)))}
+    scales = {n: np.full((shape[0], shape[1] // 32), 0x3C00, np.uint16)
+              for n, shape in (("g", (f, d)), ("u", (f, d)), ("d", (d, f)))}
+    for n, ents, sc in (("g", gate, 0x3000), ("u", up, 0x3000), ("d", down, 0x3C00)):
+        for r, c, u in ents:
+            codes[n][r, c] = u
+            scales[n][r, c // 32] = sc
+    return M.Layer(np.ones((1, d), np.float32), None,
+                   F.pack_codes(codes["g"])[None], scales["g"][None], F.pack_codes(codes["u"])[None],
+                   scales["u"][None], F.pack_codes(codes["d"])[None], scales["d"][None])
+
+
+def test_stack_two_layers_hand_worked():
+    """The pre-norm residual stack of two one-expert layers against the
+    values worked by hand in golden/stack_two_layers.txt: the bf16 pre-norm
+    of every layer, each layer's output and the fp32 residual after both.
+    Feeding the un-normalized r_l to a layer, or adding y twice, fails it."""
+    g = {ln[0]: float(ln[1]) for ln in golden_lines("stack_two_layers.txt")}
+    k0 = int(g["k0"])
+    A = _one_entry_layer(gate=[(0, k0, 9)], up=[(0, k0, 9)], down=[(9, 0, 9)])
+    B = _one_entry_layer(gate=[(0, 9, 9)], up=[(0, k0, 9)], down=[(k0, 0, 7)])
+    x0 = np.zeros(128, np.uint16)
+    x0[k0] = 0x3F80  # bf16 1.0
+    out = M.stack_forward([A, B], x0, 1, 1e-6)
+    x1, x2 = F.bf16_to_f64(out["xs"][0]), F.bf16_to_f64(out["xs"][1])
+    assert x1[k0] == g["x1_k0"] and np.count_nonzero(x1) == 1
+    assert x2[k0] == g["x2_k0"] and x2[9] == g["x2_9"] and np.count_nonzero(x2) == 2
+    yA, yB = out["ys"]
+    assert yA.dtype == np.float32 and yA[9] == np.float32(g["yA_9"]) and np.count_nonzero(yA) == 1
+    assert yB[k0] == np.float32(g["yB_k0"]) and np.count_nonzero(yB) == 1
+    r = out["r"]
+    assert r.dtype == np.float32
+    assert r[k0] == np.float32(g["r2_k0"]) and r[9] == np.float32(g["r2_9"]) and np.count_nonzero(r) == 2
+
+
 def test_forward_on_given_set():
     """moe_forward_on_set: on the selected set it is moe_forward exactly; on
     any set of identical experts it reduces to one expert's output times the
