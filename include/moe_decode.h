@@ -272,6 +272,20 @@ moe_status lmhead_int4_argmax(const uint8_t* w_q, const uint16_t* w_s, int32_t V
                               const uint16_t* x, int32_t B, int32_t* token, float* max_logit,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same as lmhead_int4_argmax, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): no workspace argument.  The library keeps a fixed
+ * scratch array of 557,568 bytes on each GPU it runs on (the workspace of
+ * the largest B), held until the process ends; the first call on a device
+ * takes its address and enqueues a clear of its counters.  Calls with a
+ * shape whose workspace would exceed it return MOE_ERR_WORKSPACE (none of
+ * the shapes accepted above does).  All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race and must be serialized by the caller.  Nothing is allocated or
+ * freed, by the library or through any library it calls. */
+moe_status lmhead_int4_argmax_noalloc(const uint8_t* w_q, const uint16_t* w_s, int32_t V, int32_t d,
+                                      const uint16_t* x, int32_t B, int32_t* token, float* max_logit, void* stream);
+
 /* Text for a status code (static storage). */
 const char* moe_status_str(moe_status s);
 

@@ -35,7 +35,7 @@ WEIGHTS_NVFP4 = 2   # FP4 E2M1 codes, E4M3 scale bytes per 16, fp32 scale per ma
 EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
     "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
-    "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit",
+    "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit", "lmhead_int4_argmax_noalloc",
 )
 DEFAULT_WAIT_POLLS = 1 << 21
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.lmhead_int4_argmax_workspace_bytes.argtypes = [i32, i32, i32]
         L.lmhead_int4_argmax.restype = i32
         L.lmhead_int4_argmax.argtypes = [p, p, i32, i32, p, i32, p, p, p, sz, p]
+        L.lmhead_int4_argmax_noalloc.restype = i32
+        L.lmhead_int4_argmax_noalloc.argtypes = [p, p, i32, i32, p, i32, p, p, p]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_status_str.argtypes = [i32]
         L.moe_decode_abi_version.restype = i32
@@ -184,6 +186,11 @@ def lmhead_int4_argmax(w_q, w_s, V: int, d: int, x, B: int, token, max_logit, wo
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     _check(lib().lmhead_int4_argmax(_ptr(w_q), _ptr(w_s), V, d, _ptr(x), B, _ptr(token), _ptr(max_logit),
                                     _ptr(workspace), nbytes, _stream(stream)), "lmhead_int4_argmax")
+
+
+def lmhead_int4_argmax_noalloc(w_q, w_s, V: int, d: int, x, B: int, token, max_logit, stream=None) -> None:
+    _check(lib().lmhead_int4_argmax_noalloc(_ptr(w_q), _ptr(w_s), V, d, _ptr(x), B, _ptr(token), _ptr(max_logit),
+                                            _stream(stream)), "lmhead_int4_argmax_noalloc")
 
 
 # ------------------------------------------------------------ conveniences

@@ -383,4 +383,19 @@ moe_status lmhead_int4_argmax(const uint8_t* w_q, const uint16_t* w_s, int32_t V
   return MOE_OK;
 }
 
+moe_status lmhead_int4_argmax_noalloc(const uint8_t* w_q, const uint16_t* w_s, int32_t V, int32_t d,
+                                      const uint16_t* x, int32_t B, int32_t* token, float* max_logit, void* stream) {
+  if (!w_q || !w_s || !x || !token) return MOE_ERR_NULL;
+  if (V < 1 || V > (1 << 24) || B < 1 || B > MOE_LMHEAD_MAX_B || d < 1 || d % 32) return MOE_ERR_SHAPE;
+  if (!is_pow2(d) || d < 256 || d > 8192) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(w_q) || !aligned16(w_s) || !aligned16(x) || !aligned4(token) ||
+      (max_logit && !aligned4(max_logit)))
+    return MOE_ERR_ALIGN;
+  if (moe::lmhead_workspace_bytes(V, d, B) > moe::lmhead_scratch_bytes()) return MOE_ERR_WORKSPACE;
+  if (moe::launch_lmhead_noalloc(w_q, w_s, V, d, x, B, token, max_logit, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 }  // extern "C"

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -543,6 +545,56 @@ hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, co
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the workspace is a file-scope device array of fixed size, one copy
+// per GPU, held until the process ends.  Its address on each device is taken
+// once, with that device current, through hipGetSymbolAddress; host code
+// never passes the array's own name to a kernel (on the host it is only a
+// stand-in for the symbol).  The arrival counters must be zero when a call
+// starts: they are cleared by a fill kernel enqueued before the first call
+// on each device, and every call leaves them at zero again.  Calls on one
+// GPU share the array, so calls that overlap in time on one GPU race.
+constexpr size_t kLmScratchBytes = 2 * (kLmCtrBytes + (size_t)kLmMaxGrid * 8 * sizeof(unsigned long long));
+static __device__ __align__(256) unsigned char scratch[kLmScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device (set-up done)
+
+__global__ void k_clear_u32(unsigned* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+size_t lmhead_scratch_bytes() { return kLmScratchBytes; }
+
+hipError_t launch_lmhead_noalloc(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,
+                                 int32_t* token, float* max_logit, hipStream_t s) {
+  if (lmhead_workspace_bytes(V, d, B) > kLmScratchBytes) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev];
+    if (!ptr) {  // set-up on this device: its copy's address, counters cleared
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      for (size_t c = 0; c < 2; ++c) {
+        unsigned* ctr = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ptr) +
+                                                    c * (kLmScratchBytes / 2));
+        hipLaunchKernelGGL(k_clear_u32, dim3(16), dim3(256), 0, s, ctr, kLmCtrBytes / sizeof(unsigned));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      g_scratch_ptr[dev] = ptr;
+    }
+  }
+  return launch_lmhead(wq, ws, V, d, x, B, token, max_logit, ptr, s);
 }
 
 }  // namespace moe

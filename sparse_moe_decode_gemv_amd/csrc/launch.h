@@ -161,4 +161,10 @@ hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, co
 
 size_t lmhead_workspace_bytes(int V, int d, int B);
 
+// The LM head with the library's own per-device scratch array as workspace
+// (no allocation; calls overlapping on one GPU race); its size.
+hipError_t launch_lmhead_noalloc(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,
+                                 int32_t* token, float* max_logit, hipStream_t s);
+size_t lmhead_scratch_bytes();
+
 }  // namespace moe
