@@ -210,6 +210,28 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
                                     float eps, uint16_t* x_trace, float* y_trace, int32_t* idx_trace,
                                     void* stream);
 
+/* moe_decode_stack_forward with options.
+ *   flags  0: as moe_decode_stack_forward (one launch, or the batched
+ *          kernels, per layer);
+ *          MOE_STACK_PERSISTENT: at T = 1, a run of layers that all take the
+ *          single-launch kernel with the same shape (d, f, top_k, n_shared,
+ *          weight_format, and E in the same band: <= 64, <= 128 or <= 256)
+ *          runs as one persistent launch per 64 layers: every workgroup
+ *          steps through the layers in turn, each layer's output reaching
+ *          the next as tagged words in the workspace, and the next layer's
+ *          router rows loading while the current layer's SwiGLU activations
+ *          are exchanged (the pages' decode kernel fuses the whole pass into
+ *          one launch, "Flint 40B: Best Mid Sized LLM", transcript 06:43).
+ *          Layers it does not apply to run as without the flag.
+ * The result is the same either way, bit for bit.  (On MI355X the hand-off
+ * of the 8 KB residual between all workgroups costs about as much as the
+ * kernel boundary it replaces, so the persistent launch is not faster per
+ * layer; it takes one launch instead of L.) */
+#define MOE_STACK_PERSISTENT 1
+moe_status moe_decode_stack_forward_ex(const moe_handle* layers, int32_t L, float* residual, int32_t T,
+                                       float eps, uint16_t* x_trace, float* y_trace, int32_t* idx_trace,
+                                       int32_t flags, void* stream);
+
 /* The grouping of (token, slot) assignments to routed experts made by the handle's
  * last forward or stack call that ran the batched kernels (T > 1, or a
  * shape without the single-launch kernel).  Assignment a = t*k + j is
@@ -229,8 +251,9 @@ moe_status moe_decode_expert_groups(moe_handle h, int32_t T, int32_t* offsets, i
 
 /* Flags the layer's single-launch kernel raised since they were last
  * cleared: bit 0, a wait for the other workgroups' router logits gave up;
- * bit 1, a wait for the SwiGLU activations gave up.  Either means that the
- * call's outputs are not valid (see moe_decode_forward).  Enqueues on
+ * bit 1, a wait for the SwiGLU activations gave up; bit 2 (persistent
+ * stack), a wait for the previous layer's output gave up.  Any means that
+ * the call's outputs are not valid (see moe_decode_forward).  Enqueues on
  * `stream` a copy of the flags to `flags` (device uint32 [1], or NULL) and,
  * when clear != 0, resets them, so the copy is ordered after every call
  * enqueued before it on that stream. */

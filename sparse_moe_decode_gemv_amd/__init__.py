@@ -36,7 +36,9 @@ EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
     "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
     "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit", "lmhead_int4_argmax_noalloc",
+    "moe_decode_stack_forward_ex",
 )
+MOE_STACK_PERSISTENT = 1
 DEFAULT_WAIT_POLLS = 1 << 21
 
 
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_forward.argtypes = [p, p, i32, p, p, p, p]
         L.moe_decode_stack_forward.restype = i32
         L.moe_decode_stack_forward.argtypes = [ctypes.POINTER(p), i32, p, i32, f32, p, p, p, p]
+        L.moe_decode_stack_forward_ex.restype = i32
+        L.moe_decode_stack_forward_ex.argtypes = [ctypes.POINTER(p), i32, p, i32, f32, p, p, p, i32, p]
         L.moe_decode_expert_groups.restype = i32
         L.moe_decode_expert_groups.argtypes = [p, i32, p, p, p, p, p]
         L.moe_decode_destroy.restype = None
@@ -157,6 +161,14 @@ def moe_decode_stack_forward(handles, residual, T: int, eps: float, x_trace=None
     arr = (ctypes.c_void_p * len(handles))(*handles)
     _check(lib().moe_decode_stack_forward(arr, len(handles), _ptr(residual), T, eps, _ptr(x_trace), _ptr(y_trace),
                                           _ptr(idx_trace), _stream(stream)), "moe_decode_stack_forward")
+
+
+def moe_decode_stack_forward_ex(handles, residual, T: int, eps: float, x_trace=None, y_trace=None, idx_trace=None,
+                                flags: int = 0, stream=None) -> None:
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(lib().moe_decode_stack_forward_ex(arr, len(handles), _ptr(residual), T, eps, _ptr(x_trace), _ptr(y_trace),
+                                             _ptr(idx_trace), int(flags), _stream(stream)),
+           "moe_decode_stack_forward_ex")
 
 
 def moe_decode_expert_groups(handle: int, T: int, offsets=None, assignments=None, active=None, n_active=None,

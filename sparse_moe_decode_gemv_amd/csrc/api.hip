@@ -14,7 +14,8 @@ constexpr int kAbiVersion = 5;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
-      hrec, epoch, sort_wc, cleared;             // [0, cleared) is zeroed at init
+      hrec, epoch, sort_wc, rrec, cleared;       // [0, cleared) is zeroed at init
+  size_t args;                                           // the single-launch kernel's arguments (persistent stack)
   size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
   size_t router_t;                                       // bf16 terms of the router matrix (same)
   size_t total;
@@ -80,7 +81,9 @@ Layout layout_of(const moe_layer_desc* d) {
   L.hrec = o, o += align256((k + ns) * (size_t)(d->f / 8) * 5 * sizeof(unsigned long long) * 2);  // + line padding
   L.epoch = o, o += align256((size_t)(moe::kMaxFusedGrid + 1) * sizeof(unsigned));  // epochs, error
   L.sort_wc = o, o += align256(T > 1 ? (size_t)64 * E * sizeof(int32_t) : 0);      // per-wave counts of the wide sort
+  L.rrec = o, o += align256(16 * d_ + 1024);  // tagged residual words of the persistent stack, a line per workgroup
   L.cleared = o;
+  L.args = o, o += align256(sizeof(moe::FusedArgs));
   const bool copy = needs_tiled_copy(d);
   // scale copy: 2 bytes per 32 elements (int4, MXFP4 uses half), 4 for NVFP4 (fp16 per 16 elements)
   const size_t sb = d->weight_format == MOE_WEIGHTS_NVFP4 ? 4 : 2;
@@ -104,6 +107,8 @@ struct moe_layer {
   void* workspace;
   float* resid_tmp;  // [max_tokens][d]: the other residual buffer when this layer leads a stack
   bool fused;        // the 1-token step runs as one launch
+  unsigned long long* rrec;     // tagged residual words (persistent stack)
+  moe::FusedArgs* args_dev;     // device copy of this layer's single-launch arguments (persistent stack)
   unsigned spin_limit = moe::kSpinLimit;  // polls of the single-launch kernel's bounded waits
   unsigned tag_skew = 0;                  // 1: the waits look for a tag nobody writes (error-path tests)
 };
@@ -116,7 +121,7 @@ moe::FusedArgs fused_args(const moe_layer* h) {
   f.router_w = a.router_w, f.router_b = a.router_b;
   f.gate_q = a.gate_q, f.gate_s = a.gate_s, f.up_q = a.up_q, f.up_s = a.up_s;
   f.down_q = a.down_q, f.down_s = a.down_s;
-  f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error;
+  f.logits = a.tagged_logits, f.hrec = a.hrec, f.epoch = a.epoch, f.error = a.error, f.rrec = h->rrec;
   f.sh_gate_q = a.sh_gate_q, f.sh_gate_s = a.sh_gate_s, f.sh_up_q = a.sh_up_q, f.sh_up_s = a.sh_up_s;
   f.sh_down_q = a.sh_down_q, f.sh_down_s = a.sh_down_s;
   f.E = a.E, f.k = a.k, f.norm = a.norm_topk, f.ns = a.ns;
@@ -229,6 +234,8 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.hrec = reinterpret_cast<unsigned long long*>(base + L.hrec);
   a.epoch = reinterpret_cast<unsigned*>(base + L.epoch);
   a.error = a.epoch + moe::kMaxFusedGrid;
+  h->rrec = reinterpret_cast<unsigned long long*>(base + L.rrec);
+  h->args_dev = reinterpret_cast<moe::FusedArgs*>(base + L.args);
   const bool copy = needs_tiled_copy(desc);
   a.gate_t = copy ? base + L.gate_t : nullptr;
   a.gate_ts = copy ? reinterpret_cast<uint16_t*>(base + L.gate_ts) : nullptr;
@@ -247,6 +254,13 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
       hipDeviceSynchronize() != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
+  }
+  if (h->fused) {  // the arguments a persistent stack reads for this layer
+    const moe::FusedArgs f = fused_args(h);
+    if (hipMemcpy(h->args_dev, &f, sizeof(f), hipMemcpyHostToDevice) != hipSuccess) {
+      delete h;
+      return MOE_ERR_HIP;
+    }
   }
   *out = h;
   return MOE_OK;
@@ -294,9 +308,16 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
 
 moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* residual, int32_t T, float eps,
                                     uint16_t* x_trace, float* y_trace, int32_t* idx_trace, void* stream) {
+  return moe_decode_stack_forward_ex(layers, L, residual, T, eps, x_trace, y_trace, idx_trace, 0, stream);
+}
+
+moe_status moe_decode_stack_forward_ex(const moe_handle* layers, int32_t L, float* residual, int32_t T, float eps,
+                                       uint16_t* x_trace, float* y_trace, int32_t* idx_trace, int32_t flags,
+                                       void* stream) {
   if (!layers || !residual) return MOE_ERR_NULL;
   if (L < 1 || T < 1) return MOE_ERR_SHAPE;
   if (!(eps >= 0.f)) return MOE_ERR_SHAPE;
+  if (flags & ~MOE_STACK_PERSISTENT) return MOE_ERR_SHAPE;
   for (int l = 0; l < L; ++l) {
     if (!layers[l]) return MOE_ERR_NULL;
     if (layers[l]->desc.d != layers[0]->desc.d || layers[l]->desc.top_k != layers[0]->desc.top_k)
@@ -308,6 +329,35 @@ moe_status moe_decode_stack_forward(const moe_handle* layers, int32_t L, float* 
     return MOE_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t d = (size_t)layers[0]->desc.d, k = (size_t)layers[0]->desc.top_k;
+  // On request, one persistent launch for runs of up to kMaxStackLayers
+  // layers when T = 1 and every layer runs as one launch with the same shape
+  // (the kernel instance: d, f, k, shared expert, weight format, E in the
+  // same band).
+  auto band = [](int E) { return E <= 64 ? 0 : E <= 128 ? 1 : 2; };
+  bool persist = T == 1 && (flags & MOE_STACK_PERSISTENT);
+  for (int l = 0; l < L && persist; ++l) {
+    const moe_layer_desc &a = layers[l]->desc, &b = layers[0]->desc;
+    persist = layers[l]->fused && a.f == b.f && a.n_shared == b.n_shared && a.weight_format == b.weight_format &&
+              band(a.n_experts) == band(b.n_experts);
+  }
+  if (persist) {
+    for (int l0 = 0; l0 < L; l0 += moe::kMaxStackLayers) {
+      const int n = L - l0 < moe::kMaxStackLayers ? L - l0 : moe::kMaxStackLayers;
+      moe::StackArgs a{};
+      for (int i = 0; i < n; ++i) a.layer[i] = layers[l0 + i]->args_dev;
+      a.L = n, a.resid_in = residual, a.resid_out = residual, a.eps = eps;
+      a.x_trace = x_trace ? x_trace + (size_t)l0 * d : nullptr;
+      a.y_trace = y_trace ? y_trace + (size_t)l0 * d : nullptr;
+      a.idx_trace = idx_trace ? idx_trace + (size_t)l0 * k : nullptr;
+      a.spin_limit = layers[0]->spin_limit, a.tag_skew = layers[0]->tag_skew;
+      const moe_layer_desc& ds = layers[l0]->desc;
+      int E = 0;
+      for (int i = 0; i < n; ++i) E = layers[l0 + i]->desc.n_experts > E ? layers[l0 + i]->desc.n_experts : E;
+      const moe::StackShape sh{ds.d, ds.f, E, ds.top_k, ds.n_shared, ds.weight_format};
+      if (moe::launch_stack_fused(a, sh, s) != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
   // Each layer runs as one launch when T = 1 and its shape has the
   // single-launch kernel, else through the batched kernels (which every
   // such layer can run: init gave it the tile-major copies).  The

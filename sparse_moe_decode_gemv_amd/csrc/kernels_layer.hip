@@ -46,6 +46,18 @@ hipError_t launch_layer_int4(const FusedArgs& a, int d, int f, int G, hipStream_
   return launch_layer_format<0>(a, d, f, G, s);
 }
 
+hipError_t launch_stack_int4(const StackArgs& a, const StackShape& sh, int G, hipStream_t s) {
+  return launch_stack_format<0>(a, sh, G, s);
+}
+
+hipError_t launch_stack_fused(const StackArgs& a, const StackShape& sh, hipStream_t s) {
+  const int G = fused_grid();
+  if (G <= 0 || a.L < 1 || a.L > kMaxStackLayers || !fits(sh.d, sh.f, sh.E, sh.k + sh.ns, G)) return hipErrorInvalidValue;
+  if (sh.fmt == 2) return launch_stack_nvfp4(a, sh, G, s);
+  if (sh.fmt == 1) return launch_stack_mxfp4(a, sh, G, s);
+  return launch_stack_int4(a, sh, G, s);
+}
+
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s) {
   const int G = fused_grid();
   if (G <= 0 || !fits(d, f, a.E, a.k + a.ns, G)) return hipErrorInvalidValue;

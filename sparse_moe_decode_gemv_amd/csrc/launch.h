@@ -98,6 +98,7 @@ struct FusedArgs {
   unsigned long long* hrec;    // tagged fp16 slices of h
   unsigned* epoch;             // per-workgroup call counts
   unsigned* error;
+  unsigned long long* rrec;    // persistent stack: tagged r_l + y words for the next layer
   const uint8_t* sh_gate_q;    // the shared expert (ns = 1): slot k of the step, weight 1
   const uint16_t* sh_gate_s;
   const uint8_t* sh_up_q;
@@ -118,6 +119,26 @@ struct FusedArgs {
 
 constexpr unsigned kSpinLimit = 1u << 21;  // default polls of a bounded wait (about 2 s)
 
+// Arguments of the persistent stack kernel: up to kMaxStackLayers layers of
+// one shape per launch, each layer's FusedArgs read from the copy in its
+// workspace (its per-call fields unused).
+constexpr int kMaxStackLayers = 64;
+struct StackArgs {
+  const FusedArgs* layer[kMaxStackLayers];
+  int L;
+  const float* resid_in;   // r_0 [d]
+  float* resid_out;        // r_L [d] (may be resid_in)
+  float eps;
+  uint16_t* x_trace;       // [L][d] or NULL
+  float* y_trace;          // [L][d] or NULL
+  int32_t* idx_trace;      // [L][k] or NULL
+  unsigned spin_limit, tag_skew;
+};
+// The shape every layer of a persistent launch shares.
+struct StackShape {
+  int d, f, E, k, ns, fmt;
+};
+
 // The whole 1-token step in one launch, for the shapes it is built for
 // (d, f) in {(256, 128), (2048, 512)}, E <= 256; ns shared experts take
 // slots k .. k+ns-1.
@@ -128,6 +149,11 @@ hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s);
 hipError_t launch_layer_int4(const FusedArgs& a, int d, int f, int G, hipStream_t s);
 hipError_t launch_layer_mxfp4(const FusedArgs& a, int d, int f, int G, hipStream_t s);
 hipError_t launch_layer_nvfp4(const FusedArgs& a, int d, int f, int G, hipStream_t s);
+// The persistent stack kernel (grid G, the same as the single-launch kernel).
+hipError_t launch_stack_fused(const StackArgs& a, const StackShape& sh, hipStream_t s);
+hipError_t launch_stack_int4(const StackArgs& a, const StackShape& sh, int G, hipStream_t s);
+hipError_t launch_stack_mxfp4(const StackArgs& a, const StackShape& sh, int G, hipStream_t s);
+hipError_t launch_stack_nvfp4(const StackArgs& a, const StackShape& sh, int G, hipStream_t s);
 
 // Router logits of T tokens (a matrix product), then softmax + top-k of
 // every token and the assignments grouped by expert.  Activations come

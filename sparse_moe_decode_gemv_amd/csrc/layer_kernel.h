@@ -94,6 +94,39 @@ __device__ void poll_logits(const unsigned long long* lg, int E, unsigned tag, i
   }
 }
 
+// Where a step takes x from and puts its output: the caller's x and y
+// (kStepX); the residual r_l from memory, r_l + y written back (kStepNorm,
+// one layer of a stack per launch); or, in a persistent stack, r_l from the
+// previous layer's tagged words (from memory for the first layer) and
+// r_l + y published as tagged words for the next layer (to memory after
+// the last one) (kStepChain).
+enum : int { kStepX = 0, kStepNorm = 1, kStepChain = 2 };
+
+// The per-call inputs and outputs of one layer step.
+struct StepIO {
+  const uint16_t* x;              // kStepX: bf16 [D]
+  const float* resid_in;          // kStepNorm, first kStepChain layer: r_l [D]
+  const unsigned long long* rin;  // later kStepChain layers: the previous layer's tagged r words
+  unsigned rin_tag;               //   and their tag
+  float* resid_out;               // kStepNorm, last kStepChain layer: r_l + y [D]
+  unsigned long long* rout;       // other kStepChain layers: this layer's tagged r words
+  float eps;
+  uint16_t* x_trace;              // x_l [D] (stack), or NULL
+  float* y;                       // y [D] (kStepX), or a trace of it, or NULL
+  int32_t* idx_out;               // [k] or NULL
+  float* w_out;                   // [k] or NULL
+  unsigned spin_limit, tag_skew;
+  const float* next_router;       // kStepChain: the next layer's router matrix, or NULL
+  int next_E;
+};
+
+// Residual word of row `row`: rows_per_wg consecutive rows per producing
+// workgroup, in lines of their own.
+__device__ __forceinline__ size_t rrec_index(int row, int rows_per_wg) {
+  const int lpw = (rows_per_wg + 15) / 16;
+  return (size_t)(row / rows_per_wg) * lpw * 16 + (row % rows_per_wg);
+}
+
 // Slice word j (= 5 * slice + field, slices in h order) sits in the lines of
 // the workgroup that produced it: wpw words per workgroup, lpw lines each.
 __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
@@ -105,8 +138,9 @@ __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
 // experts per lane in the top-k wave; FMT: expert weights int4 with binary16
 // scales (0), MXFP4 (1: E2M1 codes, an E8M0 scale byte per 32) or NVFP4 (2:
 // E2M1 codes, an E4M3 scale byte per 16, an fp32 scale per matrix).
-template <int D, int F, int KP, int EPL, bool NORM, bool SH, int FMT>
-__global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
+template <int D, int F, int KP, int EPL, int MODE, bool SH, int FMT, class A>
+__device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, float4 (&w)[D / 256], bool w_ready) {
+  constexpr bool NORM = MODE != kStepX;  // x is the normalized residual
   constexpr bool FP4 = FMT != 0, NV = FMT == 2;
   constexpr int CPR = D / 32;        // 16-byte pieces per gate/up row
   constexpr int CPRF = F / 32;       // pieces per down row
@@ -120,6 +154,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   constexpr int ROWS_W = (NLD / LPRD) * RPLD;
   constexpr int NI = D / 256;        // router float4 per lane (one row per wave)
   constexpr int ROWS_G = 64 * NL / CPR * 4;  // gate/up rows per workgroup (C2: 16)
+  constexpr int RPG = 4 * ROWS_W;             // output rows per workgroup (C2: 8)
   static_assert(NL % LPRG == 0 && NI >= 1 && ROWS_G % 8 == 0, "shape");
 
   extern __shared__ unsigned s_sl[];  // k*F/8 slices x 5 words
@@ -133,6 +168,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   __shared__ unsigned s_pub[ROWS_G / 8 * 5];
 
   __shared__ __align__(16) uint16_t s_x[D];
+  __shared__ __align__(16) float s_r[NORM ? D : 4];  // the residual r_l (stack)
   __shared__ float s_ss[4];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -149,8 +185,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   // router row wg (one per wave): its weight loads go out first and stay in
   // flight while the activation is staged
   const bool router_row = blockIdx.x * 4 < E && wg < E;
-  float4 w[NI];
-  if (router_row) {
+  if (router_row && !w_ready) {
     const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)wg * D);
 #pragma unroll
     for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane];
@@ -227,17 +262,56 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     }
   if constexpr (!NORM) {
 #pragma unroll
-    for (int c = threadIdx.x; c < D / 8; c += 256) reinterpret_cast<uint4*>(s_x)[c] = reinterpret_cast<const uint4*>(a.x)[c];
+    for (int c = threadIdx.x; c < D / 8; c += 256) reinterpret_cast<uint4*>(s_x)[c] = reinterpret_cast<const uint4*>(io.x)[c];
     __syncthreads();
   } else {
     // x = bf16(r / sqrt(mean(r^2) + eps)), the same in every workgroup
     constexpr int NR = (D / 4 + 255) / 256;
     float4 rv[NR];
+#pragma unroll
+    for (int m = 0; m < NR; ++m) rv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (MODE == kStepNorm || !io.rin) {  // r from memory
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int c = threadIdx.x + 256 * m;
+        rv[m] = c < D / 4 ? reinterpret_cast<const float4*>(io.resid_in)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else {  // r from the previous layer's tagged words, each thread the 4 * NR it normalizes
+      unsigned missing = 0;
+#pragma unroll
+      for (int m = 0; m < NR; ++m) missing |= (threadIdx.x + 256 * m < D / 4 ? 0xFu : 0u) << (4 * m);
+      const unsigned want = io.rin_tag + io.tag_skew;
+      for (unsigned spin = 0;; ++spin) {
+        unsigned long long t[4 * NR];
+#pragma unroll
+        for (int i = 0; i < 4 * NR; ++i) {
+          const int e = 4 * (threadIdx.x + 256 * (i / 4)) + i % 4;
+          t[i] = (missing >> i) & 1u ? load_coherent(io.rin + rrec_index(min(e, D - 1), RPG)) : 0ull;
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * NR; ++i) {
+          if (((missing >> i) & 1u) && (uint32_t)(t[i] >> 32) == want) {
+            const float f = __uint_as_float((uint32_t)t[i]);
+            float4& r4 = rv[i / 4];
+            if (i % 4 == 0) r4.x = f;
+            else if (i % 4 == 1) r4.y = f;
+            else if (i % 4 == 2) r4.z = f;
+            else r4.w = f;
+            missing &= ~(1u << i);
+          }
+        }
+        if (__syncthreads_or(missing != 0) == 0) break;
+        if (spin + 1 >= io.spin_limit) {
+          if (threadIdx.x == 0) atomicOr(a.error, 4u);
+          break;
+        }
+      }
+    }
     float ss = 0.f;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
       const int c = threadIdx.x + 256 * m;
-      rv[m] = c < D / 4 ? reinterpret_cast<const float4*>(a.resid_in)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < D / 4) reinterpret_cast<float4*>(s_r)[c] = rv[m];
       ss = fmaf(rv[m].x, rv[m].x, ss);
       ss = fmaf(rv[m].y, rv[m].y, ss);
       ss = fmaf(rv[m].z, rv[m].z, ss);
@@ -246,14 +320,14 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     ss = wave_sum(ss);
     if (lane == 0) s_ss[wid] = ss;
     __syncthreads();
-    const float den = sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)D + a.eps);
+    const float den = sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)D + io.eps);
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
       const int c = threadIdx.x + 256 * m;
       if (c < D / 4) {
         const uint2 pk = make_uint2(pack_bf16(rv[m].x / den, rv[m].y / den), pack_bf16(rv[m].z / den, rv[m].w / den));
         reinterpret_cast<uint2*>(s_x)[c] = pk;
-        if (a.x_trace && blockIdx.x == 0) reinterpret_cast<uint2*>(a.x_trace)[c] = pk;
+        if (io.x_trace && blockIdx.x == 0) reinterpret_cast<uint2*>(io.x_trace)[c] = pk;
       }
     }
     __syncthreads();
@@ -290,7 +364,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
   // are in flight (they are needed only at the end of gate/up).
   if (wid == 0) {
     float v0[EPL];
-    poll_logits<EPL>(a.logits, E, tag + a.tag_skew, lane, v0, a.error, a.spin_limit);
+    poll_logits<EPL>(a.logits, E, tag + io.tag_skew, lane, v0, a.error, io.spin_limit);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) s_lg[lane + 64 * i] = v0[i];
   }
@@ -348,8 +422,8 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       s_w[lane] = sw;
     }
     if (blockIdx.x == 0 && lane < k) {
-      if (a.idx_out) a.idx_out[lane] = se;
-      if (a.w_out) a.w_out[lane] = sw;
+      if (io.idx_out) io.idx_out[lane] = se;
+      if (io.w_out) io.w_out[lane] = sw;
     }
   }
   __syncthreads();
@@ -451,7 +525,7 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     const bool writer = has_down && (P >= 64 ? lane == 0 : lane % P == 0) && n % LPRD == LPRD - 1;
     radd[n] = 0.f;
     if constexpr (NORM)
-      if (writer) radd[n] = a.resid_in[row];
+      if (writer) radd[n] = s_r[row];
   }
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
@@ -467,6 +541,15 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
       sd[n] = make_uint2(0, 0);
     }
   }
+
+  // the next layer's router rows (a persistent stack): loaded while this
+  // layer's h is exchanged, ready when its activation is
+  if constexpr (MODE == kStepChain)
+    if (io.next_router && blockIdx.x * 4 < io.next_E && wg < io.next_E) {
+      const float4* wr = reinterpret_cast<const float4*>(io.next_router + (size_t)wg * D);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane];
+    }
 
   // ---------------------------------------------------------------- collect h
   // all k*F/8 slices straight into LDS; a word is taken once it carries the
@@ -484,13 +567,13 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
         r[m] = (missing >> m) & 1u ? load_coherent(a.hrec + hrec_index(threadIdx.x + 256 * m, WPW, LPW)) : 0ull;
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
-        if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag + a.tag_skew) {
+        if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag + io.tag_skew) {
           s_sl[threadIdx.x + 256 * m] = (uint32_t)r[m];
           missing &= ~(1u << m);
         }
       }
       if (__syncthreads_or(missing != 0) == 0) break;
-      if (spin + 1 >= a.spin_limit) {
+      if (spin + 1 >= io.spin_limit) {
         if (threadIdx.x == 0) atomicOr(a.error, 2u);
         break;
       }
@@ -500,11 +583,15 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
 
   // ---------------------------------------------------------------- down + combine
   auto put_y = [&](int row, float v, float r) {
-    if constexpr (NORM) {
-      a.resid_out[row] = r + v;
-      if (a.y) a.y[row] = v;
+    if constexpr (MODE == kStepChain) {
+      if (io.y) io.y[row] = v;
+      if (io.rout) store_tagged(io.rout + rrec_index(row, RPG), r + v, tag);  // to every workgroup
+      else io.resid_out[row] = r + v;
+    } else if constexpr (NORM) {
+      io.resid_out[row] = r + v;
+      if (io.y) io.y[row] = v;
     } else {
-      a.y[row] = v;
+      io.y[row] = v;
     }
   };
   if (has_down) {
@@ -539,6 +626,54 @@ __global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
     }
   }
   if (threadIdx.x == 0) a.epoch[blockIdx.x] = tag;
+  return tag;
+}
+
+
+// One layer: x from the caller (NORM false) or the normalized residual of a
+// stack (NORM true), arguments in the kernel's own argument block.
+template <int D, int F, int KP, int EPL, bool NORM, bool SH, int FMT>
+__global__ __launch_bounds__(256) void k_layer(FusedArgs a) {
+  StepIO io{};
+  io.x = a.x, io.resid_in = a.resid_in, io.resid_out = a.resid_out, io.eps = a.eps;
+  io.x_trace = a.x_trace, io.y = a.y, io.idx_out = a.idx_out, io.w_out = a.w_out;
+  io.spin_limit = a.spin_limit, io.tag_skew = a.tag_skew;
+  float4 w[D / 256];
+  layer_step<D, F, KP, EPL, NORM ? kStepNorm : kStepX, SH, FMT>(a, io, w, false);
+}
+
+// A persistent stack: every workgroup runs the L layers in turn (the
+// single-launch analogue of the pages' decode mega-kernel, "Flint 40B: Best
+// Mid Sized LLM", transcript 06:43: no launch between layers, and the next
+// layer's router rows load while the current layer's h is exchanged).  The
+// residual crosses from layer to layer as tagged words in the producing
+// layer's workspace; each layer's arguments are read from the copy that
+// init wrote into its workspace.
+typedef const __attribute__((address_space(4))) FusedArgs ConstFusedArgs;
+
+template <int D, int F, int KP, int EPL, bool SH, int FMT>
+__global__ __launch_bounds__(256) void k_stack(StackArgs s) {
+  float4 w[D / 256];
+  unsigned tag = 0;
+  const unsigned long long* rin = nullptr;
+  for (int l = 0; l < s.L; ++l) {
+    ConstFusedArgs& a = *(ConstFusedArgs*)s.layer[l];
+    const bool last = l + 1 == s.L;
+    StepIO io{};
+    io.resid_in = s.resid_in, io.rin = rin, io.rin_tag = tag;
+    io.resid_out = s.resid_out, io.rout = last ? nullptr : a.rrec;
+    io.eps = s.eps;
+    io.x_trace = s.x_trace ? s.x_trace + (size_t)l * D : nullptr;
+    io.y = s.y_trace ? s.y_trace + (size_t)l * D : nullptr;
+    io.idx_out = s.idx_trace ? s.idx_trace + (size_t)l * a.k : nullptr;
+    io.spin_limit = s.spin_limit, io.tag_skew = s.tag_skew;
+    if (!last) {
+      ConstFusedArgs& n = *(ConstFusedArgs*)s.layer[l + 1];
+      io.next_router = n.router_w, io.next_E = n.E;
+    }
+    tag = layer_step<D, F, KP, EPL, kStepChain, SH, FMT>(a, io, w, l > 0);
+    rin = a.rrec;
+  }
 }
 
 // ---------------------------------------------------------------- launch chain (per format)
@@ -582,6 +717,42 @@ template <int FMT>
 static hipError_t launch_layer_format(const FusedArgs& a, int d, int f, int G, hipStream_t s) {
   if (d == 256 && f == 128) return layer_kp<FMT, 256, 128>(a, G, s);
   if (d == 2048 && f == 512) return layer_kp<FMT, 2048, 512>(a, G, s);
+  return hipErrorInvalidValue;
+}
+
+// The persistent stack kernel for the shape `sh` (all of the launch's
+// layers have it).
+template <int D, int F, int KP, int EPL, int FMT>
+static hipError_t stack_launch_fmt(const StackArgs& a, const StackShape& sh, int G, hipStream_t s) {
+  const size_t lds = (size_t)(sh.k + sh.ns) * (F / 8) * 5 * sizeof(unsigned);
+  if (sh.ns)
+    hipLaunchKernelGGL((k_stack<D, F, KP, EPL, true, FMT>), dim3(G), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_stack<D, F, KP, EPL, false, FMT>), dim3(G), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int D, int F, int KP>
+static hipError_t stack_epl(const StackArgs& a, const StackShape& sh, int G, hipStream_t s) {
+  if (sh.E <= 64) return stack_launch_fmt<D, F, KP, 1, FMT>(a, sh, G, s);
+  if (sh.E <= 128) return stack_launch_fmt<D, F, KP, 2, FMT>(a, sh, G, s);
+  return stack_launch_fmt<D, F, KP, 4, FMT>(a, sh, G, s);
+}
+
+template <int FMT, int D, int F>
+static hipError_t stack_kp(const StackArgs& a, const StackShape& sh, int G, hipStream_t s) {
+  const int k = sh.k + sh.ns;
+  if (k <= 1) return stack_epl<FMT, D, F, 1>(a, sh, G, s);
+  if (k <= 2) return stack_epl<FMT, D, F, 2>(a, sh, G, s);
+  if (k <= 4) return stack_epl<FMT, D, F, 4>(a, sh, G, s);
+  if (k <= 8) return stack_epl<FMT, D, F, 8>(a, sh, G, s);
+  return stack_epl<FMT, D, F, 16>(a, sh, G, s);
+}
+
+template <int FMT>
+static hipError_t launch_stack_format(const StackArgs& a, const StackShape& sh, int G, hipStream_t s) {
+  if (sh.d == 256 && sh.f == 128) return stack_kp<FMT, 256, 128>(a, sh, G, s);
+  if (sh.d == 2048 && sh.f == 512) return stack_kp<FMT, 2048, 512>(a, sh, G, s);
   return hipErrorInvalidValue;
 }
 
