@@ -7,11 +7,12 @@ one fp16 scale per 32, bf16 activations.  The pages give no layer shapes;
 these reproduce their totals (256 routed experts per layer, 40B total, 2.5B
 active, "Flint 40B: Best Mid Sized LLM", transcript 02:35).
 
-So that the 256 MB memory-side cache cannot serve repeats, step i runs layer
-i mod P of a pool of P = 49 independent seeded layers (22.3 GB of weights,
-the 49-layer stack's layers) with a fresh activation: every step reads its
-router and chosen experts from HBM.  Steps run in stream order, replayed as
-one HIP graph (the eager number is reported beside it).
+So that the 256 MB memory-side cache cannot serve repeats, steps rotate over
+a pool of P = 49 independent seeded layers (22.3 GB of weights, the 49-layer
+stack's layers) with a fresh activation, and every timed window of K steps
+(eager launches; window r starts at layer r*K mod P) follows a 1 GiB read:
+every step reads its router and chosen experts from HBM, whatever K is.  The same windows as one HIP-graph replay each are reported beside it
+(a replay carries a fixed cost of tens of microseconds).
 
 Also reported (not the headline): the 49-layer stack per-token time, the
 LM head (V=131072, d=2048) at B=1 and B=8, and the plain fp64 CPU oracle
@@ -170,24 +171,33 @@ def time_eager(fn, steps, warmup, stream):
     return start.elapsed_time(end) / 1e3
 
 
-def cpu_baseline(pool_np, xs_np, cfg, budget_s):
-    """The fp64 oracle as it stands, on a bounded sample of the same steps."""
-    from threadpoolctl import threadpool_info
+def cpu_baseline(pool_np, xs_np, cfg, steps_per_run, runs=5):
+    """The fp64 oracle as it stands, on a bounded sample of the same steps:
+    `runs` timed runs of `steps_per_run` single-token layer steps, once with
+    one BLAS thread and once with the default thread pool; medians."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import moe as OM
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        li = n % len(pool_np)
-        OM.moe_forward(OM.Layer.from_dict(pool_np[li]), xs_np[li][n % len(xs_np[li])], cfg.k)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+
+    def one_run():
+        t0 = time.perf_counter()
+        for n in range(steps_per_run):
+            li = n % len(pool_np)
+            OM.moe_forward(OM.Layer.from_dict(pool_np[li]), xs_np[li][n % len(xs_np[li])], cfg.k)
+        return time.perf_counter() - t0
+
+    one_run()  # first touch of the layers' pages
+    with threadpool_limits(1):
+        single = sorted(one_run() for _ in range(runs))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return dict(value=n / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{n} single-token layer steps over {min(n, len(pool_np))} layers of the pool, "
-                       f"{dt:.1f} s, numpy fp64 (BLAS threads {threads})")
+    multi = sorted(one_run() for _ in range(runs))
+    med1, medn = single[runs // 2], multi[runs // 2]
+    return dict(value=round(steps_per_run / medn, 3), unit="tokens/s", cores=threads, kind="oracle",
+                host_cores=os.cpu_count(),
+                single_thread={"value": round(steps_per_run / med1, 3), "unit": "tokens/s", "cores": 1},
+                sample=f"{runs} runs of {steps_per_run} single-token layer steps over {min(steps_per_run, len(pool_np))} "
+                       f"layers of the pool, median; numpy fp64 with {threads} BLAS threads (value) and with 1 "
+                       f"(single_thread); host cores {os.cpu_count()}")
 
 
 def main():
@@ -198,11 +208,11 @@ def main():
     ap.add_argument("--pool", type=int, default=49, help="distinct layers rotated through")
     ap.add_argument("--tokens", type=int, default=16, help="distinct activations per layer")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-steps", type=int, default=8, help="oracle steps per timed run (5 runs per thread setting)")
     ap.add_argument("--no-extras", action="store_true", help="skip stack, batch, LM head and CPU legs")
     ap.add_argument("--extras", default="stack,batch,prefill,flint,fp4,lmhead,cpu",
                     help="comma list of the legs run after the headline (stack, batch, prefill, flint, fp4, lmhead, cpu)")
-    ap.add_argument("--eager", action="store_true", help="headline from eager launches instead of a graph")
+    ap.add_argument("--windows", type=int, default=7, help="timed windows of K steps (median reported)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -251,21 +261,78 @@ def main():
 
     y = torch.empty((1, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
+    # Reading 1 GiB (four times the 256 MB memory-side cache) leaves it full
+    # of clean lines of another buffer; a write would leave dirty lines whose
+    # write-back the next steps would pay for.
+    flush = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    flush_sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def step(i):
-        l = i % P
-        t = (i // P) % args.tokens
-        M.moe_decode_forward(layers[l].handle, X[l, t:t + 1], 1, y, None, None, stream)
+    def mall_flush():
+        M.moe_decode_read_probe(flush, flush.numel(), flush_sink, stream)
 
+    def step_at(off):
+        def step(i):
+            j = off + i
+            l = j % P
+            t = (j // P) % args.tokens
+            M.moe_decode_forward(layers[l].handle, X[l, t:t + 1], 1, y, None, None, stream)
+        return step
+
+    step = step_at(0)
     K, W = args.steps, args.warmup
     eager_s = time_eager(step, K, W, stream)
-    graph_s = None
-    try:
-        graph_s, _g = time_graph(step, K, W, stream)
-        del _g
-    except Exception as e:  # graph capture unavailable: report eager only
+
+    # A GPU-side pause after the write, long enough for the host to enqueue
+    # a whole window (about 10 us of Python per launch), so that the timed
+    # region holds GPU time only: torch's spin kernel, its cycles calibrated
+    # against events once.
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(1 << 20)
+        e1.record(stream)
+    e1.synchronize()
+    cycles_per_us = (1 << 20) / max(e0.elapsed_time(e1) * 1e3, 1.0)
+
+    def windows(launch_window):
+        """Per-step times of args.windows timed windows of exactly K steps,
+        each after a 1 GiB read and a pause covering the host's enqueue;
+        window r starts at layer r*K mod P."""
+        out_us = []
+        for r in range(args.windows):
+            mall_flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(int(cycles_per_us * (200 + 25 * K)))
+                e0.record(stream)
+                launch_window(r)
+                e1.record(stream)
+            e1.synchronize()
+            out_us.append(e0.elapsed_time(e1) * 1e3 / K)
+        return out_us
+
+    win_us = windows(lambda r: [step_at(r * K)(i) for i in range(K)])
+    gwin_us = []
+    try:  # the same windows as K-node graph replays (one replay per window)
+        ng = max(1, min(4, (P + K - 1) // K))
+        graphs = []
+        for j in range(ng):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(K):
+                    step_at(j * K)(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        gwin_us = windows(lambda r: graphs[r % ng].replay())
+        del graphs
+    except Exception as e:  # graph capture unavailable
         log(f"graph capture failed: {e!r}")
-    total_s = eager_s if (args.eager or graph_s is None) else graph_s
+    win_s = sorted(win_us)[len(win_us) // 2] * K / 1e6
+    graph_s = sorted(gwin_us)[len(gwin_us) // 2] * K / 1e6 if gwin_us else None
+    total_s = win_s
     ms_per_step = total_s / K * 1e3
     value = K / total_s
 
@@ -282,6 +349,42 @@ def main():
     # around single launches add the markers' own cost; reported aside.
     kernel_us = step_us
     achieved = by["b_alg"] / (kernel_us * 1e-6) / 1e9
+
+    # Cold single calls: each after a 1 GiB write, so that neither the
+    # memory-side cache nor the L2 holds anything of the layer; events around
+    # one eager call, enqueued while the write runs.
+    cold = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold_us = []
+    for r in range(5):
+        with torch.cuda.stream(stream):
+            cold.fill_(r)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(7 * r + 3)
+            e1.record(stream)
+        e1.synchronize()
+        cold_us.append(e0.elapsed_time(e1) * 1e3)
+    cold_us.sort()
+    # Achievable read bandwidth: the library's plain streaming read of a
+    # 2 GiB buffer, after the 1 GiB write (so the memory-side cache holds
+    # none of it); median of 5.
+    probe = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe_us = []
+    for r in range(6):
+        with torch.cuda.stream(stream):
+            cold.fill_(r)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            M.moe_decode_read_probe(probe, probe.numel(), sink, stream)
+            e1.record(stream)
+        e1.synchronize()
+        if r:
+            probe_us.append(e0.elapsed_time(e1) * 1e3)
+    probe_us.sort()
+    achievable = probe.numel() / (probe_us[len(probe_us) // 2] * 1e-6) / 1e9
+    del probe, cold
+    wins = sorted(win_us) if win_us else [step_us]
     out = {
         "metric": "MoE-layer decode tokens/s at 1 token + achieved HBM GB/s (% of peak)",
         "value": round(value, 1),
@@ -298,21 +401,31 @@ def main():
         "config": {"workload": "1-token MoE layer decode, d=2048 f=512 E=256 top-8, "
                                f"rotating over {P} distinct layers, fresh x per step",
                    "d": d, "f": f, "experts": E, "top_k": k, "tokens_per_step": 1, "pool_layers": P,
-                   "launch": "eager" if total_s == eager_s else "hip-graph"},
+                   "launch": "eager launches, timed in windows of K steps after a 1 GiB read"},
         "roofline": {"bound": "hbm", "kernel": "k_layer (whole 1-token layer step, one launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic_from_profile(KERNEL_SOURCES, "traffic_k_layer_flagship.txt"),
                      "bytes_per_launch": by["b_alg"],
                      "launch_us": round(kernel_us, 3),
-                     "launch_timing": "HIP events around the timed region on the launch stream / steps "
-                                      "(one launch per step)",
-                     "event_pair_us": round(kt["mean_us"], 3) if kt else None},
+                     "launch_timing": "HIP events around each timed window of K steps on the launch stream / "
+                                      "K (one launch per step); median window",
+                     "achievable": round(achievable, 1),
+                     "frac_of_achievable": round(achieved / achievable, 4)},
+        "step_us": {"median": round(step_us, 3), "p10": round(wins[len(wins) // 10], 3),
+                    "p90": round(wins[(len(wins) * 9) // 10], 3), "windows": len(win_us),
+                    "over": "per-step time of each timed window of K steps (each after a 1 GiB read)"},
+        "launch_event_pairs_us": ({k2: round(v, 3) for k2, v in kt.items()} if kt else None),
+        "cold_call_us": {"median": round(cold_us[len(cold_us) // 2], 3), "min": round(cold_us[0], 3),
+                         "max": round(cold_us[-1], 3), "calls": len(cold_us),
+                         "over": "one eager call after a 1 GiB write, HIP events around it"},
+        "read_probe": {"gbs": round(achievable, 1), "bytes": 2 << 30, "frac_of_peak": round(achievable / PEAK_HBM_GBS, 4),
+                       "us": round(probe_us[len(probe_us) // 2], 2)},
         "bytes_per_step": by,
         "gbs_on_int4_weights": round(by["b_q"] / (step_us * 1e-6) / 1e9, 1),
         "frac_on_int4_weights": round(by["b_q"] / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "eager_ms_per_step": round(eager_s / K * 1e3, 6),
-        "graph_ms_per_step": round(graph_s / K * 1e3, 6) if graph_s else None,
+        "graph_window_ms_per_step": round(graph_s / K * 1e3, 6) if graph_s else None,
     }
 
     extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
@@ -324,21 +437,32 @@ def main():
         resid = torch.empty((1, d), dtype=torch.float32, device=dev)
         handles = [L.handle for L in layers]
 
-        def stack_step(i):
-            resid.copy_(base)
-            M.moe_decode_stack_forward(handles, resid, 1, 1e-6, None, None, None, stream)
+        def stack_time(flags):
+            def stack_step(i):
+                resid.copy_(base)
+                M.moe_decode_stack_forward_ex(handles, resid, 1, 1e-6, None, None, None, flags, stream)
 
-        st_s = time_eager(stack_step, 10, 2, stream) / 10
-        try:
-            gs, _g = time_graph(stack_step, 10, 2, stream)
-            st_s = gs / 10
-            del _g
-        except Exception as e:
-            log(f"stack graph failed: {e!r}")
+            st_s = time_eager(stack_step, 10, 2, stream) / 10
+            try:
+                gs, _g = time_graph(stack_step, 10, 2, stream)
+                st_s = gs / 10
+                del _g
+            except Exception as e:
+                log(f"stack graph failed: {e!r}")
+            return st_s
+
+        st_s = stack_time(0)
+        sp_s = stack_time(M.MOE_STACK_PERSISTENT)
         out["stack"] = {"layers": P, "ms_per_token": round(st_s * 1e3, 4),
                         "tokens_per_s": round(1 / st_s, 1),
                         "in_stack_layer_us": round(st_s / P * 1e6, 3),
-                        "achieved_gbs": round(P * by["b_alg"] / st_s / 1e9, 1)}
+                        "achieved_gbs": round(P * by["b_alg"] / st_s / 1e9, 1),
+                        "launch": "one launch per layer, graph"}
+        out["stack_persistent"] = {"layers": P, "ms_per_token": round(sp_s * 1e3, 4),
+                                   "tokens_per_s": round(1 / sp_s, 1),
+                                   "in_stack_layer_us": round(sp_s / P * 1e6, 3),
+                                   "achieved_gbs": round(P * by["b_alg"] / sp_s / 1e9, 1),
+                                   "launch": "one persistent launch for the 49 layers (MOE_STACK_PERSISTENT), graph"}
 
     if "batch" in extras:
         # batch: 64 tokens per call through one layer, Zipf(1.1) router bias
@@ -545,7 +669,7 @@ def main():
         del heads
 
     if "cpu" in extras:
-        out["cpu_baseline"] = cpu_baseline(pool_np, xs_np, cfg, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(pool_np, xs_np, cfg, args.cpu_steps)
 
     print(json.dumps(out), flush=True)
 

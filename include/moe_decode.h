@@ -267,6 +267,15 @@ moe_status moe_decode_error_flags(moe_handle h, uint32_t* flags, int32_t clear, 
  * applies to calls enqueued afterwards. */
 moe_status moe_decode_set_wait_limit(moe_handle h, uint32_t polls, int32_t unreachable);
 
+/* Diagnostic for measurements: reads `bytes` (a multiple of 16) from the
+ * device buffer `buf` with 16-byte loads spread over every compute unit
+ * (sixteen workgroups of 256 threads per CU, each reading a contiguous
+ * range, eight loads in flight per thread) and writes nothing but, in
+ * practice never, one word to `sink` (device uint32 [1]).  Timing it over a buffer larger than
+ * the memory-side cache gives the read bandwidth a plain streaming kernel
+ * achieves on this GPU, the "achievable" figure beside the 8 TB/s peak. */
+moe_status moe_decode_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Free the host handle (no device memory is touched). NULL is ignored. */
 void moe_decode_destroy(moe_handle h);
 
