@@ -81,7 +81,9 @@ typedef int32_t moe_status;
  *              MXFP4: one E8M0 scale byte 2^(b-127) per 32 elements (OCP MX
  *              v1.0; byte 255, NaN, is not supported; the batched kernels,
  *              which round each weight to fp16, are exact for bytes
- *              104..140).  NVFP4: one FP8 E4M3 scale byte per 16 elements
+ *              104..140: moe_decode_init scans the scale bytes and returns
+ *              MOE_ERR_UNSUPPORTED for a 255, or for a byte outside
+ *              104..140 in a layer that may run the batched kernels).  NVFP4: one FP8 E4M3 scale byte per 16 elements
  *              (OCP E4M3FN) and one fp32 scale per expert matrix
  *              (moe_layer_weights.*_tscale) */
 #define MOE_WEIGHTS_INT4 0
@@ -186,11 +188,15 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
  * until a wait gives up, the call still ends but its outputs are not valid,
  * and moe_decode_error_flags reports it.
  * Intermediate precision: the router, gate/up and down sums accumulate in
- * fp32; the SwiGLU activations h = w_j silu(g) u reach the down projection
- * in binary16 (relative rounding 2^-11), so |h| must stay below 65504 and
- * values below 2^-14 of it keep fewer bits; the batched kernels (T > 1)
- * also round each dequantized weight q*s and each activation to binary16
- * (|x| < 65504; elements below 2^-14 lose low bits). */
+ * fp32.  The SwiGLU activations reach the down projection in binary16
+ * (relative rounding 2^-11) as h 2^(2a), with 2^a the power of two that
+ * puts the token's largest |x| in [1, 2) and the output scaled back by
+ * 2^(-2a): exact scalings, so x of any magnitude works; what must stay
+ * below 65504 is w_j silu(g) u computed from x 2^a, which the weights
+ * bound (at most about 4 |W_g row|_1 |W_u row|_1), and elements of h 2^(2a)
+ * below 2^-14 keep fewer bits.  The batched kernels (T > 1) also round each
+ * dequantized weight q*s and each element of x 2^a to binary16 (elements
+ * below 2^-14 of the token's largest lose low bits). */
 moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float* y,
                               int32_t* topk_idx, float* topk_w, void* stream);
 
@@ -266,6 +272,15 @@ moe_status moe_decode_error_flags(moe_handle h, uint32_t* flags, int32_t clear, 
  * wait gives up and the call ends with both flags set.  Host-side only; it
  * applies to calls enqueued afterwards. */
 moe_status moe_decode_set_wait_limit(moe_handle h, uint32_t polls, int32_t unreachable);
+
+/* Repack int4 (or FP4) codes from the canonical order -- element k of a row
+ * in byte k/2, the low nibble for even k, rows of K/2 bytes one after
+ * another -- into the stored format above (the scales keep their layout).
+ * Enqueued on `stream`.
+ *   src, dst  (device) [rows][K/2] bytes each, 16-byte aligned, not
+ *             overlapping (MOE_ERR_SHAPE if they do)
+ *   rows      >= 1;  K  a multiple of 128 */
+moe_status moe_int4_repack(const uint8_t* src, uint8_t* dst, int64_t rows, int32_t K, void* stream);
 
 /* Diagnostic for measurements: reads `bytes` (a multiple of 16) from the
  * device buffer `buf` with 16-byte loads spread over every compute unit

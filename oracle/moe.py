@@ -139,9 +139,13 @@ def select_topk(p: np.ndarray, k: int) -> np.ndarray:
 
 
 def route(l: np.ndarray, k: int, norm_topk: bool = True):
-    """(chosen experts S, their weights w) from router logits."""
+    """(chosen experts S, their weights w) from router logits.  The softmax
+    is strictly increasing in the logit, so its k largest probabilities are
+    those of the k largest logits (ties alike): S is selected on l, which
+    stays exact where the fp64 probabilities of far smaller logits underflow
+    to 0 and would tie."""
     p = softmax(l)
-    S = select_topk(p, k)
+    S = select_topk(l, k)
     w = p[S] / p[S].sum() if norm_topk else p[S]
     return S, w
 
@@ -239,7 +243,7 @@ def moe_forward_dense_einsum(layer: Layer, x_bits: np.ndarray, k: int, norm_topk
     p = np.exp(l - l.max())
     p /= p.sum()
     # k-subset with the largest total logit, ties by the lexicographically smallest set
-    chosen = np.lexsort((np.arange(layer.E), -p))[:k]
+    chosen = np.lexsort((np.arange(layer.E), -l))[:k]
     wv = np.zeros(layer.E)
     wv[chosen] = p[chosen] / p[chosen].sum() if norm_topk else p[chosen]
     Wg = dequant_4bit(layer.gate_q, layer.gate_s, layer.d, layer._t("gate_ts"))

@@ -36,7 +36,7 @@ EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
     "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
     "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit", "lmhead_int4_argmax_noalloc",
-    "moe_decode_stack_forward_ex", "moe_decode_read_probe",
+    "moe_decode_stack_forward_ex", "moe_decode_read_probe", "moe_int4_repack",
 )
 MOE_STACK_PERSISTENT = 1
 DEFAULT_WAIT_POLLS = 1 << 21
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_stack_forward.argtypes = [ctypes.POINTER(p), i32, p, i32, f32, p, p, p, p]
         L.moe_decode_stack_forward_ex.restype = i32
         L.moe_decode_stack_forward_ex.argtypes = [ctypes.POINTER(p), i32, p, i32, f32, p, p, p, i32, p]
+        L.moe_int4_repack.restype = i32
+        L.moe_int4_repack.argtypes = [p, p, ctypes.c_int64, i32, p]
         L.moe_decode_read_probe.restype = i32
         L.moe_decode_read_probe.argtypes = [p, sz, p, p]
         L.moe_decode_expert_groups.restype = i32
@@ -171,6 +173,10 @@ def moe_decode_stack_forward_ex(handles, residual, T: int, eps: float, x_trace=N
     _check(lib().moe_decode_stack_forward_ex(arr, len(handles), _ptr(residual), T, eps, _ptr(x_trace), _ptr(y_trace),
                                              _ptr(idx_trace), int(flags), _stream(stream)),
            "moe_decode_stack_forward_ex")
+
+
+def moe_int4_repack(src, dst, rows: int, K: int, stream=None) -> None:
+    _check(lib().moe_int4_repack(_ptr(src), _ptr(dst), int(rows), int(K), _stream(stream)), "moe_int4_repack")
 
 
 def moe_decode_read_probe(buf, nbytes: int, sink, stream=None) -> None:

@@ -13,7 +13,7 @@ namespace {
 constexpr int kAbiVersion = 5;
 
 struct Layout {
-  size_t logits, sel_idx, sel_w, xp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
+  size_t logits, sel_idx, sel_w, xp, xexp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
       hrec, epoch, sort_wc, rrec, cleared;       // [0, cleared) is zeroed at init
   size_t args;                                           // the single-launch kernel's arguments (persistent stack)
   size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
@@ -68,6 +68,7 @@ Layout layout_of(const moe_layer_desc* d) {
   L.sel_idx = o, o += align256(Tk * sizeof(int32_t));
   L.sel_w = o, o += align256(Tk * sizeof(float));
   L.xp = o, o += align256(T * d_ * sizeof(uint16_t));
+  L.xexp = o, o += align256(T * sizeof(int32_t));
   L.xn = o, o += align256(T * d_ * sizeof(uint16_t));
   L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
   L.act = o, o += align256(E * sizeof(int32_t));
@@ -163,6 +164,34 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// MXFP4 scale bytes: bit 0 of *flags if any is 255 (NaN), bit 1 if any lies
+// outside [lo, hi].
+__global__ __launch_bounds__(256) void k_scan_e8m0(const uint8_t* __restrict__ p, size_t n, unsigned lo, unsigned hi,
+                                                   unsigned* flags) {
+  unsigned f = 0;
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const unsigned b = p[i];
+    f |= (b == 255u ? 1u : 0u) | (b < lo || b > hi ? 2u : 0u);
+  }
+  if (f) atomicOr(flags, f);
+}
+
+// Canonical int4 rows (element k in byte k/2, the low nibble for even k) to
+// the stored order: per 128-element block (64 bytes, 16 dwords of 8
+// consecutive elements), canonical dword 4j + q, the elements 32j + 8q ..
+// +7, goes to stored dword 4q + j (piece q, group j): a 4 x 4 transpose of
+// dwords.  One thread per block.
+__global__ __launch_bounds__(256) void k_repack_int4(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                     size_t blocks) {
+  const size_t b = blockIdx.x * (size_t)256 + threadIdx.x;
+  if (b >= blocks) return;
+  const uint4 c0 = src[4 * b], c1 = src[4 * b + 1], c2 = src[4 * b + 2], c3 = src[4 * b + 3];  // c_j = dwords 4j .. 4j+3
+  dst[4 * b] = make_uint4(c0.x, c1.x, c2.x, c3.x);
+  dst[4 * b + 1] = make_uint4(c0.y, c1.y, c2.y, c3.y);
+  dst[4 * b + 2] = make_uint4(c0.z, c1.z, c2.z, c3.z);
+  dst[4 * b + 3] = make_uint4(c0.w, c1.w, c2.w, c3.w);
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,6 +272,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
   a.sel_idx = reinterpret_cast<int32_t*>(base + L.sel_idx);
   a.sel_w = reinterpret_cast<float*>(base + L.sel_w);
   a.xp = reinterpret_cast<uint16_t*>(base + L.xp);
+  a.xexp = reinterpret_cast<int32_t*>(base + L.xexp);
   a.xn = reinterpret_cast<uint16_t*>(base + L.xn);
   a.sort_wc = reinterpret_cast<int32_t*>(base + L.sort_wc);
   a.off = reinterpret_cast<int32_t*>(base + L.off);
@@ -274,8 +304,36 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
     delete h;
     return MOE_ERR_UNSUPPORTED;
   }
-  if (hipMemset(workspace, 0, L.cleared) != hipSuccess || (copy && moe::launch_tile_weights(a, nullptr) != hipSuccess) ||
-      hipDeviceSynchronize() != hipSuccess) {
+  if (hipMemset(workspace, 0, L.cleared) != hipSuccess) {
+    delete h;
+    return MOE_ERR_HIP;
+  }
+  if (desc->weight_format == MOE_WEIGHTS_MXFP4) {
+    // E8M0 byte 255 (NaN) is not supported; the batched kernels round each
+    // weight to binary16 with the scale folded in, exact for bytes 104..140
+    const unsigned lo = copy ? 104u : 0u, hi = copy ? 140u : 254u;
+    const size_t per = (size_t)desc->f * (desc->d / 32);  // scale bytes per matrix (gate, up and down alike)
+    struct {
+      const void* p;
+      size_t n;
+    } sc[] = {{w->gate_s, per * desc->n_experts}, {w->up_s, per * desc->n_experts}, {w->down_s, per * desc->n_experts},
+              {desc->n_shared ? w->shared_gate_s : nullptr, per}, {desc->n_shared ? w->shared_up_s : nullptr, per},
+              {desc->n_shared ? w->shared_down_s : nullptr, per}};
+    for (const auto& c : sc)
+      if (c.p) hipLaunchKernelGGL(k_scan_e8m0, dim3(1024), dim3(256), 0, nullptr, static_cast<const uint8_t*>(c.p),
+                                  c.n, lo, hi, a.error);
+    unsigned flags = 0;
+    if (hipGetLastError() != hipSuccess || hipMemcpy(&flags, a.error, sizeof(flags), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemset(a.error, 0, sizeof(unsigned)) != hipSuccess) {
+      delete h;
+      return MOE_ERR_HIP;
+    }
+    if (flags) {
+      delete h;
+      return MOE_ERR_UNSUPPORTED;
+    }
+  }
+  if ((copy && moe::launch_tile_weights(a, nullptr) != hipSuccess) || hipDeviceSynchronize() != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
   }
@@ -424,6 +482,20 @@ moe_status moe_decode_error_flags(moe_handle h, uint32_t* flags, int32_t clear, 
   if (flags && !aligned4(flags)) return MOE_ERR_ALIGN;
   hipLaunchKernelGGL(k_take_flags, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), h->args.error, flags,
                      clear ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_int4_repack(const uint8_t* src, uint8_t* dst, int64_t rows, int32_t K, void* stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (rows < 1 || K < 128 || K % 128) return MOE_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  const size_t bytes = (size_t)rows * (K / 2);
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_SHAPE;  // overlapping
+  const size_t blocks = (size_t)rows * (K / 128);
+  hipLaunchKernelGGL(k_repack_int4, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst),
+                     blocks);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -370,6 +370,23 @@ __device__ __forceinline__ unsigned arrive(unsigned* counter) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Activation range.  Activations reach binary16 operands (the batched
+// kernels' x, and h on every path) scaled by a power of two: x 2^a with a
+// chosen from the row's largest magnitude, so that it lies in [1, 2).  Then
+// g and u carry 2^a, h = w silu(g) u is formed as 2^(2a) h, and the output
+// is scaled back by 2^(-2a); all scalings are exact, so any bf16 magnitude
+// works (h 2^(2a) is bounded by the weights alone).
+// The larger magnitude (bits, sign cleared) of a dword's two bf16 values.
+__device__ __forceinline__ uint32_t bf16_mag_max(uint32_t w) { return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu); }
+// a for a row whose largest magnitude has bf16 bits mb (sign cleared): 127
+// minus its biased exponent, within [-126, 126]; 0 for an all-zero row.
+__device__ __forceinline__ int act_exponent(uint32_t mb) {
+  if (mb == 0u) return 0;
+  return min(max(127 - (int)(mb >> 7), -126), 126);
+}
+// 2^a silu(g) from g (exact scaling of the quotient).
+__device__ __forceinline__ float silu_scaled(float g, int a) { return ldexpf(g, a) / (1.0f + expf(-g)); }
+
 // Byte offset, within its matrix, of the 16-byte piece c of row r.
 __device__ __forceinline__ size_t piece_offset(size_t row, int pieces_per_row, int c) {
   return (row * (size_t)pieces_per_row + (size_t)c) * 16u;

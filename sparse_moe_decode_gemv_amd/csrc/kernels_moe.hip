@@ -4,10 +4,12 @@
 // turns the residual into x):
 //   router  : logits = W_r x as a matrix product on the matrix cores (x
 //             against three exact bf16 terms of W_r), split over K into
-//             partial sums; the workgroups of expert tile 0 also write each
-//             token's activations in MFMA operand order (fp16).
+//             partial sums.
 //   top-k   : one wave per token: the partial sums and bias added in a
-//             fixed order, then softmax + top-k.
+//             fixed order, then softmax + top-k; the wave also writes the
+//             token's activations in MFMA operand order (fp16), scaled by
+//             the power of two 2^a_t that puts their largest magnitude in
+//             [1, 2), so any bf16 magnitude converts exactly.
 //   sort    : one workgroup of 16 waves: the T*k (token, slot) assignments
 //             grouped by expert (a stable counting sort built from wave
 //             ballots).
@@ -36,9 +38,10 @@
 // order e = 0,4,1,5,2,6,3,7 that the magic-number extraction yields (see
 // device_common.h); the activation operands are stored in that same order.
 // The MFMAs then accumulate over all of K in their C operand.  The
-// activations are fp16 here (finite bf16 activations below 65504 in
-// magnitude convert exactly, except that magnitudes under 2^-14 lose low
-// bits, an absolute error below 2^-25).
+// activations are fp16 here, as x_t 2^a_t (exact, except that elements
+// under 2^-14 of the row's largest lose low bits); gate and up then hold
+// 2^a_t g and 2^a_t u, SwiGLU stores h 2^(2 a_t) (silu of the true g), and
+// the combine scales the token's sum back by 2^(-2 a_t).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -54,6 +57,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------- top-k
 
+// One token's 8 activations of one chunk (bf16) times 2^ea as the fp16 MFMA
+// operand of the expert kernels, in the order (x0, x4, x1, x5, x2, x6, x3, x7).
+__device__ __forceinline__ uint4 operand_chunk(uint4 q, int ea) {
+  const float x0 = ldexpf(bf16_bits_to_f32(q.x & 0xFFFFu), ea), x1 = ldexpf(__uint_as_float(q.x & 0xFFFF0000u), ea);
+  const float x2 = ldexpf(bf16_bits_to_f32(q.y & 0xFFFFu), ea), x3 = ldexpf(__uint_as_float(q.y & 0xFFFF0000u), ea);
+  const float x4 = ldexpf(bf16_bits_to_f32(q.z & 0xFFFFu), ea), x5 = ldexpf(__uint_as_float(q.z & 0xFFFF0000u), ea);
+  const float x6 = ldexpf(bf16_bits_to_f32(q.w & 0xFFFFu), ea), x7 = ldexpf(__uint_as_float(q.w & 0xFFFF0000u), ea);
+  return make_uint4(pack_f16(x0, x4), pack_f16(x1, x5), pack_f16(x2, x6), pack_f16(x3, x7));
+}
+
+
 // This wave's LDS operations have completed (and act as a compiler barrier).
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -62,10 +76,18 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // VALU instruction takes 4 cycles, so waves sharing a SIMD would serialize).
 // The logits are the S partial sums of the router (slice order) plus the
 // bias.
-template <int EPL, int KP>
-__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int T, int S, int32_t* __restrict__ idx_out,
-                                             float* __restrict__ w_out) {
+template <int EPL, int KP, int D>
+__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, const uint16_t* __restrict__ x, int T, int S,
+                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   const int t = blockIdx.x, lane = threadIdx.x, E = a.E, k = a.k, E16 = (E + 15) & ~15;
+  // the token's activations, loaded first (they are written back below as
+  // the expert kernels' operand row)
+  constexpr int XC = D / 8 > 64 ? D / 8 / 64 : 1;  // 8-element chunks per lane
+  uint4 xc[XC];
+#pragma unroll
+  for (int i = 0; i < XC; ++i)
+    xc[i] = 64 * i + lane < D / 8 ? reinterpret_cast<const uint4*>(x + (size_t)t * D)[64 * i + lane]
+                                  : make_uint4(0u, 0u, 0u, 0u);
   constexpr int SU = EPL <= 4 ? 8 : 2;  // slices loaded at a time (all EPL * SU loads in flight)
   const float* p = a.logits + (size_t)t * E16;
   float l[EPL];
@@ -99,6 +121,17 @@ __global__ __launch_bounds__(64) void k_topk(const LayerArgs a, int T, int S, in
     if (idx_out) idx_out[(size_t)t * k + lane] = se;
     if (w_out) w_out[(size_t)t * k + lane] = sw;
   }
+  // operand row: x 2^a with the largest |x| in [1, 2)
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < XC; ++i)
+    mb = max(mb, max(max(bf16_mag_max(xc[i].x), bf16_mag_max(xc[i].y)), max(bf16_mag_max(xc[i].z), bf16_mag_max(xc[i].w))));
+  const int ea = act_exponent(wave_max_u32(mb));
+  uint4* xr = reinterpret_cast<uint4*>(a.xp + (size_t)t * D);
+#pragma unroll
+  for (int i = 0; i < XC; ++i)
+    if (64 * i + lane < D / 8) xr[64 * i + lane] = operand_chunk(xc[i], ea);
+  if (lane == 0) a.xexp[t] = ea;
 }
 
 // ----------------------------------------------------------------- sort
@@ -419,15 +452,6 @@ __global__ __launch_bounds__(64) void k_prenorm(const float* __restrict__ resid,
     xr[64 * i + lane] = make_uint2(pack_bf16(rv[i].x / den, rv[i].y / den), pack_bf16(rv[i].z / den, rv[i].w / den));
 }
 
-// One token's 8 activations of one chunk (bf16) as the fp16 MFMA operand
-// of the expert kernels, in the order (x0, x4, x1, x5, x2, x6, x3, x7).
-__device__ __forceinline__ uint4 operand_chunk(uint4 q) {
-  const float x0 = bf16_bits_to_f32(q.x & 0xFFFFu), x1 = __uint_as_float(q.x & 0xFFFF0000u);
-  const float x2 = bf16_bits_to_f32(q.y & 0xFFFFu), x3 = __uint_as_float(q.y & 0xFFFF0000u);
-  const float x4 = bf16_bits_to_f32(q.z & 0xFFFFu), x5 = __uint_as_float(q.z & 0xFFFF0000u);
-  const float x6 = bf16_bits_to_f32(q.w & 0xFFFFu), x7 = __uint_as_float(q.w & 0xFFFF0000u);
-  return make_uint4(pack_f16(x0, x4), pack_f16(x1, x5), pack_f16(x2, x6), pack_f16(x3, x7));
-}
 
 // grid = ceil(E/64) * ceil(T/(16 NB)) * S workgroups of 256.  Wave w holds
 // the A operands (16 experts x 32 k, three terms) of its expert block; the
@@ -435,8 +459,7 @@ __device__ __forceinline__ uint4 operand_chunk(uint4 q) {
 // buffered, and each wave reads its B operands (16 tokens x 32 k) there.
 // Rows past T hold token T-1 again (loads clamped); their sums are not
 // stored.  Lane l ends with the logits of token 16j + l%16, experts
-// 4(l/16) .. +3 of its block.  The workgroups of expert tile 0 also write
-// each token's fp16 operand row xp for the expert kernels.
+// 4(l/16) .. +3 of its block.
 template <int NB>
 __global__ __launch_bounds__(256) void k_router_mm(const LayerArgs a, const uint16_t* __restrict__ x, int T,
                                                    int S) {
@@ -459,14 +482,10 @@ __global__ __launch_bounds__(256) void k_router_mm(const LayerArgs a, const uint
   // staging: chunk c = threadIdx.x + 256 i is chunk c%4 of token row c/4
   const bool st_ok = 4 * TT >= 256 || (int)threadIdx.x < 4 * TT;
   const uint4* xs[NC];
-  uint4* ps[NC];
-  bool pw[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const int c = threadIdx.x + 256 * i, t = t0 + c / 4;
     xs[i] = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * d + kb0 * 32) + (c & 3);
-    ps[i] = reinterpret_cast<uint4*>(a.xp + (size_t)min(t, T - 1) * d + kb0 * 32) + (c & 3);
-    pw[i] = et == 0 && st_ok && t < T;
   }
 
   // operands of 4 steps in flight (a ring of register slots; nk is a
@@ -484,7 +503,6 @@ __global__ __launch_bounds__(256) void k_router_mm(const LayerArgs a, const uint
     for (int i = 0; i < NC; ++i) {
       const int c = threadIdx.x + 256 * i;
       if (st_ok) s_x[buf][(c >> 2) * kRtRow + (c & 3)] = X[i];
-      if (pw[i]) ps[i][ks * 4] = operand_chunk(X[i]);
     }
   };
 #pragma unroll
@@ -879,7 +897,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
         if (pt < it.n) {
           const int asg = a.asg[it.p0 + pt];
           const float wj = asg < Tk ? a.sel_w[asg] : 1.f;
-          const float h = wj * silu(acc[0][tt][v]) * acc[1][tt][v];
+          const int ea = a.xexp[asg < Tk ? asg / k : asg - Tk];
+          // gate and up hold 2^ea g and 2^ea u: h 2^(2 ea) with silu of the true g
+          const float gs = acc[0][tt][v];
+          const float h = wj * (gs / (1.0f + expf(-ldexpf(gs, -ea)))) * acc[1][tt][v];
           a.h16[(size_t)(it.p0 + pt) * f + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
       }
@@ -939,9 +960,10 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
 
 // ----------------------------------------------------------------- combine
 
-// y_t = sum_{j<k} o_{t,j} (slot order); with resid, resid_t += y_t.
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf, int T, int d, int k, int ns,
-                                                 float* __restrict__ y_out, float* __restrict__ resid) {
+// y_t = 2^(-2 a_t) sum_{j<k} o_{t,j} (slot order); with resid, resid_t += y_t.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf, const int32_t* __restrict__ xexp,
+                                                 int T, int d, int k, int ns, float* __restrict__ y_out,
+                                                 float* __restrict__ resid) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // float4 index over [T][d]
   if (i >= T * d / 4) return;
   const int t = (4 * i) / d, r = 4 * i - t * d;
@@ -960,6 +982,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf,
     s.z += o.z;
     s.w += o.w;
   }
+  // the outputs of token t were formed from h 2^(2 a_t)
+  const int e2 = -2 * xexp[t];
+  s = make_float4(ldexpf(s.x, e2), ldexpf(s.y, e2), ldexpf(s.z, e2), ldexpf(s.w, e2));
   if (resid) {
     float4* rp = reinterpret_cast<float4*>(resid + (size_t)t * d + r);
     float4 rv = *rp;
@@ -979,12 +1004,26 @@ static void prenorm_inst(const float* r, float eps, int T, uint16_t* xn, hipStre
   hipLaunchKernelGGL((k_prenorm<D>), dim3(T), dim3(64), 0, s, r, eps, xn);
 }
 
-template <int EPL>
-static void topk_inst(const LayerArgs& a, int T, int S, int32_t* idx_out, float* w_out, hipStream_t s) {
+template <int EPL, int D>
+static void topk_inst_d(const LayerArgs& a, const uint16_t* x, int T, int S, int32_t* idx_out, float* w_out,
+                        hipStream_t s) {
   if (a.k <= 8)
-    hipLaunchKernelGGL((k_topk<EPL, 8>), dim3(T), dim3(64), 0, s, a, T, S, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<EPL, 8, D>), dim3(T), dim3(64), 0, s, a, x, T, S, idx_out, w_out);
   else
-    hipLaunchKernelGGL((k_topk<EPL, 16>), dim3(T), dim3(64), 0, s, a, T, S, idx_out, w_out);
+    hipLaunchKernelGGL((k_topk<EPL, 16, D>), dim3(T), dim3(64), 0, s, a, x, T, S, idx_out, w_out);
+}
+
+template <int EPL>
+static void topk_inst(const LayerArgs& a, const uint16_t* x, int T, int S, int32_t* idx_out, float* w_out,
+                      hipStream_t s) {
+  switch (a.d) {
+    case 256: topk_inst_d<EPL, 256>(a, x, T, S, idx_out, w_out, s); break;
+    case 512: topk_inst_d<EPL, 512>(a, x, T, S, idx_out, w_out, s); break;
+    case 1024: topk_inst_d<EPL, 1024>(a, x, T, S, idx_out, w_out, s); break;
+    case 2048: topk_inst_d<EPL, 2048>(a, x, T, S, idx_out, w_out, s); break;
+    case 4096: topk_inst_d<EPL, 4096>(a, x, T, S, idx_out, w_out, s); break;
+    default: topk_inst_d<EPL, 8192>(a, x, T, S, idx_out, w_out, s); break;
+  }
 }
 
 hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, float eps, int T,
@@ -1012,15 +1051,15 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
   }
   const int epl = (a.E + 63) / 64;
   if (epl <= 1)
-    topk_inst<1>(a, T, S, idx_out, w_out, s);
+    topk_inst<1>(a, x, T, S, idx_out, w_out, s);
   else if (epl <= 2)
-    topk_inst<2>(a, T, S, idx_out, w_out, s);
+    topk_inst<2>(a, x, T, S, idx_out, w_out, s);
   else if (epl <= 4)
-    topk_inst<4>(a, T, S, idx_out, w_out, s);
+    topk_inst<4>(a, x, T, S, idx_out, w_out, s);
   else if (epl <= 8)
-    topk_inst<8>(a, T, S, idx_out, w_out, s);
+    topk_inst<8>(a, x, T, S, idx_out, w_out, s);
   else
-    topk_inst<16>(a, T, S, idx_out, w_out, s);
+    topk_inst<16>(a, x, T, S, idx_out, w_out, s);
   const size_t lds = sort_lds_bytes(a.E, T * a.k);
   if (lds > 64 * 1024) {
     static bool raised = false;
@@ -1159,7 +1198,7 @@ hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s) {
   const int n4 = T * a.d / 4;
-  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, T, a.d, a.k, a.ns, y_out,
+  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out,
                      residual);
   return hipGetLastError();
 }

@@ -52,7 +52,8 @@ struct LayerArgs {
   uint16_t* xn;           // [T][d] pre-normed activations of a stack layer (bf16), unless x_trace holds them
   int32_t* sel_idx;       // [T][k] chosen experts of assignment t*k + j
   float* sel_w;           // [T][k] their weights
-  uint16_t* xp;           // [T][d] activations in MFMA operand order (fp16)
+  uint16_t* xp;           // [T][d] activations x 2^a_t in MFMA operand order (fp16)
+  int32_t* xexp;          // [T] a_t: the power of two that puts token t's largest |x| in [1, 2)
   int32_t* off;           // [E+1] first position of each expert in asg
   int32_t* act;           // [E] experts with assignments, ascending
   int32_t* chunk_off;     // [E+1] 32-token chunks of the active experts before each

@@ -170,6 +170,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   __shared__ __align__(16) uint16_t s_x[D];
   __shared__ __align__(16) float s_r[NORM ? D : 4];  // the residual r_l (stack)
   __shared__ float s_ss[4];
+  __shared__ uint32_t s_xm[4];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wg = blockIdx.x * 4 + wid;
@@ -261,8 +262,15 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
       }
     }
   if constexpr (!NORM) {
+    uint32_t mb = 0;  // the largest |x| (bf16 bits)
 #pragma unroll
-    for (int c = threadIdx.x; c < D / 8; c += 256) reinterpret_cast<uint4*>(s_x)[c] = reinterpret_cast<const uint4*>(io.x)[c];
+    for (int c = threadIdx.x; c < D / 8; c += 256) {
+      const uint4 q = reinterpret_cast<const uint4*>(io.x)[c];
+      reinterpret_cast<uint4*>(s_x)[c] = q;
+      mb = max(mb, max(max(bf16_mag_max(q.x), bf16_mag_max(q.y)), max(bf16_mag_max(q.z), bf16_mag_max(q.w))));
+    }
+    mb = wave_max_u32(mb);
+    if (lane == 0) s_xm[wid] = mb;
     __syncthreads();
   } else {
     // x = bf16(r / sqrt(mean(r^2) + eps)), the same in every workgroup
@@ -321,17 +329,24 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     if (lane == 0) s_ss[wid] = ss;
     __syncthreads();
     const float den = sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)D + io.eps);
+    uint32_t mb = 0;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
       const int c = threadIdx.x + 256 * m;
       if (c < D / 4) {
         const uint2 pk = make_uint2(pack_bf16(rv[m].x / den, rv[m].y / den), pack_bf16(rv[m].z / den, rv[m].w / den));
         reinterpret_cast<uint2*>(s_x)[c] = pk;
+        mb = max(mb, max(bf16_mag_max(pk.x), bf16_mag_max(pk.y)));
         if (io.x_trace && blockIdx.x == 0) reinterpret_cast<uint2*>(io.x_trace)[c] = pk;
       }
     }
+    mb = wave_max_u32(mb);
+    if (lane == 0) s_xm[wid] = mb;
     __syncthreads();
   }
+  // h goes to the down phase as h 2^(2 ea) in binary16, ea from the largest
+  // |x| (the same in every workgroup): exact scalings, any magnitude of x
+  const int ea = act_exponent(max(max(s_xm[0], s_xm[1]), max(s_xm[2], s_xm[3])));
 
   // ---------------------------------------------------------------- router
   // rows 4*b .. 4*b+3 in workgroup b, one per wave; the 4 logits go out as
@@ -461,10 +476,10 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
         // row within this workgroup's ROWS_G consecutive rows of slot gslot
         if constexpr (CPR >= 64) {
           const float g = wave_sum(ag) * tg, u = wave_sum(au) * tu;
-          if (lane == 0) s_hv[(wid * 64 * NL + 64 * n) / CPR] = wj * silu(g) * u;
+          if (lane == 0) s_hv[(wid * 64 * NL + 64 * n) / CPR] = wj * silu_scaled(g, ea) * ldexpf(u, ea);
         } else {
           const float g = seg_sum<(CPR < 64 ? CPR : 64)>(ag) * tg, u = seg_sum<(CPR < 64 ? CPR : 64)>(au) * tu;
-          if (lane % CPR == 0) s_hv[(wid * 64 * NL + 64 * n + lane) / CPR] = wj * silu(g) * u;
+          if (lane % CPR == 0) s_hv[(wid * 64 * NL + 64 * n + lane) / CPR] = wj * silu_scaled(g, ea) * ldexpf(u, ea);
         }
         ag = au = 0.f;
       }
@@ -615,10 +630,10 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
       else acc += dot_piece_f16(qd[n], hs8[m], sd[n]);
       if (n % LPRD == LPRD - 1) {
         if constexpr (P >= 64) {
-          const float v = wave_sum(acc);
+          const float v = ldexpf(wave_sum(acc), -2 * ea);
           if (lane == 0) put_y(r0 + n / LPRD, v, radd[n]);
         } else {
-          const float v = seg_sum<(P < 64 ? P : 64)>(acc);
+          const float v = ldexpf(seg_sum<(P < 64 ? P : 64)>(acc), -2 * ea);
           if (lane % P == 0) put_y(r0 + n * RPLD + lane / P, v, radd[n]);
         }
         acc = 0.f;

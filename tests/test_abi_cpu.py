@@ -118,6 +118,13 @@ def test_forward_and_stack_reject_null_handles():
     assert L.moe_decode_stack_forward(None, 1, FAKE, 1, 1e-6, None, None, None, None) == M.MOE_ERR_NULL
     assert L.moe_decode_expert_groups(None, 1, FAKE, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
     assert L.moe_decode_error_flags(None, FAKE, 1, None) == M.MOE_ERR_NULL
+    assert L.moe_int4_repack(None, FAKE, 1, 128, None) == M.MOE_ERR_NULL
+    assert L.moe_int4_repack(FAKE, FAKE + (1 << 20), 1, 96, None) == M.MOE_ERR_SHAPE
+    assert L.moe_int4_repack(FAKE, FAKE + (1 << 20), 0, 128, None) == M.MOE_ERR_SHAPE
+    assert L.moe_int4_repack(FAKE, FAKE + 32, 1, 128, None) == M.MOE_ERR_SHAPE  # overlapping
+    assert L.moe_int4_repack(FAKE + 8, FAKE + (1 << 20), 1, 128, None) == M.MOE_ERR_ALIGN
+    assert L.moe_decode_read_probe(FAKE, 100, FAKE, None) == M.MOE_ERR_SHAPE
+    assert L.moe_decode_read_probe(None, 128, FAKE, None) == M.MOE_ERR_NULL
     assert L.moe_decode_set_wait_limit(None, 1, 0) == M.MOE_ERR_NULL
     M.moe_decode_destroy(None)  # ignored
 

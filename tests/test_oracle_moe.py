@@ -53,6 +53,20 @@ def test_topk_equals_best_subset_bruteforce():
         assert w[0] >= w[1]
 
 
+def test_topk_where_probabilities_underflow():
+    """Logits spread over 2^20: all but the largest softmax probability
+    underflow to 0 in fp64, yet the chosen set is still the k largest
+    logits (the brute-force best subset), in descending order."""
+    rng = np.random.default_rng(21)
+    l = rng.standard_normal(16) * 2.0 ** 20
+    p = M.softmax(l)
+    assert np.count_nonzero(p) == 1
+    S, w = M.route(l, 4)
+    assert sorted(S.tolist()) == sorted(M.best_subset_bruteforce(l, 4).tolist())
+    assert np.all(np.diff(l[S]) < 0)
+    assert w.tolist() == [1.0, 0.0, 0.0, 0.0]
+
+
 def test_topk_tie_lower_index_first():
     p = np.array([0.1, 0.3, 0.3, 0.3])
     assert M.select_topk(p, 1).tolist() == [1]
