@@ -20,7 +20,7 @@ static bool fits(int d, int f, int E, int k, int G) {
   const int nld = lprd > 4 ? lprd : 4;
   const int rows_w = (nld / lprd) * rpld;
   if (d / rows_w > W) return false;
-  if ((size_t)k * (f / 8) * 5 * sizeof(unsigned) > 64 * 1024) return false;
+  if ((size_t)kp * (f / 8) * 5 * sizeof(unsigned) > 64 * 1024) return false;  // slices of h in LDS
   if (E > 256 || E > W) return false;
   return true;
 }

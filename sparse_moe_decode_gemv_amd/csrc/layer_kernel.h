@@ -157,7 +157,14 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   constexpr int RPG = 4 * ROWS_W;             // output rows per workgroup (C2: 8)
   static_assert(NL % LPRG == 0 && NI >= 1 && ROWS_G % 8 == 0, "shape");
 
-  extern __shared__ unsigned s_sl[];  // k*F/8 slices x 5 words
+  // the KP*F/8 slices of h as the down phase reads them: p0..p3 of the
+  // slice read at (m, j) by lane l at position (4m + j) * 64 + l (or
+  // j * P + l % P when a row has fewer than 64 pieces), and its corr word
+  // at the same position of a second array, so that each read is one
+  // 16-byte (or 4-byte) load per lane at consecutive addresses
+  extern __shared__ unsigned s_dyn[];
+  uint4* s_slp = reinterpret_cast<uint4*>(s_dyn);
+  float* s_slc = reinterpret_cast<float*>(s_dyn + 4 * KP * F / 8);
   __shared__ int s_idx[16];
   __shared__ float s_w[16];
   __shared__ float s_part[4];
@@ -573,8 +580,17 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     constexpr int NR = (KP * F / 8 * 5 + 255) / 256;
     const int nw = nslots * (F / 8) * 5;  // slice words; word j = 5 * slice + field
     unsigned missing = 0;
+    unsigned dst[NR];  // where word j goes in LDS (s_dyn words)
 #pragma unroll
-    for (int m = 0; m < NR; ++m) missing |= (threadIdx.x + 256 * m < (unsigned)nw ? 1u : 0u) << m;
+    for (int m = 0; m < NR; ++m) {
+      const int jw = threadIdx.x + 256 * m;
+      missing |= (jw < nw ? 1u : 0u) << m;
+      const int sl = jw / 5, fld = jw - 5 * sl;
+      const int slot = sl / (F / 8), sidx = sl % (F / 8);
+      const int flat = slot * CPRF + 4 * (sidx / 16) + (sidx & 3), jg = (sidx >> 2) & 3;  // piece, group of the slice
+      const int pos = P >= 64 ? ((flat / 64) * 4 + jg) * 64 + flat % 64 : jg * P + flat;
+      dst[m] = fld < 4 ? 4 * pos + fld : 4 * KP * F / 8 + pos;
+    }
     for (unsigned spin = 0;; ++spin) {
       unsigned long long r[NR];
 #pragma unroll
@@ -583,7 +599,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
         if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag + io.tag_skew) {
-          s_sl[threadIdx.x + 256 * m] = (uint32_t)r[m];
+          s_dyn[dst[m]] = (uint32_t)r[m];
           missing &= ~(1u << m);
         }
       }
@@ -615,10 +631,10 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     for (int m = 0; m < LPRD; ++m) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int c = (act[m] ? dslot[m] : 0) * (F / 8) + 16 * (cc[m] >> 2) + 4 * j + (cc[m] & 3);
-        const unsigned* sp = s_sl + 5 * c;
-        hs8[m][j] = act[m] ? Slice8{sp[0], sp[1], sp[2], sp[3], __uint_as_float(sp[4])}
-                           : Slice8{0u, 0u, 0u, 0u, 0.f};
+        const int pos = P >= 64 ? (4 * m + j) * 64 + lane : j * P + lane % P;
+        const uint4 pv = s_slp[pos];
+        const float cv = s_slc[pos];
+        hs8[m][j] = act[m] ? Slice8{pv.x, pv.y, pv.z, pv.w, cv} : Slice8{0u, 0u, 0u, 0u, 0.f};
       }
     }
     float acc = 0.f;
@@ -695,7 +711,7 @@ __global__ __launch_bounds__(256) void k_stack(StackArgs s) {
 
 template <int D, int F, int KP, int EPL, int FMT>
 static hipError_t layer_launch_fmt(const FusedArgs& a, int G, hipStream_t s) {
-  const size_t lds = (size_t)(a.k + a.ns) * (F / 8) * 5 * sizeof(unsigned);
+  const size_t lds = (size_t)KP * (F / 8) * 5 * sizeof(unsigned);
   if (a.ns) {
     if (a.resid_in)
       hipLaunchKernelGGL((k_layer<D, F, KP, EPL, true, true, FMT>), dim3(G), dim3(256), lds, s, a);
@@ -739,7 +755,7 @@ static hipError_t launch_layer_format(const FusedArgs& a, int d, int f, int G, h
 // layers have it).
 template <int D, int F, int KP, int EPL, int FMT>
 static hipError_t stack_launch_fmt(const StackArgs& a, const StackShape& sh, int G, hipStream_t s) {
-  const size_t lds = (size_t)(sh.k + sh.ns) * (F / 8) * 5 * sizeof(unsigned);
+  const size_t lds = (size_t)KP * (F / 8) * 5 * sizeof(unsigned);
   if (sh.ns)
     hipLaunchKernelGGL((k_stack<D, F, KP, EPL, true, FMT>), dim3(G), dim3(256), lds, s, a);
   else
