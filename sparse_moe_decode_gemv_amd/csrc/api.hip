@@ -14,7 +14,7 @@ constexpr int kAbiVersion = 5;
 
 struct Layout {
   size_t logits, sel_idx, sel_w, xp, xexp, xn, off, act, chunk_off, chunks, asg, h16, obuf, resid, tagged,
-      hrec, epoch, sort_wc, rrec, cleared;       // [0, cleared) is zeroed at init
+      hrec, epoch, sort_wc, rrec, cleared; // [0, cleared) is zeroed at init
   size_t args;                                           // the single-launch kernel's arguments (persistent stack)
   size_t gate_t, gate_ts, up_t, up_ts, down_t, down_ts;  // tile-major expert copies (0 bytes if unused)
   size_t router_t;                                       // bf16 terms of the router matrix (same)
@@ -70,7 +70,7 @@ Layout layout_of(const moe_layer_desc* d) {
   L.xp = o, o += align256(T * d_ * sizeof(uint16_t));
   L.xexp = o, o += align256(T * sizeof(int32_t));
   L.xn = o, o += align256(T * d_ * sizeof(uint16_t));
-  L.off = o, o += align256((E + 1 + 4) * sizeof(int32_t));  // off[E+1], then meta
+  L.off = o, o += align256((E + 1 + 64) * sizeof(int32_t));  // off[E+1], then meta (meta[32]: an arrival count on a line of its own)
   L.act = o, o += align256(E * sizeof(int32_t));
   L.chunk_off = o, o += align256((E + 1) * sizeof(int32_t));
   L.chunks = o, o += align256(((E < Tk ? E : Tk) + Tk / 32 + ns * ((T + 31) / 32)) * 4 * sizeof(int32_t));
@@ -383,8 +383,7 @@ moe_status moe_decode_forward(moe_handle h, const uint16_t* x, int32_t T, float*
   }
   if (moe::launch_router(a, x, nullptr, 0.f, T, topk_idx, topk_w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_gateup(a, T, s) != hipSuccess) return MOE_ERR_HIP;
-  if (moe::launch_down(a, T, s) != hipSuccess) return MOE_ERR_HIP;
-  if (moe::launch_combine(a, T, y, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_down_combine(a, T, y, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -468,8 +467,7 @@ moe_status moe_decode_stack_forward_ex(const moe_handle* layers, int32_t L, floa
       float* r = buf[cur];
       if (moe::launch_router(a, nullptr, r, eps, T, it, nullptr, xt, s) != hipSuccess) return MOE_ERR_HIP;
       if (moe::launch_gateup(a, T, s) != hipSuccess) return MOE_ERR_HIP;
-      if (moe::launch_down(a, T, s) != hipSuccess) return MOE_ERR_HIP;
-      if (moe::launch_combine(a, T, yt, r, s) != hipSuccess) return MOE_ERR_HIP;
+      if (moe::launch_down_combine(a, T, yt, r, s) != hipSuccess) return MOE_ERR_HIP;
     }
   }
   if (cur && hipMemcpyAsync(residual, buf[1], (size_t)T * d * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -516,7 +514,7 @@ moe_status moe_decode_set_wait_limit(moe_handle h, uint32_t polls, int32_t unrea
   if (!h) return MOE_ERR_NULL;
   if (polls < 1 || (unreachable != 0 && unreachable != 1)) return MOE_ERR_SHAPE;
   h->spin_limit = polls;
-  h->tag_skew = (unsigned)unreachable;
+  h->tag_skew = unreachable ? 1u : 0u;
   return MOE_OK;
 }
 

@@ -82,20 +82,33 @@ __device__ __forceinline__ Slice8 make_slice_bf16(uint4 q) {
   return s;
 }
 
+// A constant held in a VGPR the compiler cannot see through.  gfx950's
+// three-operand (VOP3) encodings take no 32-bit literal, so (w & mask) |
+// magic with literal constants compiles to a v_and and a v_or; with both
+// constants in VGPRs it is one v_and_or_b32.  (The empty asm has no side
+// effect, so repeated uses are merged and hoisted out of loops.)
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // acc + sum_e (128+u_e or 128+8u_e) * (x_e or x_e/8); started from s.corr
 // this is sum_e (u_e - 8) x_e.
 __device__ __forceinline__ float dot8(uint32_t w, const Slice8& s, float acc) {
-  acc = dot2_bf16((w & 0x000F000Fu) | 0x43004300u, s.p0, acc);
-  acc = dot2_bf16(((w >> 1) & 0x00780078u) | 0x43004300u, s.p1, acc);
-  acc = dot2_bf16(((w >> 8) & 0x000F000Fu) | 0x43004300u, s.p2, acc);
-  acc = dot2_bf16(((w >> 9) & 0x00780078u) | 0x43004300u, s.p3, acc);
+  const uint32_t lo = vgpr_const(0x000F000Fu), mid = vgpr_const(0x00780078u), mg = vgpr_const(0x43004300u);
+  acc = dot2_bf16((w & lo) | mg, s.p0, acc);
+  acc = dot2_bf16(((w >> 1) & mid) | mg, s.p1, acc);
+  acc = dot2_bf16(((w >> 8) & lo) | mg, s.p2, acc);
+  acc = dot2_bf16(((w >> 9) & mid) | mg, s.p3, acc);
   return acc;
 }
 
 // One 16-byte piece (4 groups x 8 codes) against 4 prepared slices, scaled by
 // the 4 groups' binary16 scales (sc.x = groups 0,1; sc.y = groups 2,3).
 __device__ __forceinline__ float dot_piece(uint4 q, const Slice8 xs[4], uint2 sc) {
-  float p = dot8(q.x, xs[0], xs[0].corr) * f16_bits_to_f32(sc.x & 0xFFFFu);
+  // the first product as an fma with +0 as well: one v_fma_mix_f32 (binary16
+  // operand) rather than a conversion and a multiply
+  float p = fmaf(dot8(q.x, xs[0], xs[0].corr), f16_bits_to_f32(sc.x & 0xFFFFu), 0.f);
   p = fmaf(dot8(q.y, xs[1], xs[1].corr), f16_bits_to_f32(sc.x >> 16), p);
   p = fmaf(dot8(q.z, xs[2], xs[2].corr), f16_bits_to_f32(sc.y & 0xFFFFu), p);
   p = fmaf(dot8(q.w, xs[3], xs[3].corr), f16_bits_to_f32(sc.y >> 16), p);
@@ -127,6 +140,13 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ float f16_lo(uint32_t p) { return (float)__builtin_bit_cast(f16x2_t, p).x; }
 __device__ __forceinline__ float f16_hi(uint32_t p) { return (float)__builtin_bit_cast(f16x2_t, p).y; }
 
+// The offset correction of a slice from its 4 binary16 pairs.
+__device__ __forceinline__ float slice_f16_corr(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+  const float e = (f16_lo(p0) + f16_hi(p0)) + (f16_lo(p2) + f16_hi(p2));
+  const float o = (f16_lo(p1) + f16_hi(p1)) + (f16_lo(p3) + f16_hi(p3));
+  return -1032.0f * e - 1152.0f * o;  // odd terms are stored /16: -72 * 16
+}
+
 // From 8 fp32 activations (rounded to fp16 here).
 __device__ __forceinline__ Slice8 make_slice_f16(const float v[8]) {
   Slice8 s;
@@ -134,24 +154,24 @@ __device__ __forceinline__ Slice8 make_slice_f16(const float v[8]) {
   s.p1 = pack_f16(v[1] * 0.0625f, v[5] * 0.0625f);
   s.p2 = pack_f16(v[2], v[6]);
   s.p3 = pack_f16(v[3] * 0.0625f, v[7] * 0.0625f);
-  const float e = (f16_lo(s.p0) + f16_hi(s.p0)) + (f16_lo(s.p2) + f16_hi(s.p2));
-  const float o = (f16_lo(s.p1) + f16_hi(s.p1)) + (f16_lo(s.p3) + f16_hi(s.p3));
-  s.corr = -1032.0f * e - 1152.0f * o;  // odd terms are stored /16: -72 * 16
+  s.corr = slice_f16_corr(s.p0, s.p1, s.p2, s.p3);
   return s;
 }
 
 // acc + sum_e (1024+u_e or 1024+16u_e) * (h_e or h_e/16); started from
 // s.corr this is sum_e (u_e - 8) h_e.
 __device__ __forceinline__ float dot8_f16(uint32_t w, const Slice8& s, float acc) {
-  acc = dot2_f16((w & 0x000F000Fu) | 0x64006400u, s.p0, acc);
-  acc = dot2_f16((w & 0x00F000F0u) | 0x64006400u, s.p1, acc);
-  acc = dot2_f16(((w >> 8) & 0x000F000Fu) | 0x64006400u, s.p2, acc);
-  acc = dot2_f16(((w >> 8) & 0x00F000F0u) | 0x64006400u, s.p3, acc);
+  const uint32_t lo = vgpr_const(0x000F000Fu), hi = vgpr_const(0x00F000F0u), mg = vgpr_const(0x64006400u);
+  const uint32_t w8 = w >> 8;
+  acc = dot2_f16((w & lo) | mg, s.p0, acc);
+  acc = dot2_f16((w & hi) | mg, s.p1, acc);
+  acc = dot2_f16((w8 & lo) | mg, s.p2, acc);
+  acc = dot2_f16((w8 & hi) | mg, s.p3, acc);
   return acc;
 }
 
 __device__ __forceinline__ float dot_piece_f16(uint4 q, const Slice8 xs[4], uint2 sc) {
-  float p = dot8_f16(q.x, xs[0], xs[0].corr) * f16_bits_to_f32(sc.x & 0xFFFFu);
+  float p = fmaf(dot8_f16(q.x, xs[0], xs[0].corr), f16_bits_to_f32(sc.x & 0xFFFFu), 0.f);
   p = fmaf(dot8_f16(q.y, xs[1], xs[1].corr), f16_bits_to_f32(sc.x >> 16), p);
   p = fmaf(dot8_f16(q.z, xs[2], xs[2].corr), f16_bits_to_f32(sc.y & 0xFFFFu), p);
   p = fmaf(dot8_f16(q.w, xs[3], xs[3].corr), f16_bits_to_f32(sc.y >> 16), p);
@@ -292,6 +312,33 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return seg_sum<64>(v); }
+
+// Eight wave sums at once (reduce-scatter): lane l receives the sum over
+// the wave of v[(l >> 3) & 7].  Each permlane swap exchanges two different
+// values, so a halving step costs one swap and one add per pair of values:
+// 18 instructions instead of the 8 x 8 of separate sums.
+__device__ __forceinline__ float wave_sum8_scatter(const float v[8]) {
+  const int lane = threadIdx.x & 63;
+  float a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // half-waves: lanes 0-31 keep values 0-3, lanes 32-63 values 4-7
+    const u32x2_t p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+    a[i] = __uint_as_float(p.x) + __uint_as_float(p.y);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 16-lane rows: even rows keep a[0..1], odd rows a[2..3]
+    const u32x2_t p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + 2]), false, false);
+    b[i] = __uint_as_float(p.x) + __uint_as_float(p.y);
+  }
+  // 8-lane halves of a row (mirror pairing): lanes 0-7 keep b[0], 8-15 b[1]
+  const bool upper = lane & 8;
+  const float keep = upper ? b[1] : b[0], give = upper ? b[0] : b[1];
+  float r = keep + dpp_f<kDppMirror>(give);
+  r += dpp_f<kDppXor1>(r);
+  r += dpp_f<kDppXor2>(r);
+  r += dpp_f<kDppHalfMirror>(r);
+  return r;
+}
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<kDppXor1>(v));

@@ -87,15 +87,31 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   for (int b = 0; b < BP; ++b) best[b] = -INFINITY, brow[b] = 0xFFFFFFFFu;
 
   // Tiles are dealt round-robin to the waves.  Every load is unconditional,
-  // so the compiler's wait counts stay exact: pieces past the matrix read
-  // its last piece (their rows are >= V and are dropped below).
+  // so the compiler's wait counts stay exact: in the last tile, pieces past
+  // the matrix read its last piece (their rows are >= V and are dropped
+  // below).  A tile's base is uniform (scalar registers) and lanes add
+  // 32-bit offsets.  The 4 scales of piece c (pieces 4i .. 4i+3 of a row
+  // hold the 4 groups 4i .. 4i+3) start at scale c & ~3.
+  static_assert(CPR % 4 == 0, "pieces of a row come in fours");
   const size_t ntiles = (total + 64 * NL - 1) / (64 * NL), stride = (size_t)gridDim.x * 4;
+  const size_t nfull = total / (64 * NL);
   auto load_tile = [&](size_t t, uint4 (&q)[NL], uint2 (&sc)[NL]) {
+    const uint4* tq = wp + t * 64 * NL;
+    const uint16_t* ts = ws + t * 64 * NL;
+    if (t < nfull) {
 #pragma unroll
-    for (int n = 0; n < NL; ++n) {
-      const size_t c = min(t * 64 * NL + 64 * n + lane, total - 1);
-      q[n] = wp[c];
-      sc[n] = *reinterpret_cast<const uint2*>(ws + (c / CPR) * CPR + ((int)(c % CPR) & ~3));
+      for (int n = 0; n < NL; ++n) {
+        const uint32_t c = 64 * n + lane;
+        q[n] = tq[c];
+        sc[n] = *reinterpret_cast<const uint2*>(ts + (c & ~3u));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const uint32_t c = (uint32_t)min((size_t)(64 * n + lane), total - 1 - t * 64 * NL);
+        q[n] = tq[c];
+        sc[n] = *reinterpret_cast<const uint2*>(ts + (c & ~3u));
+      }
     }
   };
   auto dot_tile = [&](size_t t, const uint4 (&q)[NL], const uint2 (&sc)[NL]) {
@@ -103,6 +119,17 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
     float acc[BP];
 #pragma unroll
     for (int b = 0; b < BP; ++b) acc[b] = 0.f;
+    if constexpr (CPR == 64 && BP == 1 && NL == 8) {
+      // one row per piece column: the 8 row sums of the tile at once, lane
+      // l holding row c0 / 64 + ((l >> 3) & 7)
+      float z8[8];
+#pragma unroll
+      for (int n = 0; n < NL; ++n) z8[n] = dot_piece(q[n], xs[0][0], sc[n]);
+      const float z = wave_sum8_scatter(z8);
+      const uint32_t row = (uint32_t)(c0 / 64) + ((lane >> 3) & 7);
+      if (row < (uint32_t)V && z > best[0]) best[0] = z, brow[0] = row;
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
       const int s = CPR > 64 ? n % XS : 0;

@@ -76,10 +76,13 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // VALU instruction takes 4 cycles, so waves sharing a SIMD would serialize).
 // The logits are the S partial sums of the router (slice order) plus the
 // bias.
-template <int EPL, int KP, int D>
-__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, const uint16_t* __restrict__ x, int T, int S,
-                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  const int t = blockIdx.x, lane = threadIdx.x, E = a.E, k = a.k, E16 = (E + 15) & ~15;
+// Token t in one wave; COH: the chosen experts are stored coherently (read
+// back by another workgroup of the same kernel).
+template <int EPL, int KP, int D, bool COH>
+__device__ __forceinline__ void topk_token(const LayerArgs& a, const uint16_t* __restrict__ x, int T, int S,
+                                           int32_t* __restrict__ idx_out, float* __restrict__ w_out, int t,
+                                           int lane) {
+  const int E = a.E, k = a.k, E16 = (E + 15) & ~15;
   // the token's activations, loaded first (they are written back below as
   // the expert kernels' operand row)
   constexpr int XC = D / 8 > 64 ? D / 8 / 64 : 1;  // 8-element chunks per lane
@@ -116,7 +119,11 @@ __global__ __launch_bounds__(64) void k_topk(const LayerArgs a, const uint16_t* 
   float sw;
   topk_fast<EPL, KP>(v, E, k, a.norm_topk, lane, se, sw);
   if (lane < k) {
-    a.sel_idx[t * k + lane] = se;
+    if constexpr (COH) {
+      __hip_atomic_store(a.sel_idx + t * k + lane, se, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      a.sel_idx[t * k + lane] = se;
+    }
     a.sel_w[t * k + lane] = sw;
     if (idx_out) idx_out[(size_t)t * k + lane] = se;
     if (w_out) w_out[(size_t)t * k + lane] = sw;
@@ -132,6 +139,12 @@ __global__ __launch_bounds__(64) void k_topk(const LayerArgs a, const uint16_t* 
   for (int i = 0; i < XC; ++i)
     if (64 * i + lane < D / 8) xr[64 * i + lane] = operand_chunk(xc[i], ea);
   if (lane == 0) a.xexp[t] = ea;
+}
+
+template <int EPL, int KP, int D>
+__global__ __launch_bounds__(64) void k_topk(const LayerArgs a, const uint16_t* __restrict__ x, int T, int S,
+                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  topk_token<EPL, KP, D, false>(a, x, T, S, idx_out, w_out, blockIdx.x, threadIdx.x);
 }
 
 // ----------------------------------------------------------------- sort
@@ -171,15 +184,20 @@ constexpr int kSortSB = 16;          // chunks of 64 whose expert loads are in f
 constexpr int kSortWideWaves = 64;   // waves of the three-kernel sort
 constexpr int kSortWideMin = 4096;   // assignments from which it is used
 
-__device__ __forceinline__ int sel_of(const LayerArgs& a, int i, int E) { return min(max(a.sel_idx[i], 0), E - 1); }
+template <bool COH>
+__device__ __forceinline__ int sel_of(const LayerArgs& a, int i, int E) {
+  const int e = COH ? __hip_atomic_load(a.sel_idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.sel_idx[i];
+  return min(max(e, 0), E - 1);
+}
 
 // Counts of the wave's slice [a0, a1) into cw[e] (zeroed).
+template <bool COH = false>
 __device__ void sort_count(const LayerArgs& a, int Tk, int a0, int a1, int lane, int* cw) {
   const int E = a.E;
   for (int cb = a0; cb < a1; cb += 64 * kSortSB) {
     int eb[kSortSB];
 #pragma unroll
-    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of(a, min(cb + 64 * u + lane, Tk - 1), E);
+    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of<COH>(a, min(cb + 64 * u + lane, Tk - 1), E);
 #pragma unroll
     for (int u = 0; u < kSortSB; ++u) {
       const int i = cb + 64 * u + lane;
@@ -194,12 +212,13 @@ __device__ void sort_count(const LayerArgs& a, int Tk, int a0, int a1, int lane,
 }
 
 // Places the wave's slice: cw[e] holds the next position of expert e.
+template <bool COH = false>
 __device__ void sort_place(const LayerArgs& a, int Tk, int a0, int a1, int lane, int* cw) {
   const int E = a.E;
   for (int cb = a0; cb < a1; cb += 64 * kSortSB) {
     int eb[kSortSB];
 #pragma unroll
-    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of(a, min(cb + 64 * u + lane, Tk - 1), E);
+    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of<COH>(a, min(cb + 64 * u + lane, Tk - 1), E);
 #pragma unroll
     for (int u = 0; u < kSortSB; ++u) {
       const int i = cb + 64 * u + lane;
@@ -267,24 +286,24 @@ __device__ void sort_tables(const LayerArgs& a, int T, int Tk, int CS, int lane,
   }
 }
 
-// One workgroup of 16 waves (up to kSortWideMin assignments).
-// LDS (dynamic): cnt [16][E], tot [E].
-__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS) {
-  extern __shared__ int sm[];
+// The sort in one workgroup of NW waves (up to kSortWideMin assignments).
+// LDS: cnt [NW][E], tot [E].
+template <int NW, bool COH>
+__device__ void sort_body(const LayerArgs& a, int T, int CS, int* sm) {
   const int E = a.E, Tk = T * a.k;
   int* cnt = sm;
-  int* tot = cnt + 16 * E;
+  int* tot = cnt + NW * E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < a.ns * T; i += 1024) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
-  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  for (int i = tid; i < a.ns * T; i += 64 * NW) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
+  for (int i = tid; i < NW * E; i += 64 * NW) cnt[i] = 0;
   __syncthreads();
-  const int per = (Tk + 15) / 16, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
+  const int per = (Tk + NW - 1) / NW, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
   int* cw = cnt + wave * E;
-  sort_count(a, Tk, a0, a1, lane, cw);
+  sort_count<COH>(a, Tk, a0, a1, lane, cw);
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) {  // base of each wave within expert e, and e's total
+  for (int e = tid; e < E; e += 64 * NW) {  // base of each wave within expert e, and e's total
     int run = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const int n = cnt[w * E + e];
       cnt[w * E + e] = run;
       run += n;
@@ -296,7 +315,38 @@ __global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS)
   __syncthreads();
   for (int e = lane; e < E; e += 64) cw[e] += tot[e];  // absolute next positions of this wave
   lds_wait();
-  sort_place(a, Tk, a0, a1, lane, cw);
+  sort_place<COH>(a, Tk, a0, a1, lane, cw);
+}
+
+// One workgroup of 16 waves (up to kSortWideMin assignments).
+// LDS (dynamic): cnt [16][E], tot [E].
+__global__ __launch_bounds__(1024) void k_sort(const LayerArgs a, int T, int CS) {
+  extern __shared__ int sm[];
+  sort_body<16, false>(a, T, CS, sm);
+}
+
+// Top-k and sort in one kernel (T <= kTopkSortMax): token 4b + w in wave w
+// of workgroup b, each wave on a SIMD of its own; the chosen experts are
+// stored coherently, every workgroup counts its arrival once they have
+// reached the coherence point, and the last to arrive (which resets the
+// count) sorts the assignments with its four waves.  LDS: cnt [4][E], tot [E].
+constexpr int kTopkSortMax = 128;
+template <int EPL, int KP, int D>
+__global__ __launch_bounds__(256) void k_topk_sort(const LayerArgs a, const uint16_t* __restrict__ x, int T, int S,
+                                                   int32_t* __restrict__ idx_out, float* __restrict__ w_out, int CS) {
+  extern __shared__ int sm[];
+  __shared__ bool s_last;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < T) topk_token<EPL, KP, D, true>(a, x, T, S, idx_out, w_out, t, threadIdx.x & 63);
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* ctr = reinterpret_cast<unsigned*>(a.meta + 32);
+    s_last = arrive(ctr) == gridDim.x - 1;
+    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (s_last) sort_body<4, true>(a, T, CS, sm);
 }
 
 // Three-kernel sort for many assignments: wave w of kSortWideWaves (16
@@ -1004,9 +1054,19 @@ static void prenorm_inst(const float* r, float eps, int T, uint16_t* xn, hipStre
   hipLaunchKernelGGL((k_prenorm<D>), dim3(T), dim3(64), 0, s, r, eps, xn);
 }
 
+// Top-k (and, for T <= kTopkSortMax, the sort in the same kernel).
 template <int EPL, int D>
 static void topk_inst_d(const LayerArgs& a, const uint16_t* x, int T, int S, int32_t* idx_out, float* w_out,
                         hipStream_t s) {
+  if (T <= kTopkSortMax) {
+    const size_t lds = (size_t)5 * a.E * sizeof(int);
+    const int g = (T + 3) / 4, CS = chunk_rows(a, T);
+    if (a.k <= 8)
+      hipLaunchKernelGGL((k_topk_sort<EPL, 8, D>), dim3(g), dim3(256), lds, s, a, x, T, S, idx_out, w_out, CS);
+    else
+      hipLaunchKernelGGL((k_topk_sort<EPL, 16, D>), dim3(g), dim3(256), lds, s, a, x, T, S, idx_out, w_out, CS);
+    return;
+  }
   if (a.k <= 8)
     hipLaunchKernelGGL((k_topk<EPL, 8, D>), dim3(T), dim3(64), 0, s, a, x, T, S, idx_out, w_out);
   else
@@ -1060,6 +1120,7 @@ hipError_t launch_router(const LayerArgs& a, const uint16_t* x, const float* r, 
     topk_inst<8>(a, x, T, S, idx_out, w_out, s);
   else
     topk_inst<16>(a, x, T, S, idx_out, w_out, s);
+  if (T <= kTopkSortMax) return hipGetLastError();  // sorted by the top-k kernel
   const size_t lds = sort_lds_bytes(a.E, T * a.k);
   if (lds > 64 * 1024) {
     static bool raised = false;
@@ -1130,12 +1191,23 @@ static hipError_t down_inst(const LayerArgs& a, dim3 g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s) {
+// The down kernel, then the combine (a kernel of its own: summing the slot
+// outputs inside the down kernel, by the last item to finish each token's
+// row group, made every item wait for its stores to reach the coherence
+// point, an arrival count and the reads of the other slots' rows -- three
+// round trips per item, measured slower than the extra kernel).
+hipError_t launch_down_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s) {
   const dim3 g(grid_for(a, T, a.d / 128));
   const bool c64 = chunk_rows(a, T) == 64;
-  if (a.fmt == 2) return c64 ? down_inst<4, 2>(a, g, s) : down_inst<2, 2>(a, g, s);
-  if (a.fmt == 1) return c64 ? down_inst<4, 1>(a, g, s) : down_inst<2, 1>(a, g, s);
-  return c64 ? down_inst<4, 0>(a, g, s) : down_inst<2, 0>(a, g, s);
+  hipError_t e;
+  if (a.fmt == 2) e = c64 ? down_inst<4, 2>(a, g, s) : down_inst<2, 2>(a, g, s);
+  else if (a.fmt == 1) e = c64 ? down_inst<4, 1>(a, g, s) : down_inst<2, 1>(a, g, s);
+  else e = c64 ? down_inst<4, 0>(a, g, s) : down_inst<2, 0>(a, g, s);
+  if (e != hipSuccess) return e;
+  const int n4 = T * a.d / 4;
+  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out,
+                     residual);
+  return hipGetLastError();
 }
 
 // fmt: 0 int4, 1 MXFP4, 2 NVFP4 (tsc: its matrix scales, rows_per_mat rows each)
@@ -1196,11 +1268,6 @@ hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s) {
                      a.d, a.f, fmt, a.sh_down_tscale, Dd, s);
 }
 
-hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s) {
-  const int n4 = T * a.d / 4;
-  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out,
-                     residual);
-  return hipGetLastError();
-}
+
 
 }  // namespace moe

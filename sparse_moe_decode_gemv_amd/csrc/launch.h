@@ -60,7 +60,7 @@ struct LayerArgs {
   int4* chunks;           // [min(E, T*k) + T*k/32 + ns*ceil(T/32)] (expert, first position, count <= CS),
                           // CS = 32, or 64 when T*k >= 32*E;
                           // the shared expert's chunks (expert E) come last
-  int32_t* meta;          // [0]: active routed experts, [1]: chunks, [2]: T*k
+  int32_t* meta;          // [0]: active routed experts, [1]: chunks, [2]: T*k; [32]: arrivals of the top-k + sort kernel
   int32_t* sort_wc;       // [64][E] per-wave expert counts, then bases (the many-assignment sort)
   int32_t* asg;           // [T*k + ns*T] assignments grouped by expert (shared: T*k + t, last)
   uint16_t* h16;          // [T*k + ns*T][f] w_j silu(g) u per position, fp16 operand order
@@ -172,15 +172,15 @@ size_t router_partial_floats(int T, int E, int d);
 // Per chosen expert, over all its tokens: h = w_j * silu(W_g x) * (W_u x).
 hipError_t launch_gateup(const LayerArgs& a, int T, hipStream_t s);
 
-// Per chosen expert, over all its tokens: o_{t,j} = W_d h.
-hipError_t launch_down(const LayerArgs& a, int T, hipStream_t s);
+// Per chosen expert, over all its tokens: o_{t,j} = W_d h; then
+// y_t = sum_j o_{t,j} (+ o_{t,shared}) into y_out (if non-NULL) and
+// residual_t += y_t (if non-NULL), inside the same kernel for small T.
+hipError_t launch_down_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
 
 // The tile-major copies of gate, up and down (from the canonical matrices)
 // and the router's bf16 terms.
 hipError_t launch_tile_weights(const LayerArgs& a, hipStream_t s);
 
-// y_t = sum_j o_{t,j} (+ o_{t,shared}) into y_out (if non-NULL); residual_t += y_t (if non-NULL).
-hipError_t launch_combine(const LayerArgs& a, int T, float* y_out, float* residual, hipStream_t s);
 
 // LM head GEMV + argmax.
 hipError_t launch_lmhead(const uint8_t* wq, const uint16_t* ws, int V, int d, const uint16_t* x, int B,

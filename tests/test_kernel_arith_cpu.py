@@ -18,13 +18,26 @@ HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "sparse_moe_decode_gemv_amd", "csrc", "device_common.h")
 
 
+def dot2_terms(body, fn):
+    """(shift, mask, magic, pair) of each `fn((word & mask) | magic, s.pN, acc)`
+    term of a dot helper: the constants are named through vgpr_const(...),
+    the word is w, w >> n, or a name bound to w >> n."""
+    names = {m.group(1): int(m.group(2), 16) for m in re.finditer(r"(\w+) = vgpr_const\((0x[0-9A-Fa-f]+)u\)", body)}
+    shifted = {m.group(1): int(m.group(2)) for m in re.finditer(r"(\w+) = w >> (\d+);", body)}
+    out = []
+    for m in re.finditer(fn + r"\(\(+(\w+)(?: >> (\d+)\))? ?& (\w+)\) \| (\w+), s\.p(\d)", body):
+        word, sh, mask, magic, pair = m.groups()
+        shift = shifted[word] if word in shifted else (int(sh) if sh else 0)
+        assert word in shifted or word == "w", word
+        out.append((shift, names[mask], names[magic], int(pair)))
+    return out
+
+
 def kernel_constants():
     src = open(HDR).read()
     body = src[src.index("float dot8("):]
     body = body[:body.index("return acc;")]
-    pairs = []
-    for m in re.finditer(r"dot2_bf16\(\(+w(?: >> (\d+)\))? ?& (0x[0-9A-Fa-f]+)u\) \| (0x[0-9A-Fa-f]+)u, s\.p(\d)", body):
-        pairs.append((int(m.group(1) or 0), int(m.group(2), 16), int(m.group(3), 16), int(m.group(4))))
+    pairs = dot2_terms(body, "dot2_bf16")
     consts = []
     for fn, var in (("make_slice(const float v[8])", "v"), ("make_slice_bf16(uint4 q)", "x")):
         mk = src[src.index(fn):]
@@ -103,14 +116,16 @@ def fp16_constants():
     src = open(HDR).read()
     body = src[src.index("float dot8_f16("):]
     body = body[:body.index("return acc;")]
-    pairs = [(int(m.group(1) or 0), int(m.group(2), 16), int(m.group(3), 16), int(m.group(4))) for m in
-             re.finditer(r"dot2_f16\(\(+w(?: >> (\d+)\))? ?& (0x[0-9A-Fa-f]+)u\) \| (0x[0-9A-Fa-f]+)u, s\.p(\d)", body)]
+    pairs = dot2_terms(body, "dot2_f16")
     mk = src[src.index("make_slice_f16(const float v[8])"):]
     mk = mk[:mk.index("return s;")]
     found = re.findall(r"s\.p(\d) = pack_f16\(v\[\d\] \* ([0-9.]+)f, v\[\d\] \* ([0-9.]+)f\)", mk)
     assert all(a == b for _, a, b in found)
     scale = {int(p): float(a) for p, a, _ in found}
-    cm = re.search(r"s\.corr = -([0-9.]+)f \* e - ([0-9.]+)f \* o;", mk)
+    cf = src[src.index("float slice_f16_corr("):]
+    cf = cf[:cf.index("}")]
+    assert "slice_f16_corr(s.p0, s.p1, s.p2, s.p3)" in mk
+    cm = re.search(r"return -([0-9.]+)f \* e - ([0-9.]+)f \* o;", cf)
     assert len(pairs) == 4 and cm and sorted(scale) == [1, 3], "fp16 helpers no longer match the expected form"
     return pairs, scale, float(cm.group(1)), float(cm.group(2))
 
