@@ -64,9 +64,18 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   const size_t total = (size_t)V * CPR;
   const uint4* wp = reinterpret_cast<const uint4*>(wq);
 
+  // x row b enters as binary16 slices of x 2^xa[b], its largest magnitude
+  // in [2^14, 2^15): the bf16 values are exact there down to 2^-24 of that
+  // maximum, and the fp16 magic number takes one shift per dword where the
+  // bf16 one takes three.  The argmax of a row is unchanged by the factor;
+  // its maximum logit is scaled back at the end.  (Each wave's lanes cover
+  // the whole row, so the wave maximum is the row's.)
   Slice8 xs[BP][XS][4];
+  int xa[BP];
 #pragma unroll
-  for (int b = 0; b < BP; ++b)
+  for (int b = 0; b < BP; ++b) {
+    uint4 xv[XS][4];
+    uint32_t mb = 0;
 #pragma unroll
     for (int s = 0; s < XS; ++s) {
       const int cc = CPR > 64 ? 64 * s + lane : lane % CPR;
@@ -77,9 +86,24 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
         // one arm of a branch makes the other arm's write of its registers
         // wait for it: the loads would run one at a time)
         const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)min(b, B - 1) * D)[(base + 32 * j) >> 3];
-        xs[b][s][j] = make_slice_bf16(b < B ? v : make_uint4(0u, 0u, 0u, 0u));
+        xv[s][j] = b < B ? v : make_uint4(0u, 0u, 0u, 0u);
+        mb = max(mb, max(max(bf16_mag_max(xv[s][j].x), bf16_mag_max(xv[s][j].y)),
+                         max(bf16_mag_max(xv[s][j].z), bf16_mag_max(xv[s][j].w))));
       }
     }
+    xa[b] = act_exponent(wave_max_u32(mb)) + 14;
+#pragma unroll
+    for (int s = 0; s < XS; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 q = xv[s][j];
+        const float f[8] = {ldexpf(bf16_bits_to_f32(q.x & 0xFFFFu), xa[b]), ldexpf(__uint_as_float(q.x & 0xFFFF0000u), xa[b]),
+                            ldexpf(bf16_bits_to_f32(q.y & 0xFFFFu), xa[b]), ldexpf(__uint_as_float(q.y & 0xFFFF0000u), xa[b]),
+                            ldexpf(bf16_bits_to_f32(q.z & 0xFFFFu), xa[b]), ldexpf(__uint_as_float(q.z & 0xFFFF0000u), xa[b]),
+                            ldexpf(bf16_bits_to_f32(q.w & 0xFFFFu), xa[b]), ldexpf(__uint_as_float(q.w & 0xFFFF0000u), xa[b])};
+        xs[b][s][j] = make_slice_f16(f);
+      }
+  }
 
   float best[BP];
   uint32_t brow[BP];
@@ -124,7 +148,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
       // l holding row c0 / 64 + ((l >> 3) & 7)
       float z8[8];
 #pragma unroll
-      for (int n = 0; n < NL; ++n) z8[n] = dot_piece(q[n], xs[0][0], sc[n]);
+      for (int n = 0; n < NL; ++n) z8[n] = dot_piece_f16(q[n], xs[0][0], sc[n]);
       const float z = wave_sum8_scatter(z8);
       const uint32_t row = (uint32_t)(c0 / 64) + ((lane >> 3) & 7);
       if (row < (uint32_t)V && z > best[0]) best[0] = z, brow[0] = row;
@@ -134,7 +158,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
     for (int n = 0; n < NL; ++n) {
       const int s = CPR > 64 ? n % XS : 0;
 #pragma unroll
-      for (int b = 0; b < BP; ++b) acc[b] += dot_piece(q[n], xs[b][s], sc[n]);
+      for (int b = 0; b < BP; ++b) acc[b] += dot_piece_f16(q[n], xs[b][s], sc[n]);
       if (n % LPR == LPR - 1) {
         const size_t c = c0 + 64 * n + lane;
         const uint32_t row = (uint32_t)((CPR >= 64 ? c0 + 64 * n : c) / CPR);
@@ -178,8 +202,11 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   __syncthreads();
   if (!s_last) return;
   // last workgroup: reduce G keys per x row, every load issued before any
-  // is waited for
-  for (int b = 0; b < B; ++b) {
+  // is waited for; 64-bit maxima within each wave (lane shuffles), then
+  // over the 4 waves
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    if (b >= B) break;
     constexpr int KL = kLmMaxGrid / 256;
     unsigned long long kv[KL];
 #pragma unroll
@@ -190,21 +217,19 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
     unsigned long long kmax = 0;
 #pragma unroll
     for (int m = 0; m < KL; ++m) kmax = kv[m] > kmax ? kv[m] : kmax;
-    // 64-bit max over the workgroup through LDS
-    __shared__ unsigned long long s_red[256];
-    s_red[threadIdx.x] = kmax;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (threadIdx.x < w) s_red[threadIdx.x] = s_red[threadIdx.x + w] > s_red[threadIdx.x] ? s_red[threadIdx.x + w]
-                                                                                            : s_red[threadIdx.x];
-      __syncthreads();
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long t = __shfl_xor(kmax, o, 64);
+      kmax = t > kmax ? t : kmax;
     }
-    if (threadIdx.x == 0) s_best[0][0] = s_red[0];
+    if (lane == 0) s_best[wid][0] = kmax;
     __syncthreads();
     if (threadIdx.x == 0) {
-      const unsigned long long m = s_best[0][0];
+      unsigned long long m = s_best[0][0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) m = s_best[w][0] > m ? s_best[w][0] : m;
       token[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
-      if (max_logit) max_logit[b] = unordered_bits((uint32_t)(m >> 32));
+      if (max_logit) max_logit[b] = ldexpf(unordered_bits((uint32_t)(m >> 32)), -xa[b]);
     }
     __syncthreads();
   }

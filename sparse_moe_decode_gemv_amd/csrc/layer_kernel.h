@@ -127,14 +127,10 @@ __device__ __forceinline__ size_t rrec_index(int row, int rows_per_wg) {
   return (size_t)(row / rows_per_wg) * lpw * 16 + (row % rows_per_wg);
 }
 
-// h word j sits in the lines of the workgroup that produced it: wpw words
-// per workgroup, lpw lines each.  A word carries 3 binary16 values of the
-// producer's slices (8 values each, in slice order) under a 16-bit tag.
+// Slice word j (= 5 * slice + field, slices in h order) sits in the lines of
+// the workgroup that produced it: wpw words per workgroup, lpw lines each.
 __device__ __forceinline__ size_t hrec_index(int j, int wpw, int lpw) {
   return (size_t)(j / wpw) * lpw * 16 + (j % wpw);
-}
-__device__ __forceinline__ unsigned long long h_word(unsigned tag, uint32_t lo, uint32_t hi16) {
-  return ((unsigned long long)(tag & 0xFFFFu) << 48) | ((unsigned long long)(hi16 & 0xFFFFu) << 32) | lo;
 }
 
 // D hidden, F expert width, KP expert slots (top_k, plus one with a shared
@@ -176,9 +172,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   __shared__ float s_lg[64 * EPL];
   __shared__ uint32_t s_top[64];
   __shared__ float s_z[4];
-  constexpr int HPW = ROWS_G;            // h values (binary16) published per workgroup
-  constexpr int HWPW = (HPW + 2) / 3;    // 64-bit words per workgroup, 3 values each
-  __shared__ uint32_t s_pub[(3 * HWPW + 1) / 2];
+  __shared__ unsigned s_pub[ROWS_G / 8 * 5];
 
   __shared__ __align__(16) uint16_t s_x[D];
   __shared__ __align__(16) float s_r[NORM ? D : 4];  // the residual r_l (stack)
@@ -499,33 +493,27 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     }
   }
   __syncthreads();
-  // publish this workgroup's rows as the binary16 values of ready-made dot
-  // slices (one per 8 consecutive h values, the 4 pairs p0..p3 of
-  // make_slice_f16 or make_slice_f16_raw; the reader recomputes the offset
-  // correction), 3 values and the tag per 64-bit word; the workgroup's words
-  // fill its own 128-byte line(s), written by consecutive lanes of one store
-  // instruction
+  // publish this workgroup's rows as ready-made fp16 dot slices, one per 8
+  // consecutive h values, every 64-bit word carrying the tag; the
+  // workgroup's words fill its own 128-byte line(s), written by consecutive
+  // lanes of one store instruction
   constexpr int SPW = ROWS_G / 8;          // slices per workgroup
-  constexpr int LPW = (HWPW + 15) / 16;    // 128-byte lines per workgroup
+  constexpr int WPW = SPW * 5;             // words per workgroup
+  constexpr int LPW = (WPW + 15) / 16;     // 128-byte lines per workgroup
   const bool producer = blockIdx.x * 4 < nslots * wpe;
   if (producer && threadIdx.x < SPW) {
     float hv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) hv[e] = s_hv[8 * threadIdx.x + e];
     const Slice8 sl = FP4 ? make_slice_f16_raw(hv) : make_slice_f16(hv);
-    s_pub[4 * threadIdx.x + 0] = sl.p0, s_pub[4 * threadIdx.x + 1] = sl.p1;
-    s_pub[4 * threadIdx.x + 2] = sl.p2, s_pub[4 * threadIdx.x + 3] = sl.p3;
+    s_pub[5 * threadIdx.x + 0] = sl.p0, s_pub[5 * threadIdx.x + 1] = sl.p1, s_pub[5 * threadIdx.x + 2] = sl.p2;
+    s_pub[5 * threadIdx.x + 3] = sl.p3, s_pub[5 * threadIdx.x + 4] = __float_as_uint(sl.corr);
   }
-  if (producer && threadIdx.x >= SPW * 4 && threadIdx.x < (3 * HWPW + 1) / 2) s_pub[threadIdx.x] = 0u;  // spare values
   __syncthreads();
   if (producer && wid == 0) {
     unsigned long long* line = a.hrec + (size_t)blockIdx.x * LPW * 16;  // producer index == workgroup index
-    const uint16_t* pv = reinterpret_cast<const uint16_t*>(s_pub);
-    for (int w0 = 0; w0 < HWPW; w0 += 64) {
-      const int w = w0 + lane;
-      if (w < HWPW)
-        store_coherent(line + w, h_word(tag, (uint32_t)pv[3 * w] | ((uint32_t)pv[3 * w + 1] << 16), pv[3 * w + 2]));
-    }
+    for (int w0 = 0; w0 < WPW; w0 += 64)
+      if (w0 + lane < WPW) store_coherent(line + w0 + lane, ((unsigned long long)tag << 32) | s_pub[w0 + lane]);
   }
 
   // ---------------------------------------------------------------- down prefetch
@@ -589,36 +577,29 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   // all k*F/8 slices straight into LDS; a word is taken once it carries the
   // tag, and later polls re-read only the words still missing
   {
-    // LDS position of slice sl (in h order) as the down phase reads it
-    auto slice_pos = [&](int sl) -> int {
+    constexpr int NR = (KP * F / 8 * 5 + 255) / 256;
+    const int nw = nslots * (F / 8) * 5;  // slice words; word j = 5 * slice + field
+    unsigned missing = 0;
+    unsigned dst[NR];  // where word j goes in LDS (s_dyn words)
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int jw = threadIdx.x + 256 * m;
+      missing |= (jw < nw ? 1u : 0u) << m;
+      const int sl = jw / 5, fld = jw - 5 * sl;
       const int slot = sl / (F / 8), sidx = sl % (F / 8);
       const int flat = slot * CPRF + 4 * (sidx / 16) + (sidx & 3), jg = (sidx >> 2) & 3;  // piece, group of the slice
-      return P >= 64 ? ((flat / 64) * 4 + jg) * 64 + flat % 64 : jg * P + flat;
-    };
-    constexpr int NR = (KP * F / ROWS_G * HWPW + 255) / 256;
-    const int nw = nslots * (F / ROWS_G) * HWPW;  // words of all producers
-    uint16_t* s_h16 = reinterpret_cast<uint16_t*>(s_slp);
-    unsigned missing = 0;
-#pragma unroll
-    for (int m = 0; m < NR; ++m) missing |= (threadIdx.x + 256 * m < nw ? 1u : 0u) << m;
-    const uint16_t want = (uint16_t)(tag + io.tag_skew);
+      const int pos = P >= 64 ? ((flat / 64) * 4 + jg) * 64 + flat % 64 : jg * P + flat;
+      dst[m] = fld < 4 ? 4 * pos + fld : 4 * KP * F / 8 + pos;
+    }
     for (unsigned spin = 0;; ++spin) {
       unsigned long long r[NR];
 #pragma unroll
       for (int m = 0; m < NR; ++m)
-        r[m] = (missing >> m) & 1u ? load_coherent(a.hrec + hrec_index(threadIdx.x + 256 * m, HWPW, LPW)) : 0ull;
+        r[m] = (missing >> m) & 1u ? load_coherent(a.hrec + hrec_index(threadIdx.x + 256 * m, WPW, LPW)) : 0ull;
 #pragma unroll
       for (int m = 0; m < NR; ++m) {
-        if (((missing >> m) & 1u) && (uint16_t)(r[m] >> 48) == want) {
-          const int jw = threadIdx.x + 256 * m, g = jw / HWPW, w = jw - g * HWPW;
-#pragma unroll
-          for (int c = 0; c < 3; ++c) {
-            const int v = 3 * w + c;  // value v of producer g
-            if (v < HPW) {
-              const int hh = g * HPW + v;  // value hh in h order: slice hh / 8, position hh % 8 in p0..p3
-              s_h16[8 * slice_pos(hh >> 3) + (hh & 7)] = (uint16_t)(r[m] >> (16 * c));
-            }
-          }
+        if (((missing >> m) & 1u) && (uint32_t)(r[m] >> 32) == tag + io.tag_skew) {
+          s_dyn[dst[m]] = (uint32_t)r[m];
           missing &= ~(1u << m);
         }
       }
@@ -626,14 +607,6 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
       if (spin + 1 >= io.spin_limit) {
         if (threadIdx.x == 0) atomicOr(a.error, 2u);
         break;
-      }
-    }
-    if constexpr (!FP4) {  // the offset correction of each slice, from its binary16 values
-      __syncthreads();
-      for (int sl = threadIdx.x; sl < nslots * (F / 8); sl += 256) {
-        const int pos = slice_pos(sl);
-        const uint4 pv = s_slp[pos];
-        s_slc[pos] = slice_f16_corr(pv.x, pv.y, pv.z, pv.w);
       }
     }
     __syncthreads();
