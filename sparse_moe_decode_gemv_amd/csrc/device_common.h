@@ -158,6 +158,11 @@ __device__ __forceinline__ Slice8 make_slice_f16(const float v[8]) {
   return s;
 }
 
+// Binary16 operands built from bf16 activations carry x 2^(a + kXf16Shift),
+// a from the row's largest magnitude (act_exponent: that magnitude times 2^a
+// lies in [1, 2)), so the largest lies in [2^14, 2^15).
+constexpr int kXf16Shift = 14;
+
 // acc + sum_e (1024+u_e or 1024+16u_e) * (h_e or h_e/16); started from
 // s.corr this is sum_e (u_e - 8) h_e.
 __device__ __forceinline__ float dot8_f16(uint32_t w, const Slice8& s, float acc) {

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
                          max(bf16_mag_max(xv[s][j].z), bf16_mag_max(xv[s][j].w))));
       }
     }
-    xa[b] = act_exponent(wave_max_u32(mb)) + 14;
+    xa[b] = act_exponent(wave_max_u32(mb)) + kXf16Shift;
 #pragma unroll
     for (int s = 0; s < XS; ++s)
 #pragma unroll

@@ -236,16 +236,46 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     const uint64_t s = (((uint64_t)v.y << 32) | v.x) >> (8 * ((c & 3) >> 1));
     return make_uint2((uint32_t)s, (uint32_t)(s >> 32));
   };
+  // The slot's loads.  With x from the caller, as 32-bit lane offsets from
+  // the matrices' uniform bases (the address arithmetic sits between the
+  // top-k and the loads): piece c at byte 16 c, its scales at (c & ~3)
+  // times the scale bytes per 32 elements -- 2 (int4, NVFP4: the group's 8
+  // E4M3 bytes start there) or 1 (MXFP4) -- since pieces 4i .. 4i+3 of a row
+  // hold its groups 4i .. 4i+3 (CPR is a multiple of 4).  Measured in one
+  // process: 11.53 -> 11.11 us per step there, but 12.25 -> 12.49 us per
+  // layer in the pre-normed stack kernel and 12.42 -> 12.99 in the
+  // persistent one, whose schedules the compiler builds differently; those
+  // keep the index form.
+  static_assert(CPR % 4 == 0, "pieces of a row come in fours");
   auto load_mats = [&](const uint8_t* gq8, const uint16_t* gsb, const uint8_t* uq8, const uint16_t* usb) {
-    const uint4* gp = reinterpret_cast<const uint4*>(gq8);
-    const uint4* up = reinterpret_cast<const uint4*>(uq8);
+    if constexpr (MODE != kStepX) {
+      const uint4* gp = reinterpret_cast<const uint4*>(gq8);
+      const uint4* up = reinterpret_cast<const uint4*>(uq8);
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const int c = c0 + 64 * n + lane;
+        qg[n] = gp[c];
+        qu[n] = up[c];
+        sg[n] = load_scales(gsb, (size_t)(c / CPR), CPR, c % CPR);
+        su[n] = load_scales(usb, (size_t)(c / CPR), CPR, c % CPR);
+      }
+      return;
+    }
+    constexpr uint32_t SB = (FP4 && !NV) ? 1u : 2u;
+    const uint8_t* gs8 = reinterpret_cast<const uint8_t*>(gsb);
+    const uint8_t* us8 = reinterpret_cast<const uint8_t*>(usb);
 #pragma unroll
     for (int n = 0; n < NL; ++n) {
-      const int c = c0 + 64 * n + lane;
-      qg[n] = gp[c];
-      qu[n] = up[c];
-      sg[n] = load_scales(gsb, (size_t)(c / CPR), CPR, c % CPR);
-      su[n] = load_scales(usb, (size_t)(c / CPR), CPR, c % CPR);
+      const uint32_t c = (uint32_t)(c0 + 64 * n + lane), so = SB * (c & ~3u);
+      qg[n] = *reinterpret_cast<const uint4*>(gq8 + 16u * c);
+      qu[n] = *reinterpret_cast<const uint4*>(uq8 + 16u * c);
+      if constexpr (FP4 && !NV) {
+        sg[n] = make_uint2(*reinterpret_cast<const uint32_t*>(gs8 + so), 0u);
+        su[n] = make_uint2(*reinterpret_cast<const uint32_t*>(us8 + so), 0u);
+      } else {
+        sg[n] = *reinterpret_cast<const uint2*>(gs8 + so);
+        su[n] = *reinterpret_cast<const uint2*>(us8 + so);
+      }
     }
   };
   auto load_gate = [&](int e_raw) {
