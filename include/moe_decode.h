@@ -291,6 +291,20 @@ moe_status moe_int4_repack(const uint8_t* src, uint8_t* dst, int64_t rows, int32
  * achieves on this GPU, the "achievable" figure beside the 8 TB/s peak. */
 moe_status moe_decode_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* Diagnostic for measurements: the phase timestamps of the last int4
+ * single-launch layer call (one token through one layer, the chain of
+ * phases -- router, logit exchange, top-k, gate/up, h exchange, down -- of
+ * "Flint 40B: Best Mid Sized LLM", transcript 02:35, in one kernel).
+ * Recorded only by the library built with MOE_PHASE_TRACE
+ * (`python -m sparse_moe_decode_gemv_amd.build --phase-trace`, a separate
+ * libmoe_decode_phase.so); every other build returns MOE_ERR_UNSUPPORTED.
+ * Copies min(n, 1024 * 16) values [workgroup][16] of the GPU's 100 MHz
+ * real-time counter, written by thread 0 of each workgroup at 11 marked
+ * points (slots 0..10; slot 2 by the router workgroups only).  Synchronous:
+ * the caller synchronizes the stream of that call first.
+ *   host_out  (host) uint64 [n] */
+moe_status moe_decode_phase_trace(uint64_t* host_out, int64_t n);
+
 /* Free the host handle (no device memory is touched). NULL is ignored. */
 void moe_decode_destroy(moe_handle h);
 

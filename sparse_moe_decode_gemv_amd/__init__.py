@@ -36,7 +36,7 @@ EXPORTED = (
     "moe_decode_workspace_bytes", "moe_decode_init", "moe_decode_forward", "moe_decode_stack_forward",
     "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
     "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit", "lmhead_int4_argmax_noalloc",
-    "moe_decode_stack_forward_ex", "moe_decode_read_probe", "moe_int4_repack",
+    "moe_decode_stack_forward_ex", "moe_decode_read_probe", "moe_int4_repack", "moe_decode_phase_trace",
 )
 MOE_STACK_PERSISTENT = 1
 DEFAULT_WAIT_POLLS = 1 << 21
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.moe_int4_repack.argtypes = [p, p, ctypes.c_int64, i32, p]
         L.moe_decode_read_probe.restype = i32
         L.moe_decode_read_probe.argtypes = [p, sz, p, p]
+        L.moe_decode_phase_trace.restype = i32
+        L.moe_decode_phase_trace.argtypes = [p, ctypes.c_int64]
         L.moe_decode_expert_groups.restype = i32
         L.moe_decode_expert_groups.argtypes = [p, i32, p, p, p, p, p]
         L.moe_decode_destroy.restype = None
@@ -181,6 +183,11 @@ def moe_int4_repack(src, dst, rows: int, K: int, stream=None) -> None:
 
 def moe_decode_read_probe(buf, nbytes: int, sink, stream=None) -> None:
     _check(lib().moe_decode_read_probe(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream)), "moe_decode_read_probe")
+
+
+def moe_decode_phase_trace(host_out) -> None:
+    """host_out: a C-contiguous numpy uint64 array (filled in place)."""
+    _check(lib().moe_decode_phase_trace(host_out.ctypes.data, int(host_out.size)), "moe_decode_phase_trace")
 
 
 def moe_decode_expert_groups(handle: int, T: int, offsets=None, assignments=None, active=None, n_active=None,

@@ -1,7 +1,9 @@
 """Build the HIP library in place: sparse_moe_decode_gemv_amd/libmoe_decode.so (gfx950).
 
 Each source compiles to an object in parallel, then one link.  Always
-recompiles.  Run as `python -m sparse_moe_decode_gemv_amd.build`.
+recompiles.  Run as `python -m sparse_moe_decode_gemv_amd.build`; with
+`--phase-trace`, the diagnostic variant libmoe_decode_phase.so instead, whose
+single-launch layer kernel records phase timestamps (MOE_PHASE_TRACE).
 """
 from __future__ import annotations
 
@@ -28,23 +30,29 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    subprocess.check_call([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+PHASE_LIB = os.path.join(HERE, "libmoe_decode_phase.so")
+
+
+def _compile(src: str, obj_dir: str, extra: tuple) -> str:
+    obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    subprocess.check_call([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, phase_trace: bool = False) -> str:
+    obj_dir = os.path.join(OBJ, "phase") if phase_trace else OBJ
+    extra = ("-DMOE_PHASE_TRACE",) if phase_trace else ()
+    lib = PHASE_LIB if phase_trace else LIB
+    os.makedirs(obj_dir, exist_ok=True)
     if verbose:
-        print(HIPCC, " ".join(FLAGS), "-c", SOURCES, flush=True)
+        print(HIPCC, " ".join(FLAGS + list(extra)), "-c", SOURCES, flush=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs])
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, extra), SOURCES))
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs])
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, phase_trace="--phase-trace" in sys.argv[1:])
     sys.exit(0)

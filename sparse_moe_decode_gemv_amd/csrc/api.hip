@@ -555,4 +555,15 @@ moe_status lmhead_int4_argmax_noalloc(const uint8_t* w_q, const uint16_t* w_s, i
   return MOE_OK;
 }
 
+moe_status moe_decode_phase_trace(uint64_t* host_out, int64_t n) {
+  if (!host_out) return MOE_ERR_NULL;
+  if (n < 1) return MOE_ERR_SHAPE;
+#ifdef MOE_PHASE_TRACE
+  return moe::phase_trace_copy(reinterpret_cast<unsigned long long*>(host_out), (size_t)n) == hipSuccess ? MOE_OK
+                                                                                                       : MOE_ERR_HIP;
+#else
+  return MOE_ERR_UNSUPPORTED;
+#endif
+}
+
 }  // extern "C"

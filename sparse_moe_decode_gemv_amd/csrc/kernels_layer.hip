@@ -58,6 +58,13 @@ hipError_t launch_stack_fused(const StackArgs& a, const StackShape& sh, hipStrea
   return launch_stack_int4(a, sh, G, s);
 }
 
+#ifdef MOE_PHASE_TRACE
+hipError_t phase_trace_copy(unsigned long long* host, size_t n) {
+  if (n > (size_t)kMaxFusedGrid * kPhaseSlots) n = (size_t)kMaxFusedGrid * kPhaseSlots;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_ts), n * sizeof(unsigned long long), 0, hipMemcpyDeviceToHost);
+}
+#endif
+
 hipError_t launch_layer_fused(const FusedArgs& a, int d, int f, hipStream_t s) {
   const int G = fused_grid();
   if (G <= 0 || !fits(d, f, a.E, a.k + a.ns, G)) return hipErrorInvalidValue;

@@ -73,6 +73,12 @@ struct LayerArgs {
 };
 
 constexpr int kMaxFusedGrid = 1024;
+constexpr int kPhaseSlots = 16;  // phase timestamps per workgroup (diagnostic build, layer_kernel.h)
+#ifdef MOE_PHASE_TRACE
+// Copies the n first phase timestamps of the last int4 single-launch call
+// ([workgroup][kPhaseSlots] 100 MHz counter values) to host memory.
+hipError_t phase_trace_copy(unsigned long long* host, size_t n);
+#endif
 constexpr int kFusedGridCUs = 256;  // compute units the single-launch kernel is sized for (MI355X)
 constexpr int kMaxGroupedGrid = 512;  // expert kernels: 2 resident workgroups on each of 256 CUs
 constexpr int kMaxAssignments = MOE_MAX_TOKENS * MOE_MAX_TOPK;  // largest T*k

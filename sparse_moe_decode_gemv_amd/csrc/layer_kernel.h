@@ -55,6 +55,24 @@
 
 namespace moe {
 
+// Phase timestamps, a diagnostic build only (-DMOE_PHASE_TRACE): thread 0
+// of every workgroup stores the 100 MHz real-time counter at the marked
+// points of the step (slots 0..10 of its 16); moe_decode_phase_trace copies
+// the last call's values out.  Without the macro the marks compile to nothing.
+#ifdef MOE_PHASE_TRACE
+// one array per translation unit (one per weight format); the int4 one is
+// read by phase_trace_copy
+static __device__ unsigned long long g_phase_ts[kMaxFusedGrid * kPhaseSlots];
+#define MOE_PHASE(i)                                                                                  \
+  do {                                                                                                \
+    if (threadIdx.x == 0) g_phase_ts[blockIdx.x * kPhaseSlots + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define MOE_PHASE(i) \
+  do {               \
+  } while (0)
+#endif
+
 // Logits are published one 128-byte line per workgroup: words written by
 // workgroups on different XCDs into one line serialize at the memory side
 // (measured: all-to-all detection 2.2 us packed vs 1.3 us one line each).
@@ -184,6 +202,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   const int E = a.E, k = a.k;
   const unsigned tag = a.epoch[blockIdx.x] + 1u;  // this workgroup's own call count
   const float bias = (a.router_b && wg < E) ? a.router_b[wg] : 0.f;
+  MOE_PHASE(0);
 
   // the activation in LDS: bf16 from the caller, or the normalized
   // residual.  Copied once at the start, so that no later phase issues a
@@ -381,6 +400,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     if (lane == 0) s_xm[wid] = mb;
     __syncthreads();
   }
+  MOE_PHASE(1);  // x (or the normalized residual) in LDS
   // h goes to the down phase as h 2^(2 ea) in binary16, ea from the largest
   // |x| (the same in every workgroup): exact scalings, any magnitude of x
   const int ea = act_exponent(max(max(s_xm[0], s_xm[1]), max(s_xm[2], s_xm[3])));
@@ -407,6 +427,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     __syncthreads();
     if (threadIdx.x < 4 && blockIdx.x * 4 + (int)threadIdx.x < E)
       store_tagged(a.logits + (size_t)blockIdx.x * kLineWords64 + threadIdx.x, s_part[threadIdx.x], tag);
+    MOE_PHASE(2);  // router workgroups: logits stored
   }
 
   // ---------------------------------------------------------------- select
@@ -421,6 +442,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     for (int i = 0; i < EPL; ++i) s_lg[lane + 64 * i] = v0[i];
   }
   __syncthreads();
+  MOE_PHASE(3);  // every wave has the logits
   int se = 0;     // lanes 0..k-1: the chosen experts, larger logit first
   float sw = 0.f; // their weights
   const int gsl = __builtin_amdgcn_readfirstlane(max(gslot, 0));  // this wave's slot (uniform)
@@ -433,6 +455,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     const float lt = t < E ? s_lg[t] : -INFINITY;
     const uint32_t key = t < E ? ((ordered_bits(lt) & ~imask) | (imask - (uint32_t)t)) : 0u;
     const uint32_t top = block_top16(key, lane, wid, s_top);
+    MOE_PHASE(4);
     // two of the k + 1 largest keys that agree above the index bits may be
     // out of order: then the exact selection below decides
     const uint32_t prev = dpp_u<kDppShr1>(top);
@@ -440,6 +463,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     if (fast) {
       se = lane < k ? (int)(imask - (top & imask)) : 0;
       if (has_gate && !shared_slot) load_gate(__builtin_amdgcn_readlane(se, gsl));
+      MOE_PHASE(5);  // this wave's gate/up loads issued
       // weights while the loads fly: lane 0 holds the largest logit
       const float l = s_lg[se];
       const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 0));
@@ -479,6 +503,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     }
   }
   __syncthreads();
+  MOE_PHASE(6);
 
   // ---------------------------------------------------------------- gate/up + SwiGLU
   if (has_gate) {
@@ -523,6 +548,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     }
   }
   __syncthreads();
+  MOE_PHASE(7);  // gate/up and SwiGLU done
   // publish this workgroup's rows as ready-made fp16 dot slices, one per 8
   // consecutive h values, every 64-bit word carrying the tag; the
   // workgroup's words fill its own 128-byte line(s), written by consecutive
@@ -545,6 +571,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     for (int w0 = 0; w0 < WPW; w0 += 64)
       if (w0 + lane < WPW) store_coherent(line + w0 + lane, ((unsigned long long)tag << 32) | s_pub[w0 + lane]);
   }
+  MOE_PHASE(8);  // h published
 
   // ---------------------------------------------------------------- down prefetch
   // issued now so that the 4.7 MB of down pieces stream in while the h
@@ -595,7 +622,10 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   }
 
   // the next layer's router rows (a persistent stack): loaded while this
-  // layer's h is exchanged, ready when its activation is
+  // layer's h is exchanged, ready when its activation is.  (With one launch
+  // per layer, loading them here only to warm the caches for the next
+  // launch measured slower: 12.23 -> 12.47 us per layer, the extra loads
+  // completing ahead of the h polls.)
   if constexpr (MODE == kStepChain)
     if (io.next_router && blockIdx.x * 4 < io.next_E && wg < io.next_E) {
       const float4* wr = reinterpret_cast<const float4*>(io.next_router + (size_t)wg * D);
@@ -640,6 +670,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
       }
     }
     __syncthreads();
+    MOE_PHASE(9);  // all h in LDS
   }
 
   // ---------------------------------------------------------------- down + combine
@@ -686,6 +717,7 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
       }
     }
   }
+  MOE_PHASE(10);
   if (threadIdx.x == 0) a.epoch[blockIdx.x] = tag;
   return tag;
 }

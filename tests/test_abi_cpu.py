@@ -129,6 +129,16 @@ def test_forward_and_stack_reject_null_handles():
     M.moe_decode_destroy(None)  # ignored
 
 
+def test_phase_trace_only_in_the_diagnostic_build():
+    """The product library records no phase timestamps: the call says so
+    (and checks its arguments first); no GPU work is involved."""
+    L = M.lib()
+    out = (ctypes.c_uint64 * 16)()
+    assert L.moe_decode_phase_trace(None, 16) == M.MOE_ERR_NULL
+    assert L.moe_decode_phase_trace(out, 0) == M.MOE_ERR_SHAPE
+    assert L.moe_decode_phase_trace(out, 16) == M.MOE_ERR_UNSUPPORTED
+
+
 def test_lmhead_validation_codes():
     L = M.lib()
     ws = M.lmhead_int4_argmax_workspace_bytes(131072, 2048, 8)
