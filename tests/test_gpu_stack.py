@@ -135,3 +135,55 @@ def test_stack_of_zero_layers_keeps_the_residual():
     r, _, yt, _ = run_stack(layers_np, cfg, X0)
     assert np.array_equal(r, F.bf16_to_f64(X0).astype(np.float32))
     assert np.all(yt == 0)
+
+
+def test_flagship_stack_all_49_layers_graph_and_persistent():
+    """The whole 49-layer stack at the flagship shape, launched as the bench
+    times it: one launch per layer captured in a HIP graph (three replays,
+    with eager work between them, each bit-identical to the eager call) and
+    the persistent launch (bit-identical too); every layer of the eager call
+    checked against the oracle from the GPU's own x_l, and no bounded wait
+    of any layer gave up."""
+    import torch
+    cfg = synth.STACK
+    L = cfg.layers
+    layers_np = [synth.make_layer(cfg, 1, l) for l in range(L)]
+    layers_o = [OM.Layer.from_dict(l) for l in layers_np]
+    X0 = tokens(cfg, layers_o[0], 1, 1)
+    dev = device()
+    Ls = [M.MoELayer.create(M.upload(l, dev), cfg.d, cfg.f, cfg.E, cfg.k, 1, 1) for l in layers_np]
+    hs = [h.handle for h in Ls]
+    base = torch.from_numpy(F.bf16_to_f64(X0).astype(np.float32)).to(dev)
+    xt = torch.zeros((L, 1, cfg.d), dtype=torch.int16, device=dev)
+    yt = torch.full((L, 1, cfg.d), float("nan"), dtype=torch.float32, device=dev)
+    it = torch.full((L, 1, cfg.k), -1, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream()
+    r = base.clone()
+    M.moe_decode_stack_forward(hs, r, 1, EPS, xt, yt, it, s)
+    s.synchronize()
+    r_eager = r.cpu().numpy()
+    check_teacher_forced(layers_o, cfg, X0, r_eager, xt.cpu().numpy().view(np.uint16), yt.cpu().numpy(),
+                         it.cpu().numpy())
+    rg = torch.empty_like(base)
+    with torch.cuda.stream(s):
+        rg.copy_(base)
+        M.moe_decode_stack_forward(hs, rg, 1, EPS, None, None, None, s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        rg.copy_(base)
+        M.moe_decode_stack_forward(hs, rg, 1, EPS, None, None, None, s)
+    for rep in range(3):
+        rg.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(rg.cpu().numpy(), r_eager), f"graph replay {rep}"
+    rp = base.clone()
+    M.moe_decode_stack_forward_ex(hs, rp, 1, EPS, None, None, None, M.MOE_STACK_PERSISTENT, s)
+    s.synchronize()
+    assert np.array_equal(rp.cpu().numpy(), r_eager), "persistent launch"
+    for l, h in enumerate(Ls):
+        assert h.error_flags() == 0, f"layer {l}"
+    del g
+    for h in Ls:
+        h.close()
