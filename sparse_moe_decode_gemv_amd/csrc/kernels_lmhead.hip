@@ -64,6 +64,43 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
   const size_t total = (size_t)V * CPR;
   const uint4* wp = reinterpret_cast<const uint4*>(wq);
 
+  // Tiles are dealt round-robin to the waves.  Every load is unconditional,
+  // so the compiler's wait counts stay exact: in the last tile, pieces past
+  // the matrix read its last piece (their rows are >= V and are dropped
+  // below).  A tile's base is uniform (scalar registers) and lanes add
+  // 32-bit offsets.  The 4 scales of piece c (pieces 4i .. 4i+3 of a row
+  // hold the 4 groups 4i .. 4i+3) start at scale c & ~3.
+  static_assert(CPR % 4 == 0, "pieces of a row come in fours");
+  const size_t ntiles = (total + 64 * NL - 1) / (64 * NL), stride = (size_t)gridDim.x * 4;
+  const size_t nfull = total / (64 * NL);
+  auto load_tile = [&](size_t t, uint4 (&q)[NL], uint2 (&sc)[NL]) {
+    const uint4* tq = wp + t * 64 * NL;
+    const uint16_t* ts = ws + t * 64 * NL;
+    if (t < nfull) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const uint32_t c = 64 * n + lane;
+        q[n] = tq[c];
+        sc[n] = *reinterpret_cast<const uint2*>(ts + (c & ~3u));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const uint32_t c = (uint32_t)min((size_t)(64 * n + lane), total - 1 - t * 64 * NL);
+        q[n] = tq[c];
+        sc[n] = *reinterpret_cast<const uint2*>(ts + (c & ~3u));
+      }
+    }
+  };
+  // This wave's first tile is requested before x: the two round trips
+  // overlap instead of following each other.  (The wave index goes through
+  // readfirstlane so that the tile sequence is known to be uniform: scalar
+  // loop control.)
+  uint4 q[NL];
+  uint2 sc[NL];
+  const size_t t0 = (size_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wid);
+  if (t0 < ntiles) load_tile(t0, q, sc);
+
   // x row b enters as binary16 slices of x 2^xa[b], its largest magnitude
   // in [2^14, 2^15): the bf16 values are exact there down to 2^-24 of that
   // maximum, and the fp16 magic number takes one shift per dword where the
@@ -110,34 +147,6 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
 #pragma unroll
   for (int b = 0; b < BP; ++b) best[b] = -INFINITY, brow[b] = 0xFFFFFFFFu;
 
-  // Tiles are dealt round-robin to the waves.  Every load is unconditional,
-  // so the compiler's wait counts stay exact: in the last tile, pieces past
-  // the matrix read its last piece (their rows are >= V and are dropped
-  // below).  A tile's base is uniform (scalar registers) and lanes add
-  // 32-bit offsets.  The 4 scales of piece c (pieces 4i .. 4i+3 of a row
-  // hold the 4 groups 4i .. 4i+3) start at scale c & ~3.
-  static_assert(CPR % 4 == 0, "pieces of a row come in fours");
-  const size_t ntiles = (total + 64 * NL - 1) / (64 * NL), stride = (size_t)gridDim.x * 4;
-  const size_t nfull = total / (64 * NL);
-  auto load_tile = [&](size_t t, uint4 (&q)[NL], uint2 (&sc)[NL]) {
-    const uint4* tq = wp + t * 64 * NL;
-    const uint16_t* ts = ws + t * 64 * NL;
-    if (t < nfull) {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const uint32_t c = 64 * n + lane;
-        q[n] = tq[c];
-        sc[n] = *reinterpret_cast<const uint2*>(ts + (c & ~3u));
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const uint32_t c = (uint32_t)min((size_t)(64 * n + lane), total - 1 - t * 64 * NL);
-        q[n] = tq[c];
-        sc[n] = *reinterpret_cast<const uint2*>(ts + (c & ~3u));
-      }
-    }
-  };
   auto dot_tile = [&](size_t t, const uint4 (&q)[NL], const uint2 (&sc)[NL]) {
     const size_t c0 = t * 64 * NL;
     float acc[BP];
@@ -171,13 +180,9 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ wq, 
       }
     }
   };
-  // The wave index goes through readfirstlane so that the tile sequence is
-  // known to be uniform (scalar loop control).
-  uint4 q[NL];
-  uint2 sc[NL];
-  for (size_t t = (size_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wid); t < ntiles; t += stride) {
-    load_tile(t, q, sc);
+  for (size_t t = t0; t < ntiles; t += stride) {
     dot_tile(t, q, sc);
+    if (t + stride < ntiles) load_tile(t + stride, q, sc);  // uniform branch
   }
 
   // wave argmax, then across the 4 waves through LDS
