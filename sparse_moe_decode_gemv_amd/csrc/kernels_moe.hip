@@ -929,6 +929,19 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
       const int tok = asg0 < Tk ? asg0 / k : asg0 - Tk;  // shared-expert assignments: Tk + token
       rows[m] = a.xp + (size_t)tok * D;
     }
+    // the epilogue's per-token values (slot weight, activation exponent) of
+    // this lane's output tokens 4q+v of each tile, fetched while the K loop
+    // runs (rows past the chunk repeat its last assignment)
+    float wjv[NTT][4];
+    int eav[NTT][4];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int asg = a.asg[it.p0 + min(16 * tt + 4 * q + v, it.n - 1)];
+        wjv[tt][v] = asg < Tk ? a.sel_w[asg] : 1.f;
+        eav[tt][v] = a.xexp[asg < Tk ? asg / k : asg - Tk];
+      }
     f32x4_t acc[2][NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -945,12 +958,9 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int pt = 16 * tt + 4 * q + v;
         if (pt < it.n) {
-          const int asg = a.asg[it.p0 + pt];
-          const float wj = asg < Tk ? a.sel_w[asg] : 1.f;
-          const int ea = a.xexp[asg < Tk ? asg / k : asg - Tk];
           // gate and up hold 2^ea g and 2^ea u: h 2^(2 ea) with silu of the true g
           const float gs = acc[0][tt][v];
-          const float h = wj * (gs / (1.0f + expf(-ldexpf(gs, -ea)))) * acc[1][tt][v];
+          const float h = wjv[tt][v] * (gs / (1.0f + expf(-ldexpf(gs, -eav[tt][v])))) * acc[1][tt][v];
           a.h16[(size_t)(it.p0 + pt) * f + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
       }
