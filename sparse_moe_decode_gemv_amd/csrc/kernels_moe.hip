@@ -854,21 +854,32 @@ __device__ __forceinline__ void block_mfma(f32x4_t (&acc)[2][NTT], const OpTile<
 // T = 2048.)  Every global load is unconditional (rows past the chunk
 // are clamped to a real one and their outputs dropped), so the compiler's
 // wait counts stay exact.
+template <int K>
+constexpr int kloop_g() { return K / 128 < 2 ? K / 128 : 2; }  // weight blocks per burst
+
+// The first burst of the two weight tiles, requested by the caller as soon
+// as the item is known (the weights depend only on the expert and the row
+// group, not on the tokens).
+template <int K, int FMT>
+__device__ __forceinline__ void k_loop_first(WBlk (&w0)[kloop_g<K>()][2], const uint4* const (&wtq)[2],
+                                             const uint2* const (&wts)[2], int lane) {
+#pragma unroll
+  for (int i = 0; i < kloop_g<K>(); ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) w0[i][m] = wload<FMT>(wtq[m], wts[m], i, lane);
+}
+
 template <int K, int NTT, int FMT>
 __device__ __forceinline__ void k_loop(f32x4_t (&acc)[2][NTT], OpTile<NTT>* tiles,
                                        const uint16_t* const (&op_rows)[NTT / 2], const uint4* const (&wtq)[2],
-                                       const uint2* const (&wts)[2], int tid, int lane, uint32_t magic) {
+                                       const uint2* const (&wts)[2], WBlk (&w)[2][kloop_g<K>()][2], int tid,
+                                       int lane, uint32_t magic) {
   constexpr int NBLK = K / 128;
-  constexpr int G = NBLK < 2 ? NBLK : 2;    // weight blocks per burst
+  constexpr int G = kloop_g<K>();           // weight blocks per burst (w[0]: requested by the caller)
   constexpr int SX = NBLK < 4 ? NBLK : 4;   // operand blocks in flight
   StageRegs<NTT / 2> sx[SX];
 #pragma unroll
   for (int i = 0; i < SX; ++i) sx[i] = stage_load(i, op_rows, tid);
-  WBlk w[2][G][2];
-#pragma unroll
-  for (int i = 0; i < G; ++i)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) w[0][i][m] = wload<FMT>(wtq[m], wts[m], i, lane);
   stage_store(tiles[0], sx[0], tid);
   sx[0] = stage_load(min(SX, NBLK - 1), op_rows, tid);
   __syncthreads();
@@ -920,25 +931,36 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
     const uint2* wts[2] = {tile_scales<FMT>(a.gate_ts, tile * (D / 128) * 16),
                            tile_scales<FMT>(a.up_ts, tile * (D / 128) * 16)};
 
-    // the operand rows this thread stages: tokens of chunk rows tid/8 + 32m
+    // The item's assignments are requested first: those of the operand
+    // rows this thread stages (chunk rows tid/8 + 32m) and those of this
+    // lane's output tokens (4q+v of each tile; rows past the chunk repeat
+    // its last assignment).  Then the first weight burst, which needs only
+    // the expert, so it is in flight while the rows' addresses come back;
+    // the epilogue's per-token values (slot weight, activation exponent)
+    // are fetched while the K loop runs.
     const int Tk = a.meta[2];
+    int asg_r[NTT / 2], asg_o[NTT][4];
+#pragma unroll
+    for (int m = 0; m < NTT / 2; ++m) asg_r[m] = a.asg[it.p0 + min((tid >> 3) + 32 * m, it.n - 1)];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) asg_o[tt][v] = a.asg[it.p0 + min(16 * tt + 4 * q + v, it.n - 1)];
+    WBlk w[2][kloop_g<D>()][2];
+    k_loop_first<D, FMT>(w[0], wtq, wts, lane);
     const uint16_t* rows[NTT / 2];
 #pragma unroll
     for (int m = 0; m < NTT / 2; ++m) {
-      const int asg0 = a.asg[it.p0 + min((tid >> 3) + 32 * m, it.n - 1)];
-      const int tok = asg0 < Tk ? asg0 / k : asg0 - Tk;  // shared-expert assignments: Tk + token
+      const int tok = asg_r[m] < Tk ? asg_r[m] / k : asg_r[m] - Tk;  // shared-expert assignments: Tk + token
       rows[m] = a.xp + (size_t)tok * D;
     }
-    // the epilogue's per-token values (slot weight, activation exponent) of
-    // this lane's output tokens 4q+v of each tile, fetched while the K loop
-    // runs (rows past the chunk repeat its last assignment)
     float wjv[NTT][4];
     int eav[NTT][4];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int asg = a.asg[it.p0 + min(16 * tt + 4 * q + v, it.n - 1)];
+        const int asg = asg_o[tt][v];
         wjv[tt][v] = asg < Tk ? a.sel_w[asg] : 1.f;
         eav[tt][v] = a.xexp[asg < Tk ? asg / k : asg - Tk];
       }
@@ -947,7 +969,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // all token tiles always (rows past the chunk repeat a real row and
     // their outputs are dropped): one code path
-    k_loop<D, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
+    k_loop<D, NTT, FMT>(acc, s_tile, rows, wtq, wts, w, tid, lane, magic);
     // lane: weight row r16, tokens 4q+v of each tile
     const int e8 = r16 & 7;
     const int col = it.rg * 64 + wave * 16 + (r16 & 8) + 2 * (e8 & 3) + (e8 >> 2);  // h in operand order
@@ -1001,7 +1023,9 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
     f32x4_t acc[2][NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[0][tt] = acc[1][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    k_loop<F, NTT, FMT>(acc, s_tile, rows, wtq, wts, tid, lane, magic);
+    WBlk w[2][kloop_g<F>()][2];
+    k_loop_first<F, FMT>(w[0], wtq, wts, lane);
+    k_loop<F, NTT, FMT>(acc, s_tile, rows, wtq, wts, w, tid, lane, magic);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       if (16 * tt >= it.n) break;
