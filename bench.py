@@ -172,32 +172,54 @@ def time_eager(fn, steps, warmup, stream):
 
 
 def cpu_baseline(pool_np, xs_np, cfg, steps_per_run, runs=5):
-    """The fp64 oracle as it stands, on a bounded sample of the same steps:
-    `runs` timed runs of `steps_per_run` single-token layer steps, once with
-    one BLAS thread and once with the default thread pool; medians."""
+    """The plain C++ fp64 oracle as it stands, on a bounded sample of the same
+    steps: `runs` timed runs of `steps_per_run` single-token layer steps,
+    once single-threaded and once with OpenMP over the threads the process
+    may use (OMP_NUM_THREADS, else every hardware thread); medians.  The
+    numpy fp64 oracle is timed the same way beside it, with one BLAS thread
+    and with the default pool."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
+    from oracle import cpp_oracle as CO
     from oracle import moe as OM
 
-    def one_run():
+    layers = [CO.CLayer(p) for p in pool_np]
+
+    def run_cpp():
+        t0 = time.perf_counter()
+        for n in range(steps_per_run):
+            li = n % len(layers)
+            CO.moe_forward(layers[li], xs_np[li][n % len(xs_np[li])], cfg.k)
+        return time.perf_counter() - t0
+
+    def run_numpy():
         t0 = time.perf_counter()
         for n in range(steps_per_run):
             li = n % len(pool_np)
             OM.moe_forward(OM.Layer.from_dict(pool_np[li]), xs_np[li][n % len(xs_np[li])], cfg.k)
         return time.perf_counter() - t0
 
-    one_run()  # first touch of the layers' pages
+    n_omp = CO.get_threads()
+    run_cpp()  # first touch of the layers' pages
+    CO.set_threads(1)
+    single = sorted(run_cpp() for _ in range(runs))
+    CO.set_threads(n_omp)
+    multi = sorted(run_cpp() for _ in range(runs))
     with threadpool_limits(1):
-        single = sorted(one_run() for _ in range(runs))
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    multi = sorted(one_run() for _ in range(runs))
-    med1, medn = single[runs // 2], multi[runs // 2]
-    return dict(value=round(steps_per_run / medn, 3), unit="tokens/s", cores=threads, kind="oracle",
-                host_cores=os.cpu_count(),
-                single_thread={"value": round(steps_per_run / med1, 3), "unit": "tokens/s", "cores": 1},
-                sample=f"{runs} runs of {steps_per_run} single-token layer steps over {min(steps_per_run, len(pool_np))} "
-                       f"layers of the pool, median; numpy fp64 with {threads} BLAS threads (value) and with 1 "
-                       f"(single_thread); host cores {os.cpu_count()}")
+        np1 = sorted(run_numpy() for _ in range(runs))
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    npn = sorted(run_numpy() for _ in range(runs))
+    med = lambda v: v[runs // 2]  # noqa: E731
+    rate = lambda t: round(steps_per_run / t, 3)  # noqa: E731
+    nl = min(steps_per_run, len(pool_np))
+    return dict(value=rate(med(multi)), unit="tokens/s", cores=n_omp, kind="oracle",
+                host_cores=CO.hw_threads(),
+                single_thread={"value": rate(med(single)), "unit": "tokens/s", "cores": 1},
+                numpy_oracle={"value": rate(med(npn)), "cores": blas, "single_thread": rate(med(np1)),
+                              "unit": "tokens/s"},
+                sample=f"{runs} runs of {steps_per_run} single-token layer steps over {nl} layers of the pool, "
+                       f"median; plain C++ fp64 oracle with OpenMP over {n_omp} threads (value) and single-threaded "
+                       f"(single_thread); host hardware threads {CO.hw_threads()}; the numpy fp64 oracle beside it")
 
 
 def main():

@@ -6,6 +6,7 @@ import synth
 import sparse_moe_decode_gemv_amd as M
 from conftest import golden_lines
 from gpu_common import as_i16, device
+from oracle import cpp_oracle as OC
 from oracle import formats as F
 from oracle import lmhead as OH
 from oracle.inputs import pick_hidden_rows
@@ -109,3 +110,8 @@ def test_full_lmhead_parity(B):
     q, s = synth.make_lmhead(cfg, 1)
     X, _ = pick_hidden_rows(q, s, cfg.margin, lambda b, a: synth.draw_hidden(cfg, 1, b, a), B)
     check(q, s, X, f"lmhead B={B}")
+    # and against the plain C++ oracle
+    tok, ml = run(q, s, X)
+    ctok, cml, _ = OC.lmhead_argmax(q, s, X, want_logits=False)
+    assert np.array_equal(tok, ctok), f"lmhead B={B}: tokens {tok} vs C++ oracle {ctok}"
+    assert np.all(np.abs(ml - cml) <= 2e-3 * np.abs(cml)), f"lmhead B={B}: max logit {ml} vs {cml}"

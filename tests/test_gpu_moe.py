@@ -7,6 +7,7 @@ import pytest
 import synth
 import sparse_moe_decode_gemv_amd as M
 from gpu_common import Y_TOL, as_i16, compare_layer, device, tokens, zero_expert_layer
+from oracle import cpp_oracle as OC
 from oracle import moe as OM
 
 pytestmark = pytest.mark.gpu
@@ -154,10 +155,12 @@ def test_flagship_layer_parity(seed):
     OL = OM.Layer.from_dict(lay)
     X = tokens(cfg, OL, seed, 3)
     out = OM.moe_forward_tokens(OL, X, cfg.k)
+    cout = OC.moe_forward_tokens(lay, X, cfg.k)  # the plain C++ oracle
     # one call per token, as decode runs it
     for t in range(3):
         _, y, idx, w = run_layer(lay, cfg, X[t:t + 1])
         compare_layer({k: v[t:t + 1] for k, v in out.items()}, idx, w, y, f"layer seed {seed} token {t}")
+        compare_layer({k: v[t:t + 1] for k, v in cout.items()}, idx, w, y, f"layer seed {seed} token {t} (C++)")
 
 
 def test_batch_with_zipf_bias_parity():
@@ -168,6 +171,7 @@ def test_batch_with_zipf_bias_parity():
     X = tokens(cfg, OL, 1, cfg.T)
     L, y, idx, w = run_layer(lay, cfg, X)
     compare_layer(OM.moe_forward_tokens(OL, X, cfg.k), idx, w, y, "batch")
+    compare_layer(OC.moe_forward_tokens(lay, X, cfg.k), idx, w, y, "batch (C++ oracle)")
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
     assert counts.max() > 32  # the skew the workload is built to have: several 32-token chunks
     check_groups(L, cfg.T, idx)

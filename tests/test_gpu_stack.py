@@ -13,6 +13,7 @@ import pytest
 import synth
 import sparse_moe_decode_gemv_amd as M
 from gpu_common import Y_TOL, as_i16, device, tokens
+from oracle import cpp_oracle as OC
 from oracle import formats as F
 from oracle import moe as OM
 
@@ -72,12 +73,16 @@ def check_teacher_forced(layers_o, cfg, X0, r_gpu, xt, yt, it):
 
 
 def end_to_end(layers_o, cfg, X0, r_gpu):
-    """Whole-stack oracle from x_0 alone: final residual within Y_TOL of
-    max |r| per token (valid when no layer fell below the margin)."""
+    """Whole-stack oracles (numpy and C++) from x_0 alone: final residual
+    within Y_TOL of max |r| per token (valid when no layer fell below the
+    margin)."""
+    layers_c = [OC.CLayer(l) for l in layers_o]
     for t in range(X0.shape[0]):
-        ro = OM.stack_forward(layers_o, X0[t], cfg.k, EPS)["r"].astype(np.float64)
-        err = np.abs(r_gpu[t].astype(np.float64) - ro).max()
-        assert err <= Y_TOL * np.abs(ro).max(), f"token {t}: final residual err {err:.3e}"
+        for name, ro in (("numpy", OM.stack_forward(layers_o, X0[t], cfg.k, EPS)["r"]),
+                         ("C++", OC.stack_forward(layers_c, X0[t], cfg.k, EPS)["r"])):
+            ro = ro.astype(np.float64)
+            err = np.abs(r_gpu[t].astype(np.float64) - ro).max()
+            assert err <= Y_TOL * np.abs(ro).max(), f"token {t}: final residual err {err:.3e} ({name} oracle)"
 
 
 @pytest.mark.parametrize("seed,T", [(1, 3), (2, 1), (3, 1)], ids=["T3-batched", "T1-fused-a", "T1-fused-b"])
