@@ -209,13 +209,42 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   // global load behind the expert weight loads and waits for all of them.
   auto x2 = [&](int i) -> uint2 { return reinterpret_cast<const uint2*>(s_x)[i]; };  // elements 4i .. 4i+3
   auto x4 = [&](int i) -> uint4 { return reinterpret_cast<const uint4*>(s_x)[i]; };  // elements 8i .. 8i+7
-  // router row wg (one per wave): its weight loads go out first and stay in
-  // flight while the activation is staged
-  const bool router_row = blockIdx.x * 4 < E && wg < E;
-  if (router_row && !w_ready) {
-    const float4* wr = reinterpret_cast<const float4*>(a.router_w + (size_t)wg * D);
+  // The activation (or the residual it is normalized from) is requested
+  // first and the router row wg (one per wave) right behind it: a wave's
+  // loads complete in order, so the activation's few bytes arrive one round
+  // trip after the start and are staged (or normalized) while the router
+  // rows are still streaming in, instead of after them.
+  constexpr int XPT = (D / 8 + 255) / 256;  // 8-element x chunks per thread
+  constexpr int NR = (D / 4 + 255) / 256;   // residual float4 per thread
+  uint4 xq[XPT];
+  float4 rv[NR];
+  if constexpr (!NORM) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) w[i] = wr[64 * i + lane];
+    for (int m = 0; m < XPT; ++m) {
+      const int c = threadIdx.x + 256 * m;
+      xq[m] = c < D / 8 ? reinterpret_cast<const uint4*>(io.x)[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NR; ++m) rv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (MODE == kStepNorm || !io.rin) {  // r from memory
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int c = threadIdx.x + 256 * m;
+        if (c < D / 4) rv[m] = reinterpret_cast<const float4*>(io.resid_in)[c];
+      }
+    }
+  }
+  // Every wave issues the NI router loads (a wave without a router row
+  // reads one 16-byte word NI times): with the same number of loads in
+  // flight on every path the compiler waits for the activation alone
+  // (vmcnt(NI)); with a branch around the router loads it has to wait for
+  // all of them.
+  const bool router_row = blockIdx.x * 4 < E && wg < E;
+  if (!w_ready) {
+    const float4* wr = reinterpret_cast<const float4*>(a.router_w) + (router_row ? (size_t)wg * (D / 4) + lane : 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) w[i] = wr[router_row ? 64 * i : 0];
   }
   // gate/up slots: the k chosen experts, then the shared one (ns = 1), wpe
   // waves each
@@ -320,27 +349,21 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
   if constexpr (!NORM) {
     uint32_t mb = 0;  // the largest |x| (bf16 bits)
 #pragma unroll
-    for (int c = threadIdx.x; c < D / 8; c += 256) {
-      const uint4 q = reinterpret_cast<const uint4*>(io.x)[c];
-      reinterpret_cast<uint4*>(s_x)[c] = q;
-      mb = max(mb, max(max(bf16_mag_max(q.x), bf16_mag_max(q.y)), max(bf16_mag_max(q.z), bf16_mag_max(q.w))));
+    for (int m = 0; m < XPT; ++m) {
+      const int c = threadIdx.x + 256 * m;
+      if (c < D / 8) {
+        const uint4 q = xq[m];
+        reinterpret_cast<uint4*>(s_x)[c] = q;
+        mb = max(mb, max(max(bf16_mag_max(q.x), bf16_mag_max(q.y)), max(bf16_mag_max(q.z), bf16_mag_max(q.w))));
+      }
     }
     mb = wave_max_u32(mb);
     if (lane == 0) s_xm[wid] = mb;
     __syncthreads();
   } else {
-    // x = bf16(r / sqrt(mean(r^2) + eps)), the same in every workgroup
-    constexpr int NR = (D / 4 + 255) / 256;
-    float4 rv[NR];
-#pragma unroll
-    for (int m = 0; m < NR; ++m) rv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (MODE == kStepNorm || !io.rin) {  // r from memory
-#pragma unroll
-      for (int m = 0; m < NR; ++m) {
-        const int c = threadIdx.x + 256 * m;
-        rv[m] = c < D / 4 ? reinterpret_cast<const float4*>(io.resid_in)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    } else {  // r from the previous layer's tagged words, each thread the 4 * NR it normalizes
+    // x = bf16(r / sqrt(mean(r^2) + eps)), the same in every workgroup; r
+    // from memory was requested at the start
+    if (MODE == kStepChain && io.rin) {  // r from the previous layer's tagged words, each thread the 4 * NR it normalizes
       unsigned missing = 0;
 #pragma unroll
       for (int m = 0; m < NR; ++m) missing |= (threadIdx.x + 256 * m < D / 4 ? 0xFu : 0u) << (4 * m);
