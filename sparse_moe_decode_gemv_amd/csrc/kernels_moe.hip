@@ -91,6 +91,13 @@ __device__ __forceinline__ void topk_token(const LayerArgs& a, const uint16_t* _
   for (int i = 0; i < XC; ++i)
     xc[i] = 64 * i + lane < D / 8 ? reinterpret_cast<const uint4*>(x + (size_t)t * D)[64 * i + lane]
                                   : make_uint4(0u, 0u, 0u, 0u);
+  // the router bias (any valid address when there is none: the value is
+  // not used), requested with the first partial sums: a conditional load
+  // after them would cost one round trip per expert chunk
+  const float* bsrc = a.router_b ? a.router_b : a.logits;
+  float bv[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) bv[i] = bsrc[min(lane + 64 * i, E - 1)];
   constexpr int SU = EPL <= 4 ? 8 : 2;  // slices loaded at a time (all EPL * SU loads in flight)
   const float* p = a.logits + (size_t)t * E16;
   float l[EPL];
@@ -111,8 +118,7 @@ __device__ __forceinline__ void topk_token(const LayerArgs& a, const uint16_t* _
   float v[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = min(lane + 64 * i, E - 1);
-    const float li = a.router_b ? l[i] + a.router_b[e] : l[i];
+    const float li = a.router_b ? l[i] + bv[i] : l[i];
     v[i] = lane + 64 * i < E && li == li ? li : -INFINITY;
   }
   int se;
@@ -286,20 +292,58 @@ __device__ void sort_tables(const LayerArgs& a, int T, int Tk, int CS, int lane,
   }
 }
 
+// Count and place of a slice that fits one batch (a1 - a0 <= 64 kSortSB),
+// from experts the caller loaded once (eb[u]: assignment a0 + 64 u + lane).
+__device__ __forceinline__ void batch_count(const int (&eb)[kSortSB], int a0, int a1, int lane, int* cw) {
+#pragma unroll
+  for (int u = 0; u < kSortSB; ++u) {
+    if (a0 + 64 * u >= a1) break;
+    const bool v = a0 + 64 * u + lane < a1;
+    const uint64_t same = same_expert_lanes(eb[u], __builtin_amdgcn_ballot_w64(v));
+    if (v && lane == __builtin_ctzll(same)) cw[eb[u]] += __builtin_popcountll(same);
+    lds_wait();
+  }
+}
+__device__ __forceinline__ void batch_place(const LayerArgs& a, const int (&eb)[kSortSB], int a0, int a1, int lane,
+                                            int* cw) {
+#pragma unroll
+  for (int u = 0; u < kSortSB; ++u) {
+    const int i = a0 + 64 * u + lane;
+    if (a0 + 64 * u >= a1) break;
+    const bool v = i < a1;
+    const int e = eb[u];
+    const uint64_t same = same_expert_lanes(e, __builtin_amdgcn_ballot_w64(v));
+    const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+    const int pos = v ? cw[e] : 0;
+    lds_wait();
+    if (v) a.asg[pos + rank] = i;
+    if (v && lane == __builtin_ctzll(same)) cw[e] += __builtin_popcountll(same);
+    lds_wait();
+  }
+}
+
 // The sort in one workgroup of NW waves (up to kSortWideMin assignments).
-// LDS: cnt [NW][E], tot [E].
+// LDS: cnt [NW][E], tot [E].  When every wave's slice fits one batch (it
+// does for the callers' sizes) the chosen experts are loaded once for the
+// count and the placement (one round trip fewer).
 template <int NW, bool COH>
 __device__ void sort_body(const LayerArgs& a, int T, int CS, int* sm) {
   const int E = a.E, Tk = T * a.k;
   int* cnt = sm;
   int* tot = cnt + NW * E;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (Tk + NW - 1) / NW, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
+  const bool one = per <= 64 * kSortSB;
+  int eb[kSortSB];
+  if (one)
+#pragma unroll
+    for (int u = 0; u < kSortSB; ++u) eb[u] = sel_of<COH>(a, min(a0 + 64 * u + lane, Tk - 1), E);
   for (int i = tid; i < a.ns * T; i += 64 * NW) a.asg[Tk + i] = Tk + i;  // the shared expert's assignments, last
   for (int i = tid; i < NW * E; i += 64 * NW) cnt[i] = 0;
   __syncthreads();
-  const int per = (Tk + NW - 1) / NW, a0 = min(wave * per, Tk), a1 = min(a0 + per, Tk);
   int* cw = cnt + wave * E;
-  sort_count<COH>(a, Tk, a0, a1, lane, cw);
+  if (one) batch_count(eb, a0, a1, lane, cw);
+  else sort_count<COH>(a, Tk, a0, a1, lane, cw);
   __syncthreads();
   for (int e = tid; e < E; e += 64 * NW) {  // base of each wave within expert e, and e's total
     int run = 0;
@@ -315,7 +359,8 @@ __device__ void sort_body(const LayerArgs& a, int T, int CS, int* sm) {
   __syncthreads();
   for (int e = lane; e < E; e += 64) cw[e] += tot[e];  // absolute next positions of this wave
   lds_wait();
-  sort_place<COH>(a, Tk, a0, a1, lane, cw);
+  if (one) batch_place(a, eb, a0, a1, lane, cw);
+  else sort_place<COH>(a, Tk, a0, a1, lane, cw);
 }
 
 // One workgroup of 16 waves (up to kSortWideMin assignments).
