@@ -1090,33 +1090,46 @@ __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
 // ----------------------------------------------------------------- combine
 
 // y_t = 2^(-2 a_t) sum_{j<k} o_{t,j} (slot order); with resid, resid_t += y_t.
+// KP: k rounded up to a power of two.  Every row of the sum, the shared
+// expert's, the exponent and the residual are requested before any is used
+// (rows past k, and the shared row without a shared expert, repeat a real
+// row and are not added), so the thread waits one round trip, not one per
+// slot.
+template <int KP>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ obuf, const int32_t* __restrict__ xexp,
                                                  int T, int d, int k, int ns, float* __restrict__ y_out,
                                                  float* __restrict__ resid) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // float4 index over [T][d]
   if (i >= T * d / 4) return;
   const int t = (4 * i) / d, r = 4 * i - t * d;
+  float4 o[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) o[j] = *reinterpret_cast<const float4*>(obuf + ((size_t)t * k + min(j, k - 1)) * d + r);
+  const float4 osh = *reinterpret_cast<const float4*>(obuf + (ns ? (size_t)T * k + t : (size_t)t * k) * d + r);
+  const int ea = xexp[t];
+  float4* rp = reinterpret_cast<float4*>((resid ? resid : y_out) + (size_t)t * d + r);
+  const float4 rv0 = resid ? *rp : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float4 o = *reinterpret_cast<const float4*>(obuf + ((size_t)t * k + j) * d + r);
-    s.x += o.x;
-    s.y += o.y;
-    s.z += o.z;
-    s.w += o.w;
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    if (j < k) {
+      s.x += o[j].x;
+      s.y += o[j].y;
+      s.z += o[j].z;
+      s.w += o[j].w;
+    }
   }
   if (ns) {  // the shared expert's output, weight 1
-    const float4 o = *reinterpret_cast<const float4*>(obuf + ((size_t)T * k + t) * d + r);
-    s.x += o.x;
-    s.y += o.y;
-    s.z += o.z;
-    s.w += o.w;
+    s.x += osh.x;
+    s.y += osh.y;
+    s.z += osh.z;
+    s.w += osh.w;
   }
   // the outputs of token t were formed from h 2^(2 a_t)
-  const int e2 = -2 * xexp[t];
+  const int e2 = -2 * ea;
   s = make_float4(ldexpf(s.x, e2), ldexpf(s.y, e2), ldexpf(s.z, e2), ldexpf(s.w, e2));
   if (resid) {
-    float4* rp = reinterpret_cast<float4*>(resid + (size_t)t * d + r);
-    float4 rv = *rp;
+    float4 rv = rv0;
     rv.x += s.x;
     rv.y += s.y;
     rv.z += s.z;
@@ -1284,8 +1297,12 @@ hipError_t launch_down_combine(const LayerArgs& a, int T, float* y_out, float* r
   else e = c64 ? down_inst<4, 0>(a, g, s) : down_inst<2, 0>(a, g, s);
   if (e != hipSuccess) return e;
   const int n4 = T * a.d / 4;
-  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out,
-                     residual);
+  const dim3 cg((n4 + 255) / 256), cb(256);
+  if (a.k <= 1) hipLaunchKernelGGL(k_combine<1>, cg, cb, 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out, residual);
+  else if (a.k <= 2) hipLaunchKernelGGL(k_combine<2>, cg, cb, 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out, residual);
+  else if (a.k <= 4) hipLaunchKernelGGL(k_combine<4>, cg, cb, 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out, residual);
+  else if (a.k <= 8) hipLaunchKernelGGL(k_combine<8>, cg, cb, 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out, residual);
+  else hipLaunchKernelGGL(k_combine<16>, cg, cb, 0, s, a.obuf, a.xexp, T, a.d, a.k, a.ns, y_out, residual);
   return hipGetLastError();
 }
 
