@@ -34,7 +34,7 @@
  *   (u - 8) * scale[row][k/32], scale an IEEE binary16 bit pattern stored
  *   row-major [rows][K/32].  (Each 16-byte piece of a row thus holds 8
  *   elements of each of 4 consecutive groups of 32.)
- *   The pages say the model ships "integer four" builds and a 4-bit output
+ *   The pages list 4-bit integer builds among the releases and a 4-bit output
  *   layer but give no group size or layout; this format is the library's.
  */
 #ifndef MOE_DECODE_H

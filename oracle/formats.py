@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: part of the plain CPU oracle.  Nothing in the
 product path may import this package.
 
-The pages say the model ships "integer four builds" and that the output layer
+The pages list 4-bit integer builds among the releases and say the output layer
 is quantized to 4 bits ("Flint 40B: Best Mid Sized LLM", transcript 05:39 and
 07:15; "Recursive Releases Flint...", section "Built by an Automated Research
 System").  They give no group size, scale type or nibble order, so the stored
