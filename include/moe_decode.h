@@ -165,6 +165,17 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc* desc);
 moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* weights,
                            void* workspace, size_t workspace_bytes, moe_handle* out);
 
+/* The same as moe_decode_init, with its device work (the workspace clear, the
+ * MXFP4 scale scan, the batched path's copies, the persistent stack's
+ * argument copy) enqueued on `stream` (hipStream_t; NULL = the null stream),
+ * and only that stream synchronized before it returns: the init of the
+ * boundary as stated for this library, taking the caller's stream like every
+ * other call.  It synchronizes, so it must not be called while `stream` is
+ * being captured into a graph.  Same validation, errors and ownership as
+ * moe_decode_init. */
+moe_status moe_decode_init_on_stream(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                                     void* workspace, size_t workspace_bytes, void* stream, moe_handle* out);
+
 /* One decode step of T tokens through the layer (per token a router picks a
  * few of the routed experts and only those run, "Flint 40B: Best Mid Sized
  * LLM", transcript 02:35):

@@ -37,6 +37,7 @@ EXPORTED = (
     "moe_decode_destroy", "moe_decode_expert_groups", "lmhead_int4_argmax_workspace_bytes", "lmhead_int4_argmax", "moe_status_str",
     "moe_decode_abi_version", "moe_decode_error_flags", "moe_decode_set_wait_limit", "lmhead_int4_argmax_noalloc",
     "moe_decode_stack_forward_ex", "moe_decode_read_probe", "moe_int4_repack", "moe_decode_phase_trace",
+    "moe_decode_init_on_stream",
 )
 MOE_STACK_PERSISTENT = 1
 DEFAULT_WAIT_POLLS = 1 << 21
@@ -80,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_init.restype = i32
         L.moe_decode_init.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), p, sz,
                                       ctypes.POINTER(p)]
+        L.moe_decode_init_on_stream.restype = i32
+        L.moe_decode_init_on_stream.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), p, sz, p,
+                                                ctypes.POINTER(p)]
         L.moe_decode_forward.restype = i32
         L.moe_decode_forward.argtypes = [p, p, i32, p, p, p, p]
         L.moe_decode_stack_forward.restype = i32
@@ -154,6 +158,17 @@ def moe_decode_init(desc: LayerDesc, weights: LayerWeights, workspace, workspace
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     _check(lib().moe_decode_init(ctypes.byref(desc), ctypes.byref(weights), _ptr(workspace), nbytes,
                                  ctypes.byref(h)), "moe_decode_init")
+    return h.value
+
+
+def moe_decode_init_on_stream(desc: LayerDesc, weights: LayerWeights, workspace, workspace_bytes: int | None = None,
+                              stream=None) -> int:
+    """moe_decode_init with its device work on `stream` (default: the current
+    torch stream), synchronizing that stream only.  Returns the handle."""
+    h = ctypes.c_void_p()
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_decode_init_on_stream(ctypes.byref(desc), ctypes.byref(weights), _ptr(workspace), nbytes,
+                                           _stream(stream), ctypes.byref(h)), "moe_decode_init_on_stream")
     return h.value
 
 
@@ -242,9 +257,11 @@ class MoELayer:
     handle: int
 
     @classmethod
-    def create(cls, tensors: dict, d: int, f: int, E: int, k: int, norm_topk: int = 1, max_tokens: int = 1):
+    def create(cls, tensors: dict, d: int, f: int, E: int, k: int, norm_topk: int = 1, max_tokens: int = 1,
+               init_stream=None):
         """tensors: device tensors router_w, router_b (or None), gate_q, gate_s, up_q, up_s, down_q, down_s,
-        and shared_gate_q ... shared_down_s when the layer has a shared expert."""
+        and shared_gate_q ... shared_down_s when the layer has a shared expert.  init_stream: a torch
+        stream to initialize on (moe_decode_init_on_stream); None uses moe_decode_init."""
         import torch
         n_shared = 1 if tensors.get("shared_gate_q") is not None else 0
         # matrix scales: NVFP4; byte scales: MXFP4 (E8M0); 16-bit scales: int4 (binary16)
@@ -262,7 +279,11 @@ class MoELayer:
             raise MoEError(MOE_ERR_SHAPE, "moe_decode_workspace_bytes")
         ws = torch.empty(nbytes, dtype=torch.uint8, device=tensors["router_w"].device)
         w = LayerWeights(*[_ptr(tensors.get(n)) for n in WEIGHT_NAMES])
-        h = moe_decode_init(desc, w, ws)
+        if init_stream is None:
+            h = moe_decode_init(desc, w, ws)
+        else:
+            init_stream.wait_stream(torch.cuda.current_stream())  # the workspace tensor was made on the current stream
+            h = moe_decode_init_on_stream(desc, w, ws, stream=init_stream)
         return cls(d, f, E, k, norm_topk, max_tokens, tensors, ws, h)
 
     def forward(self, x, y=None, topk_idx=None, topk_w=None, stream=None):

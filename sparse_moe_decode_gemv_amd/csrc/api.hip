@@ -216,8 +216,10 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc* desc) {
   return layout_of(desc).total;
 }
 
-moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* w, void* workspace,
-                           size_t workspace_bytes, moe_handle* out) {
+// Init on stream s; device_sync: wait for the whole device at the end (the
+// plain init), else for s alone.
+static moe_status init_impl(const moe_layer_desc* desc, const moe_layer_weights* w, void* workspace,
+                            size_t workspace_bytes, hipStream_t s, bool device_sync, moe_handle* out) {
   if (!out) return MOE_ERR_NULL;
   *out = nullptr;
   const moe_status st = check_desc(desc);
@@ -304,7 +306,7 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
     delete h;
     return MOE_ERR_UNSUPPORTED;
   }
-  if (hipMemset(workspace, 0, L.cleared) != hipSuccess) {
+  if (hipMemsetAsync(workspace, 0, L.cleared, s) != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
   }
@@ -320,11 +322,12 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
               {desc->n_shared ? w->shared_gate_s : nullptr, per}, {desc->n_shared ? w->shared_up_s : nullptr, per},
               {desc->n_shared ? w->shared_down_s : nullptr, per}};
     for (const auto& c : sc)
-      if (c.p) hipLaunchKernelGGL(k_scan_e8m0, dim3(1024), dim3(256), 0, nullptr, static_cast<const uint8_t*>(c.p),
+      if (c.p) hipLaunchKernelGGL(k_scan_e8m0, dim3(1024), dim3(256), 0, s, static_cast<const uint8_t*>(c.p),
                                   c.n, lo, hi, a.error);
     unsigned flags = 0;
-    if (hipGetLastError() != hipSuccess || hipMemcpy(&flags, a.error, sizeof(flags), hipMemcpyDeviceToHost) != hipSuccess ||
-        hipMemset(a.error, 0, sizeof(unsigned)) != hipSuccess) {
+    if (hipGetLastError() != hipSuccess ||
+        hipMemcpyAsync(&flags, a.error, sizeof(flags), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess || hipMemsetAsync(a.error, 0, sizeof(unsigned), s) != hipSuccess) {
       delete h;
       return MOE_ERR_HIP;
     }
@@ -333,19 +336,27 @@ moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* 
       return MOE_ERR_UNSUPPORTED;
     }
   }
-  if ((copy && moe::launch_tile_weights(a, nullptr) != hipSuccess) || hipDeviceSynchronize() != hipSuccess) {
+  // the arguments a persistent stack reads for this layer (from a host copy
+  // that lives until the synchronization below)
+  const moe::FusedArgs f = h->fused ? fused_args(h) : moe::FusedArgs{};
+  if ((copy && moe::launch_tile_weights(a, s) != hipSuccess) ||
+      (h->fused && hipMemcpyAsync(h->args_dev, &f, sizeof(f), hipMemcpyHostToDevice, s) != hipSuccess) ||
+      (device_sync ? hipDeviceSynchronize() : hipStreamSynchronize(s)) != hipSuccess) {
     delete h;
     return MOE_ERR_HIP;
   }
-  if (h->fused) {  // the arguments a persistent stack reads for this layer
-    const moe::FusedArgs f = fused_args(h);
-    if (hipMemcpy(h->args_dev, &f, sizeof(f), hipMemcpyHostToDevice) != hipSuccess) {
-      delete h;
-      return MOE_ERR_HIP;
-    }
-  }
   *out = h;
   return MOE_OK;
+}
+
+moe_status moe_decode_init(const moe_layer_desc* desc, const moe_layer_weights* w, void* workspace,
+                           size_t workspace_bytes, moe_handle* out) {
+  return init_impl(desc, w, workspace, workspace_bytes, nullptr, true, out);
+}
+
+moe_status moe_decode_init_on_stream(const moe_layer_desc* desc, const moe_layer_weights* w, void* workspace,
+                                     size_t workspace_bytes, void* stream, moe_handle* out) {
+  return init_impl(desc, w, workspace, workspace_bytes, static_cast<hipStream_t>(stream), false, out);
 }
 
 void moe_decode_destroy(moe_handle h) { delete h; }

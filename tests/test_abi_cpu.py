@@ -93,6 +93,26 @@ def test_init_validation_codes():
     assert M.lib().moe_decode_init(None, ctypes.byref(weights()), FAKE, need, None) == M.MOE_ERR_NULL
 
 
+def test_init_on_stream_validation_codes():
+    """The stream form validates like moe_decode_init, before any GPU work."""
+    L = M.lib()
+
+    def st(d, w, ws_ptr=FAKE, ws_bytes=1 << 30):
+        h = ctypes.c_void_p()
+        return L.moe_decode_init_on_stream(ctypes.byref(d), ctypes.byref(w), ws_ptr, ws_bytes, None, ctypes.byref(h)), h
+
+    assert st(desc(), weights(gate_q=None))[0] == M.MOE_ERR_NULL
+    assert st(desc(), weights(up_s=FAKE + 2))[0] == M.MOE_ERR_ALIGN
+    assert st(desc(top_k=0), weights())[0] == M.MOE_ERR_SHAPE
+    assert st(desc(d=1536), weights())[0] == M.MOE_ERR_UNSUPPORTED
+    need = M.moe_decode_workspace_bytes(desc())
+    s, h = st(desc(), weights(), FAKE, need - 1)
+    assert s == M.MOE_ERR_WORKSPACE and h.value is None
+    assert st(desc(), weights(), FAKE + 16, need)[0] == M.MOE_ERR_ALIGN
+    assert L.moe_decode_init_on_stream(ctypes.byref(desc()), ctypes.byref(weights()), FAKE, need, None,
+                                       None) == M.MOE_ERR_NULL
+
+
 def test_shared_expert_validation_and_workspace():
     """n_shared = 1 needs all six shared matrices, 16-byte aligned; the
     batched workspace grows by the shared expert's assignments and copy."""

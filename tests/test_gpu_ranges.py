@@ -232,3 +232,55 @@ def test_int4_repack_matches_the_stored_layout(rows, K):
     M.moe_int4_repack(src, dst, rows, K)
     torch.cuda.synchronize()
     assert np.array_equal(dst.cpu().numpy(), F.pack_codes(u))
+
+
+# ---------------------------------------------------------------- init on a stream
+
+def test_init_on_stream_matches_init():
+    """A flagship layer that may run the batched kernels, initialized on a
+    side stream (moe_decode_init_on_stream: workspace clear, tile-major
+    copies and argument copy on that stream, only it synchronized): 1-token
+    steps and a T = 64 call bit-identical to the layer initialized by
+    moe_decode_init, and the 1-token steps within the bar of the oracle."""
+    import torch
+    dev = device()
+    cfg = synth.BATCH
+    lay = synth.make_layer(cfg, 3)
+    OL = OM.Layer.from_dict(lay)
+    X = tokens(cfg, OL, 3, cfg.T)
+    up = M.upload(lay, dev)
+    side = torch.cuda.Stream()
+    La = M.MoELayer.create(up, cfg.d, cfg.f, cfg.E, cfg.k, 1, cfg.T)
+    Lb = M.MoELayer.create(up, cfg.d, cfg.f, cfg.E, cfg.k, 1, cfg.T, init_stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    xd = torch.from_numpy(as_i16(X)).to(dev)
+    outs = []
+    for L in (La, Lb):
+        y1 = torch.empty((2, cfg.d), device=dev)
+        i1 = torch.empty((2, cfg.k), dtype=torch.int32, device=dev)
+        w1 = torch.empty((2, cfg.k), device=dev)
+        for t in range(2):
+            L.forward(xd[t:t + 1], y1[t:t + 1], i1[t:t + 1], w1[t:t + 1])
+        yb = torch.empty((cfg.T, cfg.d), device=dev)
+        ib = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+        L.forward(xd, yb, ib)
+        torch.cuda.synchronize()
+        outs.append([a.cpu().numpy() for a in (y1, i1, w1, yb, ib)])
+        assert L.error_flags() == 0
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    compare_layer(OM.moe_forward_tokens(OL, X[:2], cfg.k), outs[1][1], outs[1][2], outs[1][0], "init on a stream")
+    La.close()
+    Lb.close()
+
+
+def test_init_on_stream_rejects_like_init():
+    """An MXFP4 scale byte outside the batched path's range: the stream form
+    of init returns the same status."""
+    import torch
+    dev = device()
+    cfg = synth.TINY_FP4
+    up = M.upload(_mx_layer_with(141), dev)
+    with pytest.raises(M.MoEError) as ei:
+        M.MoELayer.create(up, cfg.d, cfg.f, cfg.E, cfg.k, 1, 8, init_stream=torch.cuda.Stream())
+    assert ei.value.status == M.MOE_ERR_UNSUPPORTED
