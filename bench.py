@@ -691,7 +691,11 @@ def main():
         del heads
 
     if "cpu" in extras:
-        out["cpu_baseline"] = cpu_baseline(pool_np, xs_np, cfg, args.cpu_steps)
+        cb = cpu_baseline(pool_np, xs_np, cfg, args.cpu_steps)
+        # the oracle's rate as algorithmic bytes per second, as for the GPU legs
+        cb["gbs_on_b_alg"] = round(cb["value"] * by["b_alg"] / 1e9, 3)
+        cb["single_thread"]["gbs_on_b_alg"] = round(cb["single_thread"]["value"] * by["b_alg"] / 1e9, 3)
+        out["cpu_baseline"] = cb
 
     print(json.dumps(out), flush=True)
 
