@@ -282,6 +282,10 @@ static moe_status init_impl(const moe_layer_desc* desc, const moe_layer_weights*
   a.act = reinterpret_cast<int32_t*>(base + L.act);
   a.chunk_off = reinterpret_cast<int32_t*>(base + L.chunk_off);
   a.chunks = reinterpret_cast<int4*>(base + L.chunks);
+  {
+    const long long T = desc->max_tokens, Tk = T * desc->top_k, E = desc->n_experts;
+    a.chunk_cap = (int)((E < Tk ? E : Tk) + Tk / 32 + desc->n_shared * ((T + 31) / 32));  // as in the layout
+  }
   a.asg = reinterpret_cast<int32_t*>(base + L.asg);
   a.h16 = reinterpret_cast<uint16_t*>(base + L.h16);
   a.obuf = reinterpret_cast<float*>(base + L.obuf);

@@ -711,6 +711,40 @@ __device__ __forceinline__ Item item_of(const LayerArgs& a, const ItemRange& r, 
   return it;
 }
 
+// Small T (32-token chunks, about one per chosen expert) takes another
+// order: chunk c goes to XCD c % 8 with all its row groups (which share
+// the chunk's activation or h rows in that XCD's L2), and workgroup slot j
+// (blockIdx / 8) of the XCD takes its items j, j + S, j + 2S, ... (S =
+// gridDim / 8), item i being chunk x + 8 (i / ngroups), row group i %
+// ngroups.  The first item's chunk is known before the chunk count, so its
+// table entry is requested together with the count: one round trip before
+// the item's own loads instead of two.  (Large T keeps the contiguous
+// ranges above, where consecutive chunks of one expert share the L2 for
+// its weights.)
+struct ItemWalk {
+  int x, j0, S, C, ngroups, cap;
+  int4 first;  // the table entry of the first item (clamped into the table)
+};
+__device__ __forceinline__ ItemWalk walk_start(const LayerArgs& a, int ngroups) {
+  ItemWalk w;
+  w.x = blockIdx.x & 7, w.j0 = blockIdx.x >> 3, w.S = gridDim.x >> 3, w.ngroups = ngroups, w.cap = a.chunk_cap;
+  w.first = a.chunks[min(w.x + 8 * (w.j0 / ngroups), w.cap - 1)];
+  w.C = a.meta[1];
+  asm volatile("" ::: "memory");  // both reads issued here, not sunk to their uses
+  return w;
+}
+// Item i of the walk; false past the last chunk.
+__device__ __forceinline__ bool walk_item(const LayerArgs& a, const ItemWalk& w, int i, Item& it) {
+  const int c = w.x + 8 * (i / w.ngroups);
+  if (c >= w.C) return false;
+  const int4 cd = i == w.j0 ? w.first : a.chunks[c];
+  it.e = cd.x;
+  it.p0 = cd.y;
+  it.n = cd.z;
+  it.rg = i - (i / w.ngroups) * w.ngroups;
+  return true;
+}
+
 // The operand rows of one 128-element block of K for the item's (up to)
 // 16*NTT rows (tokens or positions), in LDS in fragment order:
 // v[tt][j][q][slot] is chunk q of group j of row 16*tt + r, at slot
@@ -965,11 +999,21 @@ template <int D, int NTT, int FMT>
 __global__ __launch_bounds__(256, 2) void k_gateup(const LayerArgs a) {
   __shared__ OpTile<NTT> s_tile[2];
   const int f = a.f, k = a.k, ngroups = f / 64;
-  const ItemRange ir = xcd_items(a, ngroups);
+  constexpr bool WALK = NTT == 2;  // 32-token chunks: the small-T order (walk_item)
+  ItemRange ir{};
+  ItemWalk wk{};
+  if constexpr (WALK) wk = walk_start(a, ngroups);
+  else ir = xcd_items(a, ngroups);
   const uint32_t magic = magic_f16x2();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
-  for (int i = blockIdx.x >> 3; i < ir.n; i += ir.step) {
-    const Item it = item_of(a, ir, ngroups, i);
+  for (int i = blockIdx.x >> 3;; i += WALK ? wk.S : ir.step) {
+    Item it;
+    if constexpr (WALK) {
+      if (!walk_item(a, wk, i, it)) break;
+    } else {
+      if (i >= ir.n) break;
+      it = item_of(a, ir, ngroups, i);
+    }
     const size_t tile = (size_t)it.e * (f / 16) + it.rg * 4 + wave;  // 16-row tile of gate and of up
     const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.gate_t) + tile * (D / 128) * 64,
                            reinterpret_cast<const uint4*>(a.up_t) + tile * (D / 128) * 64};
@@ -1044,11 +1088,21 @@ template <int F, int NTT, int FMT>
 __global__ __launch_bounds__(256, 2) void k_down(const LayerArgs a) {
   __shared__ OpTile<NTT> s_tile[2];
   const int d = a.d, ngroups = d / 128;
-  const ItemRange ir = xcd_items(a, ngroups);
+  constexpr bool WALK = NTT == 2;  // 32-token chunks: the small-T order (walk_item)
+  ItemRange ir{};
+  ItemWalk wk{};
+  if constexpr (WALK) wk = walk_start(a, ngroups);
+  else ir = xcd_items(a, ngroups);
   const uint32_t magic = magic_f16x2();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, q = lane >> 4;
-  for (int i = blockIdx.x >> 3; i < ir.n; i += ir.step) {
-    const Item it = item_of(a, ir, ngroups, i);
+  for (int i = blockIdx.x >> 3;; i += WALK ? wk.S : ir.step) {
+    Item it;
+    if constexpr (WALK) {
+      if (!walk_item(a, wk, i, it)) break;
+    } else {
+      if (i >= ir.n) break;
+      it = item_of(a, ir, ngroups, i);
+    }
     const int row0 = it.rg * 128 + wave * 32 + r16;
     const size_t tile = (size_t)it.e * (d / 16) + it.rg * 8 + wave * 2;  // two 16-row tiles of W_d
     const uint4* wtq[2] = {reinterpret_cast<const uint4*>(a.down_t) + tile * (F / 128) * 64,

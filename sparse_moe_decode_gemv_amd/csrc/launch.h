@@ -14,6 +14,7 @@ struct LayerArgs {
   int d, f, E, k, norm_topk;
   int ns;  // shared experts, 0 or 1: expert index E of the tile-major copies, assignments T*k + t
   int fmt;  // 0 int4; 1 MXFP4 (the *_s pointers and scale copies hold E8M0 bytes); 2 NVFP4 (E4M3 bytes per 16)
+  int chunk_cap;  // entries of the chunk table (its size for max_tokens tokens)
   const float* gate_tscale;  // NVFP4: fp32 scale of each expert matrix [E] (shared: [1])
   const float* up_tscale;
   const float* down_tscale;
