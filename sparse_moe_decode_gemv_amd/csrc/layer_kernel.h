@@ -407,13 +407,15 @@ __device__ __forceinline__ unsigned layer_step(const A& a, const StepIO& io, flo
     ss = wave_sum(ss);
     if (lane == 0) s_ss[wid] = ss;
     __syncthreads();
-    const float den = sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)D + io.eps);
+    // one reciprocal of the root, then products (within an ulp of the
+    // quotients before the bf16 rounding)
+    const float inv = 1.0f / sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)D + io.eps);
     uint32_t mb = 0;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
       const int c = threadIdx.x + 256 * m;
       if (c < D / 4) {
-        const uint2 pk = make_uint2(pack_bf16(rv[m].x / den, rv[m].y / den), pack_bf16(rv[m].z / den, rv[m].w / den));
+        const uint2 pk = make_uint2(pack_bf16(rv[m].x * inv, rv[m].y * inv), pack_bf16(rv[m].z * inv, rv[m].w * inv));
         reinterpret_cast<uint2*>(s_x)[c] = pk;
         mb = max(mb, max(bf16_mag_max(pk.x), bf16_mag_max(pk.y)));
         if (io.x_trace && blockIdx.x == 0) reinterpret_cast<uint2*>(io.x_trace)[c] = pk;
